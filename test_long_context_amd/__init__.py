@@ -1,0 +1,196 @@
+"""TTT-E2E inner loop on AMD MI355X (gfx950): Python binding of libttt.so.
+
+Argument marshalling only: every step of the path runs in the HIP library
+(include/ttt.h); torch provides device memory and the current stream. The
+binding raises if the library is missing or a call fails -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libttt.so")
+
+TTT_OK = 0
+STATUS = {0: "TTT_OK", -1: "TTT_ERR_INVALID_ARG", -2: "TTT_ERR_UNSUPPORTED", -3: "TTT_ERR_OOM",
+          -4: "TTT_ERR_HIP", -5: "TTT_ERR_STATE", -6: "TTT_ERR_TOKEN_RANGE",
+          -7: "TTT_ERR_NONFINITE", -8: "TTT_ERR_NO_DEVICE"}
+
+
+class TTTError(RuntimeError):
+    def __init__(self, code: int, msg: str = ""):
+        self.code = code
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn_hidden", ctypes.c_int32),
+                ("dyn_ffn_hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("minibatch", ctypes.c_int32),
+                ("n_dynamic", ctypes.c_int32), ("max_seq", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("reduction", ctypes.c_int32)]
+
+
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("final_norm", ctypes.c_void_p)] + [
+        (n, _PP) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w1", "w2", "w3",
+                           "dyn_norm", "dyn_w1", "dyn_w2", "dyn_w3")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libttt.so (built by `python -m test_long_context_amd.build`)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m test_long_context_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+        L.ttt_init.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), vp, ctypes.POINTER(vp)]
+        L.ttt_prefill.argtypes = [vp, vp, i64, vp, vp, vp]
+        L.ttt_decode_step.argtypes = [vp, vp, vp, vp]
+        L.ttt_get_fast_weights.argtypes = [vp, i32, vp, vp, vp, vp]
+        L.ttt_reset.argtypes = [vp, vp]
+        L.ttt_sync.argtypes = [vp, vp]
+        L.ttt_position.argtypes = [vp]
+        L.ttt_position.restype = i64
+        L.ttt_last_error.argtypes = [vp]
+        L.ttt_last_error.restype = ctypes.c_char_p
+        L.ttt_destroy.argtypes = [vp]
+        L.ttt_destroy.restype = None
+        L.e2ttt_chunk_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
+        for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_get_fast_weights", "ttt_reset",
+                  "ttt_sync", "e2ttt_chunk_scan"):
+            getattr(L, f).restype = st
+        _lib = L
+    return _lib
+
+
+def _stream(stream=None):
+    import torch
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    if torch.cuda.is_available():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(None)
+
+
+def make_config(c: dict, max_seq: Optional[int] = None) -> Config:
+    return Config(n_layers=c["n_layers"], d_model=c["d_model"], n_heads=c["n_heads"],
+                  n_kv_heads=c["n_kv_heads"], head_dim=c["head_dim"], ffn_hidden=c["ffn_hidden"],
+                  dyn_ffn_hidden=c["dyn_ffn_hidden"], vocab=c["vocab"], window=c["window"],
+                  minibatch=c["minibatch"], n_dynamic=c.get("n_dynamic", 0),
+                  max_seq=int(max_seq if max_seq is not None else c.get("max_seq", c["seq"])),
+                  alpha=float(c["alpha"]), rms_eps=float(c["rms_eps"]),
+                  rope_theta=float(c["rope_theta"]), dtype=0 if c["dtype"] == "f32" else 1,
+                  reduction=0 if c.get("reduction", "mean") == "mean" else 1)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _arr(ptrs):
+    a = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    return a, ctypes.cast(a, _PP)
+
+
+class TTT:
+    """One inner-loop context on the current GPU (see include/ttt.h)."""
+
+    def __init__(self, cfg: dict, weights: dict, max_seq: Optional[int] = None, stream=None):
+        self.cfg = dict(cfg)
+        self._keep = []
+        W = Weights(embed=_ptr(weights["embed"]), lm_head=_ptr(weights["lm_head"]),
+                    final_norm=_ptr(weights["final_norm"]))
+        for f in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w1", "w2", "w3"):
+            a, p = _arr([_ptr(x[f]) for x in weights["layers"]])
+            self._keep.append(a)
+            setattr(W, f, p)
+        for f, k in (("dyn_norm", "norm"), ("dyn_w1", "w1"), ("dyn_w2", "w2"), ("dyn_w3", "w3")):
+            a, p = _arr([_ptr(x[k]) for x in weights["dyn"]])
+            self._keep.append(a)
+            setattr(W, f, p)
+        self.c_cfg = make_config(cfg, max_seq)
+        h = ctypes.c_void_p()
+        st = lib().ttt_init(ctypes.byref(self.c_cfg), ctypes.byref(W), _stream(stream), ctypes.byref(h))
+        if st != TTT_OK:
+            raise TTTError(st, "ttt_init")
+        self.h = h
+
+    def _chk(self, st, what):
+        if st != TTT_OK:
+            raise TTTError(st, f"{what}: {lib().ttt_last_error(self.h).decode()}")
+
+    def prefill(self, tokens, loss=None, last_logits=None, stream=None):
+        import torch
+        T = tokens.numel()
+        if loss is None:
+            loss = torch.empty(T - 1, dtype=torch.float32, device=tokens.device)
+        self._chk(lib().ttt_prefill(self.h, _ptr(tokens), T, _ptr(loss), _ptr(last_logits),
+                                    _stream(stream)), "ttt_prefill")
+        return loss
+
+    def decode_step(self, token, logits=None, stream=None):
+        import torch
+        if logits is None:
+            logits = torch.empty(self.cfg["vocab"], dtype=torch.float32, device=token.device)
+        self._chk(lib().ttt_decode_step(self.h, _ptr(token), _ptr(logits), _stream(stream)),
+                  "ttt_decode_step")
+        return logits
+
+    def fast_weights(self, i: int, stream=None):
+        import torch
+        d, Fd = self.cfg["d_model"], self.cfg["dyn_ffn_hidden"]
+        dev = torch.device("cuda")
+        w1 = torch.empty(Fd, d, dtype=torch.float32, device=dev)
+        w2 = torch.empty(Fd, d, dtype=torch.float32, device=dev)
+        w3 = torch.empty(d, Fd, dtype=torch.float32, device=dev)
+        self._chk(lib().ttt_get_fast_weights(self.h, i, _ptr(w1), _ptr(w2), _ptr(w3), _stream(stream)),
+                  "ttt_get_fast_weights")
+        return w1, w2, w3
+
+    def reset(self, stream=None):
+        self._chk(lib().ttt_reset(self.h, _stream(stream)), "ttt_reset")
+
+    def sync(self, stream=None):
+        self._chk(lib().ttt_sync(self.h, _stream(stream)), "ttt_sync")
+
+    @property
+    def position(self) -> int:
+        return int(lib().ttt_position(self.h))
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().ttt_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def e2ttt_chunk_scan(k, v, eta, beta, gamma, W, M, chunk: int, stream=None):
+    """In-place E2-TTT chunk-end scan over all chunks (see include/ttt.h)."""
+    H, T, D = k.shape
+    st = lib().e2ttt_chunk_scan(_ptr(k), _ptr(v), _ptr(eta), _ptr(beta), _ptr(gamma), _ptr(W),
+                                _ptr(M), H, T, D, chunk, _stream(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "e2ttt_chunk_scan")
+    return W, M

@@ -1,0 +1,369 @@
+// Row-wise and elementwise kernels of the TTT-E2E path: embedding gather,
+// RMSNorm forward/backward, RoPE application + key/value store scatter, the
+// RoPE backward that packs dQKV, the fused vocabulary softmax-CE with its
+// logit gradient, and small helpers. All are HBM-bound; they read and write
+// each element once, with 16-byte accesses where the layout allows.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ttt {
+
+static constexpr int RB = 256;  // threads per row-block
+
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += sh[i];
+  return t;
+}
+
+// --------------------------------------------------------------- embedding
+template <typename T>
+__global__ void embed_kernel(const int32_t* tok, int n, const T* E, int d, float* h, int V, int* err) {
+  const int t = blockIdx.x;
+  const int id = tok[t];
+  const bool ok = id >= 0 && id < V;
+  if (!ok && threadIdx.x == 0) atomicOr(err, 1);
+  for (int j = threadIdx.x; j < d; j += blockDim.x)
+    h[(long)t * d + j] = ok ? to_f(E[(long)id * d + j]) : 0.f;
+}
+
+hipError_t embed_gather(DT dt, const int32_t* tok, int n, const void* E, int d, float* h, int V,
+                        int* err, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(n), dim3(RB), 0, st, tok, n, (const bf16*)E, d, h, V, err);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(n), dim3(RB), 0, st, tok, n, (const float*)E, d, h, V, err);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- RMSNorm
+template <typename T>
+__global__ void rms_fwd_kernel(const float* x, const float* g, int d, float eps, T* y, float* r) {
+  __shared__ float sh[RB / 64];
+  const long t = blockIdx.x;
+  const float* xr = x + t * d;
+  float ss = 0.f;
+  for (int j = threadIdx.x; j < d; j += blockDim.x) ss += xr[j] * xr[j];
+  ss = block_sum(ss, sh);
+  const float rr = rsqrtf(ss / d + eps);
+  for (int j = threadIdx.x; j < d; j += blockDim.x) y[t * d + j] = from_f<T>(g[j] * xr[j] * rr);
+  if (threadIdx.x == 0) r[t] = rr;
+}
+
+hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, float eps, void* y,
+                       float* r, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(rms_fwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, x, g, d, eps, (bf16*)y, r);
+  else
+    hipLaunchKernelGGL(rms_fwd_kernel<float>, dim3(n), dim3(RB), 0, st, x, g, d, eps, (float*)y, r);
+  return hipGetLastError();
+}
+
+// dx = r (g dy) - x r^3 mean((g dy) x); dh (+)= dx; dh_t = T(dh).
+template <typename T>
+__global__ void rms_bwd_kernel(const float* dy, int nsplit, long sstride, const float* x,
+                               const float* g, const float* r, int d, float* dh, T* dh_t, int acc) {
+  __shared__ float sh[RB / 64];
+  const long t = blockIdx.x;
+  const float rr = r[t];
+  float dot = 0.f;
+  for (int j = threadIdx.x; j < d; j += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += dy[s * sstride + t * d + j];
+    dot += g[j] * v * x[t * d + j];
+  }
+  dot = block_sum(dot, sh) / d;
+  const float c = rr * rr * rr * dot;
+  for (int j = threadIdx.x; j < d; j += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += dy[s * sstride + t * d + j];
+    float o = rr * g[j] * v - x[t * d + j] * c;
+    if (acc) o += dh[t * d + j];
+    dh[t * d + j] = o;
+    if (dh_t) dh_t[t * d + j] = from_f<T>(o);
+  }
+}
+
+hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const float* g,
+                       const float* r, int n, int d, float* dh, void* dh_t, int accumulate,
+                       hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long ss = (long)n * d;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(rms_bwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, dy, nsplit, ss, x, g, r, d, dh,
+                       (bf16*)dh_t, accumulate);
+  else
+    hipLaunchKernelGGL(rms_bwd_kernel<float>, dim3(n), dim3(RB), 0, st, dy, nsplit, ss, x, g, r, d, dh,
+                       (float*)dh_t, accumulate);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------------- RoPE
+// Half-split rotation: (x1, x2) -> (x1 c - x2 s, x1 s + x2 c), with (c, s)
+// at tab[pos * dh/2 + j] (built on the host from float64 angles).
+template <typename T>
+__global__ void rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, int64_t pos0,
+                                    const float2* tab, T* q, T* ks, T* vs, int cap,
+                                    int64_t min_pos) {
+  const int t = blockIdx.x;
+  const int64_t pos = pos0 + t;
+  const int half = dh / 2;
+  const int W = (H + 2 * Hk) * dh;
+  const T* row = qkv + (long)t * W;
+  const float2* tb = tab + pos * half;
+  const bool store = pos >= min_pos;
+  const long slot = (long)(pos & (cap - 1));
+  // q and k heads: pairs
+  for (int i = threadIdx.x; i < (H + Hk) * half; i += blockDim.x) {
+    const int hh = i / half, j = i % half;
+    const float2 cs = tb[j];
+    const float x1 = to_f(row[hh * dh + j]), x2 = to_f(row[hh * dh + j + half]);
+    const float y1 = x1 * cs.x - x2 * cs.y, y2 = x1 * cs.y + x2 * cs.x;
+    if (hh < H) {
+      q[((long)t * H + hh) * dh + j] = from_f<T>(y1);
+      q[((long)t * H + hh) * dh + j + half] = from_f<T>(y2);
+    } else if (store) {
+      const int kh = hh - H;
+      ks[((long)kh * cap + slot) * dh + j] = from_f<T>(y1);
+      ks[((long)kh * cap + slot) * dh + j + half] = from_f<T>(y2);
+    }
+  }
+  if (store)
+    for (int i = threadIdx.x; i < Hk * dh; i += blockDim.x) {
+      const int kh = i / dh, j = i % dh;
+      vs[((long)kh * cap + slot) * dh + j] = row[(H + Hk) * dh + i];
+    }
+}
+
+hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, int64_t pos0,
+                        const float2* tab, void* q, void* ks, void* vs, int cap, int64_t min_pos,
+                        hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(n), dim3(RB), 0, st, (const bf16*)qkv, n, H, Hk,
+                       dh, pos0, tab, (bf16*)q, (bf16*)ks, (bf16*)vs, cap, min_pos);
+  else
+    hipLaunchKernelGGL(rope_scatter_kernel<float>, dim3(n), dim3(RB), 0, st, (const float*)qkv, n, H,
+                       Hk, dh, pos0, tab, (float*)q, (float*)ks, (float*)vs, cap, min_pos);
+  return hipGetLastError();
+}
+
+// Transpose of the rotation (rotation by -angle) for dq, dk; dv copied.
+template <typename T>
+__global__ void rope_bwd_kernel(const float* dq, const float* dk, const float* dv, int H, int Hk,
+                                int dh, int64_t pos0, const float2* tab, T* out) {
+  const int t = blockIdx.x;
+  const int half = dh / 2;
+  const int W = (H + 2 * Hk) * dh;
+  const float2* tb = tab + (pos0 + t) * half;
+  for (int i = threadIdx.x; i < (H + Hk) * half; i += blockDim.x) {
+    const int hh = i / half, j = i % half;
+    const float2 cs = tb[j];
+    const float* src = hh < H ? dq + ((long)t * H + hh) * dh : dk + ((long)t * Hk + (hh - H)) * dh;
+    const float g1 = src[j], g2 = src[j + half];
+    out[(long)t * W + hh * dh + j] = from_f<T>(g1 * cs.x + g2 * cs.y);
+    out[(long)t * W + hh * dh + j + half] = from_f<T>(-g1 * cs.y + g2 * cs.x);
+  }
+  for (int i = threadIdx.x; i < Hk * dh; i += blockDim.x)
+    out[(long)t * W + (H + Hk) * dh + i] = from_f<T>(dv[(long)t * Hk * dh + i]);
+}
+
+hipError_t rope_bwd_pack(DT dt, const float* dq, const float* dk, const float* dv, int n, int H,
+                         int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
+                         hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(rope_bwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, dq, dk, dv, H, Hk, dh, pos0, tab,
+                       (bf16*)dqkv);
+  else
+    hipLaunchKernelGGL(rope_bwd_kernel<float>, dim3(n), dim3(RB), 0, st, dq, dk, dv, H, Hk, dh, pos0, tab,
+                       (float*)dqkv);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- softmax CE + dz
+// One workgroup per row: pass 1 keeps a per-thread running (max, sum-exp)
+// over float4 chunks, combined across the block; pass 2 writes
+// dz = (exp(z - lse) - [v == label]) * scale.
+template <typename T>
+__global__ void __launch_bounds__(RB) ce_kernel(const float* z, int nt, int V, const int32_t* lab,
+                                                float scale, float* loss, T* dz, int* err) {
+  __shared__ float shm[RB / 64], shs[RB / 64];
+  const long t = blockIdx.x;
+  const float* zr = z + t * V;
+  T* dr = dz + t * V;
+  if ((int)t >= nt) {
+    for (int j = threadIdx.x; j < V; j += blockDim.x) dr[j] = from_f<T>(0.f);
+    return;
+  }
+  float m = -INFINITY, s = 0.f;
+  const float4* z4 = (const float4*)zr;
+  for (int j = threadIdx.x; j < V / 4; j += blockDim.x) {
+    const float4 v = z4[j];
+    const float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    if (mx > m) {
+      s *= __expf(m - mx);
+      m = mx;
+    }
+    s += __expf(v.x - m) + __expf(v.y - m) + __expf(v.z - m) + __expf(v.w - m);
+  }
+  // combine (m, s) across the wave, then the block
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    const float mn = fmaxf(m, m2);
+    s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mn));
+    m = mn;
+  }
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) {
+    shm[w] = m;
+    shs[w] = s;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int i = 0; i < RB / 64; ++i) M = fmaxf(M, shm[i]);
+  float S = 0.f;
+  for (int i = 0; i < RB / 64; ++i) S += shs[i] * __expf(shm[i] - M);
+  const float lse = M + __logf(S);
+  const int y = lab[t];
+  const bool yok = y >= 0 && y < V;
+  if (threadIdx.x == 0) {
+    const float li = yok ? lse - zr[y] : NAN;
+    loss[t] = li;
+    if (!yok) atomicOr(err, 1);
+    else if (!isfinite(li)) atomicOr(err, 4);
+  }
+  for (int j = threadIdx.x; j < V / 4; j += blockDim.x) {
+    const float4 v = z4[j];
+    const int b = 4 * j;
+    dr[b + 0] = from_f<T>((__expf(v.x - lse) - (b + 0 == y ? 1.f : 0.f)) * scale);
+    dr[b + 1] = from_f<T>((__expf(v.y - lse) - (b + 1 == y ? 1.f : 0.f)) * scale);
+    dr[b + 2] = from_f<T>((__expf(v.z - lse) - (b + 2 == y ? 1.f : 0.f)) * scale);
+    dr[b + 3] = from_f<T>((__expf(v.w - lse) - (b + 3 == y ? 1.f : 0.f)) * scale);
+  }
+}
+
+hipError_t ce_fwd_bwd(DT dt, const float* z, int n, int nt, int V, const int32_t* lab, float scale,
+                      float* loss, void* dz, int* err, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(ce_kernel<bf16>, dim3(n), dim3(RB), 0, st, z, nt, V, lab, scale, loss, (bf16*)dz, err);
+  else
+    hipLaunchKernelGGL(ce_kernel<float>, dim3(n), dim3(RB), 0, st, z, nt, V, lab, scale, loss, (float*)dz,
+                       err);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ rowdot D
+template <typename T>
+__global__ void rowdot_kernel(const T* dO, const T* O, int n, int H, int dh, float* D) {
+  // one wave per (t, h)
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (w >= (long)n * H) return;
+  const long t = w / H, h = w % H;
+  float s = 0.f;
+  for (int j = l; j < dh; j += 64) s += to_f(dO[w * dh + j]) * to_f(O[w * dh + j]);
+  s = wave_sum(s);
+  if (l == 0) D[h * n + t] = s;
+}
+
+hipError_t attn_rowdot(DT dt, const void* dO, const void* O, int n, int H, int dh, float* D,
+                       hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long nw = (long)n * H;
+  dim3 grid((unsigned)((nw + 3) / 4));
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(rowdot_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)dO, (const bf16*)O, n, H, dh, D);
+  else
+    hipLaunchKernelGGL(rowdot_kernel<float>, grid, dim3(256), 0, st, (const float*)dO, (const float*)O, n, H, dh,
+                       D);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- helpers
+__global__ void copy_f32_kernel(const float* s, float* d, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    d[i] = s[i];
+}
+template <typename T>
+__global__ void cast_to_kernel(const float* s, T* d, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    d[i] = from_f<T>(s[i]);
+}
+template <typename T>
+__global__ void cast_from_kernel(const T* s, float* d, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    d[i] = to_f(s[i]);
+}
+__global__ void fill_i32_kernel(int* p, int v, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+__global__ void fill_f32_kernel(float* p, float v, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+__global__ void fill_u32_kernel(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+__global__ void fill_u8_kernel(uint8_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+static dim3 grid_for(size_t n) {
+  size_t b = (n + 255) / 256;
+  if (b > 65536) b = 65536;
+  if (b == 0) b = 1;
+  return dim3((unsigned)b);
+}
+
+hipError_t copy_f32(const float* s, float* d, size_t n, hipStream_t st) {
+  if (!n) return hipSuccess;
+  hipLaunchKernelGGL(copy_f32_kernel, grid_for(n), dim3(256), 0, st, s, d, n);
+  return hipGetLastError();
+}
+hipError_t cast_to(DT dt, const float* s, void* d, size_t n, hipStream_t st) {
+  if (!n) return hipSuccess;
+  if (dt == DT::BF16) hipLaunchKernelGGL(cast_to_kernel<bf16>, grid_for(n), dim3(256), 0, st, s, (bf16*)d, n);
+  else hipLaunchKernelGGL(cast_to_kernel<float>, grid_for(n), dim3(256), 0, st, s, (float*)d, n);
+  return hipGetLastError();
+}
+hipError_t cast_from(DT dt, const void* s, float* d, size_t n, hipStream_t st) {
+  if (!n) return hipSuccess;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(cast_from_kernel<bf16>, grid_for(n), dim3(256), 0, st, (const bf16*)s, d, n);
+  else hipLaunchKernelGGL(cast_from_kernel<float>, grid_for(n), dim3(256), 0, st, (const float*)s, d, n);
+  return hipGetLastError();
+}
+hipError_t fill_i32(int* p, int v, size_t n, hipStream_t st) {
+  if (!n) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, grid_for(n), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+hipError_t fill_f32(float* p, float v, size_t n, hipStream_t st) {
+  if (!n) return hipSuccess;
+  hipLaunchKernelGGL(fill_f32_kernel, grid_for(n), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+hipError_t fill_zero_bytes(void* p, size_t nb, hipStream_t st) {
+  if (!nb) return hipSuccess;
+  if ((nb & 3) == 0 && ((uintptr_t)p & 3) == 0)
+    hipLaunchKernelGGL(fill_u32_kernel, grid_for(nb / 4), dim3(256), 0, st, (uint32_t*)p, nb / 4);
+  else
+    hipLaunchKernelGGL(fill_u8_kernel, grid_for(nb), dim3(256), 0, st, (uint8_t*)p, nb);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -1,0 +1,714 @@
+// TTT-E2E engine: owns the context state on one GPU and schedules the
+// kernels of the inner loop on the caller's stream. Implements include/ttt.h.
+//
+// Phases of ttt_prefill (all on the caller's stream):
+//   prefix  -- blocks 0 .. s-1 and the attention + static MLP of block s do not
+//              depend on any fast weight, so they run once over the sequence
+//              in slabs of up to `slab` positions (large GEMMs); their keys and
+//              values go to the per-layer rings, and the residual stream at the
+//              input of block s's dynamic MLP is kept for every position.
+//   loop    -- for each mini-batch: block s's dynamic MLP, blocks s+1 .. L-1
+//              (attention over the ring window, static MLP, dynamic MLP), final
+//              norm, lm_head, fused softmax-CE + dz, then the backward into the
+//              dynamic MLP weights, whose dW products apply the fp32 SGD update
+//              W -= alpha dW in their epilogue (bf16 working copy re-rounded
+//              from the fp32 master).
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/ttt.h"
+#include "kernels.hpp"
+
+using namespace ttt;
+
+namespace {
+
+struct Buf {
+  void* p = nullptr;
+  size_t n = 0;
+};
+
+int64_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+struct ttt_ctx {
+  ttt_config cfg{};
+  DT dt = DT::BF16;
+  size_t es = 2;
+  int L = 0, d = 0, H = 0, Hk = 0, dh = 0, F = 0, Fd = 0, V = 0, k = 0, b = 0, nd = 0, s = 0;
+  int64_t max_seq = 0, cap = 0, slab = 0;
+  int QKV = 0;  // (H + 2 Hk) dh
+  int64_t pos = 0;
+  std::string err;
+  std::vector<void*> allocs;
+
+  // weights
+  void* embed = nullptr;
+  void* lm_head = nullptr;
+  float* final_norm = nullptr;
+  std::vector<float*> attn_norm, mlp_norm, dyn_norm;
+  std::vector<void*> wqkv, wo, w12, w3;       // static, storage dtype
+  std::vector<float*> m12, m3;               // dynamic fp32 masters (interleaved W1|W2)
+  std::vector<void*> dw12, dw3;              // dynamic working copies (== master for f32)
+  std::vector<void*> w0_12, w0_3;            // W0 snapshot (storage dtype, interleaved)
+  std::vector<void*> kring, vring;           // per layer [Hk][cap][dh]
+  float2* rope = nullptr;                    // [max_seq][dh/2] (cos, sin)
+
+  // prefix / shared activations
+  float* hres = nullptr;   // [max_seq, d] residual stream (input of block s's dynamic MLP)
+  float* rbuf = nullptr;   // [slab]
+  void* xn = nullptr;      // [slab, d]
+  void* qkv = nullptr;     // [slab, QKV]
+  void* qb = nullptr;      // [slab, H dh]
+  void* ob = nullptr;      // [slab, H dh]
+  void* hmid = nullptr;    // [slab, max(F, Fd)]
+
+  // loop (per dynamic block i = l - s)
+  float* hl = nullptr;                       // [b, d]
+  std::vector<float*> h_att, h_mlp, h_dyn, r_att, r_mlp, r_dyn, lse;
+  std::vector<void*> q_l, o_l, h12_s, xn_d, h12_d, hm_d;
+  float* h_f = nullptr;
+  float* r_f = nullptr;
+  float* logits = nullptr;                   // [b, V]
+  void* dz = nullptr;                        // [b, V]
+  // backward
+  float* gh = nullptr;                       // [b, d] gradient of the residual stream
+  void* gh_t = nullptr;                      // [b, d]
+  void* dh12 = nullptr;                      // [b, 2 max(F, Fd)]
+  float* part = nullptr;                     // [max_split, b, d]
+  int max_split = 1;
+  void* dO = nullptr;                        // [b, H dh]
+  float* Dbuf = nullptr;                     // [H, b]
+  float* dq = nullptr;                       // [b, H dh]
+  float* dk = nullptr;                       // [b, Hk dh]
+  float* dv = nullptr;
+  void* dqkv = nullptr;                      // [b, QKV]
+  int* d_err = nullptr;
+  int64_t* d_pos = nullptr;
+  float* dec = nullptr;                      // decode scratch
+  int dec_split = 1;
+};
+
+namespace {
+
+ttt_status fail(ttt_ctx* c, ttt_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  return s;
+}
+
+#define HIPCHK(c, call)                                                               \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(c, TTT_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+bool dalloc(ttt_ctx* c, void** p, size_t bytes) {
+  if (bytes == 0) bytes = 16;
+  if (hipMalloc(p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return false;
+  }
+  c->allocs.push_back(*p);
+  return true;
+}
+
+template <typename P>
+bool dalloc_t(ttt_ctx* c, P** p, size_t bytes) {
+  void* v = nullptr;
+  bool ok = dalloc(c, &v, bytes);
+  *p = (P*)v;
+  return ok;
+}
+
+ttt_status validate(const ttt_config* cfg) {
+  if (!cfg) return TTT_ERR_INVALID_ARG;
+  const ttt_config& c = *cfg;
+  if (c.dtype != TTT_F32 && c.dtype != TTT_BF16) return TTT_ERR_INVALID_ARG;
+  if (c.reduction != TTT_LOSS_MEAN && c.reduction != TTT_LOSS_SUM) return TTT_ERR_INVALID_ARG;
+  if (c.n_layers < 1 || c.d_model < 1 || c.n_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 ||
+      c.ffn_hidden < 1 || c.dyn_ffn_hidden < 1 || c.vocab < 2 || c.minibatch < 1 ||
+      c.max_seq < 2 || c.n_dynamic < 0 || c.n_dynamic > c.n_layers)
+    return TTT_ERR_INVALID_ARG;
+  if (c.window < c.minibatch) return TTT_ERR_INVALID_ARG;  // k >= b
+  if (!(c.alpha >= 0.f) || !isfinite(c.alpha) || !(c.rms_eps > 0.f) || !(c.rope_theta > 1.f))
+    return TTT_ERR_INVALID_ARG;
+  if (c.n_heads % c.n_kv_heads) return TTT_ERR_INVALID_ARG;
+  const bool bf = c.dtype == TTT_BF16;
+  if (!(c.head_dim == 16 || c.head_dim == 64 || (bf && c.head_dim == 128))) return TTT_ERR_UNSUPPORTED;
+  if (c.d_model % 16 || c.ffn_hidden % 32 || c.dyn_ffn_hidden % 32 || c.vocab % 8)
+    return TTT_ERR_UNSUPPORTED;
+  if ((int64_t)c.max_seq > (int64_t(1) << 30)) return TTT_ERR_UNSUPPORTED;
+  if ((int64_t)c.vocab * c.d_model > (int64_t(1) << 31)) return TTT_ERR_UNSUPPORTED;
+  return TTT_OK;
+}
+
+ttt_status check_device(ttt_ctx* c) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return fail(c, TTT_ERR_NO_DEVICE, "no HIP device");
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(c, TTT_ERR_NO_DEVICE, "hipGetDevice failed");
+  hipDeviceProp_t pr;
+  if (hipGetDeviceProperties(&pr, dev) != hipSuccess) return fail(c, TTT_ERR_NO_DEVICE, "no properties");
+  if (strncmp(pr.gcnArchName, "gfx950", 6) != 0)
+    return fail(c, TTT_ERR_NO_DEVICE, std::string("device is ") + pr.gcnArchName + ", need gfx950");
+  return TTT_OK;
+}
+
+// Copy src [F, d] into rows of the 16-interleaved fused layout (gate rows at
+// 32 j + w, up rows at 32 j + 16 + w).
+hipError_t interleave(void* dst, const void* src, int F, int d, size_t es, int which, hipStream_t st) {
+  const size_t blk = (size_t)16 * d * es;
+  return hipMemcpy2DAsync((char*)dst + which * blk, 2 * blk, src, blk, blk, F / 16,
+                          hipMemcpyDeviceToDevice, st);
+}
+hipError_t deinterleave(void* dst, const void* src, int F, int d, size_t es, int which, hipStream_t st) {
+  const size_t blk = (size_t)16 * d * es;
+  return hipMemcpy2DAsync(dst, blk, (const char*)src + which * blk, 2 * blk, blk, F / 16,
+                          hipMemcpyDeviceToDevice, st);
+}
+
+int choose_split(int tiles, int K) {
+  // aim for >= 2 workgroups per CU on the 256-CU part
+  int s = (512 + tiles - 1) / tiles;
+  s = std::min(s, std::max(1, K / 256));
+  return std::max(1, std::min(s, 16));
+}
+
+GemmArgs ga(const void* A, long lda, const void* B, long ldb, int M, int N, int K, void* C, long ldc) {
+  GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.C = C;
+  g.ldc = ldc;
+  g.scale = 1.f;
+  g.kchunk = 0;
+  return g;
+}
+
+// C (float partials) = A [M, K] (k-major) * B (k-row-major [K, N]), split-K.
+// Returns the number of partial slices written.
+hipError_t gemm_nn_split(ttt_ctx* c, const void* A, long lda, const void* B, long ldb, int M, int N,
+                         int K, float* part, int* nsplit, hipStream_t st) {
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int s = std::min(choose_split(tiles, K), c->max_split);
+  const int gran = gemm_k_granule(c->dt);
+  int chunk = (K + s - 1) / s;
+  chunk = (chunk + gran - 1) / gran * gran;
+  s = (K + chunk - 1) / chunk;
+  GemmArgs g = ga(A, lda, B, ldb, M, N, K, part, N);
+  g.kchunk = chunk;
+  *nsplit = s;
+  return gemm(c->dt, true, false, Epi::PARTIAL, g, st);
+}
+
+// ------------------------------------------------------------ prefix phase
+ttt_status run_prefix(ttt_ctx* c, const int32_t* tok, int64_t T, hipStream_t st) {
+  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV;
+  const float scale = 1.f / sqrtf((float)dh);
+  for (int64_t p0 = 0; p0 < T; p0 += c->slab) {
+    const int n = (int)std::min<int64_t>(c->slab, T - p0);
+    float* h = c->hres + p0 * d;
+    HIPCHK(c, embed_gather(c->dt, tok + p0, n, c->embed, d, h, c->V, c->d_err, st));
+    for (int l = 0; l <= c->s && l < c->L; ++l) {
+      HIPCHK(c, rmsnorm_fwd(c->dt, h, c->attn_norm[l], n, d, c->cfg.rms_eps, c->xn, c->rbuf, st));
+      HIPCHK(c, gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
+      HIPCHK(c, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, p0, c->rope, c->qb, c->kring[l], c->vring[l],
+                             (int)c->cap, 0, st));
+      AttnArgs a{};
+      a.q = c->qb;
+      a.k = c->kring[l];
+      a.v = c->vring[l];
+      a.o = c->ob;
+      a.lse = nullptr;
+      a.n = n;
+      a.H = H;
+      a.Hk = Hk;
+      a.dh = dh;
+      a.cap = (int)c->cap;
+      a.window = c->k;
+      a.pos0 = p0;
+      a.scale = scale;
+      HIPCHK(c, attn_fwd(c->dt, a, st));
+      HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->ob, (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, h, d), st));
+      HIPCHK(c, rmsnorm_fwd(c->dt, h, c->mlp_norm[l], n, d, c->cfg.rms_eps, c->xn, c->rbuf, st));
+      GemmArgs g = ga(c->xn, d, c->w12[l], d, n, 2 * c->F, d, nullptr, 2 * c->F);
+      g.C2 = c->hmid;
+      HIPCHK(c, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
+      HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->hmid, c->F, c->w3[l], c->F, n, d, c->F, h, d), st));
+      (void)0;
+    }
+  }
+  return TTT_OK;
+}
+
+// ------------------------------------------------------------ loop phase
+ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipStream_t st) {
+  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s;
+  const float eps = c->cfg.rms_eps;
+  const float scale = 1.f / sqrtf((float)dh);
+  float* hl = c->hl;
+  HIPCHK(c, copy_f32(c->hres + a0 * d, hl, (size_t)n * d, st));
+  for (int l = s; l < c->L; ++l) {
+    const int i = l - s;
+    if (l > s) {
+      // attention
+      HIPCHK(c, copy_f32(hl, c->h_att[i], (size_t)n * d, st));
+      HIPCHK(c, rmsnorm_fwd(c->dt, hl, c->attn_norm[l], n, d, eps, c->xn, c->r_att[i], st));
+      HIPCHK(c, gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
+      HIPCHK(c, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, a0, c->rope, c->q_l[i], c->kring[l], c->vring[l],
+                             (int)c->cap, 0, st));
+      AttnArgs a{};
+      a.q = c->q_l[i];
+      a.k = c->kring[l];
+      a.v = c->vring[l];
+      a.o = c->o_l[i];
+      a.lse = c->lse[i];
+      a.n = n;
+      a.H = H;
+      a.Hk = Hk;
+      a.dh = dh;
+      a.cap = (int)c->cap;
+      a.window = c->k;
+      a.pos0 = a0;
+      a.scale = scale;
+      HIPCHK(c, attn_fwd(c->dt, a, st));
+      HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, hl, d), st));
+      // static MLP
+      HIPCHK(c, copy_f32(hl, c->h_mlp[i], (size_t)n * d, st));
+      HIPCHK(c, rmsnorm_fwd(c->dt, hl, c->mlp_norm[l], n, d, eps, c->xn, c->r_mlp[i], st));
+      GemmArgs g = ga(c->xn, d, c->w12[l], d, n, 2 * c->F, d, c->h12_s[i], 2 * c->F);
+      g.C2 = c->hmid;
+      HIPCHK(c, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
+      HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->hmid, c->F, c->w3[l], c->F, n, d, c->F, hl, d), st));
+    }
+    // dynamic MLP
+    HIPCHK(c, copy_f32(hl, c->h_dyn[i], (size_t)n * d, st));
+    HIPCHK(c, rmsnorm_fwd(c->dt, hl, c->dyn_norm[i], n, d, eps, c->xn_d[i], c->r_dyn[i], st));
+    GemmArgs g = ga(c->xn_d[i], d, c->dw12[i], d, n, 2 * c->Fd, d, c->h12_d[i], 2 * c->Fd);
+    g.C2 = c->hm_d[i];
+    HIPCHK(c, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
+    HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->hm_d[i], c->Fd, c->dw3[i], c->Fd, n, d, c->Fd, hl, d), st));
+  }
+  HIPCHK(c, copy_f32(hl, c->h_f, (size_t)n * d, st));
+  HIPCHK(c, rmsnorm_fwd(c->dt, hl, c->final_norm, n, d, eps, c->xn, c->r_f, st));
+  HIPCHK(c, gemm(c->dt, true, true, Epi::STORE_F32, ga(c->xn, d, c->lm_head, d, n, c->V, d, c->logits, c->V), st));
+  return TTT_OK;
+}
+
+ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
+  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s;
+  const float scale = 1.f / sqrtf((float)dh);
+  const float lr = c->cfg.alpha;
+  int ns = 1;
+  // lm_head^T and final norm
+  HIPCHK(c, gemm_nn_split(c, c->dz, c->V, c->lm_head, d, n, d, c->V, c->part, &ns, st));
+  HIPCHK(c, rmsnorm_bwd(c->dt, c->part, ns, c->h_f, c->final_norm, c->r_f, n, d, c->gh, c->gh_t, 0, st));
+  for (int l = c->L - 1; l >= s; --l) {
+    const int i = l - s;
+    // dynamic MLP: dHmid = dY W3 with the SwiGLU backward in the epilogue
+    {
+      GemmArgs g = ga(c->gh_t, d, c->dw3[i], c->Fd, n, c->Fd, d, c->dh12, 2 * c->Fd);
+      g.X = c->h12_d[i];
+      HIPCHK(c, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
+    }
+    if (l > s)
+      HIPCHK(c, gemm_nn_split(c, c->dh12, 2 * c->Fd, c->dw12[i], d, n, d, 2 * c->Fd, c->part, &ns, st));
+    // dW3 = dY^T Hmid and dW12 = dH12^T U, with W -= alpha dW in the epilogue
+    {
+      GemmArgs g = ga(c->gh_t, d, c->hm_d[i], c->Fd, d, c->Fd, n, c->m3[i], c->Fd);
+      g.C2 = c->dw3[i];
+      g.scale = lr;
+      HIPCHK(c, gemm(c->dt, false, false, Epi::SGD, g, st));
+      GemmArgs g2 = ga(c->dh12, 2 * c->Fd, c->xn_d[i], d, 2 * c->Fd, d, n, c->m12[i], d);
+      g2.C2 = c->dw12[i];
+      g2.scale = lr;
+      HIPCHK(c, gemm(c->dt, false, false, Epi::SGD, g2, st));
+    }
+    if (l == s) break;
+    HIPCHK(c, rmsnorm_bwd(c->dt, c->part, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], n, d, c->gh, c->gh_t, 1, st));
+    // static MLP
+    {
+      GemmArgs g = ga(c->gh_t, d, c->w3[l], c->F, n, c->F, d, c->dh12, 2 * c->F);
+      g.X = c->h12_s[i];
+      HIPCHK(c, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
+      HIPCHK(c, gemm_nn_split(c, c->dh12, 2 * c->F, c->w12[l], d, n, d, 2 * c->F, c->part, &ns, st));
+      HIPCHK(c, rmsnorm_bwd(c->dt, c->part, ns, c->h_mlp[i], c->mlp_norm[l], c->r_mlp[i], n, d, c->gh, c->gh_t, 1, st));
+    }
+    // attention
+    {
+      HIPCHK(c, gemm(c->dt, true, false, Epi::STORE, ga(c->gh_t, d, c->wo[l], (long)H * dh, n, H * dh, d, c->dO, (long)H * dh), st));
+      HIPCHK(c, attn_rowdot(c->dt, c->dO, c->o_l[i], n, H, dh, c->Dbuf, st));
+      AttnArgs a{};
+      a.q = c->q_l[i];
+      a.k = c->kring[l];
+      a.v = c->vring[l];
+      a.o = c->o_l[i];
+      a.lse = c->lse[i];
+      a.n = n;
+      a.H = H;
+      a.Hk = Hk;
+      a.dh = dh;
+      a.cap = (int)c->cap;
+      a.window = c->k;
+      a.pos0 = a0;
+      a.scale = scale;
+      a.dO = c->dO;
+      a.D = c->Dbuf;
+      a.dq = c->dq;
+      a.dk = c->dk;
+      a.dv = c->dv;
+      HIPCHK(c, attn_bwd_dq(c->dt, a, st));
+      HIPCHK(c, attn_bwd_dkdv(c->dt, a, st));
+      HIPCHK(c, rope_bwd_pack(c->dt, c->dq, c->dk, c->dv, n, H, Hk, dh, a0, c->rope, c->dqkv, st));
+      HIPCHK(c, gemm_nn_split(c, c->dqkv, QKV, c->wqkv[l], d, n, d, QKV, c->part, &ns, st));
+      HIPCHK(c, rmsnorm_bwd(c->dt, c->part, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->gh_t, 1, st));
+    }
+  }
+  return TTT_OK;
+}
+
+}  // namespace
+
+// ==================================================================== C ABI
+extern "C" {
+
+ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, ttt_ctx** out) {
+  if (!out) return TTT_ERR_INVALID_ARG;
+  *out = nullptr;
+  ttt_status vs = validate(cfg);
+  if (vs != TTT_OK) return vs;
+  if (!w || !w->embed || !w->lm_head || !w->final_norm || !w->attn_norm || !w->wq || !w->wk || !w->wv ||
+      !w->wo || !w->mlp_norm || !w->w1 || !w->w2 || !w->w3)
+    return TTT_ERR_INVALID_ARG;
+  const int nd0 = cfg->n_dynamic ? cfg->n_dynamic : cfg->n_layers - (3 * cfg->n_layers) / 4;
+  if (nd0 > 0 && (!w->dyn_norm || !w->dyn_w1 || !w->dyn_w2 || !w->dyn_w3)) return TTT_ERR_INVALID_ARG;
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->mlp_norm[l] ||
+        !w->w1[l] || !w->w2[l] || !w->w3[l])
+      return TTT_ERR_INVALID_ARG;
+  for (int i = 0; i < nd0; ++i)
+    if (!w->dyn_norm[i] || !w->dyn_w1[i] || !w->dyn_w2[i] || !w->dyn_w3[i]) return TTT_ERR_INVALID_ARG;
+
+  ttt_ctx* c = new ttt_ctx();
+  ttt_status ds = check_device(c);
+  if (ds != TTT_OK) {
+    delete c;
+    return ds;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  c->cfg = *cfg;
+  c->dt = cfg->dtype == TTT_BF16 ? DT::BF16 : DT::F32;
+  c->es = dt_size(c->dt);
+  c->L = cfg->n_layers;
+  c->d = cfg->d_model;
+  c->H = cfg->n_heads;
+  c->Hk = cfg->n_kv_heads;
+  c->dh = cfg->head_dim;
+  c->F = cfg->ffn_hidden;
+  c->Fd = cfg->dyn_ffn_hidden;
+  c->V = cfg->vocab;
+  c->k = cfg->window;
+  c->b = cfg->minibatch;
+  c->nd = nd0;
+  c->s = c->L - c->nd;
+  c->max_seq = cfg->max_seq;
+  c->QKV = (c->H + 2 * c->Hk) * c->dh;
+  c->slab = std::min<int64_t>(c->max_seq, 16384);
+  c->slab = std::max<int64_t>(c->slab, c->b);
+  c->cap = next_pow2(std::max<int64_t>((int64_t)c->k + std::max<int64_t>(c->b, c->slab), 128));
+  c->max_split = 16;
+  const size_t es = c->es;
+  const int d = c->d, L = c->L, nd = c->nd, b = c->b;
+  const int64_t S = c->slab;
+  const int Fm = std::max(c->F, c->Fd);
+
+  bool ok = true;
+  auto A = [&](void** p, size_t bytes) { ok = ok && dalloc(c, p, bytes); };
+  auto Af = [&](float** p, size_t n) { ok = ok && dalloc_t(c, p, n * 4); };
+
+  A(&c->embed, (size_t)c->V * d * es);
+  if (w->lm_head == w->embed) c->lm_head = c->embed;
+  else A(&c->lm_head, (size_t)c->V * d * es);
+  Af(&c->final_norm, d);
+  c->attn_norm.resize(L);
+  c->mlp_norm.resize(L);
+  c->wqkv.resize(L);
+  c->wo.resize(L);
+  c->w12.resize(L);
+  c->w3.resize(L);
+  c->kring.resize(L);
+  c->vring.resize(L);
+  for (int l = 0; l < L && ok; ++l) {
+    Af(&c->attn_norm[l], d);
+    Af(&c->mlp_norm[l], d);
+    A(&c->wqkv[l], (size_t)c->QKV * d * es);
+    A(&c->wo[l], (size_t)d * c->H * c->dh * es);
+    A(&c->w12[l], (size_t)2 * c->F * d * es);
+    A(&c->w3[l], (size_t)d * c->F * es);
+    A(&c->kring[l], (size_t)c->Hk * c->cap * c->dh * es);
+    A(&c->vring[l], (size_t)c->Hk * c->cap * c->dh * es);
+  }
+  c->dyn_norm.resize(nd);
+  c->m12.resize(nd);
+  c->m3.resize(nd);
+  c->dw12.resize(nd);
+  c->dw3.resize(nd);
+  c->w0_12.resize(nd);
+  c->w0_3.resize(nd);
+  for (int i = 0; i < nd && ok; ++i) {
+    Af(&c->dyn_norm[i], d);
+    Af(&c->m12[i], (size_t)2 * c->Fd * d);
+    Af(&c->m3[i], (size_t)d * c->Fd);
+    if (c->dt == DT::F32) {
+      c->dw12[i] = c->m12[i];
+      c->dw3[i] = c->m3[i];
+    } else {
+      A(&c->dw12[i], (size_t)2 * c->Fd * d * es);
+      A(&c->dw3[i], (size_t)d * c->Fd * es);
+    }
+    A(&c->w0_12[i], (size_t)2 * c->Fd * d * es);
+    A(&c->w0_3[i], (size_t)d * c->Fd * es);
+  }
+  {
+    void* p = nullptr;
+    A(&p, (size_t)c->max_seq * (c->dh / 2) * sizeof(float2));
+    c->rope = (float2*)p;
+  }
+  Af(&c->hres, (size_t)c->max_seq * d);
+  Af(&c->rbuf, (size_t)S);
+  A(&c->xn, (size_t)S * d * es);
+  A(&c->qkv, (size_t)S * c->QKV * es);
+  A(&c->qb, (size_t)S * c->H * c->dh * es);
+  A(&c->ob, (size_t)S * c->H * c->dh * es);
+  A(&c->hmid, (size_t)S * Fm * es);
+  Af(&c->hl, (size_t)b * d);
+  c->h_att.resize(nd);
+  c->h_mlp.resize(nd);
+  c->h_dyn.resize(nd);
+  c->r_att.resize(nd);
+  c->r_mlp.resize(nd);
+  c->r_dyn.resize(nd);
+  c->lse.resize(nd);
+  c->q_l.resize(nd);
+  c->o_l.resize(nd);
+  c->h12_s.resize(nd);
+  c->xn_d.resize(nd);
+  c->h12_d.resize(nd);
+  c->hm_d.resize(nd);
+  for (int i = 0; i < nd && ok; ++i) {
+    Af(&c->h_att[i], (size_t)b * d);
+    Af(&c->h_mlp[i], (size_t)b * d);
+    Af(&c->h_dyn[i], (size_t)b * d);
+    Af(&c->r_att[i], b);
+    Af(&c->r_mlp[i], b);
+    Af(&c->r_dyn[i], b);
+    Af(&c->lse[i], (size_t)c->H * b);
+    A(&c->q_l[i], (size_t)b * c->H * c->dh * es);
+    A(&c->o_l[i], (size_t)b * c->H * c->dh * es);
+    A(&c->h12_s[i], (size_t)b * 2 * c->F * es);
+    A(&c->xn_d[i], (size_t)b * d * es);
+    A(&c->h12_d[i], (size_t)b * 2 * c->Fd * es);
+    A(&c->hm_d[i], (size_t)b * c->Fd * es);
+  }
+  Af(&c->h_f, (size_t)b * d);
+  Af(&c->r_f, b);
+  Af(&c->logits, (size_t)b * c->V);
+  A(&c->dz, (size_t)b * c->V * es);
+  Af(&c->gh, (size_t)b * d);
+  A(&c->gh_t, (size_t)b * d * es);
+  A(&c->dh12, (size_t)b * 2 * Fm * es);
+  Af(&c->part, (size_t)c->max_split * b * d);
+  A(&c->dO, (size_t)b * c->H * c->dh * es);
+  Af(&c->Dbuf, (size_t)c->H * b);
+  Af(&c->dq, (size_t)b * c->H * c->dh);
+  Af(&c->dk, (size_t)b * c->Hk * c->dh);
+  Af(&c->dv, (size_t)b * c->Hk * c->dh);
+  A(&c->dqkv, (size_t)b * c->QKV * es);
+  {
+    void* p = nullptr;
+    A(&p, 64);
+    c->d_err = (int*)p;
+    A(&p, 64);
+    c->d_pos = (int64_t*)p;
+  }
+  c->dec_split = 32;
+  Af(&c->dec, (size_t)4 * (c->QKV + 2 * Fm + 2 * d + c->H * c->dh) +
+                  (size_t)c->H * c->dec_split * (c->dh + 2));
+  if (!ok) {
+    ttt_destroy(c);
+    return TTT_ERR_OOM;
+  }
+
+  // ---- upload / repack
+  auto fin = [&](ttt_status s) {
+    if (s != TTT_OK) {
+      ttt_destroy(c);
+      return s;
+    }
+    *out = c;
+    return TTT_OK;
+  };
+#define UP(call)                                            \
+  do {                                                      \
+    if ((call) != hipSuccess) {                             \
+      (void)hipGetLastError();                              \
+      return fin(TTT_ERR_HIP);                              \
+    }                                                       \
+  } while (0)
+  const hipMemcpyKind D2D = hipMemcpyDeviceToDevice;
+  UP(hipMemcpyAsync(c->embed, w->embed, (size_t)c->V * d * es, D2D, st));
+  if (c->lm_head != c->embed) UP(hipMemcpyAsync(c->lm_head, w->lm_head, (size_t)c->V * d * es, D2D, st));
+  UP(cast_from(c->dt, w->final_norm, c->final_norm, d, st));
+  const size_t qsz = (size_t)c->H * c->dh * d * es, ksz = (size_t)c->Hk * c->dh * d * es;
+  for (int l = 0; l < L; ++l) {
+    UP(cast_from(c->dt, w->attn_norm[l], c->attn_norm[l], d, st));
+    UP(cast_from(c->dt, w->mlp_norm[l], c->mlp_norm[l], d, st));
+    UP(hipMemcpyAsync(c->wqkv[l], w->wq[l], qsz, D2D, st));
+    UP(hipMemcpyAsync((char*)c->wqkv[l] + qsz, w->wk[l], ksz, D2D, st));
+    UP(hipMemcpyAsync((char*)c->wqkv[l] + qsz + ksz, w->wv[l], ksz, D2D, st));
+    UP(hipMemcpyAsync(c->wo[l], w->wo[l], (size_t)d * c->H * c->dh * es, D2D, st));
+    UP(interleave(c->w12[l], w->w1[l], c->F, d, es, 0, st));
+    UP(interleave(c->w12[l], w->w2[l], c->F, d, es, 1, st));
+    UP(hipMemcpyAsync(c->w3[l], w->w3[l], (size_t)d * c->F * es, D2D, st));
+    UP(fill_zero_bytes(c->kring[l], (size_t)c->Hk * c->cap * c->dh * es, st));
+    UP(fill_zero_bytes(c->vring[l], (size_t)c->Hk * c->cap * c->dh * es, st));
+  }
+  for (int i = 0; i < nd; ++i) {
+    UP(cast_from(c->dt, w->dyn_norm[i], c->dyn_norm[i], d, st));
+    UP(interleave(c->w0_12[i], w->dyn_w1[i], c->Fd, d, es, 0, st));
+    UP(interleave(c->w0_12[i], w->dyn_w2[i], c->Fd, d, es, 1, st));
+    UP(hipMemcpyAsync(c->w0_3[i], w->dyn_w3[i], (size_t)d * c->Fd * es, D2D, st));
+  }
+  // RoPE table: angle = pos * theta^(-2j/dh) in float64, stored as fp32 (cos, sin).
+  {
+    const int half = c->dh / 2;
+    std::vector<float2> tab((size_t)c->max_seq * half);
+    std::vector<double> inv(half);
+    for (int j = 0; j < half; ++j) inv[j] = 1.0 / pow((double)c->cfg.rope_theta, 2.0 * j / c->dh);
+    for (int64_t p = 0; p < c->max_seq; ++p)
+      for (int j = 0; j < half; ++j) {
+        const double ang = (double)p * inv[j];
+        tab[(size_t)p * half + j] = make_float2((float)cos(ang), (float)sin(ang));
+      }
+    UP(hipMemcpyAsync(c->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice, st));
+    UP(hipStreamSynchronize(st));
+  }
+  UP(fill_i32(c->d_err, 0, 16, st));
+  UP(hipStreamSynchronize(st));
+  ttt_status rs = ttt_reset(c, stream);
+  if (rs != TTT_OK) return fin(rs);
+  UP(hipStreamSynchronize(st));
+#undef UP
+  return fin(TTT_OK);
+}
+
+ttt_status ttt_reset(ttt_ctx* c, void* stream) {
+  if (!c) return TTT_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t es = c->es;
+  for (int i = 0; i < c->nd; ++i) {
+    const size_t n12 = (size_t)2 * c->Fd * c->d, n3 = (size_t)c->d * c->Fd;
+    HIPCHK(c, cast_from(c->dt, c->w0_12[i], c->m12[i], n12, st));
+    HIPCHK(c, cast_from(c->dt, c->w0_3[i], c->m3[i], n3, st));
+    if (c->dt != DT::F32) {
+      HIPCHK(c, hipMemcpyAsync(c->dw12[i], c->w0_12[i], n12 * es, hipMemcpyDeviceToDevice, st));
+      HIPCHK(c, hipMemcpyAsync(c->dw3[i], c->w0_3[i], n3 * es, hipMemcpyDeviceToDevice, st));
+    }
+  }
+  c->pos = 0;
+  return TTT_OK;
+}
+
+ttt_status ttt_prefill(ttt_ctx* c, const int32_t* tok, int64_t T, float* loss, float* last_logits,
+                       void* stream) {
+  if (!c) return TTT_ERR_INVALID_ARG;
+  if (!tok || !loss) return fail(c, TTT_ERR_INVALID_ARG, "null tokens or loss");
+  if (T < 2 || T > c->max_seq) return fail(c, TTT_ERR_INVALID_ARG, "T outside [2, max_seq]");
+  if (c->pos != 0) return fail(c, TTT_ERR_STATE, "prefill needs position 0 (call ttt_reset)");
+  hipStream_t st = (hipStream_t)stream;
+  ttt_status r = run_prefix(c, tok, T, st);
+  if (r != TTT_OK) return r;
+  const float red_sum = c->cfg.reduction == TTT_LOSS_SUM;
+  for (int64_t a0 = 0; a0 < T; a0 += c->b) {
+    const int n = (int)std::min<int64_t>(c->b, T - a0);
+    r = loop_forward(c, tok, a0, n, st);
+    if (r != TTT_OK) return r;
+    if (a0 + n == T && last_logits)
+      HIPCHK(c, hipMemcpyAsync(last_logits, c->logits + (size_t)(n - 1) * c->V, (size_t)c->V * 4,
+                               hipMemcpyDeviceToDevice, st));
+    const int nt = (int)(std::min<int64_t>(a0 + n, T - 1) - a0);
+    if (nt <= 0) continue;
+    const float scale = red_sum ? 1.f : 1.f / nt;
+    HIPCHK(c, ce_fwd_bwd(c->dt, c->logits, n, nt, c->V, tok + a0 + 1, scale, loss + a0, c->dz, c->d_err, st));
+    r = loop_backward(c, a0, n, st);
+    if (r != TTT_OK) return r;
+  }
+  c->pos = T;
+  return TTT_OK;
+}
+
+ttt_status ttt_decode_step(ttt_ctx* c, const int32_t* token, float* logits, void* stream) {
+  if (!c) return TTT_ERR_INVALID_ARG;
+  (void)token;
+  (void)logits;
+  (void)stream;
+  return fail(c, TTT_ERR_UNSUPPORTED, "decode not built yet");
+}
+
+ttt_status ttt_get_fast_weights(ttt_ctx* c, int32_t i, float* w1, float* w2, float* w3, void* stream) {
+  if (!c) return TTT_ERR_INVALID_ARG;
+  if (i < 0 || i >= c->nd || !w1 || !w2 || !w3) return fail(c, TTT_ERR_INVALID_ARG, "bad dyn index or null");
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(c, deinterleave(w1, c->m12[i], c->Fd, c->d, 4, 0, st));
+  HIPCHK(c, deinterleave(w2, c->m12[i], c->Fd, c->d, 4, 1, st));
+  HIPCHK(c, hipMemcpyAsync(w3, c->m3[i], (size_t)c->d * c->Fd * 4, hipMemcpyDeviceToDevice, st));
+  return TTT_OK;
+}
+
+ttt_status ttt_sync(ttt_ctx* c, void* stream) {
+  if (!c) return TTT_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(c, hipStreamSynchronize(st));
+  int flags = 0;
+  HIPCHK(c, hipMemcpy(&flags, c->d_err, sizeof(int), hipMemcpyDeviceToHost));
+  if (flags) {
+    HIPCHK(c, fill_i32(c->d_err, 0, 1, st));
+    HIPCHK(c, hipStreamSynchronize(st));
+    if (flags & 1) return fail(c, TTT_ERR_TOKEN_RANGE, "token id outside [0, vocab)");
+    if (flags & 4) return fail(c, TTT_ERR_NONFINITE, "non-finite loss");
+  }
+  return TTT_OK;
+}
+
+int64_t ttt_position(const ttt_ctx* c) { return c ? c->pos : -1; }
+
+const char* ttt_last_error(const ttt_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+void ttt_destroy(ttt_ctx* c) {
+  if (!c) return;
+  (void)hipDeviceSynchronize();
+  for (void* p : c->allocs) (void)hipFree(p);
+  delete c;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Internal launchers of the TTT-E2E gfx950 kernels (host-callable).
+// Every launcher enqueues on the given stream and returns hipSuccess or the
+// launch error; shape requirements are validated by the engine before the
+// first launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+enum class DT : int { F32 = 0, BF16 = 1 };
+inline size_t dt_size(DT t) { return t == DT::F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------- GEMM family
+// C[m, n] = sum_k A(m, k) B(n, k).
+//   A(m, k) = A[m * lda + k] if a_kmajor else A[k * lda + m]
+//   B(n, k) = B[n * ldb + k] if b_kmajor else B[k * ldb + n]
+// The contiguous dimension of each operand must be a multiple of 8 elements
+// and its base 16-byte aligned; other dimensions are arbitrary (zero-filled).
+enum class Epi : int {
+  STORE = 0,    // C (storage type) = scale * acc
+  STORE_F32,    // C (float) = acc
+  ADD_F32,      // C (float) += acc            (residual stream)
+  SWIGLU,       // columns interleaved by 16 (gate | up): C2 (T)[m, j] = silu(a) c,
+                // optional C (T) = the pre-activations themselves
+  SWIGLU_BWD,   // acc = dHmid[m, j]; X = pre-activations (ld = 2N):
+                // C (T) [m, gate/up col] = (dA, dC)
+  SGD,          // C (float master) -= scale * acc; C2 (T) = round(master)
+  PARTIAL,      // C (float) [split][M][ldc] = acc  (split-K)
+};
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  int M, N, K;
+  long lda, ldb;
+  void* C;
+  long ldc;
+  void* C2;
+  const void* X;
+  float scale;
+  int kchunk;  // split-K chunk (multiple of the K tile); <= 0 means no split
+};
+
+hipError_t gemm(DT dt, bool a_kmajor, bool b_kmajor, Epi epi, const GemmArgs& g, hipStream_t st);
+// Tile K granule that split-K chunks must be a multiple of.
+int gemm_k_granule(DT dt);
+
+// -------------------------------------------------------- elementwise / norm
+// h[t, :] = embed[tok[t], :] (as float); bad ids set *err |= 1 and give zeros.
+hipError_t embed_gather(DT dt, const int32_t* tok, int n, const void* embed, int d, float* h,
+                        int V, int* err, hipStream_t st);
+// y (T) = g * x * r, r = rsqrt(mean(x^2) + eps); x float [n, d]; r float [n].
+hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, float eps, void* y,
+                       float* r, hipStream_t st);
+// dh[t] += rmsnorm_bwd(dy[t]) where dy = sum over nsplit partials of
+// [n, d] float (stride n*d); writes dh (float) and dh_t (T copy).
+hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const float* g,
+                       const float* r, int n, int d, float* dh, void* dh_t, int accumulate,
+                       hipStream_t st);
+// Apply RoPE to q and k of a fused qkv buffer [n, (H + 2Hk) dh] (T) at
+// positions pos0 + t; write q (T) [n, H dh]; write k, v into the key/value
+// store [Hk][cap][dh] at slot (pos & (cap - 1)) for rows whose position is
+// >= min_store_pos; optionally also into a full-length buffer.
+hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, int64_t pos0,
+                        const float2* rope_tab, void* q, void* kstore, void* vstore, int cap,
+                        int64_t min_store_pos, hipStream_t st);
+// dQKV (T) [n, (H+2Hk) dh] from dq [n, H dh] (float), dk, dv [n, Hk dh]
+// (float): inverse rotation of dq and dk.
+hipError_t rope_bwd_pack(DT dt, const float* dq, const float* dk, const float* dv, int n, int H,
+                         int Hk, int dh, int64_t pos0, const float2* rope_tab, void* dqkv,
+                         hipStream_t st);
+// Fused softmax cross-entropy over the vocabulary for rows with a target
+// (rows < nt): loss[t] = lse - z[t, label]; dz (T) = (softmax - onehot) * scale;
+// rows >= nt get dz = 0. Also flags non-finite losses in *err (bit 2).
+hipError_t ce_fwd_bwd(DT dt, const float* logits, int n, int nt, int V, const int32_t* labels,
+                      float scale, float* loss, void* dz, int* err, hipStream_t st);
+// D[h][t] = sum_j dO[t, h, j] O[t, h, j].
+hipError_t attn_rowdot(DT dt, const void* dO, const void* O, int n, int H, int dh, float* D,
+                       hipStream_t st);
+hipError_t copy_f32(const float* src, float* dst, size_t n, hipStream_t st);
+hipError_t cast_to(DT dt, const float* src, void* dst, size_t n, hipStream_t st);
+hipError_t cast_from(DT dt, const void* src, float* dst, size_t n, hipStream_t st);
+hipError_t fill_i32(int* p, int v, size_t n, hipStream_t st);
+hipError_t fill_f32(float* p, float v, size_t n, hipStream_t st);
+hipError_t fill_zero_bytes(void* p, size_t nbytes, hipStream_t st);
+
+// ------------------------------------------------------------------- attention
+struct AttnArgs {
+  const void* q;      // [n, H, dh] (T) queries at positions pos0 + i
+  const void* k;      // key store [Hk][cap][dh] (T)
+  const void* v;      // value store [Hk][cap][dh] (T)
+  void* o;            // [n, H, dh] (T)
+  float* lse;         // [H][n] (may be null)
+  int n, H, Hk, dh, cap, window;
+  int64_t pos0;
+  float scale;
+  // backward only
+  const void* dO;     // [n, H, dh] (T)
+  const float* D;     // [H][n]
+  float* dq;          // [n, H, dh] float
+  float* dk;          // [n, Hk, dh] float, keys of this call's own positions
+  float* dv;
+};
+hipError_t attn_fwd(DT dt, const AttnArgs& a, hipStream_t st);
+hipError_t attn_bwd_dq(DT dt, const AttnArgs& a, hipStream_t st);
+hipError_t attn_bwd_dkdv(DT dt, const AttnArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- decode
+// y[n] = sum_k x[k] W[n, k] for one row (T weights, float x), with epilogues.
+enum class GvEpi : int { STORE = 0, ADD_F32, SWIGLU };
+hipError_t gemv(DT dt, const void* W, const float* x, int N, int K, GvEpi epi, float* y,
+                hipStream_t st);
+// rmsnorm of one row into float.
+hipError_t rmsnorm_row(const float* x, const float* g, int d, float eps, float* y, hipStream_t st);
+// rope + store for one position read from a device counter.
+hipError_t decode_rope_store(DT dt, const float* qkv, int H, int Hk, int dh, const int64_t* pos,
+                             const float2* rope_tab, float* q, void* kstore, void* vstore, int cap,
+                             hipStream_t st);
+hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vstore, int H, int Hk,
+                       int dh, int cap, int window, const int64_t* pos, float* part, float* o,
+                       int nsplit, hipStream_t st);
+hipError_t embed_row(DT dt, const int32_t* tok, const void* embed, int d, int V, float* h,
+                     int* err, hipStream_t st);
+hipError_t bump_pos(int64_t* pos, hipStream_t st);
+
+// ---------------------------------------------------------------- E2-TTT
+// Per (head, chunk) scalars: KW_t = eta_t A_t, KM_t = eta_t beta~_t and the
+// chunk coefficients (gamma~_0, beta_1 A_1, beta~_0).
+hipError_t e2_scalars(const float* eta, const float* beta, const float* gamma, int H, int64_t T,
+                      int C, float* KW, float* KM, float* coef, hipStream_t st);
+
+}  // namespace ttt
