@@ -1,0 +1,176 @@
+#!/usr/bin/env python3
+"""Throughput of the TTT-E2E inner loop (prefill) on one MI355X.
+
+Workload (default): the 3B-shape model -- 28 blocks, d = 3072, 24 query / 8 KV
+heads of 128, SwiGLU 8192, vocab 128256, window 8192, the last 7 blocks
+updated with a dynamic SwiGLU MLP -- over a 131072-token (128K) seeded
+Zipf(1.1) stream, mini-batch b = 1024, alpha = 0.005, bf16 storage with fp32
+accumulation and an fp32 fast-weight master. One step = one ttt_prefill
+over the whole stream (hoisted prefix + 128 mini-batches of forward, CE,
+backward and SGD update) after ttt_reset; inputs are resident in HBM.
+
+Prints one JSON line: tokens/s, the fraction of the bf16 MFMA peak reached by
+the whole step (algorithmic FLOPs / time / 2.5 PFLOP/s), the live roofline of
+the dominant kernel class (HIP events around its launches during the timed
+steps), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TTT prefill tokens/s @128K ctx 3B-shape, 1 MI355X; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_flops(c: dict, T: int) -> float:
+    """Matrix-product FLOPs of one prefill (recompute not counted; the causal
+    window counted exactly)."""
+    L, d, H, Hk, dh = c["n_layers"], c["d_model"], c["n_heads"], c["n_kv_heads"], c["head_dim"]
+    F, Fd, V, k, b = c["ffn_hidden"], c["dyn_ffn_hidden"], c["vocab"], c["window"], c["minibatch"]
+    Ld = c["n_dynamic"] or L - (3 * L) // 4
+    Pa = d * H * dh + 2 * d * Hk * dh + H * dh * d
+    Pm, Pmd = 3 * d * F, 3 * d * Fd
+    kk = min(k, T)
+    Wsum = kk * (kk + 1) / 2 + (T - kk) * k
+    Ib = sum(min(b, T - a) * (min(b, T - a) + 1) / 2 for a in range(0, T, b))
+    fwd = 2 * (L * (Pa + Pm) + Ld * Pmd + d * V) * T + L * 4 * H * dh * Wsum
+    bwd = (2 * d * V + (Ld - 1) * (4 * Pmd + 2 * Pm + 2 * Pa) + 2 * Pmd + 2 * d * Fd) * T
+    bwd += (Ld - 1) * (4 * H * dh * Wsum + 4 * H * dh * Ib)
+    return float(fwd + bwd)
+
+
+def cpu_baseline(c, w, tok, ntok):
+    """The oracle (float32 numpy) on the first mini-batch of the same stream."""
+    import numpy as np
+    import torch
+    from oracle import ttt_e2e as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([x.get("num_threads", 0) for x in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    wn = {"embed": w["embed"].float().cpu().numpy(), "final_norm": w["final_norm"].float().cpu().numpy()}
+    wn["lm_head"] = wn["embed"]
+    wn["layers"] = [{k: v.float().cpu().numpy() for k, v in x.items()} for x in w["layers"]]
+    wn["dyn"] = [{k: v.float().cpu().numpy() for k, v in x.items()} for x in w["dyn"]]
+    t = tok[: ntok + 1].cpu().numpy()
+    t0 = time.perf_counter()
+    out = O.ttt_inner_loop(c, wn, t, dtype=np.float32)
+    dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(out["loss"]))
+    return dict(value=round(ntok / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"mini-batch 0 of the same stream: {ntok} positions forward + 1 SGD step, "
+                       f"plus the forward-only position {ntok}; {dt:.1f} s on the host",
+                seconds=round(dt, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="3b", help="synth workload name (3b, 1b, 125m)")
+    ap.add_argument("--seq", type=int, default=None, help="override the stream length")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="print the per-class timing table")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the inner loop on one GPU only; --gpus N > 1 is not "
+              "supported (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import test_long_context_amd as tla
+
+    c = synth.config(args.workload)
+    T = args.seq or c["seq"]
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    w = synth.gen_weights(c, device="cuda")
+    tok = synth.gen_tokens(c, n=T, device="cuda")
+    m = tla.TTT(c, w, max_seq=T + 1024)
+    loss = torch.empty(T - 1, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+    print(f"# setup {t_setup:.1f} s (weights generated on the GPU, context built)", file=sys.stderr, flush=True)
+
+    # warm-up; the last warm-up step records every kernel class
+    for i in range(max(1, args.warmup)):
+        if i == max(1, args.warmup) - 1:
+            m.timing_enable((1 << 9) - 1)
+        m.reset()
+        m.prefill(tok, loss)
+        m.sync()
+        print(f"# warm-up step {i} done", file=sys.stderr, flush=True)
+    classes = [m.timing_read(k) for k in range(9)]
+    dom = max(range(9), key=lambda k: classes[k]["ms"])
+    if args.breakdown:
+        tot = sum(x["ms"] for x in classes)
+        for x in classes:
+            eff = x["flops"] / (x["ms"] * 1e9) if x["ms"] > 0 and x["flops"] else 0.0
+            bw = x["bytes"] / (x["ms"] * 1e6) if x["ms"] > 0 and x["bytes"] else 0.0
+            print(f"# {x['kind']:12s} {x['ms']:9.2f} ms {100 * x['ms'] / tot:5.1f}%  launches {x['launches']:6d}"
+                  f"  {eff:8.1f} TFLOP/s  {bw:8.1f} GB/s", file=sys.stderr)
+
+    # timed steps: events only around the dominant class
+    m.timing_enable(1 << dom)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        m.reset()
+        m.prefill(tok, loss)
+    e1.record()
+    torch.cuda.synchronize()
+    m.sync()
+    ms = e0.elapsed_time(e1) / args.steps
+    dk = m.timing_read(dom)
+    m.timing_enable(0)
+    assert bool(torch.isfinite(loss).all()), "non-finite loss"
+    mean_loss = float(loss.mean())
+
+    flops = algorithmic_flops(c, T)
+    tps = T / (ms / 1e3)
+    frac = flops / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
+    hbm_kind = dk["kind"] in ("ce",)
+    if dk["kind"] in ("ce",):
+        ach = dk["bytes"] / dk["launches"] / (dk["ms"] / dk["launches"] * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=None)
+    else:
+        ach = dk["flops"] / dk["launches"] / (dk["ms"] / dk["launches"] * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None)
+    roof.update(kernel_class=dk["kind"], launches_per_step=dk["launches"] // args.steps,
+                avg_launch_us=round(dk["ms"] / dk["launches"] * 1e3, 2),
+                share_of_step=round(dk["ms"] / args.steps / ms, 4))
+
+    out = dict(metric=METRIC, value=round(tps, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=round(ms, 2), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="bf16" if c["dtype"] == "bf16" else "f32", data="synthetic",
+               config=dict(workload=f"{args.workload}-shape TTT-E2E prefill, T={T}, b={c['minibatch']}, "
+                                    f"k={c['window']}, alpha={c['alpha']}, Zipf(1.1) ids",
+                           seq_len=T, minibatch=c["minibatch"], window=c["window"]),
+               mfma_peak_frac=round(frac, 4), algorithmic_tflop=round(flops / 1e12, 1),
+               mean_loss=round(mean_loss, 4), roofline=roof)
+    del m
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        out["cpu_baseline"] = cpu_baseline(c, w, tok, min(c["minibatch"], T - 1))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -72,7 +72,7 @@ typedef struct {
   int32_t d_model;        /* d, multiple of 16 */
   int32_t n_heads;        /* query heads H */
   int32_t n_kv_heads;     /* Hk, divides H */
-  int32_t head_dim;       /* 16, 64 or 128 (128 only for TTT_BF16) */
+  int32_t head_dim;       /* 16, 64 or 128 */
   int32_t ffn_hidden;     /* static SwiGLU hidden size, multiple of 32 */
   int32_t dyn_ffn_hidden; /* dynamic SwiGLU hidden size, multiple of 32 */
   int32_t vocab;          /* V, multiple of 8 */
@@ -156,6 +156,32 @@ int64_t ttt_position(const ttt_ctx* ctx);
 const char* ttt_last_error(const ttt_ctx* ctx);
 
 void ttt_destroy(ttt_ctx* ctx);
+
+/* Diagnostics: live per-kernel-class timing with HIP events recorded on the
+ * launch stream around every launch of the selected classes. */
+typedef enum {
+  TTT_KC_GEMM_PREFIX = 0, /* projections and MLP GEMMs of the hoisted prefix */
+  TTT_KC_ATTN_PREFIX = 1, /* SWA forward of the hoisted prefix */
+  TTT_KC_GEMM_LOOP = 2,   /* loop forward GEMMs and backward dX / dHmid GEMMs */
+  TTT_KC_ATTN_LOOP = 3,   /* SWA forward inside the loop */
+  TTT_KC_LMHEAD = 4,      /* lm_head forward and its dX product */
+  TTT_KC_CE = 5,          /* fused softmax-CE + logit gradient */
+  TTT_KC_ATTN_BWD = 6,    /* SWA backward (dQ and dK/dV kernels) */
+  TTT_KC_DW_SGD = 7,      /* dW = X^T dH with the fused fp32 SGD update */
+  TTT_KC_OTHER = 8,       /* norms, RoPE, embedding, copies */
+  TTT_KC_COUNT = 9
+} ttt_kernel_class;
+
+/* Starts timing the classes in class_mask (bit i = class i) and clears the
+ * counters; 0 stops timing. */
+ttt_status ttt_timing_enable(ttt_ctx* ctx, uint32_t class_mask);
+
+/* Synchronises the device and returns, for one class, the summed kernel time
+ * (ms), the number of launches and their algorithmic FLOPs and HBM bytes
+ * (the minimal operand/result traffic each launch must move). Any pointer
+ * may be NULL. */
+ttt_status ttt_timing_read(ttt_ctx* ctx, int32_t kclass, double* total_ms, int64_t* launches,
+                           double* flops, double* bytes);
 
 /* E2-TTT chunk-end scan ([P3] 方法细节, Proposition 3.1; Algorithm 1 state
  * update). For every head h and chunk [r C, min((r+1) C, T)), with W0, M0 the

@@ -73,8 +73,11 @@ def lib() -> ctypes.CDLL:
         L.ttt_destroy.argtypes = [vp]
         L.ttt_destroy.restype = None
         L.e2ttt_chunk_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
+        L.ttt_timing_enable.argtypes = [vp, ctypes.c_uint32]
+        dp, lp = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)
+        L.ttt_timing_read.argtypes = [vp, i32, dp, lp, dp, dp]
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_get_fast_weights", "ttt_reset",
-                  "ttt_sync", "e2ttt_chunk_scan"):
+                  "ttt_sync", "e2ttt_chunk_scan", "ttt_timing_enable", "ttt_timing_read"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -169,6 +172,20 @@ class TTT:
 
     def sync(self, stream=None):
         self._chk(lib().ttt_sync(self.h, _stream(stream)), "ttt_sync")
+
+    # live per-kernel-class timing (HIP events on the launch stream)
+    KC = ("gemm_prefix", "attn_prefix", "gemm_loop", "attn_loop", "lmhead", "ce", "attn_bwd",
+          "dw_sgd", "other")
+
+    def timing_enable(self, mask: int = (1 << 9) - 1):
+        self._chk(lib().ttt_timing_enable(self.h, mask), "ttt_timing_enable")
+
+    def timing_read(self, kind: int) -> dict:
+        ms, fl, by = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        n = ctypes.c_int64()
+        self._chk(lib().ttt_timing_read(self.h, kind, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(fl),
+                                        ctypes.byref(by)), "ttt_timing_read")
+        return dict(kind=self.KC[kind], ms=ms.value, launches=n.value, flops=fl.value, bytes=by.value)
 
     @property
     def position(self) -> int:

@@ -514,6 +514,7 @@ static hipError_t dkdv_dh(const AttnArgs& a, hipStream_t st) {
     switch (a.dh) {                                                    \
       case 16: return FN<float, 16>(a, st);                            \
       case 64: return FN<float, 64>(a, st);                            \
+      case 128: return FN<float, 128>(a, st);                          \
     }                                                                  \
   }                                                                    \
   return hipErrorInvalidValue;

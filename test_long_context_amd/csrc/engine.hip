@@ -60,6 +60,7 @@ struct ttt_ctx {
   std::vector<void*> wqkv, wo, w12, w3;       // static, storage dtype
   std::vector<float*> m12, m3;               // dynamic fp32 masters (interleaved W1|W2)
   std::vector<void*> dw12, dw3;              // dynamic working copies (== master for f32)
+  std::vector<void*> dw12_lo, dw3_lo;        // bf16: low terms, master ~= working + low
   std::vector<void*> w0_12, w0_3;            // W0 snapshot (storage dtype, interleaved)
   std::vector<void*> kring, vring;           // per layer [Hk][cap][dh]
   float2* rope = nullptr;                    // [max_seq][dh/2] (cos, sin)
@@ -97,6 +98,25 @@ struct ttt_ctx {
   int64_t* d_pos = nullptr;
   float* dec = nullptr;                      // decode scratch
   int dec_split = 1;
+
+  // live per-class timing (ttt_timing_enable / ttt_timing_read)
+  struct TRec {
+    int kind;
+    hipEvent_t a, b;
+    double flops, bytes;
+  };
+  uint32_t tmask = 0;
+  std::vector<hipEvent_t> evpool;
+  size_t evused = 0;
+  std::vector<TRec> trecs;
+  hipEvent_t ev() {
+    if (evused == evpool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      evpool.push_back(e);
+    }
+    return evpool[evused++];
+  }
 };
 
 namespace {
@@ -112,6 +132,49 @@ ttt_status fail(ttt_ctx* c, ttt_status s, const std::string& msg) {
     if (e_ != hipSuccess)                                                             \
       return fail(c, TTT_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
   } while (0)
+
+// Records HIP events around one launch when its class is being timed.
+struct Timed {
+  ttt_ctx* c;
+  hipStream_t st;
+  int kind;
+  double fl, by;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(ttt_ctx* c_, hipStream_t st_, int kind_, double fl_, double by_)
+      : c(c_), st(st_), kind(kind_), fl(fl_), by(by_) {
+    if (c->tmask & (1u << kind)) {
+      a = c->ev();
+      b = c->ev();
+      if (a && b) (void)hipEventRecord(a, st);
+      else a = b = nullptr;
+    }
+  }
+  ~Timed() {
+    if (a) {
+      (void)hipEventRecord(b, st);
+      c->trecs.push_back({kind, a, b, fl, by});
+    }
+  }
+};
+
+#define TCALL(kind, fl, by, call)       \
+  do {                                  \
+    Timed t_(c, st, (kind), (fl), (by)); \
+    HIPCHK(c, call);                    \
+  } while (0)
+
+constexpr int KC_GP = TTT_KC_GEMM_PREFIX, KC_AP = TTT_KC_ATTN_PREFIX, KC_GL = TTT_KC_GEMM_LOOP,
+              KC_AL = TTT_KC_ATTN_LOOP, KC_LM = TTT_KC_LMHEAD, KC_CE = TTT_KC_CE,
+              KC_AB = TTT_KC_ATTN_BWD, KC_SGD = TTT_KC_DW_SGD, KC_OT = TTT_KC_OTHER;
+
+inline double gfl(double m, double n, double k) { return 2.0 * m * n * k; }
+
+// sum over queries at positions p0 .. p0+n-1 of the number of visible keys
+double window_pairs(int64_t p0, int n, int k) {
+  double s = 0;
+  for (int i = 0; i < n; ++i) s += (double)std::min<int64_t>(p0 + i + 1, k);
+  return s;
+}
 
 bool dalloc(ttt_ctx* c, void** p, size_t bytes) {
   if (bytes == 0) bytes = 16;
@@ -145,8 +208,7 @@ ttt_status validate(const ttt_config* cfg) {
   if (!(c.alpha >= 0.f) || !isfinite(c.alpha) || !(c.rms_eps > 0.f) || !(c.rope_theta > 1.f))
     return TTT_ERR_INVALID_ARG;
   if (c.n_heads % c.n_kv_heads) return TTT_ERR_INVALID_ARG;
-  const bool bf = c.dtype == TTT_BF16;
-  if (!(c.head_dim == 16 || c.head_dim == 64 || (bf && c.head_dim == 128))) return TTT_ERR_UNSUPPORTED;
+  if (!(c.head_dim == 16 || c.head_dim == 64 || c.head_dim == 128)) return TTT_ERR_UNSUPPORTED;
   if (c.d_model % 16 || c.ffn_hidden % 32 || c.dyn_ffn_hidden % 32 || c.vocab % 8)
     return TTT_ERR_UNSUPPORTED;
   if ((int64_t)c.max_seq > (int64_t(1) << 30)) return TTT_ERR_UNSUPPORTED;
@@ -205,10 +267,10 @@ GemmArgs ga(const void* A, long lda, const void* B, long ldb, int M, int N, int 
   return g;
 }
 
-// C (float partials) = A [M, K] (k-major) * B (k-row-major [K, N]), split-K.
-// Returns the number of partial slices written.
-hipError_t gemm_nn_split(ttt_ctx* c, const void* A, long lda, const void* B, long ldb, int M, int N,
-                         int K, float* part, int* nsplit, hipStream_t st) {
+// C (float partials) = A [M, K] (k-major) * B (k-row-major [K, N]), split-K;
+// *nsplit receives the number of partial slices written.
+ttt_status gemm_nn_split(ttt_ctx* c, int kind, const void* A, long lda, const void* B, long ldb, int M,
+                         int N, int K, float* part, int* nsplit, hipStream_t st) {
   const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int s = std::min(choose_split(tiles, K), c->max_split);
   const int gran = gemm_k_granule(c->dt);
@@ -218,44 +280,58 @@ hipError_t gemm_nn_split(ttt_ctx* c, const void* A, long lda, const void* B, lon
   GemmArgs g = ga(A, lda, B, ldb, M, N, K, part, N);
   g.kchunk = chunk;
   *nsplit = s;
-  return gemm(c->dt, true, false, Epi::PARTIAL, g, st);
+  TCALL(kind, gfl(M, N, K), 0, gemm(c->dt, true, false, Epi::PARTIAL, g, st));
+  return TTT_OK;
+}
+
+#define RUN(x)                      \
+  do {                              \
+    ttt_status r_ = (x);            \
+    if (r_ != TTT_OK) return r_;    \
+  } while (0)
+
+AttnArgs attn_args(ttt_ctx* c, int l, const void* q, void* o, float* lse, int n, int64_t p0) {
+  AttnArgs a{};
+  a.q = q;
+  a.k = c->kring[l];
+  a.v = c->vring[l];
+  a.o = o;
+  a.lse = lse;
+  a.n = n;
+  a.H = c->H;
+  a.Hk = c->Hk;
+  a.dh = c->dh;
+  a.cap = (int)c->cap;
+  a.window = c->k;
+  a.pos0 = p0;
+  a.scale = 1.f / sqrtf((float)c->dh);
+  return a;
 }
 
 // ------------------------------------------------------------ prefix phase
 ttt_status run_prefix(ttt_ctx* c, const int32_t* tok, int64_t T, hipStream_t st) {
-  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV;
-  const float scale = 1.f / sqrtf((float)dh);
+  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, F = c->F;
+  const float eps = c->cfg.rms_eps;
   for (int64_t p0 = 0; p0 < T; p0 += c->slab) {
     const int n = (int)std::min<int64_t>(c->slab, T - p0);
     float* h = c->hres + p0 * d;
-    HIPCHK(c, embed_gather(c->dt, tok + p0, n, c->embed, d, h, c->V, c->d_err, st));
-    for (int l = 0; l <= c->s && l < c->L; ++l) {
-      HIPCHK(c, rmsnorm_fwd(c->dt, h, c->attn_norm[l], n, d, c->cfg.rms_eps, c->xn, c->rbuf, st));
-      HIPCHK(c, gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
-      HIPCHK(c, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, p0, c->rope, c->qb, c->kring[l], c->vring[l],
-                             (int)c->cap, 0, st));
-      AttnArgs a{};
-      a.q = c->qb;
-      a.k = c->kring[l];
-      a.v = c->vring[l];
-      a.o = c->ob;
-      a.lse = nullptr;
-      a.n = n;
-      a.H = H;
-      a.Hk = Hk;
-      a.dh = dh;
-      a.cap = (int)c->cap;
-      a.window = c->k;
-      a.pos0 = p0;
-      a.scale = scale;
-      HIPCHK(c, attn_fwd(c->dt, a, st));
-      HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->ob, (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, h, d), st));
-      HIPCHK(c, rmsnorm_fwd(c->dt, h, c->mlp_norm[l], n, d, c->cfg.rms_eps, c->xn, c->rbuf, st));
-      GemmArgs g = ga(c->xn, d, c->w12[l], d, n, 2 * c->F, d, nullptr, 2 * c->F);
+    TCALL(KC_OT, 0, 0, embed_gather(c->dt, tok + p0, n, c->embed, d, h, c->V, c->d_err, st));
+    for (int l = 0; l <= c->s; ++l) {
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, h, c->attn_norm[l], n, d, eps, c->xn, c->rbuf, st));
+      TCALL(KC_GP, gfl(n, QKV, d), 0,
+            gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
+      TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, p0, c->rope, c->qb, c->kring[l],
+                                      c->vring[l], (int)c->cap, 0, st));
+      AttnArgs a = attn_args(c, l, c->qb, c->ob, nullptr, n, p0);
+      TCALL(KC_AP, 4.0 * H * dh * window_pairs(p0, n, c->k), 0, attn_fwd(c->dt, a, st));
+      TCALL(KC_GP, gfl(n, d, H * dh), 0,
+            gemm(c->dt, true, true, Epi::ADD_F32, ga(c->ob, (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, h, d), st));
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, h, c->mlp_norm[l], n, d, eps, c->xn, c->rbuf, st));
+      GemmArgs g = ga(c->xn, d, c->w12[l], d, n, 2 * F, d, nullptr, 2 * F);
       g.C2 = c->hmid;
-      HIPCHK(c, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
-      HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->hmid, c->F, c->w3[l], c->F, n, d, c->F, h, d), st));
-      (void)0;
+      TCALL(KC_GP, gfl(n, 2 * F, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
+      TCALL(KC_GP, gfl(n, d, F), 0,
+            gemm(c->dt, true, true, Epi::ADD_F32, ga(c->hmid, F, c->w3[l], F, n, d, F, h, d), st));
     }
   }
   return TTT_OK;
@@ -263,125 +339,109 @@ ttt_status run_prefix(ttt_ctx* c, const int32_t* tok, int64_t T, hipStream_t st)
 
 // ------------------------------------------------------------ loop phase
 ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipStream_t st) {
-  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s;
+  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s, F = c->F, Fd = c->Fd;
   const float eps = c->cfg.rms_eps;
-  const float scale = 1.f / sqrtf((float)dh);
   float* hl = c->hl;
-  HIPCHK(c, copy_f32(c->hres + a0 * d, hl, (size_t)n * d, st));
+  TCALL(KC_OT, 0, 0, copy_f32(c->hres + a0 * d, hl, (size_t)n * d, st));
   for (int l = s; l < c->L; ++l) {
     const int i = l - s;
     if (l > s) {
-      // attention
-      HIPCHK(c, copy_f32(hl, c->h_att[i], (size_t)n * d, st));
-      HIPCHK(c, rmsnorm_fwd(c->dt, hl, c->attn_norm[l], n, d, eps, c->xn, c->r_att[i], st));
-      HIPCHK(c, gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
-      HIPCHK(c, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, a0, c->rope, c->q_l[i], c->kring[l], c->vring[l],
-                             (int)c->cap, 0, st));
-      AttnArgs a{};
-      a.q = c->q_l[i];
-      a.k = c->kring[l];
-      a.v = c->vring[l];
-      a.o = c->o_l[i];
-      a.lse = c->lse[i];
-      a.n = n;
-      a.H = H;
-      a.Hk = Hk;
-      a.dh = dh;
-      a.cap = (int)c->cap;
-      a.window = c->k;
-      a.pos0 = a0;
-      a.scale = scale;
-      HIPCHK(c, attn_fwd(c->dt, a, st));
-      HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, hl, d), st));
-      // static MLP
-      HIPCHK(c, copy_f32(hl, c->h_mlp[i], (size_t)n * d, st));
-      HIPCHK(c, rmsnorm_fwd(c->dt, hl, c->mlp_norm[l], n, d, eps, c->xn, c->r_mlp[i], st));
-      GemmArgs g = ga(c->xn, d, c->w12[l], d, n, 2 * c->F, d, c->h12_s[i], 2 * c->F);
+      // attention sublayer
+      TCALL(KC_OT, 0, 0, copy_f32(hl, c->h_att[i], (size_t)n * d, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, hl, c->attn_norm[l], n, d, eps, c->xn, c->r_att[i], st));
+      TCALL(KC_GL, gfl(n, QKV, d), 0,
+            gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
+      TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, a0, c->rope, c->q_l[i], c->kring[l],
+                                      c->vring[l], (int)c->cap, 0, st));
+      AttnArgs a = attn_args(c, l, c->q_l[i], c->o_l[i], c->lse[i], n, a0);
+      TCALL(KC_AL, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_fwd(c->dt, a, st));
+      TCALL(KC_GL, gfl(n, d, H * dh), 0,
+            gemm(c->dt, true, true, Epi::ADD_F32, ga(c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, hl, d), st));
+      // static MLP sublayer
+      TCALL(KC_OT, 0, 0, copy_f32(hl, c->h_mlp[i], (size_t)n * d, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, hl, c->mlp_norm[l], n, d, eps, c->xn, c->r_mlp[i], st));
+      GemmArgs g = ga(c->xn, d, c->w12[l], d, n, 2 * F, d, c->h12_s[i], 2 * F);
       g.C2 = c->hmid;
-      HIPCHK(c, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
-      HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->hmid, c->F, c->w3[l], c->F, n, d, c->F, hl, d), st));
+      TCALL(KC_GL, gfl(n, 2 * F, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
+      TCALL(KC_GL, gfl(n, d, F), 0,
+            gemm(c->dt, true, true, Epi::ADD_F32, ga(c->hmid, F, c->w3[l], F, n, d, F, hl, d), st));
     }
-    // dynamic MLP
-    HIPCHK(c, copy_f32(hl, c->h_dyn[i], (size_t)n * d, st));
-    HIPCHK(c, rmsnorm_fwd(c->dt, hl, c->dyn_norm[i], n, d, eps, c->xn_d[i], c->r_dyn[i], st));
-    GemmArgs g = ga(c->xn_d[i], d, c->dw12[i], d, n, 2 * c->Fd, d, c->h12_d[i], 2 * c->Fd);
+    // dynamic MLP sublayer under the current fast weights
+    TCALL(KC_OT, 0, 0, copy_f32(hl, c->h_dyn[i], (size_t)n * d, st));
+    TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, hl, c->dyn_norm[i], n, d, eps, c->xn_d[i], c->r_dyn[i], st));
+    // (bf16: the fp32 master enters as two bf16 terms, working + low, so that
+    // updates below half a bf16 ulp reach the forward)
+    GemmArgs g = ga(c->xn_d[i], d, c->dw12[i], d, n, 2 * Fd, d, c->h12_d[i], 2 * Fd);
     g.C2 = c->hm_d[i];
-    HIPCHK(c, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
-    HIPCHK(c, gemm(c->dt, true, true, Epi::ADD_F32, ga(c->hm_d[i], c->Fd, c->dw3[i], c->Fd, n, d, c->Fd, hl, d), st));
+    g.B2 = c->dw12_lo[i];
+    TCALL(KC_GL, gfl(n, 2 * Fd, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
+    GemmArgs g3 = ga(c->hm_d[i], Fd, c->dw3[i], Fd, n, d, Fd, hl, d);
+    g3.B2 = c->dw3_lo[i];
+    TCALL(KC_GL, gfl(n, d, Fd), 0, gemm(c->dt, true, true, Epi::ADD_F32, g3, st));
   }
-  HIPCHK(c, copy_f32(hl, c->h_f, (size_t)n * d, st));
-  HIPCHK(c, rmsnorm_fwd(c->dt, hl, c->final_norm, n, d, eps, c->xn, c->r_f, st));
-  HIPCHK(c, gemm(c->dt, true, true, Epi::STORE_F32, ga(c->xn, d, c->lm_head, d, n, c->V, d, c->logits, c->V), st));
+  TCALL(KC_OT, 0, 0, copy_f32(hl, c->h_f, (size_t)n * d, st));
+  TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, hl, c->final_norm, n, d, eps, c->xn, c->r_f, st));
+  TCALL(KC_LM, gfl(n, c->V, d), 0,
+        gemm(c->dt, true, true, Epi::STORE_F32, ga(c->xn, d, c->lm_head, d, n, c->V, d, c->logits, c->V), st));
   return TTT_OK;
 }
 
 ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
-  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s;
-  const float scale = 1.f / sqrtf((float)dh);
+  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s, F = c->F, Fd = c->Fd;
   const float lr = c->cfg.alpha;
+  const double upd_bytes = 8.0 + (c->dt == DT::F32 ? 0.0 : (double)c->es);  // master r/w + working copy
   int ns = 1;
-  // lm_head^T and final norm
-  HIPCHK(c, gemm_nn_split(c, c->dz, c->V, c->lm_head, d, n, d, c->V, c->part, &ns, st));
-  HIPCHK(c, rmsnorm_bwd(c->dt, c->part, ns, c->h_f, c->final_norm, c->r_f, n, d, c->gh, c->gh_t, 0, st));
+  // lm_head^T and the final norm
+  RUN(gemm_nn_split(c, KC_LM, c->dz, c->V, c->lm_head, d, n, d, c->V, c->part, &ns, st));
+  TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_f, c->final_norm, c->r_f, n, d, c->gh, c->gh_t, 0, st));
   for (int l = c->L - 1; l >= s; --l) {
     const int i = l - s;
     // dynamic MLP: dHmid = dY W3 with the SwiGLU backward in the epilogue
     {
-      GemmArgs g = ga(c->gh_t, d, c->dw3[i], c->Fd, n, c->Fd, d, c->dh12, 2 * c->Fd);
+      GemmArgs g = ga(c->gh_t, d, c->dw3[i], Fd, n, Fd, d, c->dh12, 2 * Fd);
       g.X = c->h12_d[i];
-      HIPCHK(c, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
+      TCALL(KC_GL, gfl(n, Fd, d), 0, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
     }
-    if (l > s)
-      HIPCHK(c, gemm_nn_split(c, c->dh12, 2 * c->Fd, c->dw12[i], d, n, d, 2 * c->Fd, c->part, &ns, st));
+    if (l > s) RUN(gemm_nn_split(c, KC_GL, c->dh12, 2 * Fd, c->dw12[i], d, n, d, 2 * Fd, c->part, &ns, st));
     // dW3 = dY^T Hmid and dW12 = dH12^T U, with W -= alpha dW in the epilogue
     {
-      GemmArgs g = ga(c->gh_t, d, c->hm_d[i], c->Fd, d, c->Fd, n, c->m3[i], c->Fd);
+      GemmArgs g = ga(c->gh_t, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
       g.C2 = c->dw3[i];
+      g.C3 = c->dw3_lo[i];
       g.scale = lr;
-      HIPCHK(c, gemm(c->dt, false, false, Epi::SGD, g, st));
-      GemmArgs g2 = ga(c->dh12, 2 * c->Fd, c->xn_d[i], d, 2 * c->Fd, d, n, c->m12[i], d);
+      TCALL(KC_SGD, gfl(d, Fd, n), (double)d * Fd * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g, st));
+      GemmArgs g2 = ga(c->dh12, 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
       g2.C2 = c->dw12[i];
+      g2.C3 = c->dw12_lo[i];
       g2.scale = lr;
-      HIPCHK(c, gemm(c->dt, false, false, Epi::SGD, g2, st));
+      TCALL(KC_SGD, gfl(2 * Fd, d, n), 2.0 * Fd * d * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g2, st));
     }
     if (l == s) break;
-    HIPCHK(c, rmsnorm_bwd(c->dt, c->part, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], n, d, c->gh, c->gh_t, 1, st));
+    TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], n, d, c->gh, c->gh_t, 1, st));
     // static MLP
     {
-      GemmArgs g = ga(c->gh_t, d, c->w3[l], c->F, n, c->F, d, c->dh12, 2 * c->F);
+      GemmArgs g = ga(c->gh_t, d, c->w3[l], F, n, F, d, c->dh12, 2 * F);
       g.X = c->h12_s[i];
-      HIPCHK(c, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
-      HIPCHK(c, gemm_nn_split(c, c->dh12, 2 * c->F, c->w12[l], d, n, d, 2 * c->F, c->part, &ns, st));
-      HIPCHK(c, rmsnorm_bwd(c->dt, c->part, ns, c->h_mlp[i], c->mlp_norm[l], c->r_mlp[i], n, d, c->gh, c->gh_t, 1, st));
+      TCALL(KC_GL, gfl(n, F, d), 0, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
+      RUN(gemm_nn_split(c, KC_GL, c->dh12, 2 * F, c->w12[l], d, n, d, 2 * F, c->part, &ns, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_mlp[i], c->mlp_norm[l], c->r_mlp[i], n, d, c->gh, c->gh_t, 1, st));
     }
     // attention
     {
-      HIPCHK(c, gemm(c->dt, true, false, Epi::STORE, ga(c->gh_t, d, c->wo[l], (long)H * dh, n, H * dh, d, c->dO, (long)H * dh), st));
-      HIPCHK(c, attn_rowdot(c->dt, c->dO, c->o_l[i], n, H, dh, c->Dbuf, st));
-      AttnArgs a{};
-      a.q = c->q_l[i];
-      a.k = c->kring[l];
-      a.v = c->vring[l];
-      a.o = c->o_l[i];
-      a.lse = c->lse[i];
-      a.n = n;
-      a.H = H;
-      a.Hk = Hk;
-      a.dh = dh;
-      a.cap = (int)c->cap;
-      a.window = c->k;
-      a.pos0 = a0;
-      a.scale = scale;
+      TCALL(KC_GL, gfl(n, H * dh, d), 0,
+            gemm(c->dt, true, false, Epi::STORE, ga(c->gh_t, d, c->wo[l], (long)H * dh, n, H * dh, d, c->dO, (long)H * dh), st));
+      TCALL(KC_OT, 0, 0, attn_rowdot(c->dt, c->dO, c->o_l[i], n, H, dh, c->Dbuf, st));
+      AttnArgs a = attn_args(c, l, c->q_l[i], c->o_l[i], c->lse[i], n, a0);
       a.dO = c->dO;
       a.D = c->Dbuf;
       a.dq = c->dq;
       a.dk = c->dk;
       a.dv = c->dv;
-      HIPCHK(c, attn_bwd_dq(c->dt, a, st));
-      HIPCHK(c, attn_bwd_dkdv(c->dt, a, st));
-      HIPCHK(c, rope_bwd_pack(c->dt, c->dq, c->dk, c->dv, n, H, Hk, dh, a0, c->rope, c->dqkv, st));
-      HIPCHK(c, gemm_nn_split(c, c->dqkv, QKV, c->wqkv[l], d, n, d, QKV, c->part, &ns, st));
-      HIPCHK(c, rmsnorm_bwd(c->dt, c->part, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->gh_t, 1, st));
+      TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq(c->dt, a, st));
+      TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv(c->dt, a, st));
+      TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, c->dq, c->dk, c->dv, n, H, Hk, dh, a0, c->rope, c->dqkv, st));
+      RUN(gemm_nn_split(c, KC_GL, c->dqkv, QKV, c->wqkv[l], d, n, d, QKV, c->part, &ns, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->gh_t, 1, st));
     }
   }
   return TTT_OK;
@@ -473,6 +533,8 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   c->m3.resize(nd);
   c->dw12.resize(nd);
   c->dw3.resize(nd);
+  c->dw12_lo.assign(nd, nullptr);
+  c->dw3_lo.assign(nd, nullptr);
   c->w0_12.resize(nd);
   c->w0_3.resize(nd);
   for (int i = 0; i < nd && ok; ++i) {
@@ -485,6 +547,8 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     } else {
       A(&c->dw12[i], (size_t)2 * c->Fd * d * es);
       A(&c->dw3[i], (size_t)d * c->Fd * es);
+      A(&c->dw12_lo[i], (size_t)2 * c->Fd * d * es);
+      A(&c->dw3_lo[i], (size_t)d * c->Fd * es);
     }
     A(&c->w0_12[i], (size_t)2 * c->Fd * d * es);
     A(&c->w0_3[i], (size_t)d * c->Fd * es);
@@ -631,8 +695,11 @@ ttt_status ttt_reset(ttt_ctx* c, void* stream) {
     HIPCHK(c, cast_from(c->dt, c->w0_12[i], c->m12[i], n12, st));
     HIPCHK(c, cast_from(c->dt, c->w0_3[i], c->m3[i], n3, st));
     if (c->dt != DT::F32) {
+      // W0 is exact in the storage dtype: working copy = W0, low term = 0
       HIPCHK(c, hipMemcpyAsync(c->dw12[i], c->w0_12[i], n12 * es, hipMemcpyDeviceToDevice, st));
       HIPCHK(c, hipMemcpyAsync(c->dw3[i], c->w0_3[i], n3 * es, hipMemcpyDeviceToDevice, st));
+      HIPCHK(c, fill_zero_bytes(c->dw12_lo[i], n12 * es, st));
+      HIPCHK(c, fill_zero_bytes(c->dw3_lo[i], n3 * es, st));
     }
   }
   c->pos = 0;
@@ -659,7 +726,8 @@ ttt_status ttt_prefill(ttt_ctx* c, const int32_t* tok, int64_t T, float* loss, f
     const int nt = (int)(std::min<int64_t>(a0 + n, T - 1) - a0);
     if (nt <= 0) continue;
     const float scale = red_sum ? 1.f : 1.f / nt;
-    HIPCHK(c, ce_fwd_bwd(c->dt, c->logits, n, nt, c->V, tok + a0 + 1, scale, loss + a0, c->dz, c->d_err, st));
+    TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
+          ce_fwd_bwd(c->dt, c->logits, n, nt, c->V, tok + a0 + 1, scale, loss + a0, c->dz, c->d_err, st));
     r = loop_backward(c, a0, n, st);
     if (r != TTT_OK) return r;
   }
@@ -700,6 +768,38 @@ ttt_status ttt_sync(ttt_ctx* c, void* stream) {
   return TTT_OK;
 }
 
+ttt_status ttt_timing_enable(ttt_ctx* c, uint32_t mask) {
+  if (!c) return TTT_ERR_INVALID_ARG;
+  HIPCHK(c, hipDeviceSynchronize());
+  c->tmask = mask;
+  c->trecs.clear();
+  c->evused = 0;
+  return TTT_OK;
+}
+
+ttt_status ttt_timing_read(ttt_ctx* c, int32_t kind, double* ms, int64_t* launches, double* flops,
+                           double* bytes) {
+  if (!c) return TTT_ERR_INVALID_ARG;
+  if (kind < 0 || kind >= TTT_KC_COUNT) return fail(c, TTT_ERR_INVALID_ARG, "bad kernel class");
+  HIPCHK(c, hipDeviceSynchronize());
+  double t = 0, f = 0, b = 0;
+  int64_t nl = 0;
+  for (const auto& r : c->trecs) {
+    if (r.kind != kind) continue;
+    float e = 0.f;
+    HIPCHK(c, hipEventElapsedTime(&e, r.a, r.b));
+    t += e;
+    f += r.flops;
+    b += r.bytes;
+    ++nl;
+  }
+  if (ms) *ms = t;
+  if (launches) *launches = nl;
+  if (flops) *flops = f;
+  if (bytes) *bytes = b;
+  return TTT_OK;
+}
+
 int64_t ttt_position(const ttt_ctx* c) { return c ? c->pos : -1; }
 
 const char* ttt_last_error(const ttt_ctx* c) { return c ? c->err.c_str() : "null context"; }
@@ -707,6 +807,7 @@ const char* ttt_last_error(const ttt_ctx* c) { return c ? c->err.c_str() : "null
 void ttt_destroy(ttt_ctx* c) {
   if (!c) return;
   (void)hipDeviceSynchronize();
+  for (hipEvent_t e : c->evpool) (void)hipEventDestroy(e);
   for (void* p : c->allocs) (void)hipFree(p);
   delete c;
 }

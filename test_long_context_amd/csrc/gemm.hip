@@ -91,7 +91,7 @@ struct TileLoader {
   }
 };
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM, int EPI>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM, int EPI, bool SPLITB>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_kernel(GemmArgs g) {
   constexpr int NWN = BN / WN;
@@ -100,6 +100,8 @@ gemm_kernel(GemmArgs g) {
   constexpr int FM = WM / 16, FN = WN / 16;
   __shared__ __attribute__((aligned(16))) T As[2][BM * LDS];
   __shared__ __attribute__((aligned(16))) T Bs[2][BN * LDS];
+  // low part of B for the two-term split (one byte when unused)
+  __shared__ __attribute__((aligned(16))) T Bs2[SPLITB ? 2 : 1][SPLITB ? BN * LDS : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,12 +130,16 @@ gemm_kernel(GemmArgs g) {
 
   TileLoader<T, BM, BK, NT, AK> la;
   TileLoader<T, BN, BK, NT, BKM> lb;
+  TileLoader<T, SPLITB ? BN : 8, BK, NT, BKM> lb2;
+  const T* __restrict__ B2 = (const T*)g.B2;
   const int nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) {
     la.load(A, g.lda, m0, g.M, kbeg, kend, tid);
     lb.load(B, g.ldb, n0, g.N, kbeg, kend, tid);
+    if constexpr (SPLITB) lb2.load(B2, g.ldb, n0, g.N, kbeg, kend, tid);
     la.template store<LDS>(As[0], tid);
     lb.template store<LDS>(Bs[0], tid);
+    if constexpr (SPLITB) lb2.template store<LDS>(Bs2[0], tid);
   }
   __syncthreads();
 
@@ -145,6 +151,7 @@ gemm_kernel(GemmArgs g) {
       const int k0 = kbeg + (kt + 1) * BK;
       la.load(A, g.lda, m0, g.M, k0, kend, tid);
       lb.load(B, g.ldb, n0, g.N, k0, kend, tid);
+      if constexpr (SPLITB) lb2.load(B2, g.ldb, n0, g.N, k0, kend, tid);
     }
     const T* as = As[cur];
     const T* bs = Bs[cur];
@@ -159,10 +166,19 @@ gemm_kernel(GemmArgs g) {
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) mma16(acc[i][j], af[i], bfr[j]);
+      if constexpr (SPLITB) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) ld8(bfr[j], Bs2[cur] + (wn0 + j * 16 + fr) * LDS + kk + fk);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mma16(acc[i][j], af[i], bfr[j]);
+      }
     }
     if (kt + 1 < nk) {
       la.template store<LDS>(As[cur ^ 1], tid);
       lb.template store<LDS>(Bs[cur ^ 1], tid);
+      if constexpr (SPLITB) lb2.template store<LDS>(Bs2[cur ^ 1], tid);
     }
     __syncthreads();
   }
@@ -217,7 +233,11 @@ gemm_kernel(GemmArgs g) {
             float* W = (float*)g.C;
             const float w = W[idx] - g.scale * a;
             W[idx] = w;
-            if (g.C2 != g.C) ((T*)g.C2)[idx] = from_f<T>(w);
+            if (g.C2 != g.C) {
+              const T hi = from_f<T>(w);
+              ((T*)g.C2)[idx] = hi;
+              if (g.C3) ((T*)g.C3)[idx] = from_f<T>(w - to_f(hi));
+            }
           } else if constexpr (EPI == (int)Epi::SWIGLU_BWD) {
             // n indexes the hidden unit j; its gate/up columns in the
             // 16-interleaved layout are (j / 16) * 32 + j % 16 and + 16.
@@ -235,23 +255,23 @@ gemm_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------ dispatch
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM, int EPI>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM, int EPI, bool SPLITB>
 static hipError_t launch(const GemmArgs& g, hipStream_t st) {
   const int tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
   int splits = 1;
   if (g.kchunk > 0) splits = (g.K + g.kchunk - 1) / g.kchunk;
   dim3 grid(tm * tn, 1, splits);
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, AK, BKM, EPI>), grid, dim3(NT), 0, st, g);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, AK, BKM, EPI, SPLITB>), grid, dim3(NT), 0, st, g);
   return hipGetLastError();
 }
 
-template <typename T, bool AK, bool BKM, int EPI>
+template <typename T, bool AK, bool BKM, int EPI, bool SPLITB = false>
 static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    return launch<T, 128, 128, 32, 64, 64, AK, BKM, EPI>(g, st);
+    return launch<T, 128, 128, 32, 64, 64, AK, BKM, EPI, SPLITB>(g, st);
   } else {
-    return launch<T, 64, 64, 32, 32, 32, AK, BKM, EPI>(g, st);
+    return launch<T, 64, 64, 32, 32, 32, AK, BKM, EPI, SPLITB>(g, st);
   }
 }
 
@@ -281,6 +301,13 @@ int gemm_k_granule(DT) { return 32; }
 
 hipError_t gemm(DT dt, bool a_kmajor, bool b_kmajor, Epi epi, const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.B2) {
+    // two-term split of B: forward products with the fast weights (bf16, NT)
+    if (dt != DT::BF16 || !a_kmajor || !b_kmajor) return hipErrorInvalidValue;
+    if (epi == Epi::SWIGLU) return launch_cfg<bf16, true, true, (int)Epi::SWIGLU, true>(g, st);
+    if (epi == Epi::ADD_F32) return launch_cfg<bf16, true, true, (int)Epi::ADD_F32, true>(g, st);
+    return hipErrorInvalidValue;
+  }
   if (dt == DT::BF16) return by_layout<bf16>(a_kmajor, b_kmajor, epi, g, st);
   return by_layout<float>(a_kmajor, b_kmajor, epi, g, st);
 }

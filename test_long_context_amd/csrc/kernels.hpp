@@ -25,18 +25,21 @@ enum class Epi : int {
                 // optional C (T) = the pre-activations themselves
   SWIGLU_BWD,   // acc = dHmid[m, j]; X = pre-activations (ld = 2N):
                 // C (T) [m, gate/up col] = (dA, dC)
-  SGD,          // C (float master) -= scale * acc; C2 (T) = round(master)
+  SGD,          // C (float master) -= scale * acc; C2 (T) = round(master),
+                // C3 (T, optional) = round(master - C2)
   PARTIAL,      // C (float) [split][M][ldc] = acc  (split-K)
 };
 
 struct GemmArgs {
   const void* A;
   const void* B;
+  const void* B2;  // optional low part of B (B = B + B2, two bf16 terms of an fp32 value)
   int M, N, K;
   long lda, ldb;
   void* C;
   long ldc;
   void* C2;
+  void* C3;        // SGD: low part of the re-rounded weight (bf16 split), or null
   const void* X;
   float scale;
   int kchunk;  // split-K chunk (multiple of the K tile); <= 0 means no split

@@ -1,0 +1,107 @@
+"""GPU parity of the bf16 path (bf16 storage, fp32 accumulation, fp32
+fast-weight master) against the float32 oracle on the same bf16-valued
+inputs. Tolerances: 2e-2 relative on per-token loss, 5e-2 on the final fast
+weights measured against the update (max |W - W_ref| / max |W_ref - W0|)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ttt_e2e as O
+from tests.util import dw_err, rel_loss_err, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+LOSS_TOL = 2e-2
+W_TOL = 5e-2
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def run_gpu(c, w, tok, max_seq=None):
+    import test_long_context_amd as tla
+    m = tla.TTT(c, w, max_seq=max_seq or tok.numel())
+    loss = m.prefill(tok)
+    m.sync()
+    fw = [tuple(x.cpu().numpy() for x in m.fast_weights(i)) for i in range(len(w["dyn"]))]
+    loss = loss.cpu().numpy()
+    m.close()
+    return loss, fw
+
+
+def check(c, T):
+    say(f"case: bf16 L={c['n_layers']} d={c['d_model']} H={c['n_heads']}/{c['n_kv_heads']}x{c['head_dim']} "
+        f"F={c['ffn_hidden']} V={c['vocab']} k={c['window']} b={c['minibatch']} T={T}")
+    w = synth.gen_weights(c)
+    tok = synth.gen_tokens(c, n=T)
+    loss, fw = run_gpu(c, to_device(w), tok.cuda())
+    wn = synth.weights_to_numpy(w, np.float32)
+    ref = O.ttt_inner_loop(c, wn, tok.numpy(), dtype=np.float32)
+    le = rel_loss_err(loss, ref["loss"])
+    errs = [dw_err(g, ref["dyn"][i][k], wn["dyn"][i][k])
+            for i, gs in enumerate(fw) for k, g in zip(("w1", "w2", "w3"), gs)]
+    say(f"  loss rel err {le:.3e}  max dW err {max(errs):.3e}  mean loss {loss.mean():.4f}")
+    assert np.all(np.isfinite(loss))
+    assert le < LOSS_TOL
+    assert max(errs) < W_TOL
+
+
+def test_bf16_small_gqa_dh128_ring_wrap():
+    c = synth.config("125m", n_layers=4, d_model=256, n_heads=4, n_kv_heads=2, head_dim=128,
+                     ffn_hidden=512, dyn_ffn_hidden=512, vocab=4096, window=256, minibatch=128,
+                     n_dynamic=2, alpha=0.01)
+    check(c, T=700)
+
+
+def test_bf16_125m_full_sequence():
+    check(synth.config("125m"), T=8192)
+
+
+def test_bf16_1b_prefix_two_minibatches():
+    check(synth.config("1b"), T=2 * 1024 + 1)
+
+
+def test_generator_cpu_gpu_identical():
+    """The counter-based generator gives the same bf16 weights on either device."""
+    a = synth._normal_tensor(4, 101, (1 << 22,), 0.02, torch.bfloat16, "cpu")
+    b = synth._normal_tensor(4, 101, (1 << 22,), 0.02, torch.bfloat16, "cuda").cpu()
+    diff = int((a.view(torch.int16) != b.view(torch.int16)).sum())
+    say(f"  generator bf16 mismatches: {diff} of {1 << 22}")
+    assert diff <= 2
+    ta = synth.gen_tokens(synth.config("3b"), n=1 << 16)
+    tb = synth.gen_tokens(synth.config("3b"), n=1 << 16, device="cuda").cpu()
+    assert torch.equal(ta, tb)
+
+
+GOLD = os.path.join(HERE, "golden", "ttt_3b_minibatch0.npz")
+
+
+@pytest.mark.skipif(not os.path.exists(GOLD), reason="golden values not generated")
+def test_bf16_3b_full_shape_first_minibatch_against_stored_oracle_values():
+    """Full 3B shapes (bench launch configuration): mini-batch 0 of the 128K
+    stream, losses of all 1024 positions and 4096 sampled coordinates of every
+    fast-weight matrix after the first SGD step, against values written by
+    tests/golden/make_golden.py (oracle only)."""
+    import test_long_context_amd as tla
+    g = np.load(GOLD, allow_pickle=False)
+    c = synth.config("3b")
+    w = synth.gen_weights(c, device="cuda")
+    tok = synth.gen_tokens(c, n=c["minibatch"] + 1, device="cuda")
+    assert np.array_equal(tok.cpu().numpy(), g["tokens"])
+    assert np.array_equal(w["embed"][:4, :8].float().cpu().numpy(), g["embed_head"])
+    m = tla.TTT(c, w, max_seq=c["seq"] + 1024)
+    loss = m.prefill(tok)
+    m.sync()
+    le = rel_loss_err(loss.cpu().numpy(), g["loss"])
+    errs = []
+    for i in range(c["n_dynamic"]):
+        ws = m.fast_weights(i)
+        for k, W in zip(("w1", "w2", "w3"), ws):
+            idx = torch.from_numpy(g[f"d{i}_{k}_idx"]).cuda()
+            got = W.reshape(-1)[idx].cpu().numpy().astype(np.float64)
+            errs.append(float(np.max(np.abs(got - g[f"d{i}_{k}_val"])) / g[f"d{i}_{k}_den"]))
+    m.close()
+    say(f"  3b mini-batch 0: loss rel err {le:.3e}  sampled dW err {max(errs):.3e}")
+    assert le < LOSS_TOL
+    assert max(errs) < W_TOL
