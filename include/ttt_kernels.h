@@ -1,0 +1,73 @@
+/*
+ * ttt_kernels.h -- kernel-level entry points of the TTT-E2E library, for
+ * testing single kernels against the oracle and measuring them in
+ * isolation. They enqueue one kernel (family) on the given stream; all
+ * pointers are device memory owned by the caller; shapes are checked on the
+ * host before launch (TTT_ERR_INVALID_ARG / TTT_ERR_UNSUPPORTED).
+ */
+#ifndef TTT_KERNELS_H_
+#define TTT_KERNELS_H_
+
+#include <stdint.h>
+
+#include "ttt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Epilogues of tttk_gemm. */
+typedef enum {
+  TTTK_EPI_STORE = 0,      /* C (dtype) = scale * acc */
+  TTTK_EPI_STORE_F32 = 1,  /* C (float) = acc */
+  TTTK_EPI_ADD_F32 = 2,    /* C (float) += acc */
+  TTTK_EPI_SWIGLU = 3,     /* N = 2F columns interleaved in blocks of 16 (gate, up):
+                              C (dtype, may be NULL) = pre-activations,
+                              C2 (dtype) [M, F] = silu(gate) * up */
+  TTTK_EPI_SWIGLU_BWD = 4, /* acc = dHmid [M, N]; X (dtype) [M, 2N] pre-activations;
+                              C (dtype) [M, 2N] = (d gate, d up) */
+  TTTK_EPI_SGD = 5,        /* C (float master) -= scale * acc; C2 (dtype) = round(C);
+                              C3 (dtype, may be NULL) = round(C - C2) */
+  TTTK_EPI_PARTIAL = 6     /* C (float) [splits][M][ldc] = partial sums over K chunks */
+} tttk_epi;
+
+/* C[m, n] = sum_k A(m, k) B(n, k) on MFMA with fp32 accumulation, where
+ * A(m, k) = A[m lda + k] if a_kmajor else A[k lda + m], and
+ * B(n, k) = B[n ldb + k] if b_kmajor else B[k ldb + n];
+ * B2 (optional, bf16, NT layout, SWIGLU/ADD_F32 only) is a second term
+ * added to B. The contiguous dimension of A and B must be a multiple of 8
+ * and the pointers 16-byte aligned. kchunk > 0 splits K into chunks (a
+ * multiple of 64) for TTTK_EPI_PARTIAL. tile: 0 = chosen from the shape,
+ * 1..4 = 128x128x32, 128x128x64, 256x128x64, 256x256x64 (bf16). */
+ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajor, int32_t epi, const void* A,
+                     int64_t lda, const void* B, int64_t ldb, const void* B2, int32_t M, int32_t N,
+                     int32_t K, void* C, int64_t ldc, void* C2, void* C3, const void* X, float scale,
+                     int32_t kchunk, int32_t tile, void* stream);
+
+/* Sliding-window attention forward for n queries at positions pos0 .. pos0+n-1
+ * (q: [n, H, dh]) over a key/value store k, v: [Hk][cap][dh] indexed by
+ * position & (cap - 1) (cap a power of two >= 64; every key the queries see
+ * must already be stored). o: [n, H, dh]; lse: float [H, n] or NULL. */
+ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                         int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t cap, int32_t window,
+                         int64_t pos0, void* stream);
+
+/* Its backward for the query side and for the keys of the call's own
+ * positions (cached earlier keys are constants): given dO [n, H, dh] and
+ * D = rowsum(dO * O) float [H, n], writes dq float [n, H, dh] and
+ * dk, dv float [n, Hk, dh]. */
+ttt_status tttk_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const float* lse,
+                         const void* dO, const float* D, float* dq, float* dk, float* dv, int32_t n,
+                         int32_t H, int32_t Hk, int32_t dh, int32_t cap, int32_t window, int64_t pos0,
+                         void* stream);
+
+/* Fused softmax cross-entropy over V columns of fp32 logits [n, V] for the
+ * first nt rows (labels int32 [nt]): loss float [nt], dz (dtype) [n, V] =
+ * (softmax - onehot) * scale (zero rows past nt). err: device int flag. */
+ttt_status tttk_ce(int32_t dtype, const float* logits, int32_t n, int32_t nt, int32_t V,
+                   const int32_t* labels, float scale, float* loss, void* dz, int* err, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_KERNELS_H_ */

@@ -76,8 +76,16 @@ def lib() -> ctypes.CDLL:
         L.ttt_timing_enable.argtypes = [vp, ctypes.c_uint32]
         dp, lp = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)
         L.ttt_timing_read.argtypes = [vp, i32, dp, lp, dp, dp]
+        f32 = ctypes.c_float
+        L.tttk_gemm.argtypes = [i32, i32, i32, i32, vp, i64, vp, i64, vp, i32, i32, i32, vp, i64, vp, vp,
+                                vp, f32, i32, i32, vp]
+        L.tttk_attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, vp]
+        L.tttk_attn_bwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                    i64, vp]
+        L.tttk_ce.argtypes = [i32, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_get_fast_weights", "ttt_reset",
-                  "ttt_sync", "e2ttt_chunk_scan", "ttt_timing_enable", "ttt_timing_read"):
+                  "ttt_sync", "e2ttt_chunk_scan", "ttt_timing_enable", "ttt_timing_read", "tttk_gemm",
+                  "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -211,3 +219,44 @@ def e2ttt_chunk_scan(k, v, eta, beta, gamma, W, M, chunk: int, stream=None):
     if st != TTT_OK:
         raise TTTError(st, "e2ttt_chunk_scan")
     return W, M
+
+
+# ---------------------------------------------------------------- kernel level
+EPI = dict(store=0, store_f32=1, add_f32=2, swiglu=3, swiglu_bwd=4, sgd=5, partial=6)
+
+
+def _dt(t) -> int:
+    import torch
+    return 1 if t.dtype == torch.bfloat16 else 0
+
+
+def _check(st, what):
+    if st != TTT_OK:
+        raise TTTError(st, what)
+
+
+def gemm(A, B, M, N, K, epi, C, *, a_kmajor=True, b_kmajor=True, lda=None, ldb=None, ldc=None,
+         B2=None, C2=None, C3=None, X=None, scale=1.0, kchunk=0, tile=0, stream=None):
+    """One GEMM-family launch (include/ttt_kernels.h, tttk_gemm)."""
+    lda = lda if lda is not None else (K if a_kmajor else M)
+    ldb = ldb if ldb is not None else (K if b_kmajor else N)
+    ldc = ldc if ldc is not None else N
+    _check(lib().tttk_gemm(_dt(A), int(a_kmajor), int(b_kmajor), EPI[epi], _ptr(A), lda, _ptr(B), ldb,
+                           _ptr(B2), M, N, K, _ptr(C), ldc, _ptr(C2), _ptr(C3), _ptr(X), float(scale),
+                           int(kchunk), int(tile), _stream(stream)), "tttk_gemm")
+
+
+def attn_fwd(q, k, v, o, lse, n, H, Hk, dh, cap, window, pos0, stream=None):
+    _check(lib().tttk_attn_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, H, Hk, dh, cap,
+                               window, pos0, _stream(stream)), "tttk_attn_fwd")
+
+
+def attn_bwd(q, k, v, lse, dO, D, dq, dk, dv, n, H, Hk, dh, cap, window, pos0, stream=None):
+    _check(lib().tttk_attn_bwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(D), _ptr(dq),
+                               _ptr(dk), _ptr(dv), n, H, Hk, dh, cap, window, pos0, _stream(stream)),
+           "tttk_attn_bwd")
+
+
+def ce(logits, n, nt, V, labels, scale, loss, dz, err, stream=None):
+    _check(lib().tttk_ce(_dt(dz), _ptr(logits), n, nt, V, _ptr(labels), float(scale), _ptr(loss), _ptr(dz),
+                         _ptr(err), _stream(stream)), "tttk_ce")

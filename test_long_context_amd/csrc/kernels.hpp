@@ -42,7 +42,8 @@ struct GemmArgs {
   void* C3;        // SGD: low part of the re-rounded weight (bf16 split), or null
   const void* X;
   float scale;
-  int kchunk;  // split-K chunk (multiple of the K tile); <= 0 means no split
+  int kchunk;  // split-K chunk (multiple of gemm_k_granule); <= 0 means no split
+  int tile;    // tile configuration (0 = chosen from the shape)
 };
 
 hipError_t gemm(DT dt, bool a_kmajor, bool b_kmajor, Epi epi, const GemmArgs& g, hipStream_t st);
