@@ -47,10 +47,13 @@ ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajor, int32_t 
 /* Sliding-window attention forward for n queries at positions pos0 .. pos0+n-1
  * (q: [n, H, dh]) over a key/value store k, v: [Hk][cap][dh] indexed by
  * position & (cap - 1) (cap a power of two >= 64; every key the queries see
- * must already be stored). o: [n, H, dh]; lse: float [H, n] or NULL. */
-ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
-                         int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t cap, int32_t window,
-                         int64_t pos0, void* stream);
+ * must already be stored); vt (optional): the values transposed,
+ * [Hk][dh][cap]. o: [n, H, dh]; lse: float [H, n] or NULL. variant: 0 =
+ * chosen from the shape, 1 = 16x16 MFMA kernel, 2 / 3 = 32x32 MFMA kernel
+ * with 32 / 64 queries per wave (bf16, dh 64/128, needs vt). */
+ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, const void* vt,
+                         void* o, float* lse, int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t cap,
+                         int32_t window, int64_t pos0, int32_t variant, void* stream);
 
 /* Its backward for the query side and for the keys of the call's own
  * positions (cached earlier keys are constants): given dO [n, H, dh] and

@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
         f32 = ctypes.c_float
         L.tttk_gemm.argtypes = [i32, i32, i32, i32, vp, i64, vp, i64, vp, i32, i32, i32, vp, i64, vp, vp,
                                 vp, f32, i32, i32, vp]
-        L.tttk_attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, vp]
+        L.tttk_attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i32, vp]
         L.tttk_attn_bwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                     i64, vp]
         L.tttk_ce.argtypes = [i32, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
@@ -246,9 +246,9 @@ def gemm(A, B, M, N, K, epi, C, *, a_kmajor=True, b_kmajor=True, lda=None, ldb=N
                            int(kchunk), int(tile), _stream(stream)), "tttk_gemm")
 
 
-def attn_fwd(q, k, v, o, lse, n, H, Hk, dh, cap, window, pos0, stream=None):
-    _check(lib().tttk_attn_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, H, Hk, dh, cap,
-                               window, pos0, _stream(stream)), "tttk_attn_fwd")
+def attn_fwd(q, k, v, o, lse, n, H, Hk, dh, cap, window, pos0, vt=None, variant=0, stream=None):
+    _check(lib().tttk_attn_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(vt), _ptr(o), _ptr(lse), n, H, Hk, dh,
+                               cap, window, pos0, int(variant), _stream(stream)), "tttk_attn_fwd")
 
 
 def attn_bwd(q, k, v, lse, dO, D, dq, dk, dv, n, H, Hk, dh, cap, window, pos0, stream=None):

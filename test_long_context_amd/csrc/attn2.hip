@@ -1,0 +1,258 @@
+// Sliding-window attention forward, second generation (bf16, head_dim 64/128)
+// on v_mfma_f32_32x32x16_bf16.
+//
+// Same window and GQA as attn.hip. A workgroup holds 128 * QB consecutive
+// queries of one head; each wave owns 32 * QB of them, kept in registers as
+// MFMA B operands for the whole key sweep. Keys advance in tiles of 64: the
+// next tile's K ([key][dh]) and V^T ([dh][key], from the transposed value
+// ring) are loaded into registers while the current tile is consumed, then
+// stored into the other half of a double-buffered, XOR-swizzled LDS area.
+// Scores are formed transposed, S^T = K Q^T, so lane l holds 16 keys of
+// query l % 32 and the softmax statistics stay lane-local (one exchange with
+// lane l ^ 32). The P V product is O^T = V^T P^T with P^T read from the
+// score registers; its contraction slot 8 g + j maps to key 4 g + j
+// (j < 4) or 8 + 4 g + (j - 4) of each 16-key group, so V^T fragments are
+// two 8-byte LDS reads. Softmax runs in base 2 (scale folded with log2 e);
+// masks are evaluated only on tiles the window or the diagonal cuts.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ttt {
+
+namespace {
+constexpr int BKV2 = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+template <int DH>
+__device__ __forceinline__ int kswz(int key, int v) {  // K tile [64][DH], 16-byte vectors
+  return key * DH + ((v ^ (key & (DH / 8 - 1))) << 3);
+}
+__device__ __forceinline__ int vswz(int row, int v) {  // V^T tile [DH][64]
+  return row * 64 + ((v ^ (row & 7)) << 3);
+}
+}  // namespace
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes, 0x00020000);
+}
+
+template <int DH, int QB>
+__global__ void __launch_bounds__(256) attn_fwd2_kernel(AttnArgs a) {
+  constexpr int BQ = 4 * 32 * QB;
+  constexpr int KS = DH / 16;   // contraction steps over dh for S^T
+  constexpr int DB = DH / 32;   // 32-row dh blocks of O^T
+  constexpr int KV = DH / 8;    // 16-byte vectors per K row
+  constexpr int NIK = BKV2 * DH * 2 / 1024;  // DMA wave-instructions per K tile
+  constexpr int NIV = DH * BKV2 * 2 / 1024;  // ... per V^T tile
+  constexpr float RESCALE = 8.f;  // log2 headroom before O is rescaled
+  // two stages as distinct objects: the compiler then knows that the DMA
+  // into one stage never aliases reads of the other
+  __shared__ __attribute__((aligned(1024))) bf16 Ks0[BKV2 * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks1[BKV2 * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs0[DH * BKV2];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs1[DH * BKV2];
+
+  const int h = blockIdx.y, kh = h / (a.H / a.Hk);
+  const int q0 = blockIdx.x * BQ;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const bf16* Q = (const bf16*)a.q;
+  const __amdgpu_buffer_rsrc_t rk = rsrc((const bf16*)a.k + (long)kh * a.cap * DH, (uint32_t)a.cap * DH * 2);
+  const __amdgpu_buffer_rsrc_t rv = rsrc((const bf16*)a.vt + (long)kh * DH * a.cap, (uint32_t)a.cap * DH * 2);
+  const int qw = q0 + wid * 32 * QB;
+
+  bf16x8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw + qb * 32 + lr;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (row < a.n) qf[qb][ks] = *(const bf16x8*)(Q + ((long)row * a.H + h) * DH + ks * 16 + lg * 8);
+      else
+        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (bf16)0.f;
+    }
+  }
+  floatx16 o[QB][DB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[qb][db][j] = 0.f;
+  }
+
+  // positions relative to pos0 fit in 32 bits
+  const int qr_lo = q0, qr_hi = min(q0 + BQ, a.n) - 1;
+  const int k_lo = (int)((max((int64_t)0, a.pos0 + qr_lo - a.window + 1) & ~(int64_t)(BKV2 - 1)) - a.pos0);
+  const int cmask = a.cap - 1;
+  const float sc2 = a.scale * LOG2E;
+  const int wq_lo = qw, wq_hi = min(qw + 32 * QB, a.n) - 1;
+
+  // DMA of key tile kt (relative position): lane l writes the swizzled slot
+  // base + 16 l, so it fetches the logical vector belonging to that slot
+  auto dma_tile = [&](int kt, bf16* kdst, bf16* vdst) {
+    const int slot = (int)((a.pos0 + kt) & cmask);
+#pragma unroll
+    for (int i = 0; i < NIK / 4; ++i) {
+      const int j = wid + 4 * i;
+      const int key = j * (1024 / (DH * 2)) + lane / KV, p = lane % KV;
+      const int v = p ^ (key & (KV - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kdst + j * 512), 16,
+                                               (uint32_t)(((slot + key) * DH + v * 8) * 2), 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NIV / 4; ++i) {
+      const int j = wid + 4 * i;
+      const int row = j * 8 + lane / 8, p = lane % 8;
+      const int v = p ^ (row & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vdst + j * 512), 16,
+                                               (uint32_t)((row * a.cap + slot + v * 8) * 2), 0, 0, 0);
+    }
+  };
+
+  auto tile = [&](int kt, const bf16* ks_, const bf16* vs_, bf16* kn, bf16* vn) {
+    if (kt + BKV2 <= qr_hi) dma_tile(kt + BKV2, kn, vn);  // overlaps this whole tile
+    const bool any = (kt <= wq_hi) && (kt + BKV2 - 1 > wq_lo - a.window);
+    const bool full = (kt + BKV2 - 1 <= wq_lo) && (kt > wq_hi - a.window);
+    if (any) {
+      floatx16 s[2][QB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) s[kb][qb][j] = 0.f;
+#pragma unroll
+        for (int ksi = 0; ksi < KS; ++ksi) {
+          const bf16x8 kf = *(const bf16x8*)(ks_ + kswz<DH>(kb * 32 + lr, ksi * 2 + lg));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) mma32(s[kb][qb], kf, qf[qb][ksi]);
+        }
+      }
+      bf16x8 pf[2][2][QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qp = qw + qb * 32 + lr;
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float v = s[kb][qb][j] * sc2;
+            if (!full) {
+              const int kp = kt + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
+              if (!(kp <= qp && kp > qp - a.window)) v = -INFINITY;
+            }
+            s[kb][qb][j] = v;
+            tmax = fmaxf(tmax, v);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        // lazy rescale: keep the reference max unless this tile exceeds it by
+        // more than RESCALE (then p <= 2^RESCALE); wave-uniform branch
+        const bool need = tmax > m_run[qb] + RESCALE;
+        if (__any(need)) {
+          const float mnew = need ? tmax : m_run[qb];
+          const float corr = (m_run[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - mnew);
+          l_run[qb] *= corr;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[qb][db] *= corr;
+          m_run[qb] = mnew;
+        }
+        const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float p = __builtin_amdgcn_exp2f(s[kb][qb][j] - mu);
+            s[kb][qb][j] = p;
+            rs += p;
+          }
+        rs += __shfl_xor(rs, 32, 64);
+        l_run[qb] += rs;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[kb][u][qb][e] = (bf16)s[kb][qb][8 * u + e];
+      }
+      // O^T += V^T P^T over the 64 keys (4 MFMAs of 16 keys each)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int ko = kb * 32 + 16 * u + 4 * lg;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int row = db * 32 + lr;
+            const bf16x4v lo = *(const bf16x4v*)(vs_ + vswz(row, ko >> 3) + (ko & 7));
+            const bf16x4v hi = *(const bf16x4v*)(vs_ + vswz(row, (ko + 8) >> 3) + ((ko + 8) & 7));
+            bf16x8 vf;
+            vf[0] = lo[0]; vf[1] = lo[1]; vf[2] = lo[2]; vf[3] = lo[3];
+            vf[4] = hi[0]; vf[5] = hi[1]; vf[6] = hi[2]; vf[7] = hi[3];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) mma32(o[qb][db], vf, pf[kb][u][qb]);
+          }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  if (k_lo <= qr_hi) dma_tile(k_lo, Ks0, Vs0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = k_lo; kt <= qr_hi; kt += 2 * BKV2) {
+    tile(kt, Ks0, Vs0, Ks1, Vs1);
+    if (kt + BKV2 > qr_hi) break;
+    tile(kt + BKV2, Ks1, Vs1, Ks0, Vs0);
+  }
+
+  bf16* O = (bf16*)a.o;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw + qb * 32 + lr;
+    if (row >= a.n) continue;
+    const float inv = l_run[qb] > 0.f ? 1.f / l_run[qb] : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        bf16x4v w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[qb][db][4 * jg + e] * inv);
+        *(bf16x4v*)(O + ((long)row * a.H + h) * DH + db * 32 + 8 * jg + 4 * lg) = w;
+      }
+    if (lg == 0 && a.lse) a.lse[(long)h * a.n + row] = (m_run[qb] + __log2f(l_run[qb])) * LN2;
+  }
+}
+
+bool attn_fwd2_supported(DT dt, const AttnArgs& a) {
+  return dt == DT::BF16 && (a.dh == 128 || a.dh == 64) && a.vt != nullptr;
+}
+
+hipError_t attn_fwd2(DT dt, const AttnArgs& a, hipStream_t st, int qb) {
+  if (a.n <= 0) return hipSuccess;
+  if (!attn_fwd2_supported(dt, a)) return hipErrorInvalidValue;
+  // dh 128 with 64 queries per wave runs out of registers (spills) and is no
+  // faster even on long prefixes, so it is only taken on request
+  const bool big = qb == 2 || (qb == 0 && a.dh == 64 && (long)((a.n + 255) / 256) * a.H >= 512);
+  if (a.dh == 128) {
+    if (big) hipLaunchKernelGGL((attn_fwd2_kernel<128, 2>), dim3((a.n + 255) / 256, a.H), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_fwd2_kernel<128, 1>), dim3((a.n + 127) / 128, a.H), dim3(256), 0, st, a);
+  } else {
+    if (big) hipLaunchKernelGGL((attn_fwd2_kernel<64, 2>), dim3((a.n + 255) / 256, a.H), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_fwd2_kernel<64, 1>), dim3((a.n + 127) / 128, a.H), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ttt

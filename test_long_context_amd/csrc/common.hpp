@@ -100,3 +100,15 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 }  // namespace ttt
+
+namespace ttt {
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_32x32x16_bf16: lane l supplies row (A) / column (B) l % 32 and
+// contraction elements 8 (l / 32) .. + 7; accumulator element j of lane l is
+// row 8 (j / 4) + 4 (l / 32) + j % 4, column l % 32.
+__device__ __forceinline__ void mma32(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+}  // namespace ttt

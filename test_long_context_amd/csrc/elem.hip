@@ -112,7 +112,7 @@ hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const
 // at tab[pos * dh/2 + j] (built on the host from float64 angles).
 template <typename T>
 __global__ void rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, int64_t pos0,
-                                    const float2* tab, T* q, T* ks, T* vs, int cap,
+                                    const float2* tab, T* q, T* ks, T* vs, T* vts, int cap,
                                     int64_t min_pos) {
   const int t = blockIdx.x;
   const int64_t pos = pos0 + t;
@@ -140,20 +140,22 @@ __global__ void rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, 
   if (store)
     for (int i = threadIdx.x; i < Hk * dh; i += blockDim.x) {
       const int kh = i / dh, j = i % dh;
-      vs[((long)kh * cap + slot) * dh + j] = row[(H + Hk) * dh + i];
+      const T v = row[(H + Hk) * dh + i];
+      vs[((long)kh * cap + slot) * dh + j] = v;
+      if (vts) vts[((long)kh * dh + j) * cap + slot] = v;
     }
 }
 
 hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, int64_t pos0,
-                        const float2* tab, void* q, void* ks, void* vs, int cap, int64_t min_pos,
-                        hipStream_t st) {
+                        const float2* tab, void* q, void* ks, void* vs, void* vts, int cap,
+                        int64_t min_pos, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   if (dt == DT::BF16)
     hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(n), dim3(RB), 0, st, (const bf16*)qkv, n, H, Hk,
-                       dh, pos0, tab, (bf16*)q, (bf16*)ks, (bf16*)vs, cap, min_pos);
+                       dh, pos0, tab, (bf16*)q, (bf16*)ks, (bf16*)vs, (bf16*)vts, cap, min_pos);
   else
     hipLaunchKernelGGL(rope_scatter_kernel<float>, dim3(n), dim3(RB), 0, st, (const float*)qkv, n, H,
-                       Hk, dh, pos0, tab, (float*)q, (float*)ks, (float*)vs, cap, min_pos);
+                       Hk, dh, pos0, tab, (float*)q, (float*)ks, (float*)vs, (float*)vts, cap, min_pos);
   return hipGetLastError();
 }
 

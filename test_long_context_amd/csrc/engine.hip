@@ -63,6 +63,7 @@ struct ttt_ctx {
   std::vector<void*> dw12_lo, dw3_lo;        // bf16: low terms, master ~= working + low
   std::vector<void*> w0_12, w0_3;            // W0 snapshot (storage dtype, interleaved)
   std::vector<void*> kring, vring;           // per layer [Hk][cap][dh]
+  std::vector<void*> vtring;                 // per layer [Hk][dh][cap] (values transposed)
   float2* rope = nullptr;                    // [max_seq][dh/2] (cos, sin)
 
   // prefix / shared activations
@@ -290,11 +291,16 @@ ttt_status gemm_nn_split(ttt_ctx* c, int kind, const void* A, long lda, const vo
     if (r_ != TTT_OK) return r_;    \
   } while (0)
 
+hipError_t attn_fwd_any(DT dt, const AttnArgs& a, hipStream_t st) {
+  return attn_fwd2_supported(dt, a) ? attn_fwd2(dt, a, st) : attn_fwd(dt, a, st);
+}
+
 AttnArgs attn_args(ttt_ctx* c, int l, const void* q, void* o, float* lse, int n, int64_t p0) {
   AttnArgs a{};
   a.q = q;
   a.k = c->kring[l];
   a.v = c->vring[l];
+  a.vt = c->vtring[l];
   a.o = o;
   a.lse = lse;
   a.n = n;
@@ -321,9 +327,9 @@ ttt_status run_prefix(ttt_ctx* c, const int32_t* tok, int64_t T, hipStream_t st)
       TCALL(KC_GP, gfl(n, QKV, d), 0,
             gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
       TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, p0, c->rope, c->qb, c->kring[l],
-                                      c->vring[l], (int)c->cap, 0, st));
+                                      c->vring[l], c->vtring[l], (int)c->cap, 0, st));
       AttnArgs a = attn_args(c, l, c->qb, c->ob, nullptr, n, p0);
-      TCALL(KC_AP, 4.0 * H * dh * window_pairs(p0, n, c->k), 0, attn_fwd(c->dt, a, st));
+      TCALL(KC_AP, 4.0 * H * dh * window_pairs(p0, n, c->k), 0, attn_fwd_any(c->dt, a, st));
       TCALL(KC_GP, gfl(n, d, H * dh), 0,
             gemm(c->dt, true, true, Epi::ADD_F32, ga(c->ob, (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, h, d), st));
       TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, h, c->mlp_norm[l], n, d, eps, c->xn, c->rbuf, st));
@@ -352,9 +358,9 @@ ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipSt
       TCALL(KC_GL, gfl(n, QKV, d), 0,
             gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
       TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, a0, c->rope, c->q_l[i], c->kring[l],
-                                      c->vring[l], (int)c->cap, 0, st));
+                                      c->vring[l], c->vtring[l], (int)c->cap, 0, st));
       AttnArgs a = attn_args(c, l, c->q_l[i], c->o_l[i], c->lse[i], n, a0);
-      TCALL(KC_AL, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_fwd(c->dt, a, st));
+      TCALL(KC_AL, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_fwd_any(c->dt, a, st));
       TCALL(KC_GL, gfl(n, d, H * dh), 0,
             gemm(c->dt, true, true, Epi::ADD_F32, ga(c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, hl, d), st));
       // static MLP sublayer
@@ -518,6 +524,7 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   c->w3.resize(L);
   c->kring.resize(L);
   c->vring.resize(L);
+  c->vtring.resize(L);
   for (int l = 0; l < L && ok; ++l) {
     Af(&c->attn_norm[l], d);
     Af(&c->mlp_norm[l], d);
@@ -527,6 +534,7 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     A(&c->w3[l], (size_t)d * c->F * es);
     A(&c->kring[l], (size_t)c->Hk * c->cap * c->dh * es);
     A(&c->vring[l], (size_t)c->Hk * c->cap * c->dh * es);
+    if (c->dt == DT::BF16) A(&c->vtring[l], (size_t)c->Hk * c->cap * c->dh * es);
   }
   c->dyn_norm.resize(nd);
   c->m12.resize(nd);
@@ -656,6 +664,7 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     UP(hipMemcpyAsync(c->w3[l], w->w3[l], (size_t)d * c->F * es, D2D, st));
     UP(fill_zero_bytes(c->kring[l], (size_t)c->Hk * c->cap * c->dh * es, st));
     UP(fill_zero_bytes(c->vring[l], (size_t)c->Hk * c->cap * c->dh * es, st));
+    if (c->vtring[l]) UP(fill_zero_bytes(c->vtring[l], (size_t)c->Hk * c->cap * c->dh * es, st));
   }
   for (int i = 0; i < nd; ++i) {
     UP(cast_from(c->dt, w->dyn_norm[i], c->dyn_norm[i], d, st));

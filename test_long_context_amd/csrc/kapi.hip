@@ -66,12 +66,12 @@ ttt_status attn_check(int32_t dtype, int32_t n, int32_t H, int32_t Hk, int32_t d
 }
 }  // namespace
 
-extern "C" ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o,
-                                    float* lse, int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t cap,
-                                    int32_t window, int64_t pos0, void* stream) {
+extern "C" ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, const void* vt,
+                                    void* o, float* lse, int32_t n, int32_t H, int32_t Hk, int32_t dh,
+                                    int32_t cap, int32_t window, int64_t pos0, int32_t variant, void* stream) {
   ttt_status s = attn_check(dtype, n, H, Hk, dh, cap, window, pos0);
   if (s != TTT_OK) return s;
-  if (!q || !k || !v || !o) return TTT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || variant < 0 || variant > 3) return TTT_ERR_INVALID_ARG;
   AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -86,7 +86,15 @@ extern "C" ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k,
   a.window = window;
   a.pos0 = pos0;
   a.scale = 1.f / sqrtf((float)dh);
-  return attn_fwd(to_dt(dtype), a, (hipStream_t)stream) == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+  a.vt = vt;
+  hipError_t e;
+  if (variant == 1 || (variant == 0 && !attn_fwd2_supported(to_dt(dtype), a))) {
+    e = attn_fwd(to_dt(dtype), a, (hipStream_t)stream);
+  } else {
+    if (!attn_fwd2_supported(to_dt(dtype), a)) return TTT_ERR_UNSUPPORTED;
+    e = attn_fwd2(to_dt(dtype), a, (hipStream_t)stream, variant == 0 ? 0 : variant - 1);
+  }
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
 extern "C" ttt_status tttk_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v,

@@ -67,8 +67,8 @@ hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const
 // store [Hk][cap][dh] at slot (pos & (cap - 1)) for rows whose position is
 // >= min_store_pos; optionally also into a full-length buffer.
 hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, int64_t pos0,
-                        const float2* rope_tab, void* q, void* kstore, void* vstore, int cap,
-                        int64_t min_store_pos, hipStream_t st);
+                        const float2* rope_tab, void* q, void* kstore, void* vstore, void* vtstore,
+                        int cap, int64_t min_store_pos, hipStream_t st);
 // dQKV (T) [n, (H+2Hk) dh] from dq [n, H dh] (float), dk, dv [n, Hk dh]
 // (float): inverse rotation of dq and dk.
 hipError_t rope_bwd_pack(DT dt, const float* dq, const float* dk, const float* dv, int n, int H,
@@ -94,6 +94,7 @@ struct AttnArgs {
   const void* q;      // [n, H, dh] (T) queries at positions pos0 + i
   const void* k;      // key store [Hk][cap][dh] (T)
   const void* v;      // value store [Hk][cap][dh] (T)
+  const void* vt;     // transposed value store [Hk][dh][cap] (T), or null
   void* o;            // [n, H, dh] (T)
   float* lse;         // [H][n] (may be null)
   int n, H, Hk, dh, cap, window;
@@ -107,6 +108,10 @@ struct AttnArgs {
   float* dv;
 };
 hipError_t attn_fwd(DT dt, const AttnArgs& a, hipStream_t st);
+// Second-generation forward (bf16, head_dim 64/128, needs a.vt).
+bool attn_fwd2_supported(DT dt, const AttnArgs& a);
+// qb: 0 = chosen from the shape, 1 / 2 = 32 / 64 queries per wave.
+hipError_t attn_fwd2(DT dt, const AttnArgs& a, hipStream_t st, int qb = 0);
 hipError_t attn_bwd_dq(DT dt, const AttnArgs& a, hipStream_t st);
 hipError_t attn_bwd_dkdv(DT dt, const AttnArgs& a, hipStream_t st);
 
