@@ -37,8 +37,11 @@ typedef enum {
  * B2 (optional, bf16, NT layout, SWIGLU/ADD_F32 only) is a second term
  * added to B. The contiguous dimension of A and B must be a multiple of 8
  * and the pointers 16-byte aligned. kchunk > 0 splits K into chunks (a
- * multiple of 64) for TTTK_EPI_PARTIAL. tile: 0 = chosen from the shape,
- * 1..4 = 128x128x32, 128x128x64, 256x128x64, 256x256x64 (bf16). */
+ * multiple of 64) for TTTK_EPI_PARTIAL. tile (bf16; fp32 always uses
+ * 64x64): 0 = chosen from the shape, 1 = 128x128 (4 waves of 64x64),
+ * 2 = 256x128 (4 of 128x64), 3 = 256x128 (8 of 64x64), 4 = 256x256 (4 of
+ * 128x128), 5 = 256x256 (8 of 128x64), 6 = 128x256 (4 of 64x128); K steps
+ * of 64. */
 ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajor, int32_t epi, const void* A,
                      int64_t lda, const void* B, int64_t ldb, const void* B2, int32_t M, int32_t N,
                      int32_t K, void* C, int64_t ldc, void* C2, void* C3, const void* X, float scale,
@@ -58,11 +61,19 @@ ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void
 /* Its backward for the query side and for the keys of the call's own
  * positions (cached earlier keys are constants): given dO [n, H, dh] and
  * D = rowsum(dO * O) float [H, n], writes dq float [n, H, dh] and
- * dk, dv float [n, Hk, dh]. */
+ * dk, dv float [n, Hk, dh]. variant: 0 = chosen from the shape, 1 = 16x16
+ * MFMA kernels, 2 = 32x32 MFMA kernels (bf16, dh 64/128), which produce
+ * partial sums in work (device memory of tttk_attn_bwd_workspace() bytes,
+ * owned by the caller; may be NULL when that is 0) and add them into dq, dk,
+ * dv. */
 ttt_status tttk_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const float* lse,
                          const void* dO, const float* D, float* dq, float* dk, float* dv, int32_t n,
                          int32_t H, int32_t Hk, int32_t dh, int32_t cap, int32_t window, int64_t pos0,
-                         void* stream);
+                         int32_t variant, void* work, void* stream);
+
+/* Bytes of work tttk_attn_bwd needs for this shape and variant. */
+int64_t tttk_attn_bwd_workspace(int32_t dtype, int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t window,
+                                int32_t variant);
 
 /* Fused softmax cross-entropy over V columns of fp32 logits [n, V] for the
  * first nt rows (labels int32 [nt]): loss float [nt], dz (dtype) [n, V] =

@@ -81,7 +81,9 @@ def lib() -> ctypes.CDLL:
                                 vp, f32, i32, i32, vp]
         L.tttk_attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i32, vp]
         L.tttk_attn_bwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                    i64, vp]
+                                    i64, i32, vp, vp]
+        L.tttk_attn_bwd_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.tttk_attn_bwd_workspace.restype = i64
         L.tttk_ce.argtypes = [i32, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_get_fast_weights", "ttt_reset",
                   "ttt_sync", "e2ttt_chunk_scan", "ttt_timing_enable", "ttt_timing_read", "tttk_gemm",
@@ -112,7 +114,11 @@ def make_config(c: dict, max_seq: Optional[int] = None) -> Config:
 
 
 def _ptr(t) -> int:
-    return 0 if t is None else t.data_ptr()
+    if t is None:
+        return 0
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
 
 
 def _arr(ptrs):
@@ -251,9 +257,19 @@ def attn_fwd(q, k, v, o, lse, n, H, Hk, dh, cap, window, pos0, vt=None, variant=
                                cap, window, pos0, int(variant), _stream(stream)), "tttk_attn_fwd")
 
 
-def attn_bwd(q, k, v, lse, dO, D, dq, dk, dv, n, H, Hk, dh, cap, window, pos0, stream=None):
+def attn_bwd_workspace(dtype, n, H, Hk, dh, window, variant=0):
+    """Bytes of device workspace tttk_attn_bwd needs (include/ttt_kernels.h);
+    dtype is a torch dtype."""
+    import torch
+    code = 1 if dtype == torch.bfloat16 else 0
+    return int(lib().tttk_attn_bwd_workspace(code, n, H, Hk, dh, window, int(variant)))
+
+
+def attn_bwd(q, k, v, lse, dO, D, dq, dk, dv, n, H, Hk, dh, cap, window, pos0, variant=0, work=None,
+             stream=None):
     _check(lib().tttk_attn_bwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(D), _ptr(dq),
-                               _ptr(dk), _ptr(dv), n, H, Hk, dh, cap, window, pos0, _stream(stream)),
+                               _ptr(dk), _ptr(dv), n, H, Hk, dh, cap, window, pos0, int(variant), _ptr(work),
+                               _stream(stream)),
            "tttk_attn_bwd")
 
 

@@ -1,0 +1,409 @@
+// Sliding-window attention backward, second generation (bf16, head_dim
+// 64/128) on v_mfma_f32_32x32x16_bf16.
+//
+// The query-side gradient over the whole window (cached keys are constants)
+// and the key/value gradients of the call's own positions, as in attn.hip:
+//   P = exp(scale q.k - lse),  dP = dO . v,  dS = P (dP - D),  D = rowsum(dO O)
+//   dq_i = scale sum_t dS[i, t] k_t;  dk_t = scale sum_i dS[i, t] q_i;  dv_t = sum_i P[i, t] dO_i.
+//
+// dQ: a workgroup holds 128 consecutive queries of one head (32 per wave,
+// kept in registers with their dO rows as MFMA B operands); key tiles of 64
+// stream through a double-buffered, XOR-swizzled LDS area by direct-to-LDS
+// loads. S^T = K Q^T and dP^T = V dO^T come out with one query per lane
+// column, so the softmax terms are lane-local; dQ^T = K^T dS^T takes dS^T
+// straight from those registers and K^T from the same K tile through the
+// CDNA4 transposing LDS read (no transposed key store needed). The key range
+// of a query block can be split over several workgroups (grid z), each
+// writing its own partial dq; the consumer adds the parts in a fixed order.
+//
+// dK, dV: a workgroup holds 128 keys of one key head (32 per wave, K and V
+// rows in registers) for one query head of the group (grid z); query tiles of
+// 64 (Q and dO rows, plus their lse and D) stream through LDS. S = Q K^T and
+// dP = dO V^T have one key per lane column; dV^T = dO^T P and dK^T = Q^T dS
+// read dO^T and Q^T through the transposing LDS read. Each query head writes
+// its own partial dk, dv.
+//
+// Contraction slots of the P / dS operands follow the accumulator layout:
+// slot 8 g + e of lane group g (= lane / 32) is row 16 u + 4 g + e (e < 4) or
+// 16 u + 8 + 4 g + (e - 4) of the 32-row block, for the 16-row step u.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ttt {
+
+namespace {
+constexpr int BT = 64;  // key tile (dQ) / query tile (dK, dV)
+constexpr float LOG2E_B = 1.4426950408889634f;
+
+typedef __attribute__((address_space(3))) void* ldsv_t;
+typedef short shortx4b __attribute__((ext_vector_type(4)));
+typedef short shortx8b __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) shortx4b* lds4_t;
+
+// [rows][DH] bf16 tile: 16-byte vector v of row r at slot v ^ (r % (DH / 8)).
+template <int DH>
+__device__ __forceinline__ int rswz(int r, int v) {
+  return r * DH + ((v ^ (r & (DH / 8 - 1))) << 3);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(const void* p, uint64_t nbytes) {
+  const uint32_t n = nbytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)nbytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+// MFMA operand of the transposed tile: lane l takes column c0 + l % 32 and
+// the permuted contraction rows rb + 4 (l / 32) + e and rb + 8 + 4 (l / 32) + e.
+// ds_read_b64_tr_b16: inside a group of 16 lanes, result lane i element e is
+// element i % 4 of what source lane 4 e + i / 4 addressed; source lane j
+// addresses (row base + j / 4, column c + 4 (j % 4)).
+template <int DH>
+__device__ __forceinline__ bf16x8 ld_tr_op(const bf16* tile, int rb, int c0, int lane) {
+  const int hgrp = lane >> 4, j = lane & 15;
+  const int row = rb + 4 * (hgrp >> 1) + (j >> 2);
+  const int col = c0 + 16 * (hgrp & 1) + 4 * (j & 3);
+  const bf16* p0 = tile + rswz<DH>(row, col >> 3) + (col & 7);
+  const bf16* p1 = tile + rswz<DH>(row + 8, col >> 3) + (col & 7);
+  const shortx4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4_t)p0);
+  const shortx4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4_t)p1);
+  const shortx8b w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ void pack_slots(bf16x8 (&f)[2], const floatx16& x) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[u][e] = (bf16)x[8 * u + e];
+}
+}  // namespace
+
+// ------------------------------------------------------------------- dQ
+template <int DH>
+__global__ void __launch_bounds__(256) attn_bwd_dq2_kernel(AttnArgs a, int ksplit) {
+  constexpr int KS = DH / 16, DB = DH / 32, KV = DH / 8;
+  constexpr int NI = BT * DH * 2 / 1024;  // DMA wave-instructions per tile
+  __shared__ __attribute__((aligned(1024))) bf16 Ks0[BT * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks1[BT * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs0[BT * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs1[BT * DH];
+
+  const int h = blockIdx.y, kh = h / (a.H / a.Hk), z = blockIdx.z;
+  const int q0 = blockIdx.x * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const bf16* Q = (const bf16*)a.q;
+  const bf16* dO = (const bf16*)a.dO;
+  const __amdgpu_buffer_rsrc_t rk = rsrc_b((const bf16*)a.k + (long)kh * a.cap * DH, (uint64_t)a.cap * DH * 2);
+  const __amdgpu_buffer_rsrc_t rv = rsrc_b((const bf16*)a.v + (long)kh * a.cap * DH, (uint64_t)a.cap * DH * 2);
+  const int qw = q0 + wid * 32;
+  const int row = qw + lr;
+
+  bf16x8 qf[KS], df[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (row < a.n) {
+      qf[ks] = *(const bf16x8*)(Q + ((long)row * a.H + h) * DH + ks * 16 + lg * 8);
+      df[ks] = *(const bf16x8*)(dO + ((long)row * a.H + h) * DH + ks * 16 + lg * 8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qf[ks][e] = (bf16)0.f;
+        df[ks][e] = (bf16)0.f;
+      }
+    }
+  }
+  const float lse2 = row < a.n ? a.lse[(long)h * a.n + row] * LOG2E_B : 0.f;
+  const float Dq = row < a.n ? a.D[(long)h * a.n + row] : 0.f;
+  floatx16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
+
+  // positions relative to pos0 fit in 32 bits
+  const int qr_hi = min(q0 + 128, a.n) - 1;
+  const int k_lo = (int)((max((int64_t)0, a.pos0 + q0 - a.window + 1) & ~(int64_t)(BT - 1)) - a.pos0);
+  const int ntile = (qr_hi - k_lo) / BT + 1;
+  const int per = (ntile + ksplit - 1) / ksplit;
+  const int t_beg = z * per, t_end = min(ntile, t_beg + per);
+  const int cmask = a.cap - 1;
+  const float sc2 = a.scale * LOG2E_B;
+  const int wq_lo = qw, wq_hi = min(qw + 32, a.n) - 1;
+
+  auto dma_tile = [&](int kt, bf16* kdst, bf16* vdst) {
+    const int slot = (int)((a.pos0 + kt) & cmask);
+#pragma unroll
+    for (int i = 0; i < NI / 4; ++i) {
+      const int jj = wid + 4 * i;
+      const int key = jj * (1024 / (DH * 2)) + lane / KV, p = lane % KV;
+      const int v = p ^ (key & (KV - 1));
+      const uint32_t off = (uint32_t)(((slot + key) * DH + v * 8) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (ldsv_t)(kdst + jj * 512), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ldsv_t)(vdst + jj * 512), 16, off, 0, 0, 0);
+    }
+  };
+
+  auto tile = [&](int t, const bf16* ks_, const bf16* vs_, bf16* kn, bf16* vn) {
+    const int kt = k_lo + t * BT;
+    if (t + 1 < t_end) dma_tile(kt + BT, kn, vn);
+    const bool any = wq_lo < a.n && (kt <= wq_hi) && (kt + BT - 1 > wq_lo - a.window);
+    const bool full = (kt + BT - 1 <= wq_lo) && (kt > wq_hi - a.window);
+    if (any) {
+      floatx16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          s[kb][j] = 0.f;
+          dp[kb][j] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int o = rswz<DH>(kb * 32 + lr, ks * 2 + lg);
+          const bf16x8 kf = *(const bf16x8*)(ks_ + o);
+          const bf16x8 vf = *(const bf16x8*)(vs_ + o);
+          mma32(s[kb], kf, qf[ks]);
+          mma32(dp[kb], vf, df[ks]);
+        }
+      }
+      bf16x8 dsf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float p = __builtin_amdgcn_exp2f(s[kb][j] * sc2 - lse2);
+          if (!full) {
+            const int kp = kt + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
+            if (!(kp <= row && kp > row - a.window)) p = 0.f;
+          }
+          s[kb][j] = p * (dp[kb][j] - Dq);
+        }
+        pack_slots(dsf[kb], s[kb]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) mma32(acc[db], ld_tr_op<DH>(ks_, kb * 32 + 16 * u, db * 32, lane), dsf[kb][u]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  if (t_beg < t_end) dma_tile(k_lo + t_beg * BT, Ks0, Vs0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = t_beg; t < t_end; t += 2) {
+    tile(t, Ks0, Vs0, Ks1, Vs1);
+    if (t + 1 >= t_end) break;
+    tile(t + 1, Ks1, Vs1, Ks0, Vs0);
+  }
+
+  if (row < a.n) {
+    float* out = a.dq + (long)z * a.n * a.H * DH + ((long)row * a.H + h) * DH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        floatx4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * jg + e] * a.scale;
+        *(floatx4*)(out + db * 32 + 8 * jg + 4 * lg) = w;
+      }
+  }
+}
+
+// --------------------------------------------------------------- dK, dV
+template <int DH>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
+  constexpr int KS = DH / 16, DB = DH / 32, KV = DH / 8;
+  constexpr int NI = BT * DH * 2 / 1024;
+  __shared__ __attribute__((aligned(1024))) bf16 Qs0[BT * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 Qs1[BT * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 Os0[BT * DH];
+  __shared__ __attribute__((aligned(1024))) bf16 Os1[BT * DH];
+  __shared__ float ls0[BT], ls1[BT], Ds0[BT], Ds1[BT];
+
+  const int grp = a.H / a.Hk;
+  const int kh = blockIdx.y, hq = blockIdx.z, h = kh * grp + hq;
+  const int k0 = blockIdx.x * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int kw = k0 + wid * 32;
+  const int key = kw + lr;  // local index of this lane's key
+  const int cmask = a.cap - 1;
+  const bf16* Kst = (const bf16*)a.k + (long)kh * a.cap * DH;
+  const bf16* Vst = (const bf16*)a.v + (long)kh * a.cap * DH;
+
+  bf16x8 kf[KS], vf[KS];
+  {
+    const long slot = (long)((a.pos0 + key) & cmask);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (key < a.n) {
+        kf[ks] = *(const bf16x8*)(Kst + slot * DH + ks * 16 + lg * 8);
+        vf[ks] = *(const bf16x8*)(Vst + slot * DH + ks * 16 + lg * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kf[ks][e] = (bf16)0.f;
+          vf[ks][e] = (bf16)0.f;
+        }
+      }
+    }
+  }
+  floatx16 accK[DB], accV[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      accK[db][j] = 0.f;
+      accV[db][j] = 0.f;
+    }
+
+  const __amdgpu_buffer_rsrc_t rq = rsrc_b(a.q, (uint64_t)a.n * a.H * DH * 2);
+  const __amdgpu_buffer_rsrc_t ro = rsrc_b(a.dO, (uint64_t)a.n * a.H * DH * 2);
+  const int q_end = (int)min((int64_t)a.n, (int64_t)k0 + 127 + a.window);  // exclusive
+  const float sc2 = a.scale * LOG2E_B;
+  const int wk_lo = kw, wk_hi = min(kw + 32, a.n) - 1;
+
+  auto dma_tile = [&](int qt, bf16* qdst, bf16* odst, float* lsd, float* Dd) {
+#pragma unroll
+    for (int i = 0; i < NI / 4; ++i) {
+      const int jj = wid + 4 * i;
+      const int r = jj * (1024 / (DH * 2)) + lane / KV, p = lane % KV;
+      const int v = p ^ (r & (KV - 1));
+      const int qrow = qt + r;
+      const uint32_t off = qrow < a.n ? (uint32_t)((((long)qrow * a.H + h) * DH + v * 8) * 2) : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (ldsv_t)(qdst + jj * 512), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (ldsv_t)(odst + jj * 512), 16, off, 0, 0, 0);
+    }
+    if (tid < BT) {
+      const int qrow = qt + tid;
+      lsd[tid] = qrow < a.n ? a.lse[(long)h * a.n + qrow] * LOG2E_B : 0.f;
+      Dd[tid] = qrow < a.n ? a.D[(long)h * a.n + qrow] : 0.f;
+    }
+  };
+
+  auto tile = [&](int qt, const bf16* qs_, const bf16* os_, const float* lsc, const float* Dc, bf16* qn, bf16* on,
+                  float* lsn, float* Dn) {
+    if (qt + BT < q_end) dma_tile(qt + BT, qn, on, lsn, Dn);
+    // key t sees query i iff t <= i < t + window
+    const bool any = wk_lo < a.n && (qt + BT - 1 >= wk_lo) && (qt <= wk_hi + a.window - 1);
+    const bool full = (qt >= wk_hi) && (qt + BT - 1 <= wk_lo + a.window - 1) && (qt + BT <= a.n);
+    if (any) {
+      floatx16 s[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          s[qb][j] = 0.f;
+          dp[qb][j] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int o = rswz<DH>(qb * 32 + lr, ks * 2 + lg);
+          mma32(s[qb], *(const bf16x8*)(qs_ + o), kf[ks]);
+          mma32(dp[qb], *(const bf16x8*)(os_ + o), vf[ks]);
+        }
+      }
+      bf16x8 pb[2][2], sb[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        floatx16 ds;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int ql = qb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
+          float p = __builtin_amdgcn_exp2f(s[qb][j] * sc2 - lsc[ql]);
+          if (!full) {
+            const int qi = qt + ql;
+            if (!(qi >= key && qi < key + a.window && qi < a.n && key < a.n)) p = 0.f;
+          }
+          s[qb][j] = p;
+          ds[j] = p * (dp[qb][j] - Dc[ql]);
+        }
+        pack_slots(pb[qb], s[qb]);
+        pack_slots(sb[qb], ds);
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            mma32(accV[db], ld_tr_op<DH>(os_, qb * 32 + 16 * u, db * 32, lane), pb[qb][u]);
+            mma32(accK[db], ld_tr_op<DH>(qs_, qb * 32 + 16 * u, db * 32, lane), sb[qb][u]);
+          }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  if (k0 < q_end) dma_tile(k0, Qs0, Os0, ls0, Ds0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int qt = k0; qt < q_end; qt += 2 * BT) {
+    tile(qt, Qs0, Os0, ls0, Ds0, Qs1, Os1, ls1, Ds1);
+    if (qt + BT >= q_end) break;
+    tile(qt + BT, Qs1, Os1, ls1, Ds1, Qs0, Os0, ls0, Ds0);
+  }
+
+  if (key < a.n) {
+    const long base = (long)hq * a.n * a.Hk * DH + ((long)key * a.Hk + kh) * DH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        floatx4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = accK[db][4 * jg + e] * a.scale;
+          wv[e] = accV[db][4 * jg + e];
+        }
+        *(floatx4*)(a.dk + base + db * 32 + 8 * jg + 4 * lg) = wk;
+        *(floatx4*)(a.dv + base + db * 32 + 8 * jg + 4 * lg) = wv;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+bool attn_bwd2_supported(DT dt, const AttnArgs& a) {
+  return dt == DT::BF16 && (a.dh == 128 || a.dh == 64);
+}
+
+int attn_bwd2_dq_parts(const AttnArgs& a) {
+  // enough workgroups to cover the CUs twice, at least 8 key tiles each
+  const long base = (long)((a.n + 127) / 128) * a.H;
+  const long tiles = (a.window + 128 + BT - 1) / BT + 1;
+  long s = (512 + base - 1) / base;
+  const long cap_t = tiles / 8 > 1 ? tiles / 8 : 1;
+  if (s > cap_t) s = cap_t;
+  if (s > 4) s = 4;
+  return s < 1 ? 1 : (int)s;
+}
+
+int attn_bwd2_kv_parts(const AttnArgs& a) { return a.H / a.Hk; }
+
+hipError_t attn_bwd_dq2(DT dt, const AttnArgs& a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  if (!attn_bwd2_supported(dt, a)) return hipErrorInvalidValue;
+  const int parts = attn_bwd2_dq_parts(a);
+  const dim3 grid((a.n + 127) / 128, a.H, parts);
+  if (a.dh == 128) hipLaunchKernelGGL(attn_bwd_dq2_kernel<128>, grid, dim3(256), 0, st, a, parts);
+  else hipLaunchKernelGGL(attn_bwd_dq2_kernel<64>, grid, dim3(256), 0, st, a, parts);
+  return hipGetLastError();
+}
+
+hipError_t attn_bwd_dkdv2(DT dt, const AttnArgs& a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  if (!attn_bwd2_supported(dt, a)) return hipErrorInvalidValue;
+  const dim3 grid((a.n + 127) / 128, a.Hk, a.H / a.Hk);
+  if (a.dh == 128) hipLaunchKernelGGL(attn_bwd_dkdv2_kernel<128>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(attn_bwd_dkdv2_kernel<64>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

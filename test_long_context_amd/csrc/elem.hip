@@ -5,6 +5,8 @@
 // each element once, with 16-byte accesses where the layout allows.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -161,34 +163,62 @@ hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, in
 
 // Transpose of the rotation (rotation by -angle) for dq, dk; dv copied.
 template <typename T>
-__global__ void rope_bwd_kernel(const float* dq, const float* dk, const float* dv, int H, int Hk,
-                                int dh, int64_t pos0, const float2* tab, T* out) {
+__global__ void rope_bwd_kernel(const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
+                                int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, T* out) {
   const int t = blockIdx.x;
   const int half = dh / 2;
   const int W = (H + 2 * Hk) * dh;
+  const long qstride = (long)n * H * dh, kstride = (long)n * Hk * dh;
   const float2* tb = tab + (pos0 + t) * half;
+  // partial sums (query-side key splits, per-query-head key gradients) are
+  // added in a fixed order
   for (int i = threadIdx.x; i < (H + Hk) * half; i += blockDim.x) {
     const int hh = i / half, j = i % half;
     const float2 cs = tb[j];
-    const float* src = hh < H ? dq + ((long)t * H + hh) * dh : dk + ((long)t * Hk + (hh - H)) * dh;
-    const float g1 = src[j], g2 = src[j + half];
+    const bool isq = hh < H;
+    const float* src = isq ? dq + ((long)t * H + hh) * dh : dk + ((long)t * Hk + (hh - H)) * dh;
+    const int np = isq ? dq_parts : kv_parts;
+    const long ps = isq ? qstride : kstride;
+    float g1 = 0.f, g2 = 0.f;
+    for (int p = 0; p < np; ++p) {
+      g1 += src[p * ps + j];
+      g2 += src[p * ps + j + half];
+    }
     out[(long)t * W + hh * dh + j] = from_f<T>(g1 * cs.x + g2 * cs.y);
     out[(long)t * W + hh * dh + j + half] = from_f<T>(-g1 * cs.y + g2 * cs.x);
   }
-  for (int i = threadIdx.x; i < Hk * dh; i += blockDim.x)
-    out[(long)t * W + (H + Hk) * dh + i] = from_f<T>(dv[(long)t * Hk * dh + i]);
+  for (int i = threadIdx.x; i < Hk * dh; i += blockDim.x) {
+    float g = 0.f;
+    for (int p = 0; p < kv_parts; ++p) g += dv[p * kstride + (long)t * Hk * dh + i];
+    out[(long)t * W + (H + Hk) * dh + i] = from_f<T>(g);
+  }
 }
 
-hipError_t rope_bwd_pack(DT dt, const float* dq, const float* dk, const float* dv, int n, int H,
-                         int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
+hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
+                         int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
                          hipStream_t st) {
   if (n <= 0) return hipSuccess;
   if (dt == DT::BF16)
-    hipLaunchKernelGGL(rope_bwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, dq, dk, dv, H, Hk, dh, pos0, tab,
-                       (bf16*)dqkv);
+    hipLaunchKernelGGL(rope_bwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H, Hk,
+                       dh, pos0, tab, (bf16*)dqkv);
   else
-    hipLaunchKernelGGL(rope_bwd_kernel<float>, dim3(n), dim3(RB), 0, st, dq, dk, dv, H, Hk, dh, pos0, tab,
-                       (float*)dqkv);
+    hipLaunchKernelGGL(rope_bwd_kernel<float>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H,
+                       Hk, dh, pos0, tab, (float*)dqkv);
+  return hipGetLastError();
+}
+
+__global__ void sum_parts_kernel(const float* parts, int nparts, long count, float* dst) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < count; i += (long)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int p = 0; p < nparts; ++p) s += parts[p * count + i];
+    dst[i] = s;
+  }
+}
+
+hipError_t sum_parts_f32(const float* parts, int nparts, long count, float* dst, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  const long blocks = std::min((count + 255) / 256, 4096L);
+  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)blocks), dim3(256), 0, st, parts, nparts, count, dst);
   return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ struct ttt_ctx {
   int max_split = 1;
   void* dO = nullptr;                        // [b, H dh]
   float* Dbuf = nullptr;                     // [H, b]
-  float* dq = nullptr;                       // [b, H dh]
+  float* dq = nullptr;                       // [parts][b, H dh] (partial sums)
   float* dk = nullptr;                       // [b, Hk dh]
   float* dv = nullptr;
   void* dqkv = nullptr;                      // [b, QKV]
@@ -272,14 +272,23 @@ GemmArgs ga(const void* A, long lda, const void* B, long ldb, int M, int N, int 
 // *nsplit receives the number of partial slices written.
 ttt_status gemm_nn_split(ttt_ctx* c, int kind, const void* A, long lda, const void* B, long ldb, int M,
                          int N, int K, float* part, int* nsplit, hipStream_t st) {
-  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  int s = std::min(choose_split(tiles, K), c->max_split);
+  // bf16: 256 x 256 tiles, K split so that the grid is about one workgroup
+  // per CU (measured at the 3B dX shapes: better than more, smaller tiles)
   const int gran = gemm_k_granule(c->dt);
+  int s;
+  if (c->dt == DT::BF16) {
+    const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    s = std::max(1, std::min(256 / tiles, K / 512));
+  } else {
+    s = choose_split(((M + 127) / 128) * ((N + 127) / 128), K);
+  }
+  s = std::min(s, c->max_split);
   int chunk = (K + s - 1) / s;
   chunk = (chunk + gran - 1) / gran * gran;
   s = (K + chunk - 1) / chunk;
   GemmArgs g = ga(A, lda, B, ldb, M, N, K, part, N);
   g.kchunk = chunk;
+  if (c->dt == DT::BF16) g.tile = 5;
   *nsplit = s;
   TCALL(kind, gfl(M, N, K), 0, gemm(c->dt, true, false, Epi::PARTIAL, g, st));
   return TTT_OK;
@@ -443,9 +452,17 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       a.dq = c->dq;
       a.dk = c->dk;
       a.dv = c->dv;
-      TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq(c->dt, a, st));
-      TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv(c->dt, a, st));
-      TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, c->dq, c->dk, c->dv, n, H, Hk, dh, a0, c->rope, c->dqkv, st));
+      int qp = 1, kp = 1;
+      if (attn_bwd2_supported(c->dt, a)) {
+        qp = attn_bwd2_dq_parts(a);
+        kp = attn_bwd2_kv_parts(a);
+        TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq2(c->dt, a, st));
+        TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv2(c->dt, a, st));
+      } else {
+        TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq(c->dt, a, st));
+        TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv(c->dt, a, st));
+      }
+      TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, c->dq, qp, c->dk, c->dv, kp, n, H, Hk, dh, a0, c->rope, c->dqkv, st));
       RUN(gemm_nn_split(c, KC_GL, c->dqkv, QKV, c->wqkv[l], d, n, d, QKV, c->part, &ns, st));
       TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->gh_t, 1, st));
     }
@@ -612,9 +629,11 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   Af(&c->part, (size_t)c->max_split * b * d);
   A(&c->dO, (size_t)b * c->H * c->dh * es);
   Af(&c->Dbuf, (size_t)c->H * b);
-  Af(&c->dq, (size_t)b * c->H * c->dh);
-  Af(&c->dk, (size_t)b * c->Hk * c->dh);
-  Af(&c->dv, (size_t)b * c->Hk * c->dh);
+  // room for the partial sums of the second-generation backward (at most 4
+  // key splits of dq; one dk / dv part per query head of a group)
+  Af(&c->dq, (size_t)4 * b * c->H * c->dh);
+  Af(&c->dk, (size_t)(c->H / c->Hk) * b * c->Hk * c->dh);
+  Af(&c->dv, (size_t)(c->H / c->Hk) * b * c->Hk * c->dh);
   A(&c->dqkv, (size_t)b * c->QKV * es);
   {
     void* p = nullptr;

@@ -7,20 +7,15 @@ namespace ttt {
 int gemm_k_granule(DT) { return 64; }
 
 // Tile choice from measured sweeps at the 3B shapes: 256 x 256 tiles (8
-// waves) once there are >= 256 of them for products with both operands
-// K-major; the transposing layouts prefer 4-wave tiles; small problems use
-// 128 x 128.
+// waves) once there are enough of them to cover the CUs; 128 x 128 for the
+// rest and for the short-K dW products (whose epilogue dominates).
 int gemm_pick_cfg(DT dt, bool ak, bool bk, const GemmArgs& g) {
   if (dt != DT::BF16) return 0;
   const long splits = g.kchunk > 0 ? (g.K + g.kchunk - 1) / g.kchunk : 1;
   auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * (long)((g.N + bn - 1) / bn) * splits; };
   if (ak && bk) return tiles(256, 256) >= 256 ? 5 : 1;
-  if (ak) {
-    if (tiles(256, 256) >= 192) return 4;
-    if (tiles(256, 128) >= 256) return 3;
-    return 1;
-  }
-  return tiles(256, 128) >= 512 ? 3 : 1;
+  if (ak) return tiles(256, 256) >= 192 ? 5 : 1;
+  return 1;
 }
 
 hipError_t gemm(DT dt, bool a_kmajor, bool b_kmajor, Epi epi, const GemmArgs& g, hipStream_t st) {

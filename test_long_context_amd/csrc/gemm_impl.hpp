@@ -8,7 +8,9 @@
 // every lane reads its 8-element MFMA fragment with one 16-byte LDS load.
 // Operands whose K dimension is not contiguous in HBM (the token-major
 // operands of dW, the weight operand of dX) are loaded as 8 x 8 blocks and
-// transposed in registers on the way into LDS.
+// transposed in registers on the way into LDS by the fp32 kernel; the bf16
+// kernel keeps them in their HBM orientation in LDS and transposes on the
+// fragment reads instead.
 #pragma once
 #include "common.hpp"
 #include "kernels.hpp"
@@ -304,11 +306,10 @@ gemm_kernel(GemmArgs g) {
 // =================================================================== bf16
 // bf16 kernel: K tile of 64, LDS rows of 64 elements without padding whose
 // logical 16-byte vector v is stored at physical slot v ^ (row & 7) (XOR
-// swizzle; conflict-free for the 16-row fragment reads). K-major operands go
+// swizzle; conflict-free for the 16-row fragment reads). Operands go
 // global -> LDS by buffer_load ... lds (no VGPR staging; the hardware puts
 // lane l's 16 bytes at base + 16 l, so each lane fetches the global vector
-// that belongs in its swizzled slot); operands with the other orientation
-// are staged through registers and transposed in 8 x 8 blocks.
+// that belongs in its swizzled slot).
 __device__ __forceinline__ int swz64(int r, int v) { return r * 64 + ((v ^ (r & 7)) << 3); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -333,43 +334,235 @@ struct DmaLoader {
   }
 };
 
-template <int ROWS, int NT>
-struct StageLoader {  // operand element (row m, k) at P[k * ld + m]
-  static constexpr int NB = 8 * (ROWS / 8);  // 8 x 8 blocks per 64-wide K tile
-  static constexpr int PER = (NB + NT - 1) / NT;
-  Frag8<bf16> r[PER * 8];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int row0, int nrows, int k0,
-                                       int kend, int tid) {
+// Operands whose K dimension is not contiguous (element (row r, k) at
+// P[k * ld + r]) keep that orientation in LDS: a [64 k][ROWS] tile, filled by
+// the same direct-to-LDS loads, whose 16-byte vector v of k-row kr sits at
+// slot v ^ trx(kr). Fragments come out through the CDNA4 transposing LDS
+// read (ds_read_b64_tr_b16): inside each group of 16 lanes, result lane i,
+// element e is element i % 4 of the 4 that source lane 4 e + i / 4 points
+// at. Pointing lane j of the group at (k-row kb + j / 4, column r0 + 4 (j % 4))
+// therefore hands lane i column r0 + i at k-rows kb .. kb + 3 -- four
+// consecutive K elements of its MFMA fragment; two reads make the eight. The
+// swizzle spreads the 16 k-rows one read instruction touches (kb + 8 g + j/4
+// for the four groups g) over 16 different slots.
+__device__ __forceinline__ int trx(int kr) { return (kr & 3) | ((kr >> 1) & 12); }
+
+template <int ROWS, int NW>
+struct TrDmaLoader {
+  static_assert(ROWS >= 128, "the swizzle needs 16 vectors per k-row");
+  static constexpr int VPR = ROWS / 8;  // 16-byte vectors per k-row
+  static constexpr int NI = VPR;        // wave instructions per 64-deep tile (1 KB each)
+  static constexpr int PER = (NI + NW - 1) / NW;
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, long ld, int row0, int nrows, int k0,
+                                        int kend, bf16* tile, int wid, int lane) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int b = tid + i * NT;
-      const int kb = b / (ROWS / 8), rb = b % (ROWS / 8);
-      const int gr = row0 + rb * 8;
-      const bool okr = (NB % NT == 0 || b < NB) && gr < nrows;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int gk = k0 + kb * 8 + j;
-        bld8<bf16>(r[i * 8 + j], rs, (okr && gk < kend) ? (uint32_t)(((long)gk * ld + gr) * 2) : OOB);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int b = tid + i * NT;
-      if (NB % NT != 0 && b >= NB) break;
-      const int kb = b / (ROWS / 8), rb = b % (ROWS / 8);
-#pragma unroll
-      for (int mm = 0; mm < 8; ++mm) {
-        Frag8<bf16> t;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) t.v[j] = r[i * 8 + j].v[mm];
-        const int row = rb * 8 + mm;
-        st8(tile + swz64(row, kb), t);
-      }
+      const int q = wid + i * NW;
+      if (NI % NW != 0 && q >= NI) break;
+      const int idx = q * 64 + lane;
+      const int kr = idx / VPR, slot = idx % VPR;
+      const int v = slot ^ trx(kr);
+      const int gk = k0 + kr, gr = row0 + v * 8;
+      const uint32_t off = (gk < kend && gr < nrows) ? (uint32_t)(((long)gk * ld + gr) * 2) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(tile + q * 512), 16, off, 0, 0, 0);
     }
   }
 };
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4* lds_s4_t;
+
+// MFMA fragment (rows r0 .. r0 + 15, K elements kb + 8 (lane / 16) .. + 7)
+// from a [64 k][ROWS] tile.
+template <int ROWS>
+__device__ __forceinline__ bf16x8 ld_tr8(const bf16* tile, int r0, int kb, int lane) {
+  const int j = lane & 15;
+  const int kr = kb + 8 * (lane >> 4) + (j >> 2), r = r0 + 4 * (j & 3);
+  const bf16* p = tile + kr * ROWS + (((r >> 3) ^ trx(kr)) << 3) + (r & 7);
+  // k-row kr + 4 has the same swizzle (kb is a multiple of 8)
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t)p);
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t)(p + 4 * ROWS));
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+
+// bf16-kernel epilogue, staged through LDS: each wave writes one 16-row block
+// of its accumulator tile into a private LDS strip, then reads it back as
+// row-contiguous 4-column chunks, so every global access of the epilogue is
+// a 16-byte (fp32) or 8-byte (bf16) vector over consecutive columns -- the
+// fp32 read-modify-write of the SGD and ADD epilogues otherwise dominates
+// the short-K dW products. Chunks that cross N, or calls whose ldc / pointers
+// do not allow vectors, take the element-wise path.
+__device__ __forceinline__ bf16x4 cvt4(floatx4 v) {
+  bf16x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = (bf16)v[e];
+  return r;
+}
+__device__ __forceinline__ floatx4 upc4(bf16x4 v) {
+  floatx4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = (float)v[e];
+  return r;
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi_chunk(const GemmArgs& g, int m, int n, floatx4 v, bool vec) {
+  const long idx = (long)m * g.ldc + n;
+  const int ne = min(4, g.N - n);
+  vec = vec && ne == 4;
+  if constexpr (EPI == (int)Epi::STORE) {
+    bf16* C = (bf16*)g.C + idx;
+    const floatx4 w = v * g.scale;
+    if (vec) *(bf16x4*)C = cvt4(w);
+    else for (int e = 0; e < ne; ++e) C[e] = (bf16)w[e];
+  } else if constexpr (EPI == (int)Epi::STORE_F32 || EPI == (int)Epi::PARTIAL) {
+    float* C = (float*)g.C + idx + (EPI == (int)Epi::PARTIAL ? (long)blockIdx.z * g.M * g.ldc : 0);
+    if (vec) *(floatx4*)C = v;
+    else for (int e = 0; e < ne; ++e) C[e] = v[e];
+  } else if constexpr (EPI == (int)Epi::ADD_F32) {
+    float* C = (float*)g.C + idx;
+    if (vec) *(floatx4*)C = *(const floatx4*)C + v;
+    else for (int e = 0; e < ne; ++e) C[e] += v[e];
+  } else if constexpr (EPI == (int)Epi::SGD) {
+    float* W = (float*)g.C + idx;
+    const bool two = g.C2 != g.C;
+    bf16* H = (bf16*)g.C2 + idx;
+    bf16* L = g.C3 ? (bf16*)g.C3 + idx : nullptr;
+    if (vec) {
+      const floatx4 w = *(const floatx4*)W - g.scale * v;
+      *(floatx4*)W = w;
+      if (two) {
+        const bf16x4 hi = cvt4(w);
+        *(bf16x4*)H = hi;
+        if (L) *(bf16x4*)L = cvt4(w - upc4(hi));
+      }
+    } else {
+      for (int e = 0; e < ne; ++e) {
+        const float w = W[e] - g.scale * v[e];
+        W[e] = w;
+        if (two) {
+          const bf16 hi = (bf16)w;
+          H[e] = hi;
+          if (L) L[e] = (bf16)(w - (float)hi);
+        }
+      }
+    }
+  } else if constexpr (EPI == (int)Epi::SWIGLU_BWD) {
+    // n indexes hidden units n .. n+3 (inside one 16-block); their gate/up
+    // columns in the 16-interleaved layout are (n / 16) * 32 + n % 16 and + 16
+    const long ca = (long)m * g.ldc + (n >> 4) * 32 + (n & 15);
+    const bf16* X = (const bf16*)g.X + ca;
+    bf16* D = (bf16*)g.C + ca;
+    floatx4 av, cv;
+    if (vec) {
+      av = upc4(*(const bf16x4*)X);
+      cv = upc4(*(const bf16x4*)(X + 16));
+    } else {
+      for (int e = 0; e < 4; ++e) {
+        av[e] = e < ne ? (float)X[e] : 0.f;
+        cv[e] = e < ne ? (float)X[e + 16] : 0.f;
+      }
+    }
+    floatx4 da, dc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sg = sigm_f(av[e]);
+      da[e] = v[e] * cv[e] * sg * (1.0f + av[e] * (1.0f - sg));
+      dc[e] = v[e] * av[e] * sg;
+    }
+    if (vec) {
+      *(bf16x4*)D = cvt4(da);
+      *(bf16x4*)(D + 16) = cvt4(dc);
+    } else {
+      for (int e = 0; e < ne; ++e) {
+        D[e] = (bf16)da[e];
+        D[e + 16] = (bf16)dc[e];
+      }
+    }
+  }
+}
+
+// SWIGLU: gate columns n .. n+3 with values a, up columns n+16 .. n+19 with c.
+__device__ __forceinline__ void epi_swiglu_chunk(const GemmArgs& g, int m, int n, floatx4 a, floatx4 c,
+                                                 bool vec) {
+  bf16* H12 = (bf16*)g.C;
+  const long ldm = g.N / 2;
+  const int jh = (n >> 5) * 16 + (n & 15);
+  floatx4 h;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = silu_f(a[e]) * c[e];
+  if (vec) {
+    if (H12) {
+      *(bf16x4*)(H12 + (long)m * g.ldc + n) = cvt4(a);
+      *(bf16x4*)(H12 + (long)m * g.ldc + n + 16) = cvt4(c);
+    }
+    *(bf16x4*)((bf16*)g.C2 + (long)m * ldm + jh) = cvt4(h);
+  } else {
+    for (int e = 0; e < 4; ++e) {
+      if (H12) {
+        H12[(long)m * g.ldc + n + e] = (bf16)a[e];
+        H12[(long)m * g.ldc + n + 16 + e] = (bf16)c[e];
+      }
+      ((bf16*)g.C2)[(long)m * ldm + jh + e] = (bf16)h[e];
+    }
+  }
+}
+
+template <int FM, int FN, int EPI>
+__device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, floatx4 (&acc)[FM][FN], int mw, int nw,
+                                                     int lane, float* strip) {
+  constexpr int WN = FN * 16;
+  constexpr int SP = WN + 4;  // strip row pitch in floats
+  const int fr = lane & 15, fg = lane >> 4;
+  auto al = [](const void* p, int a) { return p == nullptr || ((uintptr_t)p & (a - 1)) == 0; };
+  bool vec = (g.ldc % 4) == 0;
+  if constexpr (EPI == (int)Epi::STORE_F32 || EPI == (int)Epi::PARTIAL || EPI == (int)Epi::ADD_F32 ||
+                EPI == (int)Epi::SGD)
+    vec = vec && al(g.C, 16);
+  else
+    vec = vec && al(g.C, 8);
+  if constexpr (EPI == (int)Epi::SGD) vec = vec && al(g.C2, 8) && al(g.C3, 8);
+  if constexpr (EPI == (int)Epi::SWIGLU) vec = vec && al(g.C2, 8) && (g.N / 2) % 4 == 0;
+  if constexpr (EPI == (int)Epi::SWIGLU_BWD) vec = vec && al(g.X, 8);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) strip[(4 * fg + r) * SP + j * 16 + fr] = acc[i][j][r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (EPI == (int)Epi::SWIGLU) {
+      static_assert(WN % 32 == 0, "SWIGLU needs whole gate/up block pairs");
+      constexpr int CPR = WN / 8;  // gate chunks per row
+#pragma unroll
+      for (int c = lane; c < 16 * CPR; c += 64) {
+        const int row = c / CPR, q = c % CPR;
+        const int col = (q >> 2) * 32 + (q & 3) * 4;
+        const floatx4 a = *(const floatx4*)(strip + row * SP + col);
+        const floatx4 cc = *(const floatx4*)(strip + row * SP + col + 16);
+        const int m = mw + 16 * i + row, n = nw + col;
+        if (m < g.M && n < g.N) epi_swiglu_chunk(g, m, n, a, cc, vec);
+      }
+    } else {
+      constexpr int CPR = WN / 4;
+#pragma unroll
+      for (int c = lane; c < 16 * CPR; c += 64) {
+        const int row = c / CPR, col = (c % CPR) * 4;
+        const floatx4 v = *(const floatx4*)(strip + row * SP + col);
+        const int m = mw + 16 * i + row, n = nw + col;
+        if (m < g.M && n < g.N) epi_chunk<EPI>(g, m, n, v, vec);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
 
 template <int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, bool SPLITB>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
@@ -410,28 +603,21 @@ gemm_bf16_kernel(GemmArgs g) {
 
   DmaLoader<BM, NW> da;
   DmaLoader<BN, NW> db;
-  StageLoader<AK ? 8 : BM, NT> sa;
-  StageLoader<BKM ? 8 : BN, NT> sb;
+  TrDmaLoader<BM, NW> ta;
+  TrDmaLoader<BN, NW> tb;
   const int nk = (kend - kbeg + BK - 1) / BK;
   auto issue = [&](int kt, int buf) {
     const int k0 = kbeg + kt * BK;
     if constexpr (AK) da.issue(ra, g.lda, m0, g.M, k0, kend, As[buf], wid, lane);
-    else sa.load(ra, g.lda, m0, g.M, k0, kend, tid);
+    else ta.issue(ra, g.lda, m0, g.M, k0, kend, As[buf], wid, lane);
     if constexpr (BKM) {
       db.issue(rb, g.ldb, n0, g.N, k0, kend, Bs[buf], wid, lane);
       if constexpr (SPLITB) db.issue(rb2, g.ldb, n0, g.N, k0, kend, Cs[buf], wid, lane);
     } else {
-      sb.load(rb, g.ldb, n0, g.N, k0, kend, tid);
+      tb.issue(rb, g.ldb, n0, g.N, k0, kend, Bs[buf], wid, lane);
     }
   };
-  auto stage_store = [&](int buf) {
-    if constexpr (!AK) sa.store(As[buf], tid);
-    if constexpr (!BKM) sb.store(Bs[buf], tid);
-  };
-  if (nk > 0) {
-    issue(0, 0);
-    stage_store(0);
-  }
+  if (nk > 0) issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -445,10 +631,14 @@ gemm_bf16_kernel(GemmArgs g) {
     for (int s = 0; s < 2; ++s) {
       const int v = s * 4 + fv;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) ld8(af[s][i], As[cur] + swz64(wm0 + i * 16 + fr, v));
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (AK) ld8(af[s][i], As[cur] + swz64(wm0 + i * 16 + fr, v));
+        else af[s][i].v = ld_tr8<BM>(As[cur], wm0 + i * 16, s * 32, lane);
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        ld8(bfr[s][j], Bs[cur] + swz64(wn0 + j * 16 + fr, v));
+        if constexpr (BKM) ld8(bfr[s][j], Bs[cur] + swz64(wn0 + j * 16 + fr, v));
+        else bfr[s][j].v = ld_tr8<BN>(Bs[cur], wn0 + j * 16, s * 32, lane);
         if constexpr (SPLITB) ld8(bf2[s][j], Cs[cur] + swz64(wn0 + j * 16 + fr, v));
       }
     }
@@ -469,11 +659,15 @@ gemm_bf16_kernel(GemmArgs g) {
           for (int j = 0; j < FN; ++j) mma16(acc[i][j], af[s][i], bf2[s][j]);
       }
     }
-    if (kt + 1 < nk) stage_store(cur ^ 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  gemm_epilogue<bf16, FM, FN, EPI>(g, acc, m0 + wm0, n0 + wn0, lane);
+  // the loop ended on a barrier with every load landed: the operand tiles
+  // are free to hold the epilogue strips
+  constexpr int STRIP = 16 * (WN + 4);
+  static_assert(NW * STRIP * 4 <= (BM >= BN ? BM : BN) * BK * 2 * 2, "epilogue strips exceed the tile area");
+  float* strips = BM >= BN ? (float*)&As[0][0] : (float*)&Bs[0][0];
+  gemm_epilogue_staged<FM, FN, EPI>(g, acc, m0 + wm0, n0 + wn0, lane, strips + wid * STRIP);
 }
 
 // ------------------------------------------------------------------ launch

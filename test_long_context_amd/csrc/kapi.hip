@@ -97,13 +97,36 @@ extern "C" ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k,
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
+namespace {
+bool use_bwd2(int32_t dtype, int32_t dh, int32_t variant) {
+  return variant == 2 || (variant == 0 && dtype == TTT_BF16 && (dh == 64 || dh == 128));
+}
+AttnArgs bwd_shape(int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t window) {
+  AttnArgs a{};
+  a.n = n;
+  a.H = H;
+  a.Hk = Hk;
+  a.dh = dh;
+  a.window = window;
+  return a;
+}
+}  // namespace
+
+extern "C" int64_t tttk_attn_bwd_workspace(int32_t dtype, int32_t n, int32_t H, int32_t Hk, int32_t dh,
+                                           int32_t window, int32_t variant) {
+  if (n <= 0 || H < 1 || Hk < 1 || H % Hk || !use_bwd2(dtype, dh, variant)) return 0;
+  const AttnArgs a = bwd_shape(n, H, Hk, dh, window);
+  return (int64_t)4 * n * dh * ((int64_t)attn_bwd2_dq_parts(a) * H + 2LL * attn_bwd2_kv_parts(a) * Hk);
+}
+
 extern "C" ttt_status tttk_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v,
                                     const float* lse, const void* dO, const float* D, float* dq, float* dk,
                                     float* dv, int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t cap,
-                                    int32_t window, int64_t pos0, void* stream) {
+                                    int32_t window, int64_t pos0, int32_t variant, void* work, void* stream) {
   ttt_status s = attn_check(dtype, n, H, Hk, dh, cap, window, pos0);
   if (s != TTT_OK) return s;
-  if (!q || !k || !v || !lse || !dO || !D || !dq || !dk || !dv) return TTT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !lse || !dO || !D || !dq || !dk || !dv || variant < 0 || variant > 2)
+    return TTT_ERR_INVALID_ARG;
   AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -119,10 +142,28 @@ extern "C" ttt_status tttk_attn_bwd(int32_t dtype, const void* q, const void* k,
   a.scale = 1.f / sqrtf((float)dh);
   a.dO = dO;
   a.D = D;
+  hipStream_t st = (hipStream_t)stream;
+  if (use_bwd2(dtype, dh, variant)) {
+    if (!attn_bwd2_supported(to_dt(dtype), a)) return TTT_ERR_UNSUPPORTED;
+    if (n == 0) return TTT_OK;
+    if (!work || !al16(work)) return TTT_ERR_INVALID_ARG;
+    const int qp = attn_bwd2_dq_parts(a), kp = attn_bwd2_kv_parts(a);
+    float* wq = (float*)work;
+    float* wk = wq + (long)qp * n * H * dh;
+    float* wv = wk + (long)kp * n * Hk * dh;
+    a.dq = wq;
+    a.dk = wk;
+    a.dv = wv;
+    if (attn_bwd_dq2(to_dt(dtype), a, st) != hipSuccess) return TTT_ERR_HIP;
+    if (attn_bwd_dkdv2(to_dt(dtype), a, st) != hipSuccess) return TTT_ERR_HIP;
+    if (sum_parts_f32(wq, qp, (long)n * H * dh, dq, st) != hipSuccess) return TTT_ERR_HIP;
+    if (sum_parts_f32(wk, kp, (long)n * Hk * dh, dk, st) != hipSuccess) return TTT_ERR_HIP;
+    if (sum_parts_f32(wv, kp, (long)n * Hk * dh, dv, st) != hipSuccess) return TTT_ERR_HIP;
+    return TTT_OK;
+  }
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  hipStream_t st = (hipStream_t)stream;
   if (attn_bwd_dq(to_dt(dtype), a, st) != hipSuccess) return TTT_ERR_HIP;
   if (attn_bwd_dkdv(to_dt(dtype), a, st) != hipSuccess) return TTT_ERR_HIP;
   return TTT_OK;

@@ -71,7 +71,7 @@ hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, in
                         int cap, int64_t min_store_pos, hipStream_t st);
 // dQKV (T) [n, (H+2Hk) dh] from dq [n, H dh] (float), dk, dv [n, Hk dh]
 // (float): inverse rotation of dq and dk.
-hipError_t rope_bwd_pack(DT dt, const float* dq, const float* dk, const float* dv, int n, int H,
+hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts, int n, int H,
                          int Hk, int dh, int64_t pos0, const float2* rope_tab, void* dqkv,
                          hipStream_t st);
 // Fused softmax cross-entropy over the vocabulary for rows with a target
@@ -114,6 +114,17 @@ bool attn_fwd2_supported(DT dt, const AttnArgs& a);
 hipError_t attn_fwd2(DT dt, const AttnArgs& a, hipStream_t st, int qb = 0);
 hipError_t attn_bwd_dq(DT dt, const AttnArgs& a, hipStream_t st);
 hipError_t attn_bwd_dkdv(DT dt, const AttnArgs& a, hipStream_t st);
+// Second-generation backward (bf16, head_dim 64/128). dq receives
+// attn_bwd2_dq_parts(a) partial sums ([parts][n][H][dh]); dk and dv receive
+// attn_bwd2_kv_parts(a) = H / Hk partial sums ([parts][n][Hk][dh]), one per
+// query head of the group.
+bool attn_bwd2_supported(DT dt, const AttnArgs& a);
+int attn_bwd2_dq_parts(const AttnArgs& a);
+int attn_bwd2_kv_parts(const AttnArgs& a);
+hipError_t attn_bwd_dq2(DT dt, const AttnArgs& a, hipStream_t st);
+hipError_t attn_bwd_dkdv2(DT dt, const AttnArgs& a, hipStream_t st);
+// dst[i] = sum_p parts[p * count + i]
+hipError_t sum_parts_f32(const float* parts, int nparts, long count, float* dst, hipStream_t st);
 
 // ---------------------------------------------------------------- decode
 // y[n] = sum_k x[k] W[n, k] for one row (T weights, float x), with epilogues.

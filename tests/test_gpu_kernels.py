@@ -1,0 +1,167 @@
+"""Kernel-level parity of the GEMM family (include/ttt_kernels.h, tttk_gemm)
+against float64 CPU products of the same bf16 / fp32 operands.
+
+Covers every operand layout and tile configuration at a ragged shape (several
+tiles plus partial ones in M, N and K), each fused epilogue against its
+definition, and the 3B-shape products of the inner loop on sampled outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.util import say
+
+pytestmark = pytest.mark.gpu
+
+tla = pytest.importorskip("test_long_context_amd")
+dev = "cuda"
+bf = torch.bfloat16
+
+
+def rnd(g, *shape, scale=0.5, dtype=bf):
+    return (torch.randn(*shape, generator=g, dtype=torch.float32) * scale).to(dtype)
+
+
+def logical(X, rows, K, kmajor):
+    """Operand as a [rows, K] float64 CPU matrix."""
+    X = X.double().cpu()
+    return X.view(rows, K) if kmajor else X.view(K, rows).T
+
+
+LAYOUTS = {"nt": (True, True), "nn": (True, False), "tn": (False, True), "tt": (False, False)}
+
+
+@pytest.mark.parametrize("lay", sorted(LAYOUTS))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gemm_layouts_tiles(lay, dtype):
+    ak, bk = LAYOUTS[lay]
+    M, N, K = 520, 392, 328
+    g = torch.Generator().manual_seed(11)
+    dt = bf if dtype == "bf16" else torch.float32
+    A = rnd(g, M * K, dtype=dt)
+    B = rnd(g, N * K, dtype=dt)
+    ref = logical(A, M, K, ak) @ logical(B, N, K, bk).T
+    Ad, Bd = A.to(dev), B.to(dev)
+    tiles = (1, 2, 3, 4, 5, 6) if dtype == "bf16" else (0,)
+    for t in tiles:
+        say(f"gemm {lay} {dtype} tile {t} {M}x{N}x{K}")
+        C = torch.full((M * N,), float("nan"), device=dev)
+        tla.gemm(Ad, Bd, M, N, K, "store_f32", C, a_kmajor=ak, b_kmajor=bk, tile=t)
+        err = float((C.cpu().double().view(M, N) - ref).abs().max() / ref.abs().max())
+        assert err < 1e-5, (lay, dtype, t, err)
+
+
+def test_gemm_epilogues():
+    g = torch.Generator().manual_seed(12)
+    M, N, K = 264, 160, 200
+    A = rnd(g, M * K)
+    B = rnd(g, N * K)
+    Ad, Bd = A.to(dev), B.to(dev)
+    acc = logical(A, M, K, True) @ logical(B, N, K, True).T
+
+    # STORE: bf16 of scale * acc
+    C = torch.empty(M * N, dtype=bf, device=dev)
+    tla.gemm(Ad, Bd, M, N, K, "store", C, scale=0.5)
+    want = (0.5 * acc).float().to(bf).double()
+    assert float((C.cpu().double().view(M, N) - want).abs().max()) <= float(want.abs().max()) * 2 ** -8
+
+    # ADD_F32
+    C0 = rnd(g, M * N, dtype=torch.float32)
+    C = C0.to(dev)
+    tla.gemm(Ad, Bd, M, N, K, "add_f32", C)
+    assert float((C.cpu().double().view(M, N) - (C0.double().view(M, N) + acc)).abs().max()) < 1e-4
+
+    # PARTIAL over K chunks of 64: the chunks sum to the product
+    nsp = (K + 63) // 64
+    C = torch.empty(nsp * M * N, device=dev)
+    tla.gemm(Ad, Bd, M, N, K, "partial", C, kchunk=64)
+    assert float((C.cpu().double().view(nsp, M, N).sum(0) - acc).abs().max()) < 1e-4
+
+    # SWIGLU: N columns interleaved (gate, up) in blocks of 16
+    C = torch.empty(M * N, dtype=bf, device=dev)
+    C2 = torch.empty(M * N // 2, dtype=bf, device=dev)
+    tla.gemm(Ad, Bd, M, N, K, "swiglu", C, C2=C2)
+    a = acc.view(M, N // 32, 2, 16)[:, :, 0, :].reshape(M, N // 2)
+    c = acc.view(M, N // 32, 2, 16)[:, :, 1, :].reshape(M, N // 2)
+    want = a / (1 + torch.exp(-a)) * c
+    assert float((C2.cpu().double().view(M, N // 2) - want).abs().max()) <= float(want.abs().max()) * 2 ** -7
+    assert float((C.cpu().double().view(M, N) - acc).abs().max()) <= float(acc.abs().max()) * 2 ** -8
+
+    # SWIGLU_BWD: acc = dHmid [M, N]; X = pre-activations [M, 2N] (interleaved)
+    X = rnd(g, M * 2 * N)
+    C = torch.empty(M * 2 * N, dtype=bf, device=dev)
+    tla.gemm(Ad, Bd, M, N, K, "swiglu_bwd", C, X=X.to(dev), ldc=2 * N)
+    Xd = X.double().view(M, N // 16, 2, 16)
+    av, cv = Xd[:, :, 0, :].reshape(M, N), Xd[:, :, 1, :].reshape(M, N)
+    sg = 1 / (1 + torch.exp(-av))
+    da = acc * cv * sg * (1 + av * (1 - sg))
+    dc = acc * av * sg
+    got = C.cpu().double().view(M, N // 16, 2, 16)
+    for got_part, want_part in ((got[:, :, 0, :].reshape(M, N), da), (got[:, :, 1, :].reshape(M, N), dc)):
+        assert float((got_part - want_part).abs().max()) <= float(want_part.abs().max()) * 2 ** -7
+
+
+@pytest.mark.parametrize("lay", ["tn", "nt"])
+def test_gemm_sgd_epilogue(lay):
+    """W -= scale * acc on the fp32 master; C2 = bf16(W); C3 = bf16(W - C2)."""
+    ak, bk = LAYOUTS[lay]
+    g = torch.Generator().manual_seed(13)
+    M, N, K = 392, 264, 136
+    A = rnd(g, M * K)
+    B = rnd(g, N * K)
+    W0 = rnd(g, M * N, scale=0.02, dtype=torch.float32)
+    W = W0.to(dev)
+    hi = torch.empty(M * N, dtype=bf, device=dev)
+    lo = torch.empty(M * N, dtype=bf, device=dev)
+    tla.gemm(A.to(dev), B.to(dev), M, N, K, "sgd", W, a_kmajor=ak, b_kmajor=bk, C2=hi, C3=lo, scale=1e-3)
+    acc = logical(A, M, K, ak) @ logical(B, N, K, bk).T
+    want = W0.double().view(M, N) - 1e-3 * acc
+    Wg = W.cpu().double().view(M, N)
+    assert float((Wg - want).abs().max()) < 1e-6
+    # hi is the RNE of the stored master, lo the RNE of the remainder
+    Wf = W.cpu().view(M, N)
+    assert torch.equal(hi.cpu().view(M, N), Wf.to(bf))
+    assert torch.equal(lo.cpu().view(M, N), (Wf - Wf.to(bf).float()).to(bf))
+
+
+# The inner loop's products at the 3B shape (d 3072, F 8192, V 128256,
+# mini-batch 1024), in the launch configuration the engine picks (tile 0),
+# checked on sampled output entries.
+BIG = [
+    ("lm_head fwd", 1024, 128256, 3072, "nt", 0),
+    ("lm_head bwd dX", 1024, 3072, 128256, "nn", 16064),
+    ("dyn up bwd dX", 1024, 3072, 16384, "nn", 4096),
+    ("dW3", 3072, 8192, 1024, "tn", 0),
+    ("dW12", 16384, 3072, 1024, "tn", 0),
+]
+
+
+@pytest.mark.parametrize("name,M,N,K,lay,split", BIG)
+def test_gemm_3b_shapes_sampled(name, M, N, K, lay, split):
+    ak, bk = LAYOUTS[lay]
+    say(f"gemm 3b {name} {M}x{N}x{K} {lay}")
+    g = torch.Generator(device=dev).manual_seed(14)
+    A = (torch.randn(M * K, generator=g, device=dev) * 0.5).to(bf)
+    B = (torch.randn(N * K, generator=g, device=dev) * 0.5).to(bf)
+    nsp = (K + split - 1) // split if split else 1
+    C = torch.empty(nsp * M * N, device=dev)
+    if split:
+        tla.gemm(A, B, M, N, K, "partial", C, a_kmajor=ak, b_kmajor=bk, kchunk=split)
+        Cm = C.view(nsp, M, N).sum(0)
+    else:
+        tla.gemm(A, B, M, N, K, "store_f32", C, a_kmajor=ak, b_kmajor=bk)
+        Cm = C.view(M, N)
+    rs = np.random.default_rng(15)
+    rows = torch.as_tensor(rs.integers(0, M, 64))
+    cols = torch.as_tensor(rs.integers(0, N, 64))
+    rows = torch.cat([rows, torch.tensor([0, M - 1])])
+    cols = torch.cat([cols, torch.tensor([N - 1, 0])])
+    Ac = A.cpu().double()
+    Bc = B.cpu().double()
+    Am = Ac.view(M, K) if ak else Ac.view(K, M).T
+    Bm = Bc.view(N, K) if bk else Bc.view(K, N).T
+    want = (Am[rows] * Bm[cols]).sum(1)
+    got = Cm[rows.to(dev), cols.to(dev)].cpu().double()
+    # fp32 accumulation over K terms of size ~0.25: error ~ sqrt(K) * 2^-24 * |terms|
+    tol = 1e-5 * max(1.0, float(want.abs().max()))
+    assert float((got - want).abs().max()) < tol, (name, float((got - want).abs().max()))
