@@ -11,9 +11,16 @@ backward and SGD update) after ttt_reset; inputs are resident in HBM.
 
 Prints one JSON line: tokens/s, the fraction of the bf16 MFMA peak reached by
 the whole step (algorithmic FLOPs / time / 2.5 PFLOP/s), the live roofline of
-the dominant kernel class (HIP events around its launches during the timed
-steps), and the CPU oracle timed on a bounded sample of the same workload.
+the dominant kernel -- the sliding-window attention forward (one kernel
+symbol, launched by the hoisted prefix and by every mini-batch), timed with
+HIP events on its launch stream during the timed steps -- and the CPU oracle
+timed on a bounded sample of the same workload.
+
+`--copy-probe` instead runs a plain 1 GiB device copy and exits: run under
+`rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE) it gives the factor that turns
+those counters into bytes.
 """
+import hashlib
 import argparse
 import json
 import os
@@ -28,6 +35,38 @@ METRIC = "TTT prefill tokens/s @128K ctx 3B-shape, 1 MI355X; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+
+# timing classes of the library (ttt_kernel_class in include/ttt.h)
+KC = dict(gemm_prefix=0, attn_prefix=1, gemm_loop=2, attn_loop=3, lmhead=4, ce=5, attn_bwd=6, dw_sgd=7,
+          other=8)
+ROOF_CLASSES = ("attn_prefix", "attn_loop")   # the attention forward kernel
+ROOF_SOURCES = ("test_long_context_amd/csrc/attn2.hip", "test_long_context_amd/csrc/common.hpp")
+
+# HBM traffic of the attention forward at the 3B workload from rocprofv3
+# --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch, averaged over one step's
+# dispatches of the kernel) and the same counters over a 1 GiB copy; valid
+# only for the kernel source they were taken on (sha256 of ROOF_SOURCES).
+TRAFFIC = {}
+
+
+def roof_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ROOF_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe():
+    import torch
+    n = 1 << 28  # 1 GiB of float32
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_bytes_per_dispatch=n * 4, dispatches=3)), flush=True)
 
 
 def algorithmic_flops(c: dict, T: int) -> float:
@@ -81,7 +120,11 @@ def main():
     ap.add_argument("--seq", type=int, default=None, help="override the stream length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print the per-class timing table")
+    ap.add_argument("--copy-probe", action="store_true", help="1 GiB device copy for PMC scaling, then exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs the inner loop on one GPU only; --gpus N > 1 is not "
@@ -113,7 +156,6 @@ def main():
         m.sync()
         print(f"# warm-up step {i} done", file=sys.stderr, flush=True)
     classes = [m.timing_read(k) for k in range(9)]
-    dom = max(range(9), key=lambda k: classes[k]["ms"])
     if args.breakdown:
         tot = sum(x["ms"] for x in classes)
         for x in classes:
@@ -122,8 +164,11 @@ def main():
             print(f"# {x['kind']:12s} {x['ms']:9.2f} ms {100 * x['ms'] / tot:5.1f}%  launches {x['launches']:6d}"
                   f"  {eff:8.1f} TFLOP/s  {bw:8.1f} GB/s", file=sys.stderr)
 
-    # timed steps: events only around the dominant class
-    m.timing_enable(1 << dom)
+    # timed steps: events only around the attention forward launches
+    mask = 0
+    for k in ROOF_CLASSES:
+        mask |= 1 << KC[k]
+    m.timing_enable(mask)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -134,7 +179,7 @@ def main():
     torch.cuda.synchronize()
     m.sync()
     ms = e0.elapsed_time(e1) / args.steps
-    dk = m.timing_read(dom)
+    parts = [m.timing_read(KC[k]) for k in ROOF_CLASSES]
     m.timing_enable(0)
     assert bool(torch.isfinite(loss).all()), "non-finite loss"
     mean_loss = float(loss.mean())
@@ -142,18 +187,23 @@ def main():
     flops = algorithmic_flops(c, T)
     tps = T / (ms / 1e3)
     frac = flops / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
-    hbm_kind = dk["kind"] in ("ce",)
-    if dk["kind"] in ("ce",):
-        ach = dk["bytes"] / dk["launches"] / (dk["ms"] / dk["launches"] * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=None)
-    else:
-        ach = dk["flops"] / dk["launches"] / (dk["ms"] / dk["launches"] * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None)
-    roof.update(kernel_class=dk["kind"], launches_per_step=dk["launches"] // args.steps,
-                avg_launch_us=round(dk["ms"] / dk["launches"] * 1e3, 2),
-                share_of_step=round(dk["ms"] / args.steps / ms, 4))
+    r_ms = sum(x["ms"] for x in parts)
+    r_fl = sum(x["flops"] for x in parts)
+    r_n = sum(x["launches"] for x in parts)
+    avg_s = r_ms / r_n * 1e-3
+    ach = r_fl / r_n / avg_s / 1e12
+    src = roof_source_hash()
+    tr = TRAFFIC.get((args.workload, T, src))
+    traffic = None
+    if tr is not None:
+        traffic = round(tr["fetch_kib"] * 1024 * tr["fetch_scale"] + tr["write_kib"] * 1024 * tr["write_scale"])
+    roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=traffic,
+                kernel=f"attn_fwd2_kernel (sliding-window attention forward, head_dim {c['head_dim']})",
+                traffic_unit="bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                launches_per_step=r_n // args.steps, avg_launch_us=round(avg_s * 1e6, 2),
+                algorithmic_gflop_per_launch=round(r_fl / r_n / 1e9, 3),
+                share_of_step=round(r_ms / args.steps / ms, 4), source_sha=src)
 
     out = dict(metric=METRIC, value=round(tps, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms, 2), higher_is_better=True, scaling="weak",

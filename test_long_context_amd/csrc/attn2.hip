@@ -36,12 +36,27 @@ __device__ __forceinline__ int vswz(int row, int v) {  // V^T tile [DH][64]
 }  // namespace
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup order: the hardware deals consecutive workgroup ids round-robin
+// over the 8 XCDs (each with its own L2). Remap so that each XCD gets a
+// contiguous range of logical blocks, ordered key head first, then query
+// block, then the query heads of the group -- workgroups that run together
+// on an XCD read the same key/value tiles. Grid: (query blocks, H).
+__device__ __forceinline__ void attn_block_order(const AttnArgs& a, int& qblk, int& h) {
+  const int nqb = gridDim.x, nwg = gridDim.x * gridDim.y;
+  int id = blockIdx.x + blockIdx.y * gridDim.x;
+  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  const int grp = a.H / a.Hk;
+  const int kh = id / (grp * nqb), rem = id % (grp * nqb);
+  qblk = rem / grp;
+  h = kh * grp + rem % grp;
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes, 0x00020000);
 }
 
 template <int DH, int QB>
-__global__ void __launch_bounds__(256) attn_fwd2_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArgs a) {
   constexpr int BQ = 4 * 32 * QB;
   constexpr int KS = DH / 16;   // contraction steps over dh for S^T
   constexpr int DB = DH / 32;   // 32-row dh blocks of O^T
@@ -56,8 +71,10 @@ __global__ void __launch_bounds__(256) attn_fwd2_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 Vs0[DH * BKV2];
   __shared__ __attribute__((aligned(1024))) bf16 Vs1[DH * BKV2];
 
-  const int h = blockIdx.y, kh = h / (a.H / a.Hk);
-  const int q0 = blockIdx.x * BQ;
+  int qblk, h;
+  attn_block_order(a, qblk, h);
+  const int kh = h / (a.H / a.Hk);
+  const int q0 = qblk * BQ;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
   const bf16* Q = (const bf16*)a.q;

@@ -89,8 +89,24 @@ __global__ void __launch_bounds__(256) attn_bwd_dq2_kernel(AttnArgs a, int kspli
   __shared__ __attribute__((aligned(1024))) bf16 Vs0[BT * DH];
   __shared__ __attribute__((aligned(1024))) bf16 Vs1[BT * DH];
 
-  const int h = blockIdx.y, kh = h / (a.H / a.Hk), z = blockIdx.z;
-  const int q0 = blockIdx.x * 128;
+  // XCD-aware order (see attn2.hip): each XCD takes a contiguous range of
+  // logical blocks ordered key head, key split, query block, query head
+  int h, z, qblk;
+  {
+    const int nqb = gridDim.x, nz = gridDim.z, grp = a.H / a.Hk;
+    const int nwg = gridDim.x * gridDim.y * gridDim.z;
+    int id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+    const int per_kh = grp * nqb * nz;
+    const int khb = id / per_kh;
+    int rem = id % per_kh;
+    z = rem / (grp * nqb);
+    rem %= grp * nqb;
+    qblk = rem / grp;
+    h = khb * grp + rem % grp;
+  }
+  const int kh = h / (a.H / a.Hk);
+  const int q0 = qblk * 128;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
   const bf16* Q = (const bf16*)a.q;
