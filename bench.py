@@ -111,6 +111,61 @@ def cpu_baseline(c, w, tok, ntok):
                 seconds=round(dt, 2))
 
 
+def decode_bytes(c: dict, p: int) -> float:
+    """HBM bytes one decode step must read at position p: every weight once
+    (static bf16, dynamic fp32 masters, lm_head) and the window's keys and
+    values in every block."""
+    L, d, H, Hk, dh = c["n_layers"], c["d_model"], c["n_heads"], c["n_kv_heads"], c["head_dim"]
+    F, Fd, V, k = c["ffn_hidden"], c["dyn_ffn_hidden"], c["vocab"], c["window"]
+    Ld = c["n_dynamic"] or L - (3 * L) // 4
+    es = 2 if c["dtype"] == "bf16" else 4
+    static = L * ((H + 2 * Hk) * dh * d + d * H * dh + 3 * F * d) * es + V * d * es
+    dyn = Ld * 3 * Fd * d * 4
+    kv = L * min(p + 1, k) * Hk * dh * 2 * es
+    return float(static + dyn + kv)
+
+
+def decode_bench(args, c, w, tok, tla, torch):
+    """Decode latency after prefills of 8K, 32K and 128K tokens: 256
+    teacher-forced steps each, every step timed with HIP events."""
+    ctxs = [x for x in (8192, 32768, 131072) if x + args.decode_steps <= tok.numel()]
+    m = tla.TTT(c, w, max_seq=max(ctxs) + args.decode_steps + 1)
+    # warm-up: the first decode step captures the launch graph
+    m.prefill(tok[:ctxs[0]])
+    m.decode_step(tok[ctxs[0]:ctxs[0] + 1])
+    m.sync()
+    res = {}
+    for ctx in ctxs:
+        m.reset()
+        m.prefill(tok[:ctx])
+        m.sync()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.decode_steps + 1)]
+        logits = torch.empty(c["vocab"], dtype=torch.float32, device="cuda")
+        ev[0].record()
+        for j in range(args.decode_steps):
+            m.decode_step(tok[ctx + j:ctx + j + 1], logits)
+            ev[j + 1].record()
+        torch.cuda.synchronize()
+        m.sync()
+        ts = sorted(ev[j].elapsed_time(ev[j + 1]) for j in range(args.decode_steps))
+        p50, p99 = ts[len(ts) // 2], ts[min(len(ts) - 1, int(0.99 * len(ts)))]
+        gbs = decode_bytes(c, ctx) / (p50 * 1e-3) / 1e9
+        res[str(ctx)] = dict(p50_ms=round(p50, 3), p99_ms=round(p99, 3), hbm_gb_per_token=round(decode_bytes(c, ctx) / 1e9, 3),
+                             achieved_gbs=round(gbs, 1))
+        print(f"# decode after {ctx}: p50 {p50:.3f} ms  p99 {p99:.3f} ms  {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    m.close()
+    big, small = res[str(ctxs[-1])], res[str(ctxs[0])]
+    out = dict(metric="TTT decode latency @3B-shape after a TTT prefill, 1 MI355X", value=big["p50_ms"],
+               unit="ms/token (p50)", n_gpus=1, steps=args.decode_steps, higher_is_better=False,
+               dtype="bf16" if c["dtype"] == "bf16" else "f32", data="synthetic",
+               config=dict(workload=f"{args.workload}-shape decode, {args.decode_steps} teacher-forced steps after "
+                                    f"prefills of {', '.join(str(x) for x in ctxs)} tokens", window=c["window"]),
+               contexts=res, flat_ratio=round(big["p50_ms"] / small["p50_ms"], 3),
+               roofline=dict(bound="hbm", achieved=big["achieved_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                             frac=round(big["achieved_gbs"] / PEAK_HBM_GBS, 4), traffic=None))
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +176,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print the per-class timing table")
     ap.add_argument("--copy-probe", action="store_true", help="1 GiB device copy for PMC scaling, then exit")
+    ap.add_argument("--decode", action="store_true", help="measure decode latency instead of prefill throughput")
+    ap.add_argument("--decode-steps", type=int, default=256)
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
@@ -140,6 +197,10 @@ def main():
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
     w = synth.gen_weights(c, device="cuda")
+    if args.decode:
+        tok = synth.gen_tokens(c, n=T + args.decode_steps, device="cuda")
+        decode_bench(args, c, w, tok, tla, torch)
+        return
     tok = synth.gen_tokens(c, n=T, device="cuda")
     m = tla.TTT(c, w, max_seq=T + 1024)
     loss = torch.empty(T - 1, dtype=torch.float32, device="cuda")

@@ -1,0 +1,410 @@
+// Decode: the forward of one new token at position p (read from a device
+// counter, so the per-token launch sequence can be captured once in a HIP
+// graph and replayed) through every block, with the window's keys/values
+// from the rings and the dynamic MLPs under the current fp32 fast-weight
+// masters ([P1] "TTT-E2E：端到端测试时训练的长上下文语言建模", 推理: decoding
+// with a constant-size window cache; [P2] 另辟蹊径: per-token cost does not
+// grow with the context). Activations are fp32; every product reads its
+// weights once, so the step is bound by HBM bandwidth.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ttt {
+
+namespace {
+constexpr int GV_THREADS = 256;
+constexpr int GV_ROWS = 4;  // rows per wave per pass (two pairs)
+
+template <typename TW> struct WVec;  // 16 bytes of weights -> floats
+template <> struct WVec<bf16> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const bf16* p, float (&o)[8]) {
+    const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
+  }
+};
+template <> struct WVec<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float (&o)[4]) {
+    const floatx4 v = *(const floatx4*)p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = v[e];
+  }
+};
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+  __syncthreads();
+  return s;
+}
+}  // namespace
+
+// y = W x for one row x (fp32 [K]); W [N][K] row-major (nn.Linear layout).
+// NORM: x = RMSNorm(h) * g computed by every workgroup while staging x in
+// LDS. EPI: STORE y[n] = acc; ADD_F32 y[n] += acc; SWIGLU: rows are the
+// 16-interleaved (gate, up) layout and y[j] = silu(gate_j) * up_j.
+// A wave takes GV_ROWS rows (two pairs) at a time; lanes stride the row in
+// 16-byte vectors, so each row is one coalesced sweep.
+template <typename TW, int EPI, bool NORM>
+__global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__ W, const float* __restrict__ x,
+                                                          const float* __restrict__ g, float eps, int N, int K,
+                                                          float* __restrict__ y) {
+  extern __shared__ float xs[];
+  __shared__ float red[GV_THREADS / 64];
+  if constexpr (NORM) {
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < K; k += GV_THREADS) ss += x[k] * x[k];
+    const float r = rsqrtf(block_sum(ss, red) / K + eps);
+    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k] * r * g[k];
+  } else {
+    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k];
+  }
+  __syncthreads();
+  constexpr int VE = WVec<TW>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (GV_THREADS / 64) + (threadIdx.x >> 6);
+  const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
+  const int p0 = wave * (GV_ROWS / 2);
+  if (p0 >= npairs) return;
+  int rows[GV_ROWS];
+#pragma unroll
+  for (int i = 0; i < GV_ROWS / 2; ++i) {
+    const int p = min(p0 + i, npairs - 1);
+    if constexpr (EPI == (int)GvEpi::SWIGLU) {
+      rows[2 * i] = (p >> 4) * 32 + (p & 15);
+      rows[2 * i + 1] = rows[2 * i] + 16;
+    } else {
+      rows[2 * i] = 2 * p;
+      rows[2 * i + 1] = min(2 * p + 1, N - 1);
+    }
+  }
+  float acc[GV_ROWS];
+#pragma unroll
+  for (int r = 0; r < GV_ROWS; ++r) acc[r] = 0.f;
+  const int nv = K / VE;
+  for (int v = lane; v < nv; v += 64) {
+    float xv[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) xv[e] = xs[v * VE + e];
+#pragma unroll
+    for (int r = 0; r < GV_ROWS; ++r) {
+      float wv[VE];
+      WVec<TW>::load(W + (long)rows[r] * K + v * VE, wv);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[r] += wv[e] * xv[e];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < GV_ROWS; ++r) acc[r] = wave_sum(acc[r]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < GV_ROWS / 2; ++i) {
+      const int p = p0 + i;
+      if (p >= npairs) break;
+      if constexpr (EPI == (int)GvEpi::SWIGLU) {
+        const float a = acc[2 * i], c = acc[2 * i + 1];
+        y[p] = silu_f(a) * c;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int n = 2 * p + u;
+          if (n >= N) break;
+          if constexpr (EPI == (int)GvEpi::ADD_F32) y[n] += acc[2 * i + u];
+          else y[n] = acc[2 * i + u];
+        }
+      }
+    }
+  }
+}
+
+template <typename TW, int EPI>
+static hipError_t gemv_t(const TW* W, const float* x, const float* g, float eps, int N, int K, float* y,
+                         hipStream_t st) {
+  const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
+  const int waves = (npairs + GV_ROWS / 2 - 1) / (GV_ROWS / 2);
+  const int blocks = (waves + GV_THREADS / 64 - 1) / (GV_THREADS / 64);
+  const size_t lds = (size_t)K * sizeof(float);
+  if (g) hipLaunchKernelGGL((gemv_kernel<TW, EPI, true>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
+  else hipLaunchKernelGGL((gemv_kernel<TW, EPI, false>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
+  return hipGetLastError();
+}
+
+hipError_t gemv(DT wdt, const void* W, const float* x, const float* g, float eps, int N, int K, GvEpi epi,
+                float* y, hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  if ((K * 4) > 64 * 1024 || K % 8) return hipErrorInvalidValue;
+  if (wdt == DT::BF16) {
+    switch (epi) {
+      case GvEpi::STORE: return gemv_t<bf16, (int)GvEpi::STORE>((const bf16*)W, x, g, eps, N, K, y, st);
+      case GvEpi::ADD_F32: return gemv_t<bf16, (int)GvEpi::ADD_F32>((const bf16*)W, x, g, eps, N, K, y, st);
+      case GvEpi::SWIGLU: return gemv_t<bf16, (int)GvEpi::SWIGLU>((const bf16*)W, x, g, eps, N, K, y, st);
+    }
+  } else {
+    switch (epi) {
+      case GvEpi::STORE: return gemv_t<float, (int)GvEpi::STORE>((const float*)W, x, g, eps, N, K, y, st);
+      case GvEpi::ADD_F32: return gemv_t<float, (int)GvEpi::ADD_F32>((const float*)W, x, g, eps, N, K, y, st);
+      case GvEpi::SWIGLU: return gemv_t<float, (int)GvEpi::SWIGLU>((const float*)W, x, g, eps, N, K, y, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------- embedding
+template <typename T>
+__global__ void embed_row_kernel(const int32_t* tok, const T* E, int d, int V, float* h, int* err) {
+  int t = *tok;
+  if (t < 0 || t >= V) {
+    if (threadIdx.x == 0) atomicOr(err, 1);
+    t = 0;
+  }
+  for (int i = threadIdx.x; i < d; i += blockDim.x) h[i] = to_f(E[(long)t * d + i]);
+}
+
+hipError_t embed_row(DT dt, const int32_t* tok, const void* embed, int d, int V, float* h, int* err,
+                     hipStream_t st) {
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(embed_row_kernel<bf16>, dim3(1), dim3(256), 0, st, tok, (const bf16*)embed, d, V, h, err);
+  else
+    hipLaunchKernelGGL(embed_row_kernel<float>, dim3(1), dim3(256), 0, st, tok, (const float*)embed, d, V, h, err);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ RoPE + ring store
+// Rotates q and k of position p (half-split pairs (j, j + dh/2) by the
+// angle table) and stores k, v (and v transposed when vts is given) at ring
+// slot p & (cap - 1).
+template <typename T>
+__global__ void decode_rope_store_kernel(const float* qkv, int H, int Hk, int dh, const int64_t* pos,
+                                         const float2* tab, float* q, T* ks, T* vs, T* vts, int cap) {
+  const int64_t p = *pos;
+  const int half = dh / 2;
+  const float2* tb = tab + p * half;
+  const long slot = p & (cap - 1);
+  for (int i = threadIdx.x; i < (H + Hk) * half; i += blockDim.x) {
+    const int hh = i / half, j = i % half;
+    const float2 cs = tb[j];
+    const float a = qkv[hh * dh + j], b = qkv[hh * dh + j + half];
+    const float ra = a * cs.x - b * cs.y, rb = b * cs.x + a * cs.y;
+    if (hh < H) {
+      q[hh * dh + j] = ra;
+      q[hh * dh + j + half] = rb;
+    } else {
+      const int kh = hh - H;
+      ks[((long)kh * cap + slot) * dh + j] = from_f<T>(ra);
+      ks[((long)kh * cap + slot) * dh + j + half] = from_f<T>(rb);
+    }
+  }
+  for (int i = threadIdx.x; i < Hk * dh; i += blockDim.x) {
+    const int kh = i / dh, j = i % dh;
+    const T v = from_f<T>(qkv[(H + Hk) * dh + i]);
+    vs[((long)kh * cap + slot) * dh + j] = v;
+    if (vts) vts[((long)kh * dh + j) * cap + slot] = v;
+  }
+}
+
+hipError_t decode_rope_store(DT dt, const float* qkv, int H, int Hk, int dh, const int64_t* pos,
+                             const float2* rope_tab, float* q, void* kstore, void* vstore, void* vtstore, int cap,
+                             hipStream_t st) {
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(decode_rope_store_kernel<bf16>, dim3(1), dim3(256), 0, st, qkv, H, Hk, dh, pos, rope_tab, q,
+                       (bf16*)kstore, (bf16*)vstore, (bf16*)vtstore, cap);
+  else
+    hipLaunchKernelGGL(decode_rope_store_kernel<float>, dim3(1), dim3(256), 0, st, qkv, H, Hk, dh, pos, rope_tab, q,
+                       (float*)kstore, (float*)vstore, (float*)vtstore, cap);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- window attention
+// One query per head at position p over keys (p - window, p]. Workgroup
+// (kv head, split) takes a contiguous chunk of the window for the query
+// heads of that key head; LPR lanes cover one key row in 16-byte vectors,
+// so a wave instruction reads 64 / LPR whole rows. Each lane group keeps an
+// online softmax (max, sum, output slice); the groups and waves are merged
+// through LDS into one partial (m, l, o) per (head, split).
+template <typename T, int DH>
+__global__ void __launch_bounds__(256) decode_attn_kernel(const float* q, const T* kst, const T* vst, int H, int Hk,
+                                                          int cap, int window, const int64_t* pos, float scale,
+                                                          int nsplit, float* part) {
+  constexpr int EV = 16 / sizeof(T);     // elements per 16-byte vector
+  constexpr int LPR = DH / EV;           // lanes per key row
+  constexpr int KPW = 64 / LPR;          // keys per wave instruction
+  constexpr int GMAX = 8;                // query heads per key head supported
+  __shared__ float sm[4 * KPW][GMAX], sl[4 * KPW][GMAX];
+  __shared__ float so[4 * KPW][DH];
+  const int kh = blockIdx.x, split = blockIdx.y;
+  const int grp = H / Hk;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int sub = lane % LPR, kg = lane / LPR;  // vector within the row, key slot of the wave
+  const int slotid = wid * KPW + kg;            // 0 .. 4 KPW - 1
+  const int64_t p = *pos;
+  const int64_t lo = p - window + 1 > 0 ? p - window + 1 : 0;
+  const int64_t count = p - lo + 1;
+  const int64_t chunk = ((count + nsplit - 1) / nsplit + 4 * KPW - 1) / (4 * KPW) * (4 * KPW);
+  const int64_t c0 = lo + (int64_t)split * chunk, c1 = min(p + 1, c0 + chunk);
+
+  float qv[GMAX][EV];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+    for (int e = 0; e < EV; ++e) qv[g][e] = g < grp ? q[(kh * grp + g) * DH + sub * EV + e] * scale : 0.f;
+  float m[GMAX], l[GMAX], o[GMAX][EV];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) o[g][e] = 0.f;
+  }
+  const T* kb = kst + (long)kh * cap * DH;
+  const T* vb = vst + (long)kh * cap * DH;
+  for (int64_t t0 = c0; t0 < c1; t0 += 4 * KPW) {
+    const int64_t t = t0 + slotid;
+    const bool ok = t < c1;  // uniform over the LPR lanes of a key row
+    const long slot = (long)(t & (cap - 1));
+    float kv[EV], vv[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) kv[e] = vv[e] = 0.f;
+    if (ok) {
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 a = *(const bf16x8*)(kb + slot * DH + sub * EV);
+        const bf16x8 b = *(const bf16x8*)(vb + slot * DH + sub * EV);
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          kv[e] = (float)a[e];
+          vv[e] = (float)b[e];
+        }
+      } else {
+        const floatx4 a = *(const floatx4*)(kb + slot * DH + sub * EV);
+        const floatx4 b = *(const floatx4*)(vb + slot * DH + sub * EV);
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          kv[e] = a[e];
+          vv[e] = b[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g >= grp) break;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) s += qv[g][e] * kv[e];
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      if (ok) {
+        const float mn = fmaxf(m[g], s);
+        const float c = __expf(m[g] - mn), pe = __expf(s - mn);
+        l[g] = l[g] * c + pe;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) o[g][e] = o[g][e] * c + pe * vv[e];
+        m[g] = mn;
+      }
+    }
+  }
+  // merge the 4 KPW lane groups of the workgroup, one query head at a time
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g >= grp) break;
+    if (sub == 0) {
+      sm[slotid][g] = m[g];
+      sl[slotid][g] = l[g];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g >= grp) break;
+    float M = -INFINITY;
+    for (int i = 0; i < 4 * KPW; ++i) M = fmaxf(M, sm[i][g]);
+    const float w = (m[g] == -INFINITY) ? 0.f : __expf(m[g] - M);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) so[slotid][sub * EV + e] = o[g][e] * w;
+    __syncthreads();
+    float* dst = part + ((long)(kh * grp + g) * nsplit + split) * (DH + 2);
+    for (int dd = threadIdx.x; dd < DH; dd += blockDim.x) {
+      float acc = 0.f;
+      for (int i = 0; i < 4 * KPW; ++i) acc += so[i][dd];
+      dst[dd] = acc;
+    }
+    if (threadIdx.x == 0) {
+      float L = 0.f;
+      for (int i = 0; i < 4 * KPW; ++i)
+        if (sm[i][g] != -INFINITY) L += sl[i][g] * __expf(sm[i][g] - M);
+      dst[DH] = M;
+      dst[DH + 1] = L;
+    }
+    __syncthreads();
+  }
+}
+
+// o[h] = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}
+__global__ void decode_attn_combine_kernel(const float* part, int nsplit, int dh, float* o) {
+  const int h = blockIdx.x;
+  const float* ph = part + (long)h * nsplit * (dh + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ph[s * (dh + 2) + dh]);
+  float L = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = ph[s * (dh + 2) + dh];
+    if (ms != -INFINITY) L += ph[s * (dh + 2) + dh + 1] * __expf(ms - M);
+  }
+  for (int dd = threadIdx.x; dd < dh; dd += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = ph[s * (dh + 2) + dh];
+      if (ms != -INFINITY) acc += ph[s * (dh + 2) + dd] * __expf(ms - M);
+    }
+    o[h * dh + dd] = acc / L;
+  }
+}
+
+template <typename T, int DH>
+static hipError_t decode_attn_t(const float* q, const void* ks, const void* vs, int H, int Hk, int cap,
+                                int window, const int64_t* pos, float* part, float* o, int nsplit,
+                                hipStream_t st) {
+  hipLaunchKernelGGL((decode_attn_kernel<T, DH>), dim3(Hk, nsplit), dim3(256), 0, st, q, (const T*)ks,
+                     (const T*)vs, H, Hk, cap, window, pos, 1.f / sqrtf((float)DH), nsplit, part);
+  hipLaunchKernelGGL(decode_attn_combine_kernel, dim3(H), dim3(128), 0, st, part, nsplit, DH, o);
+  return hipGetLastError();
+}
+
+hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vstore, int H, int Hk, int dh,
+                       int cap, int window, const int64_t* pos, float* part, float* o, int nsplit,
+                       hipStream_t st) {
+  if (H / Hk > 8) return hipErrorInvalidValue;
+  if (dt == DT::BF16) {
+    if (dh == 128) return decode_attn_t<bf16, 128>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);
+    if (dh == 64) return decode_attn_t<bf16, 64>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);
+    if (dh == 16) return decode_attn_t<bf16, 16>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);
+  } else {
+    if (dh == 128) return decode_attn_t<float, 128>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);
+    if (dh == 64) return decode_attn_t<float, 64>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);
+    if (dh == 16) return decode_attn_t<float, 16>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------- position
+__global__ void pos_kernel(int64_t* pos, int64_t value, int add) {
+  if (threadIdx.x == 0) *pos = add ? *pos + 1 : value;
+}
+
+hipError_t bump_pos(int64_t* pos, hipStream_t st) {
+  hipLaunchKernelGGL(pos_kernel, dim3(1), dim3(64), 0, st, pos, (int64_t)0, 1);
+  return hipGetLastError();
+}
+
+hipError_t set_pos(int64_t* pos, int64_t value, hipStream_t st) {
+  hipLaunchKernelGGL(pos_kernel, dim3(1), dim3(64), 0, st, pos, value, 0);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -18,6 +18,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -99,6 +100,9 @@ struct ttt_ctx {
   int64_t* d_pos = nullptr;
   float* dec = nullptr;                      // decode scratch
   int dec_split = 1;
+  int32_t* d_tok = nullptr;                  // decode input token
+  hipStream_t dstream = nullptr;             // decode graph capture stream
+  hipGraphExec_t dgraph = nullptr;           // captured decode blocks
 
   // live per-class timing (ttt_timing_enable / ttt_timing_read)
   struct TRec {
@@ -470,6 +474,58 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
   return TTT_OK;
 }
 
+// Decode blocks of one token: reads the token from d_tok and the position
+// from d_pos (device memory, so the sequence can be captured once and
+// replayed); leaves the final residual row in dec[0 .. d).
+ttt_status decode_blocks(ttt_ctx* c, hipStream_t st) {
+  const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh;
+  const float eps = c->cfg.rms_eps;
+  float* h = c->dec;
+  float* qkv = h + d;
+  float* q = qkv + c->QKV;
+  float* o = q + (size_t)H * dh;
+  float* hm = o + (size_t)H * dh;
+  float* part = hm + std::max(c->F, c->Fd);
+  HIPCHK(c, embed_row(c->dt, c->d_tok, c->embed, d, c->V, h, c->d_err, st));
+  for (int l = 0; l < c->L; ++l) {
+    HIPCHK(c, gemv(c->dt, c->wqkv[l], h, c->attn_norm[l], eps, c->QKV, d, GvEpi::STORE, qkv, st));
+    HIPCHK(c, decode_rope_store(c->dt, qkv, H, Hk, dh, c->d_pos, c->rope, q, c->kring[l], c->vring[l],
+                                c->vtring[l], (int)c->cap, st));
+    HIPCHK(c, decode_attn(c->dt, q, c->kring[l], c->vring[l], H, Hk, dh, (int)c->cap, c->k, c->d_pos, part, o,
+                          c->dec_split, st));
+    HIPCHK(c, gemv(c->dt, c->wo[l], o, nullptr, 0.f, d, H * dh, GvEpi::ADD_F32, h, st));
+    HIPCHK(c, gemv(c->dt, c->w12[l], h, c->mlp_norm[l], eps, 2 * c->F, d, GvEpi::SWIGLU, hm, st));
+    HIPCHK(c, gemv(c->dt, c->w3[l], hm, nullptr, 0.f, d, c->F, GvEpi::ADD_F32, h, st));
+    if (l >= c->s) {
+      // the dynamic MLP under the current fast weights (fp32 masters)
+      const int i = l - c->s;
+      HIPCHK(c, gemv(DT::F32, c->m12[i], h, c->dyn_norm[i], eps, 2 * c->Fd, d, GvEpi::SWIGLU, hm, st));
+      HIPCHK(c, gemv(DT::F32, c->m3[i], hm, nullptr, 0.f, d, c->Fd, GvEpi::ADD_F32, h, st));
+    }
+  }
+  return TTT_OK;
+}
+
+ttt_status capture_decode(ttt_ctx* c) {
+  if (!c->dstream) HIPCHK(c, hipStreamCreateWithFlags(&c->dstream, hipStreamNonBlocking));
+  HIPCHK(c, hipStreamBeginCapture(c->dstream, hipStreamCaptureModeThreadLocal));
+  const ttt_status r = decode_blocks(c, c->dstream);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(c->dstream, &g);
+  if (r != TTT_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return r;
+  }
+  if (e != hipSuccess) return fail(c, TTT_ERR_HIP, std::string("decode capture: ") + hipGetErrorString(e));
+  const hipError_t e2 = hipGraphInstantiate(&c->dgraph, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e2 != hipSuccess) {
+    c->dgraph = nullptr;
+    return fail(c, TTT_ERR_HIP, std::string("decode graph: ") + hipGetErrorString(e2));
+  }
+  return TTT_OK;
+}
+
 }  // namespace
 
 // ==================================================================== C ABI
@@ -641,6 +697,8 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     c->d_err = (int*)p;
     A(&p, 64);
     c->d_pos = (int64_t*)p;
+    A(&p, 64);
+    c->d_tok = (int32_t*)p;
   }
   c->dec_split = 32;
   Af(&c->dec, (size_t)4 * (c->QKV + 2 * Fm + 2 * d + c->H * c->dh) +
@@ -759,16 +817,34 @@ ttt_status ttt_prefill(ttt_ctx* c, const int32_t* tok, int64_t T, float* loss, f
     r = loop_backward(c, a0, n, st);
     if (r != TTT_OK) return r;
   }
+  HIPCHK(c, set_pos(c->d_pos, T, st));
   c->pos = T;
   return TTT_OK;
 }
 
 ttt_status ttt_decode_step(ttt_ctx* c, const int32_t* token, float* logits, void* stream) {
   if (!c) return TTT_ERR_INVALID_ARG;
-  (void)token;
-  (void)logits;
-  (void)stream;
-  return fail(c, TTT_ERR_UNSUPPORTED, "decode not built yet");
+  if (!token || !logits) return fail(c, TTT_ERR_INVALID_ARG, "null token or logits");
+  if (c->pos < 1 || c->pos >= c->max_seq)
+    return fail(c, TTT_ERR_STATE, "decode needs a prefilled context with position < max_seq");
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(c, hipMemcpyAsync(c->d_tok, token, sizeof(int32_t), hipMemcpyDeviceToDevice, st));
+  const char* eg = getenv("TTT_DECODE_GRAPH");
+  const bool use_graph = !(eg && eg[0] == '0');
+  if (use_graph) {
+    if (!c->dgraph) {
+      ttt_status r = capture_decode(c);
+      if (r != TTT_OK) return r;
+    }
+    HIPCHK(c, hipGraphLaunch(c->dgraph, st));
+  } else {
+    ttt_status r = decode_blocks(c, st);
+    if (r != TTT_OK) return r;
+  }
+  HIPCHK(c, gemv(c->dt, c->lm_head, c->dec, c->final_norm, c->cfg.rms_eps, c->V, c->d, GvEpi::STORE, logits, st));
+  HIPCHK(c, bump_pos(c->d_pos, st));
+  ++c->pos;
+  return TTT_OK;
 }
 
 ttt_status ttt_get_fast_weights(ttt_ctx* c, int32_t i, float* w1, float* w2, float* w3, void* stream) {
@@ -836,6 +912,8 @@ void ttt_destroy(ttt_ctx* c) {
   if (!c) return;
   (void)hipDeviceSynchronize();
   for (hipEvent_t e : c->evpool) (void)hipEventDestroy(e);
+  if (c->dgraph) (void)hipGraphExecDestroy(c->dgraph);
+  if (c->dstream) (void)hipStreamDestroy(c->dstream);
   for (void* p : c->allocs) (void)hipFree(p);
   delete c;
 }

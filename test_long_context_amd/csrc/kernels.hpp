@@ -127,22 +127,25 @@ hipError_t attn_bwd_dkdv2(DT dt, const AttnArgs& a, hipStream_t st);
 hipError_t sum_parts_f32(const float* parts, int nparts, long count, float* dst, hipStream_t st);
 
 // ---------------------------------------------------------------- decode
-// y[n] = sum_k x[k] W[n, k] for one row (T weights, float x), with epilogues.
+// y = W x for one fp32 row x (W [N][K] of storage type wdt); with g given,
+// x is first RMS-normalised with gain g. Epilogues: STORE, ADD_F32 (y +=),
+// SWIGLU (W rows 16-interleaved (gate, up); y [N/2] = silu(gate) * up).
 enum class GvEpi : int { STORE = 0, ADD_F32, SWIGLU };
-hipError_t gemv(DT dt, const void* W, const float* x, int N, int K, GvEpi epi, float* y,
-                hipStream_t st);
-// rmsnorm of one row into float.
-hipError_t rmsnorm_row(const float* x, const float* g, int d, float eps, float* y, hipStream_t st);
-// rope + store for one position read from a device counter.
+hipError_t gemv(DT wdt, const void* W, const float* x, const float* g, float eps, int N, int K, GvEpi epi,
+                float* y, hipStream_t st);
+// RoPE of q, k at position *pos; k, v (and v transposed) into ring slot
+// *pos & (cap - 1).
 hipError_t decode_rope_store(DT dt, const float* qkv, int H, int Hk, int dh, const int64_t* pos,
-                             const float2* rope_tab, float* q, void* kstore, void* vstore, int cap,
+                             const float2* rope_tab, float* q, void* kstore, void* vstore, void* vtstore, int cap,
                              hipStream_t st);
-hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vstore, int H, int Hk,
-                       int dh, int cap, int window, const int64_t* pos, float* part, float* o,
-                       int nsplit, hipStream_t st);
-hipError_t embed_row(DT dt, const int32_t* tok, const void* embed, int d, int V, float* h,
-                     int* err, hipStream_t st);
+// One query per head at position *pos over the window; part: [H][nsplit][dh + 2].
+hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vstore, int H, int Hk, int dh,
+                       int cap, int window, const int64_t* pos, float* part, float* o, int nsplit,
+                       hipStream_t st);
+hipError_t embed_row(DT dt, const int32_t* tok, const void* embed, int d, int V, float* h, int* err,
+                     hipStream_t st);
 hipError_t bump_pos(int64_t* pos, hipStream_t st);
+hipError_t set_pos(int64_t* pos, int64_t value, hipStream_t st);
 
 // ---------------------------------------------------------------- E2-TTT
 // Per (head, chunk) scalars: KW_t = eta_t A_t, KM_t = eta_t beta~_t and the
