@@ -16,10 +16,17 @@ symbol, launched by the hoisted prefix and by every mini-batch), timed with
 HIP events on its launch stream during the timed steps -- and the CPU oracle
 timed on a bounded sample of the same workload.
 
-`--copy-probe` instead runs a plain 1 GiB device copy and exits: run under
-`rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE) it gives the factor that turns
-those counters into bytes.
+Counter runs (each under `rocprofv3 --pmc FETCH_SIZE`, then WRITE_SIZE):
+`--copy-probe` runs a plain 1 GiB device copy (the factor that turns the
+counters into bytes); `--attn-replay` runs the distinct attention-forward
+launches of one step at the workload's shapes through the kernel-level entry
+point (tttk_attn_fwd): every prefix slab once, then every mini-batch once.
+`--pmc-summary FETCH WRITE COPY_FETCH COPY_WRITE` turns the four runs'
+counter_collection CSVs into bytes per launch of one step (prefix launches
+weighted by the blocks of the hoisted prefix, mini-batch launches by the
+updated blocks that run attention in the loop).
 """
+import csv
 import hashlib
 import argparse
 import json
@@ -42,11 +49,15 @@ KC = dict(gemm_prefix=0, attn_prefix=1, gemm_loop=2, attn_loop=3, lmhead=4, ce=5
 ROOF_CLASSES = ("attn_prefix", "attn_loop")   # the attention forward kernel
 ROOF_SOURCES = ("test_long_context_amd/csrc/attn2.hip", "test_long_context_amd/csrc/common.hpp")
 
-# HBM traffic of the attention forward at the 3B workload from rocprofv3
-# --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch, averaged over one step's
-# dispatches of the kernel) and the same counters over a 1 GiB copy; valid
-# only for the kernel source they were taken on (sha256 of ROOF_SOURCES).
-TRAFFIC = {}
+# HBM traffic of the attention forward from rocprofv3 --pmc FETCH_SIZE /
+# WRITE_SIZE (--attn-replay, scaled by the --copy-probe counters; printed by
+# --pmc-summary), keyed by (workload, T, source hash): valid only for the
+# kernel source the counters were taken on.
+TRAFFIC = {
+    ("3b", 131072, "63221bd2a0e39b1d"): dict(fetch_bytes_per_launch=50739248, write_bytes_per_launch=23887739,
+                                             fetch_scale=1.9999, write_scale=1.0,
+                                             traffic_bytes_per_launch=125362996),
+}
 
 
 def roof_source_hash() -> str:
@@ -109,6 +120,63 @@ def cpu_baseline(c, w, tok, ntok):
                 sample=f"mini-batch 0 of the same stream: {ntok} positions forward + 1 SGD step, "
                        f"plus the forward-only position {ntok}; {dt:.1f} s on the host",
                 seconds=round(dt, 2))
+
+
+def attn_launches(c: dict, T: int):
+    """(kind, n, pos0) of the distinct attention-forward launches of one step
+    and the number of blocks that make each: the prefix covers blocks 0..s in
+    slabs of up to 16384 positions, the loop blocks s+1..L-1 per mini-batch."""
+    L = c["n_layers"]
+    nd = c["n_dynamic"] or L - (3 * L) // 4
+    s = L - nd
+    slab = max(min(T + 1024, 16384), c["minibatch"])
+    out = [("prefix", min(slab, T - p0), p0, s + 1) for p0 in range(0, T, slab)]
+    out += [("loop", min(c["minibatch"], T - a0), a0, L - s - 1) for a0 in range(0, T, c["minibatch"])]
+    return out
+
+
+def attn_replay(c, T, tla, torch):
+    """The attention forward launches of one step (attn_launches), each once,
+    on random rings of the engine's capacity."""
+    H, Hk, dh, k = c["n_heads"], c["n_kv_heads"], c["head_dim"], c["window"]
+    slab = max(min(T + 1024, 16384), c["minibatch"])
+    cap = 1 << (max(k + max(c["minibatch"], slab), 128) - 1).bit_length()
+    bf = torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(0)
+    K = torch.randn(Hk, cap, dh, device="cuda", generator=g).to(bf)
+    V = torch.randn(Hk, cap, dh, device="cuda", generator=g).to(bf)
+    VT = V.transpose(1, 2).contiguous()
+    q = torch.randn(slab, H, dh, device="cuda", generator=g).to(bf)
+    o = torch.empty(slab, H, dh, dtype=bf, device="cuda")
+    launches = attn_launches(c, T)
+    for kind, n, p0, _ in launches:
+        tla.attn_fwd(q[:n].contiguous() if n < slab else q, K, V, o, None, n, H, Hk, dh, cap, k, p0, vt=VT)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(launches=len(launches))), flush=True)
+
+
+def pmc_summary(c, T, dirs, workload):
+    """Bytes per attention-forward launch of one step from four rocprofv3
+    counter runs (FETCH_SIZE and WRITE_SIZE of --attn-replay and of
+    --copy-probe), each counter scaled by copy bytes / copy counter."""
+    def read(d, name_part):
+        f = os.path.join(d, "run_counter_collection.csv")
+        with open(f) as fh:
+            return [float(r["Counter_Value"]) * 1024 for r in csv.DictReader(fh) if name_part in r["Kernel_Name"]]
+    fetch, write = read(dirs[0], "attn_fwd2"), read(dirs[1], "attn_fwd2")
+    cf, cw = read(dirs[2], "copyBuffer"), read(dirs[3], "copyBuffer")
+    copy_bytes = float(1 << 30)
+    fs, ws = copy_bytes / (sum(cf) / len(cf)), copy_bytes / (sum(cw) / len(cw))
+    launches = attn_launches(c, T)
+    assert len(fetch) == len(write) == len(launches), (len(fetch), len(write), len(launches))
+    tot_n = sum(wt for *_, wt in launches)
+    tf = sum(f * wt for f, (*_, wt) in zip(fetch, launches))
+    tw = sum(x * wt for x, (*_, wt) in zip(write, launches))
+    out = dict(kernel="attn_fwd2_kernel", workload=workload, seq=T, source_sha=roof_source_hash(),
+               fetch_scale=round(fs, 4), write_scale=round(ws, 4), launches_per_step=tot_n,
+               fetch_bytes_per_launch=round(tf / tot_n), write_bytes_per_launch=round(tw / tot_n),
+               traffic_bytes_per_launch=round((tf * fs + tw * ws) / tot_n))
+    print(json.dumps(out), flush=True)
 
 
 def decode_bytes(c: dict, p: int) -> float:
@@ -177,6 +245,8 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="print the per-class timing table")
     ap.add_argument("--copy-probe", action="store_true", help="1 GiB device copy for PMC scaling, then exit")
     ap.add_argument("--decode", action="store_true", help="measure decode latency instead of prefill throughput")
+    ap.add_argument("--attn-replay", action="store_true", help="one step's attention-forward launches, then exit")
+    ap.add_argument("--pmc-summary", nargs=4, metavar="DIR", help="bytes per attention launch from counter runs")
     ap.add_argument("--decode-steps", type=int, default=256)
     args = ap.parse_args()
     if args.copy_probe:
@@ -194,6 +264,12 @@ def main():
 
     c = synth.config(args.workload)
     T = args.seq or c["seq"]
+    if args.pmc_summary:
+        pmc_summary(c, T, args.pmc_summary, args.workload)
+        return
+    if args.attn_replay:
+        attn_replay(c, T, tla, torch)
+        return
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
     w = synth.gen_weights(c, device="cuda")
@@ -255,9 +331,7 @@ def main():
     ach = r_fl / r_n / avg_s / 1e12
     src = roof_source_hash()
     tr = TRAFFIC.get((args.workload, T, src))
-    traffic = None
-    if tr is not None:
-        traffic = round(tr["fetch_kib"] * 1024 * tr["fetch_scale"] + tr["write_kib"] * 1024 * tr["write_scale"])
+    traffic = None if tr is None else tr["traffic_bytes_per_launch"]
     roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=traffic,
                 kernel=f"attn_fwd2_kernel (sliding-window attention forward, head_dim {c['head_dim']})",
