@@ -34,7 +34,7 @@ typedef enum {
 /* C[m, n] = sum_k A(m, k) B(n, k) on MFMA with fp32 accumulation, where
  * A(m, k) = A[m lda + k] if a_kmajor else A[k lda + m], and
  * B(n, k) = B[n ldb + k] if b_kmajor else B[k ldb + n];
- * B2 (optional, bf16, NT layout, SWIGLU/ADD_F32 only) is a second term
+ * B2 (optional, bf16, NT layout, SWIGLU/ADD_F32/PARTIAL only) is a second term
  * added to B. The contiguous dimension of A and B must be a multiple of 8
  * and the pointers 16-byte aligned. kchunk > 0 splits K into chunks (a
  * multiple of 64) for TTTK_EPI_PARTIAL. tile (bf16; fp32 always uses

@@ -47,51 +47,161 @@ hipError_t embed_gather(DT dt, const int32_t* tok, int n, const void* E, int d, 
 }
 
 // ----------------------------------------------------------------- RMSNorm
+// One workgroup per row; each thread keeps its float4 chunks of the row in
+// registers between the reduction and the output pass (d <= RMS_MAXV * 4 * RB;
+// larger rows take the strided loops).
+static constexpr int RMS_MAXV = 8;
+
 template <typename T>
-__global__ void rms_fwd_kernel(const float* x, const float* g, int d, float eps, T* y, float* r) {
+__device__ __forceinline__ void store4(T* p, float4 v);
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float4 v) {
+  bf16x4 w;
+  w[0] = (bf16)v.x;
+  w[1] = (bf16)v.y;
+  w[2] = (bf16)v.z;
+  w[3] = (bf16)v.w;
+  *(bf16x4*)p = w;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float4 v) {
+  *(float4*)p = v;
+}
+__device__ __forceinline__ float4 f4add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+
+// x = x_in + sum_p parts[p] (pending split-K residual updates); x_out and
+// save (either may be null) receive x; y = g * x * r with r = rsqrt(mean x^2 + eps).
+template <typename T>
+__global__ void __launch_bounds__(RB) rms_fwd_kernel(const float* x_in, const float* parts, int nsplit, long pstride,
+                                                     float* x_out, float* save, const float* g, int d, float eps,
+                                                     T* y, float* r) {
   __shared__ float sh[RB / 64];
   const long t = blockIdx.x;
-  const float* xr = x + t * d;
+  const int nv = d / 4;
+  float4 xv[RMS_MAXV];
   float ss = 0.f;
-  for (int j = threadIdx.x; j < d; j += blockDim.x) ss += xr[j] * xr[j];
+  const bool fits = nv <= RMS_MAXV * RB;
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < RMS_MAXV; ++i) {
+      const int v = threadIdx.x + i * RB;
+      if (v < nv) {
+        float4 a = ((const float4*)(x_in + t * d))[v];
+        for (int p = 0; p < nsplit; ++p) a = f4add(a, ((const float4*)(parts + p * pstride + t * d))[v]);
+        xv[i] = a;
+        ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+      }
+    }
+  } else {
+    for (int j = threadIdx.x; j < d; j += RB) {
+      float a = x_in[t * d + j];
+      for (int p = 0; p < nsplit; ++p) a += parts[p * pstride + t * d + j];
+      ss += a * a;
+    }
+  }
   ss = block_sum(ss, sh);
   const float rr = rsqrtf(ss / d + eps);
-  for (int j = threadIdx.x; j < d; j += blockDim.x) y[t * d + j] = from_f<T>(g[j] * xr[j] * rr);
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < RMS_MAXV; ++i) {
+      const int v = threadIdx.x + i * RB;
+      if (v < nv) {
+        const float4 a = xv[i];
+        if (x_out) ((float4*)(x_out + t * d))[v] = a;
+        if (save) ((float4*)(save + t * d))[v] = a;
+        const float4 gg = ((const float4*)g)[v];
+        store4<T>(y + t * d + 4 * v, make_float4(gg.x * a.x * rr, gg.y * a.y * rr, gg.z * a.z * rr, gg.w * a.w * rr));
+      }
+    }
+  } else {
+    for (int j = threadIdx.x; j < d; j += RB) {
+      float a = x_in[t * d + j];
+      for (int p = 0; p < nsplit; ++p) a += parts[p * pstride + t * d + j];
+      if (x_out) x_out[t * d + j] = a;
+      if (save) save[t * d + j] = a;
+      y[t * d + j] = from_f<T>(g[j] * a * rr);
+    }
+  }
   if (threadIdx.x == 0) r[t] = rr;
+}
+
+hipError_t rmsnorm_fwd_fused(DT dt, const float* x_in, const float* parts, int nsplit, float* x_out, float* save,
+                             const float* g, int n, int d, float eps, void* y, float* r, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (d % 4) return hipErrorInvalidValue;
+  const long ps = (long)n * d;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(rms_fwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, x_in, parts, nsplit, ps, x_out, save, g, d,
+                       eps, (bf16*)y, r);
+  else
+    hipLaunchKernelGGL(rms_fwd_kernel<float>, dim3(n), dim3(RB), 0, st, x_in, parts, nsplit, ps, x_out, save, g, d,
+                       eps, (float*)y, r);
+  return hipGetLastError();
 }
 
 hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, float eps, void* y,
                        float* r, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  if (dt == DT::BF16)
-    hipLaunchKernelGGL(rms_fwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, x, g, d, eps, (bf16*)y, r);
-  else
-    hipLaunchKernelGGL(rms_fwd_kernel<float>, dim3(n), dim3(RB), 0, st, x, g, d, eps, (float*)y, r);
-  return hipGetLastError();
+  return rmsnorm_fwd_fused(dt, x, nullptr, 0, nullptr, nullptr, g, n, d, eps, y, r, st);
 }
 
-// dx = r (g dy) - x r^3 mean((g dy) x); dh (+)= dx; dh_t = T(dh).
+// dx = r (g dy) - x r^3 mean((g dy) x); dh (+)= dx; dh_t = T(dh); dy is the
+// sum of nsplit partials (read once, kept in registers).
 template <typename T>
-__global__ void rms_bwd_kernel(const float* dy, int nsplit, long sstride, const float* x,
-                               const float* g, const float* r, int d, float* dh, T* dh_t, int acc) {
+__global__ void __launch_bounds__(RB) rms_bwd_kernel(const float* dy, int nsplit, long sstride, const float* x,
+                                                     const float* g, const float* r, int d, float* dh, T* dh_t,
+                                                     int acc) {
   __shared__ float sh[RB / 64];
   const long t = blockIdx.x;
   const float rr = r[t];
+  const int nv = d / 4;
+  const bool fits = nv <= RMS_MAXV * RB;
+  float4 gv[RMS_MAXV];
   float dot = 0.f;
-  for (int j = threadIdx.x; j < d; j += blockDim.x) {
-    float v = 0.f;
-    for (int s = 0; s < nsplit; ++s) v += dy[s * sstride + t * d + j];
-    dot += g[j] * v * x[t * d + j];
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < RMS_MAXV; ++i) {
+      const int v = threadIdx.x + i * RB;
+      if (v < nv) {
+        float4 a = ((const float4*)(dy + t * d))[v];
+        for (int s = 1; s < nsplit; ++s) a = f4add(a, ((const float4*)(dy + s * sstride + t * d))[v]);
+        const float4 gg = ((const float4*)g)[v];
+        a = make_float4(a.x * gg.x, a.y * gg.y, a.z * gg.z, a.w * gg.w);  // g dy
+        gv[i] = a;
+        const float4 xx = ((const float4*)(x + t * d))[v];
+        dot += a.x * xx.x + a.y * xx.y + a.z * xx.z + a.w * xx.w;
+      }
+    }
+  } else {
+    for (int j = threadIdx.x; j < d; j += RB) {
+      float v = 0.f;
+      for (int s = 0; s < nsplit; ++s) v += dy[s * sstride + t * d + j];
+      dot += g[j] * v * x[t * d + j];
+    }
   }
   dot = block_sum(dot, sh) / d;
   const float c = rr * rr * rr * dot;
-  for (int j = threadIdx.x; j < d; j += blockDim.x) {
-    float v = 0.f;
-    for (int s = 0; s < nsplit; ++s) v += dy[s * sstride + t * d + j];
-    float o = rr * g[j] * v - x[t * d + j] * c;
-    if (acc) o += dh[t * d + j];
-    dh[t * d + j] = o;
-    if (dh_t) dh_t[t * d + j] = from_f<T>(o);
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < RMS_MAXV; ++i) {
+      const int v = threadIdx.x + i * RB;
+      if (v < nv) {
+        const float4 a = gv[i];
+        const float4 xx = ((const float4*)(x + t * d))[v];
+        float4 o = make_float4(rr * a.x - xx.x * c, rr * a.y - xx.y * c, rr * a.z - xx.z * c, rr * a.w - xx.w * c);
+        if (acc) o = f4add(o, ((const float4*)(dh + t * d))[v]);
+        ((float4*)(dh + t * d))[v] = o;
+        if (dh_t) store4<T>(dh_t + t * d + 4 * v, o);
+      }
+    }
+  } else {
+    for (int j = threadIdx.x; j < d; j += RB) {
+      float v = 0.f;
+      for (int s = 0; s < nsplit; ++s) v += dy[s * sstride + t * d + j];
+      float o = rr * g[j] * v - x[t * d + j] * c;
+      if (acc) o += dh[t * d + j];
+      dh[t * d + j] = o;
+      if (dh_t) dh_t[t * d + j] = from_f<T>(o);
+    }
   }
 }
 
@@ -99,6 +209,7 @@ hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const
                        const float* r, int n, int d, float* dh, void* dh_t, int accumulate,
                        hipStream_t st) {
   if (n <= 0) return hipSuccess;
+  if (d % 4 || nsplit < 1) return hipErrorInvalidValue;
   const long ss = (long)n * d;
   if (dt == DT::BF16)
     hipLaunchKernelGGL(rms_bwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, dy, nsplit, ss, x, g, r, d, dh,

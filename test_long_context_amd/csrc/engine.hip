@@ -101,6 +101,14 @@ struct ttt_ctx {
   float* dec = nullptr;                      // decode scratch
   int dec_split = 1;
   int32_t* d_tok = nullptr;                  // decode input token
+  // fast-weight updates run on a side stream, overlapping the rest of the
+  // backward; their inputs are per dynamic block so that the main stream
+  // never overwrites what an update still reads
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> ev_dyn;            // per dynamic block: its dW inputs are ready
+  hipEvent_t ev_join = nullptr;              // side stream done with this mini-batch
+  std::vector<void*> ghd_t;                  // [b, d] gradient into each dynamic MLP (storage dtype)
+  std::vector<void*> dh12d;                  // [b, 2 Fd] SwiGLU pre-activation gradients per dynamic block
   hipStream_t dstream = nullptr;             // decode graph capture stream
   hipGraphExec_t dgraph = nullptr;           // captured decode blocks
 
@@ -357,49 +365,74 @@ ttt_status run_prefix(ttt_ctx* c, const int32_t* tok, int64_t T, hipStream_t st)
 }
 
 // ------------------------------------------------------------ loop phase
+// Residual-stream product C[M, N] += A B^T at a mini-batch's row count: too
+// few output tiles to fill the CUs, so K is split and the partial sums are
+// left in c->part for the next fused RMSNorm to add (returns their count).
+ttt_status gemm_resid(ttt_ctx* c, int kind, const void* A, long lda, const void* B, long ldb, const void* B2, int M,
+                      int N, int K, int* np, hipStream_t st) {
+  const int gran = gemm_k_granule(c->dt);
+  int s = 1;
+  if (c->dt == DT::BF16) {
+    const int bm = 256, bn = B2 ? 128 : 256;
+    const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    s = std::max(1, std::min(256 / tiles, K / 512));
+  }
+  s = std::min(s, c->max_split);
+  int chunk = (K + s - 1) / s;
+  chunk = (chunk + gran - 1) / gran * gran;
+  s = (K + chunk - 1) / chunk;
+  GemmArgs g = ga(A, lda, B, ldb, M, N, K, c->part, N);
+  g.B2 = B2;
+  g.kchunk = chunk;
+  if (c->dt == DT::BF16) g.tile = 5;
+  *np = s;
+  TCALL(kind, gfl(M, N, K) * (B2 ? 2.0 : 1.0), 0, gemm(c->dt, true, true, Epi::PARTIAL, g, st));
+  return TTT_OK;
+}
+
 ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipStream_t st) {
   const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s, F = c->F, Fd = c->Fd;
   const float eps = c->cfg.rms_eps;
   float* hl = c->hl;
-  TCALL(KC_OT, 0, 0, copy_f32(c->hres + a0 * d, hl, (size_t)n * d, st));
+  int np = 0;  // split-K partial sums of the last residual product, pending in c->part
   for (int l = s; l < c->L; ++l) {
     const int i = l - s;
     if (l > s) {
-      // attention sublayer
-      TCALL(KC_OT, 0, 0, copy_f32(hl, c->h_att[i], (size_t)n * d, st));
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, hl, c->attn_norm[l], n, d, eps, c->xn, c->r_att[i], st));
+      // attention sublayer (adds the pending dynamic-MLP output of block l-1)
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_att[i], c->attn_norm[l], n, d, eps,
+                                            c->xn, c->r_att[i], st));
       TCALL(KC_GL, gfl(n, QKV, d), 0,
             gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
       TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, a0, c->rope, c->q_l[i], c->kring[l],
                                       c->vring[l], c->vtring[l], (int)c->cap, 0, st));
       AttnArgs a = attn_args(c, l, c->q_l[i], c->o_l[i], c->lse[i], n, a0);
       TCALL(KC_AL, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_fwd_any(c->dt, a, st));
-      TCALL(KC_GL, gfl(n, d, H * dh), 0,
-            gemm(c->dt, true, true, Epi::ADD_F32, ga(c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, hl, d), st));
+      RUN(gemm_resid(c, KC_GL, c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, nullptr, n, d, H * dh, &np, st));
       // static MLP sublayer
-      TCALL(KC_OT, 0, 0, copy_f32(hl, c->h_mlp[i], (size_t)n * d, st));
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, hl, c->mlp_norm[l], n, d, eps, c->xn, c->r_mlp[i], st));
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_mlp[i], c->mlp_norm[l], n, d, eps,
+                                            c->xn, c->r_mlp[i], st));
       GemmArgs g = ga(c->xn, d, c->w12[l], d, n, 2 * F, d, c->h12_s[i], 2 * F);
       g.C2 = c->hmid;
       TCALL(KC_GL, gfl(n, 2 * F, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
-      TCALL(KC_GL, gfl(n, d, F), 0,
-            gemm(c->dt, true, true, Epi::ADD_F32, ga(c->hmid, F, c->w3[l], F, n, d, F, hl, d), st));
+      RUN(gemm_resid(c, KC_GL, c->hmid, F, c->w3[l], F, nullptr, n, d, F, &np, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_dyn[i], c->dyn_norm[i], n, d, eps,
+                                            c->xn_d[i], c->r_dyn[i], st));
+    } else {
+      // block s: the residual stream comes from the hoisted prefix
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, c->hres + a0 * d, nullptr, 0, hl, c->h_dyn[i], c->dyn_norm[i], n,
+                                            d, eps, c->xn_d[i], c->r_dyn[i], st));
     }
     // dynamic MLP sublayer under the current fast weights
-    TCALL(KC_OT, 0, 0, copy_f32(hl, c->h_dyn[i], (size_t)n * d, st));
-    TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, hl, c->dyn_norm[i], n, d, eps, c->xn_d[i], c->r_dyn[i], st));
     // (bf16: the fp32 master enters as two bf16 terms, working + low, so that
     // updates below half a bf16 ulp reach the forward)
     GemmArgs g = ga(c->xn_d[i], d, c->dw12[i], d, n, 2 * Fd, d, c->h12_d[i], 2 * Fd);
     g.C2 = c->hm_d[i];
     g.B2 = c->dw12_lo[i];
     TCALL(KC_GL, gfl(n, 2 * Fd, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
-    GemmArgs g3 = ga(c->hm_d[i], Fd, c->dw3[i], Fd, n, d, Fd, hl, d);
-    g3.B2 = c->dw3_lo[i];
-    TCALL(KC_GL, gfl(n, d, Fd), 0, gemm(c->dt, true, true, Epi::ADD_F32, g3, st));
+    RUN(gemm_resid(c, KC_GL, c->hm_d[i], Fd, c->dw3[i], Fd, c->dw3_lo[i], n, d, Fd, &np, st));
   }
-  TCALL(KC_OT, 0, 0, copy_f32(hl, c->h_f, (size_t)n * d, st));
-  TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, hl, c->final_norm, n, d, eps, c->xn, c->r_f, st));
+  TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_f, c->final_norm, n, d, eps, c->xn, c->r_f,
+                                        st));
   TCALL(KC_LM, gfl(n, c->V, d), 0,
         gemm(c->dt, true, true, Epi::STORE_F32, ga(c->xn, d, c->lm_head, d, n, c->V, d, c->logits, c->V), st));
   return TTT_OK;
@@ -410,26 +443,32 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
   const float lr = c->cfg.alpha;
   const double upd_bytes = 8.0 + (c->dt == DT::F32 ? 0.0 : (double)c->es);  // master r/w + working copy
   int ns = 1;
+  const int nd = c->nd;
   // lm_head^T and the final norm
   RUN(gemm_nn_split(c, KC_LM, c->dz, c->V, c->lm_head, d, n, d, c->V, c->part, &ns, st));
-  TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_f, c->final_norm, c->r_f, n, d, c->gh, c->gh_t, 0, st));
+  TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_f, c->final_norm, c->r_f, n, d, c->gh, c->ghd_t[nd - 1], 0, st));
   for (int l = c->L - 1; l >= s; --l) {
     const int i = l - s;
+    void* gt = c->ghd_t[i];
     // dynamic MLP: dHmid = dY W3 with the SwiGLU backward in the epilogue
     {
-      GemmArgs g = ga(c->gh_t, d, c->dw3[i], Fd, n, Fd, d, c->dh12, 2 * Fd);
+      GemmArgs g = ga(gt, d, c->dw3[i], Fd, n, Fd, d, c->dh12d[i], 2 * Fd);
       g.X = c->h12_d[i];
       TCALL(KC_GL, gfl(n, Fd, d), 0, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
     }
-    if (l > s) RUN(gemm_nn_split(c, KC_GL, c->dh12, 2 * Fd, c->dw12[i], d, n, d, 2 * Fd, c->part, &ns, st));
-    // dW3 = dY^T Hmid and dW12 = dH12^T U, with W -= alpha dW in the epilogue
+    if (l > s) RUN(gemm_nn_split(c, KC_GL, c->dh12d[i], 2 * Fd, c->dw12[i], d, n, d, 2 * Fd, c->part, &ns, st));
+    // dW3 = dY^T Hmid and dW12 = dH12^T U, with W -= alpha dW in the epilogue,
+    // on the side stream once this block's products with the old W are queued
+    HIPCHK(c, hipEventRecord(c->ev_dyn[i], st));
+    HIPCHK(c, hipStreamWaitEvent(c->side, c->ev_dyn[i], 0));
     {
-      GemmArgs g = ga(c->gh_t, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
+      hipStream_t st = c->side;
+      GemmArgs g = ga(gt, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
       g.C2 = c->dw3[i];
       g.C3 = c->dw3_lo[i];
       g.scale = lr;
       TCALL(KC_SGD, gfl(d, Fd, n), (double)d * Fd * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g, st));
-      GemmArgs g2 = ga(c->dh12, 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
+      GemmArgs g2 = ga(c->dh12d[i], 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
       g2.C2 = c->dw12[i];
       g2.C3 = c->dw12_lo[i];
       g2.scale = lr;
@@ -468,9 +507,12 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       }
       TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, c->dq, qp, c->dk, c->dv, kp, n, H, Hk, dh, a0, c->rope, c->dqkv, st));
       RUN(gemm_nn_split(c, KC_GL, c->dqkv, QKV, c->wqkv[l], d, n, d, QKV, c->part, &ns, st));
-      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->gh_t, 1, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->ghd_t[i - 1], 1, st));
     }
   }
+  // the next mini-batch's forward reads the updated fast weights
+  HIPCHK(c, hipEventRecord(c->ev_join, c->side));
+  HIPCHK(c, hipStreamWaitEvent(st, c->ev_join, 0));
   return TTT_OK;
 }
 
@@ -691,6 +733,17 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   Af(&c->dk, (size_t)(c->H / c->Hk) * b * c->Hk * c->dh);
   Af(&c->dv, (size_t)(c->H / c->Hk) * b * c->Hk * c->dh);
   A(&c->dqkv, (size_t)b * c->QKV * es);
+  c->ghd_t.assign(nd, nullptr);
+  c->dh12d.assign(nd, nullptr);
+  for (int i = 0; i < nd && ok; ++i) {
+    A(&c->ghd_t[i], (size_t)b * d * es);
+    A(&c->dh12d[i], (size_t)b * 2 * c->Fd * es);
+  }
+  if (ok && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) ok = false;
+  c->ev_dyn.assign(nd, nullptr);
+  for (int i = 0; i < nd && ok; ++i)
+    if (hipEventCreateWithFlags(&c->ev_dyn[i], hipEventDisableTiming) != hipSuccess) ok = false;
+  if (ok && hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess) ok = false;
   {
     void* p = nullptr;
     A(&p, 64);
@@ -914,6 +967,10 @@ void ttt_destroy(ttt_ctx* c) {
   for (hipEvent_t e : c->evpool) (void)hipEventDestroy(e);
   if (c->dgraph) (void)hipGraphExecDestroy(c->dgraph);
   if (c->dstream) (void)hipStreamDestroy(c->dstream);
+  for (hipEvent_t e : c->ev_dyn)
+    if (e) (void)hipEventDestroy(e);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->side) (void)hipStreamDestroy(c->side);
   for (void* p : c->allocs) (void)hipFree(p);
   delete c;
 }

@@ -10,6 +10,7 @@ hipError_t gemm_nt(DT dt, Epi e, int cfg, const GemmArgs& g, hipStream_t st) {
     const int c = cfg;
     if (e == Epi::SWIGLU) return gemm_cfg<bf16, true, true, (int)Epi::SWIGLU, true>(c, g, st);
     if (e == Epi::ADD_F32) return gemm_cfg<bf16, true, true, (int)Epi::ADD_F32, true>(c, g, st);
+    if (e == Epi::PARTIAL) return gemm_cfg<bf16, true, true, (int)Epi::PARTIAL, true>(c, g, st);
     return hipErrorInvalidValue;
   }
   if (dt == DT::BF16) return gemm_by_epi<bf16, true, true>(e, cfg, g, st);

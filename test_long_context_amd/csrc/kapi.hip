@@ -30,7 +30,7 @@ extern "C" ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajo
   if (epi == TTTK_EPI_SGD && !C2) return TTT_ERR_INVALID_ARG;
   if (epi == TTTK_EPI_PARTIAL && kchunk > 0 && kchunk % gemm_k_granule(to_dt(dtype))) return TTT_ERR_INVALID_ARG;
   if (B2 && (dtype != TTT_BF16 || !a_kmajor || !b_kmajor ||
-             (epi != TTTK_EPI_SWIGLU && epi != TTTK_EPI_ADD_F32) || !al16(B2)))
+             (epi != TTTK_EPI_SWIGLU && epi != TTTK_EPI_ADD_F32 && epi != TTTK_EPI_PARTIAL) || !al16(B2)))
     return TTT_ERR_INVALID_ARG;
   GemmArgs g{};
   g.A = A;

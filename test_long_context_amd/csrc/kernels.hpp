@@ -55,6 +55,11 @@ int gemm_k_granule(DT dt);
 hipError_t embed_gather(DT dt, const int32_t* tok, int n, const void* embed, int d, float* h,
                         int V, int* err, hipStream_t st);
 // y (T) = g * x * r, r = rsqrt(mean(x^2) + eps); x float [n, d]; r float [n].
+// x = x_in + sum of nsplit partials ([nsplit][n][d], pending split-K
+// residual updates; parts may be null when nsplit = 0); x_out and save
+// (either may be null) receive x; y = RMSNorm(x) * g, r = 1 / rms.
+hipError_t rmsnorm_fwd_fused(DT dt, const float* x_in, const float* parts, int nsplit, float* x_out, float* save,
+                             const float* g, int n, int d, float eps, void* y, float* r, hipStream_t st);
 hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, float eps, void* y,
                        float* r, hipStream_t st);
 // dh[t] += rmsnorm_bwd(dy[t]) where dy = sum over nsplit partials of

@@ -165,3 +165,35 @@ def test_gemm_3b_shapes_sampled(name, M, N, K, lay, split):
     # fp32 accumulation over K terms of size ~0.25: error ~ sqrt(K) * 2^-24 * |terms|
     tol = 1e-5 * max(1.0, float(want.abs().max()))
     assert float((got - want).abs().max()) < tol, (name, float((got - want).abs().max()))
+
+
+@pytest.mark.parametrize("epi", ["add_f32", "partial", "swiglu"])
+def test_gemm_two_term_b(epi):
+    """B2 adds a second bf16 term to B (the fast weights' low part):
+    C = A (B + B2)^T, for the epilogues that take it."""
+    g = torch.Generator().manual_seed(16)
+    M, N, K = 392, 320, 456
+    A = rnd(g, M * K)
+    B = rnd(g, N * K)
+    B2 = rnd(g, N * K, scale=0.004)
+    acc = logical(A, M, K, True) @ (logical(B, N, K, True) + logical(B2, N, K, True)).T
+    Ad, Bd, B2d = A.to(dev), B.to(dev), B2.to(dev)
+    for t in (0, 1, 3, 5):
+        say(f"gemm two-term {epi} tile {t}")
+        if epi == "add_f32":
+            C = torch.zeros(M * N, device=dev)
+            tla.gemm(Ad, Bd, M, N, K, epi, C, B2=B2d, tile=t)
+            got = C.cpu().double().view(M, N)
+        elif epi == "partial":
+            nsp = (K + 127) // 128
+            C = torch.empty(nsp * M * N, device=dev)
+            tla.gemm(Ad, Bd, M, N, K, epi, C, B2=B2d, tile=t, kchunk=128)
+            got = C.cpu().double().view(nsp, M, N).sum(0)
+        else:
+            C = torch.empty(M * N, dtype=bf, device=dev)
+            C2 = torch.empty(M * N // 2, dtype=bf, device=dev)
+            tla.gemm(Ad, Bd, M, N, K, epi, C, C2=C2, B2=B2d, tile=t)
+            got = C.cpu().double().view(M, N)
+            assert float((got - acc).abs().max()) <= float(acc.abs().max()) * 2 ** -8
+            continue
+        assert float((got - acc).abs().max() / acc.abs().max()) < 1e-5, (epi, t)
