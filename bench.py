@@ -145,7 +145,10 @@ def attn_replay(c, T, tla, torch):
     g = torch.Generator(device="cuda").manual_seed(0)
     K = torch.randn(Hk, cap, dh, device="cuda", generator=g).to(bf)
     V = torch.randn(Hk, cap, dh, device="cuda", generator=g).to(bf)
-    VT = V.transpose(1, 2).contiguous()
+    sl = torch.arange(cap, device="cuda")
+    perm = (sl & ~15) | (sl & 3) | ((sl & 4) << 1) | ((sl & 8) >> 1)  # the store's slot order
+    VT = torch.empty(Hk, dh, cap, dtype=bf, device="cuda")
+    VT[:, :, perm] = V.transpose(1, 2)
     q = torch.randn(slab, H, dh, device="cuda", generator=g).to(bf)
     o = torch.empty(slab, H, dh, dtype=bf, device="cuda")
     launches = attn_launches(c, T)

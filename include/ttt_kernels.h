@@ -51,7 +51,9 @@ ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajor, int32_t 
  * (q: [n, H, dh]) over a key/value store k, v: [Hk][cap][dh] indexed by
  * position & (cap - 1) (cap a power of two >= 64; every key the queries see
  * must already be stored); vt (optional): the values transposed,
- * [Hk][dh][cap]. o: [n, H, dh]; lse: float [H, n] or NULL. variant: 0 =
+ * [Hk][dh][cap], slot s of the store at position (s & ~15) | (s & 3) |
+ * ((s & 4) << 1) | ((s & 8) >> 1) (bits 2 and 3 swapped inside each block of
+ * 16). o: [n, H, dh]; lse: float [H, n] or NULL. variant: 0 =
  * chosen from the shape, 1 = 16x16 MFMA kernel, 2 / 3 = 32x32 MFMA kernel
  * with 32 / 64 queries per wave (bf16, dh 64/128, needs vt). */
 ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, const void* vt,

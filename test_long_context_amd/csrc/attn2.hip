@@ -11,8 +11,9 @@
 // query l % 32 and the softmax statistics stay lane-local (one exchange with
 // lane l ^ 32). The P V product is O^T = V^T P^T with P^T read from the
 // score registers; its contraction slot 8 g + j maps to key 4 g + j
-// (j < 4) or 8 + 4 g + (j - 4) of each 16-key group, so V^T fragments are
-// two 8-byte LDS reads. Softmax runs in base 2 (scale folded with log2 e);
+// (j < 4) or 8 + 4 g + (j - 4) of each 16-key group, and the transposed
+// value store keeps each 16-key group in that order (vt_slot), so a V^T
+// fragment is one 16-byte LDS read. Softmax runs in base 2 (scale folded with log2 e);
 // masks are evaluated only on tiles the window or the diagonal cuts.
 #include <math.h>
 
@@ -30,8 +31,9 @@ template <int DH>
 __device__ __forceinline__ int kswz(int key, int v) {  // K tile [64][DH], 16-byte vectors
   return key * DH + ((v ^ (key & (DH / 8 - 1))) << 3);
 }
-__device__ __forceinline__ int vswz(int row, int v) {  // V^T tile [DH][64]
-  return row * 64 + ((v ^ (row & 7)) << 3);
+__device__ __forceinline__ int vswz(int row, int v) {  // V^T tile [DH][64], rows of 128 bytes
+  // consecutive rows alternate bank halves; row pairs take different slots
+  return row * 64 + ((v ^ ((row >> 1) & 7)) << 3);
 }
 }  // namespace
 
@@ -128,7 +130,7 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
     for (int i = 0; i < NIV / 4; ++i) {
       const int j = wid + 4 * i;
       const int row = j * 8 + lane / 8, p = lane % 8;
-      const int v = p ^ (row & 7);
+      const int v = p ^ ((row >> 1) & 7);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vdst + j * 512), 16,
                                                (uint32_t)((row * a.cap + slot + v * 8) * 2), 0, 0, 0);
     }
@@ -206,15 +208,12 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int ko = kb * 32 + 16 * u + 4 * lg;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const int row = db * 32 + lr;
-            const bf16x4v lo = *(const bf16x4v*)(vs_ + vswz(row, ko >> 3) + (ko & 7));
-            const bf16x4v hi = *(const bf16x4v*)(vs_ + vswz(row, (ko + 8) >> 3) + ((ko + 8) & 7));
-            bf16x8 vf;
-            vf[0] = lo[0]; vf[1] = lo[1]; vf[2] = lo[2]; vf[3] = lo[3];
-            vf[4] = hi[0]; vf[5] = hi[1]; vf[6] = hi[2]; vf[7] = hi[3];
+            // keys of this lane's contraction slots are positions
+            // 16 u + 8 lg .. + 7 of the tile (vt_slot order): one vector
+            const bf16x8 vf = *(const bf16x8*)(vs_ + vswz(row, 4 * kb + 2 * u + lg));
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) mma32(o[qb][db], vf, pf[kb][u][qb]);
           }

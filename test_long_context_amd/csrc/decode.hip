@@ -206,7 +206,7 @@ __global__ void decode_rope_store_kernel(const float* qkv, int H, int Hk, int dh
     const int kh = i / dh, j = i % dh;
     const T v = from_f<T>(qkv[(H + Hk) * dh + i]);
     vs[((long)kh * cap + slot) * dh + j] = v;
-    if (vts) vts[((long)kh * dh + j) * cap + slot] = v;
+    if (vts) vts[((long)kh * dh + j) * cap + vt_slot(slot)] = v;
   }
 }
 

@@ -255,7 +255,7 @@ __global__ void rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, 
       const int kh = i / dh, j = i % dh;
       const T v = row[(H + Hk) * dh + i];
       vs[((long)kh * cap + slot) * dh + j] = v;
-      if (vts) vts[((long)kh * dh + j) * cap + slot] = v;
+      if (vts) vts[((long)kh * dh + j) * cap + vt_slot(slot)] = v;
     }
 }
 

@@ -95,11 +95,19 @@ hipError_t fill_f32(float* p, float v, size_t n, hipStream_t st);
 hipError_t fill_zero_bytes(void* p, size_t nbytes, hipStream_t st);
 
 // ------------------------------------------------------------------- attention
+// Position of ring slot s in the transposed value store: inside each block
+// of 16 slots, bits 2 and 3 are swapped, so that the eight keys one lane
+// feeds to a 32x32x16 MFMA contraction (keys 4g .. 4g+3 and 8+4g .. 11+4g of
+// a 16-key block) are eight consecutive positions.
+__host__ __device__ __forceinline__ long vt_slot(long s) {
+  return (s & ~15L) | (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1);
+}
+
 struct AttnArgs {
   const void* q;      // [n, H, dh] (T) queries at positions pos0 + i
   const void* k;      // key store [Hk][cap][dh] (T)
   const void* v;      // value store [Hk][cap][dh] (T)
-  const void* vt;     // transposed value store [Hk][dh][cap] (T), or null
+  const void* vt;     // transposed value store [Hk][dh][cap] (T), slots at vt_slot(), or null
   void* o;            // [n, H, dh] (T)
   float* lse;         // [H][n] (may be null)
   int n, H, Hk, dh, cap, window;

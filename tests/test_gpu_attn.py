@@ -73,7 +73,13 @@ def test_attention_fwd_bwd(case):
     o_ref, lse_ref, D_ref, dq_ref, dk_ref, dv_ref = reference(q, Kr, Vr, dO, n, H, Hk, dh, cap, window, pos0)
 
     qd, Kd, Vd, dOd = q.to(dev), Kr.to(dev), Vr.to(dev), dO.to(dev)
-    VTd = Vd.transpose(1, 2).contiguous()
+    # transposed values with the store's slot order inside blocks of 16
+    # (bits 2 and 3 of the slot swapped; include/ttt_kernels.h)
+    sl = torch.arange(cap)
+    perm = (sl & ~15) | (sl & 3) | ((sl & 4) << 1) | ((sl & 8) >> 1)
+    VT = torch.empty(Hk, dh, cap, dtype=bf)
+    VT[:, :, perm] = Vr.transpose(1, 2)
+    VTd = VT.contiguous().to(dev)
     for variant in (1, 2, 3):
         say(f"attn fwd variant {variant} case {case}")
         o = torch.full((n, H, dh), float("nan"), dtype=bf, device=dev)
