@@ -42,10 +42,23 @@ typedef short shortx4b __attribute__((ext_vector_type(4)));
 typedef short shortx8b __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) shortx4b* lds4_t;
 
-// [rows][DH] bf16 tile: 16-byte vector v of row r at slot v ^ (r % (DH / 8)).
+// [rows][DH] bf16 tile: 16-byte vector v of row r at slot v ^ rsw(r). Two
+// access patterns must be conflict-free: plain 16-byte reads of one vector
+// from 16 consecutive rows (a pass), and transposing reads of 64 bytes (an
+// aligned group of 4 slots) from each of 4 consecutive rows. DH = 128 (rows
+// of 256 bytes, all starting at bank 0): rsw = 4 (r & 3) + ((r >> 2) & 3) is
+// a bijection on r % 16 and gives the 4 rows different slot groups. DH = 64
+// (rows of 128 bytes: even and odd rows in different bank halves):
+// rsw = 4 ((r >> 1) & 1) + ((r >> 2) & 3), a bijection on (r >> 1) % 8 that
+// separates rows r and r + 2.
+template <int DH>
+__device__ __forceinline__ int rsw(int r) {
+  if constexpr (DH == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 template <int DH>
 __device__ __forceinline__ int rswz(int r, int v) {
-  return r * DH + ((v ^ (r & (DH / 8 - 1))) << 3);
+  return r * DH + ((v ^ rsw<DH>(r)) << 3);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(const void* p, uint64_t nbytes) {
@@ -81,7 +94,7 @@ __device__ __forceinline__ void pack_slots(bf16x8 (&f)[2], const floatx16& x) {
 
 // ------------------------------------------------------------------- dQ
 template <int DH>
-__global__ void __launch_bounds__(256) attn_bwd_dq2_kernel(AttnArgs a, int ksplit) {
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq2_kernel(AttnArgs a, int ksplit) {
   constexpr int KS = DH / 16, DB = DH / 32, KV = DH / 8;
   constexpr int NI = BT * DH * 2 / 1024;  // DMA wave-instructions per tile
   __shared__ __attribute__((aligned(1024))) bf16 Ks0[BT * DH];
@@ -154,7 +167,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq2_kernel(AttnArgs a, int kspli
     for (int i = 0; i < NI / 4; ++i) {
       const int jj = wid + 4 * i;
       const int key = jj * (1024 / (DH * 2)) + lane / KV, p = lane % KV;
-      const int v = p ^ (key & (KV - 1));
+      const int v = p ^ rsw<DH>(key);
       const uint32_t off = (uint32_t)(((slot + key) * DH + v * 8) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (ldsv_t)(kdst + jj * 512), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ldsv_t)(vdst + jj * 512), 16, off, 0, 0, 0);
@@ -167,43 +180,40 @@ __global__ void __launch_bounds__(256) attn_bwd_dq2_kernel(AttnArgs a, int kspli
     const bool any = wq_lo < a.n && (kt <= wq_hi) && (kt + BT - 1 > wq_lo - a.window);
     const bool full = (kt + BT - 1 <= wq_lo) && (kt > wq_hi - a.window);
     if (any) {
-      floatx16 s[2], dp[2];
+      // one 32-key half of the tile at a time, end to end (scores, softmax
+      // terms, dQ update): fewer live registers, two waves per SIMD
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        floatx16 sv, dpv;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          s[kb][j] = 0.f;
-          dp[kb][j] = 0.f;
+          sv[j] = 0.f;
+          dpv[j] = 0.f;
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int o = rswz<DH>(kb * 32 + lr, ks * 2 + lg);
           const bf16x8 kf = *(const bf16x8*)(ks_ + o);
           const bf16x8 vf = *(const bf16x8*)(vs_ + o);
-          mma32(s[kb], kf, qf[ks]);
-          mma32(dp[kb], vf, df[ks]);
+          mma32(sv, kf, qf[ks]);
+          mma32(dpv, vf, df[ks]);
         }
-      }
-      bf16x8 dsf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          float p = __builtin_amdgcn_exp2f(s[kb][j] * sc2 - lse2);
+          float p = __builtin_amdgcn_exp2f(sv[j] * sc2 - lse2);
           if (!full) {
             const int kp = kt + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
             if (!(kp <= row && kp > row - a.window)) p = 0.f;
           }
-          s[kb][j] = p * (dp[kb][j] - Dq);
+          sv[j] = p * (dpv[j] - Dq);
         }
-        pack_slots(dsf[kb], s[kb]);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        bf16x8 dsf[2];
+        pack_slots(dsf, sv);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int db = 0; db < DB; ++db) mma32(acc[db], ld_tr_op<DH>(ks_, kb * 32 + 16 * u, db * 32, lane), dsf[kb][u]);
+          for (int db = 0; db < DB; ++db) mma32(acc[db], ld_tr_op<DH>(ks_, kb * 32 + 16 * u, db * 32, lane), dsf[u]);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -291,7 +301,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
     for (int i = 0; i < NI / 4; ++i) {
       const int jj = wid + 4 * i;
       const int r = jj * (1024 / (DH * 2)) + lane / KV, p = lane % KV;
-      const int v = p ^ (r & (KV - 1));
+      const int v = p ^ rsw<DH>(r);
       const int qrow = qt + r;
       const uint32_t off = qrow < a.n ? (uint32_t)((((long)qrow * a.H + h) * DH + v * 8) * 2) : 0xFFFFFFF0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (ldsv_t)(qdst + jj * 512), 16, off, 0, 0, 0);

@@ -342,10 +342,13 @@ struct DmaLoader {
 // element e is element i % 4 of the 4 that source lane 4 e + i / 4 points
 // at. Pointing lane j of the group at (k-row kb + j / 4, column r0 + 4 (j % 4))
 // therefore hands lane i column r0 + i at k-rows kb .. kb + 3 -- four
-// consecutive K elements of its MFMA fragment; two reads make the eight. The
-// swizzle spreads the 16 k-rows one read instruction touches (kb + 8 g + j/4
-// for the four groups g) over 16 different slots.
-__device__ __forceinline__ int trx(int kr) { return (kr & 3) | ((kr >> 1) & 12); }
+// consecutive K elements of its MFMA fragment; two reads make the eight.
+// Swizzle: the half-wave a pass serves reads 32 contiguous bytes (an even
+// slot pair) from each of 8 k-rows (kb + 8 h + j / 4, h = 0, 1, or the same
+// + 16); XOR-ing the slot with 2 (kr & 3) + (kr & 8) sends those 8 rows to 8
+// different slot pairs, i.e. all 64 banks once. k-row kr + 4 shares kr's
+// swizzle (kb is a multiple of 32).
+__device__ __forceinline__ int trx(int kr) { return ((kr & 3) << 1) | (kr & 8); }
 
 template <int ROWS, int NW>
 struct TrDmaLoader {
