@@ -153,7 +153,10 @@ def attn_replay(c, T, tla, torch):
     o = torch.empty(slab, H, dh, dtype=bf, device="cuda")
     launches = attn_launches(c, T)
     for kind, n, p0, _ in launches:
-        tla.attn_fwd(q[:n].contiguous() if n < slab else q, K, V, o, None, n, H, Hk, dh, cap, k, p0, vt=VT)
+        ws = tla.attn_fwd_workspace(n, H, dh, k, 0)   # the engine's key split for this shape
+        work = torch.empty(max(ws // 4, 1), device="cuda")
+        tla.attn_fwd(q[:n].contiguous() if n < slab else q, K, V, o, None, n, H, Hk, dh, cap, k, p0, vt=VT,
+                     ksplit=0, work=work)
     torch.cuda.synchronize()
     print(json.dumps(dict(launches=len(launches))), flush=True)
 
@@ -166,7 +169,7 @@ def pmc_summary(c, T, dirs, workload):
         f = os.path.join(d, "run_counter_collection.csv")
         with open(f) as fh:
             return [float(r["Counter_Value"]) * 1024 for r in csv.DictReader(fh) if name_part in r["Kernel_Name"]]
-    fetch, write = read(dirs[0], "attn_fwd2"), read(dirs[1], "attn_fwd2")
+    fetch, write = read(dirs[0], "attn_fwd2_kernel"), read(dirs[1], "attn_fwd2_kernel")
     cf, cw = read(dirs[2], "copyBuffer"), read(dirs[3], "copyBuffer")
     copy_bytes = float(1 << 30)
     fs, ws = copy_bytes / (sum(cf) / len(cf)), copy_bytes / (sum(cw) / len(cw))

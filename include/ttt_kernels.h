@@ -58,7 +58,15 @@ ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajor, int32_t 
  * with 32 / 64 queries per wave (bf16, dh 64/128, needs vt). */
 ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, const void* vt,
                          void* o, float* lse, int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t cap,
-                         int32_t window, int64_t pos0, int32_t variant, void* stream);
+                         int32_t window, int64_t pos0, int32_t variant, int32_t ksplit, void* work,
+                         void* stream);
+
+/* ksplit (32x32 kernels only): the key range of each query block is split
+ * over that many workgroups (1..4; 0 = chosen from the shape) whose partial
+ * results go to work (caller-owned device memory of
+ * tttk_attn_fwd_workspace() bytes; may be NULL when that is 0) and are
+ * merged by a combine pass. */
+int64_t tttk_attn_fwd_workspace(int32_t n, int32_t H, int32_t dh, int32_t window, int32_t ksplit);
 
 /* Its backward for the query side and for the keys of the call's own
  * positions (cached earlier keys are constants): given dO [n, H, dh] and

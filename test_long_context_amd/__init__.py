@@ -79,7 +79,10 @@ def lib() -> ctypes.CDLL:
         f32 = ctypes.c_float
         L.tttk_gemm.argtypes = [i32, i32, i32, i32, vp, i64, vp, i64, vp, i32, i32, i32, vp, i64, vp, vp,
                                 vp, f32, i32, i32, vp]
-        L.tttk_attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i32, vp]
+        L.tttk_attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, vp,
+                                    vp]
+        L.tttk_attn_fwd_workspace.argtypes = [i32, i32, i32, i32, i32]
+        L.tttk_attn_fwd_workspace.restype = i64
         L.tttk_attn_bwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                     i64, i32, vp, vp]
         L.tttk_attn_bwd_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -252,9 +255,16 @@ def gemm(A, B, M, N, K, epi, C, *, a_kmajor=True, b_kmajor=True, lda=None, ldb=N
                            int(kchunk), int(tile), _stream(stream)), "tttk_gemm")
 
 
-def attn_fwd(q, k, v, o, lse, n, H, Hk, dh, cap, window, pos0, vt=None, variant=0, stream=None):
+def attn_fwd_workspace(n, H, dh, window, ksplit=0):
+    """Bytes of device workspace tttk_attn_fwd needs (include/ttt_kernels.h)."""
+    return int(lib().tttk_attn_fwd_workspace(n, H, dh, window, int(ksplit)))
+
+
+def attn_fwd(q, k, v, o, lse, n, H, Hk, dh, cap, window, pos0, vt=None, variant=0, ksplit=1, work=None,
+             stream=None):
     _check(lib().tttk_attn_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(vt), _ptr(o), _ptr(lse), n, H, Hk, dh,
-                               cap, window, pos0, int(variant), _stream(stream)), "tttk_attn_fwd")
+                               cap, window, pos0, int(variant), int(ksplit), _ptr(work), _stream(stream)),
+           "tttk_attn_fwd")
 
 
 def attn_bwd_workspace(dtype, n, H, Hk, dh, window, variant=0):

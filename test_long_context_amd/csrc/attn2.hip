@@ -43,13 +43,18 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // over the 8 XCDs (each with its own L2). Remap so that each XCD gets a
 // contiguous range of logical blocks, ordered key head first, then query
 // block, then the query heads of the group -- workgroups that run together
-// on an XCD read the same key/value tiles. Grid: (query blocks, H).
-__device__ __forceinline__ void attn_block_order(const AttnArgs& a, int& qblk, int& h) {
-  const int nqb = gridDim.x, nwg = gridDim.x * gridDim.y;
-  int id = blockIdx.x + blockIdx.y * gridDim.x;
+// on an XCD read the same key/value tiles. Grid: (query blocks, H, key
+// splits); logical order key head, key split, query block, query head.
+__device__ __forceinline__ void attn_block_order(const AttnArgs& a, int& qblk, int& h, int& z) {
+  const int nqb = gridDim.x, nz = gridDim.z, nwg = gridDim.x * gridDim.y * gridDim.z;
+  int id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
   const int grp = a.H / a.Hk;
-  const int kh = id / (grp * nqb), rem = id % (grp * nqb);
+  const int per_kh = grp * nqb * nz;
+  const int kh = id / per_kh;
+  int rem = id % per_kh;
+  z = rem / (grp * nqb);
+  rem %= grp * nqb;
   qblk = rem / grp;
   h = kh * grp + rem % grp;
 }
@@ -73,8 +78,8 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
   __shared__ __attribute__((aligned(1024))) bf16 Vs0[DH * BKV2];
   __shared__ __attribute__((aligned(1024))) bf16 Vs1[DH * BKV2];
 
-  int qblk, h;
-  attn_block_order(a, qblk, h);
+  int qblk, h, z;
+  attn_block_order(a, qblk, h, z);
   const int kh = h / (a.H / a.Hk);
   const int q0 = qblk * BQ;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -113,6 +118,10 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
   const int cmask = a.cap - 1;
   const float sc2 = a.scale * LOG2E;
   const int wq_lo = qw, wq_hi = min(qw + 32 * QB, a.n) - 1;
+  // key tiles [k_lo, qr_hi], split over gridDim.z workgroups
+  const int ntile = (qr_hi - k_lo) / BKV2 + 1;
+  const int per = (ntile + gridDim.z - 1) / gridDim.z;
+  const int t_beg = z * per, t_end = min(ntile, t_beg + per);
 
   // DMA of key tile kt (relative position): lane l writes the swizzled slot
   // base + 16 l, so it fetches the logical vector belonging to that slot
@@ -136,8 +145,9 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
     }
   };
 
-  auto tile = [&](int kt, const bf16* ks_, const bf16* vs_, bf16* kn, bf16* vn) {
-    if (kt + BKV2 <= qr_hi) dma_tile(kt + BKV2, kn, vn);  // overlaps this whole tile
+  auto tile = [&](int t, const bf16* ks_, const bf16* vs_, bf16* kn, bf16* vn) {
+    const int kt = k_lo + t * BKV2;
+    if (t + 1 < t_end) dma_tile(kt + BKV2, kn, vn);  // overlaps this whole tile
     const bool any = (kt <= wq_hi) && (kt + BKV2 - 1 > wq_lo - a.window);
     const bool full = (kt + BKV2 - 1 <= wq_lo) && (kt > wq_hi - a.window);
     if (any) {
@@ -223,13 +233,38 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
     __syncthreads();
   };
 
-  if (k_lo <= qr_hi) dma_tile(k_lo, Ks0, Vs0);
+  if (t_beg < t_end) dma_tile(k_lo + t_beg * BKV2, Ks0, Vs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = k_lo; kt <= qr_hi; kt += 2 * BKV2) {
-    tile(kt, Ks0, Vs0, Ks1, Vs1);
-    if (kt + BKV2 > qr_hi) break;
-    tile(kt + BKV2, Ks1, Vs1, Ks0, Vs0);
+  for (int t = t_beg; t < t_end; t += 2) {
+    tile(t, Ks0, Vs0, Ks1, Vs1);
+    if (t + 1 >= t_end) break;
+    tile(t + 1, Ks1, Vs1, Ks0, Vs0);
+  }
+
+  if (gridDim.z > 1) {
+    // partial: unnormalised output and (max, sum) of this key range
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = qw + qb * 32 + lr;
+      if (row >= a.n) continue;
+      float* op = a.opart + (long)z * a.n * a.H * DH + ((long)row * a.H + h) * DH;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          floatx4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = o[qb][db][4 * jg + e];
+          *(floatx4*)(op + db * 32 + 8 * jg + 4 * lg) = w;
+        }
+      if (lg == 0) {
+        float* ml = a.mlpart + (long)z * 2 * a.H * a.n;
+        ml[(long)h * a.n + row] = m_run[qb];
+        ml[(long)a.H * a.n + (long)h * a.n + row] = l_run[qb];
+      }
+    }
+    return;
   }
 
   bf16* O = (bf16*)a.o;
@@ -251,6 +286,47 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
   }
 }
 
+// o = sum_z o_z 2^(m_z - M) / sum_z l_z 2^(m_z - M), lse = (M + log2 L) ln 2;
+// one workgroup per query row.
+__global__ void __launch_bounds__(256) attn_fwd_combine_kernel(const float* opart, const float* ml, int ks, int n,
+                                                               int H, int DH, bf16* o, float* lse) {
+  const int row = blockIdx.x;
+  for (int i = threadIdx.x; i < H * DH; i += blockDim.x) {
+    const int h = i / DH;
+    float M = -INFINITY;
+    for (int z = 0; z < ks; ++z) M = fmaxf(M, ml[(long)z * 2 * H * n + (long)h * n + row]);
+    float L = 0.f, acc = 0.f;
+    for (int z = 0; z < ks; ++z) {
+      const float mz = ml[(long)z * 2 * H * n + (long)h * n + row];
+      if (mz == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(mz - M);
+      L += ml[(long)z * 2 * H * n + (long)H * n + (long)h * n + row] * w;
+      acc += opart[(long)z * n * H * DH + (long)row * H * DH + i] * w;
+    }
+    o[(long)row * H * DH + i] = (bf16)(L > 0.f ? acc / L : 0.f);
+    if (lse && i % DH == 0) lse[(long)h * n + row] = (M + __log2f(L)) * LN2;
+  }
+}
+
+hipError_t attn_fwd2_combine(const AttnArgs& a, hipStream_t st) {
+  const int ks = (a.ksplit > 1 && a.opart && a.mlpart) ? a.ksplit : 1;
+  if (ks <= 1 || a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_fwd_combine_kernel, dim3(a.n), dim3(256), 0, st, a.opart, a.mlpart, ks, a.n, a.H, a.dh,
+                     (bf16*)a.o, a.lse);
+  return hipGetLastError();
+}
+
+int attn_fwd2_splits(const AttnArgs& a) {
+  if (a.n <= 0) return 1;
+  const long base = (long)((a.n + 127) / 128) * a.H;  // 32 queries per wave
+  if (base >= 512) return 1;
+  const long tiles = (a.window + 128 + BKV2 - 1) / BKV2;
+  long s = (512 + base - 1) / base;
+  if (s > tiles / 4) s = tiles / 4;
+  if (s > 4) s = 4;
+  return s < 1 ? 1 : (int)s;
+}
+
 bool attn_fwd2_supported(DT dt, const AttnArgs& a) {
   return dt == DT::BF16 && (a.dh == 128 || a.dh == 64) && a.vt != nullptr;
 }
@@ -261,12 +337,15 @@ hipError_t attn_fwd2(DT dt, const AttnArgs& a, hipStream_t st, int qb) {
   // dh 128 with 64 queries per wave runs out of registers (spills) and is no
   // faster even on long prefixes, so it is only taken on request
   const bool big = qb == 2 || (qb == 0 && a.dh == 64 && (long)((a.n + 255) / 256) * a.H >= 512);
+  const int ks = (a.ksplit > 1 && a.opart && a.mlpart) ? a.ksplit : 1;
+  const int bq = big ? 256 : 128;
+  const dim3 grid((a.n + bq - 1) / bq, a.H, ks);
   if (a.dh == 128) {
-    if (big) hipLaunchKernelGGL((attn_fwd2_kernel<128, 2>), dim3((a.n + 255) / 256, a.H), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_fwd2_kernel<128, 1>), dim3((a.n + 127) / 128, a.H), dim3(256), 0, st, a);
+    if (big) hipLaunchKernelGGL((attn_fwd2_kernel<128, 2>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_fwd2_kernel<128, 1>), grid, dim3(256), 0, st, a);
   } else {
-    if (big) hipLaunchKernelGGL((attn_fwd2_kernel<64, 2>), dim3((a.n + 255) / 256, a.H), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_fwd2_kernel<64, 1>), dim3((a.n + 127) / 128, a.H), dim3(256), 0, st, a);
+    if (big) hipLaunchKernelGGL((attn_fwd2_kernel<64, 2>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_fwd2_kernel<64, 1>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

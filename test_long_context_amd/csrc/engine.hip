@@ -93,6 +93,8 @@ struct ttt_ctx {
   void* dO = nullptr;                        // [b, H dh]
   float* Dbuf = nullptr;                     // [H, b]
   float* dq = nullptr;                       // [parts][b, H dh] (partial sums)
+  float* apart = nullptr;                    // forward key-split partial outputs [4][b, H dh]
+  float* aml = nullptr;                      // ... and their (max, sum) [4][2][H][b]
   float* dk = nullptr;                       // [b, Hk dh]
   float* dv = nullptr;
   void* dqkv = nullptr;                      // [b, QKV]
@@ -406,7 +408,13 @@ ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipSt
       TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, a0, c->rope, c->q_l[i], c->kring[l],
                                       c->vring[l], c->vtring[l], (int)c->cap, 0, st));
       AttnArgs a = attn_args(c, l, c->q_l[i], c->o_l[i], c->lse[i], n, a0);
+      if (attn_fwd2_supported(c->dt, a)) {
+        a.ksplit = std::min(4, attn_fwd2_splits(a));
+        a.opart = c->apart;
+        a.mlpart = c->aml;
+      }
       TCALL(KC_AL, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_fwd_any(c->dt, a, st));
+      TCALL(KC_OT, 0, 0, attn_fwd2_combine(a, st));
       RUN(gemm_resid(c, KC_GL, c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, nullptr, n, d, H * dh, &np, st));
       // static MLP sublayer
       TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_mlp[i], c->mlp_norm[l], n, d, eps,
@@ -730,6 +738,8 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   // room for the partial sums of the second-generation backward (at most 4
   // key splits of dq; one dk / dv part per query head of a group)
   Af(&c->dq, (size_t)4 * b * c->H * c->dh);
+  Af(&c->apart, (size_t)4 * b * c->H * c->dh);
+  Af(&c->aml, (size_t)4 * 2 * c->H * b);
   Af(&c->dk, (size_t)(c->H / c->Hk) * b * c->Hk * c->dh);
   Af(&c->dv, (size_t)(c->H / c->Hk) * b * c->Hk * c->dh);
   A(&c->dqkv, (size_t)b * c->QKV * es);

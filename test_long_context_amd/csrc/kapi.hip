@@ -66,12 +66,32 @@ ttt_status attn_check(int32_t dtype, int32_t n, int32_t H, int32_t Hk, int32_t d
 }
 }  // namespace
 
+namespace {
+int fwd_splits(int32_t n, int32_t H, int32_t dh, int32_t window, int32_t ksplit) {
+  if (ksplit > 0) return ksplit;
+  AttnArgs a{};
+  a.n = n;
+  a.H = H;
+  a.dh = dh;
+  a.window = window;
+  return attn_fwd2_splits(a);
+}
+}  // namespace
+
+extern "C" int64_t tttk_attn_fwd_workspace(int32_t n, int32_t H, int32_t dh, int32_t window, int32_t ksplit) {
+  if (n <= 0 || H < 1 || ksplit < 0 || ksplit > 4) return 0;
+  const int s = fwd_splits(n, H, dh, window, ksplit);
+  if (s <= 1) return 0;
+  return (int64_t)4 * s * ((int64_t)n * H * dh + 2LL * H * n);
+}
+
 extern "C" ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, const void* vt,
                                     void* o, float* lse, int32_t n, int32_t H, int32_t Hk, int32_t dh,
-                                    int32_t cap, int32_t window, int64_t pos0, int32_t variant, void* stream) {
+                                    int32_t cap, int32_t window, int64_t pos0, int32_t variant, int32_t ksplit,
+                                    void* work, void* stream) {
   ttt_status s = attn_check(dtype, n, H, Hk, dh, cap, window, pos0);
   if (s != TTT_OK) return s;
-  if (!q || !k || !v || !o || variant < 0 || variant > 3) return TTT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || variant < 0 || variant > 3 || ksplit < 0 || ksplit > 4) return TTT_ERR_INVALID_ARG;
   AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -92,7 +112,15 @@ extern "C" ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k,
     e = attn_fwd(to_dt(dtype), a, (hipStream_t)stream);
   } else {
     if (!attn_fwd2_supported(to_dt(dtype), a)) return TTT_ERR_UNSUPPORTED;
+    const int ks = fwd_splits(n, H, dh, window, ksplit);
+    if (ks > 1 && n > 0) {
+      if (!work || !al16(work)) return TTT_ERR_INVALID_ARG;
+      a.ksplit = ks;
+      a.opart = (float*)work;
+      a.mlpart = a.opart + (long)ks * n * H * dh;
+    }
     e = attn_fwd2(to_dt(dtype), a, (hipStream_t)stream, variant == 0 ? 0 : variant - 1);
+    if (e == hipSuccess) e = attn_fwd2_combine(a, (hipStream_t)stream);
   }
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }

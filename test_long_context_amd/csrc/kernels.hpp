@@ -119,12 +119,24 @@ struct AttnArgs {
   float* dq;          // [n, H, dh] float
   float* dk;          // [n, Hk, dh] float, keys of this call's own positions
   float* dv;
+  // forward key-range split (second-generation forward): ksplit parts, each
+  // an unnormalised output [n, H, dh] in opart and (max, sum) in mlpart
+  // [ksplit][2][H][n] (log2 domain), merged by a combine pass
+  int ksplit;
+  float* opart;
+  float* mlpart;
 };
 hipError_t attn_fwd(DT dt, const AttnArgs& a, hipStream_t st);
 // Second-generation forward (bf16, head_dim 64/128, needs a.vt).
 bool attn_fwd2_supported(DT dt, const AttnArgs& a);
 // qb: 0 = chosen from the shape, 1 / 2 = 32 / 64 queries per wave.
+// With a.ksplit > 1 (and a.opart, a.mlpart), the key range is split over
+// that many workgroups per query block; attn_fwd2_combine then writes o and
+// lse (a no-op without a split).
 hipError_t attn_fwd2(DT dt, const AttnArgs& a, hipStream_t st, int qb = 0);
+hipError_t attn_fwd2_combine(const AttnArgs& a, hipStream_t st);
+// Key-range split that fills the CUs for this shape (1 = none).
+int attn_fwd2_splits(const AttnArgs& a);
 hipError_t attn_bwd_dq(DT dt, const AttnArgs& a, hipStream_t st);
 hipError_t attn_bwd_dkdv(DT dt, const AttnArgs& a, hipStream_t st);
 // Second-generation backward (bf16, head_dim 64/128). dq receives

@@ -80,12 +80,15 @@ def test_attention_fwd_bwd(case):
     VT = torch.empty(Hk, dh, cap, dtype=bf)
     VT[:, :, perm] = Vr.transpose(1, 2)
     VTd = VT.contiguous().to(dev)
-    for variant in (1, 2, 3):
-        say(f"attn fwd variant {variant} case {case}")
+    for variant, ksplit in ((1, 1), (2, 1), (3, 1), (2, 2), (2, 3), (3, 4)):
+        say(f"attn fwd variant {variant} ksplit {ksplit} case {case}")
         o = torch.full((n, H, dh), float("nan"), dtype=bf, device=dev)
         lse = torch.full((H, n), float("nan"), device=dev)
-        tla.attn_fwd(qd, Kd, Vd, o, lse, n, H, Hk, dh, cap, window, pos0, vt=VTd, variant=variant)
-        assert rel(o.cpu(), o_ref) < 1e-2, (variant, rel(o.cpu(), o_ref))
+        ws = tla.attn_fwd_workspace(n, H, dh, window, ksplit)
+        work = torch.empty(max(ws // 4, 1), device=dev)
+        tla.attn_fwd(qd, Kd, Vd, o, lse, n, H, Hk, dh, cap, window, pos0, vt=VTd, variant=variant, ksplit=ksplit,
+                     work=work)
+        assert rel(o.cpu(), o_ref) < 1e-2, (variant, ksplit, rel(o.cpu(), o_ref))
         assert float((lse.cpu().double() - lse_ref).abs().max()) < 1e-2
 
     lse_in = lse_ref.float().to(dev)
