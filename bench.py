@@ -97,20 +97,28 @@ def algorithmic_flops(c: dict, T: int) -> float:
     return float(fwd + bwd)
 
 
-def cpu_baseline(c, w, tok, ntok):
-    """The oracle (float32 numpy) on the first mini-batch of the same stream."""
-    import numpy as np
-    import torch
-    from oracle import ttt_e2e as O
+def _host_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([x.get("num_threads", 0) for x in threadpool_info()] + [1])
+        return max([x.get("num_threads", 0) for x in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count()
+        return os.cpu_count()
+
+
+def _oracle_weights(w):
     wn = {"embed": w["embed"].float().cpu().numpy(), "final_norm": w["final_norm"].float().cpu().numpy()}
     wn["lm_head"] = wn["embed"]
     wn["layers"] = [{k: v.float().cpu().numpy() for k, v in x.items()} for x in w["layers"]]
     wn["dyn"] = [{k: v.float().cpu().numpy() for k, v in x.items()} for x in w["dyn"]]
+    return wn
+
+
+def cpu_baseline(c, w, tok, ntok):
+    """The oracle (float32 numpy) on the first mini-batch of the same stream."""
+    import numpy as np
+    from oracle import ttt_e2e as O
+    cores = _host_threads()
+    wn = _oracle_weights(w)
     t = tok[: ntok + 1].cpu().numpy()
     t0 = time.perf_counter()
     out = O.ttt_inner_loop(c, wn, t, dtype=np.float32)
@@ -120,6 +128,88 @@ def cpu_baseline(c, w, tok, ntok):
                 sample=f"mini-batch 0 of the same stream: {ntok} positions forward + 1 SGD step, "
                        f"plus the forward-only position {ntok}; {dt:.1f} s on the host",
                 seconds=round(dt, 2))
+
+
+def cpu_decode_baseline(c, w, p, nsteps=2):
+    """The oracle's decode (float32 numpy) of nsteps tokens at position p of
+    the same model: a full window of stored keys/values (random values: the
+    cost does not depend on them) and the initial fast weights."""
+    import numpy as np
+    from oracle import ttt_e2e as O
+    cores = _host_threads()
+    cfg = O.Cfg.from_dict(c)
+    wc = O._cast_weights(_oracle_weights(w), np.float32)
+    store = O.KVStore(cfg, p + nsteps + 1, np.float32)
+    rng = np.random.default_rng(0)
+    lo = max(0, p - cfg.window)
+    for l in range(cfg.L):
+        store.K[l][lo:p] = rng.standard_normal((p - lo, cfg.Hk, cfg.dh), dtype=np.float32)
+        store.V[l][lo:p] = rng.standard_normal((p - lo, cfg.Hk, cfg.dh), dtype=np.float32)
+    store.n = p
+    state = dict(cfg=cfg, weights=wc, store=store, dyn=[{k: np.array(b[k]) for k in ("w1", "w2", "w3")} for b in wc["dyn"]])
+    t0 = time.perf_counter()
+    for j in range(nsteps):
+        z = O.decode_step(state, j % c["vocab"])
+    dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(z))
+    return dict(value=round(dt / nsteps * 1e3, 1), unit="ms/token", cores=int(cores), kind="oracle",
+                sample=f"{nsteps} decode steps at position {p} (full {cfg.window}-key window); {dt:.1f} s on the host",
+                seconds=round(dt, 2))
+
+
+def e2_bench(args, tla, torch, synth):
+    """E2-TTT chunk-end state over the whole sequence (16 heads x 32768
+    tokens, D 128, chunks of 2048): e2ttt_chunk_scan timed with HIP events;
+    HBM roofline on its algorithmic bytes; the oracle's closed form timed on
+    the host."""
+    import numpy as np
+    e = synth.E2_CONFIG
+    H, T, D, C = e["heads"], e["seq"], e["dim"], e["chunk"]
+    x = synth.gen_e2(H, T, D, e["seed"], device="cuda")
+    W0, M0 = x["W"].clone(), x["M"].clone()
+    W, M = x["W"], x["M"]
+    for _ in range(max(1, args.warmup)):
+        W.copy_(W0)
+        M.copy_(M0)
+        tla.e2ttt_chunk_scan(x["k"], x["v"], x["eta"], x["beta"], x["gamma"], W, M, C)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(args.steps):
+        W.copy_(W0)
+        M.copy_(M0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tla.e2ttt_chunk_scan(x["k"], x["v"], x["eta"], x["beta"], x["gamma"], W, M, C)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = sorted(ts)[len(ts) // 2]
+    nch = (T + C - 1) // C
+    algo = 2 * H * T * D * 2 + 3 * H * T * 4 + nch * H * D * D * 4 * 2 * 2   # k, v; eta, beta, gamma; W, M per chunk
+    gbs = algo / (ms * 1e-3) / 1e9
+    flops = H * nch * 3 * 2 * C * D * D
+    out = dict(metric="E2-TTT chunk-end state (16 heads x 32K tokens, D 128, C 2048), 1 MI355X",
+               value=round(H * T / (ms * 1e-3), 1), unit="token-heads/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="bf16 inputs, fp32/fp64 scalars", data="synthetic",
+               config=dict(workload=f"e2ttt chunk scan, H={H}, T={T}, D={D}, C={C}"),
+               roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                             frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
+                             kernel="e2ttt_chunk_scan (scalars, partial aggregation, combine)",
+                             algorithmic_bytes=algo, mfma_tflops=round(flops / (ms * 1e-3) / 1e12, 2)))
+    if not args.no_cpu_baseline:
+        from oracle import e2ttt as E
+        xs = {k_: v_.double().cpu().numpy() for k_, v_ in x.items() if k_ in ("k", "v", "eta", "beta", "gamma")}
+        t0 = time.perf_counter()
+        E.e2_closed_form(xs["k"], xs["v"], xs["eta"], xs["beta"], xs["gamma"], W0.double().cpu().numpy(),
+                         M0.double().cpu().numpy(), C)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(value=round(H * T / dt, 1), unit="token-heads/s", cores=int(_host_threads()),
+                                   kind="oracle", sample=f"the whole workload, float64 numpy; {dt:.1f} s on the host",
+                                   seconds=round(dt, 2))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
 
 
 def attn_launches(c: dict, T: int):
@@ -236,7 +326,9 @@ def decode_bench(args, c, w, tok, tla, torch):
                                     f"prefills of {', '.join(str(x) for x in ctxs)} tokens", window=c["window"]),
                contexts=res, flat_ratio=round(big["p50_ms"] / small["p50_ms"], 3),
                roofline=dict(bound="hbm", achieved=big["achieved_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
-                             frac=round(big["achieved_gbs"] / PEAK_HBM_GBS, 4), traffic=None))
+                             frac=round(big["achieved_gbs"] / PEAK_HBM_GBS, 4), traffic=None,
+                             kernel="whole decode step (GEMVs, window attention, lm_head)"))
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_decode_baseline(c, w, ctxs[0])
     print(json.dumps(out), flush=True)
 
 
@@ -254,6 +346,7 @@ def main():
     ap.add_argument("--attn-replay", action="store_true", help="one step's attention-forward launches, then exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar="DIR", help="bytes per attention launch from counter runs")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--e2", action="store_true", help="measure the E2-TTT chunk-end kernel instead")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
@@ -268,6 +361,9 @@ def main():
     import synth
     import test_long_context_amd as tla
 
+    if args.e2:
+        e2_bench(args, tla, torch, synth)
+        return
     c = synth.config(args.workload)
     T = args.seq or c["seq"]
     if args.pmc_summary:

@@ -29,47 +29,127 @@
 namespace ttt {
 
 // ------------------------------------------------------------ scalar scan
-// One thread per (head, chunk), sequential over the chunk in float64.
-__global__ void e2_scalar_kernel(const float* eta, const float* beta, const float* gamma, int H,
-                                 int64_t T, int C, float* KW, float* KM, float* coef) {
+// One workgroup of E2_ST threads per (head, chunk), 8 consecutive tokens per
+// thread, all in float64. For token i of the chunk (0-based, n tokens):
+//   Pb(i) = prod_{j>i} beta_j,  Pg(i) = prod_{j>i} gamma_j   (beta~, gamma~)
+//   A(n-1) = 1,  A(i) = Pg(i) + beta_{i+1} A(i+1)
+// The products are suffix scans; A is a suffix scan of the affine maps
+// f_i(x) = Pg(i) + beta_{i+1} x (f_{n-1} = 1 + 0 x), composed as
+// (c1, m1) o (c2, m2) = (c1 + m1 c2, m1 m2) -- no division anywhere.
+// KW_i = eta_i A(i), KM_i = eta_i Pb(i); chunk coefficients gamma~_0 =
+// prod gamma, beta_1 A_1 = beta_0 A(0) and beta~_0 = prod beta.
+static constexpr int E2_ST = 256;
+static constexpr int E2_TPT = 8;  // tokens per thread (C <= E2_ST * E2_TPT)
+
+__global__ void __launch_bounds__(E2_ST) e2_scalar_kernel(const float* eta, const float* beta, const float* gamma,
+                                                          int H, int64_t T, int C, float* KW, float* KM,
+                                                          float* coef) {
+  __shared__ double sb[E2_ST], sg[E2_ST], sc[E2_ST], sm[E2_ST];
   const int64_t nch = (T + C - 1) / C;
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= nch * H) return;
-  const int h = (int)(id / nch);
-  const int64_t r = id % nch;
+  const int h = blockIdx.x / (int)nch;
+  const int64_t r = blockIdx.x % nch;
   const int64_t a = r * C;
   const int n = (int)min((int64_t)C, T - a);
+  const int tid = threadIdx.x;
   const float* et = eta + h * T + a;
   const float* bt = beta + h * T + a;
   const float* gt = gamma + h * T + a;
+  const int i0 = tid * E2_TPT;
+  double b[E2_TPT], g[E2_TPT], bn[E2_TPT];
+#pragma unroll
+  for (int j = 0; j < E2_TPT; ++j) {
+    const int i = i0 + j;
+    b[j] = i < n ? (double)bt[i] : 1.0;
+    g[j] = i < n ? (double)gt[i] : 1.0;
+    bn[j] = (i + 1 < n) ? (double)bt[i + 1] : 0.0;  // beta_{i+1}; 0 ends the chain at n-1
+  }
+  // thread-local suffix products (exclusive) and the thread's totals
+  double lb[E2_TPT], lg[E2_TPT];
+  double pb = 1.0, pg = 1.0;
+#pragma unroll
+  for (int j = E2_TPT - 1; j >= 0; --j) {
+    lb[j] = pb;
+    lg[j] = pg;
+    pb *= b[j];
+    pg *= g[j];
+  }
+  // suffix scans over threads (inclusive), then shift to exclusive
+  sb[tid] = pb;
+  sg[tid] = pg;
+  __syncthreads();
+  for (int d = 1; d < E2_ST; d <<= 1) {
+    const double xb = tid + d < E2_ST ? sb[tid + d] : 1.0;
+    const double xg = tid + d < E2_ST ? sg[tid + d] : 1.0;
+    __syncthreads();
+    sb[tid] *= xb;
+    sg[tid] *= xg;
+    __syncthreads();
+  }
+  const double eb = tid + 1 < E2_ST ? sb[tid + 1] : 1.0;
+  const double eg = tid + 1 < E2_ST ? sg[tid + 1] : 1.0;
+  double Pb[E2_TPT], Pg[E2_TPT];
+#pragma unroll
+  for (int j = 0; j < E2_TPT; ++j) {
+    Pb[j] = lb[j] * eb;
+    Pg[j] = lg[j] * eg;
+  }
+  // affine maps f_i(x) = Pg(i) + bn_i x for tokens of the chunk; identity
+  // (0 + 1 x) past its end; the thread's composition f_i0 o ... o f_i7
+  double C_ = 0.0, M_ = 1.0;
+#pragma unroll
+  for (int j = E2_TPT - 1; j >= 0; --j) {
+    const bool in = i0 + j < n;
+    const double c = in ? Pg[j] : 0.0, m = in ? bn[j] : 1.0;
+    C_ = c + m * C_;
+    M_ = m * M_;
+  }
+  sc[tid] = C_;
+  sm[tid] = M_;
+  __syncthreads();
+  for (int d = 1; d < E2_ST; d <<= 1) {
+    const double c2 = tid + d < E2_ST ? sc[tid + d] : 0.0;
+    const double m2 = tid + d < E2_ST ? sm[tid + d] : 1.0;
+    __syncthreads();
+    // (c1, m1) o (c2, m2): this thread's maps applied after the later ones
+    sc[tid] = sc[tid] + sm[tid] * c2;
+    sm[tid] = sm[tid] * m2;
+    __syncthreads();
+  }
+  // value of the chain after this thread's tokens (its later threads'
+  // composition evaluated anywhere: it ends in f_{n-1}, a constant)
+  double v = tid + 1 < E2_ST ? sc[tid + 1] : 0.0;
+  double A[E2_TPT];
+#pragma unroll
+  for (int j = E2_TPT - 1; j >= 0; --j) {
+    if (i0 + j < n) v = Pg[j] + bn[j] * v;
+    A[j] = v;
+  }
   float* kw = KW + h * T + a;
   float* km = KM + h * T + a;
-  double btil = 1.0, gtil = 1.0, A = 1.0;  // values at t = n (1-based)
-  // t runs n .. 1; token t is index t-1.
-  for (int t = n; t >= 1; --t) {
-    if (t < n) {
-      const double bnext = bt[t];  // beta_{t+1}
-      btil *= bnext;               // beta~_t = beta_{t+1} beta~_{t+1}
-      gtil *= (double)gt[t];       // gamma~_t
-      A = gtil + bnext * A;        // A_t = gamma~_t + beta_{t+1} A_{t+1}
+#pragma unroll
+  for (int j = 0; j < E2_TPT; ++j) {
+    const int i = i0 + j;
+    if (i < n) {
+      const double e = et[i];
+      kw[i] = (float)(e * A[j]);
+      km[i] = (float)(e * Pb[j]);
     }
-    const double e = et[t - 1];
-    kw[t - 1] = (float)(e * A);
-    km[t - 1] = (float)(e * btil);
   }
-  // after the loop btil = beta~_1, gtil = gamma~_1, A = A_1
-  float* cf = coef + ((int64_t)h * nch + r) * 4;
-  cf[0] = (float)(gtil * (double)gt[0]);  // gamma~_0
-  cf[1] = (float)((double)bt[0] * A);     // beta~_0 R_1 = beta_1 A_1
-  cf[2] = (float)(btil * (double)bt[0]);  // beta~_0
-  cf[3] = 0.f;
+  if (tid == 0) {
+    float* cf = coef + ((int64_t)h * nch + r) * 4;
+    cf[0] = (float)(Pg[0] * g[0]);  // gamma~_0 = prod gamma
+    cf[1] = (float)(b[0] * A[0]);   // beta~_0 R_1 = beta_1 A_1
+    cf[2] = (float)(Pb[0] * b[0]);  // beta~_0 = prod beta
+    cf[3] = 0.f;
+  }
 }
 
 hipError_t e2_scalars(const float* eta, const float* beta, const float* gamma, int H, int64_t T, int C,
                       float* KW, float* KM, float* coef, hipStream_t st) {
-  const int64_t n = ((T + C - 1) / C) * H;
-  hipLaunchKernelGGL(e2_scalar_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, eta, beta,
-                     gamma, H, T, C, KW, KM, coef);
+  if (C > E2_ST * E2_TPT) return hipErrorInvalidValue;
+  const int64_t nch = (T + C - 1) / C;
+  hipLaunchKernelGGL(e2_scalar_kernel, dim3((unsigned)(nch * H)), dim3(E2_ST), 0, st, eta, beta, gamma, H, T, C,
+                     KW, KM, coef);
   return hipGetLastError();
 }
 
@@ -264,7 +344,7 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
   if (!k || !v || !eta || !beta || !gamma || !W || !M) return TTT_ERR_INVALID_ARG;
   if (H < 1 || T < 1 || C < 1) return TTT_ERR_INVALID_ARG;
   if (D != 128 && D != 64) return TTT_ERR_UNSUPPORTED;
-  if (C % 64) return TTT_ERR_UNSUPPORTED;
+  if (C % 64 || C > 2048) return TTT_ERR_UNSUPPORTED;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
     (void)hipGetLastError();
