@@ -15,7 +15,8 @@ namespace ttt {
 
 namespace {
 constexpr int GV_THREADS = 256;
-constexpr int GV_ROWS = 4;  // rows per wave per pass (two pairs)
+constexpr int GV_ROWS = 8;  // split-K kernel: rows per workgroup (four pairs)
+constexpr int GV_RPW = 4;   // row kernel: rows per wave (two pairs)
 
 template <typename TW> struct WVec;  // 16 bytes of weights -> floats
 template <> struct WVec<bf16> {
@@ -51,10 +52,10 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // NORM: x = RMSNorm(h) * g computed by every workgroup while staging x in
 // LDS. EPI: STORE y[n] = acc; ADD_F32 y[n] += acc; SWIGLU: rows are the
 // 16-interleaved (gate, up) layout and y[j] = silu(gate_j) * up_j.
-// A wave takes GV_ROWS rows (two pairs) at a time; lanes stride the row in
-// 16-byte vectors, so each row is one coalesced sweep.
+// Large N: a wave takes GV_RPW rows (two pairs) over the whole K; lanes
+// stride the row in 16-byte vectors, so each row is one coalesced sweep.
 template <typename TW, int EPI, bool NORM>
-__global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__ W, const float* __restrict__ x,
+__global__ void __launch_bounds__(GV_THREADS) gemv_rows_kernel(const TW* __restrict__ W, const float* __restrict__ x,
                                                           const float* __restrict__ g, float eps, int N, int K,
                                                           float* __restrict__ y) {
   extern __shared__ float xs[];
@@ -72,11 +73,11 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * (GV_THREADS / 64) + (threadIdx.x >> 6);
   const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
-  const int p0 = wave * (GV_ROWS / 2);
+  const int p0 = wave * (GV_RPW / 2);
   if (p0 >= npairs) return;
-  int rows[GV_ROWS];
+  int rows[GV_RPW];
 #pragma unroll
-  for (int i = 0; i < GV_ROWS / 2; ++i) {
+  for (int i = 0; i < GV_RPW / 2; ++i) {
     const int p = min(p0 + i, npairs - 1);
     if constexpr (EPI == (int)GvEpi::SWIGLU) {
       rows[2 * i] = (p >> 4) * 32 + (p & 15);
@@ -86,16 +87,16 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__
       rows[2 * i + 1] = min(2 * p + 1, N - 1);
     }
   }
-  float acc[GV_ROWS];
+  float acc[GV_RPW];
 #pragma unroll
-  for (int r = 0; r < GV_ROWS; ++r) acc[r] = 0.f;
+  for (int r = 0; r < GV_RPW; ++r) acc[r] = 0.f;
   const int nv = K / VE;
   for (int v = lane; v < nv; v += 64) {
     float xv[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) xv[e] = xs[v * VE + e];
 #pragma unroll
-    for (int r = 0; r < GV_ROWS; ++r) {
+    for (int r = 0; r < GV_RPW; ++r) {
       float wv[VE];
       WVec<TW>::load(W + (long)rows[r] * K + v * VE, wv);
 #pragma unroll
@@ -103,10 +104,10 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__
     }
   }
 #pragma unroll
-  for (int r = 0; r < GV_ROWS; ++r) acc[r] = wave_sum(acc[r]);
+  for (int r = 0; r < GV_RPW; ++r) acc[r] = wave_sum(acc[r]);
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < GV_ROWS / 2; ++i) {
+    for (int i = 0; i < GV_RPW / 2; ++i) {
       const int p = p0 + i;
       if (p >= npairs) break;
       if constexpr (EPI == (int)GvEpi::SWIGLU) {
@@ -125,13 +126,112 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__
   }
 }
 
+// y = W x for one row x (fp32 [K]); W [N][K] row-major (nn.Linear layout).
+// NORM: x = RMSNorm(h) * g computed by every workgroup while staging x in
+// LDS. EPI: STORE y[n] = acc; ADD_F32 y[n] += acc; SWIGLU: rows are the
+// 16-interleaved (gate, up) layout and y[j] = silu(gate_j) * up_j.
+// A workgroup takes GV_ROWS rows (GV_ROWS / 2 pairs) and splits K over its
+// waves; lanes stride each row's quarter in 16-byte vectors, so every row
+// is read once, coalesced, with many loads in flight per lane; the partial
+// dot products meet in LDS.
+template <typename TW, int EPI, bool NORM>
+__global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__ W, const float* __restrict__ x,
+                                                          const float* __restrict__ g, float eps, int N, int K,
+                                                          float* __restrict__ y) {
+  extern __shared__ float xs[];
+  __shared__ float red[GV_THREADS / 64];
+  __shared__ float part[GV_THREADS / 64][GV_ROWS];
+  if constexpr (NORM) {
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < K; k += GV_THREADS) ss += x[k] * x[k];
+    const float r = rsqrtf(block_sum(ss, red) / K + eps);
+    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k] * r * g[k];
+  } else {
+    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k];
+  }
+  __syncthreads();
+  constexpr int VE = WVec<TW>::N;
+  constexpr int NWV = GV_THREADS / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
+  const int p0 = blockIdx.x * (GV_ROWS / 2);
+  int rows[GV_ROWS];
+#pragma unroll
+  for (int i = 0; i < GV_ROWS / 2; ++i) {
+    const int p = min(p0 + i, npairs - 1);
+    if constexpr (EPI == (int)GvEpi::SWIGLU) {
+      rows[2 * i] = (p >> 4) * 32 + (p & 15);
+      rows[2 * i + 1] = rows[2 * i] + 16;
+    } else {
+      rows[2 * i] = 2 * p;
+      rows[2 * i + 1] = min(2 * p + 1, N - 1);
+    }
+  }
+  float acc[GV_ROWS];
+#pragma unroll
+  for (int r = 0; r < GV_ROWS; ++r) acc[r] = 0.f;
+  const int nv = K / VE;
+  const int q = (nv + NWV - 1) / NWV;  // vectors per wave
+  const int v0 = wid * q, v1 = min(nv, v0 + q);
+  for (int v = v0 + lane; v < v1; v += 64) {
+    float xv[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) xv[e] = xs[v * VE + e];
+    float wv[GV_ROWS][VE];
+#pragma unroll
+    for (int r = 0; r < GV_ROWS; ++r) WVec<TW>::load(W + (long)rows[r] * K + v * VE, wv[r]);
+#pragma unroll
+    for (int r = 0; r < GV_ROWS; ++r)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[r] += wv[r][e] * xv[e];
+  }
+#pragma unroll
+  for (int r = 0; r < GV_ROWS; ++r) acc[r] = wave_sum(acc[r]);
+  if (lane == 0)
+#pragma unroll
+    for (int r = 0; r < GV_ROWS; ++r) part[wid][r] = acc[r];
+  __syncthreads();
+  if (threadIdx.x < GV_ROWS / 2) {
+    const int i = threadIdx.x;
+    const int p = p0 + i;
+    if (p < npairs) {
+      float a = 0.f, c = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        a += part[w][2 * i];
+        c += part[w][2 * i + 1];
+      }
+      if constexpr (EPI == (int)GvEpi::SWIGLU) {
+        y[p] = silu_f(a) * c;
+      } else {
+        const int n = 2 * p;
+        if constexpr (EPI == (int)GvEpi::ADD_F32) {
+          y[n] += a;
+          if (n + 1 < N) y[n + 1] += c;
+        } else {
+          y[n] = a;
+          if (n + 1 < N) y[n + 1] = c;
+        }
+      }
+    }
+  }
+}
+
 template <typename TW, int EPI>
 static hipError_t gemv_t(const TW* W, const float* x, const float* g, float eps, int N, int K, float* y,
                          hipStream_t st) {
   const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
-  const int waves = (npairs + GV_ROWS / 2 - 1) / (GV_ROWS / 2);
-  const int blocks = (waves + GV_THREADS / 64 - 1) / (GV_THREADS / 64);
   const size_t lds = (size_t)K * sizeof(float);
+  // many rows: a wave per GV_RPW rows keeps enough loads in flight; few
+  // rows: split K over the waves of a workgroup to occupy more of the chip
+  const int waves_rows = (npairs + GV_RPW / 2 - 1) / (GV_RPW / 2);
+  if (waves_rows >= 2048) {
+    const int blocks = (waves_rows + GV_THREADS / 64 - 1) / (GV_THREADS / 64);
+    if (g) hipLaunchKernelGGL((gemv_rows_kernel<TW, EPI, true>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
+    else hipLaunchKernelGGL((gemv_rows_kernel<TW, EPI, false>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
+    return hipGetLastError();
+  }
+  const int blocks = (npairs + GV_ROWS / 2 - 1) / (GV_ROWS / 2);
   if (g) hipLaunchKernelGGL((gemv_kernel<TW, EPI, true>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
   else hipLaunchKernelGGL((gemv_kernel<TW, EPI, false>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
   return hipGetLastError();
@@ -184,40 +284,45 @@ hipError_t embed_row(DT dt, const int32_t* tok, const void* embed, int d, int V,
 template <typename T>
 __global__ void decode_rope_store_kernel(const float* qkv, int H, int Hk, int dh, const int64_t* pos,
                                          const float2* tab, float* q, T* ks, T* vs, T* vts, int cap) {
+  // workgroup hh < H: query head; H <= hh < H + Hk: key head; then value heads
   const int64_t p = *pos;
   const int half = dh / 2;
-  const float2* tb = tab + p * half;
   const long slot = p & (cap - 1);
-  for (int i = threadIdx.x; i < (H + Hk) * half; i += blockDim.x) {
-    const int hh = i / half, j = i % half;
-    const float2 cs = tb[j];
-    const float a = qkv[hh * dh + j], b = qkv[hh * dh + j + half];
-    const float ra = a * cs.x - b * cs.y, rb = b * cs.x + a * cs.y;
-    if (hh < H) {
-      q[hh * dh + j] = ra;
-      q[hh * dh + j + half] = rb;
-    } else {
-      const int kh = hh - H;
-      ks[((long)kh * cap + slot) * dh + j] = from_f<T>(ra);
-      ks[((long)kh * cap + slot) * dh + j + half] = from_f<T>(rb);
+  const int hh = blockIdx.x;
+  if (hh < H + Hk) {
+    const float2* tb = tab + p * half;
+    for (int j = threadIdx.x; j < half; j += blockDim.x) {
+      const float2 cs = tb[j];
+      const float a = qkv[hh * dh + j], b = qkv[hh * dh + j + half];
+      const float ra = a * cs.x - b * cs.y, rb = b * cs.x + a * cs.y;
+      if (hh < H) {
+        q[hh * dh + j] = ra;
+        q[hh * dh + j + half] = rb;
+      } else {
+        const int kh = hh - H;
+        ks[((long)kh * cap + slot) * dh + j] = from_f<T>(ra);
+        ks[((long)kh * cap + slot) * dh + j + half] = from_f<T>(rb);
+      }
     }
-  }
-  for (int i = threadIdx.x; i < Hk * dh; i += blockDim.x) {
-    const int kh = i / dh, j = i % dh;
-    const T v = from_f<T>(qkv[(H + Hk) * dh + i]);
-    vs[((long)kh * cap + slot) * dh + j] = v;
-    if (vts) vts[((long)kh * dh + j) * cap + vt_slot(slot)] = v;
+  } else {
+    const int kh = hh - H - Hk;
+    for (int j = threadIdx.x; j < dh; j += blockDim.x) {
+      const T v = from_f<T>(qkv[(H + Hk) * dh + kh * dh + j]);
+      vs[((long)kh * cap + slot) * dh + j] = v;
+      if (vts) vts[((long)kh * dh + j) * cap + vt_slot(slot)] = v;
+    }
   }
 }
 
 hipError_t decode_rope_store(DT dt, const float* qkv, int H, int Hk, int dh, const int64_t* pos,
                              const float2* rope_tab, float* q, void* kstore, void* vstore, void* vtstore, int cap,
                              hipStream_t st) {
+  const dim3 grid(H + 2 * Hk);
   if (dt == DT::BF16)
-    hipLaunchKernelGGL(decode_rope_store_kernel<bf16>, dim3(1), dim3(256), 0, st, qkv, H, Hk, dh, pos, rope_tab, q,
+    hipLaunchKernelGGL(decode_rope_store_kernel<bf16>, grid, dim3(64), 0, st, qkv, H, Hk, dh, pos, rope_tab, q,
                        (bf16*)kstore, (bf16*)vstore, (bf16*)vtstore, cap);
   else
-    hipLaunchKernelGGL(decode_rope_store_kernel<float>, dim3(1), dim3(256), 0, st, qkv, H, Hk, dh, pos, rope_tab, q,
+    hipLaunchKernelGGL(decode_rope_store_kernel<float>, grid, dim3(64), 0, st, qkv, H, Hk, dh, pos, rope_tab, q,
                        (float*)kstore, (float*)vstore, (float*)vtstore, cap);
   return hipGetLastError();
 }
@@ -229,14 +334,14 @@ hipError_t decode_rope_store(DT dt, const float* qkv, int H, int Hk, int dh, con
 // so a wave instruction reads 64 / LPR whole rows. Each lane group keeps an
 // online softmax (max, sum, output slice); the groups and waves are merged
 // through LDS into one partial (m, l, o) per (head, split).
-template <typename T, int DH>
+template <typename T, int DH, int GMAX>
 __global__ void __launch_bounds__(256) decode_attn_kernel(const float* q, const T* kst, const T* vst, int H, int Hk,
                                                           int cap, int window, const int64_t* pos, float scale,
                                                           int nsplit, float* part) {
   constexpr int EV = 16 / sizeof(T);     // elements per 16-byte vector
   constexpr int LPR = DH / EV;           // lanes per key row
   constexpr int KPW = 64 / LPR;          // keys per wave instruction
-  constexpr int GMAX = 8;                // query heads per key head supported
+  // GMAX = query heads per key head (the group)
   __shared__ float sm[4 * KPW][GMAX], sl[4 * KPW][GMAX];
   __shared__ float so[4 * KPW][DH];
   const int kh = blockIdx.x, split = blockIdx.y;
@@ -247,7 +352,7 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(const float* q, const 
   const int64_t p = *pos;
   const int64_t lo = p - window + 1 > 0 ? p - window + 1 : 0;
   const int64_t count = p - lo + 1;
-  const int64_t chunk = ((count + nsplit - 1) / nsplit + 4 * KPW - 1) / (4 * KPW) * (4 * KPW);
+  const int64_t chunk = ((count + nsplit - 1) / nsplit + 4 * KPW - 1) / (4 * KPW) * (4 * KPW);  // whole key groups
   const int64_t c0 = lo + (int64_t)split * chunk, c1 = min(p + 1, c0 + chunk);
 
   float qv[GMAX][EV];
@@ -265,47 +370,55 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(const float* q, const 
   }
   const T* kb = kst + (long)kh * cap * DH;
   const T* vb = vst + (long)kh * cap * DH;
-  for (int64_t t0 = c0; t0 < c1; t0 += 4 * KPW) {
-    const int64_t t = t0 + slotid;
-    const bool ok = t < c1;  // uniform over the LPR lanes of a key row
-    const long slot = (long)(t & (cap - 1));
-    float kv[EV], vv[EV];
+  constexpr int UNR = 4;  // key groups whose loads are in flight together
+  for (int64_t t0 = c0; t0 < c1; t0 += 4 * KPW * UNR) {
+    float kv[UNR][EV], vv[UNR][EV];
+    bool okv[UNR];
 #pragma unroll
-    for (int e = 0; e < EV; ++e) kv[e] = vv[e] = 0.f;
-    if (ok) {
-      if constexpr (sizeof(T) == 2) {
-        const bf16x8 a = *(const bf16x8*)(kb + slot * DH + sub * EV);
-        const bf16x8 b = *(const bf16x8*)(vb + slot * DH + sub * EV);
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t t = t0 + u * 4 * KPW + slotid;
+      okv[u] = t < c1;  // uniform over the LPR lanes of a key row
+      const long slot = (long)(t & (cap - 1));
 #pragma unroll
-        for (int e = 0; e < EV; ++e) {
-          kv[e] = (float)a[e];
-          vv[e] = (float)b[e];
-        }
-      } else {
-        const floatx4 a = *(const floatx4*)(kb + slot * DH + sub * EV);
-        const floatx4 b = *(const floatx4*)(vb + slot * DH + sub * EV);
+      for (int e = 0; e < EV; ++e) kv[u][e] = vv[u][e] = 0.f;
+      if (okv[u]) {
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8 a = *(const bf16x8*)(kb + slot * DH + sub * EV);
+          const bf16x8 b = *(const bf16x8*)(vb + slot * DH + sub * EV);
 #pragma unroll
-        for (int e = 0; e < EV; ++e) {
-          kv[e] = a[e];
-          vv[e] = b[e];
+          for (int e = 0; e < EV; ++e) {
+            kv[u][e] = (float)a[e];
+            vv[u][e] = (float)b[e];
+          }
+        } else {
+          const floatx4 a = *(const floatx4*)(kb + slot * DH + sub * EV);
+          const floatx4 b = *(const floatx4*)(vb + slot * DH + sub * EV);
+#pragma unroll
+          for (int e = 0; e < EV; ++e) {
+            kv[u][e] = a[e];
+            vv[u][e] = b[e];
+          }
         }
       }
     }
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g >= grp) break;
-      float s = 0.f;
+    for (int u = 0; u < UNR; ++u) {
 #pragma unroll
-      for (int e = 0; e < EV; ++e) s += qv[g][e] * kv[e];
+      for (int g = 0; g < GMAX; ++g) {
+        if (g >= grp) break;
+        float s = 0.f;
 #pragma unroll
-      for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-      if (ok) {
-        const float mn = fmaxf(m[g], s);
-        const float c = __expf(m[g] - mn), pe = __expf(s - mn);
-        l[g] = l[g] * c + pe;
+        for (int e = 0; e < EV; ++e) s += qv[g][e] * kv[u][e];
 #pragma unroll
-        for (int e = 0; e < EV; ++e) o[g][e] = o[g][e] * c + pe * vv[e];
-        m[g] = mn;
+        for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+        if (okv[u]) {
+          const float mn = fmaxf(m[g], s);
+          const float c = __expf(m[g] - mn), pe = __expf(s - mn);
+          l[g] = l[g] * c + pe;
+#pragma unroll
+          for (int e = 0; e < EV; ++e) o[g][e] = o[g][e] * c + pe * vv[u][e];
+          m[g] = mn;
+        }
       }
     }
   }
@@ -345,24 +458,34 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(const float* q, const 
   }
 }
 
-// o[h] = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}
-__global__ void decode_attn_combine_kernel(const float* part, int nsplit, int dh, float* o) {
+// o[h] = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}: the split weights
+// are formed once per head in LDS, then each thread sums one output column.
+__global__ void __launch_bounds__(128) decode_attn_combine_kernel(const float* part, int nsplit, int dh, float* o) {
+  __shared__ float wsh[256];
+  __shared__ float Lsh;
   const int h = blockIdx.x;
   const float* ph = part + (long)h * nsplit * (dh + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ph[s * (dh + 2) + dh]);
-  float L = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = ph[s * (dh + 2) + dh];
-    if (ms != -INFINITY) L += ph[s * (dh + 2) + dh + 1] * __expf(ms - M);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    float mloc = -INFINITY;
+    for (int s = lane; s < nsplit; s += 64) mloc = fmaxf(mloc, ph[s * (dh + 2) + dh]);
+    const float M = wave_max(mloc);
+    float lsum = 0.f;
+    for (int s = lane; s < nsplit; s += 64) {
+      const float ms = ph[s * (dh + 2) + dh];
+      const float w = ms == -INFINITY ? 0.f : __expf(ms - M);
+      wsh[s] = w;
+      lsum += ph[s * (dh + 2) + dh + 1] * w;
+    }
+    const float L = wave_sum(lsum);
+    if (lane == 0) Lsh = L;
   }
+  __syncthreads();
+  const float inv = 1.f / Lsh;
   for (int dd = threadIdx.x; dd < dh; dd += blockDim.x) {
     float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = ph[s * (dh + 2) + dh];
-      if (ms != -INFINITY) acc += ph[s * (dh + 2) + dd] * __expf(ms - M);
-    }
-    o[h * dh + dd] = acc / L;
+    for (int s = 0; s < nsplit; ++s) acc += ph[s * (dh + 2) + dd] * wsh[s];
+    o[h * dh + dd] = acc * inv;
   }
 }
 
@@ -370,8 +493,16 @@ template <typename T, int DH>
 static hipError_t decode_attn_t(const float* q, const void* ks, const void* vs, int H, int Hk, int cap,
                                 int window, const int64_t* pos, float* part, float* o, int nsplit,
                                 hipStream_t st) {
-  hipLaunchKernelGGL((decode_attn_kernel<T, DH>), dim3(Hk, nsplit), dim3(256), 0, st, q, (const T*)ks,
-                     (const T*)vs, H, Hk, cap, window, pos, 1.f / sqrtf((float)DH), nsplit, part);
+  const dim3 grid(Hk, nsplit);
+  const float sc = 1.f / sqrtf((float)DH);
+  switch (H / Hk) {
+    case 1: hipLaunchKernelGGL((decode_attn_kernel<T, DH, 1>), grid, dim3(256), 0, st, q, (const T*)ks, (const T*)vs, H, Hk, cap, window, pos, sc, nsplit, part); break;
+    case 2: hipLaunchKernelGGL((decode_attn_kernel<T, DH, 2>), grid, dim3(256), 0, st, q, (const T*)ks, (const T*)vs, H, Hk, cap, window, pos, sc, nsplit, part); break;
+    case 3: hipLaunchKernelGGL((decode_attn_kernel<T, DH, 3>), grid, dim3(256), 0, st, q, (const T*)ks, (const T*)vs, H, Hk, cap, window, pos, sc, nsplit, part); break;
+    case 4: hipLaunchKernelGGL((decode_attn_kernel<T, DH, 4>), grid, dim3(256), 0, st, q, (const T*)ks, (const T*)vs, H, Hk, cap, window, pos, sc, nsplit, part); break;
+    case 8: hipLaunchKernelGGL((decode_attn_kernel<T, DH, 8>), grid, dim3(256), 0, st, q, (const T*)ks, (const T*)vs, H, Hk, cap, window, pos, sc, nsplit, part); break;
+    default: return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL(decode_attn_combine_kernel, dim3(H), dim3(128), 0, st, part, nsplit, DH, o);
   return hipGetLastError();
 }
@@ -379,7 +510,7 @@ static hipError_t decode_attn_t(const float* q, const void* ks, const void* vs, 
 hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vstore, int H, int Hk, int dh,
                        int cap, int window, const int64_t* pos, float* part, float* o, int nsplit,
                        hipStream_t st) {
-  if (H / Hk > 8) return hipErrorInvalidValue;
+  if (nsplit > 256) return hipErrorInvalidValue;
   if (dt == DT::BF16) {
     if (dh == 128) return decode_attn_t<bf16, 128>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);
     if (dh == 64) return decode_attn_t<bf16, 64>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);

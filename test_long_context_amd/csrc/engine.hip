@@ -763,7 +763,7 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     A(&p, 64);
     c->d_tok = (int32_t*)p;
   }
-  c->dec_split = 32;
+  c->dec_split = 64;
   Af(&c->dec, (size_t)4 * (c->QKV + 2 * Fm + 2 * d + c->H * c->dh) +
                   (size_t)c->H * c->dec_split * (c->dh + 2));
   if (!ok) {
