@@ -662,6 +662,10 @@ gemm_bf16_kernel(GemmArgs g) {
           for (int j = 0; j < FN; ++j) mma16(acc[i][j], af[s][i], bf2[s][j]);
       }
     }
+    // keep every MFMA of this tile issued before the wait for the next
+    // tile's loads: left to itself the scheduler hoists the wait (and the
+    // barrier) above most of them, exposing the whole load latency
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
