@@ -229,8 +229,6 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
           }
         }
     }
-    // every MFMA of the tile stays ahead of the wait for the next tile
-    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };

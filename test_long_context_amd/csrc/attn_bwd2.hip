@@ -215,8 +215,6 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq2_kernel(AttnArgs a, int ks
           for (int db = 0; db < DB; ++db) mma32(acc[db], ld_tr_op<DH>(ks_, kb * 32 + 16 * u, db * 32, lane), dsf[u]);
       }
     }
-    // every MFMA of the tile stays ahead of the wait for the next tile
-    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -366,8 +364,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
             mma32(accK[db], ld_tr_op<DH>(qs_, qb * 32 + 16 * u, db * 32, lane), sb[qb][u]);
           }
     }
-    // every MFMA of the tile stays ahead of the wait for the next tile
-    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
