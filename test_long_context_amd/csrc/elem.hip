@@ -225,7 +225,7 @@ hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const
 // at tab[pos * dh/2 + j] (built on the host from float64 angles).
 template <typename T>
 __global__ void rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, int64_t pos0,
-                                    const float2* tab, T* q, T* ks, T* vs, T* vts, int cap,
+                                    const float2* tab, T* q, T* ks, T* vs, int cap,
                                     int64_t min_pos) {
   const int t = blockIdx.x;
   const int64_t pos = pos0 + t;
@@ -253,22 +253,52 @@ __global__ void rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, 
   if (store)
     for (int i = threadIdx.x; i < Hk * dh; i += blockDim.x) {
       const int kh = i / dh, j = i % dh;
-      const T v = row[(H + Hk) * dh + i];
-      vs[((long)kh * cap + slot) * dh + j] = v;
-      if (vts) vts[((long)kh * dh + j) * cap + vt_slot(slot)] = v;
+      vs[((long)kh * cap + slot) * dh + j] = row[(H + Hk) * dh + i];
     }
+}
+
+// The transposed value store: a workgroup takes 64 tokens of one key head,
+// stages their value rows in LDS and writes each of the dh rows of the store
+// as 64 consecutive positions (vt_slot permutes within aligned groups of 16,
+// so a wave's stores still cover whole 128-byte runs).
+template <typename T>
+__global__ void __launch_bounds__(256) vt_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, int64_t pos0,
+                                                         T* vts, int cap, int64_t min_pos) {
+  extern __shared__ unsigned char vt_lds[];
+  T* Vs = (T*)vt_lds;  // [dh][65]
+  constexpr int TT = 64, PITCH = TT + 1;
+  const int t0 = blockIdx.x * TT, kh = blockIdx.y;
+  const int W = (H + 2 * Hk) * dh;
+  for (int e = threadIdx.x; e < TT * dh; e += blockDim.x) {
+    const int t = e / dh, d = e % dh;
+    if (t0 + t < n) Vs[d * PITCH + t] = qkv[(long)(t0 + t) * W + (H + Hk) * dh + kh * dh + d];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < TT * dh; e += blockDim.x) {
+    const int d = e / TT, t = e % TT;
+    const int64_t pos = pos0 + t0 + t;
+    if (t0 + t < n && pos >= min_pos) vts[((long)kh * dh + d) * cap + vt_slot(pos & (cap - 1))] = Vs[d * PITCH + t];
+  }
 }
 
 hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, int64_t pos0,
                         const float2* tab, void* q, void* ks, void* vs, void* vts, int cap,
                         int64_t min_pos, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  if (dt == DT::BF16)
+  const dim3 vgrid((n + 63) / 64, Hk);
+  if (dt == DT::BF16) {
     hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(n), dim3(RB), 0, st, (const bf16*)qkv, n, H, Hk,
-                       dh, pos0, tab, (bf16*)q, (bf16*)ks, (bf16*)vs, (bf16*)vts, cap, min_pos);
-  else
+                       dh, pos0, tab, (bf16*)q, (bf16*)ks, (bf16*)vs, cap, min_pos);
+    if (vts)
+      hipLaunchKernelGGL(vt_scatter_kernel<bf16>, vgrid, dim3(256), (size_t)dh * 65 * sizeof(bf16), st,
+                         (const bf16*)qkv, n, H, Hk, dh, pos0, (bf16*)vts, cap, min_pos);
+  } else {
     hipLaunchKernelGGL(rope_scatter_kernel<float>, dim3(n), dim3(RB), 0, st, (const float*)qkv, n, H,
-                       Hk, dh, pos0, tab, (float*)q, (float*)ks, (float*)vs, (float*)vts, cap, min_pos);
+                       Hk, dh, pos0, tab, (float*)q, (float*)ks, (float*)vs, cap, min_pos);
+    if (vts)
+      hipLaunchKernelGGL(vt_scatter_kernel<float>, vgrid, dim3(256), (size_t)dh * 65 * sizeof(float), st,
+                         (const float*)qkv, n, H, Hk, dh, pos0, (float*)vts, cap, min_pos);
+  }
   return hipGetLastError();
 }
 
