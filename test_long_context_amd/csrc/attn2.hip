@@ -287,44 +287,69 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
 }
 
 // o = sum_z o_z 2^(m_z - M) / sum_z l_z 2^(m_z - M), lse = (M + log2 L) ln 2;
-// one workgroup per query row.
+// one workgroup per query row: the first H threads turn each head's ks
+// (m, l) pairs into weights in LDS, then the row's H * DH outputs are
+// combined four at a time.
 __global__ void __launch_bounds__(256) attn_fwd_combine_kernel(const float* opart, const float* ml, int ks, int n,
                                                                int H, int DH, bf16* o, float* lse) {
+  extern __shared__ float cw[];  // [ks][H]
   const int row = blockIdx.x;
-  for (int i = threadIdx.x; i < H * DH; i += blockDim.x) {
-    const int h = i / DH;
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
     float M = -INFINITY;
     for (int z = 0; z < ks; ++z) M = fmaxf(M, ml[(long)z * 2 * H * n + (long)h * n + row]);
-    float L = 0.f, acc = 0.f;
+    float L = 0.f;
     for (int z = 0; z < ks; ++z) {
       const float mz = ml[(long)z * 2 * H * n + (long)h * n + row];
-      if (mz == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(mz - M);
+      const float w = mz == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mz - M);
       L += ml[(long)z * 2 * H * n + (long)H * n + (long)h * n + row] * w;
-      acc += opart[(long)z * n * H * DH + (long)row * H * DH + i] * w;
+      cw[z * H + h] = w;
     }
-    o[(long)row * H * DH + i] = (bf16)(L > 0.f ? acc / L : 0.f);
-    if (lse && i % DH == 0) lse[(long)h * n + row] = (M + __log2f(L)) * LN2;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    for (int z = 0; z < ks; ++z) cw[z * H + h] *= inv;
+    if (lse) lse[(long)h * n + row] = (M + __log2f(L)) * LN2;
+  }
+  __syncthreads();
+  const int W4 = H * DH / 4;  // DH is a multiple of 4
+  for (int i = threadIdx.x; i < W4; i += blockDim.x) {
+    const int h = i * 4 / DH;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < ks; ++z)
+      acc += *(const floatx4*)(opart + (long)z * n * H * DH + (long)row * H * DH + 4 * i) * cw[z * H + h];
+    bf16x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (bf16)acc[e];
+    *(bf16x4*)(o + (long)row * H * DH + 4 * i) = r;
   }
 }
 
 hipError_t attn_fwd2_combine(const AttnArgs& a, hipStream_t st) {
   const int ks = (a.ksplit > 1 && a.opart && a.mlpart) ? a.ksplit : 1;
   if (ks <= 1 || a.n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_combine_kernel, dim3(a.n), dim3(256), 0, st, a.opart, a.mlpart, ks, a.n, a.H, a.dh,
-                     (bf16*)a.o, a.lse);
+  hipLaunchKernelGGL(attn_fwd_combine_kernel, dim3(a.n), dim3(256), (size_t)ks * a.H * sizeof(float), st, a.opart,
+                     a.mlpart, ks, a.n, a.H, a.dh, (bf16*)a.o, a.lse);
   return hipGetLastError();
 }
 
+// Key-range splits for a launch of few query blocks: the split count s
+// (1..4, at least 4 key tiles per part) that minimises the per-CU load,
+// ceil(base s / 256) parts of 1/s of the keys each, plus a small charge per
+// split for the combine pass (measured at 1024 queries x 24 heads: s = 4
+// fills 256 CUs evenly and beats s = 3 by a sixth).
 int attn_fwd2_splits(const AttnArgs& a) {
   if (a.n <= 0) return 1;
   const long base = (long)((a.n + 127) / 128) * a.H;  // 32 queries per wave
   if (base >= 512) return 1;
   const long tiles = (a.window + 128 + BKV2 - 1) / BKV2;
-  long s = (512 + base - 1) / base;
-  if (s > tiles / 4) s = tiles / 4;
-  if (s > 4) s = 4;
-  return s < 1 ? 1 : (int)s;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int s = 1; s <= 4 && (s == 1 || s <= tiles / 4); ++s) {
+    const double cost = (double)((base * s + 255) / 256) / s + 0.02 * s;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
 }
 
 bool attn_fwd2_supported(DT dt, const AttnArgs& a) {

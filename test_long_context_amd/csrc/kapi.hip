@@ -112,6 +112,7 @@ extern "C" ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k,
     e = attn_fwd(to_dt(dtype), a, (hipStream_t)stream);
   } else {
     if (!attn_fwd2_supported(to_dt(dtype), a)) return TTT_ERR_UNSUPPORTED;
+    if (!al16(q) || !al16(k) || !al16(v) || !al16(vt) || !al16(o)) return TTT_ERR_INVALID_ARG;
     const int ks = fwd_splits(n, H, dh, window, ksplit);
     if (ks > 1 && n > 0) {
       if (!work || !al16(work)) return TTT_ERR_INVALID_ARG;
