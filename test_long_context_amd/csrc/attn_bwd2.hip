@@ -401,14 +401,21 @@ bool attn_bwd2_supported(DT dt, const AttnArgs& a) {
 }
 
 int attn_bwd2_dq_parts(const AttnArgs& a) {
-  // enough workgroups to cover the CUs twice, at least 8 key tiles each
+  // key-range parts (1..4, at least 8 key tiles each) minimising the per-CU
+  // load ceil(base s / 256) / s, with a small charge per part for the
+  // partial sums (as for the forward's key splits)
   const long base = (long)((a.n + 127) / 128) * a.H;
   const long tiles = (a.window + 128 + BT - 1) / BT + 1;
-  long s = (512 + base - 1) / base;
-  const long cap_t = tiles / 8 > 1 ? tiles / 8 : 1;
-  if (s > cap_t) s = cap_t;
-  if (s > 4) s = 4;
-  return s < 1 ? 1 : (int)s;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int s = 1; s <= 4 && (s == 1 || s <= tiles / 8); ++s) {
+    const double cost = (double)((base * s + 255) / 256) / s + 0.02 * s;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
 }
 
 int attn_bwd2_kv_parts(const AttnArgs& a) { return a.H / a.Hk; }
