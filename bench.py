@@ -54,9 +54,9 @@ ROOF_SOURCES = ("test_long_context_amd/csrc/attn2.hip", "test_long_context_amd/c
 # --pmc-summary), keyed by (workload, T, source hash): valid only for the
 # kernel source the counters were taken on.
 TRAFFIC = {
-    ("3b", 131072, "f3c275ca586b13fd"): dict(fetch_bytes_per_launch=56579911, write_bytes_per_launch=49959304,
+    ("3b", 131072, "2762ceee5ab004fd"): dict(fetch_bytes_per_launch=56914576, write_bytes_per_launch=60356263,
                                              fetch_scale=1.9999, write_scale=1.0,
-                                             traffic_bytes_per_launch=163116047),
+                                             traffic_bytes_per_launch=174181774),
 }
 
 
