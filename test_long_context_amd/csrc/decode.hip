@@ -489,6 +489,139 @@ __global__ void __launch_bounds__(128) decode_attn_combine_kernel(const float* p
   }
 }
 
+// Window attention of one token on MFMA (bf16 stores, dh 64 / 128, up to 16
+// query heads per key head). Workgroup (key head, split) of 4 waves; wave w
+// of split s takes the key blocks of 32 positions (aligned to 32, so a block
+// never wraps the ring) blk = b0 + 4 s + w + i * 4 nsplit. Per block:
+//   S^T [32 keys x 16 queries] = K Q^T as two 16x16x32 tiles per 32 of dh,
+//   masked to the window, exponentiated (base 2, scale folded into q) after
+//   the running maximum is raised to the block's;
+//   O^T [dh x 16] += V^T P^T with V^T read from the transposed store.
+// The PV product's k-slot 8 g + e (lane group g) is key 4 g + e for e < 4 and
+// 16 + 4 g + (e - 4) otherwise: exactly the keys the S^T tiles leave in lane
+// group g, so P goes from the accumulators to the B operand without a lane
+// exchange; under the store's slot permutation (bits 2 and 3 swapped) those
+// four keys sit at four consecutive slots of each 16-slot group. The waves
+// merge through LDS into one (o, max, sum) partial per (query head, split),
+// max in natural-log units for the combine kernel.
+constexpr float LN2F = 0.6931471805599453f;
+
+template <int DH>
+__global__ void __launch_bounds__(256) decode_attn_mfma_kernel(const float* q, const bf16* kst, const bf16* vts,
+                                                               int H, int Hk, int cap, int window,
+                                                               const int64_t* pos, float scale2, int nsplit,
+                                                               float* part) {
+  constexpr int KS = DH / 32;  // 32-wide steps of the QK product
+  constexpr int MT = DH / 16;  // 16-row tiles of O^T
+  __shared__ float sm[4][16], sl[4][16];
+  __shared__ float so[4][DH][17];
+  const int kh = blockIdx.x, split = blockIdx.y;
+  const int G = H / Hk;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t p = *pos;
+  const int64_t lo = p - window + 1 > 0 ? p - window + 1 : 0;
+  const int64_t b0 = lo >> 5, b1 = p >> 5;
+
+  Frag8<bf16> qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      qf[s].v[e] = (bf16)(c < G ? q[(long)(kh * G + c) * DH + 32 * s + 8 * g + e] * scale2 : 0.f);
+  float m = -INFINITY, l = 0.f;
+  floatx4 o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) o[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const bf16* kb = kst + (long)kh * cap * DH;
+  const bf16* vb = vts + (long)kh * DH * cap;
+  const int vo = 8 * (g & 1) + 4 * (g >> 1);
+  for (int64_t blk = b0 + 4 * split + wid; blk <= b1; blk += 4 * (int64_t)nsplit) {
+    const long base = (long)((blk << 5) & (cap - 1));
+    Frag8<bf16> kf[2][KS];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) ld8(kf[t][s], kb + (base + 16 * t + c) * DH + 32 * s + 8 * g);
+    Frag8<bf16> vf[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16* row = vb + (long)(16 * mt + c) * cap + base + vo;
+      const bf16x4 a = *(const bf16x4*)row;
+      const bf16x4 bq = *(const bf16x4*)(row + 16);
+      vf[mt].v = __builtin_shufflevector(a, bq, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    floatx4 st[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) mma16(st[t], kf[t][s], qf[s]);
+    float sv[8];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t pk = (blk << 5) + 16 * t + 4 * g + j;
+        const float x = (pk >= lo && pk <= p) ? st[t][j] : -INFINITY;
+        sv[4 * t + j] = x;
+        bm = fmaxf(bm, x);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = fmaxf(m, bm);
+    if (mn == -INFINITY) continue;  // no key of the window so far (the same for every lane)
+    const float cr = __builtin_amdgcn_exp2f(m - mn);
+    float ps = 0.f;
+    Frag8<bf16> pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(sv[e] - mn);
+      ps += pe;
+      pf.v[e] = (bf16)pe;
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * cr + ps;
+    m = mn;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      o[mt] *= cr;
+      mma16(o[mt], vf[mt], pf);
+    }
+  }
+  if (g == 0) {
+    sm[wid][c] = m;
+    sl[wid][c] = l;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) so[wid][16 * mt + 4 * g + j][c] = o[mt][j];
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * DH; e += blockDim.x) {
+    const int qc = e / DH, dd = e % DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][qc]);
+    float acc = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float ww = __builtin_amdgcn_exp2f(sm[w][qc] - M);
+        acc += ww * so[w][dd][qc];
+        L += ww * sl[w][qc];
+      }
+    }
+    float* dst = part + ((long)(kh * G + qc) * nsplit + split) * (DH + 2);
+    dst[dd] = acc;
+    if (dd == 0) {
+      dst[DH] = M == -INFINITY ? -INFINITY : M * LN2F;
+      dst[DH + 1] = L;
+    }
+  }
+}
+
 template <typename T, int DH>
 static hipError_t decode_attn_t(const float* q, const void* ks, const void* vs, int H, int Hk, int cap,
                                 int window, const int64_t* pos, float* part, float* o, int nsplit,
@@ -507,10 +640,34 @@ static hipError_t decode_attn_t(const float* q, const void* ks, const void* vs, 
   return hipGetLastError();
 }
 
-hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vstore, int H, int Hk, int dh,
-                       int cap, int window, const int64_t* pos, float* part, float* o, int nsplit,
+static bool decode_mfma_ok(DT dt, int H, int Hk, int dh, bool has_vt) {
+  return dt == DT::BF16 && has_vt && (dh == 64 || dh == 128) && H / Hk <= 16;
+}
+
+int decode_attn_splits(DT dt, int H, int Hk, int dh, int window, bool has_vt) {
+  if (!decode_mfma_ok(dt, H, Hk, dh, has_vt)) return 64;
+  // one 32-key block per wave: the window touches at most window / 32 + 1 blocks
+  const long blocks = (long)window / 32 + 1;
+  const long s = (blocks + 3) / 4;
+  return (int)std::min<long>(std::max<long>(s, 1), 256);
+}
+
+hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vstore, const void* vtstore, int H,
+                       int Hk, int dh, int cap, int window, const int64_t* pos, float* part, float* o,
                        hipStream_t st) {
-  if (nsplit > 256) return hipErrorInvalidValue;
+  const int nsplit = decode_attn_splits(dt, H, Hk, dh, window, vtstore != nullptr);
+  if (decode_mfma_ok(dt, H, Hk, dh, vtstore != nullptr)) {
+    const dim3 grid(Hk, nsplit);
+    const float sc2 = 1.f / sqrtf((float)dh) * 1.4426950408889634f;
+    if (dh == 128)
+      hipLaunchKernelGGL(decode_attn_mfma_kernel<128>, grid, dim3(256), 0, st, q, (const bf16*)kstore,
+                         (const bf16*)vtstore, H, Hk, cap, window, pos, sc2, nsplit, part);
+    else
+      hipLaunchKernelGGL(decode_attn_mfma_kernel<64>, grid, dim3(256), 0, st, q, (const bf16*)kstore,
+                         (const bf16*)vtstore, H, Hk, cap, window, pos, sc2, nsplit, part);
+    hipLaunchKernelGGL(decode_attn_combine_kernel, dim3(H), dim3(128), 0, st, part, nsplit, dh, o);
+    return hipGetLastError();
+  }
   if (dt == DT::BF16) {
     if (dh == 128) return decode_attn_t<bf16, 128>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);
     if (dh == 64) return decode_attn_t<bf16, 64>(q, kstore, vstore, H, Hk, cap, window, pos, part, o, nsplit, st);

@@ -541,8 +541,8 @@ ttt_status decode_blocks(ttt_ctx* c, hipStream_t st) {
     HIPCHK(c, gemv(c->dt, c->wqkv[l], h, c->attn_norm[l], eps, c->QKV, d, GvEpi::STORE, qkv, st));
     HIPCHK(c, decode_rope_store(c->dt, qkv, H, Hk, dh, c->d_pos, c->rope, q, c->kring[l], c->vring[l],
                                 c->vtring[l], (int)c->cap, st));
-    HIPCHK(c, decode_attn(c->dt, q, c->kring[l], c->vring[l], H, Hk, dh, (int)c->cap, c->k, c->d_pos, part, o,
-                          c->dec_split, st));
+    HIPCHK(c, decode_attn(c->dt, q, c->kring[l], c->vring[l], c->vtring[l], H, Hk, dh, (int)c->cap, c->k, c->d_pos,
+                          part, o, st));
     HIPCHK(c, gemv(c->dt, c->wo[l], o, nullptr, 0.f, d, H * dh, GvEpi::ADD_F32, h, st));
     HIPCHK(c, gemv(c->dt, c->w12[l], h, c->mlp_norm[l], eps, 2 * c->F, d, GvEpi::SWIGLU, hm, st));
     HIPCHK(c, gemv(c->dt, c->w3[l], hm, nullptr, 0.f, d, c->F, GvEpi::ADD_F32, h, st));
@@ -763,7 +763,7 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     A(&p, 64);
     c->d_tok = (int32_t*)p;
   }
-  c->dec_split = 64;
+  c->dec_split = decode_attn_splits(c->dt, c->H, c->Hk, c->dh, c->k, c->dt == DT::BF16);
   Af(&c->dec, (size_t)4 * (c->QKV + 2 * Fm + 2 * d + c->H * c->dh) +
                   (size_t)c->H * c->dec_split * (c->dh + 2));
   if (!ok) {

@@ -163,9 +163,12 @@ hipError_t gemv(DT wdt, const void* W, const float* x, const float* g, float eps
 hipError_t decode_rope_store(DT dt, const float* qkv, int H, int Hk, int dh, const int64_t* pos,
                              const float2* rope_tab, float* q, void* kstore, void* vstore, void* vtstore, int cap,
                              hipStream_t st);
-// One query per head at position *pos over the window; part: [H][nsplit][dh + 2].
-hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vstore, int H, int Hk, int dh,
-                       int cap, int window, const int64_t* pos, float* part, float* o, int nsplit,
+// One query per head at position *pos over the window; part: [H][nsplit][dh + 2]
+// with nsplit = decode_attn_splits(...) (vtstore, the transposed value store,
+// may be null: then the lane-parallel kernel runs).
+int decode_attn_splits(DT dt, int H, int Hk, int dh, int window, bool has_vt);
+hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vstore, const void* vtstore, int H,
+                       int Hk, int dh, int cap, int window, const int64_t* pos, float* part, float* o,
                        hipStream_t st);
 hipError_t embed_row(DT dt, const int32_t* tok, const void* embed, int d, int V, float* h, int* err,
                      hipStream_t st);
