@@ -60,6 +60,32 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_rows_kernel(const TW* __restr
                                                           float* __restrict__ y) {
   extern __shared__ float xs[];
   __shared__ float red[GV_THREADS / 64];
+  constexpr int VE = WVec<TW>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (GV_THREADS / 64) + (threadIdx.x >> 6);
+  const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
+  const int p0 = wave * (GV_RPW / 2);
+  const bool active = p0 < npairs;  // waves past the last row still help stage x
+  int rows[GV_RPW];
+#pragma unroll
+  for (int i = 0; i < GV_RPW / 2; ++i) {
+    const int p = max(0, min(p0 + i, npairs - 1));
+    if constexpr (EPI == (int)GvEpi::SWIGLU) {
+      rows[2 * i] = (p >> 4) * 32 + (p & 15);
+      rows[2 * i + 1] = rows[2 * i] + 16;
+    } else {
+      rows[2 * i] = 2 * p;
+      rows[2 * i + 1] = min(2 * p + 1, N - 1);
+    }
+  }
+  const int nv = K / VE;
+  // the first sweep's weights are requested before x is staged, so their
+  // latency overlaps the normalisation
+  float w0[GV_RPW][VE];
+  const bool first = active && lane < nv;
+  if (first)
+#pragma unroll
+    for (int r = 0; r < GV_RPW; ++r) WVec<TW>::load(W + (long)rows[r] * K + lane * VE, w0[r]);
   if constexpr (NORM) {
     float ss = 0.f;
     for (int k = threadIdx.x; k < K; k += GV_THREADS) ss += x[k] * x[k];
@@ -69,29 +95,20 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_rows_kernel(const TW* __restr
     for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k];
   }
   __syncthreads();
-  constexpr int VE = WVec<TW>::N;
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * (GV_THREADS / 64) + (threadIdx.x >> 6);
-  const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
-  const int p0 = wave * (GV_RPW / 2);
-  if (p0 >= npairs) return;
-  int rows[GV_RPW];
-#pragma unroll
-  for (int i = 0; i < GV_RPW / 2; ++i) {
-    const int p = min(p0 + i, npairs - 1);
-    if constexpr (EPI == (int)GvEpi::SWIGLU) {
-      rows[2 * i] = (p >> 4) * 32 + (p & 15);
-      rows[2 * i + 1] = rows[2 * i] + 16;
-    } else {
-      rows[2 * i] = 2 * p;
-      rows[2 * i + 1] = min(2 * p + 1, N - 1);
-    }
-  }
+  if (!active) return;
   float acc[GV_RPW];
 #pragma unroll
   for (int r = 0; r < GV_RPW; ++r) acc[r] = 0.f;
-  const int nv = K / VE;
-  for (int v = lane; v < nv; v += 64) {
+  if (first) {
+    float xv[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) xv[e] = xs[lane * VE + e];
+#pragma unroll
+    for (int r = 0; r < GV_RPW; ++r)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[r] += w0[r][e] * xv[e];
+  }
+  for (int v = lane + 64; v < nv; v += 64) {
     float xv[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) xv[e] = xs[v * VE + e];
@@ -141,15 +158,6 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__
   extern __shared__ float xs[];
   __shared__ float red[GV_THREADS / 64];
   __shared__ float part[GV_THREADS / 64][GV_ROWS];
-  if constexpr (NORM) {
-    float ss = 0.f;
-    for (int k = threadIdx.x; k < K; k += GV_THREADS) ss += x[k] * x[k];
-    const float r = rsqrtf(block_sum(ss, red) / K + eps);
-    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k] * r * g[k];
-  } else {
-    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k];
-  }
-  __syncthreads();
   constexpr int VE = WVec<TW>::N;
   constexpr int NWV = GV_THREADS / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -167,13 +175,38 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__
       rows[2 * i + 1] = min(2 * p + 1, N - 1);
     }
   }
-  float acc[GV_ROWS];
-#pragma unroll
-  for (int r = 0; r < GV_ROWS; ++r) acc[r] = 0.f;
   const int nv = K / VE;
   const int q = (nv + NWV - 1) / NWV;  // vectors per wave
   const int v0 = wid * q, v1 = min(nv, v0 + q);
-  for (int v = v0 + lane; v < v1; v += 64) {
+  // the first sweep's weights are requested before x is staged, so their
+  // latency overlaps the normalisation
+  float w0[GV_ROWS][VE];
+  const bool first = v0 + lane < v1;
+  if (first)
+#pragma unroll
+    for (int r = 0; r < GV_ROWS; ++r) WVec<TW>::load(W + (long)rows[r] * K + (v0 + lane) * VE, w0[r]);
+  if constexpr (NORM) {
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < K; k += GV_THREADS) ss += x[k] * x[k];
+    const float r = rsqrtf(block_sum(ss, red) / K + eps);
+    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k] * r * g[k];
+  } else {
+    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k];
+  }
+  __syncthreads();
+  float acc[GV_ROWS];
+#pragma unroll
+  for (int r = 0; r < GV_ROWS; ++r) acc[r] = 0.f;
+  if (first) {
+    float xv[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) xv[e] = xs[(v0 + lane) * VE + e];
+#pragma unroll
+    for (int r = 0; r < GV_ROWS; ++r)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[r] += w0[r][e] * xv[e];
+  }
+  for (int v = v0 + lane + 64; v < v1; v += 64) {
     float xv[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) xv[e] = xs[v * VE + e];
