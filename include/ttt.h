@@ -191,9 +191,11 @@ ttt_status ttt_timing_read(ttt_ctx* ctx, int32_t kclass, double* total_ms, int64
  * which equals the per-token recursion M_t = beta_t M_{t-1} + eta_t G_t,
  * W_t = gamma_t W_{t-1} + M_t at the chunk end. k, v: device bf16 [H, T, D];
  * eta, beta, gamma: device float [H, T], beta, gamma in (0, 1], eta >= 0;
- * W, M: device float [H, D, D], updated in place to the state after the last
- * chunk. D must be 128 or 64; C a multiple of 64, at most 2048; T >= 1.
- * Device errors: TTT_ERR_UNSUPPORTED for other D or C. */
+ * W, M: device float [H, D, D], 16-byte aligned, updated in place to the
+ * state after the last chunk. D must be 128 or 64; C a multiple of 64, at
+ * most 2048; T >= 1. Errors: TTT_ERR_UNSUPPORTED for other D or C,
+ * TTT_ERR_INVALID_ARG for null or misaligned pointers. The call keeps a
+ * device work buffer per process (grown on demand). */
 ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float* eta, const float* beta,
                             const float* gamma, float* W, float* M, int32_t H, int64_t T,
                             int32_t D, int32_t C, void* stream);

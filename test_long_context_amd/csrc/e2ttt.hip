@@ -15,9 +15,8 @@
 // (W0 for e_t, then the scaled e_t) are split into bf16 hi + lo parts so that
 // the products keep ~16 significant bits; k, v are bf16 inputs (exact).
 //
-// Kernels: e2_scalars (all chunks at once), then per chunk e2_partial (one
-// workgroup per (128-token slice, head): partial sums of the two
-// aggregations) and e2_combine (sum of slices + the W0/M0 terms, in place).
+// Kernels: e2_scalars (all chunks at once), then one e2_chunk launch per
+// chunk (the aggregations and the state update for that chunk).
 #include <math.h>
 
 #include <algorithm>
@@ -154,176 +153,194 @@ hipError_t e2_scalars(const float* eta, const float* beta, const float* gamma, i
 }
 
 // ------------------------------------------------------- slice aggregation
-static constexpr int SL = 128;  // tokens per slice
+// ------------------------------------------------------------ chunk kernel
+// One launch per chunk; workgroup (16-row block of the state, half of its
+// columns, head) of 4 waves. Each wave takes 32-token blocks of the chunk
+// (block b for b = wave, wave + 4, ...):
+//   E [32 t x 16 i] = K W0^T - V  (A = K rows from LDS, B = W0 rows i as
+//                                   bf16 hi + lo terms held in registers),
+//   x = K_t E split into bf16 hi + lo -- the A operand of the aggregations,
+//     straight from the accumulators: k-slot 8 g + e of lane group g is token
+//     4 g + e (e < 4) or 16 + 4 g + (e - 4), the tokens the E tiles leave
+//     there;
+//   dW, dM [16 i x 16 j tiles] += x^T K with the B operand K^T (tokens in
+//     that slot order) read from the wave's LDS copy of the K block by
+//     transposing LDS reads (ds_read_b64_tr_b16, rows 4 g .. 4 g + 3 and
+//     16 + 4 g .. 16 + 4 g + 3).
+// The waves' sums meet in LDS and the workgroup writes
+//   W_out = gamma~_0 W0 + beta~_0 R_1 M0 + dW,  M = beta~_0 M0 + dM.
+// W is read whole-row (for E) by both column halves of a row block, so it
+// ping-pongs between two buffers across chunks; M is read and written
+// element by element by one workgroup and stays in place.
+typedef short e2_shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) e2_shortx4* e2_lds_s4_t;
 
 template <int D>
-__global__ void __launch_bounds__(256) e2_partial_kernel(const bf16* __restrict__ K,
-                                                         const bf16* __restrict__ Vv,
-                                                         const float* __restrict__ KW,
-                                                         const float* __restrict__ KM,
-                                                         const float* __restrict__ W, int64_t T,
-                                                         int64_t a0, int n, float* __restrict__ part,
-                                                         int nslice, int H) {
-  constexpr int P = SL + 8;     // row stride of token-contiguous tiles
-  constexpr int PD = D + 8;     // row stride of feature-contiguous tiles
-  // region X: W0 hi/lo [D][PD] during phase 1, then E hi/lo [D][P]
-  __shared__ __attribute__((aligned(16))) bf16 X[2 * D * (P > PD ? P : PD)];
-  __shared__ __attribute__((aligned(16))) bf16 Ks[SL * PD];  // [t][j]
-  __shared__ __attribute__((aligned(16))) bf16 Kt[D * P];    // [j][t]
-  __shared__ float ksc[2][SL];
+__global__ void __launch_bounds__(256) e2_chunk_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Vv,
+                                                       const float* __restrict__ KW, const float* __restrict__ KM,
+                                                       const float* __restrict__ coef, const float* __restrict__ Win,
+                                                       float* __restrict__ Wout, float* __restrict__ M, int64_t T,
+                                                       int64_t a0, int n, int64_t nch, int64_t r) {
+  constexpr int KS = D / 32;   // 32-wide steps over the feature dimension
+  constexpr int JH = D / 2;    // state columns per workgroup
+  constexpr int JT = JH / 16;  // their 16-column tiles
+  constexpr int KP = D + 8;    // LDS row pitch of a K block (elements)
+  constexpr int BT = 32;       // tokens per block
+  constexpr int NV = BT * D / 8 / 64;  // 16-byte vectors of a K block per lane
+  constexpr int RED = 4 * 2 * 16 * JH;  // floats of the cross-wave sums
+  static_assert(RED * 4 <= 4 * BT * KP * 2, "the cross-wave sums reuse the K blocks' LDS");
+  __shared__ __attribute__((aligned(16))) bf16 Kb[4][BT * KP];
+  const int ib = blockIdx.x >> 1, jh = blockIdx.x & 1, h = blockIdx.y;
+  const int i0 = ib * 16, j0 = jh * JH;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const bf16* Kh = K + ((int64_t)h * T + a0) * D;
+  const bf16* Vh = Vv + ((int64_t)h * T + a0) * D;
+  const float* KWh = KW + (int64_t)h * T + a0;
+  const float* KMh = KM + (int64_t)h * T + a0;
+  const float* W0 = Win + (int64_t)h * D * D;
 
-  const int slice = blockIdx.x, h = blockIdx.y;
-  const int t0 = slice * SL;
-  const int nt = min(SL, n - t0);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int fr = lane & 15, fg = lane >> 4;
-  const bf16* Kh = K + ((int64_t)h * T + a0 + t0) * D;
-  const bf16* Vh = Vv + ((int64_t)h * T + a0 + t0) * D;
-  const float* W0 = W + (int64_t)h * D * D;
-
-  // W0 -> hi/lo (bf16) rows [i][j]
-  bf16* Whi = X;
-  bf16* Wlo = X + D * PD;
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e % D;
-    const float w = W0[e];
-    const bf16 hi = (bf16)w;
-    Whi[i * PD + j] = hi;
-    Wlo[i * PD + j] = (bf16)(w - (float)hi);
-  }
-  // K slice [t][j] and its transpose [j][t]; rows past the chunk are zero
-  for (int e = tid; e < SL * (D / 8); e += 256) {
-    const int t = e / (D / 8), j8 = (e % (D / 8)) * 8;
-    Frag8<bf16> f;
-    if (t < nt) ld8(f, Kh + (int64_t)t * D + j8);
-    else zero8(f);
-    st8(Ks + t * PD + j8, f);
+  Frag8<bf16> wh[KS], wl[KS];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) Kt[(j8 + q) * P + t] = f.v[q];
+  for (int s = 0; s < KS; ++s) {
+    const floatx4* src = (const floatx4*)(W0 + (i0 + c) * D + 32 * s + 8 * g);
+    const floatx4 w4[2] = {src[0], src[1]};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float w = w4[e >> 2][e & 3];
+      const bf16 hi = (bf16)w;
+      wh[s].v[e] = hi;
+      wl[s].v[e] = (bf16)(w - (float)hi);
+    }
   }
-  if (tid < SL) {
-    ksc[0][tid] = tid < nt ? KW[h * T + a0 + t0 + tid] : 0.f;
-    ksc[1][tid] = tid < nt ? KM[h * T + a0 + t0 + tid] : 0.f;
+  floatx4 dw[JT], dm[JT];
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) dw[jt] = dm[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  bf16* Ks = Kb[wid];
+  const int nb = (n + BT - 1) / BT;
+  // a block's operands: its K rows (NV vectors per lane) and, for the tokens
+  // of this lane's accumulator rows, v (column i0 + c), K^W and K^M
+  // Loads are unconditional (token indices past the chunk clamp to its last
+  // token) and raw, so nothing consumes them before the block is processed;
+  // tokens past the chunk get K^W = K^M = 0 there, which zeroes their x and
+  // hence their share of the products (the clamped rows are finite).
+  struct Blk {
+    bf16x8 k[NV];
+    bf16 v[2][4];
+    float kw[2][4], km[2][4];
+  };
+  auto load = [&](Blk& o, int blk) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int vi = lane + 64 * q, row = vi / (D / 8), col = (vi % (D / 8)) * 8;
+      const int t = min(blk * BT + row, n - 1);
+      o.k[q] = *(const bf16x8*)(Kh + (int64_t)t * D + col);
+    }
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = min(blk * BT + 16 * tile + 4 * g + e, n - 1);
+        o.v[tile][e] = Vh[(int64_t)t * D + i0 + c];
+        o.kw[tile][e] = KWh[t];
+        o.km[tile][e] = KMh[t];
+      }
+  };
+  // operands run three blocks ahead of the products (a ring of four; one
+  // wave per SIMD leaves the registers for it)
+  auto step = [&](Blk& cur, Blk& nxt, int blk) {
+    // the previous block's LDS reads were consumed by its products, so the
+    // wave's single buffer can be refilled (LDS operations of a wave are in order)
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int vi = lane + 64 * q, row = vi / (D / 8), col = (vi % (D / 8)) * 8;
+      *(bf16x8*)(Ks + row * KP + col) = cur.k[q];
+    }
+    if (blk + 12 < nb) load(nxt, blk + 12);
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    floatx4 et[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        Frag8<bf16> a;
+        ld8(a, Ks + (16 * tile + c) * KP + 32 * s + 8 * g);
+        mma16(et[tile], a, wh[s]);
+        mma16(et[tile], a, wl[s]);
+      }
+    Frag8<bf16> xwh, xwl, xmh, xml;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = blk * BT + 16 * tile + 4 * g + e < n;
+        const float ee = et[tile][e] - (float)cur.v[tile][e];
+        const float xw = ok ? cur.kw[tile][e] * ee : 0.f, xm = ok ? cur.km[tile][e] * ee : 0.f;
+        const bf16 hw = (bf16)xw, hm = (bf16)xm;
+        xwh.v[4 * tile + e] = hw;
+        xwl.v[4 * tile + e] = (bf16)(xw - (float)hw);
+        xmh.v[4 * tile + e] = hm;
+        xml.v[4 * tile + e] = (bf16)(xm - (float)hm);
+      }
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const bf16* p = Ks + (4 * g + (c >> 2)) * KP + j0 + 16 * jt + 4 * (c & 3);
+      const e2_shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((e2_lds_s4_t)p);
+      const e2_shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((e2_lds_s4_t)(p + 16 * KP));
+      typedef short e2_shortx8 __attribute__((ext_vector_type(8)));
+      Frag8<bf16> bk;
+      bk.v = __builtin_bit_cast(bf16x8, (e2_shortx8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      mma16(dw[jt], xwh, bk);
+      mma16(dw[jt], xwl, bk);
+      mma16(dm[jt], xmh, bk);
+      mma16(dm[jt], xml, bk);
+    }
+  };
+  Blk b0, b1, b2, b3;
+  if (wid < nb) load(b0, wid);
+  if (wid + 4 < nb) load(b1, wid + 4);
+  if (wid + 8 < nb) load(b2, wid + 8);
+  for (int blk = wid; blk < nb; blk += 16) {
+    step(b0, b3, blk);
+    if (blk + 4 < nb) step(b1, b0, blk + 4);
+    if (blk + 8 < nb) step(b2, b1, blk + 8);
+    if (blk + 12 < nb) step(b3, b2, blk + 12);
   }
+  // cross-wave sums: red[w][0 / 1][i][j]
   __syncthreads();
-
-  // phase 1: E[t][i] = sum_j K[t][j] W0[i][j] - V[t][i]; wave owns 32 tokens.
-  constexpr int FI = D / 16;
-  floatx4 e[2][FI];
+  float* red = (float*)&Kb[0][0];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-    for (int ni = 0; ni < FI; ++ni) e[mt][ni] = floatx4{0, 0, 0, 0};
-#pragma unroll
-  for (int kk = 0; kk < D; kk += 32) {
-    Frag8<bf16> a[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) ld8(a[mt], Ks + (wid * 32 + mt * 16 + fr) * PD + kk + fg * 8);
-#pragma unroll
-    for (int ni = 0; ni < FI; ++ni) {
-      Frag8<bf16> bh, bl;
-      ld8(bh, Whi + (ni * 16 + fr) * PD + kk + fg * 8);
-      ld8(bl, Wlo + (ni * 16 + fr) * PD + kk + fg * 8);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        mma16(e[mt][ni], a[mt], bh);
-        mma16(e[mt][ni], a[mt], bl);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * g + e, j = 16 * jt + c;
+      red[((wid * 2 + 0) * 16 + i) * JH + j] = dw[jt][e];
+      red[((wid * 2 + 1) * 16 + i) * JH + j] = dm[jt][e];
     }
-  }
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int ni = 0; ni < FI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = wid * 32 + mt * 16 + fg * 4 + r;
-        const int i = ni * 16 + fr;
-        const float vv = t < nt ? (float)Vh[(int64_t)t * D + i] : 0.f;
-        e[mt][ni][r] -= vv;
-      }
-  __syncthreads();  // W0 tiles no longer needed
-
-  // phase 2: for each aggregation, write the scaled E^T split hi/lo as
-  // [i][t] rows and contract over t with K^T rows [j][t].
-  bf16* Ehi = X;
-  bf16* Elo = X + D * P;
-  for (int which = 0; which < 2; ++which) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int ni = 0; ni < FI; ++ni)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = wid * 32 + mt * 16 + fg * 4 + r;
-          const int i = ni * 16 + fr;
-          const float x = e[mt][ni][r] * ksc[which][t];
-          const bf16 hi = (bf16)x;
-          Ehi[i * P + t] = hi;
-          Elo[i * P + t] = (bf16)(x - (float)hi);
-        }
-    __syncthreads();
-    // output [i][j], wave owns rows i in [wid * D/4, +D/4)
-    constexpr int FM = D / 64;  // 16-row tiles per wave
-    floatx4 acc[FM][FI];
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-      for (int nj = 0; nj < FI; ++nj) acc[mi][nj] = floatx4{0, 0, 0, 0};
-#pragma unroll
-    for (int kk = 0; kk < SL; kk += 32) {
-      Frag8<bf16> ah[FM], al[FM];
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi) {
-        const int i = wid * (D / 4) + mi * 16 + fr;
-        ld8(ah[mi], Ehi + i * P + kk + fg * 8);
-        ld8(al[mi], Elo + i * P + kk + fg * 8);
-      }
-#pragma unroll
-      for (int nj = 0; nj < FI; ++nj) {
-        Frag8<bf16> bk;
-        ld8(bk, Kt + (nj * 16 + fr) * P + kk + fg * 8);
-#pragma unroll
-        for (int mi = 0; mi < FM; ++mi) {
-          mma16(acc[mi][nj], ah[mi], bk);
-          mma16(acc[mi][nj], al[mi], bk);
-        }
-      }
-    }
-    float* out = part + ((((int64_t)slice * H + h) * 2 + which) * D) * D;
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-      for (int nj = 0; nj < FI; ++nj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = wid * (D / 4) + mi * 16 + fg * 4 + r;
-          const int j = nj * 16 + fr;
-          out[i * D + j] = acc[mi][nj][r];
-        }
-    __syncthreads();
-  }
-}
-
-// W <- c0 W + c1 M + sum_s dW_s ;  M <- c2 M + sum_s dM_s   (per head)
-__global__ void e2_combine_kernel(float* W, float* M, const float* part, const float* coef, int H,
-                                  int D, int nslice, int64_t nch, int64_t r) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per = (int64_t)D * D;
-  if (e >= per * H) return;
-  const int h = (int)(e / per);
-  const int64_t o = e % per;
+  __syncthreads();
   const float* cf = coef + ((int64_t)h * nch + r) * 4;
-  float dw = 0.f, dm = 0.f;
-  for (int s = 0; s < nslice; ++s) {
-    const float* p = part + (((int64_t)s * H + h) * 2) * per;
-    dw += p[o];
-    dm += p[per + o];
+  const float c0 = cf[0], c1 = cf[1], c2 = cf[2];
+  float* Wo = Wout + (int64_t)h * D * D;
+  float* Mh = M + (int64_t)h * D * D;
+  for (int e = threadIdx.x; e < 16 * JH; e += 256) {
+    const int i = e / JH, j = e % JH;
+    float sw = 0.f, sm = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      sw += red[((w * 2 + 0) * 16 + i) * JH + j];
+      sm += red[((w * 2 + 1) * 16 + i) * JH + j];
+    }
+    const int64_t idx = (int64_t)(i0 + i) * D + j0 + j;
+    const float w0 = W0[idx], m0 = Mh[idx];
+    Wo[idx] = c0 * w0 + c1 * m0 + sw;
+    Mh[idx] = c2 * m0 + sm;
   }
-  const float w0 = W[e], m0 = M[e];
-  W[e] = cf[0] * w0 + cf[1] * m0 + dw;
-  M[e] = cf[2] * m0 + dm;
 }
+
 
 }  // namespace ttt
 
@@ -342,6 +359,7 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
                                        int32_t D, int32_t C, void* stream) {
   using namespace ttt;
   if (!k || !v || !eta || !beta || !gamma || !W || !M) return TTT_ERR_INVALID_ARG;
+  if (((uintptr_t)W & 15) || ((uintptr_t)M & 15)) return TTT_ERR_INVALID_ARG;
   if (H < 1 || T < 1 || C < 1) return TTT_ERR_INVALID_ARG;
   if (D != 128 && D != 64) return TTT_ERR_UNSUPPORTED;
   if (C % 64 || C > 2048) return TTT_ERR_UNSUPPORTED;
@@ -352,9 +370,7 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
   }
   hipStream_t st = (hipStream_t)stream;
   const int64_t nch = (T + C - 1) / C;
-  const int nslice = (C + SL - 1) / SL;
-  const size_t need = (size_t)2 * H * T * 4 + (size_t)H * nch * 4 * 4 +
-                      (size_t)nslice * H * 2 * D * D * 4 + 256 * 4;
+  const size_t need = (size_t)2 * H * T * 4 + (size_t)H * nch * 4 * 4 + (size_t)H * D * D * 4 + 512;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
   // Work buffer cached per process (grown on demand, reallocated on a device change).
@@ -375,21 +391,25 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
   float* KW = (float*)g_e2.p;
   float* KM = KW + (size_t)H * T;
   float* coef = KM + (size_t)H * T;
-  float* part = coef + (size_t)H * nch * 4 + 64;
+  // the other W buffer, 256-byte aligned (its rows are read as 16-byte vectors)
+  float* W2 = (float*)(((uintptr_t)(coef + (size_t)H * nch * 4) + 255) & ~(uintptr_t)255);
   if (e2_scalars(eta, beta, gamma, H, T, C, KW, KM, coef, st) != hipSuccess) return TTT_ERR_HIP;
-  const int64_t per = (int64_t)H * D * D;
+  const dim3 grid(2 * (D / 16), H);
   for (int64_t r = 0; r < nch; ++r) {
     const int n = (int)std::min<int64_t>(C, T - r * C);
-    const int ns = (n + SL - 1) / SL;
+    const float* src = (r & 1) ? W2 : W;
+    float* dst = (r & 1) ? W : W2;
     if (D == 128)
-      hipLaunchKernelGGL(e2_partial_kernel<128>, dim3(ns, H), dim3(256), 0, st, (const bf16*)k,
-                         (const bf16*)v, KW, KM, W, T, r * C, n, part, ns, H);
+      hipLaunchKernelGGL(e2_chunk_kernel<128>, grid, dim3(256), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
+                         src, dst, M, T, r * C, n, nch, r);
     else
-      hipLaunchKernelGGL(e2_partial_kernel<64>, dim3(ns, H), dim3(256), 0, st, (const bf16*)k,
-                         (const bf16*)v, KW, KM, W, T, r * C, n, part, ns, H);
-    hipLaunchKernelGGL(e2_combine_kernel, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, st, W, M,
-                       part, coef, H, D, ns, nch, r);
+      hipLaunchKernelGGL(e2_chunk_kernel<64>, grid, dim3(256), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
+                         src, dst, M, T, r * C, n, nch, r);
     if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
+  }
+  // an odd number of chunks leaves the state in the work buffer
+  if (nch & 1) {
+    if (hipMemcpyAsync(W, W2, (size_t)H * D * D * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return TTT_ERR_HIP;
   }
   return TTT_OK;
 }
