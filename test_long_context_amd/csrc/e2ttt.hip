@@ -175,8 +175,10 @@ hipError_t e2_scalars(const float* eta, const float* beta, const float* gamma, i
 typedef short e2_shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) e2_shortx4* e2_lds_s4_t;
 
+constexpr int E2_NW = 8;  // waves per chunk workgroup
+
 template <int D>
-__global__ void __launch_bounds__(256) e2_chunk_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Vv,
+__global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Vv,
                                                        const float* __restrict__ KW, const float* __restrict__ KM,
                                                        const float* __restrict__ coef, const float* __restrict__ Win,
                                                        float* __restrict__ Wout, float* __restrict__ M, int64_t T,
@@ -187,9 +189,10 @@ __global__ void __launch_bounds__(256) e2_chunk_kernel(const bf16* __restrict__ 
   constexpr int KP = D + 8;    // LDS row pitch of a K block (elements)
   constexpr int BT = 32;       // tokens per block
   constexpr int NV = BT * D / 8 / 64;  // 16-byte vectors of a K block per lane
-  constexpr int RED = 4 * 2 * 16 * JH;  // floats of the cross-wave sums
-  static_assert(RED * 4 <= 4 * BT * KP * 2, "the cross-wave sums reuse the K blocks' LDS");
-  __shared__ __attribute__((aligned(16))) bf16 Kb[4][BT * KP];
+  constexpr int NW = E2_NW;
+  constexpr int RED = NW * 2 * 16 * JH;  // floats of the cross-wave sums
+  static_assert(RED * 4 <= NW * BT * KP * 2, "the cross-wave sums reuse the K blocks' LDS");
+  __shared__ __attribute__((aligned(16))) bf16 Kb[NW][BT * KP];
   const int ib = blockIdx.x >> 1, jh = blockIdx.x & 1, h = blockIdx.y;
   const int i0 = ib * 16, j0 = jh * JH;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -247,8 +250,8 @@ __global__ void __launch_bounds__(256) e2_chunk_kernel(const bf16* __restrict__ 
         o.km[tile][e] = KMh[t];
       }
   };
-  // operands run three blocks ahead of the products (a ring of four; one
-  // wave per SIMD leaves the registers for it)
+  // operands run one block ahead of the products (two waves per SIMD hide
+  // the rest)
   auto step = [&](Blk& cur, Blk& nxt, int blk) {
     // the previous block's LDS reads were consumed by its products, so the
     // wave's single buffer can be refilled (LDS operations of a wave are in order)
@@ -257,7 +260,7 @@ __global__ void __launch_bounds__(256) e2_chunk_kernel(const bf16* __restrict__ 
       const int vi = lane + 64 * q, row = vi / (D / 8), col = (vi % (D / 8)) * 8;
       *(bf16x8*)(Ks + row * KP + col) = cur.k[q];
     }
-    if (blk + 12 < nb) load(nxt, blk + 12);
+    if (blk + NW < nb) load(nxt, blk + NW);
 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -300,15 +303,11 @@ __global__ void __launch_bounds__(256) e2_chunk_kernel(const bf16* __restrict__ 
       mma16(dm[jt], xml, bk);
     }
   };
-  Blk b0, b1, b2, b3;
+  Blk b0, b1;
   if (wid < nb) load(b0, wid);
-  if (wid + 4 < nb) load(b1, wid + 4);
-  if (wid + 8 < nb) load(b2, wid + 8);
-  for (int blk = wid; blk < nb; blk += 16) {
-    step(b0, b3, blk);
-    if (blk + 4 < nb) step(b1, b0, blk + 4);
-    if (blk + 8 < nb) step(b2, b1, blk + 8);
-    if (blk + 12 < nb) step(b3, b2, blk + 12);
+  for (int blk = wid; blk < nb; blk += 2 * NW) {
+    step(b0, b1, blk);
+    if (blk + NW < nb) step(b1, b0, blk + NW);
   }
   // cross-wave sums: red[w][0 / 1][i][j]
   __syncthreads();
@@ -326,11 +325,11 @@ __global__ void __launch_bounds__(256) e2_chunk_kernel(const bf16* __restrict__ 
   const float c0 = cf[0], c1 = cf[1], c2 = cf[2];
   float* Wo = Wout + (int64_t)h * D * D;
   float* Mh = M + (int64_t)h * D * D;
-  for (int e = threadIdx.x; e < 16 * JH; e += 256) {
+  for (int e = threadIdx.x; e < 16 * JH; e += NW * 64) {
     const int i = e / JH, j = e % JH;
     float sw = 0.f, sm = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       sw += red[((w * 2 + 0) * 16 + i) * JH + j];
       sm += red[((w * 2 + 1) * 16 + i) * JH + j];
     }
@@ -400,10 +399,10 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
     const float* src = (r & 1) ? W2 : W;
     float* dst = (r & 1) ? W : W2;
     if (D == 128)
-      hipLaunchKernelGGL(e2_chunk_kernel<128>, grid, dim3(256), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
+      hipLaunchKernelGGL(e2_chunk_kernel<128>, grid, dim3(E2_NW * 64), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
                          src, dst, M, T, r * C, n, nch, r);
     else
-      hipLaunchKernelGGL(e2_chunk_kernel<64>, grid, dim3(256), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
+      hipLaunchKernelGGL(e2_chunk_kernel<64>, grid, dim3(E2_NW * 64), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
                          src, dst, M, T, r * C, n, nch, r);
     if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
   }
