@@ -195,7 +195,7 @@ def e2_bench(args, tla, torch, synth):
                config=dict(workload=f"e2ttt chunk scan, H={H}, T={T}, D={D}, C={C}"),
                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                              frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
-                             kernel="e2ttt_chunk_scan (scalars, partial aggregation, combine)",
+                             kernel="e2ttt_chunk_scan (scalar scan, one fused aggregation + update launch per chunk)",
                              algorithmic_bytes=algo, mfma_tflops=round(flops / (ms * 1e-3) / 1e12, 2)))
     if not args.no_cpu_baseline:
         from oracle import e2ttt as E
