@@ -169,12 +169,14 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int qp = qw + qb * 32 + lr;
+        // the maximum is taken on raw scores and the scale folded into the
+        // exponent below (exp2(s sc2 - m) as one fma), sc2 > 0
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            float v = s[kb][qb][j] * sc2;
+            float v = s[kb][qb][j];
             if (!full) {
               const int kp = kt + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
               if (!(kp <= qp && kp > qp - a.window)) v = -INFINITY;
@@ -182,7 +184,7 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
             s[kb][qb][j] = v;
             tmax = fmaxf(tmax, v);
           }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc2;
         // lazy rescale: keep the reference max unless this tile exceeds it by
         // more than RESCALE (then p <= 2^RESCALE); wave-uniform branch
         const bool need = tmax > m_run[qb] + RESCALE;
@@ -194,13 +196,13 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
           for (int db = 0; db < DB; ++db) o[qb][db] *= corr;
           m_run[qb] = mnew;
         }
-        const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+        const float nmu = (m_run[qb] == -INFINITY) ? 0.f : -m_run[qb];
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const float p = __builtin_amdgcn_exp2f(s[kb][qb][j] - mu);
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][j], sc2, nmu));
             s[kb][qb][j] = p;
             rs += p;
           }
