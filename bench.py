@@ -60,6 +60,13 @@ TRAFFIC = {
 }
 
 
+# MFMA busy of the same kernel (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
+# SIMDs x active cycles, --pmc-busy), keyed like TRAFFIC.
+MFMA_BUSY = {
+    ("3b", 131072, "9c731710cdbb97a5"): 0.4268,
+}
+
+
 def roof_source_hash() -> str:
     h = hashlib.sha256()
     for f in ROOF_SOURCES:
@@ -332,6 +339,33 @@ def decode_bench(args, c, w, tok, tla, torch):
     print(json.dumps(out), flush=True)
 
 
+def pmc_busy(c, T, d):
+    """MFMA busy of the attention-forward launches of one step, from a rocprofv3
+    --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_INSTS_MFMA
+    run of `bench.py --attn-replay`. SQ_VALU_MFMA_BUSY_CYCLES is summed over
+    the chip's 1024 SIMDs; GRBM_GUI_ACTIVE over its 8 XCDs and SQ_BUSY_CYCLES
+    over its 32 shader engines count the active cycles during each dispatch,
+    so busy / (1024 x active per XCD) is the fraction of the kernel's time the
+    matrix cores were busy, independent of the clock (both normalisations are
+    printed as a cross-check). Launches are weighted as in --pmc-summary."""
+    per = {}
+    with open(os.path.join(d, "run_counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if "attn_fwd2_kernel" not in r["Kernel_Name"]:
+                continue
+            x = per.setdefault(int(r["Dispatch_Id"]), {})
+            x[r["Counter_Name"]] = x.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [per[k] for k in sorted(per)]
+    launches = attn_launches(c, T)
+    assert len(disp) == len(launches), (len(disp), len(launches))
+    def tot(name):
+        return sum(wt * x.get(name, 0.0) for x, (*_, wt) in zip(disp, launches))
+    busy, grbm, sq = tot("SQ_VALU_MFMA_BUSY_CYCLES"), tot("GRBM_GUI_ACTIVE"), tot("SQ_BUSY_CYCLES")
+    print(json.dumps(dict(kernel="attn_fwd2_kernel", dispatches=len(disp), source_sha=roof_source_hash(),
+                          mfma_busy_frac=round(busy / (1024 * grbm / 8), 4) if grbm else None,
+                          mfma_busy_frac_by_se_cycles=round(busy / (1024 * sq / 32), 4) if sq else None)))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,7 +381,10 @@ def main():
     ap.add_argument("--pmc-summary", nargs=4, metavar="DIR", help="bytes per attention launch from counter runs")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--e2", action="store_true", help="measure the E2-TTT chunk-end kernel instead")
+    ap.add_argument("--pmc-busy", metavar="DIR",
+                    help="MFMA-busy fraction of the attention forward from a counter run of --attn-replay")
     args = ap.parse_args()
+
     if args.copy_probe:
         copy_probe()
         return
@@ -368,6 +405,9 @@ def main():
     T = args.seq or c["seq"]
     if args.pmc_summary:
         pmc_summary(c, T, args.pmc_summary, args.workload)
+        return
+    if args.pmc_busy:
+        pmc_busy(c, T, args.pmc_busy)
         return
     if args.attn_replay:
         attn_replay(c, T, tla, torch)
@@ -434,13 +474,15 @@ def main():
     src = roof_source_hash()
     tr = TRAFFIC.get((args.workload, T, src))
     traffic = None if tr is None else tr["traffic_bytes_per_launch"]
+    busy = MFMA_BUSY.get((args.workload, T, src))
     roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=traffic,
                 kernel=f"attn_fwd2_kernel (sliding-window attention forward, head_dim {c['head_dim']})",
                 traffic_unit="bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                 launches_per_step=r_n // args.steps, avg_launch_us=round(avg_s * 1e6, 2),
                 algorithmic_gflop_per_launch=round(r_fl / r_n / 1e9, 3),
-                share_of_step=round(r_ms / args.steps / ms, 4), source_sha=src)
+                share_of_step=round(r_ms / args.steps / ms, 4), source_sha=src,
+                mfma_busy_frac=busy)
 
     out = dict(metric=METRIC, value=round(tps, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms, 2), higher_is_better=True, scaling="weak",

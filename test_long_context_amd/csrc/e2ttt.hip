@@ -358,10 +358,10 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
                                        int32_t D, int32_t C, void* stream) {
   using namespace ttt;
   if (!k || !v || !eta || !beta || !gamma || !W || !M) return TTT_ERR_INVALID_ARG;
-  if (((uintptr_t)W & 15) || ((uintptr_t)M & 15)) return TTT_ERR_INVALID_ARG;
   if (H < 1 || T < 1 || C < 1) return TTT_ERR_INVALID_ARG;
   if (D != 128 && D != 64) return TTT_ERR_UNSUPPORTED;
   if (C % 64 || C > 2048) return TTT_ERR_UNSUPPORTED;
+  if (((uintptr_t)W & 15) || ((uintptr_t)M & 15)) return TTT_ERR_INVALID_ARG;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
     (void)hipGetLastError();
