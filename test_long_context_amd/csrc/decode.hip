@@ -15,7 +15,7 @@ namespace ttt {
 
 namespace {
 constexpr int GV_THREADS = 256;
-constexpr int GV_ROWS = 8;  // split-K kernel: rows per workgroup (four pairs)
+constexpr int GV_ROWS = 4;   // split-K kernel: rows per workgroup (two pairs)
 constexpr int GV_RPW = 4;   // row kernel: rows per wave (two pairs)
 
 template <typename TW> struct WVec;  // 16 bytes of weights -> floats
