@@ -108,7 +108,8 @@ struct ttt_ctx {
   // never overwrites what an update still reads
   hipStream_t side = nullptr;
   std::vector<hipEvent_t> ev_dyn;            // per dynamic block: its dW inputs are ready
-  hipEvent_t ev_join = nullptr;              // side stream done with this mini-batch
+  std::vector<hipEvent_t> ev_upd;            // per dynamic block: its update is done
+  hipEvent_t ev_join = nullptr;              // side stream done with the prefill
   std::vector<void*> ghd_t;                  // [b, d] gradient into each dynamic MLP (storage dtype)
   std::vector<void*> dh12d;                  // [b, 2 Fd] SwiGLU pre-activation gradients per dynamic block
   hipStream_t dstream = nullptr;             // decode graph capture stream
@@ -423,10 +424,14 @@ ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipSt
       g.C2 = c->hmid;
       TCALL(KC_GL, gfl(n, 2 * F, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
       RUN(gemm_resid(c, KC_GL, c->hmid, F, c->w3[l], F, nullptr, n, d, F, &np, st));
+      // the previous mini-batch's update of this block (side stream) reads
+      // xn_d and the saved activations written from here on
+      HIPCHK(c, hipStreamWaitEvent(st, c->ev_upd[i], 0));
       TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_dyn[i], c->dyn_norm[i], n, d, eps,
                                             c->xn_d[i], c->r_dyn[i], st));
     } else {
       // block s: the residual stream comes from the hoisted prefix
+      HIPCHK(c, hipStreamWaitEvent(st, c->ev_upd[i], 0));
       TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, c->hres + a0 * d, nullptr, 0, hl, c->h_dyn[i], c->dyn_norm[i], n,
                                             d, eps, c->xn_d[i], c->r_dyn[i], st));
     }
@@ -481,6 +486,7 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       g2.C3 = c->dw12_lo[i];
       g2.scale = lr;
       TCALL(KC_SGD, gfl(2 * Fd, d, n), 2.0 * Fd * d * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g2, st));
+      HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
     }
     if (l == s) break;
     TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], n, d, c->gh, c->gh_t, 1, st));
@@ -518,9 +524,8 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->ghd_t[i - 1], 1, st));
     }
   }
-  // the next mini-batch's forward reads the updated fast weights
-  HIPCHK(c, hipEventRecord(c->ev_join, c->side));
-  HIPCHK(c, hipStreamWaitEvent(st, c->ev_join, 0));
+  // the next mini-batch's forward waits for each block's update just before
+  // it first touches that block's update inputs (loop_forward)
   return TTT_OK;
 }
 
@@ -751,6 +756,9 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   }
   if (ok && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) ok = false;
   c->ev_dyn.assign(nd, nullptr);
+  c->ev_upd.assign(nd, nullptr);
+  for (int i = 0; i < nd && ok; ++i)
+    if (hipEventCreateWithFlags(&c->ev_upd[i], hipEventDisableTiming) != hipSuccess) ok = false;
   for (int i = 0; i < nd && ok; ++i)
     if (hipEventCreateWithFlags(&c->ev_dyn[i], hipEventDisableTiming) != hipSuccess) ok = false;
   if (ok && hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess) ok = false;
@@ -880,6 +888,9 @@ ttt_status ttt_prefill(ttt_ctx* c, const int32_t* tok, int64_t T, float* loss, f
     r = loop_backward(c, a0, n, st);
     if (r != TTT_OK) return r;
   }
+  // the caller's stream sees every update
+  HIPCHK(c, hipEventRecord(c->ev_join, c->side));
+  HIPCHK(c, hipStreamWaitEvent(st, c->ev_join, 0));
   HIPCHK(c, set_pos(c->d_pos, T, st));
   c->pos = T;
   return TTT_OK;
@@ -978,6 +989,8 @@ void ttt_destroy(ttt_ctx* c) {
   if (c->dgraph) (void)hipGraphExecDestroy(c->dgraph);
   if (c->dstream) (void)hipStreamDestroy(c->dstream);
   for (hipEvent_t e : c->ev_dyn)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->ev_upd)
     if (e) (void)hipEventDestroy(e);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->side) (void)hipStreamDestroy(c->side);
