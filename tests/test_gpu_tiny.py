@@ -91,3 +91,43 @@ def test_tiny_dh64_window_spanning_many_tiles():
     c = synth.config("tiny", d_model=128, n_heads=2, n_kv_heads=1, head_dim=64, window=100,
                      minibatch=40, ffn_hidden=128, dyn_ffn_hidden=96)
     check(c, T=230)
+
+
+# Edge cases of the loop's tiling and the block split (fp32, float64 oracle):
+# the shortest stream (one target), a stream shorter than one mini-batch, a
+# window equal to the mini-batch, every block dynamic (nothing hoisted but
+# block 0's attention and static MLP), and a single-layer model.
+EDGE = [
+    ("T=2", dict(), 2),
+    ("T<b", dict(minibatch=16), 11),
+    ("window=b", dict(window=16, minibatch=16), 70),
+    ("all blocks dynamic", dict(n_layers=2, n_dynamic=2), 60),
+    ("one layer", dict(n_layers=1, n_dynamic=1), 50),
+]
+
+
+@pytest.mark.parametrize("name,over,T", EDGE, ids=[e[0] for e in EDGE])
+def test_tiny_edge_cases(name, over, T):
+    check(synth.config("tiny", **over), T=T)
+
+
+def test_tiny_reset_and_repeat_is_bitwise_identical():
+    """ttt_reset restores W0, clears the store and the position: a second
+    prefill of the same stream gives the same losses and fast weights, bit
+    for bit (no atomics or order-dependent sums on the path)."""
+    import test_long_context_amd as tla
+    c = synth.config("tiny", n_layers=3, n_kv_heads=2, n_dynamic=2, window=24, minibatch=16)
+    w = to_device(synth.gen_weights(c))
+    tok = synth.gen_tokens(c, n=120).cuda()
+    m = tla.TTT(c, w, max_seq=120)
+    runs = []
+    for _ in range(2):
+        m.reset()
+        loss = m.prefill(tok)
+        m.sync()
+        runs.append((loss.cpu().numpy(), [tuple(x.cpu().numpy() for x in m.fast_weights(i)) for i in range(2)]))
+    m.close()
+    assert np.array_equal(runs[0][0], runs[1][0])
+    for a, b in zip(runs[0][1], runs[1][1]):
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
