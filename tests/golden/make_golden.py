@@ -1,17 +1,20 @@
-"""Writes expected values for the full-size 3B-shape parity test.
+"""Writes expected values for the full-size bf16 parity tests.
 
-Calls only the input generators (synth) and the CPU oracle: the 3B-shape
-weights and the first 1025 tokens of its Zipf stream are generated on the
-host, the float32 oracle runs the inner loop over them (mini-batch 0 with one
-SGD step, then the forward-only position 1024), and the file stores
+Calls only the input generators (synth) and the CPU oracle. Two cases:
 
-  * the per-token losses of positions 0..1023;
-  * for every dynamic block and matrix, 4096 seeded sample coordinates, the
-    oracle's fast weights there after the step, and max |W1 - W0| over the
-    whole matrix (the normaliser of the update-relative error);
-  * a fingerprint of the inputs (token ids, a few weight values).
+  * 3b_minibatch0 (default): the 3B-shape weights and the first 1025 tokens
+    of its Zipf stream; the float32 oracle runs mini-batch 0 with one SGD
+    step, then the forward-only position 1024 (about 10 minutes, ~30 GB RAM);
+  * 1b_full: the 1B-shape weights and its whole 32768-token stream: all 32
+    mini-batches and their updates (about 30 minutes, ~25 GB RAM).
 
-Usage: python tests/golden/make_golden.py  (about 10 minutes, ~30 GB RAM)
+Each file stores the per-token losses; for every dynamic block and matrix,
+4096 seeded sample coordinates, the oracle's fast weights there after the
+last update, and max |W_T - W0| over the whole matrix (the normaliser of the
+update-relative error); and a fingerprint of the inputs (token ids, a few
+weight values).
+
+Usage: python tests/golden/make_golden.py [3b_minibatch0 | 1b_full]
 """
 import os
 import sys
@@ -25,16 +28,22 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 import synth  # noqa: E402
 from oracle import ttt_e2e as O  # noqa: E402
 
-OUT = os.path.join(HERE, "ttt_3b_minibatch0.npz")
 NSAMPLE = 4096
+CASES = {
+    # name: (workload, tokens, output file)
+    "3b_minibatch0": ("3b", lambda c: c["minibatch"] + 1, "ttt_3b_minibatch0.npz"),
+    "1b_full": ("1b", lambda c: c["seq"], "ttt_1b_full.npz"),
+}
 
 
-def main():
-    c = synth.config("3b")
+def main(name="3b_minibatch0"):
+    workload, ntok, fname = CASES[name]
+    OUT = os.path.join(HERE, fname)
+    c = synth.config(workload)
     t0 = time.time()
     w = synth.gen_weights(c)
     print(f"weights generated in {time.time() - t0:.0f} s", flush=True)
-    tok = synth.gen_tokens(c, n=c["minibatch"] + 1).numpy()
+    tok = synth.gen_tokens(c, n=ntok(c)).numpy()
     wn = synth.weights_to_numpy(w, np.float32)
     del w
     t0 = time.time()
@@ -42,7 +51,7 @@ def main():
     print(f"oracle ran in {time.time() - t0:.0f} s", flush=True)
     rng = np.random.default_rng(1234)
     rec = {"loss": out["loss"].astype(np.float32), "tokens": tok.astype(np.int32),
-           "embed_head": wn["embed"][:4, :8].copy(), "w3_head": wn["layers"][27]["w3"][:4, :8].copy()}
+           "embed_head": wn["embed"][:4, :8].copy(), "w3_head": wn["layers"][-1]["w3"][:4, :8].copy()}
     for i, (blk, b0) in enumerate(zip(out["dyn"], wn["dyn"])):
         for k in ("w1", "w2", "w3"):
             W1, W0 = blk[k], b0[k]
@@ -55,4 +64,4 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    main(*sys.argv[1:2])

@@ -105,3 +105,37 @@ def test_bf16_3b_full_shape_first_minibatch_against_stored_oracle_values():
     say(f"  3b mini-batch 0: loss rel err {le:.3e}  sampled dW err {max(errs):.3e}")
     assert le < LOSS_TOL
     assert max(errs) < W_TOL
+
+
+GOLD_1B = os.path.join(HERE, "golden", "ttt_1b_full.npz")
+
+
+@pytest.mark.skipif(not os.path.exists(GOLD_1B), reason="golden values not generated")
+def test_bf16_1b_full_sequence_against_stored_oracle_values():
+    """The whole 1B-shape workload (32768 tokens, 32 mini-batches and their
+    updates): losses of all positions and 4096 sampled coordinates of every
+    fast-weight matrix after the last update, against values written by
+    tests/golden/make_golden.py 1b_full (oracle only)."""
+    import test_long_context_amd as tla
+    g = np.load(GOLD_1B, allow_pickle=False)
+    c = synth.config("1b")
+    w = synth.gen_weights(c, device="cuda")
+    tok = synth.gen_tokens(c, device="cuda")
+    assert np.array_equal(tok.cpu().numpy(), g["tokens"])
+    assert np.array_equal(w["embed"][:4, :8].float().cpu().numpy(), g["embed_head"])
+    m = tla.TTT(c, w, max_seq=c["seq"] + 1024)
+    loss = m.prefill(tok)
+    m.sync()
+    le = rel_loss_err(loss.cpu().numpy(), g["loss"])
+    nd = c["n_dynamic"] or (c["n_layers"] - (3 * c["n_layers"]) // 4)
+    errs = []
+    for i in range(nd):
+        ws = m.fast_weights(i)
+        for k, W in zip(("w1", "w2", "w3"), ws):
+            idx = torch.from_numpy(g[f"d{i}_{k}_idx"]).cuda()
+            got = W.reshape(-1)[idx].cpu().numpy().astype(np.float64)
+            errs.append(float(np.max(np.abs(got - g[f"d{i}_{k}_val"])) / g[f"d{i}_{k}_den"]))
+    m.close()
+    say(f"  1b full sequence: loss rel err {le:.3e}  sampled W_T err {max(errs):.3e}")
+    assert le < LOSS_TOL
+    assert max(errs) < W_TOL
