@@ -6,7 +6,10 @@ Calls only the input generators (synth) and the CPU oracle. Two cases:
     of its Zipf stream; the float32 oracle runs mini-batch 0 with one SGD
     step, then the forward-only position 1024 (about 10 minutes, ~30 GB RAM);
   * 1b_full: the 1B-shape weights and its whole 32768-token stream: all 32
-    mini-batches and their updates (about 30 minutes, ~25 GB RAM).
+    mini-batches and their updates (about 35 minutes, ~27 GB RAM);
+  * 3b_8minibatches: the 3B-shape weights and the first 8193 tokens of its
+    stream: 8 mini-batches and their updates, then the forward-only
+    position 8192 (about 30 minutes, ~30 GB RAM).
 
 Each file stores the per-token losses; for every dynamic block and matrix,
 4096 seeded sample coordinates, the oracle's fast weights there after the
@@ -14,7 +17,7 @@ last update, and max |W_T - W0| over the whole matrix (the normaliser of the
 update-relative error); and a fingerprint of the inputs (token ids, a few
 weight values).
 
-Usage: python tests/golden/make_golden.py [3b_minibatch0 | 1b_full]
+Usage: python tests/golden/make_golden.py [3b_minibatch0 | 1b_full | 3b_8minibatches]
 """
 import os
 import sys
@@ -33,6 +36,7 @@ CASES = {
     # name: (workload, tokens, output file)
     "3b_minibatch0": ("3b", lambda c: c["minibatch"] + 1, "ttt_3b_minibatch0.npz"),
     "1b_full": ("1b", lambda c: c["seq"], "ttt_1b_full.npz"),
+    "3b_8minibatches": ("3b", lambda c: 8 * c["minibatch"] + 1, "ttt_3b_8minibatches.npz"),
 }
 
 

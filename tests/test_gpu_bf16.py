@@ -74,53 +74,16 @@ def test_generator_cpu_gpu_identical():
     assert torch.equal(ta, tb)
 
 
-GOLD = os.path.join(HERE, "golden", "ttt_3b_minibatch0.npz")
-
-
-@pytest.mark.skipif(not os.path.exists(GOLD), reason="golden values not generated")
-def test_bf16_3b_full_shape_first_minibatch_against_stored_oracle_values():
-    """Full 3B shapes (bench launch configuration): mini-batch 0 of the 128K
-    stream, losses of all 1024 positions and 4096 sampled coordinates of every
-    fast-weight matrix after the first SGD step, against values written by
-    tests/golden/make_golden.py (oracle only)."""
+def check_stored(fname, workload, ntok, label):
+    """GPU prefill of the workload's first ntok tokens against values written
+    by tests/golden/make_golden.py (oracle only): losses of every position and
+    4096 sampled coordinates of every fast-weight matrix after the last
+    update, normalised by max |W_T - W0| over the matrix."""
     import test_long_context_amd as tla
-    g = np.load(GOLD, allow_pickle=False)
-    c = synth.config("3b")
+    g = np.load(os.path.join(HERE, "golden", fname), allow_pickle=False)
+    c = synth.config(workload)
     w = synth.gen_weights(c, device="cuda")
-    tok = synth.gen_tokens(c, n=c["minibatch"] + 1, device="cuda")
-    assert np.array_equal(tok.cpu().numpy(), g["tokens"])
-    assert np.array_equal(w["embed"][:4, :8].float().cpu().numpy(), g["embed_head"])
-    m = tla.TTT(c, w, max_seq=c["seq"] + 1024)
-    loss = m.prefill(tok)
-    m.sync()
-    le = rel_loss_err(loss.cpu().numpy(), g["loss"])
-    errs = []
-    for i in range(c["n_dynamic"]):
-        ws = m.fast_weights(i)
-        for k, W in zip(("w1", "w2", "w3"), ws):
-            idx = torch.from_numpy(g[f"d{i}_{k}_idx"]).cuda()
-            got = W.reshape(-1)[idx].cpu().numpy().astype(np.float64)
-            errs.append(float(np.max(np.abs(got - g[f"d{i}_{k}_val"])) / g[f"d{i}_{k}_den"]))
-    m.close()
-    say(f"  3b mini-batch 0: loss rel err {le:.3e}  sampled dW err {max(errs):.3e}")
-    assert le < LOSS_TOL
-    assert max(errs) < W_TOL
-
-
-GOLD_1B = os.path.join(HERE, "golden", "ttt_1b_full.npz")
-
-
-@pytest.mark.skipif(not os.path.exists(GOLD_1B), reason="golden values not generated")
-def test_bf16_1b_full_sequence_against_stored_oracle_values():
-    """The whole 1B-shape workload (32768 tokens, 32 mini-batches and their
-    updates): losses of all positions and 4096 sampled coordinates of every
-    fast-weight matrix after the last update, against values written by
-    tests/golden/make_golden.py 1b_full (oracle only)."""
-    import test_long_context_amd as tla
-    g = np.load(GOLD_1B, allow_pickle=False)
-    c = synth.config("1b")
-    w = synth.gen_weights(c, device="cuda")
-    tok = synth.gen_tokens(c, device="cuda")
+    tok = synth.gen_tokens(c, n=ntok(c), device="cuda")
     assert np.array_equal(tok.cpu().numpy(), g["tokens"])
     assert np.array_equal(w["embed"][:4, :8].float().cpu().numpy(), g["embed_head"])
     m = tla.TTT(c, w, max_seq=c["seq"] + 1024)
@@ -136,6 +99,32 @@ def test_bf16_1b_full_sequence_against_stored_oracle_values():
             got = W.reshape(-1)[idx].cpu().numpy().astype(np.float64)
             errs.append(float(np.max(np.abs(got - g[f"d{i}_{k}_val"])) / g[f"d{i}_{k}_den"]))
     m.close()
-    say(f"  1b full sequence: loss rel err {le:.3e}  sampled W_T err {max(errs):.3e}")
+    say(f"  {label}: loss rel err {le:.3e}  sampled W_T err {max(errs):.3e}")
     assert le < LOSS_TOL
     assert max(errs) < W_TOL
+
+
+def _stored(fname):
+    return pytest.mark.skipif(not os.path.exists(os.path.join(HERE, "golden", fname)),
+                              reason="golden values not generated")
+
+
+@_stored("ttt_3b_minibatch0.npz")
+def test_bf16_3b_full_shape_first_minibatch_against_stored_oracle_values():
+    """Full 3B shapes (bench launch configuration): mini-batch 0 of the 128K
+    stream (1024 positions, one update) and the forward-only position 1024."""
+    check_stored("ttt_3b_minibatch0.npz", "3b", lambda c: c["minibatch"] + 1, "3b mini-batch 0")
+
+
+@_stored("ttt_3b_8minibatches.npz")
+def test_bf16_3b_full_shape_eight_minibatches_against_stored_oracle_values():
+    """Full 3B shapes: the first 8 mini-batches of the stream and their
+    updates (each mini-batch under the previous one's fast weights)."""
+    check_stored("ttt_3b_8minibatches.npz", "3b", lambda c: 8 * c["minibatch"] + 1, "3b 8 mini-batches")
+
+
+@_stored("ttt_1b_full.npz")
+def test_bf16_1b_full_sequence_against_stored_oracle_values():
+    """The whole 1B-shape workload: 32768 tokens, 32 mini-batches and their
+    updates."""
+    check_stored("ttt_1b_full.npz", "1b", lambda c: c["seq"], "1b full sequence")
