@@ -55,8 +55,9 @@ ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajor, int32_t 
  * ((s & 4) << 1) | ((s & 8) >> 1) (bits 2 and 3 swapped inside each block of
  * 16). o: [n, H, dh]; lse: float [H, n] or NULL. variant: 0 =
  * chosen from the shape, 1 = 16x16 MFMA kernel, 2 / 3 = 32x32 MFMA kernel
- * with 32 / 64 queries per wave (bf16, dh 64/128, needs vt; q, k, v, vt
- * and o 16-byte aligned, else TTT_ERR_INVALID_ARG). */
+ * with 32 / 64 queries per wave, 4 = 32x32 MFMA kernel with 32 queries per
+ * wave in 8-wave workgroups (2-4: bf16, dh 64/128, need vt; q, k, v, vt and
+ * o 16-byte aligned, else TTT_ERR_INVALID_ARG). */
 ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, const void* vt,
                          void* o, float* lse, int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t cap,
                          int32_t window, int64_t pos0, int32_t variant, int32_t ksplit, void* work,

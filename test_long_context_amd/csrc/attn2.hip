@@ -62,9 +62,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t n
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes, 0x00020000);
 }
 
-template <int DH, int QB>
-__global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArgs a) {
-  constexpr int BQ = 4 * 32 * QB;
+template <int DH, int QB, int NWV = 4>
+__global__ void __launch_bounds__(NWV * 64, (QB == 1 && NWV == 4) ? 2 : 1) attn_fwd2_kernel(AttnArgs a) {
+  constexpr int BQ = NWV * 32 * QB;
   constexpr int KS = DH / 16;   // contraction steps over dh for S^T
   constexpr int DB = DH / 32;   // 32-row dh blocks of O^T
   constexpr int KV = DH / 8;    // 16-byte vectors per K row
@@ -127,17 +127,18 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) attn_fwd2_kernel(AttnArg
   // base + 16 l, so it fetches the logical vector belonging to that slot
   auto dma_tile = [&](int kt, bf16* kdst, bf16* vdst) {
     const int slot = (int)((a.pos0 + kt) & cmask);
+    static_assert(NIK % NWV == 0 && NIV % NWV == 0, "tile loads must split evenly over the waves");
 #pragma unroll
-    for (int i = 0; i < NIK / 4; ++i) {
-      const int j = wid + 4 * i;
+    for (int i = 0; i < NIK / NWV; ++i) {
+      const int j = wid + NWV * i;
       const int key = j * (1024 / (DH * 2)) + lane / KV, p = lane % KV;
       const int v = p ^ (key & (KV - 1));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kdst + j * 512), 16,
                                                (uint32_t)(((slot + key) * DH + v * 8) * 2), 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < NIV / 4; ++i) {
-      const int j = wid + 4 * i;
+    for (int i = 0; i < NIV / NWV; ++i) {
+      const int j = wid + NWV * i;
       const int row = j * 8 + lane / 8, p = lane % 8;
       const int v = p ^ ((row >> 1) & 7);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vdst + j * 512), 16,
@@ -358,20 +359,30 @@ bool attn_fwd2_supported(DT dt, const AttnArgs& a) {
   return dt == DT::BF16 && (a.dh == 128 || a.dh == 64) && a.vt != nullptr;
 }
 
+static int ks_of(const AttnArgs& a) { return (a.ksplit > 1 && a.opart && a.mlpart) ? a.ksplit : 1; }
+
 hipError_t attn_fwd2(DT dt, const AttnArgs& a, hipStream_t st, int qb) {
   if (a.n <= 0) return hipSuccess;
   if (!attn_fwd2_supported(dt, a)) return hipErrorInvalidValue;
-  // dh 128 with 64 queries per wave runs out of registers (spills) and is no
-  // faster even on long prefixes, so it is only taken on request
+  // qb: 0 = chosen from the shape, 1 = 32 queries per wave (4 waves),
+  // 2 = 64 queries per wave, 3 = 32 queries per wave in 8-wave workgroups
+  // (one K/V^T tile per CU instead of two). dh 128 with 64 queries per wave
+  // runs out of registers (spills) and is no faster even on long prefixes,
+  // so it is only taken on request.
   const bool big = qb == 2 || (qb == 0 && a.dh == 64 && (long)((a.n + 255) / 256) * a.H >= 512);
-  const int ks = (a.ksplit > 1 && a.opart && a.mlpart) ? a.ksplit : 1;
-  const int bq = big ? 256 : 128;
+  // 8-wave workgroups are faster on isolated long launches (3-9% at 16384
+  // queries x 24 heads) but not inside the prefill step, so only on request
+  const bool wide = qb == 3;
+  const int ks = ks_of(a);
+  const int bq = (big || wide) ? 256 : 128;
   const dim3 grid((a.n + bq - 1) / bq, a.H, ks);
   if (a.dh == 128) {
-    if (big) hipLaunchKernelGGL((attn_fwd2_kernel<128, 2>), grid, dim3(256), 0, st, a);
+    if (wide) hipLaunchKernelGGL((attn_fwd2_kernel<128, 1, 8>), grid, dim3(512), 0, st, a);
+    else if (big) hipLaunchKernelGGL((attn_fwd2_kernel<128, 2>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_fwd2_kernel<128, 1>), grid, dim3(256), 0, st, a);
   } else {
-    if (big) hipLaunchKernelGGL((attn_fwd2_kernel<64, 2>), grid, dim3(256), 0, st, a);
+    if (wide) hipLaunchKernelGGL((attn_fwd2_kernel<64, 1, 8>), grid, dim3(512), 0, st, a);
+    else if (big) hipLaunchKernelGGL((attn_fwd2_kernel<64, 2>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_fwd2_kernel<64, 1>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();

@@ -91,7 +91,7 @@ extern "C" ttt_status tttk_attn_fwd(int32_t dtype, const void* q, const void* k,
                                     void* work, void* stream) {
   ttt_status s = attn_check(dtype, n, H, Hk, dh, cap, window, pos0);
   if (s != TTT_OK) return s;
-  if (!q || !k || !v || !o || variant < 0 || variant > 3 || ksplit < 0 || ksplit > 4) return TTT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || variant < 0 || variant > 4 || ksplit < 0 || ksplit > 4) return TTT_ERR_INVALID_ARG;
   AttnArgs a{};
   a.q = q;
   a.k = k;

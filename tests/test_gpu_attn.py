@@ -80,7 +80,7 @@ def test_attention_fwd_bwd(case):
     VT = torch.empty(Hk, dh, cap, dtype=bf)
     VT[:, :, perm] = Vr.transpose(1, 2)
     VTd = VT.contiguous().to(dev)
-    for variant, ksplit in ((1, 1), (2, 1), (3, 1), (2, 2), (2, 3), (3, 4)):
+    for variant, ksplit in ((1, 1), (2, 1), (3, 1), (4, 1), (2, 2), (2, 3), (3, 4), (4, 2)):
         say(f"attn fwd variant {variant} ksplit {ksplit} case {case}")
         o = torch.full((n, H, dh), float("nan"), dtype=bf, device=dev)
         lse = torch.full((H, n), float("nan"), device=dev)
