@@ -8,6 +8,8 @@
 // weights once, so the step is bound by HBM bandwidth.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -15,26 +17,7 @@ namespace ttt {
 
 namespace {
 constexpr int GV_THREADS = 256;
-constexpr int GV_ROWS = 4;   // split-K kernel: rows per workgroup (two pairs)
-constexpr int GV_RPW = 4;   // row kernel: rows per wave (two pairs)
-
-template <typename TW> struct WVec;  // 16 bytes of weights -> floats
-template <> struct WVec<bf16> {
-  static constexpr int N = 8;
-  __device__ __forceinline__ static void load(const bf16* p, float (&o)[8]) {
-    const bf16x8 v = *(const bf16x8*)p;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
-  }
-};
-template <> struct WVec<float> {
-  static constexpr int N = 4;
-  __device__ __forceinline__ static void load(const float* p, float (&o)[4]) {
-    const floatx4 v = *(const floatx4*)p;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = v[e];
-  }
-};
+constexpr int GV_ROWS = 4;   // rows per wave (two pairs)
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -48,225 +31,389 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 }  // namespace
 
-// y = W x for one row x (fp32 [K]); W [N][K] row-major (nn.Linear layout).
-// NORM: x = RMSNorm(h) * g computed by every workgroup while staging x in
-// LDS. EPI: STORE y[n] = acc; ADD_F32 y[n] += acc; SWIGLU: rows are the
-// 16-interleaved (gate, up) layout and y[j] = silu(gate_j) * up_j.
-// Large N: a wave takes GV_RPW rows (two pairs) over the whole K; lanes
-// stride the row in 16-byte vectors, so each row is one coalesced sweep.
-template <typename TW, int EPI, bool NORM>
-__global__ void __launch_bounds__(GV_THREADS) gemv_rows_kernel(const TW* __restrict__ W, const float* __restrict__ x,
-                                                          const float* __restrict__ g, float eps, int N, int K,
-                                                          float* __restrict__ y) {
-  extern __shared__ float xs[];
-  __shared__ float red[GV_THREADS / 64];
-  constexpr int VE = WVec<TW>::N;
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * (GV_THREADS / 64) + (threadIdx.x >> 6);
-  const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
-  const int p0 = wave * (GV_RPW / 2);
-  const bool active = p0 < npairs;  // waves past the last row still help stage x
-  int rows[GV_RPW];
-#pragma unroll
-  for (int i = 0; i < GV_RPW / 2; ++i) {
-    const int p = max(0, min(p0 + i, npairs - 1));
-    if constexpr (EPI == (int)GvEpi::SWIGLU) {
-      rows[2 * i] = (p >> 4) * 32 + (p & 15);
-      rows[2 * i + 1] = rows[2 * i] + 16;
-    } else {
-      rows[2 * i] = 2 * p;
-      rows[2 * i + 1] = min(2 * p + 1, N - 1);
-    }
-  }
-  const int nv = K / VE;
-  // the first sweep's weights are requested before x is staged, so their
-  // latency overlaps the normalisation
-  float w0[GV_RPW][VE];
-  const bool first = active && lane < nv;
-  if (first)
-#pragma unroll
-    for (int r = 0; r < GV_RPW; ++r) WVec<TW>::load(W + (long)rows[r] * K + lane * VE, w0[r]);
-  if constexpr (NORM) {
-    float ss = 0.f;
-    for (int k = threadIdx.x; k < K; k += GV_THREADS) ss += x[k] * x[k];
-    const float r = rsqrtf(block_sum(ss, red) / K + eps);
-    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k] * r * g[k];
+// Destinations of the ROPE epilogue: the query row (fp32 [H dh]) and the
+// key / value rings ([Hk][cap][dh], values also transposed [Hk][dh][cap] at
+// vt_slot()) of the decode step at position *pos.
+struct GvRope {
+  const int64_t* pos;
+  const float2* tab;  // cos / sin per (position, frequency)
+  float* q;
+  void* ks;
+  void* vs;
+  void* vts;  // may be null
+  int H, Hk, dh, cap;
+};
+
+// Rows (r0, r1) that pair p of a GEMV produces together: adjacent rows,
+// the (gate, up) rows of the 16-interleaved SwiGLU layout, or the two rows
+// (j, j + dh / 2) of one head that RoPE rotates together.
+template <int EPI>
+__device__ __forceinline__ void gv_pair_rows(int p, int N, int half, int& r0, int& r1) {
+  if constexpr (EPI == (int)GvEpi::SWIGLU) {
+    r0 = (p >> 4) * 32 + (p & 15);
+    r1 = r0 + 16;
+  } else if constexpr (EPI == (int)GvEpi::ROPE) {
+    const int hh = p / half, j = p - hh * half;
+    r0 = hh * 2 * half + j;
+    r1 = r0 + half;
   } else {
-    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k];
+    r0 = 2 * p;
+    r1 = min(2 * p + 1, N - 1);
   }
-  __syncthreads();
-  if (!active) return;
-  float acc[GV_RPW];
-#pragma unroll
-  for (int r = 0; r < GV_RPW; ++r) acc[r] = 0.f;
-  if (first) {
-    float xv[VE];
-#pragma unroll
-    for (int e = 0; e < VE; ++e) xv[e] = xs[lane * VE + e];
-#pragma unroll
-    for (int r = 0; r < GV_RPW; ++r)
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[r] += w0[r][e] * xv[e];
-  }
-  for (int v = lane + 64; v < nv; v += 64) {
-    float xv[VE];
-#pragma unroll
-    for (int e = 0; e < VE; ++e) xv[e] = xs[v * VE + e];
-#pragma unroll
-    for (int r = 0; r < GV_RPW; ++r) {
-      float wv[VE];
-      WVec<TW>::load(W + (long)rows[r] * K + v * VE, wv);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[r] += wv[e] * xv[e];
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < GV_RPW; ++r) acc[r] = wave_sum(acc[r]);
-  if (lane == 0) {
-#pragma unroll
-    for (int i = 0; i < GV_RPW / 2; ++i) {
-      const int p = p0 + i;
-      if (p >= npairs) break;
-      if constexpr (EPI == (int)GvEpi::SWIGLU) {
-        const float a = acc[2 * i], c = acc[2 * i + 1];
-        y[p] = silu_f(a) * c;
+}
+
+template <int EPI>
+__host__ __device__ __forceinline__ int gv_npairs(int N) {
+  return EPI == (int)GvEpi::SWIGLU || EPI == (int)GvEpi::ROPE ? N / 2 : (N + 1) / 2;
+}
+
+// Writes the results (a, c) of rows (r0, r1) of pair p.
+template <typename TW, int EPI>
+__device__ __forceinline__ void gv_store_pair(int p, float a, float c, int N, float* y, const GvRope& rp) {
+  if constexpr (EPI == (int)GvEpi::SWIGLU) {
+    y[p] = silu_f(a) * c;
+  } else if constexpr (EPI == (int)GvEpi::ROPE) {
+    const int half = rp.dh / 2;
+    const int hh = p / half, j = p - hh * half;
+    const int64_t pos = *rp.pos;
+    const long slot = pos & (rp.cap - 1);
+    if (hh < rp.H + rp.Hk) {
+      const float2 cs = rp.tab[pos * half + j];
+      const float ra = a * cs.x - c * cs.y, rb = c * cs.x + a * cs.y;
+      if (hh < rp.H) {
+        rp.q[hh * rp.dh + j] = ra;
+        rp.q[hh * rp.dh + j + half] = rb;
       } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int n = 2 * p + u;
-          if (n >= N) break;
-          if constexpr (EPI == (int)GvEpi::ADD_F32) y[n] += acc[2 * i + u];
-          else y[n] = acc[2 * i + u];
-        }
+        TW* ks = (TW*)rp.ks + ((long)(hh - rp.H) * rp.cap + slot) * rp.dh;
+        ks[j] = from_f<TW>(ra);
+        ks[j + half] = from_f<TW>(rb);
       }
+    } else {
+      const int kh = hh - rp.H - rp.Hk;
+      const TW va = from_f<TW>(a), vc = from_f<TW>(c);
+      TW* vs = (TW*)rp.vs + ((long)kh * rp.cap + slot) * rp.dh;
+      vs[j] = va;
+      vs[j + half] = vc;
+      if (rp.vts) {
+        TW* vt = (TW*)rp.vts + (long)kh * rp.dh * rp.cap + vt_slot(slot);
+        vt[(long)j * rp.cap] = va;
+        vt[(long)(j + half) * rp.cap] = vc;
+      }
+    }
+  } else {
+    const int n = 2 * p;
+    if constexpr (EPI == (int)GvEpi::ADD_F32) {
+      y[n] += a;
+      if (n + 1 < N) y[n + 1] += c;
+    } else {
+      y[n] = a;
+      if (n + 1 < N) y[n + 1] = c;
     }
   }
 }
 
-// y = W x for one row x (fp32 [K]); W [N][K] row-major (nn.Linear layout).
-// NORM: x = RMSNorm(h) * g computed by every workgroup while staging x in
-// LDS. EPI: STORE y[n] = acc; ADD_F32 y[n] += acc; SWIGLU: rows are the
-// 16-interleaved (gate, up) layout and y[j] = silu(gate_j) * up_j.
-// A workgroup takes GV_ROWS rows (GV_ROWS / 2 pairs) and splits K over its
-// waves; lanes stride each row's quarter in 16-byte vectors, so every row
-// is read once, coalesced, with many loads in flight per lane; the partial
-// dot products meet in LDS.
-template <typename TW, int EPI, bool NORM>
-__global__ void __launch_bounds__(GV_THREADS) gemv_kernel(const TW* __restrict__ W, const float* __restrict__ x,
-                                                          const float* __restrict__ g, float eps, int N, int K,
-                                                          float* __restrict__ y) {
-  extern __shared__ float xs[];
-  __shared__ float red[GV_THREADS / 64];
-  __shared__ float part[GV_THREADS / 64][GV_ROWS];
-  constexpr int VE = WVec<TW>::N;
+// 16 bytes of weights -> floats (bf16 widens by a shift).
+__device__ __forceinline__ void gv_unpack(const uint4& u, float (&o)[8]) {
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void gv_unpack(const uint4& u, float (&o)[4]) {
+  o[0] = __uint_as_float(u.x);
+  o[1] = __uint_as_float(u.y);
+  o[2] = __uint_as_float(u.z);
+  o[3] = __uint_as_float(u.w);
+}
+
+// The GEMVs below compute y = W x for one row x (fp32 [K]); W [N][K]
+// row-major (nn.Linear layout), fp32 or bf16. NORM: x is RMS-normalised
+// with gain g first; since RMSNorm(x) g = r (x g) with the scalar
+// r = 1 / rms(x), the products use x g and the sums are scaled by r at the
+// end, r coming from the same pass over x. EPI: STORE y[n] = acc; ADD_F32
+// y[n] += acc; SWIGLU: rows are the 16-interleaved (gate, up) layout and
+// y[j] = silu(gate_j) * up_j; ROPE: the fused q/k/v projection, stored
+// rotated into q and the rings (gv_store_pair). Rows come in pairs, GV_ROWS
+// (two pairs) per wave. Every load a lane needs for a sweep is issued
+// before any is used (out-of-range lanes load a clamped, valid address and
+// drop the value), so a sweep costs one memory latency, not one per vector;
+// lane l reads vectors l, l + 64, ... of its range, so a wave instruction
+// reads 1 KB of a row.
+
+// Few rows: the four waves of a workgroup share its GV_ROWS rows and take
+// a quarter of K each; each lane loads the x (and g) elements that match
+// its weight vectors straight from global memory (no staging, no barrier
+// before the products), and the partial sums (and the sum of squares of x)
+// meet in LDS.
+template <typename TW, int EPI, bool NORM, int NVL>
+__global__ void __launch_bounds__(GV_THREADS) gemv_split_kernel(const TW* __restrict__ W, const float* __restrict__ x,
+                                                                const float* __restrict__ g, float eps, int N, int K,
+                                                                float* __restrict__ y, GvRope rp) {
+  __shared__ float part[GV_THREADS / 64][GV_ROWS + 1];
+  constexpr int VE = 16 / sizeof(TW);
   constexpr int NWV = GV_THREADS / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
+  const int npairs = gv_npairs<EPI>(N);
   const int p0 = blockIdx.x * (GV_ROWS / 2);
-  int rows[GV_ROWS];
+  const int nv = K / VE;
+  const uint4* Wr[GV_ROWS];
 #pragma unroll
   for (int i = 0; i < GV_ROWS / 2; ++i) {
-    const int p = min(p0 + i, npairs - 1);
-    if constexpr (EPI == (int)GvEpi::SWIGLU) {
-      rows[2 * i] = (p >> 4) * 32 + (p & 15);
-      rows[2 * i + 1] = rows[2 * i] + 16;
-    } else {
-      rows[2 * i] = 2 * p;
-      rows[2 * i + 1] = min(2 * p + 1, N - 1);
-    }
+    int r0, r1;
+    gv_pair_rows<EPI>(min(p0 + i, npairs - 1), N, rp.dh / 2, r0, r1);
+    Wr[2 * i] = (const uint4*)W + (long)r0 * nv;
+    Wr[2 * i + 1] = (const uint4*)W + (long)r1 * nv;
   }
-  const int nv = K / VE;
-  const int q = (nv + NWV - 1) / NWV;  // vectors per wave
-  const int v0 = wid * q, v1 = min(nv, v0 + q);
-  // the first sweep's weights are requested before x is staged, so their
-  // latency overlaps the normalisation
-  float w0[GV_ROWS][VE];
-  const bool first = v0 + lane < v1;
-  if (first)
+  const int q = (nv + NWV - 1) / NWV;
+  const int kb = min(nv, wid * q), ke = min(nv, kb + q);
+  floatx4 xr[NVL][VE / 4], gr[NVL][VE / 4];
+  uint4 wr[NVL][GV_ROWS];
 #pragma unroll
-    for (int r = 0; r < GV_ROWS; ++r) WVec<TW>::load(W + (long)rows[r] * K + (v0 + lane) * VE, w0[r]);
-  if constexpr (NORM) {
-    float ss = 0.f;
-    for (int k = threadIdx.x; k < K; k += GV_THREADS) ss += x[k] * x[k];
-    const float r = rsqrtf(block_sum(ss, red) / K + eps);
-    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k] * r * g[k];
-  } else {
-    for (int k = threadIdx.x; k < K; k += GV_THREADS) xs[k] = x[k];
-  }
-  __syncthreads();
-  float acc[GV_ROWS];
+  for (int v = 0; v < NVL; ++v)
+    if (kb + 64 * v < ke) {  // wave-uniform
+      const int vi = min(kb + 64 * v + lane, nv - 1);
+#pragma unroll
+      for (int u = 0; u < VE / 4; ++u) {
+        xr[v][u] = ((const floatx4*)x)[vi * (VE / 4) + u];
+        if constexpr (NORM) gr[v][u] = ((const floatx4*)g)[vi * (VE / 4) + u];
+      }
+    }
+#pragma unroll
+  for (int v = 0; v < NVL; ++v)
+    if (kb + 64 * v < ke) {
+      const int vi = min(kb + 64 * v + lane, nv - 1);
+#pragma unroll
+      for (int r = 0; r < GV_ROWS; ++r) wr[v][r] = Wr[r][vi];
+    }
+  float acc[GV_ROWS], ss = 0.f;
 #pragma unroll
   for (int r = 0; r < GV_ROWS; ++r) acc[r] = 0.f;
-  if (first) {
-    float xv[VE];
 #pragma unroll
-    for (int e = 0; e < VE; ++e) xv[e] = xs[(v0 + lane) * VE + e];
+  for (int v = 0; v < NVL; ++v)
+    if (kb + 64 * v < ke && kb + 64 * v + lane < ke) {
+      float xv[VE];
 #pragma unroll
-    for (int r = 0; r < GV_ROWS; ++r)
+      for (int u = 0; u < VE / 4; ++u)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc[r] += w0[r][e] * xv[e];
-  }
-  for (int v = v0 + lane + 64; v < v1; v += 64) {
-    float xv[VE];
+        for (int e = 0; e < 4; ++e) {
+          const float t = xr[v][u][e];
+          if constexpr (NORM) {
+            ss = fmaf(t, t, ss);
+            xv[4 * u + e] = t * gr[v][u][e];
+          } else {
+            xv[4 * u + e] = t;
+          }
+        }
 #pragma unroll
-    for (int e = 0; e < VE; ++e) xv[e] = xs[v * VE + e];
-    float wv[GV_ROWS][VE];
+      for (int r = 0; r < GV_ROWS; ++r) {
+        float wv[VE];
+        gv_unpack(wr[v][r], wv);
 #pragma unroll
-    for (int r = 0; r < GV_ROWS; ++r) WVec<TW>::load(W + (long)rows[r] * K + v * VE, wv[r]);
-#pragma unroll
-    for (int r = 0; r < GV_ROWS; ++r)
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[r] += wv[r][e] * xv[e];
-  }
+        for (int e = 0; e < VE; ++e) acc[r] = fmaf(wv[e], xv[e], acc[r]);
+      }
+    }
 #pragma unroll
   for (int r = 0; r < GV_ROWS; ++r) acc[r] = wave_sum(acc[r]);
-  if (lane == 0)
+  if constexpr (NORM) ss = wave_sum(ss);
+  if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < GV_ROWS; ++r) part[wid][r] = acc[r];
+    part[wid][GV_ROWS] = ss;
+  }
   __syncthreads();
   if (threadIdx.x < GV_ROWS / 2) {
     const int i = threadIdx.x;
-    const int p = p0 + i;
-    if (p < npairs) {
-      float a = 0.f, c = 0.f;
+    if (p0 + i < npairs) {
+      float a = 0.f, c = 0.f, sq = 0.f;
 #pragma unroll
       for (int w = 0; w < NWV; ++w) {
         a += part[w][2 * i];
         c += part[w][2 * i + 1];
+        sq += part[w][GV_ROWS];
       }
-      if constexpr (EPI == (int)GvEpi::SWIGLU) {
-        y[p] = silu_f(a) * c;
-      } else {
-        const int n = 2 * p;
-        if constexpr (EPI == (int)GvEpi::ADD_F32) {
-          y[n] += a;
-          if (n + 1 < N) y[n + 1] += c;
-        } else {
-          y[n] = a;
-          if (n + 1 < N) y[n + 1] = c;
-        }
+      if constexpr (NORM) {
+        const float rn = rsqrtf(sq / K + eps);
+        a *= rn;
+        c *= rn;
       }
+      gv_store_pair<TW, EPI>(p0 + i, a, c, N, y, rp);
     }
   }
 }
 
+// Many rows: a persistent grid; each workgroup stages x g (float4 loads)
+// in LDS once, and each wave then sweeps its own groups of GV_ROWS rows
+// over all of K, group after group (the first group's weights requested
+// before the staging). K is read in chunks of 64 NVL vectors.
+template <typename TW, int EPI, bool NORM, int NVL>
+__global__ void __launch_bounds__(GV_THREADS) gemv_rows_kernel(const TW* __restrict__ W, const float* __restrict__ x,
+                                                               const float* __restrict__ g, float eps, int N, int K,
+                                                               float* __restrict__ y, GvRope rp) {
+  extern __shared__ float xs[];
+  __shared__ float red[GV_THREADS / 64];
+  constexpr int VE = 16 / sizeof(TW);
+  constexpr int NWV = GV_THREADS / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int npairs = gv_npairs<EPI>(N);
+  const int ngroups = (npairs + GV_ROWS / 2 - 1) / (GV_ROWS / 2);
+  const int nv = K / VE;
+  const int gstride = gridDim.x * NWV;
+  int grp = blockIdx.x * NWV + wid;
+  const uint4* Wr[GV_ROWS];
+  auto set_rows = [&](int gi) {
+#pragma unroll
+    for (int i = 0; i < GV_ROWS / 2; ++i) {
+      int r0, r1;
+      gv_pair_rows<EPI>(max(0, min(gi * (GV_ROWS / 2) + i, npairs - 1)), N, rp.dh / 2, r0, r1);
+      Wr[2 * i] = (const uint4*)W + (long)r0 * nv;
+      Wr[2 * i + 1] = (const uint4*)W + (long)r1 * nv;
+    }
+  };
+  uint4 wr[NVL][GV_ROWS];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int v = 0; v < NVL; ++v)
+      if (c0 + 64 * v < nv) {  // wave-uniform
+        const int vi = min(c0 + 64 * v + lane, nv - 1);
+#pragma unroll
+        for (int r = 0; r < GV_ROWS; ++r) wr[v][r] = Wr[r][vi];
+      }
+  };
+  set_rows(grp);
+  if (grp < ngroups) load(0);
+  // stage x g; sum of squares of x for the norm
+  float ss = 0.f;
+  const int K4 = K / 4;
+  for (int b = 0; b < K4; b += 4 * GV_THREADS) {
+    floatx4 xv[4], gv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = b + u * GV_THREADS + threadIdx.x;
+      if (i < K4) {
+        xv[u] = ((const floatx4*)x)[i];
+        if constexpr (NORM) gv[u] = ((const floatx4*)g)[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = b + u * GV_THREADS + threadIdx.x;
+      if (i < K4) {
+        floatx4 t = xv[u];
+        if constexpr (NORM) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ss = fmaf(t[e], t[e], ss);
+            t[e] *= gv[u][e];
+          }
+        }
+        ((floatx4*)xs)[i] = t;
+      }
+    }
+  }
+  float rn = 1.f;
+  if constexpr (NORM) rn = rsqrtf(block_sum(ss, red) / K + eps);
+  else __syncthreads();
+  for (; grp < ngroups; grp += gstride) {
+    float acc[GV_ROWS];
+#pragma unroll
+    for (int r = 0; r < GV_ROWS; ++r) acc[r] = 0.f;
+    for (int c0 = 0; c0 < nv; c0 += 64 * NVL) {
+      if (c0 != 0) load(c0);
+#pragma unroll
+      for (int v = 0; v < NVL; ++v) {
+        const int vi = c0 + 64 * v + lane;
+        if (c0 + 64 * v < nv && vi < nv) {
+          float xv[VE];
+          const floatx4* xp = (const floatx4*)(xs + vi * VE);
+#pragma unroll
+          for (int u = 0; u < VE / 4; ++u) {
+            const floatx4 t = xp[u];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[4 * u + e] = t[e];
+          }
+#pragma unroll
+          for (int r = 0; r < GV_ROWS; ++r) {
+            float wv[VE];
+            gv_unpack(wr[v][r], wv);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[r] = fmaf(wv[e], xv[e], acc[r]);
+          }
+        }
+      }
+    }
+    const int p0 = grp * (GV_ROWS / 2);
+    // the next group's first chunk is requested before this one's sums
+    // are reduced and stored
+    set_rows(grp + gstride);
+    if (grp + gstride < ngroups) load(0);
+#pragma unroll
+    for (int r = 0; r < GV_ROWS; ++r) acc[r] = wave_sum(acc[r]) * rn;
+    if (lane == 0)
+#pragma unroll
+      for (int i = 0; i < GV_ROWS / 2; ++i)
+        if (p0 + i < npairs) gv_store_pair<TW, EPI>(p0 + i, acc[2 * i], acc[2 * i + 1], N, y, rp);
+  }
+}
+
+template <typename TW, int EPI, bool NORM, int NVL>
+static int gemv_rows_grid(size_t lds) {
+  // workgroups that fit on the device at once (the device the first call
+  // runs on; every device of a process is assumed alike), kept for the
+  // last LDS size asked for
+  static size_t last_lds = 0;
+  static int n = 0;
+  if (lds != last_lds) {
+    int dev = 0, cus = 0, per = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, gemv_rows_kernel<TW, EPI, NORM, NVL>, GV_THREADS, lds);
+    n = std::max(1, cus) * std::max(1, per);
+    last_lds = lds;
+  }
+  return n;
+}
+
+template <typename TW, int EPI, bool NORM, int NVL>
+static void gemv_rows_launch(int groups, size_t lds, hipStream_t st, const TW* W, const float* x, const float* g,
+                             float eps, int N, int K, float* y, const GvRope& rp) {
+  const int need = (groups + GV_THREADS / 64 - 1) / (GV_THREADS / 64);
+  const int blocks = std::min(need, gemv_rows_grid<TW, EPI, NORM, NVL>(lds));
+  hipLaunchKernelGGL((gemv_rows_kernel<TW, EPI, NORM, NVL>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N,
+                     K, y, rp);
+}
+
+template <typename TW, int EPI, bool NORM>
+static void gemv_dispatch(const TW* W, const float* x, const float* g, float eps, int N, int K, float* y,
+                          const GvRope& rp, hipStream_t st) {
+  const int npairs = gv_npairs<EPI>(N);
+  const int nv = K / (16 / (int)sizeof(TW));
+  // many rows: a wave per GV_ROWS rows keeps enough loads in flight; few
+  // rows: split K over the waves of a workgroup to occupy more of the chip
+  const int groups = (npairs + GV_ROWS / 2 - 1) / (GV_ROWS / 2);
+  if (groups >= 2048) {
+    const size_t lds = (size_t)K * sizeof(float);
+    const int nvl = (nv + 63) / 64;
+    if (nvl <= 4) gemv_rows_launch<TW, EPI, NORM, 4>(groups, lds, st, W, x, g, eps, N, K, y, rp);
+    else if (nvl <= 6) gemv_rows_launch<TW, EPI, NORM, 6>(groups, lds, st, W, x, g, eps, N, K, y, rp);
+    else gemv_rows_launch<TW, EPI, NORM, 8>(groups, lds, st, W, x, g, eps, N, K, y, rp);
+    return;
+  }
+  const int nvl = ((nv + 3) / 4 + 63) / 64;
+  if (nvl <= 2)
+    hipLaunchKernelGGL((gemv_split_kernel<TW, EPI, NORM, 2>), dim3(groups), dim3(GV_THREADS), 0, st, W, x, g, eps, N, K, y, rp);
+  else if (nvl <= 4)
+    hipLaunchKernelGGL((gemv_split_kernel<TW, EPI, NORM, 4>), dim3(groups), dim3(GV_THREADS), 0, st, W, x, g, eps, N, K, y, rp);
+  else
+    hipLaunchKernelGGL((gemv_split_kernel<TW, EPI, NORM, 8>), dim3(groups), dim3(GV_THREADS), 0, st, W, x, g, eps, N, K, y, rp);
+}
+
 template <typename TW, int EPI>
 static hipError_t gemv_t(const TW* W, const float* x, const float* g, float eps, int N, int K, float* y,
-                         hipStream_t st) {
-  const int npairs = EPI == (int)GvEpi::SWIGLU ? N / 2 : (N + 1) / 2;
-  const size_t lds = (size_t)K * sizeof(float);
-  // many rows: a wave per GV_RPW rows keeps enough loads in flight; few
-  // rows: split K over the waves of a workgroup to occupy more of the chip
-  const int waves_rows = (npairs + GV_RPW / 2 - 1) / (GV_RPW / 2);
-  if (waves_rows >= 2048) {
-    const int blocks = (waves_rows + GV_THREADS / 64 - 1) / (GV_THREADS / 64);
-    if (g) hipLaunchKernelGGL((gemv_rows_kernel<TW, EPI, true>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
-    else hipLaunchKernelGGL((gemv_rows_kernel<TW, EPI, false>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
-    return hipGetLastError();
-  }
-  const int blocks = (npairs + GV_ROWS / 2 - 1) / (GV_ROWS / 2);
-  if (g) hipLaunchKernelGGL((gemv_kernel<TW, EPI, true>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
-  else hipLaunchKernelGGL((gemv_kernel<TW, EPI, false>), dim3(blocks), dim3(GV_THREADS), lds, st, W, x, g, eps, N, K, y);
+                         const GvRope& rp, hipStream_t st) {
+  if (g) gemv_dispatch<TW, EPI, true>(W, x, g, eps, N, K, y, rp, st);
+  else gemv_dispatch<TW, EPI, false>(W, x, g, eps, N, K, y, rp, st);
   return hipGetLastError();
 }
 
@@ -274,20 +421,34 @@ hipError_t gemv(DT wdt, const void* W, const float* x, const float* g, float eps
                 float* y, hipStream_t st) {
   if (N <= 0) return hipSuccess;
   if ((K * 4) > 64 * 1024 || K % 8) return hipErrorInvalidValue;
+  const GvRope rp{};
   if (wdt == DT::BF16) {
     switch (epi) {
-      case GvEpi::STORE: return gemv_t<bf16, (int)GvEpi::STORE>((const bf16*)W, x, g, eps, N, K, y, st);
-      case GvEpi::ADD_F32: return gemv_t<bf16, (int)GvEpi::ADD_F32>((const bf16*)W, x, g, eps, N, K, y, st);
-      case GvEpi::SWIGLU: return gemv_t<bf16, (int)GvEpi::SWIGLU>((const bf16*)W, x, g, eps, N, K, y, st);
+      case GvEpi::STORE: return gemv_t<bf16, (int)GvEpi::STORE>((const bf16*)W, x, g, eps, N, K, y, rp, st);
+      case GvEpi::ADD_F32: return gemv_t<bf16, (int)GvEpi::ADD_F32>((const bf16*)W, x, g, eps, N, K, y, rp, st);
+      case GvEpi::SWIGLU: return gemv_t<bf16, (int)GvEpi::SWIGLU>((const bf16*)W, x, g, eps, N, K, y, rp, st);
+      default: break;
     }
   } else {
     switch (epi) {
-      case GvEpi::STORE: return gemv_t<float, (int)GvEpi::STORE>((const float*)W, x, g, eps, N, K, y, st);
-      case GvEpi::ADD_F32: return gemv_t<float, (int)GvEpi::ADD_F32>((const float*)W, x, g, eps, N, K, y, st);
-      case GvEpi::SWIGLU: return gemv_t<float, (int)GvEpi::SWIGLU>((const float*)W, x, g, eps, N, K, y, st);
+      case GvEpi::STORE: return gemv_t<float, (int)GvEpi::STORE>((const float*)W, x, g, eps, N, K, y, rp, st);
+      case GvEpi::ADD_F32: return gemv_t<float, (int)GvEpi::ADD_F32>((const float*)W, x, g, eps, N, K, y, rp, st);
+      case GvEpi::SWIGLU: return gemv_t<float, (int)GvEpi::SWIGLU>((const float*)W, x, g, eps, N, K, y, rp, st);
+      default: break;
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t gemv_qkv_rope(DT dt, const void* W, const float* x, const float* g, float eps, int H, int Hk, int dh,
+                         int K, const int64_t* pos, const float2* rope_tab, float* q, void* kstore, void* vstore,
+                         void* vtstore, int cap, hipStream_t st) {
+  if ((K * 4) > 64 * 1024 || K % 8 || dh % 2) return hipErrorInvalidValue;
+  const int N = (H + 2 * Hk) * dh;
+  const GvRope rp{pos, rope_tab, q, kstore, vstore, vtstore, H, Hk, dh, cap};
+  if (dt == DT::BF16)
+    return gemv_t<bf16, (int)GvEpi::ROPE>((const bf16*)W, x, g, eps, N, K, nullptr, rp, st);
+  return gemv_t<float, (int)GvEpi::ROPE>((const float*)W, x, g, eps, N, K, nullptr, rp, st);
 }
 
 // ------------------------------------------------------------- embedding
@@ -307,56 +468,6 @@ hipError_t embed_row(DT dt, const int32_t* tok, const void* embed, int d, int V,
     hipLaunchKernelGGL(embed_row_kernel<bf16>, dim3(1), dim3(256), 0, st, tok, (const bf16*)embed, d, V, h, err);
   else
     hipLaunchKernelGGL(embed_row_kernel<float>, dim3(1), dim3(256), 0, st, tok, (const float*)embed, d, V, h, err);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------ RoPE + ring store
-// Rotates q and k of position p (half-split pairs (j, j + dh/2) by the
-// angle table) and stores k, v (and v transposed when vts is given) at ring
-// slot p & (cap - 1).
-template <typename T>
-__global__ void decode_rope_store_kernel(const float* qkv, int H, int Hk, int dh, const int64_t* pos,
-                                         const float2* tab, float* q, T* ks, T* vs, T* vts, int cap) {
-  // workgroup hh < H: query head; H <= hh < H + Hk: key head; then value heads
-  const int64_t p = *pos;
-  const int half = dh / 2;
-  const long slot = p & (cap - 1);
-  const int hh = blockIdx.x;
-  if (hh < H + Hk) {
-    const float2* tb = tab + p * half;
-    for (int j = threadIdx.x; j < half; j += blockDim.x) {
-      const float2 cs = tb[j];
-      const float a = qkv[hh * dh + j], b = qkv[hh * dh + j + half];
-      const float ra = a * cs.x - b * cs.y, rb = b * cs.x + a * cs.y;
-      if (hh < H) {
-        q[hh * dh + j] = ra;
-        q[hh * dh + j + half] = rb;
-      } else {
-        const int kh = hh - H;
-        ks[((long)kh * cap + slot) * dh + j] = from_f<T>(ra);
-        ks[((long)kh * cap + slot) * dh + j + half] = from_f<T>(rb);
-      }
-    }
-  } else {
-    const int kh = hh - H - Hk;
-    for (int j = threadIdx.x; j < dh; j += blockDim.x) {
-      const T v = from_f<T>(qkv[(H + Hk) * dh + kh * dh + j]);
-      vs[((long)kh * cap + slot) * dh + j] = v;
-      if (vts) vts[((long)kh * dh + j) * cap + vt_slot(slot)] = v;
-    }
-  }
-}
-
-hipError_t decode_rope_store(DT dt, const float* qkv, int H, int Hk, int dh, const int64_t* pos,
-                             const float2* rope_tab, float* q, void* kstore, void* vstore, void* vtstore, int cap,
-                             hipStream_t st) {
-  const dim3 grid(H + 2 * Hk);
-  if (dt == DT::BF16)
-    hipLaunchKernelGGL(decode_rope_store_kernel<bf16>, grid, dim3(64), 0, st, qkv, H, Hk, dh, pos, rope_tab, q,
-                       (bf16*)kstore, (bf16*)vstore, (bf16*)vtstore, cap);
-  else
-    hipLaunchKernelGGL(decode_rope_store_kernel<float>, grid, dim3(64), 0, st, qkv, H, Hk, dh, pos, rope_tab, q,
-                       (float*)kstore, (float*)vstore, (float*)vtstore, cap);
   return hipGetLastError();
 }
 

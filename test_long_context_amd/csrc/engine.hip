@@ -543,9 +543,8 @@ ttt_status decode_blocks(ttt_ctx* c, hipStream_t st) {
   float* part = hm + std::max(c->F, c->Fd);
   HIPCHK(c, embed_row(c->dt, c->d_tok, c->embed, d, c->V, h, c->d_err, st));
   for (int l = 0; l < c->L; ++l) {
-    HIPCHK(c, gemv(c->dt, c->wqkv[l], h, c->attn_norm[l], eps, c->QKV, d, GvEpi::STORE, qkv, st));
-    HIPCHK(c, decode_rope_store(c->dt, qkv, H, Hk, dh, c->d_pos, c->rope, q, c->kring[l], c->vring[l],
-                                c->vtring[l], (int)c->cap, st));
+    HIPCHK(c, gemv_qkv_rope(c->dt, c->wqkv[l], h, c->attn_norm[l], eps, H, Hk, dh, d, c->d_pos, c->rope, q,
+                            c->kring[l], c->vring[l], c->vtring[l], (int)c->cap, st));
     HIPCHK(c, decode_attn(c->dt, q, c->kring[l], c->vring[l], c->vtring[l], H, Hk, dh, (int)c->cap, c->k, c->d_pos,
                           part, o, st));
     HIPCHK(c, gemv(c->dt, c->wo[l], o, nullptr, 0.f, d, H * dh, GvEpi::ADD_F32, h, st));

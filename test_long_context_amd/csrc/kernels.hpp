@@ -155,14 +155,18 @@ hipError_t sum_parts_f32(const float* parts, int nparts, long count, float* dst,
 // y = W x for one fp32 row x (W [N][K] of storage type wdt); with g given,
 // x is first RMS-normalised with gain g. Epilogues: STORE, ADD_F32 (y +=),
 // SWIGLU (W rows 16-interleaved (gate, up); y [N/2] = silu(gate) * up).
-enum class GvEpi : int { STORE = 0, ADD_F32, SWIGLU };
+// ROPE is the epilogue of gemv_qkv_rope only.
+enum class GvEpi : int { STORE = 0, ADD_F32, SWIGLU, ROPE };
 hipError_t gemv(DT wdt, const void* W, const float* x, const float* g, float eps, int N, int K, GvEpi epi,
                 float* y, hipStream_t st);
-// RoPE of q, k at position *pos; k, v (and v transposed) into ring slot
-// *pos & (cap - 1).
-hipError_t decode_rope_store(DT dt, const float* qkv, int H, int Hk, int dh, const int64_t* pos,
-                             const float2* rope_tab, float* q, void* kstore, void* vstore, void* vtstore, int cap,
-                             hipStream_t st);
+// The fused q/k/v projection of one token (W [(H + 2 Hk) dh][K] of type dt,
+// x RMS-normalised with gain g) whose epilogue applies RoPE and stores: each
+// pair of rows (j, j + dh / 2) of a head is rotated at position *pos (q and
+// k heads) and written to q (fp32), the key ring, or the value ring and its
+// transpose (slot *pos & (cap - 1)).
+hipError_t gemv_qkv_rope(DT dt, const void* W, const float* x, const float* g, float eps, int H, int Hk, int dh,
+                         int K, const int64_t* pos, const float2* rope_tab, float* q, void* kstore, void* vstore,
+                         void* vtstore, int cap, hipStream_t st);
 // One query per head at position *pos over the window; part: [H][nsplit][dh + 2]
 // with nsplit = decode_attn_splits(...) (vtstore, the transposed value store,
 // may be null: then the lane-parallel kernel runs).
