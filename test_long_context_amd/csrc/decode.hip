@@ -603,9 +603,12 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(const float* q, const 
 }
 
 // o[h] = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}: the split weights
-// are formed once per head in LDS, then each thread sums one output column.
-__global__ void __launch_bounds__(128) decode_attn_combine_kernel(const float* part, int nsplit, int dh, float* o) {
+// are formed once per head in LDS; then thread t sums the splits
+// s = t / dh (mod 256 / dh) of column t % dh, eight loads in flight, and
+// the column's partial sums meet in LDS.
+__global__ void __launch_bounds__(256) decode_attn_combine_kernel(const float* part, int nsplit, int dh, float* o) {
   __shared__ float wsh[256];
+  __shared__ float csum[256];
   __shared__ float Lsh;
   const int h = blockIdx.x;
   const float* ph = part + (long)h * nsplit * (dh + 2);
@@ -625,11 +628,19 @@ __global__ void __launch_bounds__(128) decode_attn_combine_kernel(const float* p
     if (lane == 0) Lsh = L;
   }
   __syncthreads();
-  const float inv = 1.f / Lsh;
-  for (int dd = threadIdx.x; dd < dh; dd += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) acc += ph[s * (dh + 2) + dd] * wsh[s];
-    o[h * dh + dd] = acc * inv;
+  const int nsub = blockDim.x / dh;
+  const int dd = threadIdx.x % dh, sub = threadIdx.x / dh;
+  float acc = 0.f;
+  if (sub < nsub) {
+#pragma unroll 8
+    for (int s = sub; s < nsplit; s += nsub) acc += ph[s * (dh + 2) + dd] * wsh[s];
+  }
+  csum[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x < dh) {
+    float t = 0.f;
+    for (int u = 0; u < nsub; ++u) t += csum[u * dh + threadIdx.x];
+    o[h * dh + threadIdx.x] = t / Lsh;
   }
 }
 
@@ -780,7 +791,7 @@ static hipError_t decode_attn_t(const float* q, const void* ks, const void* vs, 
     case 8: hipLaunchKernelGGL((decode_attn_kernel<T, DH, 8>), grid, dim3(256), 0, st, q, (const T*)ks, (const T*)vs, H, Hk, cap, window, pos, sc, nsplit, part); break;
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(decode_attn_combine_kernel, dim3(H), dim3(128), 0, st, part, nsplit, DH, o);
+  hipLaunchKernelGGL(decode_attn_combine_kernel, dim3(H), dim3(256), 0, st, part, nsplit, DH, o);
   return hipGetLastError();
 }
 
@@ -809,7 +820,7 @@ hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vs
     else
       hipLaunchKernelGGL(decode_attn_mfma_kernel<64>, grid, dim3(256), 0, st, q, (const bf16*)kstore,
                          (const bf16*)vtstore, H, Hk, cap, window, pos, sc2, nsplit, part);
-    hipLaunchKernelGGL(decode_attn_combine_kernel, dim3(H), dim3(128), 0, st, part, nsplit, dh, o);
+    hipLaunchKernelGGL(decode_attn_combine_kernel, dim3(H), dim3(256), 0, st, part, nsplit, dh, o);
     return hipGetLastError();
   }
   if (dt == DT::BF16) {
