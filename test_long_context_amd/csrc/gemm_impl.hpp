@@ -411,8 +411,11 @@ __device__ __forceinline__ floatx4 upc4(bf16x4 v) {
   return r;
 }
 
+// pre: for ADD_F32 / SGD, the chunk's fp32 C values loaded ahead (used
+// when the chunk is a whole vector)
 template <int EPI>
-__device__ __forceinline__ void epi_chunk(const GemmArgs& g, int m, int n, floatx4 v, bool vec) {
+__device__ __forceinline__ void epi_chunk(const GemmArgs& g, int m, int n, floatx4 v, bool vec,
+                                          floatx4 pre = floatx4{0.f, 0.f, 0.f, 0.f}) {
   const long idx = (long)m * g.ldc + n;
   const int ne = min(4, g.N - n);
   vec = vec && ne == 4;
@@ -427,7 +430,7 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& g, int m, int n, float
     else for (int e = 0; e < ne; ++e) C[e] = v[e];
   } else if constexpr (EPI == (int)Epi::ADD_F32) {
     float* C = (float*)g.C + idx;
-    if (vec) *(floatx4*)C = *(const floatx4*)C + v;
+    if (vec) *(floatx4*)C = pre + v;
     else for (int e = 0; e < ne; ++e) C[e] += v[e];
   } else if constexpr (EPI == (int)Epi::SGD) {
     float* W = (float*)g.C + idx;
@@ -435,7 +438,7 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& g, int m, int n, float
     bf16* H = (bf16*)g.C2 + idx;
     bf16* L = g.C3 ? (bf16*)g.C3 + idx : nullptr;
     if (vec) {
-      const floatx4 w = *(const floatx4*)W - g.scale * v;
+      const floatx4 w = pre - g.scale * v;
       *(floatx4*)W = w;
       if (two) {
         const bf16x4 hi = cvt4(w);
@@ -530,6 +533,26 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, floatx4 
   if constexpr (EPI == (int)Epi::SGD) vec = vec && al(g.C2, 8) && al(g.C3, 8);
   if constexpr (EPI == (int)Epi::SWIGLU) vec = vec && al(g.C2, 8) && (g.N / 2) % 4 == 0;
   if constexpr (EPI == (int)Epi::SWIGLU_BWD) vec = vec && al(g.X, 8);
+  constexpr bool RMW = EPI == (int)Epi::ADD_F32 || EPI == (int)Epi::SGD;
+  constexpr int CPR = WN / 4;              // 4-column chunks per strip row
+  constexpr int NCH = RMW ? 16 * CPR / 64 : 1;  // chunks per lane per row block
+  static_assert(!RMW || (16 * CPR) % 64 == 0, "whole chunk rounds per lane");
+  if constexpr (RMW) vec = vec && g.N >= 4;
+  // C values of row block i, loaded unconditionally from a clamped (valid)
+  // address so no lane branches around a load; out-of-range chunks drop them
+  floatx4 cur[NCH], nxt[NCH];
+  auto rmw_load = [&](int i, floatx4 (&dst)[NCH]) {
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c = lane + 64 * k;
+      const int row = c / CPR, col = (c % CPR) * 4;
+      const int m = min(mw + 16 * i + row, g.M - 1), n = min(nw + col, g.N - 4);
+      dst[k] = *(const floatx4*)((const float*)g.C + (long)m * g.ldc + n);
+    }
+  };
+  if constexpr (RMW) {
+    if (vec) rmw_load(0, cur);  // wave-uniform
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -551,8 +574,22 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, floatx4 
         const int m = mw + 16 * i + row, n = nw + col;
         if (m < g.M && n < g.N) epi_swiglu_chunk(g, m, n, a, cc, vec);
       }
+    } else if constexpr (RMW) {
+      // the next row block's C values are requested before this block's
+      // stores, so no chunk waits on a store's completion (the counter
+      // that tracks loads also tracks stores)
+      if (vec && i + 1 < FM) rmw_load(i + 1, nxt);
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const int c = lane + 64 * k;
+        const int row = c / CPR, col = (c % CPR) * 4;
+        const floatx4 v = *(const floatx4*)(strip + row * SP + col);
+        const int m = mw + 16 * i + row, n = nw + col;
+        if (m < g.M && n < g.N) epi_chunk<EPI>(g, m, n, v, vec, cur[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) cur[k] = nxt[k];
     } else {
-      constexpr int CPR = WN / 4;
 #pragma unroll
       for (int c = lane; c < 16 * CPR; c += 64) {
         const int row = c / CPR, col = (c % CPR) * 4;
