@@ -69,7 +69,7 @@ typedef enum { TTT_LOSS_MEAN = 0, TTT_LOSS_SUM = 1 } ttt_reduction;
 /* Model and inner-loop hyper-parameters. */
 typedef struct {
   int32_t n_layers;       /* L >= 1 */
-  int32_t d_model;        /* d, multiple of 16 */
+  int32_t d_model;        /* d, multiple of 16, at most 8192 */
   int32_t n_heads;        /* query heads H */
   int32_t n_kv_heads;     /* Hk, divides H */
   int32_t head_dim;       /* 16, 64 or 128 */

@@ -47,9 +47,7 @@ hipError_t embed_gather(DT dt, const int32_t* tok, int n, const void* E, int d, 
 }
 
 // ----------------------------------------------------------------- RMSNorm
-// One workgroup per row; each thread keeps its float4 chunks of the row in
-// registers between the reduction and the output pass (d <= RMS_MAXV * 4 * RB;
-// larger rows take the strided loops).
+// Rows of up to RMS_MAXV float4 chunks per thread (d <= 4 RB RMS_MAXV).
 static constexpr int RMS_MAXV = 8;
 
 template <typename T>
@@ -69,74 +67,117 @@ __device__ __forceinline__ void store4<float>(float* p, float4 v) {
 }
 __device__ __forceinline__ float4 f4add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
 
+// Row-sum of a float4 chunk set: a[i] += sum_p src[p * stride][chunk i]
+// for p < np, the loads of four partials issued together before any add
+// (one memory round trip per four partials, not one per load).
+template <int NVT>
+__device__ __forceinline__ void rms_add_parts(float4 (&a)[NVT], const float* src, long stride, int np, long row,
+                                              int nv) {
+  int p = 0;
+  for (; p + 4 <= np; p += 4) {
+    float4 t[4][NVT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NVT; ++i) {
+        const int v = threadIdx.x + i * RB;
+        if (v < nv) t[u][i] = ((const float4*)(src + (p + u) * stride + row))[v];
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NVT; ++i)
+        if (threadIdx.x + i * RB < nv) a[i] = f4add(a[i], t[u][i]);
+  }
+  for (; p < np; ++p) {
+    float4 t[NVT];
+#pragma unroll
+    for (int i = 0; i < NVT; ++i) {
+      const int v = threadIdx.x + i * RB;
+      if (v < nv) t[i] = ((const float4*)(src + p * stride + row))[v];
+    }
+#pragma unroll
+    for (int i = 0; i < NVT; ++i)
+      if (threadIdx.x + i * RB < nv) a[i] = f4add(a[i], t[i]);
+  }
+}
+
 // x = x_in + sum_p parts[p] (pending split-K residual updates); x_out and
 // save (either may be null) receive x; y = g * x * r with r = rsqrt(mean x^2 + eps).
-template <typename T>
+// One workgroup per row; thread t holds float4 chunks t, t + RB, ... (NVT of
+// them, d <= 4 RB NVT) in registers between the reduction and the output
+// pass; the gain is requested with the row.
+template <typename T, int NVT>
 __global__ void __launch_bounds__(RB) rms_fwd_kernel(const float* x_in, const float* parts, int nsplit, long pstride,
                                                      float* x_out, float* save, const float* g, int d, float eps,
                                                      T* y, float* r) {
   __shared__ float sh[RB / 64];
   const long t = blockIdx.x;
   const int nv = d / 4;
-  float4 xv[RMS_MAXV];
-  float ss = 0.f;
-  const bool fits = nv <= RMS_MAXV * RB;
-  if (fits) {
+  float4 xv[NVT], gv[NVT];
 #pragma unroll
-    for (int i = 0; i < RMS_MAXV; ++i) {
-      const int v = threadIdx.x + i * RB;
-      if (v < nv) {
-        float4 a = ((const float4*)(x_in + t * d))[v];
-        for (int p = 0; p < nsplit; ++p) a = f4add(a, ((const float4*)(parts + p * pstride + t * d))[v]);
-        xv[i] = a;
-        ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
-      }
-    }
-  } else {
-    for (int j = threadIdx.x; j < d; j += RB) {
-      float a = x_in[t * d + j];
-      for (int p = 0; p < nsplit; ++p) a += parts[p * pstride + t * d + j];
-      ss += a * a;
+  for (int i = 0; i < NVT; ++i) {
+    const int v = threadIdx.x + i * RB;
+    if (v < nv) {
+      xv[i] = ((const float4*)(x_in + t * d))[v];
+      gv[i] = ((const float4*)g)[v];
     }
   }
+  rms_add_parts<NVT>(xv, parts, pstride, nsplit, t * d, nv);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NVT; ++i)
+    if (threadIdx.x + i * RB < nv) {
+      const float4 a = xv[i];
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
   ss = block_sum(ss, sh);
   const float rr = rsqrtf(ss / d + eps);
-  if (fits) {
 #pragma unroll
-    for (int i = 0; i < RMS_MAXV; ++i) {
-      const int v = threadIdx.x + i * RB;
-      if (v < nv) {
-        const float4 a = xv[i];
-        if (x_out) ((float4*)(x_out + t * d))[v] = a;
-        if (save) ((float4*)(save + t * d))[v] = a;
-        const float4 gg = ((const float4*)g)[v];
-        store4<T>(y + t * d + 4 * v, make_float4(gg.x * a.x * rr, gg.y * a.y * rr, gg.z * a.z * rr, gg.w * a.w * rr));
-      }
-    }
-  } else {
-    for (int j = threadIdx.x; j < d; j += RB) {
-      float a = x_in[t * d + j];
-      for (int p = 0; p < nsplit; ++p) a += parts[p * pstride + t * d + j];
-      if (x_out) x_out[t * d + j] = a;
-      if (save) save[t * d + j] = a;
-      y[t * d + j] = from_f<T>(g[j] * a * rr);
+  for (int i = 0; i < NVT; ++i) {
+    const int v = threadIdx.x + i * RB;
+    if (v < nv) {
+      const float4 a = xv[i], gg = gv[i];
+      if (x_out) ((float4*)(x_out + t * d))[v] = a;
+      if (save) ((float4*)(save + t * d))[v] = a;
+      store4<T>(y + t * d + 4 * v, make_float4(gg.x * a.x * rr, gg.y * a.y * rr, gg.z * a.z * rr, gg.w * a.w * rr));
     }
   }
   if (threadIdx.x == 0) r[t] = rr;
 }
 
+template <typename T, int NVT>
+static void rms_fwd_launch(const float* x_in, const float* parts, int nsplit, long ps, float* x_out, float* save,
+                           const float* g, int n, int d, float eps, T* y, float* r, hipStream_t st) {
+  hipLaunchKernelGGL((rms_fwd_kernel<T, NVT>), dim3(n), dim3(RB), 0, st, x_in, parts, nsplit, ps, x_out, save, g, d,
+                     eps, y, r);
+}
+
+template <typename T>
+static hipError_t rms_fwd_t(const float* x_in, const float* parts, int nsplit, long ps, float* x_out, float* save,
+                            const float* g, int n, int d, float eps, T* y, float* r, hipStream_t st) {
+  const int nvt = (d / 4 + RB - 1) / RB;
+  switch (nvt) {
+    case 1: rms_fwd_launch<T, 1>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, y, r, st); break;
+    case 2: rms_fwd_launch<T, 2>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, y, r, st); break;
+    case 3: rms_fwd_launch<T, 3>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, y, r, st); break;
+    case 4: rms_fwd_launch<T, 4>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, y, r, st); break;
+    case 5:
+    case 6: rms_fwd_launch<T, 6>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, y, r, st); break;
+    case 7:
+    case 8: rms_fwd_launch<T, 8>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, y, r, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t rmsnorm_fwd_fused(DT dt, const float* x_in, const float* parts, int nsplit, float* x_out, float* save,
                              const float* g, int n, int d, float eps, void* y, float* r, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  if (d % 4) return hipErrorInvalidValue;
+  if (d % 4 || d > 4 * RB * RMS_MAXV) return hipErrorInvalidValue;
   const long ps = (long)n * d;
-  if (dt == DT::BF16)
-    hipLaunchKernelGGL(rms_fwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, x_in, parts, nsplit, ps, x_out, save, g, d,
-                       eps, (bf16*)y, r);
-  else
-    hipLaunchKernelGGL(rms_fwd_kernel<float>, dim3(n), dim3(RB), 0, st, x_in, parts, nsplit, ps, x_out, save, g, d,
-                       eps, (float*)y, r);
-  return hipGetLastError();
+  if (dt == DT::BF16) return rms_fwd_t<bf16>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, (bf16*)y, r, st);
+  return rms_fwd_t<float>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, (float*)y, r, st);
 }
 
 hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, float eps, void* y,
@@ -145,8 +186,10 @@ hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, floa
 }
 
 // dx = r (g dy) - x r^3 mean((g dy) x); dh (+)= dx; dh_t = T(dh); dy is the
-// sum of nsplit partials (read once, kept in registers).
-template <typename T>
+// sum of nsplit partials. Every input of the row (the partials, g, x and,
+// when accumulating, dh) is requested before the first use and kept in
+// registers (NVT float4 chunks per thread, as in the forward).
+template <typename T, int NVT>
 __global__ void __launch_bounds__(RB) rms_bwd_kernel(const float* dy, int nsplit, long sstride, const float* x,
                                                      const float* g, const float* r, int d, float* dh, T* dh_t,
                                                      int acc) {
@@ -154,70 +197,72 @@ __global__ void __launch_bounds__(RB) rms_bwd_kernel(const float* dy, int nsplit
   const long t = blockIdx.x;
   const float rr = r[t];
   const int nv = d / 4;
-  const bool fits = nv <= RMS_MAXV * RB;
-  float4 gv[RMS_MAXV];
-  float dot = 0.f;
-  if (fits) {
+  float4 a[NVT], gv[NVT], xv[NVT], hv[NVT];
 #pragma unroll
-    for (int i = 0; i < RMS_MAXV; ++i) {
-      const int v = threadIdx.x + i * RB;
-      if (v < nv) {
-        float4 a = ((const float4*)(dy + t * d))[v];
-        for (int s = 1; s < nsplit; ++s) a = f4add(a, ((const float4*)(dy + s * sstride + t * d))[v]);
-        const float4 gg = ((const float4*)g)[v];
-        a = make_float4(a.x * gg.x, a.y * gg.y, a.z * gg.z, a.w * gg.w);  // g dy
-        gv[i] = a;
-        const float4 xx = ((const float4*)(x + t * d))[v];
-        dot += a.x * xx.x + a.y * xx.y + a.z * xx.z + a.w * xx.w;
-      }
-    }
-  } else {
-    for (int j = threadIdx.x; j < d; j += RB) {
-      float v = 0.f;
-      for (int s = 0; s < nsplit; ++s) v += dy[s * sstride + t * d + j];
-      dot += g[j] * v * x[t * d + j];
+  for (int i = 0; i < NVT; ++i) {
+    const int v = threadIdx.x + i * RB;
+    if (v < nv) {
+      a[i] = ((const float4*)(dy + t * d))[v];
+      gv[i] = ((const float4*)g)[v];
+      xv[i] = ((const float4*)(x + t * d))[v];
+      if (acc) hv[i] = ((const float4*)(dh + t * d))[v];
     }
   }
+  rms_add_parts<NVT>(a, dy + sstride, sstride, nsplit - 1, t * d, nv);
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < NVT; ++i)
+    if (threadIdx.x + i * RB < nv) {
+      const float4 gg = gv[i], xx = xv[i];
+      a[i] = make_float4(a[i].x * gg.x, a[i].y * gg.y, a[i].z * gg.z, a[i].w * gg.w);  // g dy
+      dot += a[i].x * xx.x + a[i].y * xx.y + a[i].z * xx.z + a[i].w * xx.w;
+    }
   dot = block_sum(dot, sh) / d;
   const float c = rr * rr * rr * dot;
-  if (fits) {
 #pragma unroll
-    for (int i = 0; i < RMS_MAXV; ++i) {
-      const int v = threadIdx.x + i * RB;
-      if (v < nv) {
-        const float4 a = gv[i];
-        const float4 xx = ((const float4*)(x + t * d))[v];
-        float4 o = make_float4(rr * a.x - xx.x * c, rr * a.y - xx.y * c, rr * a.z - xx.z * c, rr * a.w - xx.w * c);
-        if (acc) o = f4add(o, ((const float4*)(dh + t * d))[v]);
-        ((float4*)(dh + t * d))[v] = o;
-        if (dh_t) store4<T>(dh_t + t * d + 4 * v, o);
-      }
-    }
-  } else {
-    for (int j = threadIdx.x; j < d; j += RB) {
-      float v = 0.f;
-      for (int s = 0; s < nsplit; ++s) v += dy[s * sstride + t * d + j];
-      float o = rr * g[j] * v - x[t * d + j] * c;
-      if (acc) o += dh[t * d + j];
-      dh[t * d + j] = o;
-      if (dh_t) dh_t[t * d + j] = from_f<T>(o);
+  for (int i = 0; i < NVT; ++i) {
+    const int v = threadIdx.x + i * RB;
+    if (v < nv) {
+      const float4 q = a[i], xx = xv[i];
+      float4 o = make_float4(rr * q.x - xx.x * c, rr * q.y - xx.y * c, rr * q.z - xx.z * c, rr * q.w - xx.w * c);
+      if (acc) o = f4add(o, hv[i]);
+      ((float4*)(dh + t * d))[v] = o;
+      if (dh_t) store4<T>(dh_t + t * d + 4 * v, o);
     }
   }
 }
 
-hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const float* g,
-                       const float* r, int n, int d, float* dh, void* dh_t, int accumulate,
-                       hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  if (d % 4 || nsplit < 1) return hipErrorInvalidValue;
-  const long ss = (long)n * d;
-  if (dt == DT::BF16)
-    hipLaunchKernelGGL(rms_bwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, dy, nsplit, ss, x, g, r, d, dh,
-                       (bf16*)dh_t, accumulate);
-  else
-    hipLaunchKernelGGL(rms_bwd_kernel<float>, dim3(n), dim3(RB), 0, st, dy, nsplit, ss, x, g, r, d, dh,
-                       (float*)dh_t, accumulate);
+template <typename T, int NVT>
+static void rms_bwd_launch(const float* dy, int nsplit, long ss, const float* x, const float* g, const float* r,
+                           int n, int d, float* dh, T* dh_t, int acc, hipStream_t st) {
+  hipLaunchKernelGGL((rms_bwd_kernel<T, NVT>), dim3(n), dim3(RB), 0, st, dy, nsplit, ss, x, g, r, d, dh, dh_t, acc);
+}
+
+template <typename T>
+static hipError_t rms_bwd_t(const float* dy, int nsplit, long ss, const float* x, const float* g, const float* r,
+                            int n, int d, float* dh, T* dh_t, int acc, hipStream_t st) {
+  const int nvt = (d / 4 + RB - 1) / RB;
+  switch (nvt) {
+    case 1: rms_bwd_launch<T, 1>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 2: rms_bwd_launch<T, 2>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 3: rms_bwd_launch<T, 3>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 4: rms_bwd_launch<T, 4>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 5:
+    case 6: rms_bwd_launch<T, 6>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 7:
+    case 8: rms_bwd_launch<T, 8>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const float* g, const float* r, int n,
+                       int d, float* dh, void* dh_t, int accumulate, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (d % 4 || nsplit < 1 || d > 4 * RB * RMS_MAXV) return hipErrorInvalidValue;
+  const long ss = (long)n * d;
+  if (dt == DT::BF16) return rms_bwd_t<bf16>(dy, nsplit, ss, x, g, r, n, d, dh, (bf16*)dh_t, accumulate, st);
+  return rms_bwd_t<float>(dy, nsplit, ss, x, g, r, n, d, dh, (float*)dh_t, accumulate, st);
 }
 
 // -------------------------------------------------------------------- RoPE

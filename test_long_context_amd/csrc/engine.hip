@@ -227,6 +227,7 @@ ttt_status validate(const ttt_config* cfg) {
   if (!(c.head_dim == 16 || c.head_dim == 64 || c.head_dim == 128)) return TTT_ERR_UNSUPPORTED;
   if (c.d_model % 16 || c.ffn_hidden % 32 || c.dyn_ffn_hidden % 32 || c.vocab % 8)
     return TTT_ERR_UNSUPPORTED;
+  if (c.d_model > 8192) return TTT_ERR_UNSUPPORTED;  // a residual row stays in one workgroup's registers
   if ((int64_t)c.max_seq > (int64_t(1) << 30)) return TTT_ERR_UNSUPPORTED;
   if ((int64_t)c.vocab * c.d_model > (int64_t(1) << 31)) return TTT_ERR_UNSUPPORTED;
   return TTT_OK;
