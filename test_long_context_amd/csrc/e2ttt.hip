@@ -193,7 +193,23 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   constexpr int RED = NW * 2 * 16 * JH;  // floats of the cross-wave sums
   static_assert(RED * 4 <= NW * BT * KP * 2, "the cross-wave sums reuse the K blocks' LDS");
   __shared__ __attribute__((aligned(16))) bf16 Kb[NW][BT * KP];
-  const int ib = blockIdx.x >> 1, jh = blockIdx.x & 1, h = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round-robin (XCD = id % 8). With
+  // H % 8 == 0 the index is remapped so all 2 D / 16 workgroups of a head
+  // run on one XCD (heads x, x + 8, ... on XCD x): each reads the head's
+  // whole K block, which then comes from that XCD's L2 instead of once per
+  // XCD from memory.
+  constexpr int NB = 2 * (D / 16);  // workgroups per head
+  const int H = gridDim.x / NB;
+  int bid = blockIdx.x, h;
+  if ((H & 7) == 0) {
+    const int x = bid & 7, j = bid >> 3;
+    h = x + 8 * (j / NB);
+    bid = j % NB;
+  } else {
+    h = bid / NB;
+    bid = bid % NB;
+  }
+  const int ib = bid >> 1, jh = bid & 1;
   const int i0 = ib * 16, j0 = jh * JH;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -393,7 +409,7 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
   // the other W buffer, 256-byte aligned (its rows are read as 16-byte vectors)
   float* W2 = (float*)(((uintptr_t)(coef + (size_t)H * nch * 4) + 255) & ~(uintptr_t)255);
   if (e2_scalars(eta, beta, gamma, H, T, C, KW, KM, coef, st) != hipSuccess) return TTT_ERR_HIP;
-  const dim3 grid(2 * (D / 16), H);
+  const dim3 grid(2 * (D / 16) * H);
   for (int64_t r = 0; r < nch; ++r) {
     const int n = (int)std::min<int64_t>(C, T - r * C);
     const float* src = (r & 1) ? W2 : W;
