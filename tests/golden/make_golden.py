@@ -1,6 +1,6 @@
 """Writes expected values for the full-size bf16 parity tests.
 
-Calls only the input generators (synth) and the CPU oracle. Two cases:
+Calls only the input generators (synth) and the CPU oracle. Cases:
 
   * 3b_minibatch0 (default): the 3B-shape weights and the first 1025 tokens
     of its Zipf stream; the float32 oracle runs mini-batch 0 with one SGD
@@ -9,7 +9,12 @@ Calls only the input generators (synth) and the CPU oracle. Two cases:
     mini-batches and their updates (about 35 minutes, ~27 GB RAM);
   * 3b_8minibatches: the 3B-shape weights and the first 8193 tokens of its
     stream: 8 mini-batches and their updates, then the forward-only
-    position 8192 (about 30 minutes, ~30 GB RAM).
+    position 8192 (about 30 minutes, ~30 GB RAM);
+  * 3b_decode8k: the 3B-shape weights, a TTT prefill of the first 8192
+    tokens (8 mini-batches and their updates), then 3 decode steps with
+    tokens 8192 .. 8194 over the full 8192-key window (about 30 minutes).
+    Instead of fast-weight samples it stores, per decode step, 16384
+    seeded logit samples, the 16 largest logits and max |z|.
 
 Each file stores the per-token losses; for every dynamic block and matrix,
 4096 seeded sample coordinates, the oracle's fast weights there after the
@@ -17,7 +22,7 @@ last update, and max |W_T - W0| over the whole matrix (the normaliser of the
 update-relative error); and a fingerprint of the inputs (token ids, a few
 weight values).
 
-Usage: python tests/golden/make_golden.py [3b_minibatch0 | 1b_full | 3b_8minibatches]
+Usage: python tests/golden/make_golden.py [3b_minibatch0 | 1b_full | 3b_8minibatches | 3b_decode8k]
 """
 import os
 import sys
@@ -37,7 +42,10 @@ CASES = {
     "3b_minibatch0": ("3b", lambda c: c["minibatch"] + 1, "ttt_3b_minibatch0.npz"),
     "1b_full": ("1b", lambda c: c["seq"], "ttt_1b_full.npz"),
     "3b_8minibatches": ("3b", lambda c: 8 * c["minibatch"] + 1, "ttt_3b_8minibatches.npz"),
+    "3b_decode8k": ("3b", lambda c: 8 * c["minibatch"] + NDEC, "ttt_3b_decode8k.npz"),
 }
+NDEC = 3          # decode steps of the decode case
+NLOGIT = 16384    # sampled logits per decode step
 
 
 def main(name="3b_minibatch0"):
@@ -51,6 +59,25 @@ def main(name="3b_minibatch0"):
     wn = synth.weights_to_numpy(w, np.float32)
     del w
     t0 = time.time()
+    if name == "3b_decode8k":
+        T = len(tok) - NDEC
+        st = O.ttt_inner_loop(c, wn, tok[:T], dtype=np.float32, keep_state=True)
+        zs = [O.decode_step(st, int(tok[T + j])) for j in range(NDEC)]
+        print(f"oracle ran in {time.time() - t0:.0f} s", flush=True)
+        rng = np.random.default_rng(4321)
+        rec = {"tokens": tok.astype(np.int32), "embed_head": wn["embed"][:4, :8].copy(),
+               "w3_head": wn["layers"][-1]["w3"][:4, :8].copy(), "prefill_len": np.int64(T)}
+        for j, z in enumerate(zs):
+            idx = rng.integers(0, z.size, NLOGIT)
+            top = np.argsort(-z)[:16]
+            rec[f"z{j}_idx"] = idx.astype(np.int64)
+            rec[f"z{j}_val"] = z[idx].astype(np.float32)
+            rec[f"z{j}_top_idx"] = top.astype(np.int64)
+            rec[f"z{j}_top_val"] = z[top].astype(np.float32)
+            rec[f"z{j}_absmax"] = np.float64(np.max(np.abs(z)))
+        np.savez_compressed(OUT, **rec)
+        print(f"wrote {OUT}", flush=True)
+        return
     out = O.ttt_inner_loop(c, wn, tok, dtype=np.float32)
     print(f"oracle ran in {time.time() - t0:.0f} s", flush=True)
     rng = np.random.default_rng(1234)

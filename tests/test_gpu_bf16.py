@@ -128,3 +128,33 @@ def test_bf16_1b_full_sequence_against_stored_oracle_values():
     """The whole 1B-shape workload: 32768 tokens, 32 mini-batches and their
     updates."""
     check_stored("ttt_1b_full.npz", "1b", lambda c: c["seq"], "1b full sequence")
+
+
+@_stored("ttt_3b_decode8k.npz")
+def test_bf16_3b_decode_full_window_against_stored_oracle_values():
+    """The decode workload's shape: after a TTT prefill of 8192 tokens of the
+    3B stream (8 updates), decode steps over the full 8192-key window
+    (captured graph, as timed). Sampled logits and the oracle's 16 largest
+    logits within 2e-2 of max |z|; the GPU's top token is among the oracle's
+    16 largest."""
+    import test_long_context_amd as tla
+    g = np.load(os.path.join(HERE, "golden", "ttt_3b_decode8k.npz"), allow_pickle=False)
+    c = synth.config("3b")
+    T = int(g["prefill_len"])
+    ndec = len(g["tokens"]) - T
+    w = synth.gen_weights(c, device="cuda")
+    tok = synth.gen_tokens(c, n=T + ndec, device="cuda")
+    assert np.array_equal(tok.cpu().numpy(), g["tokens"])
+    assert np.array_equal(w["embed"][:4, :8].float().cpu().numpy(), g["embed_head"])
+    m = tla.TTT(c, w, max_seq=T + ndec + 1)
+    m.prefill(tok[:T])
+    for j in range(ndec):
+        z = m.decode_step(tok[T + j:T + j + 1]).cpu().numpy().astype(np.float64)
+        den = float(g[f"z{j}_absmax"])
+        e_s = float(np.max(np.abs(z[g[f"z{j}_idx"]] - g[f"z{j}_val"]))) / den
+        e_t = float(np.max(np.abs(z[g[f"z{j}_top_idx"]] - g[f"z{j}_top_val"]))) / den
+        say(f"  3b decode step {j}: sampled logit err {e_s:.3e}  top-16 err {e_t:.3e}")
+        assert np.all(np.isfinite(z))
+        assert e_s < 2e-2 and e_t < 2e-2
+        assert int(np.argmax(z)) in set(g[f"z{j}_top_idx"].tolist())
+    m.close()
