@@ -425,13 +425,30 @@ __global__ void __launch_bounds__(RB) ce_kernel(const float* z, int nt, int V, c
   }
   float m = -INFINITY, s = 0.f;
   const float4* z4 = (const float4*)zr;
-  for (int j = threadIdx.x; j < V / 4; j += blockDim.x) {
+  const int nv4 = V / 4;
+  // four float4 chunks per thread per round, loaded before they are used
+  constexpr int U = 4;
+  int j = threadIdx.x;
+  for (; j + (U - 1) * RB < nv4; j += U * RB) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = z4[j + u * RB];
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+    if (mx == -INFINITY) continue;  // nothing finite yet (s is still 0)
+    s *= __expf(m - mx);
+    m = mx;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      s += __expf(v[u].x - m) + __expf(v[u].y - m) + __expf(v[u].z - m) + __expf(v[u].w - m);
+  }
+  for (; j < nv4; j += RB) {
     const float4 v = z4[j];
-    const float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
-    if (mx > m) {
-      s *= __expf(m - mx);
-      m = mx;
-    }
+    const float mx = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    if (mx == -INFINITY) continue;
+    s *= __expf(m - mx);
+    m = mx;
     s += __expf(v.x - m) + __expf(v.y - m) + __expf(v.z - m) + __expf(v.w - m);
   }
   // combine (m, s) across the wave, then the block
@@ -460,19 +477,27 @@ __global__ void __launch_bounds__(RB) ce_kernel(const float* z, int nt, int V, c
     if (!yok) atomicOr(err, 1);
     else if (!isfinite(li)) atomicOr(err, 4);
   }
-  for (int j = threadIdx.x; j < V / 4; j += blockDim.x) {
-    const float4 v = z4[j];
-    const int b = 4 * j;
-    dr[b + 0] = from_f<T>((__expf(v.x - lse) - (b + 0 == y ? 1.f : 0.f)) * scale);
-    dr[b + 1] = from_f<T>((__expf(v.y - lse) - (b + 1 == y ? 1.f : 0.f)) * scale);
-    dr[b + 2] = from_f<T>((__expf(v.z - lse) - (b + 2 == y ? 1.f : 0.f)) * scale);
-    dr[b + 3] = from_f<T>((__expf(v.w - lse) - (b + 3 == y ? 1.f : 0.f)) * scale);
+  auto dz4 = [&](float4 v, int b) {
+    return make_float4((__expf(v.x - lse) - (b + 0 == y ? 1.f : 0.f)) * scale,
+                       (__expf(v.y - lse) - (b + 1 == y ? 1.f : 0.f)) * scale,
+                       (__expf(v.z - lse) - (b + 2 == y ? 1.f : 0.f)) * scale,
+                       (__expf(v.w - lse) - (b + 3 == y ? 1.f : 0.f)) * scale);
+  };
+  j = threadIdx.x;
+  for (; j + (U - 1) * RB < nv4; j += U * RB) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = z4[j + u * RB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) store4<T>(dr + 4 * (j + u * RB), dz4(v[u], 4 * (j + u * RB)));
   }
+  for (; j < nv4; j += RB) store4<T>(dr + 4 * j, dz4(z4[j], 4 * j));
 }
 
 hipError_t ce_fwd_bwd(DT dt, const float* z, int n, int nt, int V, const int32_t* lab, float scale,
                       float* loss, void* dz, int* err, hipStream_t st) {
   if (n <= 0) return hipSuccess;
+  if (V % 4) return hipErrorInvalidValue;
   if (dt == DT::BF16)
     hipLaunchKernelGGL(ce_kernel<bf16>, dim3(n), dim3(RB), 0, st, z, nt, V, lab, scale, loss, (bf16*)dz, err);
   else
