@@ -302,27 +302,45 @@ __global__ void rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, 
     }
 }
 
-// The transposed value store: a workgroup takes 64 tokens of one key head,
-// stages their value rows in LDS and writes each of the dh rows of the store
-// as 64 consecutive positions (vt_slot permutes within aligned groups of 16,
-// so a wave's stores still cover whole 128-byte runs).
+// The transposed value store: a workgroup takes 64 tokens of one key head
+// and DS of its dh rows (blockIdx.z selects which), loads their values as
+// 16-byte vectors (all loads issued before the first LDS write), stages them
+// in LDS and writes each row of the store as 64 consecutive positions
+// (vt_slot permutes within aligned groups of 16, so a wave's stores still
+// cover whole 128-byte runs).
 template <typename T>
 __global__ void __launch_bounds__(256) vt_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, int64_t pos0,
                                                          T* vts, int cap, int64_t min_pos) {
   extern __shared__ unsigned char vt_lds[];
-  T* Vs = (T*)vt_lds;  // [dh][65]
+  T* Vs = (T*)vt_lds;  // [ds][65]
   constexpr int TT = 64, PITCH = TT + 1;
+  constexpr int VE = 16 / sizeof(T);
   const int t0 = blockIdx.x * TT, kh = blockIdx.y;
+  const int ds = dh / gridDim.z, d0 = blockIdx.z * ds;
   const int W = (H + 2 * Hk) * dh;
-  for (int e = threadIdx.x; e < TT * dh; e += blockDim.x) {
-    const int t = e / dh, d = e % dh;
-    if (t0 + t < n) Vs[d * PITCH + t] = qkv[(long)(t0 + t) * W + (H + Hk) * dh + kh * dh + d];
+  const int vpr = ds / VE;  // 16-byte vectors per token row
+  constexpr int MAXL = 4;   // vectors per thread (TT * ds / VE <= 256 * MAXL)
+  uint4 r[MAXL];
+#pragma unroll
+  for (int i = 0; i < MAXL; ++i) {
+    const int e = threadIdx.x + i * 256, t = e / vpr, v = e % vpr;
+    if (t < TT && t0 + t < n) r[i] = *(const uint4*)(qkv + (long)(t0 + t) * W + (H + Hk) * dh + kh * dh + d0 + v * VE);
+  }
+#pragma unroll
+  for (int i = 0; i < MAXL; ++i) {
+    const int e = threadIdx.x + i * 256, t = e / vpr, v = e % vpr;
+    if (t < TT && t0 + t < n) {
+      const T* x = (const T*)&r[i];
+#pragma unroll
+      for (int k = 0; k < VE; ++k) Vs[(v * VE + k) * PITCH + t] = x[k];
+    }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < TT * dh; e += blockDim.x) {
+  for (int e = threadIdx.x; e < TT * ds; e += blockDim.x) {
     const int d = e / TT, t = e % TT;
     const int64_t pos = pos0 + t0 + t;
-    if (t0 + t < n && pos >= min_pos) vts[((long)kh * dh + d) * cap + vt_slot(pos & (cap - 1))] = Vs[d * PITCH + t];
+    if (t0 + t < n && pos >= min_pos)
+      vts[((long)kh * dh + d0 + d) * cap + vt_slot(pos & (cap - 1))] = Vs[d * PITCH + t];
   }
 }
 
@@ -330,18 +348,25 @@ hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, in
                         const float2* tab, void* q, void* ks, void* vs, void* vts, int cap,
                         int64_t min_pos, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  const dim3 vgrid((n + 63) / 64, Hk);
+  // dh split in two for dh 128 (more workgroups for a mini-batch); each
+  // part must be whole 16-byte vectors and fit the loader (64 x part <= 256 x 4 vectors)
+  const int esz = (int)dt_size(dt);
+  int dsp = (dh >= 128) ? 2 : 1;
+  while (dsp > 1 && ((dh / dsp) * esz) % 16) dsp = 1;
+  if (((dh / dsp) * esz) % 16 || 64 * (dh / dsp) * esz / 16 > 256 * 4) return hipErrorInvalidValue;
+  const dim3 vgrid((n + 63) / 64, Hk, dsp);
+  const size_t vlds = (size_t)(dh / dsp) * 65;
   if (dt == DT::BF16) {
     hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(n), dim3(RB), 0, st, (const bf16*)qkv, n, H, Hk,
                        dh, pos0, tab, (bf16*)q, (bf16*)ks, (bf16*)vs, cap, min_pos);
     if (vts)
-      hipLaunchKernelGGL(vt_scatter_kernel<bf16>, vgrid, dim3(256), (size_t)dh * 65 * sizeof(bf16), st,
+      hipLaunchKernelGGL(vt_scatter_kernel<bf16>, vgrid, dim3(256), vlds * sizeof(bf16), st,
                          (const bf16*)qkv, n, H, Hk, dh, pos0, (bf16*)vts, cap, min_pos);
   } else {
     hipLaunchKernelGGL(rope_scatter_kernel<float>, dim3(n), dim3(RB), 0, st, (const float*)qkv, n, H,
                        Hk, dh, pos0, tab, (float*)q, (float*)ks, (float*)vs, cap, min_pos);
     if (vts)
-      hipLaunchKernelGGL(vt_scatter_kernel<float>, vgrid, dim3(256), (size_t)dh * 65 * sizeof(float), st,
+      hipLaunchKernelGGL(vt_scatter_kernel<float>, vgrid, dim3(256), vlds * sizeof(float), st,
                          (const float*)qkv, n, H, Hk, dh, pos0, (float*)vts, cap, min_pos);
   }
   return hipGetLastError();
@@ -507,29 +532,60 @@ hipError_t ce_fwd_bwd(DT dt, const float* z, int n, int nt, int V, const int32_t
 }
 
 // ------------------------------------------------------------ rowdot D
-template <typename T>
-__global__ void rowdot_kernel(const T* dO, const T* O, int n, int H, int dh, float* D) {
-  // one wave per (t, h)
-  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
-  if (w >= (long)n * H) return;
-  const long t = w / H, h = w % H;
+// D[h][t] = dO[t, h, :] . O[t, h, :]. A row (t, h) is dh * sizeof(T) bytes,
+// taken by LPR lanes reading 16 bytes each from both operands (every load of
+// a lane issued before the products), the LPR partial sums meeting through
+// lane shuffles; a 64-lane wave covers 64 / LPR rows.
+template <typename T, int LPR>
+__global__ void __launch_bounds__(256) rowdot_kernel(const T* dO, const T* O, int n, int H, int dh, float* D) {
+  constexpr int VE = 16 / sizeof(T);
+  const long rows = (long)n * H;
+  const long w = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;  // row of this lane
+  const int sub = threadIdx.x % LPR;
+  const int nvr = dh / VE;  // 16-byte vectors per row
   float s = 0.f;
-  for (int j = l; j < dh; j += 64) s += to_f(dO[w * dh + j]) * to_f(O[w * dh + j]);
-  s = wave_sum(s);
-  if (l == 0) D[h * n + t] = s;
+  if (w < rows) {
+    constexpr int MAXV = 4;  // vectors per lane (dh * sizeof(T) <= 64 LPR bytes)
+    uint4 a[MAXV], c[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int v = sub + i * LPR;
+      if (v < nvr) {
+        a[i] = ((const uint4*)(dO + w * dh))[v];
+        c[i] = ((const uint4*)(O + w * dh))[v];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      if (sub + i * LPR >= nvr) continue;
+      const T* x = (const T*)&a[i];
+      const T* y = (const T*)&c[i];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s += to_f(x[e]) * to_f(y[e]);
+    }
+  }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (w < rows && sub == 0) {
+    const long t = w / H, h = w % H;
+    D[h * n + t] = s;
+  }
 }
 
 hipError_t attn_rowdot(DT dt, const void* dO, const void* O, int n, int H, int dh, float* D,
                        hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  const long nw = (long)n * H;
-  dim3 grid((unsigned)((nw + 3) / 4));
+  const long rows = (long)n * H;
+  const int es = (int)dt_size(dt);
+  if ((dh * es) % 16 || dh * es > 16 * 16 * 4) return hipErrorInvalidValue;
+  // lanes per row: 16 for rows of up to 256 bytes, else 16 with several vectors each
+  constexpr int LPR = 16;
+  const dim3 grid((unsigned)((rows * LPR + 255) / 256));
   if (dt == DT::BF16)
-    hipLaunchKernelGGL(rowdot_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)dO, (const bf16*)O, n, H, dh, D);
+    hipLaunchKernelGGL((rowdot_kernel<bf16, LPR>), grid, dim3(256), 0, st, (const bf16*)dO, (const bf16*)O, n, H, dh, D);
   else
-    hipLaunchKernelGGL(rowdot_kernel<float>, grid, dim3(256), 0, st, (const float*)dO, (const float*)O, n, H, dh,
-                       D);
+    hipLaunchKernelGGL((rowdot_kernel<float, LPR>), grid, dim3(256), 0, st, (const float*)dO, (const float*)O, n, H,
+                       dh, D);
   return hipGetLastError();
 }
 
