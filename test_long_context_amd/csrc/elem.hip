@@ -269,7 +269,7 @@ hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const
 // Half-split rotation: (x1, x2) -> (x1 c - x2 s, x1 s + x2 c), with (c, s)
 // at tab[pos * dh/2 + j] (built on the host from float64 angles).
 template <typename T>
-__global__ void rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, int64_t pos0,
+__global__ void rope_scatter_generic_kernel(const T* qkv, int n, int H, int Hk, int dh, int64_t pos0,
                                     const float2* tab, T* q, T* ks, T* vs, int cap,
                                     int64_t min_pos) {
   const int t = blockIdx.x;
@@ -300,6 +300,80 @@ __global__ void rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, 
       const int kh = i / dh, j = i % dh;
       vs[((long)kh * cap + slot) * dh + j] = row[(H + Hk) * dh + i];
     }
+}
+
+// Four consecutive elements of a row (T) as floats.
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> {
+  typedef bf16x4 raw;
+  __device__ __forceinline__ static float4 f(raw v) {
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+  }
+};
+template <> struct Vec4<float> {
+  typedef float4 raw;
+  __device__ __forceinline__ static float4 f(raw v) { return v; }
+};
+
+// One workgroup per token; thread i takes the rotation groups i, i + RB, ...
+// (KR at most: 4 consecutive pairs (j .. j+3, j+dh/2 .. j+dh/2+3) of one q
+// or k head) and the i-th 16-byte vector of the token's values. Every load
+// is issued before the first store: the memory counter that tracks loads
+// also tracks stores, so interleaving them would cost a round trip each.
+// Shapes beyond (H + Hk) dh <= 16 KR RB / ... take the element-wise kernel
+// above (rope_scatter chooses).
+constexpr int ROPE_KR = 4;
+template <typename T>
+__global__ void __launch_bounds__(RB) rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, int64_t pos0,
+                                                          const float2* tab, T* q, T* ks, T* vs, int cap,
+                                                          int64_t min_pos) {
+  typedef typename Vec4<T>::raw R4;
+  constexpr int VE = 16 / sizeof(T);
+  const int t = blockIdx.x;
+  const int64_t pos = pos0 + t;
+  const int half = dh / 2;
+  const int W = (H + 2 * Hk) * dh;
+  const T* row = qkv + (long)t * W;
+  const float4* tb = (const float4*)(tab + pos * half);  // (c, s) of pairs j and j + 1
+  const bool store = pos >= min_pos;
+  const long slot = (long)(pos & (cap - 1));
+  const int gph = half / 4, ng = (H + Hk) * gph, nvv = Hk * dh / VE;
+  R4 x1[ROPE_KR], x2[ROPE_KR];
+  float4 c01[ROPE_KR], c23[ROPE_KR];
+  uint4 vv;
+#pragma unroll
+  for (int k = 0; k < ROPE_KR; ++k) {
+    const int gi = threadIdx.x + k * RB;
+    if (gi < ng) {
+      const int hh = gi / gph, j = (gi % gph) * 4;
+      x1[k] = *(const R4*)(row + hh * dh + j);
+      x2[k] = *(const R4*)(row + hh * dh + j + half);
+      c01[k] = tb[j / 2];
+      c23[k] = tb[j / 2 + 1];
+    }
+  }
+  const bool hv = store && (int)threadIdx.x < nvv;
+  if (hv) vv = ((const uint4*)(row + (H + Hk) * dh))[threadIdx.x];
+#pragma unroll
+  for (int k = 0; k < ROPE_KR; ++k) {
+    const int gi = threadIdx.x + k * RB;
+    if (gi >= ng) continue;
+    const int hh = gi / gph, j = (gi % gph) * 4;
+    T* d;
+    if (hh < H) d = q + ((long)t * H + hh) * dh + j;
+    else if (store) d = ks + ((long)(hh - H) * cap + slot) * dh + j;
+    else continue;
+    const float4 a = Vec4<T>::f(x1[k]), b = Vec4<T>::f(x2[k]);
+    const float4 c = c01[k], e = c23[k];
+    store4<T>(d, make_float4(a.x * c.x - b.x * c.y, a.y * c.z - b.y * c.w, a.z * e.x - b.z * e.y,
+                             a.w * e.z - b.w * e.w));
+    store4<T>(d + half, make_float4(a.x * c.y + b.x * c.x, a.y * c.w + b.y * c.z, a.z * e.y + b.z * e.x,
+                                    a.w * e.w + b.w * e.z));
+  }
+  if (hv) {
+    const int e0 = threadIdx.x * VE, kh = e0 / dh, j = e0 % dh;
+    *(uint4*)(vs + ((long)kh * cap + slot) * dh + j) = vv;
+  }
 }
 
 // The transposed value store: a workgroup takes 64 tokens of one key head
@@ -356,15 +430,27 @@ hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, in
   if (((dh / dsp) * esz) % 16 || 64 * (dh / dsp) * esz / 16 > 256 * 4) return hipErrorInvalidValue;
   const dim3 vgrid((n + 63) / 64, Hk, dsp);
   const size_t vlds = (size_t)(dh / dsp) * 65;
+  // the vector kernel: whole 4-pair groups, at most ROPE_KR per thread, and
+  // one 16-byte value vector per thread
+  const bool vec = dh % 8 == 0 && (H + Hk) * (dh / 8) <= ROPE_KR * RB && Hk * dh * esz / 16 <= RB &&
+                   (dh * esz) % 16 == 0;
   if (dt == DT::BF16) {
-    hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(n), dim3(RB), 0, st, (const bf16*)qkv, n, H, Hk,
-                       dh, pos0, tab, (bf16*)q, (bf16*)ks, (bf16*)vs, cap, min_pos);
+    if (vec)
+      hipLaunchKernelGGL(rope_scatter_kernel<bf16>, dim3(n), dim3(RB), 0, st, (const bf16*)qkv, n, H, Hk,
+                         dh, pos0, tab, (bf16*)q, (bf16*)ks, (bf16*)vs, cap, min_pos);
+    else
+      hipLaunchKernelGGL(rope_scatter_generic_kernel<bf16>, dim3(n), dim3(RB), 0, st, (const bf16*)qkv, n, H, Hk,
+                         dh, pos0, tab, (bf16*)q, (bf16*)ks, (bf16*)vs, cap, min_pos);
     if (vts)
       hipLaunchKernelGGL(vt_scatter_kernel<bf16>, vgrid, dim3(256), vlds * sizeof(bf16), st,
                          (const bf16*)qkv, n, H, Hk, dh, pos0, (bf16*)vts, cap, min_pos);
   } else {
-    hipLaunchKernelGGL(rope_scatter_kernel<float>, dim3(n), dim3(RB), 0, st, (const float*)qkv, n, H,
-                       Hk, dh, pos0, tab, (float*)q, (float*)ks, (float*)vs, cap, min_pos);
+    if (vec)
+      hipLaunchKernelGGL(rope_scatter_kernel<float>, dim3(n), dim3(RB), 0, st, (const float*)qkv, n, H,
+                         Hk, dh, pos0, tab, (float*)q, (float*)ks, (float*)vs, cap, min_pos);
+    else
+      hipLaunchKernelGGL(rope_scatter_generic_kernel<float>, dim3(n), dim3(RB), 0, st, (const float*)qkv, n, H,
+                         Hk, dh, pos0, tab, (float*)q, (float*)ks, (float*)vs, cap, min_pos);
     if (vts)
       hipLaunchKernelGGL(vt_scatter_kernel<float>, vgrid, dim3(256), vlds * sizeof(float), st,
                          (const float*)qkv, n, H, Hk, dh, pos0, (float*)vts, cap, min_pos);
@@ -374,7 +460,7 @@ hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, in
 
 // Transpose of the rotation (rotation by -angle) for dq, dk; dv copied.
 template <typename T>
-__global__ void rope_bwd_kernel(const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
+__global__ void rope_bwd_generic_kernel(const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
                                 int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, T* out) {
   const int t = blockIdx.x;
   const int half = dh / 2;
@@ -405,16 +491,96 @@ __global__ void rope_bwd_kernel(const float* dq, int dq_parts, const float* dk, 
   }
 }
 
+// The same, vectorized: thread i takes rotation groups i and i + RB (4
+// consecutive pairs of one head; ROPE_BKR at most) and the i-th group of 4
+// value-gradient elements; the loads of every partial are issued before the
+// first store. At most ROPE_BNP partials per side (rope_bwd_pack chooses).
+constexpr int ROPE_BKR = 2, ROPE_BNP = 4;
+template <typename T>
+__global__ void __launch_bounds__(RB) rope_bwd_kernel(const float* dq, int dq_parts, const float* dk, const float* dv,
+                                                      int kv_parts, int n, int H, int Hk, int dh, int64_t pos0,
+                                                      const float2* tab, T* out) {
+  const int t = blockIdx.x;
+  const int half = dh / 2;
+  const int W = (H + 2 * Hk) * dh;
+  const long qstride = (long)n * H * dh, kstride = (long)n * Hk * dh;
+  const float4* tb = (const float4*)(tab + (pos0 + t) * half);
+  const int gph = half / 4, ng = (H + Hk) * gph, nvg = Hk * dh / 4;
+  float4 g1[ROPE_BKR][ROPE_BNP], g2[ROPE_BKR][ROPE_BNP], c01[ROPE_BKR], c23[ROPE_BKR], gv[ROPE_BNP];
+#pragma unroll
+  for (int k = 0; k < ROPE_BKR; ++k) {
+    const int gi = threadIdx.x + k * RB;
+    if (gi < ng) {
+      const int hh = gi / gph, j = (gi % gph) * 4;
+      const bool isq = hh < H;
+      const float* src = isq ? dq + ((long)t * H + hh) * dh : dk + ((long)t * Hk + (hh - H)) * dh;
+      const int np = isq ? dq_parts : kv_parts;
+      const long ps = isq ? qstride : kstride;
+#pragma unroll
+      for (int p = 0; p < ROPE_BNP; ++p)
+        if (p < np) {
+          g1[k][p] = *(const float4*)(src + p * ps + j);
+          g2[k][p] = *(const float4*)(src + p * ps + j + half);
+        }
+      c01[k] = tb[j / 2];
+      c23[k] = tb[j / 2 + 1];
+    }
+  }
+  const bool hv = (int)threadIdx.x < nvg;
+#pragma unroll
+  for (int p = 0; p < ROPE_BNP; ++p)
+    if (hv && p < kv_parts) gv[p] = *(const float4*)(dv + p * kstride + (long)t * Hk * dh + 4 * threadIdx.x);
+  // partial sums added in a fixed order
+#pragma unroll
+  for (int k = 0; k < ROPE_BKR; ++k) {
+    const int gi = threadIdx.x + k * RB;
+    if (gi >= ng) continue;
+    const int hh = gi / gph, j = (gi % gph) * 4;
+    const int np = hh < H ? dq_parts : kv_parts;
+    float4 a = g1[k][0], b = g2[k][0];
+#pragma unroll
+    for (int p = 1; p < ROPE_BNP; ++p)
+      if (p < np) {
+        a = f4add(a, g1[k][p]);
+        b = f4add(b, g2[k][p]);
+      }
+    const float4 c = c01[k], e = c23[k];
+    T* d = out + (long)t * W + hh * dh + j;
+    store4<T>(d, make_float4(a.x * c.x + b.x * c.y, a.y * c.z + b.y * c.w, a.z * e.x + b.z * e.y,
+                             a.w * e.z + b.w * e.w));
+    store4<T>(d + half, make_float4(-a.x * c.y + b.x * c.x, -a.y * c.w + b.y * c.z, -a.z * e.y + b.z * e.x,
+                                    -a.w * e.w + b.w * e.z));
+  }
+  if (hv) {
+    float4 g = gv[0];
+#pragma unroll
+    for (int p = 1; p < ROPE_BNP; ++p)
+      if (p < kv_parts) g = f4add(g, gv[p]);
+    store4<T>(out + (long)t * W + (H + Hk) * dh + 4 * threadIdx.x, g);
+  }
+}
+
 hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
                          int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
                          hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  if (dt == DT::BF16)
-    hipLaunchKernelGGL(rope_bwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H, Hk,
-                       dh, pos0, tab, (bf16*)dqkv);
-  else
-    hipLaunchKernelGGL(rope_bwd_kernel<float>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H,
-                       Hk, dh, pos0, tab, (float*)dqkv);
+  const bool vec = dh % 8 == 0 && (H + Hk) * (dh / 8) <= ROPE_BKR * RB && Hk * dh / 4 <= RB && dq_parts >= 1 &&
+                   dq_parts <= ROPE_BNP && kv_parts >= 1 && kv_parts <= ROPE_BNP;
+  if (dt == DT::BF16) {
+    if (vec)
+      hipLaunchKernelGGL(rope_bwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H, Hk,
+                         dh, pos0, tab, (bf16*)dqkv);
+    else
+      hipLaunchKernelGGL(rope_bwd_generic_kernel<bf16>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n,
+                         H, Hk, dh, pos0, tab, (bf16*)dqkv);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL(rope_bwd_kernel<float>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H,
+                         Hk, dh, pos0, tab, (float*)dqkv);
+    else
+      hipLaunchKernelGGL(rope_bwd_generic_kernel<float>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts,
+                         n, H, Hk, dh, pos0, tab, (float*)dqkv);
+  }
   return hipGetLastError();
 }
 
