@@ -359,18 +359,20 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_rows_kernel(const TW* __restr
 
 template <typename TW, int EPI, bool NORM, int NVL>
 static int gemv_rows_grid(size_t lds) {
-  // workgroups that fit on the device at once (the device the first call
-  // runs on; every device of a process is assumed alike), kept for the
-  // last LDS size asked for
-  static size_t last_lds = 0;
-  static int n = 0;
-  if (lds != last_lds) {
-    int dev = 0, cus = 0, per = 0;
-    (void)hipGetDevice(&dev);
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  // workgroups that fit on the current device at once, kept per host thread
+  // for the last (device, LDS size) asked for
+  static thread_local size_t last_lds = 0;
+  static thread_local int last_dev = -1;
+  static thread_local int n = 0;
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  if (lds != last_lds || cur != last_dev) {
+    int cus = 0, per = 0;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cur);
     (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, gemv_rows_kernel<TW, EPI, NORM, NVL>, GV_THREADS, lds);
     n = std::max(1, cus) * std::max(1, per);
     last_lds = lds;
+    last_dev = cur;
   }
   return n;
 }
