@@ -48,6 +48,7 @@ def _init(cfg_overrides, ptr=1):
     (dict(head_dim=32, d_model=64, n_heads=2, n_kv_heads=2), -2),  # unsupported head size
     (dict(ffn_hidden=200), -2),                  # not a multiple of 32
     (dict(vocab=250), -2),                       # not a multiple of 8
+    (dict(d_model=8208), -2),                    # residual row wider than one workgroup keeps
     (dict(dtype="bf16", head_dim=128, n_heads=1, n_kv_heads=1, d_model=128), None),
 ])
 def test_init_validates_config_before_touching_the_device(over, code):
