@@ -77,7 +77,6 @@ struct ttt_ctx {
   void* hmid = nullptr;    // [slab, max(F, Fd)]
 
   // loop (per dynamic block i = l - s)
-  float* hl = nullptr;                       // [b, d]
   std::vector<float*> h_att, h_mlp, h_dyn, r_att, r_mlp, r_dyn, lse;
   std::vector<void*> q_l, o_l, h12_s, xn_d, h12_d, hm_d;
   float* h_f = nullptr;
@@ -397,14 +396,18 @@ ttt_status gemm_resid(ttt_ctx* c, int kind, const void* A, long lda, const void*
 ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipStream_t st) {
   const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s, F = c->F, Fd = c->Fd;
   const float eps = c->cfg.rms_eps;
-  float* hl = c->hl;
+  // the residual stream lives in the buffers saved for the backward: xr is
+  // the latest one, and each fused RMSNorm adds the pending partial sums to
+  // it and saves the result as the next
+  const float* xr = c->hres + a0 * d;
   int np = 0;  // split-K partial sums of the last residual product, pending in c->part
   for (int l = s; l < c->L; ++l) {
     const int i = l - s;
     if (l > s) {
       // attention sublayer (adds the pending dynamic-MLP output of block l-1)
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_att[i], c->attn_norm[l], n, d, eps,
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_att[i], c->attn_norm[l], n, d, eps,
                                             c->xn, c->r_att[i], st));
+      xr = c->h_att[i];
       TCALL(KC_GL, gfl(n, QKV, d), 0,
             gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
       TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, a0, c->rope, c->q_l[i], c->kring[l],
@@ -419,8 +422,9 @@ ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipSt
       TCALL(KC_OT, 0, 0, attn_fwd2_combine(a, st));
       RUN(gemm_resid(c, KC_GL, c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, nullptr, n, d, H * dh, &np, st));
       // static MLP sublayer
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_mlp[i], c->mlp_norm[l], n, d, eps,
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_mlp[i], c->mlp_norm[l], n, d, eps,
                                             c->xn, c->r_mlp[i], st));
+      xr = c->h_mlp[i];
       GemmArgs g = ga(c->xn, d, c->w12[l], d, n, 2 * F, d, c->h12_s[i], 2 * F);
       g.C2 = c->hmid;
       TCALL(KC_GL, gfl(n, 2 * F, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
@@ -428,13 +432,15 @@ ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipSt
       // the previous mini-batch's update of this block (side stream) reads
       // xn_d and the saved activations written from here on
       HIPCHK(c, hipStreamWaitEvent(st, c->ev_upd[i], 0));
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_dyn[i], c->dyn_norm[i], n, d, eps,
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_dyn[i], c->dyn_norm[i], n, d, eps,
                                             c->xn_d[i], c->r_dyn[i], st));
+      xr = c->h_dyn[i];
     } else {
       // block s: the residual stream comes from the hoisted prefix
       HIPCHK(c, hipStreamWaitEvent(st, c->ev_upd[i], 0));
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, c->hres + a0 * d, nullptr, 0, hl, c->h_dyn[i], c->dyn_norm[i], n,
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, nullptr, 0, nullptr, c->h_dyn[i], c->dyn_norm[i], n,
                                             d, eps, c->xn_d[i], c->r_dyn[i], st));
+      xr = c->h_dyn[i];
     }
     // dynamic MLP sublayer under the current fast weights
     // (bf16: the fp32 master enters as two bf16 terms, working + low, so that
@@ -445,8 +451,8 @@ ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipSt
     TCALL(KC_GL, gfl(n, 2 * Fd, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
     RUN(gemm_resid(c, KC_GL, c->hm_d[i], Fd, c->dw3[i], Fd, c->dw3_lo[i], n, d, Fd, &np, st));
   }
-  TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, hl, c->part, np, hl, c->h_f, c->final_norm, n, d, eps, c->xn, c->r_f,
-                                        st));
+  TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_f, c->final_norm, n, d, eps, c->xn,
+                                        c->r_f, st));
   TCALL(KC_LM, gfl(n, c->V, d), 0,
         gemm(c->dt, true, true, Epi::STORE_F32, ga(c->xn, d, c->lm_head, d, n, c->V, d, c->logits, c->V), st));
   return TTT_OK;
@@ -701,7 +707,6 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   A(&c->qb, (size_t)S * c->H * c->dh * es);
   A(&c->ob, (size_t)S * c->H * c->dh * es);
   A(&c->hmid, (size_t)S * Fm * es);
-  Af(&c->hl, (size_t)b * d);
   c->h_att.resize(nd);
   c->h_mlp.resize(nd);
   c->h_dyn.resize(nd);
