@@ -102,10 +102,14 @@ struct ttt_ctx {
   float* dec = nullptr;                      // decode scratch
   int dec_split = 1;
   int32_t* d_tok = nullptr;                  // decode input token
-  // fast-weight updates run on a side stream, overlapping the rest of the
+  // fast-weight updates run on side streams, overlapping the rest of the
   // backward; their inputs are per dynamic block so that the main stream
-  // never overwrites what an update still reads
+  // never overwrites what an update still reads. A block's two update
+  // products (dW3 on side2, dW12 on side) run side by side, so one's
+  // epilogue traffic overlaps the other's products.
   hipStream_t side = nullptr;
+  hipStream_t side2 = nullptr;
+  hipEvent_t ev_w3 = nullptr;                // side2: the last dW3 update is done
   std::vector<hipEvent_t> ev_dyn;            // per dynamic block: its dW inputs are ready
   std::vector<hipEvent_t> ev_upd;            // per dynamic block: its update is done
   hipEvent_t ev_join = nullptr;              // side stream done with the prefill
@@ -481,18 +485,25 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     // on the side stream once this block's products with the old W are queued
     HIPCHK(c, hipEventRecord(c->ev_dyn[i], st));
     HIPCHK(c, hipStreamWaitEvent(c->side, c->ev_dyn[i], 0));
+    HIPCHK(c, hipStreamWaitEvent(c->side2, c->ev_dyn[i], 0));
     {
-      hipStream_t st = c->side;
+      hipStream_t st = c->side2;
       GemmArgs g = ga(gt, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
       g.C2 = c->dw3[i];
       g.C3 = c->dw3_lo[i];
       g.scale = lr;
       TCALL(KC_SGD, gfl(d, Fd, n), (double)d * Fd * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g, st));
+      HIPCHK(c, hipEventRecord(c->ev_w3, st));
+    }
+    {
+      hipStream_t st = c->side;
       GemmArgs g2 = ga(c->dh12d[i], 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
       g2.C2 = c->dw12[i];
       g2.C3 = c->dw12_lo[i];
       g2.scale = lr;
       TCALL(KC_SGD, gfl(2 * Fd, d, n), 2.0 * Fd * d * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g2, st));
+      // the block's update is done once both products are
+      HIPCHK(c, hipStreamWaitEvent(st, c->ev_w3, 0));
       HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
     }
     if (l == s) break;
@@ -760,6 +771,8 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     A(&c->dh12d[i], (size_t)b * 2 * c->Fd * es);
   }
   if (ok && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) ok = false;
+  if (ok && hipStreamCreateWithFlags(&c->side2, hipStreamNonBlocking) != hipSuccess) ok = false;
+  if (ok && hipEventCreateWithFlags(&c->ev_w3, hipEventDisableTiming) != hipSuccess) ok = false;
   c->ev_dyn.assign(nd, nullptr);
   c->ev_upd.assign(nd, nullptr);
   for (int i = 0; i < nd && ok; ++i)
@@ -998,7 +1011,9 @@ void ttt_destroy(ttt_ctx* c) {
   for (hipEvent_t e : c->ev_upd)
     if (e) (void)hipEventDestroy(e);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->ev_w3) (void)hipEventDestroy(c->ev_w3);
   if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->side2) (void)hipStreamDestroy(c->side2);
   for (void* p : c->allocs) (void)hipFree(p);
   delete c;
 }
