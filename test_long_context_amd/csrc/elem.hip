@@ -320,8 +320,9 @@ template <> struct Vec4<float> {
 // or k head) and the i-th 16-byte vector of the token's values. Every load
 // is issued before the first store: the memory counter that tracks loads
 // also tracks stores, so interleaving them would cost a round trip each.
-// Shapes beyond (H + Hk) dh <= 16 KR RB / ... take the element-wise kernel
-// above (rope_scatter chooses).
+// Shapes past its limits ((H + Hk) dh / 8 groups at most ROPE_KR * RB, Hk
+// dh values at most RB 16-byte vectors) take the element-wise kernel above
+// (rope_scatter chooses).
 constexpr int ROPE_KR = 4;
 template <typename T>
 __global__ void __launch_bounds__(RB) rope_scatter_kernel(const T* qkv, int n, int H, int Hk, int dh, int64_t pos0,
