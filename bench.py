@@ -390,8 +390,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the inner loop on one GPU only; --gpus N > 1 is not "
-              "supported (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py: the inner loop runs on one GPU only; --gpus N > 1 is not supported "
+              "(one GPU's share of a sharded run is what this measures).", file=sys.stderr)
         sys.exit(2)
 
     import torch
