@@ -254,8 +254,24 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
   __shared__ float ls0[BT], ls1[BT], Ds0[BT], Ds1[BT];
 
   const int grp = a.H / a.Hk;
-  const int kh = blockIdx.y, hq = blockIdx.z, h = kh * grp + hq;
-  const int k0 = blockIdx.x * 128;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin; remap so
+  // that each XCD takes a contiguous range of logical blocks ordered key head,
+  // query head, key block. The key blocks of a query head then read that
+  // head's query and output-gradient rows through one L2.
+  int kh, hq, kb;
+  {
+    const int nkb = gridDim.x;
+    const int nwg = gridDim.x * gridDim.y * gridDim.z;
+    int id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+    const int per_kh = grp * nkb;
+    kh = id / per_kh;
+    const int rem = id % per_kh;
+    hq = rem / nkb;
+    kb = rem % nkb;
+  }
+  const int h = kh * grp + hq;
+  const int k0 = kb * 128;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
   const int kw = k0 + wid * 32;
