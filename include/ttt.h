@@ -194,8 +194,11 @@ ttt_status ttt_timing_read(ttt_ctx* ctx, int32_t kclass, double* total_ms, int64
  * W, M: device float [H, D, D], 16-byte aligned, updated in place to the
  * state after the last chunk. D must be 128 or 64; C a multiple of 64, at
  * most 2048; T >= 1. Errors: TTT_ERR_UNSUPPORTED for other D or C,
- * TTT_ERR_INVALID_ARG for null or misaligned pointers. The call keeps a
- * device work buffer per process (grown on demand). */
+ * TTT_ERR_INVALID_ARG for null or misaligned pointers. The call keeps one
+ * device work buffer per process (grown on demand; growing it waits for the
+ * calling stream), so calls must not run concurrently on different streams
+ * or host threads: a later call may only start once the earlier one's work
+ * on its stream is ordered before it. */
 ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float* eta, const float* beta,
                             const float* gamma, float* W, float* M, int32_t H, int64_t T,
                             int32_t D, int32_t C, void* stream);

@@ -20,6 +20,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/ttt.h"
 #include "common.hpp"
@@ -367,6 +368,7 @@ struct E2Scratch {
   int dev = -1;
 };
 E2Scratch g_e2;
+std::mutex g_e2_mu;  // guards g_e2 on the host
 }  // namespace
 
 extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float* eta, const float* beta,
@@ -389,6 +391,7 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
   // Work buffer cached per process (grown on demand, reallocated on a device change).
+  std::lock_guard<std::mutex> lock(g_e2_mu);
   if (g_e2.bytes < need || g_e2.dev != dev) {
     if (g_e2.p) {
       (void)hipStreamSynchronize(st);
