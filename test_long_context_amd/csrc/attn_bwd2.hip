@@ -417,15 +417,16 @@ bool attn_bwd2_supported(DT dt, const AttnArgs& a) {
 }
 
 int attn_bwd2_dq_parts(const AttnArgs& a) {
-  // key-range parts (1..4, at least 8 key tiles each) minimising the per-CU
-  // load ceil(base s / 256) / s, with a small charge per part for the
-  // partial sums (as for the forward's key splits)
+  // key-range parts (1..ATTN_BWD2_MAX_DQ_PARTS, at least 8 key tiles each)
+  // minimising the load per workgroup slot, ceil(base s / 512) / s (two
+  // workgroups fit on each of the 256 CUs), with a small charge per part for
+  // the partial sums (as for the forward's key splits)
   const long base = (long)((a.n + 127) / 128) * a.H;
   const long tiles = (a.window + 128 + BT - 1) / BT + 1;
   int best = 1;
   double best_cost = 1e30;
-  for (int s = 1; s <= 4 && (s == 1 || s <= tiles / 8); ++s) {
-    const double cost = (double)((base * s + 255) / 256) / s + 0.02 * s;
+  for (int s = 1; s <= ATTN_BWD2_MAX_DQ_PARTS && (s == 1 || s <= tiles / 8); ++s) {
+    const double cost = (double)((base * s + 511) / 512) / s + 0.02 * s;
     if (cost < best_cost) {
       best_cost = cost;
       best = s;

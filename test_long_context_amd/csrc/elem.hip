@@ -496,7 +496,7 @@ __global__ void rope_bwd_generic_kernel(const float* dq, int dq_parts, const flo
 // consecutive pairs of one head; ROPE_BKR at most) and the i-th group of 4
 // value-gradient elements; the loads of every partial are issued before the
 // first store. At most ROPE_BNP partials per side (rope_bwd_pack chooses).
-constexpr int ROPE_BKR = 2, ROPE_BNP = 4;
+constexpr int ROPE_BKR = 2, ROPE_BNP = 8;
 template <typename T>
 __global__ void __launch_bounds__(RB) rope_bwd_kernel(const float* dq, int dq_parts, const float* dk, const float* dv,
                                                       int kv_parts, int n, int H, int Hk, int dh, int64_t pos0,

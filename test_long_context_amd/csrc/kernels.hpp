@@ -145,6 +145,8 @@ hipError_t attn_bwd_dkdv(DT dt, const AttnArgs& a, hipStream_t st);
 // query head of the group.
 bool attn_bwd2_supported(DT dt, const AttnArgs& a);
 int attn_bwd2_dq_parts(const AttnArgs& a);
+// Upper bound of attn_bwd2_dq_parts().
+constexpr int ATTN_BWD2_MAX_DQ_PARTS = 8;
 int attn_bwd2_kv_parts(const AttnArgs& a);
 hipError_t attn_bwd_dq2(DT dt, const AttnArgs& a, hipStream_t st);
 hipError_t attn_bwd_dkdv2(DT dt, const AttnArgs& a, hipStream_t st);
