@@ -756,8 +756,9 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   Af(&c->part, (size_t)c->max_split * b * d);
   A(&c->dO, (size_t)b * c->H * c->dh * es);
   Af(&c->Dbuf, (size_t)c->H * b);
-  // room for the partial sums of the second-generation backward (at most 4
-  // key splits of dq; one dk / dv part per query head of a group)
+  // room for the partial sums of the second-generation backward (at most
+  // ATTN_BWD2_MAX_DQ_PARTS key splits of dq; one dk / dv part per query head
+  // of a group)
   Af(&c->dq, (size_t)ATTN_BWD2_MAX_DQ_PARTS * b * c->H * c->dh);
   Af(&c->apart, (size_t)4 * b * c->H * c->dh);
   Af(&c->aml, (size_t)4 * 2 * c->H * b);
