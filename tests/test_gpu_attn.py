@@ -28,6 +28,8 @@ CASES = [
     (150, 6, 2, 64, 512, 64, 300),     # window shorter than the call
     (130, 4, 4, 128, 512, 128, 0),     # first call: only its own keys
     (64, 3, 1, 64, 128, 40, 1000),     # window ends inside one key tile
+    (256, 24, 8, 128, 8192, 4096, 5000),  # many heads, long window: the dq key range
+                                          # splits into more than four parts
 ]
 
 
