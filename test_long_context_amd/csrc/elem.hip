@@ -70,8 +70,15 @@ __device__ __forceinline__ float4 f4add(float4 a, float4 b) { return make_float4
 // Row-sum of a float4 chunk set: a[i] += sum_p src[p * stride][chunk i]
 // for p < np, the loads of four partials issued together before any add
 // (one memory round trip per four partials, not one per load).
-template <int NVT>
-__device__ __forceinline__ void rms_add_parts(float4 (&a)[NVT], const float* src, long stride, int np, long row,
+// 4 consecutive partial values at vector index v (float or bf16 storage)
+__device__ __forceinline__ float4 ld_part4(const float* p, int v) { return ((const float4*)p)[v]; }
+__device__ __forceinline__ float4 ld_part4(const bf16* p, int v) {
+  const bf16x4 h = ((const bf16x4*)p)[v];
+  return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+}
+
+template <int NVT, typename PT = float>
+__device__ __forceinline__ void rms_add_parts(float4 (&a)[NVT], const PT* src, long stride, int np, long row,
                                               int nv) {
   int p = 0;
   for (; p + 4 <= np; p += 4) {
@@ -81,7 +88,7 @@ __device__ __forceinline__ void rms_add_parts(float4 (&a)[NVT], const float* src
 #pragma unroll
       for (int i = 0; i < NVT; ++i) {
         const int v = threadIdx.x + i * RB;
-        if (v < nv) t[u][i] = ((const float4*)(src + (p + u) * stride + row))[v];
+        if (v < nv) t[u][i] = ld_part4(src + (p + u) * stride + row, v);
       }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -94,7 +101,7 @@ __device__ __forceinline__ void rms_add_parts(float4 (&a)[NVT], const float* src
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
       const int v = threadIdx.x + i * RB;
-      if (v < nv) t[i] = ((const float4*)(src + p * stride + row))[v];
+      if (v < nv) t[i] = ld_part4(src + p * stride + row, v);
     }
 #pragma unroll
     for (int i = 0; i < NVT; ++i)
@@ -189,8 +196,8 @@ hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, floa
 // sum of nsplit partials. Every input of the row (the partials, g, x and,
 // when accumulating, dh) is requested before the first use and kept in
 // registers (NVT float4 chunks per thread, as in the forward).
-template <typename T, int NVT>
-__global__ void __launch_bounds__(RB) rms_bwd_kernel(const float* dy, int nsplit, long sstride, const float* x,
+template <typename T, int NVT, typename PT>
+__global__ void __launch_bounds__(RB) rms_bwd_kernel(const PT* dy, int nsplit, long sstride, const float* x,
                                                      const float* g, const float* r, int d, float* dh, T* dh_t,
                                                      int acc) {
   __shared__ float sh[RB / 64];
@@ -202,13 +209,13 @@ __global__ void __launch_bounds__(RB) rms_bwd_kernel(const float* dy, int nsplit
   for (int i = 0; i < NVT; ++i) {
     const int v = threadIdx.x + i * RB;
     if (v < nv) {
-      a[i] = ((const float4*)(dy + t * d))[v];
+      a[i] = ld_part4(dy + t * d, v);
       gv[i] = ((const float4*)g)[v];
       xv[i] = ((const float4*)(x + t * d))[v];
       if (acc) hv[i] = ((const float4*)(dh + t * d))[v];
     }
   }
-  rms_add_parts<NVT>(a, dy + sstride, sstride, nsplit - 1, t * d, nv);
+  rms_add_parts<NVT, PT>(a, dy + sstride, sstride, nsplit - 1, t * d, nv);
   float dot = 0.f;
 #pragma unroll
   for (int i = 0; i < NVT; ++i)
@@ -232,37 +239,42 @@ __global__ void __launch_bounds__(RB) rms_bwd_kernel(const float* dy, int nsplit
   }
 }
 
-template <typename T, int NVT>
-static void rms_bwd_launch(const float* dy, int nsplit, long ss, const float* x, const float* g, const float* r,
+template <typename T, int NVT, typename PT>
+static void rms_bwd_launch(const PT* dy, int nsplit, long ss, const float* x, const float* g, const float* r,
                            int n, int d, float* dh, T* dh_t, int acc, hipStream_t st) {
-  hipLaunchKernelGGL((rms_bwd_kernel<T, NVT>), dim3(n), dim3(RB), 0, st, dy, nsplit, ss, x, g, r, d, dh, dh_t, acc);
+  hipLaunchKernelGGL((rms_bwd_kernel<T, NVT, PT>), dim3(n), dim3(RB), 0, st, dy, nsplit, ss, x, g, r, d, dh, dh_t,
+                     acc);
 }
 
-template <typename T>
-static hipError_t rms_bwd_t(const float* dy, int nsplit, long ss, const float* x, const float* g, const float* r,
+template <typename T, typename PT>
+static hipError_t rms_bwd_t(const PT* dy, int nsplit, long ss, const float* x, const float* g, const float* r,
                             int n, int d, float* dh, T* dh_t, int acc, hipStream_t st) {
   const int nvt = (d / 4 + RB - 1) / RB;
   switch (nvt) {
-    case 1: rms_bwd_launch<T, 1>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
-    case 2: rms_bwd_launch<T, 2>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
-    case 3: rms_bwd_launch<T, 3>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
-    case 4: rms_bwd_launch<T, 4>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 1: rms_bwd_launch<T, 1, PT>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 2: rms_bwd_launch<T, 2, PT>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 3: rms_bwd_launch<T, 3, PT>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 4: rms_bwd_launch<T, 4, PT>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
     case 5:
-    case 6: rms_bwd_launch<T, 6>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 6: rms_bwd_launch<T, 6, PT>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
     case 7:
-    case 8: rms_bwd_launch<T, 8>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
+    case 8: rms_bwd_launch<T, 8, PT>(dy, nsplit, ss, x, g, r, n, d, dh, dh_t, acc, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const float* g, const float* r, int n,
-                       int d, float* dh, void* dh_t, int accumulate, hipStream_t st) {
+hipError_t rmsnorm_bwd(DT dt, const void* dy, bool dy_bf16, int nsplit, const float* x, const float* g,
+                       const float* r, int n, int d, float* dh, void* dh_t, int accumulate, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   if (d % 4 || nsplit < 1 || d > 4 * RB * RMS_MAXV) return hipErrorInvalidValue;
   const long ss = (long)n * d;
-  if (dt == DT::BF16) return rms_bwd_t<bf16>(dy, nsplit, ss, x, g, r, n, d, dh, (bf16*)dh_t, accumulate, st);
-  return rms_bwd_t<float>(dy, nsplit, ss, x, g, r, n, d, dh, (float*)dh_t, accumulate, st);
+  if (dt == DT::BF16) {
+    if (dy_bf16) return rms_bwd_t<bf16>((const bf16*)dy, nsplit, ss, x, g, r, n, d, dh, (bf16*)dh_t, accumulate, st);
+    return rms_bwd_t<bf16>((const float*)dy, nsplit, ss, x, g, r, n, d, dh, (bf16*)dh_t, accumulate, st);
+  }
+  if (dy_bf16) return hipErrorInvalidValue;
+  return rms_bwd_t<float>((const float*)dy, nsplit, ss, x, g, r, n, d, dh, (float*)dh_t, accumulate, st);
 }
 
 // -------------------------------------------------------------------- RoPE

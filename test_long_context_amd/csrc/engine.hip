@@ -309,7 +309,10 @@ ttt_status gemm_nn_split(ttt_ctx* c, int kind, const void* A, long lda, const vo
   g.kchunk = chunk;
   if (c->dt == DT::BF16) g.tile = 5;
   *nsplit = s;
-  TCALL(kind, gfl(M, N, K), 0, gemm(c->dt, true, false, Epi::PARTIAL, g, st));
+  // bf16: the gradient partials are stored in bf16 (half the traffic of
+  // writing them here and reading them back in the RMSNorm backward)
+  const Epi e = c->dt == DT::BF16 ? Epi::PARTIAL_BF16 : Epi::PARTIAL;
+  TCALL(kind, gfl(M, N, K), 0, gemm(c->dt, true, false, e, g, st));
   return TTT_OK;
 }
 
@@ -470,7 +473,7 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
   const int nd = c->nd;
   // lm_head^T and the final norm
   RUN(gemm_nn_split(c, KC_LM, c->dz, c->V, c->lm_head, d, n, d, c->V, c->part, &ns, st));
-  TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_f, c->final_norm, c->r_f, n, d, c->gh, c->ghd_t[nd - 1], 0, st));
+  TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_f, c->final_norm, c->r_f, n, d, c->gh, c->ghd_t[nd - 1], 0, st));
   for (int l = c->L - 1; l >= s; --l) {
     const int i = l - s;
     void* gt = c->ghd_t[i];
@@ -507,14 +510,14 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
     }
     if (l == s) break;
-    TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], n, d, c->gh, c->gh_t, 1, st));
+    TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], n, d, c->gh, c->gh_t, 1, st));
     // static MLP
     {
       GemmArgs g = ga(c->gh_t, d, c->w3[l], F, n, F, d, c->dh12, 2 * F);
       g.X = c->h12_s[i];
       TCALL(KC_GL, gfl(n, F, d), 0, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
       RUN(gemm_nn_split(c, KC_GL, c->dh12, 2 * F, c->w12[l], d, n, d, 2 * F, c->part, &ns, st));
-      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_mlp[i], c->mlp_norm[l], c->r_mlp[i], n, d, c->gh, c->gh_t, 1, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_mlp[i], c->mlp_norm[l], c->r_mlp[i], n, d, c->gh, c->gh_t, 1, st));
     }
     // attention
     {
@@ -539,7 +542,7 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       }
       TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, c->dq, qp, c->dk, c->dv, kp, n, H, Hk, dh, a0, c->rope, c->dqkv, st));
       RUN(gemm_nn_split(c, KC_GL, c->dqkv, QKV, c->wqkv[l], d, n, d, QKV, c->part, &ns, st));
-      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->ghd_t[i - 1], 1, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->ghd_t[i - 1], 1, st));
     }
   }
   // the next mini-batch's forward waits for each block's update just before

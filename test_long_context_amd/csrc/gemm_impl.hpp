@@ -163,6 +163,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, floatx4 (&acc)[
             ((float*)g.C)[idx] += a;
           } else if constexpr (EPI == (int)Epi::PARTIAL) {
             ((float*)g.C)[(long)blockIdx.z * g.M * g.ldc + idx] = a;
+          } else if constexpr (EPI == (int)Epi::PARTIAL_BF16) {
+            ((bf16*)g.C)[(long)blockIdx.z * g.M * g.ldc + idx] = (bf16)a;
           } else if constexpr (EPI == (int)Epi::SGD) {
             float* W = (float*)g.C;
             const float w = W[idx] - g.scale * a;
@@ -428,6 +430,10 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& g, int m, int n, float
     float* C = (float*)g.C + idx + (EPI == (int)Epi::PARTIAL ? (long)blockIdx.z * g.M * g.ldc : 0);
     if (vec) *(floatx4*)C = v;
     else for (int e = 0; e < ne; ++e) C[e] = v[e];
+  } else if constexpr (EPI == (int)Epi::PARTIAL_BF16) {
+    bf16* C = (bf16*)g.C + idx + (long)blockIdx.z * g.M * g.ldc;
+    if (vec) *(bf16x4*)C = cvt4(v);
+    else for (int e = 0; e < ne; ++e) C[e] = (bf16)v[e];
   } else if constexpr (EPI == (int)Epi::ADD_F32) {
     float* C = (float*)g.C + idx;
     if (vec) *(floatx4*)C = pre + v;
@@ -773,6 +779,7 @@ static hipError_t gemm_by_epi(Epi e, int cfg, const GemmArgs& g, hipStream_t st)
     case Epi::SWIGLU_BWD: return gemm_cfg<T, AK, BKM, (int)Epi::SWIGLU_BWD, false>(cfg, g, st);
     case Epi::SGD: return gemm_cfg<T, AK, BKM, (int)Epi::SGD, false>(cfg, g, st);
     case Epi::PARTIAL: return gemm_cfg<T, AK, BKM, (int)Epi::PARTIAL, false>(cfg, g, st);
+    default: break;  // PARTIAL_BF16: bf16 NN only (gemm_nn)
   }
   return hipErrorInvalidValue;
 }

@@ -28,6 +28,7 @@ enum class Epi : int {
   SGD,          // C (float master) -= scale * acc; C2 (T) = round(master),
                 // C3 (T, optional) = round(master - C2)
   PARTIAL,      // C (float) [split][M][ldc] = acc  (split-K)
+  PARTIAL_BF16, // C (bf16) [split][M][ldc] = acc  (split-K gradient partials; bf16 NN only)
 };
 
 struct GemmArgs {
@@ -63,8 +64,9 @@ hipError_t rmsnorm_fwd_fused(DT dt, const float* x_in, const float* parts, int n
 hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, float eps, void* y,
                        float* r, hipStream_t st);
 // dh[t] += rmsnorm_bwd(dy[t]) where dy = sum over nsplit partials of
-// [n, d] float (stride n*d); writes dh (float) and dh_t (T copy).
-hipError_t rmsnorm_bwd(DT dt, const float* dy, int nsplit, const float* x, const float* g,
+// [n, d] (stride n*d), float or, with dy_bf16, bf16; writes dh (float) and
+// dh_t (T copy).
+hipError_t rmsnorm_bwd(DT dt, const void* dy, bool dy_bf16, int nsplit, const float* x, const float* g,
                        const float* r, int n, int d, float* dh, void* dh_t, int accumulate,
                        hipStream_t st);
 // Apply RoPE to q and k of a fused qkv buffer [n, (H + 2Hk) dh] (T) at
