@@ -79,12 +79,25 @@ typedef struct {
   int32_t window;         /* k, >= minibatch */
   int32_t minibatch;      /* b >= 1: tokens per SGD step */
   int32_t n_dynamic;      /* updated blocks (the last n_dynamic); 0 => L - (3L)/4 */
-  int32_t max_seq;        /* largest position + 1 ever used (prefill + decode) */
+  int32_t max_seq;        /* largest position + 1 ever used (prefill + decode); a
+                           * window above max(max_seq, minibatch) is clamped to it
+                           * (no query can see more keys) */
   float alpha;            /* SGD step size, finite, >= 0 */
   float rms_eps;          /* RMSNorm epsilon, > 0 */
   float rope_theta;       /* RoPE base, > 1 */
   int32_t dtype;          /* ttt_dtype of weights and activations */
   int32_t reduction;      /* ttt_reduction of each mini-batch's loss */
+  int32_t prefix_slab;    /* positions per slab of the frozen prefix (the blocks
+                           * that precede the first fast weight run once over
+                           * the whole stream, slab by slab); 0 => min(max_seq,
+                           * 16384); raised to minibatch, lowered to max_seq. The
+                           * per-layer key/value ring holds cap = next power of
+                           * two >= max(window + max(minibatch, slab), 128)
+                           * positions (slot = position mod cap), so a small slab
+                           * gives a small ring that is reused sooner; results do
+                           * not depend on it. Negative => TTT_ERR_INVALID_ARG;
+                           * a ring slice of one key head of 2^31 bytes or more
+                           * => TTT_ERR_UNSUPPORTED. */
 } ttt_config;
 
 /* Weights (device pointers, storage dtype). Per-layer fields are host arrays

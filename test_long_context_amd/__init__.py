@@ -35,7 +35,7 @@ class Config(ctypes.Structure):
                 ("n_dynamic", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("reduction", ctypes.c_int32)]
+                ("reduction", ctypes.c_int32), ("prefix_slab", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -113,7 +113,8 @@ def make_config(c: dict, max_seq: Optional[int] = None) -> Config:
                   max_seq=int(max_seq if max_seq is not None else c.get("max_seq", c["seq"])),
                   alpha=float(c["alpha"]), rms_eps=float(c["rms_eps"]),
                   rope_theta=float(c["rope_theta"]), dtype=0 if c["dtype"] == "f32" else 1,
-                  reduction=0 if c.get("reduction", "mean") == "mean" else 1)
+                  reduction=0 if c.get("reduction", "mean") == "mean" else 1,
+                  prefix_slab=int(c.get("prefix_slab", 0)))
 
 
 def _ptr(t) -> int:

@@ -214,6 +214,19 @@ bool dalloc_t(ttt_ctx* c, P** p, size_t bytes) {
   return ok;
 }
 
+// Effective window (a window longer than any stream cannot see more keys),
+// prefix slab and ring capacity of a config.
+int64_t eff_window(const ttt_config& c) {
+  return std::min<int64_t>(c.window, std::max<int64_t>(c.max_seq, c.minibatch));
+}
+void ring_shape(const ttt_config& c, int64_t* slab, int64_t* cap) {
+  int64_t s = c.prefix_slab > 0 ? std::min<int64_t>(c.prefix_slab, c.max_seq)
+                                : std::min<int64_t>(c.max_seq, 16384);
+  s = std::max<int64_t>(s, c.minibatch);
+  *slab = s;
+  *cap = next_pow2(std::max<int64_t>(eff_window(c) + s, 128));
+}
+
 ttt_status validate(const ttt_config* cfg) {
   if (!cfg) return TTT_ERR_INVALID_ARG;
   const ttt_config& c = *cfg;
@@ -221,7 +234,7 @@ ttt_status validate(const ttt_config* cfg) {
   if (c.reduction != TTT_LOSS_MEAN && c.reduction != TTT_LOSS_SUM) return TTT_ERR_INVALID_ARG;
   if (c.n_layers < 1 || c.d_model < 1 || c.n_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 ||
       c.ffn_hidden < 1 || c.dyn_ffn_hidden < 1 || c.vocab < 2 || c.minibatch < 1 ||
-      c.max_seq < 2 || c.n_dynamic < 0 || c.n_dynamic > c.n_layers)
+      c.max_seq < 2 || c.n_dynamic < 0 || c.n_dynamic > c.n_layers || c.prefix_slab < 0)
     return TTT_ERR_INVALID_ARG;
   if (c.window < c.minibatch) return TTT_ERR_INVALID_ARG;  // k >= b
   if (!(c.alpha >= 0.f) || !isfinite(c.alpha) || !(c.rms_eps > 0.f) || !(c.rope_theta > 1.f))
@@ -233,6 +246,11 @@ ttt_status validate(const ttt_config* cfg) {
   if (c.d_model > 8192) return TTT_ERR_UNSUPPORTED;  // a residual row stays in one workgroup's registers
   if ((int64_t)c.max_seq > (int64_t(1) << 30)) return TTT_ERR_UNSUPPORTED;
   if ((int64_t)c.vocab * c.d_model > (int64_t(1) << 31)) return TTT_ERR_UNSUPPORTED;
+  // one key head's slice of a ring is addressed with 32-bit byte offsets
+  int64_t slab = 0, cap = 0;
+  ring_shape(c, &slab, &cap);
+  const int64_t es = c.dtype == TTT_BF16 ? 2 : 4;
+  if (cap * c.head_dim * es >= (int64_t(1) << 31)) return TTT_ERR_UNSUPPORTED;
   return TTT_OK;
 }
 
@@ -641,15 +659,13 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   c->F = cfg->ffn_hidden;
   c->Fd = cfg->dyn_ffn_hidden;
   c->V = cfg->vocab;
-  c->k = cfg->window;
+  c->k = (int)eff_window(*cfg);
   c->b = cfg->minibatch;
   c->nd = nd0;
   c->s = c->L - c->nd;
   c->max_seq = cfg->max_seq;
   c->QKV = (c->H + 2 * c->Hk) * c->dh;
-  c->slab = std::min<int64_t>(c->max_seq, 16384);
-  c->slab = std::max<int64_t>(c->slab, c->b);
-  c->cap = next_pow2(std::max<int64_t>((int64_t)c->k + std::max<int64_t>(c->b, c->slab), 128));
+  ring_shape(*cfg, &c->slab, &c->cap);
   c->max_split = 16;
   const size_t es = c->es;
   const int d = c->d, L = c->L, nd = c->nd, b = c->b;

@@ -10,7 +10,7 @@ import torch
 
 import synth
 from oracle import ttt_e2e as O
-from tests.util import dw_err, rel_loss_err, say, to_device
+from tests.util import dw_err, rel_loss_err, ring_capacity, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def check(c, T):
     assert max(errs) < W_TOL
 
 
-def test_bf16_small_gqa_dh128_ring_wrap():
+def test_bf16_small_gqa_dh128():
     c = synth.config("125m", n_layers=4, d_model=256, n_heads=4, n_kv_heads=2, head_dim=128,
                      ffn_hidden=512, dyn_ffn_hidden=512, vocab=4096, window=256, minibatch=128,
                      n_dynamic=2, alpha=0.01)
@@ -74,34 +74,76 @@ def test_generator_cpu_gpu_identical():
     assert torch.equal(ta, tb)
 
 
-def check_stored(fname, workload, ntok, label):
-    """GPU prefill of the workload's first ntok tokens against values written
-    by tests/golden/make_golden.py (oracle only): losses of every position and
-    4096 sampled coordinates of every fast-weight matrix after the last
-    update, normalised by max |W_T - W0| over the matrix."""
-    import test_long_context_amd as tla
-    g = np.load(os.path.join(HERE, "golden", fname), allow_pickle=False)
-    c = synth.config(workload)
-    w = synth.gen_weights(c, device="cuda")
-    tok = synth.gen_tokens(c, n=ntok(c), device="cuda")
-    assert np.array_equal(tok.cpu().numpy(), g["tokens"])
-    assert np.array_equal(w["embed"][:4, :8].float().cpu().numpy(), g["embed_head"])
-    m = tla.TTT(c, w, max_seq=c["seq"] + 1024)
-    loss = m.prefill(tok)
-    m.sync()
-    le = rel_loss_err(loss.cpu().numpy(), g["loss"])
-    nd = c["n_dynamic"] or (c["n_layers"] - (3 * c["n_layers"]) // 4)
-    errs = []
+def check_fast_weights(m, g, nd, w):
+    """Fast weights after the last update against the stored oracle record:
+    4096 sampled coordinates per matrix and, where stored, the maximum of
+    |W_T - W0| over every row and every column (a wrong row or column moves
+    its maximum whichever entries the samples hit). Errors are normalised by
+    max |W_T - W0| over the matrix; |max|a| - max|b|| <= max|a - b|, so the
+    extrema errors never exceed the full-matrix error."""
+    errs, ext = [], []
     for i in range(nd):
         ws = m.fast_weights(i)
         for k, W in zip(("w1", "w2", "w3"), ws):
+            den = float(g[f"d{i}_{k}_den"])
             idx = torch.from_numpy(g[f"d{i}_{k}_idx"]).cuda()
             got = W.reshape(-1)[idx].cpu().numpy().astype(np.float64)
-            errs.append(float(np.max(np.abs(got - g[f"d{i}_{k}_val"])) / g[f"d{i}_{k}_den"]))
+            errs.append(float(np.max(np.abs(got - g[f"d{i}_{k}_val"]))) / den)
+            if f"d{i}_{k}_rowmax" in g:
+                w0 = w["dyn"][i][k]
+                dW = (W.double() - w0.double()).abs()
+                rmax = dW.amax(dim=1).cpu().numpy()
+                cmax = dW.amax(dim=0).cpu().numpy()
+                ext.append(max(float(np.max(np.abs(rmax - g[f"d{i}_{k}_rowmax"]))),
+                               float(np.max(np.abs(cmax - g[f"d{i}_{k}_colmax"])))) / den)
+            del ws
+    return errs, ext
+
+
+def check_stored(fname, workload, ntok, label, prefix_slab=0):
+    """GPU prefill of the workload's first ntok tokens against values written
+    by tests/golden/make_golden.py (oracle only): losses of every position and
+    4096 sampled coordinates of every fast-weight matrix after the last
+    update, normalised by max |W_T - W0| over the matrix (and the row and
+    column maxima of the update where the file holds them); then any decode
+    steps the file holds."""
+    import test_long_context_amd as tla
+    g = np.load(os.path.join(HERE, "golden", fname), allow_pickle=False)
+    c = synth.config(workload, prefix_slab=prefix_slab)
+    ndec = len(g["tokens"]) - int(g["prefill_len"]) if "prefill_len" in g else 0
+    T = len(g["tokens"]) - ndec
+    assert T == ntok(c)
+    w = synth.gen_weights(c, device="cuda")
+    tok = synth.gen_tokens(c, n=T + ndec, device="cuda")
+    assert np.array_equal(tok.cpu().numpy(), g["tokens"])
+    assert np.array_equal(w["embed"][:4, :8].float().cpu().numpy(), g["embed_head"])
+    max_seq = c["seq"] + 1024 if not prefix_slab else T + ndec + 1
+    cap = ring_capacity(c, max_seq)
+    say(f"  {label}: ring of {cap} slots for {T + ndec} positions")
+    m = tla.TTT(c, w, max_seq=max_seq)
+    loss = m.prefill(tok[:T])
+    m.sync()
+    le = rel_loss_err(loss.cpu().numpy(), g["loss"])
+    nd = c["n_dynamic"] or (c["n_layers"] - (3 * c["n_layers"]) // 4)
+    errs, ext = check_fast_weights(m, g, nd, w)
+    say(f"  {label}: loss rel err {le:.3e}  sampled W_T err {max(errs):.3e}"
+        + (f"  row/col max err {max(ext):.3e}" if ext else ""))
+    zerr = []
+    for j in range(ndec):
+        z = m.decode_step(tok[T + j:T + j + 1]).cpu().numpy().astype(np.float64)
+        den = float(g[f"z{j}_absmax"])
+        e_s = float(np.max(np.abs(z[g[f"z{j}_idx"]] - g[f"z{j}_val"]))) / den
+        e_t = float(np.max(np.abs(z[g[f"z{j}_top_idx"]] - g[f"z{j}_top_val"]))) / den
+        say(f"  {label} decode step {j} (slot {(T + j) % cap}): sampled logit err {e_s:.3e}  top-16 err {e_t:.3e}")
+        assert np.all(np.isfinite(z))
+        zerr.append((e_s, e_t, int(np.argmax(z)) in set(g[f"z{j}_top_idx"].tolist())))
     m.close()
-    say(f"  {label}: loss rel err {le:.3e}  sampled W_T err {max(errs):.3e}")
     assert le < LOSS_TOL
     assert max(errs) < W_TOL
+    assert not ext or max(ext) < W_TOL
+    for e_s, e_t, top_ok in zerr:
+        assert e_s < 2e-2 and e_t < 2e-2 and top_ok
+    return cap
 
 
 def _stored(fname):
@@ -121,6 +163,19 @@ def test_bf16_3b_full_shape_eight_minibatches_against_stored_oracle_values():
     """Full 3B shapes: the first 8 mini-batches of the stream and their
     updates (each mini-batch under the previous one's fast weights)."""
     check_stored("ttt_3b_8minibatches.npz", "3b", lambda c: 8 * c["minibatch"] + 1, "3b 8 mini-batches")
+
+
+@_stored("ttt_3b_16minibatches.npz")
+def test_bf16_3b_full_shape_sixteen_minibatches_ring_reused_against_stored_oracle_values():
+    """Full 3B shapes over the first 16 mini-batches: 8 that fill the
+    8192-key window, then 8 with the window sliding across mini-batch edges
+    (every query sees 8192 keys), the forward-only position 16384 and 3
+    decode steps. A prefix slab of 1024 gives a 16384-slot ring, so position
+    16384 and the decode steps reuse slots of positions 0..3 while the
+    window reads across the wrap."""
+    cap = check_stored("ttt_3b_16minibatches.npz", "3b", lambda c: 16 * c["minibatch"] + 1,
+                       "3b 16 mini-batches", prefix_slab=1024)
+    assert cap == 16384
 
 
 @_stored("ttt_1b_full.npz")
@@ -158,3 +213,29 @@ def test_bf16_3b_decode_full_window_against_stored_oracle_values():
         assert e_s < 2e-2 and e_t < 2e-2
         assert int(np.argmax(z)) in set(g[f"z{j}_top_idx"].tolist())
     m.close()
+
+
+def test_bf16_3b_shape_two_minibatches_repeat_bitwise():
+    """Two prefills of the same 2049 tokens at the full 3B shapes (bench
+    launch configuration: side streams, split-K partials, key-split
+    attention) after ttt_reset give identical losses and fast weights, bit
+    for bit: every sum on the path is taken in a fixed order."""
+    import test_long_context_amd as tla
+    c = synth.config("3b")
+    T = 2 * c["minibatch"] + 1
+    say(f"case: 3b shape, {T} tokens, two prefills")
+    w = synth.gen_weights(c, device="cuda")
+    tok = synth.gen_tokens(c, n=T, device="cuda")
+    m = tla.TTT(c, w, max_seq=c["seq"] + 1024)
+    runs = []
+    for _ in range(2):
+        m.reset()
+        loss = m.prefill(tok)
+        m.sync()
+        runs.append((loss.clone(), [tuple(x.clone() for x in m.fast_weights(i)) for i in range(c["n_dynamic"])]))
+    m.close()
+    assert bool(torch.isfinite(runs[0][0]).all())
+    assert torch.equal(runs[0][0], runs[1][0])
+    for a, b in zip(runs[0][1], runs[1][1]):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)

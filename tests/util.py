@@ -48,3 +48,15 @@ def dw_err(w_gpu, w_ref, w0):
 
 def say(msg):
     print(msg, flush=True)
+
+
+def ring_capacity(c: dict, max_seq: int) -> int:
+    """Positions held by each layer's key/value ring, by the rule that
+    include/ttt.h states for ttt_config.prefix_slab."""
+    b = c["minibatch"]
+    slab = c.get("prefix_slab", 0)
+    slab = min(slab, max_seq) if slab > 0 else min(max_seq, 16384)
+    slab = max(slab, b)
+    k = min(c["window"], max(max_seq, b))
+    need = max(k + slab, 128)
+    return 1 << (need - 1).bit_length()
