@@ -11,10 +11,13 @@ backward and SGD update) after ttt_reset; inputs are resident in HBM.
 
 Prints one JSON line: tokens/s, the fraction of the bf16 MFMA peak reached by
 the whole step (algorithmic FLOPs / time / 2.5 PFLOP/s), the live roofline of
-the dominant kernel -- the sliding-window attention forward (one kernel
-symbol, launched by the hoisted prefix and by every mini-batch), timed with
-HIP events on its launch stream during the timed steps -- and the CPU oracle
-timed on a bounded sample of the same workload.
+the dominant kernel -- the fused dW + fp32 SGD update product (the largest
+kernel symbol by summed duration in the step's rocprofv3 trace), timed with
+HIP events on its launch streams during the timed steps, against the HBM
+roofline of the update's algorithmic bytes -- the HBM rates of the
+cross-entropy and update kernels, a per-class table from the warm-up step,
+and the CPU oracle timed on a bounded sample of the same workload (one
+steady-state mini-batch).
 
 Counter runs (each under `rocprofv3 --pmc FETCH_SIZE`, then WRITE_SIZE):
 `--copy-probe` runs a plain 1 GiB device copy (the factor that turns the
@@ -46,7 +49,9 @@ PEAK_HBM_GBS = 8000.0
 # timing classes of the library (ttt_kernel_class in include/ttt.h)
 KC = dict(gemm_prefix=0, attn_prefix=1, gemm_loop=2, attn_loop=3, lmhead=4, ce=5, attn_bwd=6, dw_sgd=7,
           other=8)
-ROOF_CLASSES = ("attn_prefix", "attn_loop")   # the attention forward kernel
+ROOF_CLASS = "dw_sgd"                          # the fused dW + SGD update product
+ATTN_CLASSES = ("attn_prefix", "attn_loop")    # the attention forward kernel
+TIMED_CLASSES = (ROOF_CLASS, "ce") + ATTN_CLASSES
 ROOF_SOURCES = ("test_long_context_amd/csrc/attn2.hip", "test_long_context_amd/csrc/common.hpp")
 
 # HBM traffic of the attention forward from rocprofv3 --pmc FETCH_SIZE /
@@ -120,20 +125,41 @@ def _oracle_weights(w):
     return wn
 
 
-def cpu_baseline(c, w, tok, ntok):
-    """The oracle (float32 numpy) on the first mini-batch of the same stream."""
+def cpu_baseline(c, w, tok):
+    """The oracle (float32 numpy) on one steady-state mini-batch of the same
+    stream: positions [k, k + b) (the window then holds k earlier keys for
+    every query) run forward through every block, cross-entropy, backward
+    and the SGD step (oracle.ttt_e2e.minibatch_step), with the key/value
+    store of positions [0, k) filled with random values (the cost does not
+    depend on them). Tokens/s of that mini-batch is the oracle's rate in the
+    steady state, which is where a long stream spends almost all its time."""
     import numpy as np
     from oracle import ttt_e2e as O
     cores = _host_threads()
-    wn = _oracle_weights(w)
-    t = tok[: ntok + 1].cpu().numpy()
+    cfg = O.Cfg.from_dict(c)
+    T = tok.numel()
+    a = min(cfg.window, max(0, T - 2) // cfg.b * cfg.b)
+    e = min(a + cfg.b, T - 1)
+    wc = O._cast_weights(_oracle_weights(w), np.float32)
+    dyn = [{k: np.array(b_[k]) for k in ("w1", "w2", "w3")} for b_ in wc["dyn"]]
+    store = O.KVStore(cfg, e + 1, np.float32)
+    rng = np.random.default_rng(0)
+    for l in range(cfg.L):
+        store.K[l][:a] = rng.standard_normal((a, cfg.Hk, cfg.dh), dtype=np.float32)
+        store.V[l][:a] = rng.standard_normal((a, cfg.Hk, cfg.dh), dtype=np.float32)
+    store.n = a
+    t = tok[: e + 1].cpu().numpy().astype(np.int64)
+    loss = np.zeros(e, dtype=np.float32)
     t0 = time.perf_counter()
-    out = O.ttt_inner_loop(c, wn, t, dtype=np.float32)
+    O.minibatch_step(cfg, wc, dyn, store, t, a, e, cfg.alpha, cfg.reduction, loss)
     dt = time.perf_counter() - t0
-    assert np.all(np.isfinite(out["loss"]))
-    return dict(value=round(ntok / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"mini-batch 0 of the same stream: {ntok} positions forward + 1 SGD step, "
-                       f"plus the forward-only position {ntok}; {dt:.1f} s on the host",
+    assert np.all(np.isfinite(loss[a:e]))
+    n = e - a
+    return dict(value=round(n / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"one steady-state mini-batch: positions {a}..{e - 1} of the same stream, each query "
+                       f"seeing {'the full ' + str(cfg.window) + '-key window' if a >= cfg.window else 'every earlier key'} "
+                       f"(store of the {a} earlier positions filled with random values), forward through all "
+                       f"{cfg.L} blocks, cross-entropy, backward and the SGD step; {dt:.1f} s on the host",
                 seconds=round(dt, 2))
 
 
@@ -443,9 +469,10 @@ def main():
             print(f"# {x['kind']:12s} {x['ms']:9.2f} ms {100 * x['ms'] / tot:5.1f}%  launches {x['launches']:6d}"
                   f"  {eff:8.1f} TFLOP/s  {bw:8.1f} GB/s", file=sys.stderr)
 
-    # timed steps: events only around the attention forward launches
+    # timed steps: events around the launches of the update products (the
+    # roofline kernel), the cross-entropy and the attention forward
     mask = 0
-    for k in ROOF_CLASSES:
+    for k in TIMED_CLASSES:
         mask |= 1 << KC[k]
     m.timing_enable(mask)
     torch.cuda.synchronize()
@@ -458,7 +485,7 @@ def main():
     torch.cuda.synchronize()
     m.sync()
     ms = e0.elapsed_time(e1) / args.steps
-    parts = [m.timing_read(KC[k]) for k in ROOF_CLASSES]
+    live = {k: m.timing_read(KC[k]) for k in TIMED_CLASSES}
     m.timing_enable(0)
     assert bool(torch.isfinite(loss).all()), "non-finite loss"
     mean_loss = float(loss.mean())
@@ -466,23 +493,45 @@ def main():
     flops = algorithmic_flops(c, T)
     tps = T / (ms / 1e3)
     frac = flops / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
-    r_ms = sum(x["ms"] for x in parts)
-    r_fl = sum(x["flops"] for x in parts)
-    r_n = sum(x["launches"] for x in parts)
-    avg_s = r_ms / r_n * 1e-3
-    ach = r_fl / r_n / avg_s / 1e12
+
+    def rate(x, what):
+        """Average launch duration and the algorithmic rate per launch."""
+        n = max(1, x["launches"])
+        avg_s = x["ms"] / n * 1e-3
+        if what == "bytes":
+            return avg_s, x["bytes"] / n / avg_s / 1e9 if avg_s > 0 else 0.0
+        return avg_s, x["flops"] / n / avg_s / 1e12 if avg_s > 0 else 0.0
+
+    upd = live[ROOF_CLASS]
+    u_avg, u_gbs = rate(upd, "bytes")
+    nu = max(1, upd["launches"])
+    roof = dict(bound="hbm", achieved=round(u_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(u_gbs / PEAK_HBM_GBS, 4), traffic=None,
+                kernel="fused dW = X^T dH product with the fp32 SGD update of the fast weights in its epilogue "
+                       "(gemm_bf16_kernel, SGD epilogue)",
+                algorithmic_bytes_per_launch=round(upd["bytes"] / nu),
+                algorithmic_unit="10 bytes per fast-weight parameter: fp32 master read + write, bf16 working copy",
+                launches_per_step=upd["launches"] // args.steps, avg_launch_us=round(u_avg * 1e6, 2),
+                mfma_tflops=round(upd["flops"] / nu / u_avg / 1e12, 1) if u_avg > 0 else None,
+                share_of_step=round(upd["ms"] / args.steps / ms, 4),
+                note="durations measured on the update's side streams, beside the main stream's kernels")
+    ce = live["ce"]
+    c_avg, c_gbs = rate(ce, "bytes")
+    attn = {k: sum(live[a][k] for a in ATTN_CLASSES) for k in ("ms", "launches", "flops", "bytes")}
+    a_avg, a_tfs = rate(attn, "flops")
     src = roof_source_hash()
     tr = TRAFFIC.get((args.workload, T, src))
-    traffic = None if tr is None else tr["traffic_bytes_per_launch"]
-    busy = MFMA_BUSY.get((args.workload, T, src))
-    roof = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=traffic,
-                kernel=f"attn_fwd2_kernel (sliding-window attention forward, head_dim {c['head_dim']})",
-                traffic_unit="bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
-                launches_per_step=r_n // args.steps, avg_launch_us=round(avg_s * 1e6, 2),
-                algorithmic_gflop_per_launch=round(r_fl / r_n / 1e9, 3),
-                share_of_step=round(r_ms / args.steps / ms, 4), source_sha=src,
-                mfma_busy_frac=busy)
+    kernels = dict(
+        update=dict(bound="hbm", gbs=round(u_gbs, 1), frac=roof["frac"], avg_launch_us=roof["avg_launch_us"],
+                    launches_per_step=roof["launches_per_step"]),
+        cross_entropy=dict(bound="hbm", gbs=round(c_gbs, 1), frac=round(c_gbs / PEAK_HBM_GBS, 4),
+                           avg_launch_us=round(c_avg * 1e6, 2), launches_per_step=ce["launches"] // args.steps,
+                           algorithmic_unit="6 bytes per logit: fp32 logit read, bf16 gradient write"),
+        attention_forward=dict(bound="mfma", tflops=round(a_tfs, 1), frac=round(a_tfs / PEAK_BF16_TFLOPS, 4),
+                               avg_launch_us=round(a_avg * 1e6, 2),
+                               launches_per_step=attn["launches"] // args.steps,
+                               traffic=None if tr is None else tr["traffic_bytes_per_launch"],
+                               mfma_busy_frac=MFMA_BUSY.get((args.workload, T, src)), source_sha=src))
 
     out = dict(metric=METRIC, value=round(tps, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms, 2), higher_is_better=True, scaling="weak",
@@ -491,11 +540,16 @@ def main():
                                     f"k={c['window']}, alpha={c['alpha']}, Zipf(1.1) ids",
                            seq_len=T, minibatch=c["minibatch"], window=c["window"]),
                mfma_peak_frac=round(frac, 4), algorithmic_tflop=round(flops / 1e12, 1),
-               mean_loss=round(mean_loss, 4), roofline=roof)
+               ce_gbs=round(c_gbs, 1), update_gbs=round(u_gbs, 1),
+               mean_loss=round(mean_loss, 4), roofline=roof, kernels=kernels,
+               breakdown_warmup={x["kind"]: dict(ms=round(x["ms"], 2), launches=x["launches"],
+                                                 tflops=round(x["flops"] / (x["ms"] * 1e9), 1) if x["ms"] > 0 and x["flops"] else None,
+                                                 gbs=round(x["bytes"] / (x["ms"] * 1e6), 1) if x["ms"] > 0 and x["bytes"] else None)
+                                 for x in classes})
     del m
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
-        out["cpu_baseline"] = cpu_baseline(c, w, tok, min(c["minibatch"], T - 1))
+        out["cpu_baseline"] = cpu_baseline(c, w, tok)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -310,6 +310,35 @@ def _dyn_init(w, dtype):
     return [{k: np.array(b[k], dtype=dtype) for k in ("w1", "w2", "w3")} for b in w["dyn"]]
 
 
+def minibatch_step(cfg: Cfg, w, dyn, store: KVStore, tokens, a: int, e: int, alpha: float, reduction: str,
+                   loss):
+    """One mini-batch P = [a, e) of the inner loop, in place: forward under
+    the fast weights dyn (earlier positions' K/V from the store, this
+    mini-batch's added to it), loss[i] = l_i for the positions with a target
+    (i <= T-2, T = len(tokens)), then, if there is one, the SGD step
+    dyn <- dyn - alpha dL/d(dyn) with L the MEAN (or SUM) of those l_i.
+    Returns the logits [e-a, V]."""
+    T = len(tokens)
+    dtype = dyn[0]["w1"].dtype.type if cfg.nd else w["embed"].dtype.type
+    z, cache = forward_positions(cfg, w, dyn, store, tokens, a, e)
+    nt = min(e, T - 1) - a          # positions with a target
+    if nt <= 0:
+        return z
+    lab = tokens[a + 1: a + 1 + nt]
+    li, p = cross_entropy(z[:nt], lab)
+    loss[a: a + nt] = li
+    scale = (1.0 / nt) if reduction == "mean" else 1.0
+    dz = np.zeros_like(z)
+    dz[:nt] = p
+    dz[np.arange(nt), lab] -= 1.0
+    dz *= scale
+    grads = backward_minibatch(cfg, w, dyn, cache, dz)
+    for i in range(cfg.nd):
+        for k in ("w1", "w2", "w3"):
+            dyn[i][k] = dyn[i][k] - dtype(alpha) * grads[i][k]
+    return z
+
+
 def ttt_inner_loop(cfg_d: dict, weights, tokens, alpha=None, b=None, reduction=None,
                    dtype=np.float64, keep_state=False):
     """The mini-batch TTT inner loop ([P1] 内层循环 and 持续学习框架; [P2] 另辟蹊径).
@@ -337,24 +366,9 @@ def ttt_inner_loop(cfg_d: dict, weights, tokens, alpha=None, b=None, reduction=N
     last_logits = None
     for a in range(0, T, b):
         e = min(a + b, T)
-        z, cache = forward_positions(cfg, w, dyn, store, tokens, a, e)
+        z = minibatch_step(cfg, w, dyn, store, tokens, a, e, alpha, reduction, loss)
         if e == T:
             last_logits = z[-1].copy()
-        nt = min(e, T - 1) - a          # positions with a target
-        if nt <= 0:
-            continue
-        lab = tokens[a + 1: a + 1 + nt]
-        li, p = cross_entropy(z[:nt], lab)
-        loss[a: a + nt] = li
-        scale = (1.0 / nt) if reduction == "mean" else 1.0
-        dz = np.zeros_like(z)
-        dz[:nt] = p
-        dz[np.arange(nt), lab] -= 1.0
-        dz *= scale
-        grads = backward_minibatch(cfg, w, dyn, cache, dz)
-        for i in range(cfg.nd):
-            for k in ("w1", "w2", "w3"):
-                dyn[i][k] = dyn[i][k] - dtype(alpha) * grads[i][k]
     out = dict(loss=loss, dyn=dyn)
     if keep_state:
         out.update(store=store, weights=w, cfg=cfg, last_logits=last_logits)

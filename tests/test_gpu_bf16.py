@@ -96,7 +96,7 @@ def check_fast_weights(m, g, nd, w):
                 cmax = dW.amax(dim=0).cpu().numpy()
                 ext.append(max(float(np.max(np.abs(rmax - g[f"d{i}_{k}_rowmax"]))),
                                float(np.max(np.abs(cmax - g[f"d{i}_{k}_colmax"])))) / den)
-            del ws
+        del ws
     return errs, ext
 
 
