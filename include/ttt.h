@@ -216,6 +216,25 @@ ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float* eta, cons
                             const float* gamma, float* W, float* M, int32_t H, int64_t T,
                             int32_t D, int32_t C, void* stream);
 
+/* Allocation-free variant of e2ttt_chunk_scan for callers that cannot
+ * allocate device memory (work under HIP graph capture, tight serving loops,
+ * hosts that forbid hipMalloc). Same arguments, result and errors. Its work
+ * buffer is a fixed device array of e2ttt_chunk_scan_noalloc_max_bytes()
+ * bytes (32 MiB), one copy per GPU, held until the process ends; a call
+ * needs 8 H T + 16 H ceil(T / C) + 4 H D^2 + 512 bytes of it (16 heads x
+ * 32768 tokens x D 128: 5.3 MB), and a larger problem returns
+ * TTT_ERR_UNSUPPORTED before any device work. The call never allocates or
+ * frees device memory; the first call on a device looks up that device's
+ * copy. The array keeps the last call's contents (every value a call reads
+ * is written by that call first). Calls on one GPU share its array, so
+ * calls that overlap on one GPU (different streams or host threads) race. */
+ttt_status e2ttt_chunk_scan_noalloc(const void* k, const void* v, const float* eta, const float* beta,
+                                    const float* gamma, float* W, float* M, int32_t H, int64_t T,
+                                    int32_t D, int32_t C, void* stream);
+
+/* Size in bytes of the allocation-free variant's work buffer. */
+int64_t e2ttt_chunk_scan_noalloc_max_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

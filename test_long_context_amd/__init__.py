@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.ttt_destroy.argtypes = [vp]
         L.ttt_destroy.restype = None
         L.e2ttt_chunk_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
+        L.e2ttt_chunk_scan_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
+        L.e2ttt_chunk_scan_noalloc_max_bytes.argtypes = []
+        L.e2ttt_chunk_scan_noalloc_max_bytes.restype = i64
         L.ttt_timing_enable.argtypes = [vp, ctypes.c_uint32]
         dp, lp = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)
         L.ttt_timing_read.argtypes = [vp, i32, dp, lp, dp, dp]
@@ -89,7 +92,7 @@ def lib() -> ctypes.CDLL:
         L.tttk_attn_bwd_workspace.restype = i64
         L.tttk_ce.argtypes = [i32, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_get_fast_weights", "ttt_reset",
-                  "ttt_sync", "e2ttt_chunk_scan", "ttt_timing_enable", "ttt_timing_read", "tttk_gemm",
+                  "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "ttt_timing_enable", "ttt_timing_read", "tttk_gemm",
                   "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce"):
             getattr(L, f).restype = st
         _lib = L
@@ -229,6 +232,21 @@ def e2ttt_chunk_scan(k, v, eta, beta, gamma, W, M, chunk: int, stream=None):
     if st != TTT_OK:
         raise TTTError(st, "e2ttt_chunk_scan")
     return W, M
+
+
+def e2ttt_chunk_scan_noalloc(k, v, eta, beta, gamma, W, M, chunk: int, stream=None):
+    """e2ttt_chunk_scan without device allocation (fixed work buffer; see
+    include/ttt.h)."""
+    H, T, D = k.shape
+    st = lib().e2ttt_chunk_scan_noalloc(_ptr(k), _ptr(v), _ptr(eta), _ptr(beta), _ptr(gamma), _ptr(W),
+                                        _ptr(M), H, T, D, chunk, _stream(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "e2ttt_chunk_scan_noalloc")
+    return W, M
+
+
+def e2ttt_chunk_scan_noalloc_max_bytes() -> int:
+    return int(lib().e2ttt_chunk_scan_noalloc_max_bytes())
 
 
 # ---------------------------------------------------------------- kernel level

@@ -369,44 +369,42 @@ struct E2Scratch {
 };
 E2Scratch g_e2;
 std::mutex g_e2_mu;  // guards g_e2 on the host
-}  // namespace
 
-extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float* eta, const float* beta,
-                                       const float* gamma, float* W, float* M, int32_t H, int64_t T,
-                                       int32_t D, int32_t C, void* stream) {
-  using namespace ttt;
+// Work buffer of the allocation-free entry point: a fixed device array, one
+// copy per GPU, alive until the process ends. Host code never passes the
+// symbol itself to a kernel (on the host it is only a stand-in): its device
+// address is looked up once per device and kept in g_scr_ptr.
+constexpr size_t E2_SCRATCH_BYTES = (size_t)32 << 20;
+__device__ __align__(256) unsigned char scratch[E2_SCRATCH_BYTES];
+constexpr int E2_MAX_DEV = 64;
+void* g_scr_ptr[E2_MAX_DEV] = {};
+std::mutex g_scr_mu;  // guards g_scr_ptr
+
+ttt_status e2_check(const void* k, const void* v, const float* eta, const float* beta, const float* gamma,
+                    const float* W, const float* M, int32_t H, int64_t T, int32_t D, int32_t C) {
   if (!k || !v || !eta || !beta || !gamma || !W || !M) return TTT_ERR_INVALID_ARG;
   if (H < 1 || T < 1 || C < 1) return TTT_ERR_INVALID_ARG;
   if (D != 128 && D != 64) return TTT_ERR_UNSUPPORTED;
   if (C % 64 || C > 2048) return TTT_ERR_UNSUPPORTED;
   if (((uintptr_t)W & 15) || ((uintptr_t)M & 15)) return TTT_ERR_INVALID_ARG;
-  int ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
-    (void)hipGetLastError();
-    return TTT_ERR_NO_DEVICE;
-  }
-  hipStream_t st = (hipStream_t)stream;
+  return TTT_OK;
+}
+
+// Bytes of work buffer a call needs: the per-token coefficients KW, KM
+// [H, T], the per-chunk coefficients [H, chunks, 4] and the second W buffer
+// [H, D, D] at a 256-byte boundary.
+size_t e2_work_bytes(int32_t H, int64_t T, int32_t D, int32_t C) {
   const int64_t nch = (T + C - 1) / C;
-  const size_t need = (size_t)2 * H * T * 4 + (size_t)H * nch * 4 * 4 + (size_t)H * D * D * 4 + 512;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
-  // Work buffer cached per process (grown on demand, reallocated on a device change).
-  std::lock_guard<std::mutex> lock(g_e2_mu);
-  if (g_e2.bytes < need || g_e2.dev != dev) {
-    if (g_e2.p) {
-      (void)hipStreamSynchronize(st);
-      (void)hipFree(g_e2.p);
-    }
-    g_e2.p = nullptr;
-    g_e2.bytes = 0;
-    if (hipMalloc(&g_e2.p, need) != hipSuccess) {
-      (void)hipGetLastError();
-      return TTT_ERR_OOM;
-    }
-    g_e2.bytes = need;
-    g_e2.dev = dev;
-  }
-  float* KW = (float*)g_e2.p;
+  return (size_t)2 * H * T * 4 + (size_t)H * nch * 4 * 4 + (size_t)H * D * D * 4 + 512;
+}
+
+// Enqueues the scan on st with the given work buffer (at least
+// e2_work_bytes, 256-byte aligned).
+ttt_status e2_run(const void* k, const void* v, const float* eta, const float* beta, const float* gamma, float* W,
+                  float* M, int32_t H, int64_t T, int32_t D, int32_t C, void* work, hipStream_t st) {
+  using namespace ttt;
+  const int64_t nch = (T + C - 1) / C;
+  float* KW = (float*)work;
   float* KM = KW + (size_t)H * T;
   float* coef = KM + (size_t)H * T;
   // the other W buffer, 256-byte aligned (its rows are read as 16-byte vectors)
@@ -430,4 +428,71 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
     if (hipMemcpyAsync(W, W2, (size_t)H * D * D * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return TTT_ERR_HIP;
   }
   return TTT_OK;
+}
+}  // namespace
+
+extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float* eta, const float* beta,
+                                       const float* gamma, float* W, float* M, int32_t H, int64_t T,
+                                       int32_t D, int32_t C, void* stream) {
+  const ttt_status cs = e2_check(k, v, eta, beta, gamma, W, M, H, T, D, C);
+  if (cs != TTT_OK) return cs;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return TTT_ERR_NO_DEVICE;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const size_t need = e2_work_bytes(H, T, D, C);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
+  // Work buffer cached per process (grown on demand, reallocated on a device change).
+  std::lock_guard<std::mutex> lock(g_e2_mu);
+  if (g_e2.bytes < need || g_e2.dev != dev) {
+    if (g_e2.p) {
+      (void)hipStreamSynchronize(st);
+      (void)hipFree(g_e2.p);
+    }
+    g_e2.p = nullptr;
+    g_e2.bytes = 0;
+    if (hipMalloc(&g_e2.p, need) != hipSuccess) {
+      (void)hipGetLastError();
+      return TTT_ERR_OOM;
+    }
+    g_e2.bytes = need;
+    g_e2.dev = dev;
+  }
+  return e2_run(k, v, eta, beta, gamma, W, M, H, T, D, C, g_e2.p, st);
+}
+
+extern "C" int64_t e2ttt_chunk_scan_noalloc_max_bytes(void) { return (int64_t)E2_SCRATCH_BYTES; }
+
+extern "C" ttt_status e2ttt_chunk_scan_noalloc(const void* k, const void* v, const float* eta, const float* beta,
+                                               const float* gamma, float* W, float* M, int32_t H, int64_t T,
+                                               int32_t D, int32_t C, void* stream) {
+  const ttt_status cs = e2_check(k, v, eta, beta, gamma, W, M, H, T, D, C);
+  if (cs != TTT_OK) return cs;
+  if (e2_work_bytes(H, T, D, C) > E2_SCRATCH_BYTES) return TTT_ERR_UNSUPPORTED;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return TTT_ERR_NO_DEVICE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
+  if (dev < 0 || dev >= E2_MAX_DEV) return TTT_ERR_UNSUPPORTED;
+  void* work = nullptr;
+  {
+    // first call on this device (it is current): look up its copy's address
+    std::lock_guard<std::mutex> lock(g_scr_mu);
+    if (!g_scr_ptr[dev]) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return TTT_ERR_HIP;
+      }
+      g_scr_ptr[dev] = p;
+    }
+    work = g_scr_ptr[dev];
+  }
+  return e2_run(k, v, eta, beta, gamma, W, M, H, T, D, C, work, (hipStream_t)stream);
 }
