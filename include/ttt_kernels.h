@@ -93,6 +93,30 @@ int64_t tttk_attn_bwd_workspace(int32_t dtype, int32_t n, int32_t H, int32_t Hk,
 ttt_status tttk_ce(int32_t dtype, const float* logits, int32_t n, int32_t nt, int32_t V,
                    const int32_t* labels, float scale, float* loss, void* dz, int* err, void* stream);
 
+/* One weight-gradient product with the fp32 SGD step fused in (bf16
+ * operands; see tttk_dw_sgd). */
+typedef struct {
+  const void* A;  /* bf16, A(m, k) = A[k lda + m] (output gradients, token-major) */
+  int64_t lda;
+  const void* B;  /* bf16, B(n, k) = B[k ldb + n] (inputs, token-major) */
+  int64_t ldb;
+  float* W;       /* fp32 master [M][ldw], updated in place */
+  void* Hi;       /* bf16 [M][ldw] = RNE(W) after the step */
+  void* Lo;       /* bf16 [M][ldw] = RNE(W - Hi), or NULL */
+  int64_t ldw;
+  int32_t M, N;
+} tttk_dw_problem;
+
+/* W -= lr * sum_k A(m, k) B(n, k) for nprob (1 or 2) problems sharing K, in
+ * one persistent launch of grid workgroups (0 = two per CU); the bf16
+ * working copy and its low term are re-rounded from the new master. This is
+ * the fused dW + SGD update of a dynamic SwiGLU block ([P1] section
+ * 持续学习框架, the SGD step). M, N multiples of 16; lda, ldb multiples of 8,
+ * ldw of 4, lda >= M, ldb >= N, ldw >= N; A, B, W 16-byte and Hi, Lo 8-byte
+ * aligned; else TTT_ERR_UNSUPPORTED / TTT_ERR_INVALID_ARG. */
+ttt_status tttk_dw_sgd(int32_t nprob, const tttk_dw_problem* probs, int32_t K, float lr, int32_t grid,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

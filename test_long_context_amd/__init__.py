@@ -41,6 +41,14 @@ class Config(ctypes.Structure):
 _PP = ctypes.POINTER(ctypes.c_void_p)
 
 
+class DwProblem(ctypes.Structure):
+    """tttk_dw_problem (include/ttt_kernels.h)."""
+    _fields_ = [("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("B", ctypes.c_void_p),
+                ("ldb", ctypes.c_int64), ("W", ctypes.c_void_p), ("Hi", ctypes.c_void_p),
+                ("Lo", ctypes.c_void_p), ("ldw", ctypes.c_int64), ("M", ctypes.c_int32),
+                ("N", ctypes.c_int32)]
+
+
 class Weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
                 ("final_norm", ctypes.c_void_p)] + [
@@ -91,9 +99,10 @@ def lib() -> ctypes.CDLL:
         L.tttk_attn_bwd_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.tttk_attn_bwd_workspace.restype = i64
         L.tttk_ce.argtypes = [i32, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
+        L.tttk_dw_sgd.argtypes = [i32, ctypes.POINTER(DwProblem), i32, f32, i32, vp]
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_get_fast_weights", "ttt_reset",
                   "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "ttt_timing_enable", "ttt_timing_read", "tttk_gemm",
-                  "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce"):
+                  "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce", "tttk_dw_sgd"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -305,3 +314,13 @@ def attn_bwd(q, k, v, lse, dO, D, dq, dk, dv, n, H, Hk, dh, cap, window, pos0, v
 def ce(logits, n, nt, V, labels, scale, loss, dz, err, stream=None):
     _check(lib().tttk_ce(_dt(dz), _ptr(logits), n, nt, V, _ptr(labels), float(scale), _ptr(loss), _ptr(dz),
                          _ptr(err), _stream(stream)), "tttk_ce")
+
+
+def dw_sgd(problems, K: int, lr: float, grid: int = 0, stream=None):
+    """Fused weight-gradient products with the fp32 SGD step (tttk_dw_sgd):
+    problems is a list of dicts with A, lda, B, ldb, W, Hi, Lo, ldw, M, N."""
+    arr = (DwProblem * len(problems))()
+    for i, p in enumerate(problems):
+        arr[i] = DwProblem(A=_ptr(p["A"]), lda=p["lda"], B=_ptr(p["B"]), ldb=p["ldb"], W=_ptr(p["W"]),
+                           Hi=_ptr(p["Hi"]), Lo=_ptr(p.get("Lo")), ldw=p["ldw"], M=p["M"], N=p["N"])
+    _check(lib().tttk_dw_sgd(len(problems), arr, int(K), float(lr), int(grid), _stream(stream)), "tttk_dw_sgd")

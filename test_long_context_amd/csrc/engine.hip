@@ -115,6 +115,8 @@ struct ttt_ctx {
   hipEvent_t ev_join = nullptr;              // side stream done with the prefill
   std::vector<void*> ghd_t;                  // [b, d] gradient into each dynamic MLP (storage dtype)
   std::vector<void*> dh12d;                  // [b, 2 Fd] SwiGLU pre-activation gradients per dynamic block
+  bool fused_update = false;                 // bf16: both update products in one dw_sgd launch
+  int upd_grid = 0;                          // its workgroups (0: two per CU)
   hipStream_t dstream = nullptr;             // decode graph capture stream
   hipGraphExec_t dgraph = nullptr;           // captured decode blocks
 
@@ -468,8 +470,9 @@ ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipSt
       xr = c->h_dyn[i];
     }
     // dynamic MLP sublayer under the current fast weights
-    // (bf16: the fp32 master enters as two bf16 terms, working + low, so that
-    // updates below half a bf16 ulp reach the forward)
+    // (bf16: the fp32 master enters as two bf16 terms, working + low: one
+    // step moves W by less than half a bf16 ulp, so RNE(master) alone would
+    // round most updates back to the old weights, coherently)
     GemmArgs g = ga(c->xn_d[i], d, c->dw12[i], d, n, 2 * Fd, d, c->h12_d[i], 2 * Fd);
     g.C2 = c->hm_d[i];
     g.B2 = c->dw12_lo[i];
@@ -506,26 +509,37 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     // on the side stream once this block's products with the old W are queued
     HIPCHK(c, hipEventRecord(c->ev_dyn[i], st));
     HIPCHK(c, hipStreamWaitEvent(c->side, c->ev_dyn[i], 0));
-    HIPCHK(c, hipStreamWaitEvent(c->side2, c->ev_dyn[i], 0));
-    {
-      hipStream_t st = c->side2;
-      GemmArgs g = ga(gt, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
-      g.C2 = c->dw3[i];
-      g.C3 = c->dw3_lo[i];
-      g.scale = lr;
-      TCALL(KC_SGD, gfl(d, Fd, n), (double)d * Fd * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g, st));
-      HIPCHK(c, hipEventRecord(c->ev_w3, st));
-    }
-    {
+    if (c->dt == DT::BF16 && c->fused_update) {
+      // both products in one persistent launch (shapes checked at init)
       hipStream_t st = c->side;
-      GemmArgs g2 = ga(c->dh12d[i], 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
-      g2.C2 = c->dw12[i];
-      g2.C3 = c->dw12_lo[i];
-      g2.scale = lr;
-      TCALL(KC_SGD, gfl(2 * Fd, d, n), 2.0 * Fd * d * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g2, st));
-      // the block's update is done once both products are
-      HIPCHK(c, hipStreamWaitEvent(st, c->ev_w3, 0));
+      const DwUpdate u[2] = {
+          DwUpdate{c->dh12d[i], 2L * Fd, c->xn_d[i], d, c->m12[i], c->dw12[i], c->dw12_lo[i], d, 2 * Fd, d},
+          DwUpdate{gt, d, c->hm_d[i], Fd, c->m3[i], c->dw3[i], c->dw3_lo[i], Fd, d, Fd}};
+      TCALL(KC_SGD, gfl(2 * Fd, d, n) + gfl(d, Fd, n), 3.0 * Fd * d * upd_bytes,
+            dw_sgd(u, 2, n, lr, c->upd_grid, st));
       HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
+    } else {
+      HIPCHK(c, hipStreamWaitEvent(c->side2, c->ev_dyn[i], 0));
+      {
+        hipStream_t st = c->side2;
+        GemmArgs g = ga(gt, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
+        g.C2 = c->dw3[i];
+        g.C3 = c->dw3_lo[i];
+        g.scale = lr;
+        TCALL(KC_SGD, gfl(d, Fd, n), (double)d * Fd * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g, st));
+        HIPCHK(c, hipEventRecord(c->ev_w3, st));
+      }
+      {
+        hipStream_t st = c->side;
+        GemmArgs g2 = ga(c->dh12d[i], 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
+        g2.C2 = c->dw12[i];
+        g2.C3 = c->dw12_lo[i];
+        g2.scale = lr;
+        TCALL(KC_SGD, gfl(2 * Fd, d, n), 2.0 * Fd * d * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g2, st));
+        // the block's update is done once both products are
+        HIPCHK(c, hipStreamWaitEvent(st, c->ev_w3, 0));
+        HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
+      }
     }
     if (l == s) break;
     TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], n, d, c->gh, c->gh_t, 1, st));
@@ -810,6 +824,18 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     c->d_tok = (int32_t*)p;
   }
   c->dec_split = decode_attn_splits(c->dt, c->H, c->Hk, c->dh, c->k, c->dt == DT::BF16);
+  // bf16 update products: two GEMM launches with the SGD epilogue on two
+  // side streams (default), or, with TTT_UPDATE_KERNEL=fused, both in one
+  // persistent wave-specialised launch (dw_sgd; TTT_UPDATE_GRID sets its
+  // grid). The fused launch passes the same parity tests but is slower at
+  // the 3B shape (about 470 vs 340 us per block in isolation): its MFMA
+  // waves, one per SIMD, wait for every K step's operand loads.
+  {
+    const char* uk = getenv("TTT_UPDATE_KERNEL");
+    c->fused_update = c->dt == DT::BF16 && uk && strcmp(uk, "fused") == 0;
+    const char* ug = getenv("TTT_UPDATE_GRID");
+    c->upd_grid = ug ? std::max(0, atoi(ug)) : 0;
+  }
   Af(&c->dec, (size_t)4 * (c->QKV + 2 * Fm + 2 * d + c->H * c->dh) +
                   (size_t)c->H * c->dec_split * (c->dh + 2));
   if (!ok) {
@@ -893,8 +919,8 @@ ttt_status ttt_reset(ttt_ctx* c, void* stream) {
       // W0 is exact in the storage dtype: working copy = W0, low term = 0
       HIPCHK(c, hipMemcpyAsync(c->dw12[i], c->w0_12[i], n12 * es, hipMemcpyDeviceToDevice, st));
       HIPCHK(c, hipMemcpyAsync(c->dw3[i], c->w0_3[i], n3 * es, hipMemcpyDeviceToDevice, st));
-      HIPCHK(c, fill_zero_bytes(c->dw12_lo[i], n12 * es, st));
-      HIPCHK(c, fill_zero_bytes(c->dw3_lo[i], n3 * es, st));
+      if (c->dw12_lo[i]) HIPCHK(c, fill_zero_bytes(c->dw12_lo[i], n12 * es, st));
+      if (c->dw3_lo[i]) HIPCHK(c, fill_zero_bytes(c->dw3_lo[i], n3 * es, st));
     }
   }
   c->pos = 0;

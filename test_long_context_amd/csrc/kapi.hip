@@ -209,3 +209,16 @@ extern "C" ttt_status tttk_ce(int32_t dtype, const float* logits, int32_t n, int
              ? TTT_OK
              : TTT_ERR_HIP;
 }
+
+extern "C" ttt_status tttk_dw_sgd(int32_t nprob, const tttk_dw_problem* probs, int32_t K, float lr, int32_t grid,
+                                  void* stream) {
+  if (nprob < 1 || nprob > 2 || !probs || K < 0 || grid < 0) return TTT_ERR_INVALID_ARG;
+  DwUpdate u[2];
+  for (int i = 0; i < nprob; ++i) {
+    const tttk_dw_problem& p = probs[i];
+    if (!p.A || !p.B || !p.W || !p.Hi || p.M < 1 || p.N < 1) return TTT_ERR_INVALID_ARG;
+    u[i] = DwUpdate{p.A, (long)p.lda, p.B, (long)p.ldb, p.W, p.Hi, p.Lo, (long)p.ldw, p.M, p.N};
+    if (!dw_sgd_supported(u[i])) return TTT_ERR_UNSUPPORTED;
+  }
+  return dw_sgd(u, nprob, K, lr, grid, (hipStream_t)stream) == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}

@@ -48,6 +48,26 @@ struct GemmArgs {
 };
 
 hipError_t gemm(DT dt, bool a_kmajor, bool b_kmajor, Epi epi, const GemmArgs& g, hipStream_t st);
+
+// Fused weight-gradient contraction and fp32 SGD step (bf16 operands):
+//   W[m, n] -= lr * sum_k A[k * lda + m] B[k * ldb + n],
+//   Hi = RNE(W) (bf16), Lo = RNE(W - Hi) (bf16, optional)
+// for one or two problems of the same K in one persistent launch (grid 0 =
+// two workgroups per CU). Needs M, N multiples of 16, lda, ldb multiples of
+// 8, ldw of 4, A, B, W 16-byte and Hi, Lo 8-byte aligned (dw_sgd_supported).
+struct DwUpdate {
+  const void* A;
+  long lda;
+  const void* B;
+  long ldb;
+  float* W;
+  void* Hi;
+  void* Lo;
+  long ldw;
+  int M, N;
+};
+bool dw_sgd_supported(const DwUpdate& u);
+hipError_t dw_sgd(const DwUpdate* u, int n, int K, float lr, int grid, hipStream_t st);
 // Tile K granule that split-K chunks must be a multiple of.
 int gemm_k_granule(DT dt);
 

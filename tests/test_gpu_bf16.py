@@ -239,3 +239,17 @@ def test_bf16_3b_shape_two_minibatches_repeat_bitwise():
     for a, b in zip(runs[0][1], runs[1][1]):
         for x, y in zip(a, b):
             assert torch.equal(x, y)
+
+
+def test_bf16_fused_update_kernel_option():
+    """TTT_UPDATE_KERNEL=fused (one persistent launch for both update
+    products of a block) against the oracle, with K = b = 1024 (update waves
+    one tile behind the MFMA waves) and a ragged last mini-batch."""
+    c = synth.config("125m", n_layers=4, d_model=512, n_heads=4, n_kv_heads=2, head_dim=128,
+                     ffn_hidden=1024, dyn_ffn_hidden=1024, vocab=4096, window=1024, minibatch=1024,
+                     n_dynamic=2, alpha=0.01)
+    os.environ["TTT_UPDATE_KERNEL"] = "fused"
+    try:
+        check(c, T=2600)
+    finally:
+        del os.environ["TTT_UPDATE_KERNEL"]

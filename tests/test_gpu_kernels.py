@@ -197,3 +197,75 @@ def test_gemm_two_term_b(epi):
             assert float((got - acc).abs().max()) <= float(acc.abs().max()) * 2 ** -8
             continue
         assert float((got - acc).abs().max() / acc.abs().max()) < 1e-5, (epi, t)
+
+
+def _dw_case(g, M, N, K, lo=True, lda=None, ldb=None):
+    lda, ldb = lda or M, ldb or N
+    A = rnd(g, K * lda).view(K, lda)
+    B = rnd(g, K * ldb).view(K, ldb)
+    W0 = rnd(g, M * N, scale=0.02, dtype=torch.float32).view(M, N)
+    p = dict(A=A.to(dev), lda=lda, B=B.to(dev), ldb=ldb, W=W0.to(dev), Hi=torch.empty(M, N, dtype=bf, device=dev),
+             Lo=torch.empty(M, N, dtype=bf, device=dev) if lo else None, ldw=N, M=M, N=N)
+    return p, A, B, W0
+
+
+def _dw_check(p, A, B, W0, lr, M, N):
+    acc = A[:, :M].double().T @ B[:, :N].double()
+    want = W0.double() - lr * acc
+    Wg = p["W"].cpu()
+    err = float((Wg.double() - want).abs().max())
+    assert err < 1e-6, err
+    # the working copy is the RNE of the stored master, the low term the RNE of the remainder
+    assert torch.equal(p["Hi"].cpu(), Wg.to(bf))
+    if p["Lo"] is not None:
+        assert torch.equal(p["Lo"].cpu(), (Wg - Wg.to(bf).float()).to(bf))
+
+
+@pytest.mark.parametrize("K,grid", [(1024, 0), (1024, 8), (1000, 16), (328, 0), (64, 8)])
+def test_dw_sgd_two_problems(K, grid):
+    """tttk_dw_sgd: W -= lr A^T B for two problems in one persistent launch
+    (K = 1024 and 1000: each tile's update overlapped with the next tile's
+    products; other K: updated after each tile), ragged tiles in M and N,
+    padded leading dimensions, one problem without the low term; grid 8 and
+    16 make every workgroup visit many tiles of both problems."""
+    g = torch.Generator().manual_seed(21)
+    lr = 1e-3
+    say(f"dw_sgd K={K} grid={grid}")
+    p0, A0, B0, W00 = _dw_case(g, 400, 272, K, lda=408)
+    p1, A1, B1, W01 = _dw_case(g, 272, 528, K, lo=False, ldb=536)
+    tla.dw_sgd([p0, p1], K, lr, grid=grid)
+    torch.cuda.synchronize()
+    _dw_check(p0, A0, B0, W00, lr, 400, 272)
+    _dw_check(p1, A1, B1, W01, lr, 272, 528)
+
+
+def test_dw_sgd_3b_block_shapes_sampled():
+    """Both products of a 3B dynamic block (dW12 [16384 x 3072] and dW3
+    [3072 x 8192], K = 1024) in the engine's launch configuration, checked on
+    4096 sampled entries each, plus the rounding of the working copy."""
+    g = torch.Generator().manual_seed(22)
+    lr = 5e-3
+    K = 1024
+    shapes = [(16384, 3072), (3072, 8192)]
+    ps = []
+    for M, N in shapes:
+        A = rnd(g, K * M).view(K, M).to(dev)
+        B = rnd(g, K * N).view(K, N).to(dev)
+        W0 = (torch.randn(M, N, generator=g) * 0.02).to(dev)
+        ps.append(dict(A=A, lda=M, B=B, ldb=N, W=W0.clone(), Hi=torch.empty(M, N, dtype=bf, device=dev),
+                       Lo=torch.empty(M, N, dtype=bf, device=dev), ldw=N, M=M, N=N, W0=W0))
+    tla.dw_sgd([{k: v for k, v in p.items() if k != "W0"} for p in ps], K, lr)
+    torch.cuda.synchronize()
+    for (M, N), p in zip(shapes, ps):
+        ms = torch.randint(0, M, (4096,), generator=g)
+        ns = torch.randint(0, N, (4096,), generator=g)
+        a = p["A"].cpu().double()[:, ms]
+        b = p["B"].cpu().double()[:, ns]
+        want = p["W0"].cpu().double()[ms, ns] - lr * (a * b).sum(0)
+        got = p["W"].cpu()[ms, ns]
+        err = float((got.double() - want).abs().max())
+        say(f"  dW+SGD {M}x{N}: max err {err:.2e}")
+        assert err < 2e-6
+        Wg = p["W"]
+        assert torch.equal(p["Hi"], Wg.to(bf))
+        assert torch.equal(p["Lo"], (Wg - Wg.to(bf).float()).to(bf))
