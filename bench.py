@@ -230,6 +230,23 @@ def e2_bench(args, tla, torch, synth):
                              frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
                              kernel="e2ttt_chunk_scan (scalar scan, one fused aggregation + update launch per chunk)",
                              algorithmic_bytes=algo, mfma_tflops=round(flops / (ms * 1e-3) / 1e12, 2)))
+    # the chunk-wise baseline (LaCT's rule: one aggregation per chunk) on the
+    # same inputs: the pages quote the exact kernel's throughput cost against it
+    lts = []
+    for i in range(max(1, args.warmup) + args.steps):
+        W.copy_(W0)
+        M.copy_(M0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tla.lact_chunk_scan(x["k"], x["v"], x["eta"], x["beta"], W, M, C)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= max(1, args.warmup):
+            lts.append(a.elapsed_time(b))
+    lms = sorted(lts)[len(lts) // 2]
+    out["lact_baseline"] = dict(ms_per_step=round(lms, 4), value=round(H * T / (lms * 1e-3), 1),
+                                unit="token-heads/s", e2_cost_vs_lact=round(ms / lms - 1.0, 4),
+                                kernel="lact_chunk_scan (chunk-mean momentum, one aggregation per chunk)")
     if not args.no_cpu_baseline:
         from oracle import e2ttt as E
         xs = {k_: v_.double().cpu().numpy() for k_, v_ in x.items() if k_ in ("k", "v", "eta", "beta", "gamma")}

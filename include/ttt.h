@@ -235,6 +235,17 @@ ttt_status e2ttt_chunk_scan_noalloc(const void* k, const void* v, const float* e
 /* Size in bytes of the allocation-free variant's work buffer. */
 int64_t e2ttt_chunk_scan_noalloc_max_bytes(void);
 
+/* The chunk-wise baseline E2-TTT is compared with ([P3] 背景知识: LaCT's
+ * large-chunk rule, whose momentum factor is the chunk's average of beta_t;
+ * section 实验结果, the "chunk-averaged" ablation). For every head and chunk,
+ * with W0, M0 the state at chunk start and G_t = (W0 k_t - v_t) k_t^T:
+ *   M_C = mean_t(beta_t) M0 + sum_t eta_t G_t,   W_C = W0 + M_C
+ * (one update direction per chunk, no decay). Arguments, layouts and errors
+ * as for e2ttt_chunk_scan without gamma; it shares that call's cached work
+ * buffer, so the two must not run concurrently either. */
+ttt_status lact_chunk_scan(const void* k, const void* v, const float* eta, const float* beta, float* W,
+                           float* M, int32_t H, int64_t T, int32_t D, int32_t C, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,12 @@ per-token gradient is taken at the chunk-start W0:
 (the gradient of 1/2 ||W0 k_t - v_t||^2; the page's G_t is its negative and
 the identity is linear in G, so both signs are exercised by the pins).
 Everything here is float64 on the bf16-valued k, v and fp32-valued scalars.
+
+The chunk-wise baseline the page compares against (section 背景知识, LaCT's
+large-chunk rule, and the "chunk-averaged" ablation of 实验结果) is
+lact_chunked: one update direction per chunk from the eta-weighted gradients
+at the chunk-start W0, a chunk-level momentum factor equal to the mean of the
+chunk's beta_t, and no decay.
 """
 from __future__ import annotations
 
@@ -88,4 +94,25 @@ def e2_closed_form(k, v, eta, beta, gamma, W, M, C, sign=1.0):
             dM = (E * KM[:, None]).T @ k[h, a:e]
             W[h] = gt[0] * W0 + bt[0] * R[1] * M0 + dW
             M[h] = bt[0] * M0 + dM
+    return W, M
+
+
+def lact_chunked(k, v, eta, beta, W, M, C, sign=1.0):
+    """LaCT's chunk-wise update, chunk by chunk ([P3] 背景知识):
+         G = sum_t eta_t G_t   (G_t = sign (W0 k_t - v_t) k_t^T at the chunk-start W0),
+         M <- mean_t(beta_t) M + G,   W <- W + M.
+    k, v [H, T, D]; eta, beta [H, T]; W, M [H, D, D]. Returns final (W, M)."""
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    eta, beta = (np.asarray(x, np.float64) for x in (eta, beta))
+    W = np.array(W, np.float64)
+    M = np.array(M, np.float64)
+    H, T, D = k.shape
+    for h in range(H):
+        for a in range(0, T, C):
+            e = min(T, a + C)
+            E = _grad_terms(W[h], k[h, a:e], v[h, a:e], sign)
+            G = (E * eta[h, a:e, None]).T @ k[h, a:e]
+            M[h] = np.mean(beta[h, a:e]) * M[h] + G
+            W[h] = W[h] + M[h]
     return W, M

@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.ttt_destroy.restype = None
         L.e2ttt_chunk_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
         L.e2ttt_chunk_scan_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
+        L.lact_chunk_scan.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
         L.e2ttt_chunk_scan_noalloc_max_bytes.argtypes = []
         L.e2ttt_chunk_scan_noalloc_max_bytes.restype = i64
         L.ttt_timing_enable.argtypes = [vp, ctypes.c_uint32]
@@ -101,7 +102,7 @@ def lib() -> ctypes.CDLL:
         L.tttk_ce.argtypes = [i32, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
         L.tttk_dw_sgd.argtypes = [i32, ctypes.POINTER(DwProblem), i32, f32, i32, vp]
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_get_fast_weights", "ttt_reset",
-                  "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "ttt_timing_enable", "ttt_timing_read", "tttk_gemm",
+                  "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan", "ttt_timing_enable", "ttt_timing_read", "tttk_gemm",
                   "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce", "tttk_dw_sgd"):
             getattr(L, f).restype = st
         _lib = L
@@ -240,6 +241,16 @@ def e2ttt_chunk_scan(k, v, eta, beta, gamma, W, M, chunk: int, stream=None):
                                 _ptr(M), H, T, D, chunk, _stream(stream))
     if st != TTT_OK:
         raise TTTError(st, "e2ttt_chunk_scan")
+    return W, M
+
+
+def lact_chunk_scan(k, v, eta, beta, W, M, chunk: int, stream=None):
+    """In-place LaCT chunk-wise scan over all chunks (see include/ttt.h)."""
+    H, T, D = k.shape
+    st = lib().lact_chunk_scan(_ptr(k), _ptr(v), _ptr(eta), _ptr(beta), _ptr(W), _ptr(M), H, T, D, chunk,
+                               _stream(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "lact_chunk_scan")
     return W, M
 
 

@@ -153,6 +153,35 @@ hipError_t e2_scalars(const float* eta, const float* beta, const float* gamma, i
   return hipGetLastError();
 }
 
+// LaCT's chunk coefficients ([P3] 背景知识): per (head, chunk) the mean of
+// the chunk's beta_t (float64, fixed-order tree), coef = (1, mean, mean, 0):
+// W_out = W0 + mean M0 + dM, M = mean M0 + dM with dM = sum_t eta_t G_t.
+__global__ void __launch_bounds__(E2_ST) lact_scalar_kernel(const float* beta, int64_t T, int C, float* coef) {
+  __shared__ double sb[E2_ST];
+  const int64_t nch = (T + C - 1) / C;
+  const int h = blockIdx.x / (int)nch;
+  const int64_t r = blockIdx.x % nch;
+  const int64_t a = r * C;
+  const int n = (int)min((int64_t)C, T - a);
+  const float* bt = beta + h * T + a;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += E2_ST) s += (double)bt[i];
+  sb[threadIdx.x] = s;
+  __syncthreads();
+  for (int d = E2_ST / 2; d > 0; d >>= 1) {
+    if (threadIdx.x < d) sb[threadIdx.x] += sb[threadIdx.x + d];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float* cf = coef + ((int64_t)h * nch + r) * 4;
+    const float mean = (float)(sb[0] / n);
+    cf[0] = 1.f;
+    cf[1] = mean;
+    cf[2] = mean;
+    cf[3] = 0.f;
+  }
+}
+
 // ------------------------------------------------------- slice aggregation
 // ------------------------------------------------------------ chunk kernel
 // One launch per chunk; workgroup (16-row block of the state, half of its
@@ -178,7 +207,9 @@ typedef __attribute__((address_space(3))) e2_shortx4* e2_lds_s4_t;
 
 constexpr int E2_NW = 8;  // waves per chunk workgroup
 
-template <int D>
+// LACT: the chunk-wise baseline's single aggregation (K^W unused, dW taken
+// as dM): W_out = coef0 W0 + coef1 M0 + dM, M = coef2 M0 + dM.
+template <int D, bool LACT = false>
 __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Vv,
                                                        const float* __restrict__ KW, const float* __restrict__ KM,
                                                        const float* __restrict__ coef, const float* __restrict__ Win,
@@ -263,7 +294,7 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
       for (int e = 0; e < 4; ++e) {
         const int t = min(blk * BT + 16 * tile + 4 * g + e, n - 1);
         o.v[tile][e] = Vh[(int64_t)t * D + i0 + c];
-        o.kw[tile][e] = KWh[t];
+        o.kw[tile][e] = LACT ? 0.f : KWh[t];
         o.km[tile][e] = KMh[t];
       }
   };
@@ -314,8 +345,10 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
       typedef short e2_shortx8 __attribute__((ext_vector_type(8)));
       Frag8<bf16> bk;
       bk.v = __builtin_bit_cast(bf16x8, (e2_shortx8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      mma16(dw[jt], xwh, bk);
-      mma16(dw[jt], xwl, bk);
+      if constexpr (!LACT) {
+        mma16(dw[jt], xwh, bk);
+        mma16(dw[jt], xwl, bk);
+      }
       mma16(dm[jt], xmh, bk);
       mma16(dm[jt], xml, bk);
     }
@@ -334,7 +367,7 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * g + e, j = 16 * jt + c;
-      red[((wid * 2 + 0) * 16 + i) * JH + j] = dw[jt][e];
+      red[((wid * 2 + 0) * 16 + i) * JH + j] = LACT ? dm[jt][e] : dw[jt][e];
       red[((wid * 2 + 1) * 16 + i) * JH + j] = dm[jt][e];
     }
   __syncthreads();
@@ -495,4 +528,73 @@ extern "C" ttt_status e2ttt_chunk_scan_noalloc(const void* k, const void* v, con
     work = g_scr_ptr[dev];
   }
   return e2_run(k, v, eta, beta, gamma, W, M, H, T, D, C, work, (hipStream_t)stream);
+}
+
+namespace {
+// Work buffer of the LaCT scan: the per-chunk coefficients [H, chunks, 4] and
+// the second W buffer [H, D, D] at a 256-byte boundary.
+size_t lact_work_bytes(int32_t H, int64_t T, int32_t D, int32_t C) {
+  const int64_t nch = (T + C - 1) / C;
+  return (size_t)H * nch * 4 * 4 + (size_t)H * D * D * 4 + 512;
+}
+
+ttt_status lact_run(const void* k, const void* v, const float* eta, const float* beta, float* W, float* M, int32_t H,
+                    int64_t T, int32_t D, int32_t C, void* work, hipStream_t st) {
+  using namespace ttt;
+  const int64_t nch = (T + C - 1) / C;
+  float* coef = (float*)work;
+  float* W2 = (float*)(((uintptr_t)(coef + (size_t)H * nch * 4) + 255) & ~(uintptr_t)255);
+  hipLaunchKernelGGL(lact_scalar_kernel, dim3((unsigned)(nch * H)), dim3(E2_ST), 0, st, beta, T, C, coef);
+  if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
+  const dim3 grid(2 * (D / 16) * H);
+  for (int64_t r = 0; r < nch; ++r) {
+    const int n = (int)std::min<int64_t>(C, T - r * C);
+    const float* src = (r & 1) ? W2 : W;
+    float* dst = (r & 1) ? W : W2;
+    // per-token weights eta_t; the K^W argument is not read by this rule
+    if (D == 128)
+      hipLaunchKernelGGL((e2_chunk_kernel<128, true>), grid, dim3(E2_NW * 64), 0, st, (const bf16*)k, (const bf16*)v,
+                         eta, eta, coef, src, dst, M, T, r * C, n, nch, r);
+    else
+      hipLaunchKernelGGL((e2_chunk_kernel<64, true>), grid, dim3(E2_NW * 64), 0, st, (const bf16*)k, (const bf16*)v,
+                         eta, eta, coef, src, dst, M, T, r * C, n, nch, r);
+    if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
+  }
+  if (nch & 1) {
+    if (hipMemcpyAsync(W, W2, (size_t)H * D * D * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return TTT_ERR_HIP;
+  }
+  return TTT_OK;
+}
+}  // namespace
+
+extern "C" ttt_status lact_chunk_scan(const void* k, const void* v, const float* eta, const float* beta, float* W,
+                                      float* M, int32_t H, int64_t T, int32_t D, int32_t C, void* stream) {
+  const ttt_status cs = e2_check(k, v, eta, beta, beta, W, M, H, T, D, C);
+  if (cs != TTT_OK) return cs;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return TTT_ERR_NO_DEVICE;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const size_t need = lact_work_bytes(H, T, D, C);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
+  // the same cached per-process work buffer as e2ttt_chunk_scan
+  std::lock_guard<std::mutex> lock(g_e2_mu);
+  if (g_e2.bytes < need || g_e2.dev != dev) {
+    if (g_e2.p) {
+      (void)hipStreamSynchronize(st);
+      (void)hipFree(g_e2.p);
+    }
+    g_e2.p = nullptr;
+    g_e2.bytes = 0;
+    if (hipMalloc(&g_e2.p, need) != hipSuccess) {
+      (void)hipGetLastError();
+      return TTT_ERR_OOM;
+    }
+    g_e2.bytes = need;
+    g_e2.dev = dev;
+  }
+  return lact_run(k, v, eta, beta, W, M, H, T, D, C, g_e2.p, st);
 }

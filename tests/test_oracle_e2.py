@@ -63,3 +63,61 @@ def test_kernel_bound_and_underflow_scale():
     bt, gt, R, KM, KW = E.chunk_scalars(eta, beta, gamma)
     assert np.all(KW <= eta.max() * 2048) and np.all(KW >= 0)
     assert bt[0] < 1.4e-45 * 1e3  # far below fp32's normal range
+
+
+# ---------------------------------------------------------------- LaCT baseline
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_lact_with_one_token_chunks_is_the_per_token_recursion_without_decay(sign):
+    """C = 1: the chunk mean of beta is beta_t itself and G = eta_t G_t, so the
+    chunk rule is the per-token recursion with gamma = 1."""
+    k, v, eta, beta, gamma, W, M = _inputs(H=2, T=23, D=6, M0=True)
+    Wl, Ml = E.lact_chunked(k, v, eta, beta, W, M, 1, sign)
+    Ws, Ms = E.e2_sequential(k, v, eta, beta, np.ones_like(gamma), W, M, 1, sign)
+    np.testing.assert_allclose(Wl, Ws, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(Ml, Ms, rtol=1e-12, atol=1e-15)
+
+
+def test_lact_update_direction_is_the_gradient_of_the_weighted_chunk_loss():
+    """One chunk from M0 = 0: M_C = G = gradient at W0 of
+    sum_t eta_t 1/2 ||W k_t - v_t||^2, checked entry by entry against central
+    finite differences of that loss."""
+    k, v, eta, beta, gamma, W, M = (np.asarray(x, np.float64) for x in _inputs(H=1, T=12, D=4))
+    C = 12
+    _, Mc = E.lact_chunked(k, v, eta, beta, W, np.zeros_like(W), C)
+
+    def loss(Wm):
+        r = k[0] @ Wm.T - v[0]
+        return 0.5 * np.sum(eta[0][:, None] * r * r)
+    eps = 1e-6
+    fd = np.zeros((4, 4))
+    for i in range(4):
+        for j in range(4):
+            dW = np.zeros((4, 4))
+            dW[i, j] = eps
+            fd[i, j] = (loss(W[0] + dW) - loss(W[0] - dW)) / (2 * eps)
+    np.testing.assert_allclose(Mc[0], fd, rtol=1e-6, atol=1e-12)
+
+
+def test_lact_without_learning_rate_is_a_geometric_series():
+    """eta = 0 and a constant beta = b: M_r = b^r M0 and
+    W_r = W0 + M0 (b - b^(r+1)) / (1 - b) after r chunks."""
+    k, v, eta, beta, gamma, W, M = (np.asarray(x, np.float64) for x in _inputs(H=1, T=70, D=5, M0=True))
+    b, C, r = 0.93, 16, 5   # 70 tokens: 4 full chunks and a ragged one
+    Wl, Ml = E.lact_chunked(k, v, np.zeros_like(eta), np.full_like(beta, b), W, M, C)
+    np.testing.assert_allclose(Ml[0], b ** r * M[0], rtol=1e-12)
+    np.testing.assert_allclose(Wl[0], W[0] + M[0] * (b - b ** (r + 1)) / (1 - b), rtol=1e-12, atol=1e-15)
+
+
+def test_lact_depends_on_beta_only_through_its_chunk_mean():
+    """Permuting beta inside each chunk leaves the chunk rule unchanged (the
+    per-token recursion does change), and a chunk whose beta are all b uses b."""
+    k, v, eta, beta, gamma, W, M = (np.asarray(x, np.float64) for x in _inputs(H=2, T=64, D=5, M0=True))
+    C = 16
+    perm = np.concatenate([a + np.random.default_rng(3).permutation(C) for a in range(0, 64, C)])
+    W1, M1 = E.lact_chunked(k, v, eta, beta, W, M, C)
+    W2, M2 = E.lact_chunked(k, v, eta, beta[:, perm], W, M, C)
+    np.testing.assert_allclose(W1, W2, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(M1, M2, rtol=1e-13, atol=1e-16)
+    Ws1, _ = E.e2_sequential(k, v, eta, beta, np.ones_like(gamma), W, M, C)
+    Ws2, _ = E.e2_sequential(k, v, eta, beta[:, perm], np.ones_like(gamma), W, M, C)
+    assert np.max(np.abs(Ws1 - Ws2)) > 1e-6 * np.max(np.abs(Ws1))

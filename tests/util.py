@@ -18,7 +18,7 @@ def header_functions():
             txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
             names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b([a-z0-9_]+)\s*\(",
                                 txt, flags=re.M)
-    return sorted(set(n for n in names if n.startswith(("ttt_", "e2ttt_"))))
+    return sorted(set(n for n in names if n.startswith(("ttt_", "e2ttt_", "lact_", "tttk_"))))
 
 
 def to_device(w: dict, device="cuda") -> dict:
