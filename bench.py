@@ -382,6 +382,50 @@ def decode_bench(args, c, w, tok, tla, torch):
     print(json.dumps(out), flush=True)
 
 
+def decode_update_bench(args, c, w, tok, tla, torch):
+    """Decode with test-time updates at the 3B shape: a prefill of 8192 + 1
+    tokens, then decode steps with ttt_decode_step_update until one update
+    (the b positions from 8192) has run and b more steps after it; every
+    step timed with HIP events. Reports the p50 of the plain steps, the
+    step that carried the update, and the cost per token amortised over a
+    mini-batch of b decode steps."""
+    b = c["minibatch"]
+    T = 8192 + 1
+    nsteps = 2 * b
+    m = tla.TTT(c, w, max_seq=T + nsteps + 1)
+    m.prefill(tok[:T])
+    m.decode_step(tok[T:T + 1])   # captures the decode graph; position T
+    m.reset()
+    m.prefill(tok[:T])
+    m.sync()
+    logits = torch.empty(c["vocab"], dtype=torch.float32, device="cuda")
+    loss = torch.empty(b, dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
+    upd_at = []
+    ev[0].record()
+    for j in range(nsteps):
+        _, l = m.decode_step_update(tok[T + j:T + j + 1], logits, loss)
+        if l is not None:
+            upd_at.append(j)
+        ev[j + 1].record()
+    torch.cuda.synchronize()
+    m.sync()
+    m.close()
+    ts = [ev[j].elapsed_time(ev[j + 1]) for j in range(nsteps)]
+    plain = sorted(t for j, t in enumerate(ts) if j not in upd_at)
+    p50 = plain[len(plain) // 2]
+    upd_ms = [ts[j] for j in upd_at]
+    amort = (p50 * (b - 1) + (sum(upd_ms) / max(1, len(upd_ms)))) / b
+    out = dict(metric="TTT decode with test-time updates @3B-shape, per-token latency amortised over a mini-batch",
+               value=round(amort, 4), unit="ms/token", n_gpus=1, steps=nsteps, higher_is_better=False,
+               dtype="bf16", data="synthetic",
+               config=dict(workload=f"{args.workload}-shape decode with updates: prefill {T} tokens, then {nsteps} "
+                                    f"decode steps, an update every {b}"),
+               plain_step_p50_ms=round(p50, 3), update_steps=len(upd_at),
+               update_step_ms=[round(x, 3) for x in upd_ms])
+    print(json.dumps(out), flush=True)
+
+
 def pmc_busy(c, T, d):
     """MFMA busy of the attention-forward launches of one step, from a rocprofv3
     --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_INSTS_MFMA
@@ -423,6 +467,8 @@ def main():
     ap.add_argument("--attn-replay", action="store_true", help="one step's attention-forward launches, then exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar="DIR", help="bytes per attention launch from counter runs")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-updates", action="store_true",
+                    help="measure decode with test-time updates every mini-batch instead")
     ap.add_argument("--e2", action="store_true", help="measure the E2-TTT chunk-end kernel instead")
     ap.add_argument("--pmc-busy", metavar="DIR",
                     help="MFMA-busy fraction of the attention forward from a counter run of --attn-replay")
@@ -458,6 +504,10 @@ def main():
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
     w = synth.gen_weights(c, device="cuda")
+    if args.decode_updates:
+        tok = synth.gen_tokens(c, n=8193 + 2 * c["minibatch"] + 1, device="cuda")
+        decode_update_bench(args, c, w, tok, tla, torch)
+        return
     if args.decode:
         tok = synth.gen_tokens(c, n=T + args.decode_steps, device="cuda")
         decode_bench(args, c, w, tok, tla, torch)

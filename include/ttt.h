@@ -150,6 +150,24 @@ ttt_status ttt_prefill(ttt_ctx* ctx, const int32_t* tokens, int64_t T, float* lo
  * update. Requires 1 <= p < max_seq (after a prefill). */
 ttt_status ttt_decode_step(ttt_ctx* ctx, const int32_t* token, float* logits, void* stream);
 
+/* Decode with test-time training continuing into generation ([P2]
+ * "NVIDIA开源TTT-E2E：128K上下文快2.7倍", section 效果惊人: the model keeps
+ * learning from what it reads after the context). The positions consumed
+ * since the last update are trained in groups of minibatch b: a prefill of T
+ * tokens leaves position T - 1 as the first without a target; when this
+ * token completes the targets of the b positions [u, u + b) (u = that
+ * first untrained position), the inner-loop step runs on them first --
+ * forward under the current fast weights (their keys/values stored again),
+ * next-token losses, backward, SGD step on the dynamic MLPs, exactly as for
+ * a prefill mini-batch -- and then this token is decoded as by
+ * ttt_decode_step, under the new weights. loss (device float [b] or NULL)
+ * receives the b losses of such an update; *updated (host, may be NULL) is
+ * set to 1 if one ran, else 0. After a prefill of T = m b + 1 tokens the
+ * updates fall on the same mini-batches, with the same results, as a prefill
+ * of the longer stream. Same requirements and errors as ttt_decode_step. */
+ttt_status ttt_decode_step_update(ttt_ctx* ctx, const int32_t* token, float* logits, float* loss,
+                                  int32_t* updated, void* stream);
+
 /* Copies dynamic block dyn_idx's current fast weights (fp32 master) into
  * device float buffers w1 [Fd, d], w2 [Fd, d], w3 [d, Fd]. */
 ttt_status ttt_get_fast_weights(ttt_ctx* ctx, int32_t dyn_idx, float* w1, float* w2, float* w3,

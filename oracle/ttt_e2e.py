@@ -371,7 +371,10 @@ def ttt_inner_loop(cfg_d: dict, weights, tokens, alpha=None, b=None, reduction=N
             last_logits = z[-1].copy()
     out = dict(loss=loss, dyn=dyn)
     if keep_state:
-        out.update(store=store, weights=w, cfg=cfg, last_logits=last_logits)
+        # trained: positions below it have been used (with their targets) for
+        # an update; T - 1 has no target yet
+        out.update(store=store, weights=w, cfg=cfg, last_logits=last_logits, tokens=list(tokens),
+                   trained=T - 1, alpha=alpha, reduction=reduction)
     return out
 
 
@@ -386,8 +389,42 @@ def decode_step(state: dict, token: int):
             store.V[l] = np.concatenate([store.V[l], np.zeros_like(store.V[l])])
     toks = np.zeros(p + 1, dtype=np.int64)
     toks[p] = token
+    if "tokens" in state:
+        state["tokens"].append(int(token))
     z, _ = forward_positions(cfg, w, state["dyn"], store, toks, p, p + 1, keep=False)
     return z[0]
+
+
+def decode_step_update(state: dict, token: int):
+    """Decode with test-time training continuing into generation ([P2]
+    "NVIDIA开源TTT-E2E：128K上下文快2.7倍", section 效果惊人: the model keeps
+    learning from the tokens it reads after the context). Reading adopted:
+    the positions consumed since the last update are trained in groups of b:
+    when the token x_p arrives and the b positions [u, u + b) before p = u + b
+    have all their targets (the last one is x_p), the inner-loop step runs on
+    them (forward under the current fast weights, their keys/values stored
+    again, loss, backward, SGD) before position p is decoded under the new
+    weights. Continues a state of ttt_inner_loop(keep_state=True), after
+    which u = T - 1.
+    Returns (logits [V] for position p, the b losses of an update made
+    before it or None)."""
+    cfg, w, store = state["cfg"], state["weights"], state["store"]
+    p = store.n
+    while p + 1 > store.K[0].shape[0]:
+        for l in range(cfg.L):
+            store.K[l] = np.concatenate([store.K[l], np.zeros_like(store.K[l])])
+            store.V[l] = np.concatenate([store.V[l], np.zeros_like(store.V[l])])
+    state["tokens"].append(int(token))
+    toks = np.asarray(state["tokens"], dtype=np.int64)
+    u = state["trained"]
+    losses = None
+    if p - u >= cfg.b:
+        loss = np.zeros(p, dtype=store.K[0].dtype)
+        minibatch_step(cfg, w, state["dyn"], store, toks, u, u + cfg.b, state["alpha"], state["reduction"], loss)
+        losses = loss[u:u + cfg.b].copy()
+        state["trained"] = u + cfg.b
+    z, _ = forward_positions(cfg, w, state["dyn"], store, toks, p, p + 1, keep=False)
+    return z[0], losses
 
 
 def plain_forward(cfg_d: dict, weights, tokens, dtype=np.float64, return_logits=False):

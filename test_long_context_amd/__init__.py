@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         L.ttt_init.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), vp, ctypes.POINTER(vp)]
         L.ttt_prefill.argtypes = [vp, vp, i64, vp, vp, vp]
         L.ttt_decode_step.argtypes = [vp, vp, vp, vp]
+        L.ttt_decode_step_update.argtypes = [vp, vp, vp, vp, ctypes.POINTER(i32), vp]
         L.ttt_get_fast_weights.argtypes = [vp, i32, vp, vp, vp, vp]
         L.ttt_reset.argtypes = [vp, vp]
         L.ttt_sync.argtypes = [vp, vp]
@@ -101,9 +102,10 @@ def lib() -> ctypes.CDLL:
         L.tttk_attn_bwd_workspace.restype = i64
         L.tttk_ce.argtypes = [i32, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
         L.tttk_dw_sgd.argtypes = [i32, ctypes.POINTER(DwProblem), i32, f32, i32, vp]
-        for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_get_fast_weights", "ttt_reset",
-                  "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan", "ttt_timing_enable", "ttt_timing_read", "tttk_gemm",
-                  "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce", "tttk_dw_sgd"):
+        for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_decode_step_update", "ttt_get_fast_weights",
+                  "ttt_reset", "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan",
+                  "ttt_timing_enable", "ttt_timing_read", "tttk_gemm", "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce",
+                  "tttk_dw_sgd"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -186,6 +188,20 @@ class TTT:
         self._chk(lib().ttt_decode_step(self.h, _ptr(token), _ptr(logits), _stream(stream)),
                   "ttt_decode_step")
         return logits
+
+    def decode_step_update(self, token, logits=None, loss=None, stream=None):
+        """Decode with test-time updates (ttt_decode_step_update): returns
+        (logits, loss or None); loss holds the b losses of an update made
+        before this token's decode."""
+        import torch
+        if logits is None:
+            logits = torch.empty(self.cfg["vocab"], dtype=torch.float32, device=token.device)
+        if loss is None:
+            loss = torch.empty(self.cfg["minibatch"], dtype=torch.float32, device=token.device)
+        upd = ctypes.c_int32(0)
+        self._chk(lib().ttt_decode_step_update(self.h, _ptr(token), _ptr(logits), _ptr(loss), ctypes.byref(upd),
+                                               _stream(stream)), "ttt_decode_step_update")
+        return logits, (loss if upd.value else None)
 
     def fast_weights(self, i: int, stream=None):
         import torch

@@ -102,6 +102,9 @@ struct ttt_ctx {
   float* dec = nullptr;                      // decode scratch
   int dec_split = 1;
   int32_t* d_tok = nullptr;                  // decode input token
+  int32_t* tokhist = nullptr;                // [max_seq] every token consumed (prefill and decode)
+  float* dloss = nullptr;                    // [b] losses of a decode-time update (when the caller passes none)
+  int64_t trained = 0;                       // positions below it were used, with their targets, by an update
   // fast-weight updates run on side streams, overlapping the rest of the
   // backward; their inputs are per dynamic block so that the main stream
   // never overwrites what an update still reads. A block's two update
@@ -366,11 +369,12 @@ AttnArgs attn_args(ttt_ctx* c, int l, const void* q, void* o, float* lse, int n,
 }
 
 // ------------------------------------------------------------ prefix phase
-ttt_status run_prefix(ttt_ctx* c, const int32_t* tok, int64_t T, hipStream_t st) {
+// Positions [pb, pe) (tok: the token of position 0 onwards).
+ttt_status run_prefix(ttt_ctx* c, const int32_t* tok, int64_t pb, int64_t pe, hipStream_t st) {
   const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, F = c->F;
   const float eps = c->cfg.rms_eps;
-  for (int64_t p0 = 0; p0 < T; p0 += c->slab) {
-    const int n = (int)std::min<int64_t>(c->slab, T - p0);
+  for (int64_t p0 = pb; p0 < pe; p0 += c->slab) {
+    const int n = (int)std::min<int64_t>(c->slab, pe - p0);
     float* h = c->hres + p0 * d;
     TCALL(KC_OT, 0, 0, embed_gather(c->dt, tok + p0, n, c->embed, d, h, c->V, c->d_err, st));
     for (int l = 0; l <= c->s; ++l) {
@@ -822,7 +826,10 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     c->d_pos = (int64_t*)p;
     A(&p, 64);
     c->d_tok = (int32_t*)p;
+    A(&p, (size_t)c->max_seq * sizeof(int32_t));
+    c->tokhist = (int32_t*)p;
   }
+  Af(&c->dloss, (size_t)b);
   c->dec_split = decode_attn_splits(c->dt, c->H, c->Hk, c->dh, c->k, c->dt == DT::BF16);
   // bf16 update products: two GEMM launches with the SGD epilogue on two
   // side streams (default), or, with TTT_UPDATE_KERNEL=fused, both in one
@@ -924,6 +931,7 @@ ttt_status ttt_reset(ttt_ctx* c, void* stream) {
     }
   }
   c->pos = 0;
+  c->trained = 0;
   return TTT_OK;
 }
 
@@ -934,7 +942,8 @@ ttt_status ttt_prefill(ttt_ctx* c, const int32_t* tok, int64_t T, float* loss, f
   if (T < 2 || T > c->max_seq) return fail(c, TTT_ERR_INVALID_ARG, "T outside [2, max_seq]");
   if (c->pos != 0) return fail(c, TTT_ERR_STATE, "prefill needs position 0 (call ttt_reset)");
   hipStream_t st = (hipStream_t)stream;
-  ttt_status r = run_prefix(c, tok, T, st);
+  HIPCHK(c, hipMemcpyAsync(c->tokhist, tok, (size_t)T * sizeof(int32_t), hipMemcpyDeviceToDevice, st));
+  ttt_status r = run_prefix(c, tok, 0, T, st);
   if (r != TTT_OK) return r;
   const float red_sum = c->cfg.reduction == TTT_LOSS_SUM;
   for (int64_t a0 = 0; a0 < T; a0 += c->b) {
@@ -957,6 +966,7 @@ ttt_status ttt_prefill(ttt_ctx* c, const int32_t* tok, int64_t T, float* loss, f
   HIPCHK(c, hipStreamWaitEvent(st, c->ev_join, 0));
   HIPCHK(c, set_pos(c->d_pos, T, st));
   c->pos = T;
+  c->trained = T - 1;  // position T - 1 has no target yet
   return TTT_OK;
 }
 
@@ -967,6 +977,7 @@ ttt_status ttt_decode_step(ttt_ctx* c, const int32_t* token, float* logits, void
     return fail(c, TTT_ERR_STATE, "decode needs a prefilled context with position < max_seq");
   hipStream_t st = (hipStream_t)stream;
   HIPCHK(c, hipMemcpyAsync(c->d_tok, token, sizeof(int32_t), hipMemcpyDeviceToDevice, st));
+  HIPCHK(c, hipMemcpyAsync(c->tokhist + c->pos, token, sizeof(int32_t), hipMemcpyDeviceToDevice, st));
   const char* eg = getenv("TTT_DECODE_GRAPH");
   const bool use_graph = !(eg && eg[0] == '0');
   if (use_graph) {
@@ -983,6 +994,39 @@ ttt_status ttt_decode_step(ttt_ctx* c, const int32_t* token, float* logits, void
   HIPCHK(c, bump_pos(c->d_pos, st));
   ++c->pos;
   return TTT_OK;
+}
+
+ttt_status ttt_decode_step_update(ttt_ctx* c, const int32_t* token, float* logits, float* loss,
+                                  int32_t* updated, void* stream) {
+  if (!c) return TTT_ERR_INVALID_ARG;
+  if (updated) *updated = 0;
+  if (!token || !logits) return fail(c, TTT_ERR_INVALID_ARG, "null token or logits");
+  if (c->pos < 1 || c->pos >= c->max_seq)
+    return fail(c, TTT_ERR_STATE, "decode needs a prefilled context with position < max_seq");
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t p = c->pos, u = c->trained;
+  if (p - u >= c->b) {
+    // the b positions [u, u + b) have all their targets (the last is at
+    // most this token): the inner-loop step on them, as a prefill
+    // mini-batch would run it
+    const int n = c->b;
+    HIPCHK(c, hipMemcpyAsync(c->tokhist + p, token, sizeof(int32_t), hipMemcpyDeviceToDevice, st));
+    ttt_status r = run_prefix(c, c->tokhist, u, u + n, st);
+    if (r != TTT_OK) return r;
+    r = loop_forward(c, c->tokhist, u, n, st);
+    if (r != TTT_OK) return r;
+    const float scale = c->cfg.reduction == TTT_LOSS_SUM ? 1.f : 1.f / n;
+    TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
+          ce_fwd_bwd(c->dt, c->logits, n, n, c->V, c->tokhist + u + 1, scale, loss ? loss : c->dloss, c->dz,
+                     c->d_err, st));
+    r = loop_backward(c, u, n, st);
+    if (r != TTT_OK) return r;
+    HIPCHK(c, hipEventRecord(c->ev_join, c->side));
+    HIPCHK(c, hipStreamWaitEvent(st, c->ev_join, 0));
+    c->trained = u + n;
+    if (updated) *updated = 1;
+  }
+  return ttt_decode_step(c, token, logits, stream);
 }
 
 ttt_status ttt_get_fast_weights(ttt_ctx* c, int32_t i, float* w1, float* w2, float* w3, void* stream) {

@@ -95,3 +95,65 @@ def test_decode_needs_prefill():
         m.decode_step(torch.zeros(1, dtype=torch.int32, device="cuda"))
     assert ei.value.code == -5  # TTT_ERR_STATE
     m.close()
+
+
+# ------------------------------------------------------- decode with updates
+def check_updates(c, T, N, tol_z, tol_l, tol_w, dtype):
+    """Prefill T tokens, then decode with updates through position N - 1,
+    against the oracle's decode_step_update on its own prefill state: logits
+    of every step, the losses of every update, and the final fast weights
+    (update-normalised)."""
+    import test_long_context_amd as tla
+    from tests.util import dw_err
+    say(f"decode-update case: L={c['n_layers']} d={c['d_model']} H={c['n_heads']}/{c['n_kv_heads']}x{c['head_dim']} "
+        f"b={c['minibatch']} dtype={c['dtype']} T={T} N={N}")
+    w = synth.gen_weights(c)
+    tok = synth.gen_tokens(c, n=N)
+    m = tla.TTT(c, to_device(w), max_seq=N + 1)
+    m.prefill(tok[:T].cuda())
+    got = []
+    for p in range(T, N):
+        z, l = m.decode_step_update(tok[p:p + 1].cuda())
+        got.append((z.cpu().numpy(), None if l is None else l.cpu().numpy()))
+    m.sync()
+    fw = [tuple(x.cpu().numpy() for x in m.fast_weights(i)) for i in range(len(w["dyn"]))]
+    m.close()
+    wn = synth.weights_to_numpy(w, dtype)
+    st = O.ttt_inner_loop(c, wn, tok[:T].numpy(), dtype=dtype, keep_state=True)
+    n_upd = 0
+    for j, p in enumerate(range(T, N)):
+        zr, lr = O.decode_step_update(st, int(tok[p]))
+        zg, lg = got[j]
+        e = float(np.abs(zg - zr).max() / np.abs(zr).max())
+        assert np.all(np.isfinite(zg))
+        assert (lg is None) == (lr is None), p
+        if lr is not None:
+            el = float(np.max(np.abs(lg - lr) / np.abs(lr)))
+            say(f"  update before position {p}: loss rel err {el:.3e}; logit rel err {e:.3e}")
+            assert el < tol_l
+            n_upd += 1
+        assert e < tol_z, (p, e)
+    errs = [dw_err(g, st["dyn"][i][k], wn["dyn"][i][k])
+            for i, gs in enumerate(fw) for k, g in zip(("w1", "w2", "w3"), gs)]
+    say(f"  {n_upd} updates; final fast weights err {max(errs):.3e}")
+    assert n_upd >= 2
+    assert max(errs) < tol_w
+
+
+def test_decode_updates_tiny_fp32():
+    # T = 2b + 1: the decode-time mini-batches continue the prefill's tiling
+    c = synth.config("tiny")
+    check_updates(c, T=33, N=81, tol_z=1e-5, tol_l=1e-5, tol_w=1e-5, dtype=np.float64)
+
+
+def test_decode_updates_tiny_fp32_gqa_off_grid():
+    # a prefill length that does not end a mini-batch; GQA, two dynamic blocks
+    c = synth.config("tiny", n_layers=4, n_kv_heads=2, n_dynamic=2, window=24, minibatch=16)
+    check_updates(c, T=50, N=99, tol_z=1e-5, tol_l=1e-5, tol_w=1e-5, dtype=np.float64)
+
+
+def test_decode_updates_bf16_small_gqa_dh128():
+    c = synth.config("125m", n_layers=4, d_model=256, n_heads=4, n_kv_heads=2, head_dim=128,
+                     ffn_hidden=512, dyn_ffn_hidden=512, vocab=4096, window=256, minibatch=128,
+                     n_dynamic=2, alpha=0.01)
+    check_updates(c, T=300, N=560, tol_z=2e-2, tol_l=2e-2, tol_w=5e-2, dtype=np.float32)

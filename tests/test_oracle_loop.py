@@ -212,3 +212,58 @@ def _wrap_bwd_rope(bwd, bad, orig):
         finally:
             O.rope = orig
     return f
+
+
+# ------------------------------------------------------- decode with updates
+def _tiny(**over):
+    c = synth.config("tiny", **over)
+    w = synth.weights_to_numpy(synth.gen_weights(c))
+    return c, w
+
+
+@pytest.mark.parametrize("over", [dict(), dict(n_layers=3, n_kv_heads=2, n_dynamic=2, window=24)])
+def test_decode_with_updates_equals_prefill_of_the_longer_stream(over):
+    """After a prefill of T = 2b + 1 tokens, decoding with updates through
+    position N - 1 = 4b trains the two mini-batches [2b, 3b) and [3b, 4b) at
+    positions 3b and 4b: the fast weights, the losses of those positions and
+    the last logits equal a prefill of the N = 4b + 1 tokens."""
+    c, w = _tiny(**over)
+    b = c["minibatch"]
+    T, N = 2 * b + 1, 4 * b + 1
+    tok = synth.gen_tokens(c, n=N).numpy()
+    st = O.ttt_inner_loop(c, w, tok[:T], keep_state=True)
+    losses = {}
+    for p in range(T, N):
+        z, l = O.decode_step_update(st, int(tok[p]))
+        if l is not None:
+            losses[p] = l
+    assert sorted(losses) == [3 * b, 4 * b]
+    ref = O.ttt_inner_loop(c, w, tok, keep_state=True)
+    for i in range(len(w["dyn"])):
+        for k in ("w1", "w2", "w3"):
+            np.testing.assert_allclose(st["dyn"][i][k], ref["dyn"][i][k], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(losses[3 * b], ref["loss"][2 * b:3 * b], rtol=1e-12)
+    np.testing.assert_allclose(losses[4 * b], ref["loss"][3 * b:4 * b], rtol=1e-12)
+    np.testing.assert_allclose(z, ref["last_logits"], rtol=1e-11, atol=1e-13)
+
+
+def test_decode_with_updates_at_alpha_zero_is_the_plain_model():
+    """alpha = 0 and a prefill length that does not end a mini-batch: the
+    updates change nothing, so every decode logit and every loss of the
+    trained positions equal the plain forward of the whole stream."""
+    c, w = _tiny(alpha=0.0)
+    b = c["minibatch"]
+    T, N = b + 7, 3 * b + 12
+    tok = synth.gen_tokens(c, n=N).numpy()
+    st = O.ttt_inner_loop(c, w, tok[:T], keep_state=True)
+    _, zref = O.plain_forward(c, w, tok, return_logits=True)
+    lref = O.plain_forward(c, w, tok)
+    n_upd = 0
+    for p in range(T, N):
+        z, l = O.decode_step_update(st, int(tok[p]))
+        np.testing.assert_allclose(z, zref[p], rtol=1e-12, atol=1e-13)
+        if l is not None:
+            np.testing.assert_allclose(l, lref[p - b:p], rtol=1e-12)
+            n_upd += 1
+    # training groups start at T - 1 (the first position without a target)
+    assert n_upd == (N - 1 - (T - 1)) // b
