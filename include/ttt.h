@@ -147,7 +147,10 @@ ttt_status ttt_prefill(ttt_ctx* ctx, const int32_t* tokens, int64_t T, float* lo
 /* Forward of one token (device int32 [1]) at the current position p under
  * the current fast weights, appending its keys/values to the window;
  * logits (device float [V]) are the prediction for position p + 1. No
- * update. Requires 1 <= p < max_seq (after a prefill). */
+ * update. Requires 1 <= p < max_seq (after a prefill). The token is read
+ * from device memory so that the per-token launch sequence can be captured
+ * once as a HIP graph and replayed. Cost independent of the context length
+ * ([P1] 实验结果 -> 推理延迟: latency flat in the context). */
 ttt_status ttt_decode_step(ttt_ctx* ctx, const int32_t* token, float* logits, void* stream);
 
 /* Decode with test-time training continuing into generation ([P2]
@@ -169,11 +172,15 @@ ttt_status ttt_decode_step_update(ttt_ctx* ctx, const int32_t* token, float* log
                                   int32_t* updated, void* stream);
 
 /* Copies dynamic block dyn_idx's current fast weights (fp32 master) into
- * device float buffers w1 [Fd, d], w2 [Fd, d], w3 [d, Fd]. */
+ * device float buffers w1 [Fd, d], w2 [Fd, d], w3 [d, Fd]: the compressed
+ * context W_T ([P1] 持续学习框架: the sequence is learned into the weights). */
 ttt_status ttt_get_fast_weights(ttt_ctx* ctx, int32_t dyn_idx, float* w1, float* w2, float* w3,
                                 void* stream);
 
-/* Restores W0 and position 0 (the rings are overwritten before being read). */
+/* Restores W0 and position 0 (the rings are overwritten before being read):
+ * the per-sequence restart of the inner loop ([P1] 完整PyTorch实现: the
+ * sketch snapshots the weights before the inner loop and restores them
+ * after it). */
 ttt_status ttt_reset(ttt_ctx* ctx, void* stream);
 
 /* Synchronises the stream and reports device flags raised since the last
