@@ -53,6 +53,18 @@ ROOF_CLASS = "dw_sgd"                          # the fused dW + SGD update produ
 ATTN_CLASSES = ("attn_prefix", "attn_loop")    # the attention forward kernel
 TIMED_CLASSES = (ROOF_CLASS, "ce") + ATTN_CLASSES
 ROOF_SOURCES = ("test_long_context_amd/csrc/attn2.hip", "test_long_context_amd/csrc/common.hpp")
+UPD_SOURCES = ("test_long_context_amd/csrc/gemm_impl.hpp", "test_long_context_amd/csrc/gemm_tn.hip",
+               "test_long_context_amd/csrc/gemm.hip", "test_long_context_amd/csrc/common.hpp",
+               "test_long_context_amd/csrc/kernels.hpp")
+
+# HBM traffic of the update products (the roofline kernel) from rocprofv3
+# --pmc FETCH_SIZE / WRITE_SIZE of --update-replay, scaled by the
+# --copy-probe counters (printed by --pmc-update-summary), bytes per launch
+# averaged over a block's dW12 and dW3 launches, keyed by (workload, source
+# hash): valid only for the kernel source the counters were taken on.
+UPD_TRAFFIC = {
+    ("3b", "17fa5e09f2360ba5"): 604996056,
+}
 
 # HBM traffic of the attention forward from rocprofv3 --pmc FETCH_SIZE /
 # WRITE_SIZE (--attn-replay, scaled by the --copy-probe counters; printed by
@@ -72,12 +84,61 @@ MFMA_BUSY = {
 }
 
 
-def roof_source_hash() -> str:
+def roof_source_hash(files=ROOF_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in ROOF_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def update_replay(c, tla, torch, blocks=2):
+    """The update products of `blocks` dynamic blocks at the workload's
+    shape, launched as the engine launches them (dW3 = dY^T Hmid, then dW12
+    = dH12^T U, each a GEMM with the SGD epilogue writing the fp32 master,
+    the bf16 working copy and its low term)."""
+    d, Fd, b = c["d_model"], c["dyn_ffn_hidden"], c["minibatch"]
+    bf = torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(0)
+    gt = (torch.randn(b, d, device="cuda", generator=g) * 0.1).to(bf)
+    hm = (torch.randn(b, Fd, device="cuda", generator=g) * 0.1).to(bf)
+    dh12 = (torch.randn(b, 2 * Fd, device="cuda", generator=g) * 0.1).to(bf)
+    xn = (torch.randn(b, d, device="cuda", generator=g) * 0.1).to(bf)
+    m3 = torch.randn(d, Fd, device="cuda", generator=g) * 0.02
+    m12 = torch.randn(2 * Fd, d, device="cuda", generator=g) * 0.02
+    h3, l3 = torch.empty(d, Fd, dtype=bf, device="cuda"), torch.empty(d, Fd, dtype=bf, device="cuda")
+    h12, l12 = torch.empty(2 * Fd, d, dtype=bf, device="cuda"), torch.empty(2 * Fd, d, dtype=bf, device="cuda")
+    for _ in range(blocks):
+        tla.gemm(gt, hm, d, Fd, b, "sgd", m3, a_kmajor=False, b_kmajor=False, C2=h3, C3=l3, scale=c["alpha"])
+        tla.gemm(dh12, xn, 2 * Fd, d, b, "sgd", m12, a_kmajor=False, b_kmajor=False, C2=h12, C3=l12,
+                 scale=c["alpha"])
+    torch.cuda.synchronize()
+    print(json.dumps(dict(launches=2 * blocks)), flush=True)
+
+
+def pmc_update_summary(c, dirs, workload):
+    """Bytes per update launch from FETCH_SIZE and WRITE_SIZE runs of
+    --update-replay and of --copy-probe (each counter scaled by copy bytes /
+    copy counter), averaged over the dW3 and dW12 launches."""
+    def read(d, name_part):
+        f = os.path.join(d, "run_counter_collection.csv")
+        with open(f) as fh:
+            return [float(r["Counter_Value"]) * 1024 for r in csv.DictReader(fh) if name_part in r["Kernel_Name"]]
+    fetch, write = read(dirs[0], "gemm_bf16_kernel"), read(dirs[1], "gemm_bf16_kernel")
+    cf, cw = read(dirs[2], "copyBuffer"), read(dirs[3], "copyBuffer")
+    copy_bytes = float(1 << 30)
+    fs, ws = copy_bytes / (sum(cf) / len(cf)), copy_bytes / (sum(cw) / len(cw))
+    assert len(fetch) == len(write) and len(fetch) % 2 == 0, (len(fetch), len(write))
+    n = len(fetch)
+    d, Fd = c["d_model"], c["dyn_ffn_hidden"]
+    algo = 10.0 * 3 * d * Fd / 2   # per launch, averaged over dW3 and dW12
+    out = dict(kernel="gemm_bf16_kernel (SGD epilogue)", workload=workload,
+               source_sha=roof_source_hash(UPD_SOURCES), fetch_scale=round(fs, 4), write_scale=round(ws, 4),
+               launches=n, fetch_bytes_per_launch=round(sum(fetch) / n), write_bytes_per_launch=round(sum(write) / n),
+               traffic_bytes_per_launch=round((sum(fetch) * fs + sum(write) * ws) / n),
+               dw3_traffic=round(fetch[0] * fs + write[0] * ws), dw12_traffic=round(fetch[1] * fs + write[1] * ws),
+               algorithmic_bytes_per_launch=round(algo))
+    print(json.dumps(out), flush=True)
 
 
 def copy_probe():
@@ -466,6 +527,9 @@ def main():
     ap.add_argument("--decode", action="store_true", help="measure decode latency instead of prefill throughput")
     ap.add_argument("--attn-replay", action="store_true", help="one step's attention-forward launches, then exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar="DIR", help="bytes per attention launch from counter runs")
+    ap.add_argument("--update-replay", action="store_true", help="two blocks' update launches, then exit")
+    ap.add_argument("--pmc-update-summary", nargs=4, metavar="DIR",
+                    help="bytes per update launch from counter runs of --update-replay and --copy-probe")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-updates", action="store_true",
                     help="measure decode with test-time updates every mini-batch instead")
@@ -494,6 +558,12 @@ def main():
     T = args.seq or c["seq"]
     if args.pmc_summary:
         pmc_summary(c, T, args.pmc_summary, args.workload)
+        return
+    if args.pmc_update_summary:
+        pmc_update_summary(c, args.pmc_update_summary, args.workload)
+        return
+    if args.update_replay:
+        update_replay(c, tla, torch)
         return
     if args.pmc_busy:
         pmc_busy(c, T, args.pmc_busy)
@@ -572,8 +642,9 @@ def main():
     upd = live[ROOF_CLASS]
     u_avg, u_gbs = rate(upd, "bytes")
     nu = max(1, upd["launches"])
+    utr = UPD_TRAFFIC.get((args.workload, roof_source_hash(UPD_SOURCES)))
     roof = dict(bound="hbm", achieved=round(u_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                frac=round(u_gbs / PEAK_HBM_GBS, 4), traffic=None,
+                frac=round(u_gbs / PEAK_HBM_GBS, 4), traffic=None if utr is None else utr,
                 kernel="fused dW = X^T dH product with the fp32 SGD update of the fast weights in its epilogue "
                        "(gemm_bf16_kernel, SGD epilogue)",
                 algorithmic_bytes_per_launch=round(upd["bytes"] / nu),
@@ -581,6 +652,8 @@ def main():
                 launches_per_step=upd["launches"] // args.steps, avg_launch_us=round(u_avg * 1e6, 2),
                 mfma_tflops=round(upd["flops"] / nu / u_avg / 1e12, 1) if u_avg > 0 else None,
                 share_of_step=round(upd["ms"] / args.steps / ms, 4),
+                traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE of --update-replay, "
+                             "copy-scaled), averaged over a block's dW3 and dW12 launches",
                 note="durations measured on the update's side streams, beside the main stream's kernels")
     ce = live["ce"]
     c_avg, c_gbs = rate(ce, "bytes")
