@@ -305,6 +305,30 @@ def e2_bench(args, tla, torch, synth):
         if i >= max(1, args.warmup):
             lts.append(a.elapsed_time(b))
     lms = sorted(lts)[len(lts) // 2]
+    # the token mixer's TTT path on its own workload (projections, SiLU +
+    # L2 norm, input-dependent scalars, outputs and chunk-end state)
+    mc = synth.E2_MIXER_CONFIG
+    mx = synth.gen_e2_mixer(mc["heads"], mc["seq"], mc["dim"], mc["d_model"], mc["seed"], device="cuda")
+    mW, mM = mx["W"].clone(), mx["M"].clone()
+    mo = torch.empty(mc["seq"], mc["heads"] * mc["dim"], device="cuda")
+    mts = []
+    for i in range(max(1, args.warmup) + args.steps):
+        mW.copy_(mx["W"])
+        mM.copy_(mx["M"])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tla.e2ttt_mixer_forward(mx["x"], mx["wqkv"], mx["bias"], mc["eta_base"], mc["alpha_base"], mc["tau"], mW, mM,
+                                mc["heads"], mc["chunk"], out=mo)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= max(1, args.warmup):
+            mts.append(a.elapsed_time(b))
+    mms = sorted(mts)[len(mts) // 2]
+    proj_flops = 2.0 * mc["seq"] * mc["d_model"] * (3 * mc["heads"] * mc["dim"] + 3 * mc["heads"])
+    out["mixer"] = dict(ms_per_step=round(mms, 4), value=round(mc["seq"] / (mms * 1e-3), 1), unit="tokens/s",
+                        config=f"E2-TTT token mixer, TTT path: T={mc['seq']}, d_model={mc['d_model']}, "
+                               f"H={mc['heads']} x {mc['dim']}, C={mc['chunk']}",
+                        projection_gflop=round(proj_flops / 1e9, 1))
     out["lact_baseline"] = dict(ms_per_step=round(lms, 4), value=round(H * T / (lms * 1e-3), 1),
                                 unit="token-heads/s", e2_cost_vs_lact=round(ms / lms - 1.0, 4),
                                 kernel="lact_chunk_scan (chunk-mean momentum, one aggregation per chunk)")

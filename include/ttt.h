@@ -271,6 +271,26 @@ int64_t e2ttt_chunk_scan_noalloc_max_bytes(void);
 ttt_status lact_chunk_scan(const void* k, const void* v, const float* eta, const float* beta, float* W,
                            float* M, int32_t H, int64_t T, int32_t D, int32_t C, void* stream);
 
+/* The E2-TTT token mixer's TTT path with a linear fast weight ([P3] 方法细节:
+ * 混合模型架构设计 -- shared projections, SiLU and L2 normalisation of q and
+ * k; 依赖于输入的动态参数化 -- eta_t = eta_base sigma(z_eta), beta_t =
+ * sigma(z_beta)^(1/tau), gamma_t = 1 - eta_t alpha_base sigma(z_alpha);
+ * Algorithm 1 -- outputs under the chunk-start state, then the chunk-end
+ * state of e2ttt_chunk_scan with the page's G_t, the negative gradient
+ * (v_t - W0 k_t) k_t^T). x: device bf16 [T, dm]; wqkv: device bf16
+ * [3 H D + 3 H, dm], rows Wq (H D), Wk (H D), Wv (H D), then the eta, beta
+ * and alpha logit rows (H each); bias: device float [3 H] added to the
+ * logits. q, k, v are kept in bf16 and eta, beta, gamma in float between the
+ * steps. out: device float [T, H D], o_t = W q_t with W the state at the
+ * start of t's chunk; W, M: device float [H, D, D], updated in place. D 128
+ * or 64, C a multiple of 64 up to 2048, dm a multiple of 8, pointers 16-byte
+ * aligned. Not built: the SwiGLU fast-weight net and the gate that mixes
+ * this path with sliding-window attention. Uses (and grows) the same cached
+ * work buffer as e2ttt_chunk_scan, so the two must not run concurrently. */
+ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
+                               float alpha_base, float tau, float* W, float* M, float* out, int32_t H,
+                               int64_t T, int32_t D, int32_t dm, int32_t C, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

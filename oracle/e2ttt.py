@@ -116,3 +116,64 @@ def lact_chunked(k, v, eta, beta, W, M, C, sign=1.0):
             M[h] = np.mean(beta[h, a:e]) * M[h] + G
             W[h] = W[h] + M[h]
     return W, M
+
+
+def _bf16(a):
+    """Round to bfloat16 (round to nearest even, through float32) and back to
+    float64: the storage precision of the chunk computation's k, v, q."""
+    import torch
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def mixer_inputs(x, wqkv, bias, eta_base, alpha_base, tau, H, D):
+    """The E2-TTT token mixer's per-token inputs from the layer input x [T, dm]
+    ([P3] 方法细节, 混合模型架构设计 and 依赖于输入的动态参数化): one
+    projection x wqkv^T gives shared queries, keys and values (H heads of D)
+    and three scalar logits per head (rows of wqkv in that order, plus bias);
+    the TTT path takes q, k through SiLU and L2 normalisation over each head;
+      eta_t = eta_base sigma(z_eta),  beta_t = sigma(z_beta)^(1 / tau),
+      alpha_t = alpha_base sigma(z_alpha),  gamma_t = 1 - eta_t alpha_t.
+    Returns q, k, v [H, T, D] (bfloat16 values, the chunk computation's input
+    precision) and eta, beta, gamma [H, T] (float32 values)."""
+    x = np.asarray(x, np.float64)
+    P = x @ np.asarray(wqkv, np.float64).T
+    T = x.shape[0]
+    HD = H * D
+
+    def heads(a):
+        return a.reshape(T, H, D).transpose(1, 0, 2)
+
+    def silu_l2(a):
+        a = a / (1.0 + np.exp(-a))
+        return a / np.linalg.norm(a, axis=-1, keepdims=True)
+    q = silu_l2(heads(P[:, :HD]))
+    k = silu_l2(heads(P[:, HD:2 * HD]))
+    v = heads(P[:, 2 * HD:3 * HD])
+    z = P[:, 3 * HD:3 * HD + 3 * H] + np.asarray(bias, np.float64)
+    sig = 1.0 / (1.0 + np.exp(-z))
+    eta = eta_base * sig[:, :H]
+    beta = sig[:, H:2 * H] ** (1.0 / tau)
+    alpha = alpha_base * sig[:, 2 * H:]
+    gamma = 1.0 - eta * alpha
+    f32 = lambda a: np.asarray(a.T, np.float32).astype(np.float64)
+    return _bf16(q), _bf16(k), _bf16(v), f32(eta), f32(beta), f32(gamma)
+
+
+def e2_mixer(x, wqkv, bias, eta_base, alpha_base, tau, W, M, H, D, C, sign=-1.0):
+    """The E2-TTT token mixer's TTT path with a linear fast weight, chunk by
+    chunk ([P3] Algorithm 1): outputs o_t = W q_t with W the state at the
+    start of t's chunk (line 1), then the chunk-end state by Proposition 3.1
+    (lines 2-7), with the page's G_t, the negative gradient of
+    1/2 ||W0 k_t - v_t||^2 (sign = -1; descent). Returns (outputs [T, H, D],
+    final W, final M)."""
+    q, k, v, eta, beta, gamma = mixer_inputs(x, wqkv, bias, eta_base, alpha_base, tau, H, D)
+    T = q.shape[1]
+    W = np.array(W, np.float64)
+    M = np.array(M, np.float64)
+    out = np.zeros((T, H, D))
+    for a in range(0, T, C):
+        e = min(T, a + C)
+        for h in range(H):
+            out[a:e, h] = q[h, a:e] @ W[h].T
+        W, M = e2_closed_form(k[:, a:e], v[:, a:e], eta[:, a:e], beta[:, a:e], gamma[:, a:e], W, M, e - a, sign)
+    return out, W, M

@@ -65,6 +65,13 @@ CONFIGS: Dict[str, dict] = {
 # E2-TTT chunk-end workload.
 E2_CONFIG = dict(heads=16, seq=32768, dim=128, chunk=2048, seed=5)
 
+# E2-TTT token-mixer workload: the same heads and length, layer width
+# 16 x 128, the pages' training chunk of 512, and scalar rates that keep the
+# chunked dynamics bounded on synthetic inputs (SiLU + L2-normalised keys are
+# strongly correlated, so the per-chunk gradients add up coherently).
+E2_MIXER_CONFIG = dict(heads=16, seq=32768, dim=128, d_model=2048, chunk=512, eta_base=1e-4, alpha_base=0.5,
+                       tau=4.0, seed=6)
+
 
 def config(name: str, **overrides) -> dict:
     c = dict(CONFIGS[name])
@@ -220,3 +227,21 @@ def gen_e2(heads: int, seq: int, dim: int, seed: int, device="cpu") -> dict:
     W = (normal(seed, 6, heads * dim * dim, device) * 0.02).to(torch.float32).view(heads, dim, dim)
     M = torch.zeros(heads, dim, dim, dtype=torch.float32, device=device)
     return dict(k=k, v=v, eta=eta, beta=beta, gamma=gamma, W=W, M=M)
+
+
+def gen_e2_mixer(heads: int, seq: int, dim: int, d_model: int, seed: int, device="cpu") -> dict:
+    """x ~ N(0, 1) [T, d_model] and wqkv [3 H D + 3 H, d_model] (rows Wq, Wk ~
+    N(0, 1/d_model); Wv ~ N(0, 1/(d_model D)), so values have about unit norm
+    as in the chunk-end workload; the eta, beta, alpha logit rows ~ N(0,
+    1/d_model)), both rounded to bf16; bias [3 H] float = (0, 3, 0) per
+    group (beta starts near 1); W ~ N(0, 0.02^2) float [H, D, D]; M = 0."""
+    H, D, dm = heads, dim, d_model
+    x = normal(seed, 1, seq * dm, device).to(torch.bfloat16).view(seq, dm)
+    rows = 3 * H * D + 3 * H
+    std = torch.full((rows, 1), 1.0 / math.sqrt(dm), dtype=torch.float64, device=device)
+    std[2 * H * D:3 * H * D] /= math.sqrt(D)
+    wqkv = (normal(seed, 2, rows * dm, device).view(rows, dm) * std).to(torch.bfloat16)
+    bias = torch.cat([torch.zeros(H), torch.full((H,), 3.0), torch.zeros(H)]).to(torch.float32).to(device)
+    W = (normal(seed, 3, H * D * D, device) * 0.02).to(torch.float32).view(H, D, D)
+    M = torch.zeros(H, D, D, dtype=torch.float32, device=device)
+    return dict(x=x, wqkv=wqkv, bias=bias, W=W, M=M)

@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.e2ttt_chunk_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
         L.e2ttt_chunk_scan_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
         L.lact_chunk_scan.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
+        L.e2ttt_mixer_forward.argtypes = [vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, vp, vp,
+                                          i32, i64, i32, i32, i32, vp]
         L.e2ttt_chunk_scan_noalloc_max_bytes.argtypes = []
         L.e2ttt_chunk_scan_noalloc_max_bytes.restype = i64
         L.ttt_timing_enable.argtypes = [vp, ctypes.c_uint32]
@@ -103,7 +105,7 @@ def lib() -> ctypes.CDLL:
         L.tttk_ce.argtypes = [i32, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
         L.tttk_dw_sgd.argtypes = [i32, ctypes.POINTER(DwProblem), i32, f32, i32, vp]
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_decode_step_update", "ttt_get_fast_weights",
-                  "ttt_reset", "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan",
+                  "ttt_reset", "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan", "e2ttt_mixer_forward",
                   "ttt_timing_enable", "ttt_timing_read", "tttk_gemm", "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce",
                   "tttk_dw_sgd"):
             getattr(L, f).restype = st
@@ -268,6 +270,22 @@ def lact_chunk_scan(k, v, eta, beta, W, M, chunk: int, stream=None):
     if st != TTT_OK:
         raise TTTError(st, "lact_chunk_scan")
     return W, M
+
+
+def e2ttt_mixer_forward(x, wqkv, bias, eta_base, alpha_base, tau, W, M, heads: int, chunk: int, out=None,
+                        stream=None):
+    """E2-TTT token mixer, TTT path (see include/ttt.h): returns out [T, H D]."""
+    import torch
+    T, dm = x.shape
+    H, D, _ = W.shape
+    assert H == heads
+    if out is None:
+        out = torch.empty(T, H * D, dtype=torch.float32, device=x.device)
+    st = lib().e2ttt_mixer_forward(_ptr(x), _ptr(wqkv), _ptr(bias), float(eta_base), float(alpha_base), float(tau),
+                                   _ptr(W), _ptr(M), _ptr(out), H, T, D, dm, chunk, _stream(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "e2ttt_mixer_forward")
+    return out
 
 
 def e2ttt_chunk_scan_noalloc(k, v, eta, beta, gamma, W, M, chunk: int, stream=None):

@@ -182,6 +182,64 @@ __global__ void __launch_bounds__(E2_ST) lact_scalar_kernel(const float* beta, i
   }
 }
 
+// ------------------------------------------------------ token-mixer inputs
+// [P3] 混合模型架构设计 and 依赖于输入的动态参数化: from the projections
+// P = x wqkv^T (float [T, 3 H D + 3 H]) of one token per workgroup: q, k =
+// L2-normalised SiLU of their head slices, v as projected (all bf16 [H, T, D],
+// the chunk kernel's layout), and per head eta = eta_base sigma(z_eta),
+// beta = sigma(z_beta)^(1/tau), gamma = 1 - eta alpha_base sigma(z_alpha)
+// (float [H, T]; z = scalar logit + bias; eta is stored negated, see
+// below). A group of 16 lanes handles one head; each lane D / 16
+// consecutive features.
+template <int D>
+__global__ void __launch_bounds__(256) mixer_prologue_kernel(const float* __restrict__ P, const float* __restrict__ bias,
+                                                             int H, int64_t T, float eta_base, float alpha_base,
+                                                             float inv_tau, bf16* __restrict__ q, bf16* __restrict__ k,
+                                                             bf16* __restrict__ v, float* __restrict__ eta,
+                                                             float* __restrict__ beta, float* __restrict__ gamma) {
+  constexpr int E = D / 16;  // features per lane
+  const int64_t t = blockIdx.x;
+  const int grp = threadIdx.x >> 4, l = threadIdx.x & 15;
+  const int64_t N = 3LL * H * D + 3LL * H;
+  const float* row = P + t * N;
+  for (int h = grp; h < H; h += 16) {
+    const int f0 = h * D + l * E;
+    // q and k: SiLU, then L2 normalisation over the head's D features
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      float x[E];
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float z = row[(int64_t)which * H * D + f0 + e];
+        x[e] = z / (1.f + __expf(-z));
+        ss += x[e] * x[e];
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 16);
+      const float rn = rsqrtf(ss);
+      bf16* dst = (which == 0 ? q : k) + ((int64_t)h * T + t) * D + l * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e] = (bf16)(x[e] * rn);
+    }
+    bf16* dv = v + ((int64_t)h * T + t) * D + l * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dv[e] = (bf16)row[2LL * H * D + f0 + e];
+    if (l == 0) {
+      const float* z = row + 3LL * H * D;
+      const float se = 1.f / (1.f + __expf(-(z[h] + bias[h])));
+      const float sb = 1.f / (1.f + __expf(-(z[H + h] + bias[H + h])));
+      const float sa = 1.f / (1.f + __expf(-(z[2 * H + h] + bias[2 * H + h])));
+      const float et = eta_base * se;
+      // the page's G_t is the negative gradient (descent) while the chunk
+      // kernels aggregate G_t = (W0 k - v) k^T: hand them -eta_t
+      eta[(int64_t)h * T + t] = -et;
+      beta[(int64_t)h * T + t] = powf(sb, inv_tau);
+      gamma[(int64_t)h * T + t] = 1.f - et * (alpha_base * sa);
+    }
+  }
+}
+
 // ------------------------------------------------------- slice aggregation
 // ------------------------------------------------------------ chunk kernel
 // One launch per chunk; workgroup (16-row block of the state, half of its
@@ -209,12 +267,16 @@ constexpr int E2_NW = 8;  // waves per chunk workgroup
 
 // LACT: the chunk-wise baseline's single aggregation (K^W unused, dW taken
 // as dM): W_out = coef0 W0 + coef1 M0 + dM, M = coef2 M0 + dM.
-template <int D, bool LACT = false>
+// OUT: also the outputs o_t = W0 q_t of the chunk's tokens (Q [H, T, D]
+// bf16, out float [T, H D]): the two workgroups of a 16-row block take one
+// 16-token tile of every 32-token block each, with the same W0 terms.
+template <int D, bool LACT = false, bool OUT = false>
 __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Vv,
                                                        const float* __restrict__ KW, const float* __restrict__ KM,
                                                        const float* __restrict__ coef, const float* __restrict__ Win,
                                                        float* __restrict__ Wout, float* __restrict__ M, int64_t T,
-                                                       int64_t a0, int n, int64_t nch, int64_t r) {
+                                                       int64_t a0, int n, int64_t nch, int64_t r,
+                                                       const bf16* __restrict__ Q = nullptr, float* __restrict__ out = nullptr) {
   constexpr int KS = D / 32;   // 32-wide steps over the feature dimension
   constexpr int JH = D / 2;    // state columns per workgroup
   constexpr int JT = JH / 16;  // their 16-column tiles
@@ -323,6 +385,26 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
         mma16(et[tile], a, wh[s]);
         mma16(et[tile], a, wl[s]);
       }
+    if constexpr (OUT) {
+      // this workgroup's output tile of the block: o = Q W0^T for rows i0 .. i0 + 15
+      const int tile = jh;
+      floatx4 ot = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int tq = min(blk * BT + 16 * tile + c, n - 1);
+      const bf16* Qh = Q + ((int64_t)h * T + a0 + tq) * D;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        Frag8<bf16> aq;
+        aq.v = *(const bf16x8*)(Qh + 32 * s + 8 * g);
+        mma16(ot, aq, wh[s]);
+        mma16(ot, aq, wl[s]);
+      }
+      const int HD = (gridDim.x / (2 * (D / 16))) * D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = blk * BT + 16 * tile + 4 * g + e;
+        if (tok < n) out[(a0 + tok) * HD + (int64_t)h * D + i0 + c] = ot[e];
+      }
+    }
     Frag8<bf16> xwh, xwl, xmh, xml;
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile)
@@ -597,4 +679,112 @@ extern "C" ttt_status lact_chunk_scan(const void* k, const void* v, const float*
     g_e2.dev = dev;
   }
   return lact_run(k, v, eta, beta, W, M, H, T, D, C, g_e2.p, st);
+}
+
+namespace {
+// 256-byte aligned carve-out of the mixer's work buffer
+struct Carve {
+  uintptr_t p;
+  template <typename X>
+  X* take(size_t bytes) {
+    X* r = (X*)p;
+    p = (p + bytes + 255) & ~(uintptr_t)255;
+    return r;
+  }
+};
+
+size_t mixer_work_bytes(int32_t H, int64_t T, int32_t D, int32_t C) {
+  const int64_t N = 3LL * H * D + 3LL * H, nch = (T + C - 1) / C;
+  const size_t al = 256;
+  return (size_t)T * N * 4 + al + 3 * ((size_t)H * T * D * 2 + al) + 5 * ((size_t)H * T * 4 + al) +
+         (size_t)H * nch * 16 + al + (size_t)H * D * D * 4 + al + 256;
+}
+}  // namespace
+
+extern "C" ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
+                                          float alpha_base, float tau, float* W, float* M, float* out, int32_t H,
+                                          int64_t T, int32_t D, int32_t dm, int32_t C, void* stream) {
+  using namespace ttt;
+  if (!x || !wqkv || !bias || !W || !M || !out) return TTT_ERR_INVALID_ARG;
+  if (H < 1 || T < 1 || C < 1 || dm < 1 || !(tau > 0.f) || !(eta_base >= 0.f) || !(alpha_base >= 0.f))
+    return TTT_ERR_INVALID_ARG;
+  if (D != 128 && D != 64) return TTT_ERR_UNSUPPORTED;
+  if (C % 64 || C > 2048 || dm % 8) return TTT_ERR_UNSUPPORTED;
+  if (((uintptr_t)x & 15) || ((uintptr_t)wqkv & 15) || ((uintptr_t)W & 15) || ((uintptr_t)M & 15))
+    return TTT_ERR_INVALID_ARG;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return TTT_ERR_NO_DEVICE;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t N = 3LL * H * D + 3LL * H, nch = (T + C - 1) / C;
+  const size_t need = mixer_work_bytes(H, T, D, C);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_e2_mu);
+  if (g_e2.bytes < need || g_e2.dev != dev) {
+    if (g_e2.p) {
+      (void)hipStreamSynchronize(st);
+      (void)hipFree(g_e2.p);
+    }
+    g_e2.p = nullptr;
+    g_e2.bytes = 0;
+    if (hipMalloc(&g_e2.p, need) != hipSuccess) {
+      (void)hipGetLastError();
+      return TTT_ERR_OOM;
+    }
+    g_e2.bytes = need;
+    g_e2.dev = dev;
+  }
+  Carve cv{((uintptr_t)g_e2.p + 255) & ~(uintptr_t)255};
+  float* P = cv.take<float>((size_t)T * N * 4);
+  bf16* q = cv.take<bf16>((size_t)H * T * D * 2);
+  bf16* k = cv.take<bf16>((size_t)H * T * D * 2);
+  bf16* v = cv.take<bf16>((size_t)H * T * D * 2);
+  float* eta = cv.take<float>((size_t)H * T * 4);
+  float* beta = cv.take<float>((size_t)H * T * 4);
+  float* gamma = cv.take<float>((size_t)H * T * 4);
+  float* KW = cv.take<float>((size_t)H * T * 4);
+  float* KM = cv.take<float>((size_t)H * T * 4);
+  float* coef = cv.take<float>((size_t)H * nch * 16);
+  float* W2 = cv.take<float>((size_t)H * D * D * 4);
+  // projections: P = x wqkv^T (bf16 operands, fp32 accumulation and result)
+  GemmArgs g{};
+  g.A = x;
+  g.B = wqkv;
+  g.M = (int)T;
+  g.N = (int)N;
+  g.K = dm;
+  g.lda = dm;
+  g.ldb = dm;
+  g.C = P;
+  g.ldc = N;
+  g.scale = 1.f;
+  if (gemm(DT::BF16, true, true, Epi::STORE_F32, g, st) != hipSuccess) return TTT_ERR_HIP;
+  if (D == 128)
+    hipLaunchKernelGGL(mixer_prologue_kernel<128>, dim3((unsigned)T), dim3(256), 0, st, P, bias, H, T, eta_base,
+                       alpha_base, 1.f / tau, q, k, v, eta, beta, gamma);
+  else
+    hipLaunchKernelGGL(mixer_prologue_kernel<64>, dim3((unsigned)T), dim3(256), 0, st, P, bias, H, T, eta_base,
+                       alpha_base, 1.f / tau, q, k, v, eta, beta, gamma);
+  if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
+  if (e2_scalars(eta, beta, gamma, H, T, C, KW, KM, coef, st) != hipSuccess) return TTT_ERR_HIP;
+  const dim3 grid(2 * (D / 16) * H);
+  for (int64_t r = 0; r < nch; ++r) {
+    const int n = (int)std::min<int64_t>(C, T - r * C);
+    const float* src = (r & 1) ? W2 : W;
+    float* dst = (r & 1) ? W : W2;
+    if (D == 128)
+      hipLaunchKernelGGL((e2_chunk_kernel<128, false, true>), grid, dim3(E2_NW * 64), 0, st, k, v, KW, KM, coef, src,
+                         dst, M, T, r * C, n, nch, r, q, out);
+    else
+      hipLaunchKernelGGL((e2_chunk_kernel<64, false, true>), grid, dim3(E2_NW * 64), 0, st, k, v, KW, KM, coef, src,
+                         dst, M, T, r * C, n, nch, r, q, out);
+    if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
+  }
+  if (nch & 1) {
+    if (hipMemcpyAsync(W, W2, (size_t)H * D * D * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return TTT_ERR_HIP;
+  }
+  return TTT_OK;
 }

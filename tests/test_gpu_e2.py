@@ -75,3 +75,41 @@ def test_lact_full_workload():
 def test_lact_ragged_and_small(H, T, D, C, M0):
     ew, em = run_lact(H, T, D, C, 7, M0)
     assert ew < 1e-5 and em < 1e-5
+
+
+def run_mixer(H, T, D, dm, C, seed, eta_base=1e-4, alpha_base=0.5, tau=4.0):
+    """The E2-TTT token mixer's TTT path (e2ttt_mixer_forward) against the
+    float64 oracle on the same bf16-valued inputs. Between the steps the
+    oracle keeps q, k, v in bf16 and the scalars in float32, as the kernels
+    do; the two sides differ by their arithmetic before those roundings.
+    Errors: max |x - ref| / max |ref| for the outputs, W and M."""
+    import test_long_context_amd as tla
+    say(f"case: e2 mixer H={H} T={T} D={D} dm={dm} C={C}")
+    g = synth.gen_e2_mixer(H, T, D, dm, seed)
+    d = {k: v.cuda() for k, v in g.items()}
+    W, M = d["W"].clone(), d["M"].clone()
+    out = tla.e2ttt_mixer_forward(d["x"], d["wqkv"], d["bias"], eta_base, alpha_base, tau, W, M, H, C)
+    torch.cuda.synchronize()
+    Or, Wr, Mr = E.e2_mixer(g["x"].double().numpy(), g["wqkv"].double().numpy(), g["bias"].numpy(), eta_base,
+                            alpha_base, tau, g["W"].numpy(), g["M"].numpy(), H, D, C)
+    eo = np.max(np.abs(out.cpu().numpy().reshape(T, H, D) - Or)) / np.max(np.abs(Or))
+    ew = np.max(np.abs(W.cpu().numpy() - Wr)) / np.max(np.abs(Wr))
+    em = np.max(np.abs(M.cpu().numpy() - Mr)) / np.max(np.abs(Mr))
+    say(f"  outputs rel err {eo:.3e}  W rel err {ew:.3e}  M rel err {em:.3e}")
+    return eo, ew, em
+
+
+# bf16 activations between the steps: the bf16 tolerances (2e-2 on outputs,
+# 5e-2 on the state)
+@pytest.mark.parametrize("H,T,D,dm,C", [(3, 1000, 128, 256, 256), (2, 200, 64, 128, 64),
+                                        (1, 2048 + 77, 128, 128, 2048)])
+def test_e2_mixer_small_and_ragged(H, T, D, dm, C):
+    eo, ew, em = run_mixer(H, T, D, dm, C, 8)
+    assert eo < 2e-2 and ew < 5e-2 and em < 5e-2
+
+
+def test_e2_mixer_full_workload():
+    c = synth.E2_MIXER_CONFIG
+    eo, ew, em = run_mixer(c["heads"], c["seq"], c["dim"], c["d_model"], c["chunk"], c["seed"], c["eta_base"],
+                           c["alpha_base"], c["tau"])
+    assert eo < 2e-2 and ew < 5e-2 and em < 5e-2

@@ -121,3 +121,57 @@ def test_lact_depends_on_beta_only_through_its_chunk_mean():
     Ws1, _ = E.e2_sequential(k, v, eta, beta, np.ones_like(gamma), W, M, C)
     Ws2, _ = E.e2_sequential(k, v, eta, beta[:, perm], np.ones_like(gamma), W, M, C)
     assert np.max(np.abs(Ws1 - Ws2)) > 1e-6 * np.max(np.abs(Ws1))
+
+
+# ---------------------------------------------------------------- token mixer
+def _mixer_case(T=96, H=2, D=8, dm=12, seed=5):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((T, dm))
+    wqkv = g.standard_normal((3 * H * D + 3 * H, dm)) / np.sqrt(dm)
+    wqkv[2 * H * D:3 * H * D] /= np.sqrt(D)
+    bias = np.concatenate([np.zeros(H), np.full(H, 3.0), np.zeros(H)])
+    W = g.standard_normal((H, D, D)) * 0.02
+    M = g.standard_normal((H, D, D)) * 0.01
+    return x, wqkv, bias, W, M
+
+
+def test_mixer_scalars_and_normalised_queries():
+    """q, k have unit norm per head (up to their bf16 rounding); eta in
+    (0, eta_base), beta in (0, 1) and closer to 1 than the plain sigmoid,
+    gamma = 1 - eta alpha in (0, 1]."""
+    x, wqkv, bias, W, M = _mixer_case()
+    q, k, v, eta, beta, gamma = E.mixer_inputs(x, wqkv, bias, 0.1, 0.5, 4.0, 2, 8)
+    for a in (q, k):
+        np.testing.assert_allclose(np.linalg.norm(a, axis=-1), 1.0, atol=8e-3)
+    assert np.all((eta > 0) & (eta < 0.1)) and np.all((beta > 0) & (beta < 1)) and np.all((gamma > 0) & (gamma <= 1))
+    _, _, _, _, beta1, _ = E.mixer_inputs(x, wqkv, bias, 0.1, 0.5, 1.0, 2, 8)
+    assert np.all(beta >= beta1)
+
+
+def test_mixer_without_learning_keeps_the_initial_weights():
+    """eta_base = 0 and M0 = 0: gamma = 1 and no gradient, so the state never
+    changes and every output is W0 q_t."""
+    x, wqkv, bias, W, M = _mixer_case()
+    out, Wf, Mf = E.e2_mixer(x, wqkv, bias, 0.0, 0.5, 4.0, W, np.zeros_like(M), 2, 8, 32)
+    q, *_ = E.mixer_inputs(x, wqkv, bias, 0.0, 0.5, 4.0, 2, 8)
+    np.testing.assert_allclose(Wf, W, rtol=0, atol=0)
+    np.testing.assert_allclose(out, np.einsum("htj,hij->thi", q, W), rtol=1e-13, atol=1e-16)
+
+
+@pytest.mark.parametrize("C", [16, 40])
+def test_mixer_outputs_use_the_state_at_the_start_of_their_chunk(C):
+    """Outputs of chunk r equal W_r q_t, where W_r is the per-token
+    recursion's state after the first r chunks (e2_sequential, an
+    independent path)."""
+    x, wqkv, bias, W, M = _mixer_case()
+    H, D, T = 2, 8, 96
+    out, Wf, Mf = E.e2_mixer(x, wqkv, bias, 0.1, 0.5, 4.0, W, M, H, D, C)
+    q, k, v, eta, beta, gamma = E.mixer_inputs(x, wqkv, bias, 0.1, 0.5, 4.0, H, D)
+    for a in range(0, T, C):
+        Wa, _ = (E.e2_sequential(k[:, :a], v[:, :a], eta[:, :a], beta[:, :a], gamma[:, :a], W, M, C, -1.0)
+                 if a else (W, M))
+        e = min(T, a + C)
+        np.testing.assert_allclose(out[a:e], np.einsum("htj,hij->thi", q[:, a:e], Wa), rtol=1e-10, atol=1e-13)
+    Ws, Ms = E.e2_sequential(k, v, eta, beta, gamma, W, M, C, -1.0)
+    np.testing.assert_allclose(Wf, Ws, rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(Mf, Ms, rtol=1e-10, atol=1e-14)
