@@ -119,6 +119,7 @@ struct ttt_ctx {
   std::vector<void*> ghd_t;                  // [b, d] gradient into each dynamic MLP (storage dtype)
   std::vector<void*> dh12d;                  // [b, 2 Fd] SwiGLU pre-activation gradients per dynamic block
   bool fused_update = false;                 // bf16: both update products in one dw_sgd launch
+  bool upd_main = false;                     // update products on the caller's stream instead of side streams
   int upd_grid = 0;                          // its workgroups (0: two per CU)
   hipStream_t dstream = nullptr;             // decode graph capture stream
   hipGraphExec_t dgraph = nullptr;           // captured decode blocks
@@ -511,11 +512,12 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     if (l > s) RUN(gemm_nn_split(c, KC_GL, c->dh12d[i], 2 * Fd, c->dw12[i], d, n, d, 2 * Fd, c->part, &ns, st));
     // dW3 = dY^T Hmid and dW12 = dH12^T U, with W -= alpha dW in the epilogue,
     // on the side stream once this block's products with the old W are queued
+    hipStream_t us1 = c->upd_main ? st : c->side, us2 = c->upd_main ? st : c->side2;
     HIPCHK(c, hipEventRecord(c->ev_dyn[i], st));
-    HIPCHK(c, hipStreamWaitEvent(c->side, c->ev_dyn[i], 0));
+    HIPCHK(c, hipStreamWaitEvent(us1, c->ev_dyn[i], 0));
     if (c->dt == DT::BF16 && c->fused_update) {
       // both products in one persistent launch (shapes checked at init)
-      hipStream_t st = c->side;
+      hipStream_t st = us1;
       const DwUpdate u[2] = {
           DwUpdate{c->dh12d[i], 2L * Fd, c->xn_d[i], d, c->m12[i], c->dw12[i], c->dw12_lo[i], d, 2 * Fd, d},
           DwUpdate{gt, d, c->hm_d[i], Fd, c->m3[i], c->dw3[i], c->dw3_lo[i], Fd, d, Fd}};
@@ -523,9 +525,9 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
             dw_sgd(u, 2, n, lr, c->upd_grid, st));
       HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
     } else {
-      HIPCHK(c, hipStreamWaitEvent(c->side2, c->ev_dyn[i], 0));
+      HIPCHK(c, hipStreamWaitEvent(us2, c->ev_dyn[i], 0));
       {
-        hipStream_t st = c->side2;
+        hipStream_t st = us2;
         GemmArgs g = ga(gt, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
         g.C2 = c->dw3[i];
         g.C3 = c->dw3_lo[i];
@@ -534,7 +536,7 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         HIPCHK(c, hipEventRecord(c->ev_w3, st));
       }
       {
-        hipStream_t st = c->side;
+        hipStream_t st = us1;
         GemmArgs g2 = ga(c->dh12d[i], 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
         g2.C2 = c->dw12[i];
         g2.C3 = c->dw12_lo[i];
@@ -840,6 +842,8 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   {
     const char* uk = getenv("TTT_UPDATE_KERNEL");
     c->fused_update = c->dt == DT::BF16 && uk && strcmp(uk, "fused") == 0;
+    const char* us = getenv("TTT_UPDATE_STREAM");
+    c->upd_main = us && strcmp(us, "main") == 0;
     const char* ug = getenv("TTT_UPDATE_GRID");
     c->upd_grid = ug ? std::max(0, atoi(ug)) : 0;
   }
