@@ -28,7 +28,10 @@ typedef enum {
                               C (dtype) [M, 2N] = (d gate, d up) */
   TTTK_EPI_SGD = 5,        /* C (float master) -= scale * acc; C2 (dtype) = round(C);
                               C3 (dtype, may be NULL) = round(C - C2) */
-  TTTK_EPI_PARTIAL = 6     /* C (float) [splits][M][ldc] = partial sums over K chunks */
+  TTTK_EPI_PARTIAL = 6,    /* C (float) [splits][M][ldc] = partial sums over K chunks */
+  TTTK_EPI_STORE_F32_LSE = 8 /* bf16, a_kmajor and b_kmajor: C (float) = acc, and for each
+                                row and 64-column group g, C2 (float2 [M][ceil(N / 64)])
+                                = (max, sum exp(acc - max)) over the group's columns < N */
 } tttk_epi;
 
 /* C[m, n] = sum_k A(m, k) B(n, k) on MFMA with fp32 accumulation, where
@@ -86,6 +89,12 @@ ttt_status tttk_attn_bwd(int32_t dtype, const void* q, const void* k, const void
 /* Bytes of work tttk_attn_bwd needs for this shape and variant. */
 int64_t tttk_attn_bwd_workspace(int32_t dtype, int32_t n, int32_t H, int32_t Hk, int32_t dh, int32_t window,
                                 int32_t variant);
+
+/* The same from the logits' per-64-column (max, sum exp) partials
+ * (TTTK_EPI_STORE_F32_LSE): float2 [n][ceil(V / 64)]; reads the logits once.
+ * bf16 dz only; V a multiple of 4. */
+ttt_status tttk_ce_lse(const float* logits, const void* parts, int32_t n, int32_t nt, int32_t V,
+                       const int32_t* labels, float scale, float* loss, void* dz, int* err, void* stream);
 
 /* Fused softmax cross-entropy over V columns of fp32 logits [n, V] for the
  * first nt rows (labels int32 [nt]): loss float [nt], dz (dtype) [n, V] =

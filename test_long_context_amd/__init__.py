@@ -103,10 +103,11 @@ def lib() -> ctypes.CDLL:
         L.tttk_attn_bwd_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.tttk_attn_bwd_workspace.restype = i64
         L.tttk_ce.argtypes = [i32, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
+        L.tttk_ce_lse.argtypes = [vp, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
         L.tttk_dw_sgd.argtypes = [i32, ctypes.POINTER(DwProblem), i32, f32, i32, vp]
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_decode_step_update", "ttt_get_fast_weights",
                   "ttt_reset", "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan", "e2ttt_mixer_forward",
-                  "ttt_timing_enable", "ttt_timing_read", "tttk_gemm", "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce",
+                  "ttt_timing_enable", "ttt_timing_read", "tttk_gemm", "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce", "tttk_ce_lse",
                   "tttk_dw_sgd"):
             getattr(L, f).restype = st
         _lib = L
@@ -304,7 +305,7 @@ def e2ttt_chunk_scan_noalloc_max_bytes() -> int:
 
 
 # ---------------------------------------------------------------- kernel level
-EPI = dict(store=0, store_f32=1, add_f32=2, swiglu=3, swiglu_bwd=4, sgd=5, partial=6)
+EPI = dict(store=0, store_f32=1, add_f32=2, swiglu=3, swiglu_bwd=4, sgd=5, partial=6, store_f32_lse=8)
 
 
 def _dt(t) -> int:
@@ -369,3 +370,8 @@ def dw_sgd(problems, K: int, lr: float, grid: int = 0, stream=None):
         arr[i] = DwProblem(A=_ptr(p["A"]), lda=p["lda"], B=_ptr(p["B"]), ldb=p["ldb"], W=_ptr(p["W"]),
                            Hi=_ptr(p["Hi"]), Lo=_ptr(p.get("Lo")), ldw=p["ldw"], M=p["M"], N=p["N"])
     _check(lib().tttk_dw_sgd(len(problems), arr, int(K), float(lr), int(grid), _stream(stream)), "tttk_dw_sgd")
+
+
+def ce_lse(logits, parts, n, nt, V, labels, scale, loss, dz, err, stream=None):
+    _check(lib().tttk_ce_lse(_ptr(logits), _ptr(parts), n, nt, V, _ptr(labels), float(scale), _ptr(loss), _ptr(dz),
+                             _ptr(err), _stream(stream)), "tttk_ce_lse")

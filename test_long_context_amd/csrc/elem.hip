@@ -710,6 +710,87 @@ hipError_t ce_fwd_bwd(DT dt, const float* z, int n, int nt, int V, const int32_t
   return hipGetLastError();
 }
 
+// Softmax CE + logit gradient from per-64-column (max, sum exp) partials of
+// the logits (written by the lm_head product's epilogue): the row's
+// log-sum-exp comes from its ceil(V / 64) partials, so the logits are read
+// once, for dz = (exp(z - lse) - [v == label]) * scale and the label's
+// logit. One workgroup per row.
+template <typename T>
+__global__ void __launch_bounds__(RB) ce_lse_kernel(const float* z, const float2* parts, int nt, int V,
+                                                    const int32_t* lab, float scale, float* loss, T* dz,
+                                                    int* err) {
+  __shared__ float shm[RB / 64], shs[RB / 64];
+  const long t = blockIdx.x;
+  const float* zr = z + t * V;
+  T* dr = dz + t * V;
+  if ((int)t >= nt) {
+    for (int j = threadIdx.x; j < V; j += blockDim.x) dr[j] = from_f<T>(0.f);
+    return;
+  }
+  const int np = (V + 63) / 64;
+  const float2* pr = parts + t * np;
+  float m = -INFINITY, s = 0.f;
+  for (int j = threadIdx.x; j < np; j += RB) {
+    const float2 p = pr[j];
+    if (p.x == -INFINITY) continue;
+    const float mn = fmaxf(m, p.x);
+    s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + p.y * __expf(p.x - mn);
+    m = mn;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    const float mn = fmaxf(m, m2);
+    s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mn));
+    m = mn;
+  }
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) {
+    shm[w] = m;
+    shs[w] = s;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int i = 0; i < RB / 64; ++i) M = fmaxf(M, shm[i]);
+  float S = 0.f;
+  for (int i = 0; i < RB / 64; ++i) S += shm[i] == -INFINITY ? 0.f : shs[i] * __expf(shm[i] - M);
+  const float lse = M + __logf(S);
+  const int y = lab[t];
+  const bool yok = y >= 0 && y < V;
+  if (threadIdx.x == 0) {
+    const float li = yok ? lse - zr[y] : NAN;
+    loss[t] = li;
+    if (!yok) atomicOr(err, 1);
+    else if (!isfinite(li)) atomicOr(err, 4);
+  }
+  auto dz4 = [&](float4 v, int b) {
+    return make_float4((__expf(v.x - lse) - (b + 0 == y ? 1.f : 0.f)) * scale,
+                       (__expf(v.y - lse) - (b + 1 == y ? 1.f : 0.f)) * scale,
+                       (__expf(v.z - lse) - (b + 2 == y ? 1.f : 0.f)) * scale,
+                       (__expf(v.w - lse) - (b + 3 == y ? 1.f : 0.f)) * scale);
+  };
+  const float4* z4 = (const float4*)zr;
+  const int nv4 = V / 4;
+  constexpr int U = 4;
+  int j = threadIdx.x;
+  for (; j + (U - 1) * RB < nv4; j += U * RB) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = z4[j + u * RB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) store4<T>(dr + 4 * (j + u * RB), dz4(v[u], 4 * (j + u * RB)));
+  }
+  for (; j < nv4; j += RB) store4<T>(dr + 4 * j, dz4(z4[j], 4 * j));
+}
+
+hipError_t ce_fwd_bwd_lse(DT dt, const float* z, const float2* parts, int n, int nt, int V, const int32_t* lab,
+                          float scale, float* loss, void* dz, int* err, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (dt != DT::BF16 || V % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ce_lse_kernel<bf16>, dim3(n), dim3(RB), 0, st, z, parts, nt, V, lab, scale, loss, (bf16*)dz,
+                     err);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ rowdot D
 // D[h][t] = dO[t, h, :] . O[t, h, :]. A row (t, h) is dh * sizeof(T) bytes,
 // taken by LPR lanes reading 16 bytes each from both operands (every load of

@@ -82,6 +82,7 @@ struct ttt_ctx {
   float* h_f = nullptr;
   float* r_f = nullptr;
   float* logits = nullptr;                   // [b, V]
+  float2* lse_part = nullptr;                // bf16: [b, ceil(V / 64)] (max, sum exp) of the logits' 64-column groups
   void* dz = nullptr;                        // [b, V]
   // backward
   float* gh = nullptr;                       // [b, d] gradient of the residual stream
@@ -486,8 +487,27 @@ ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipSt
   }
   TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_f, c->final_norm, n, d, eps, c->xn,
                                         c->r_f, st));
-  TCALL(KC_LM, gfl(n, c->V, d), 0,
-        gemm(c->dt, true, true, Epi::STORE_F32, ga(c->xn, d, c->lm_head, d, n, c->V, d, c->logits, c->V), st));
+  {
+    // bf16: the epilogue also leaves each row's per-64-column (max, sum exp)
+    // for the single-pass cross-entropy
+    GemmArgs g = ga(c->xn, d, c->lm_head, d, n, c->V, d, c->logits, c->V);
+    g.C2 = c->lse_part;
+    TCALL(KC_LM, gfl(n, c->V, d), 0,
+          gemm(c->dt, true, true, c->dt == DT::BF16 ? Epi::STORE_F32_LSE : Epi::STORE_F32, g, st));
+  }
+  return TTT_OK;
+}
+
+// Softmax CE + logit gradient of a mini-batch's n rows (the first nt have
+// labels): bf16 from the lm_head epilogue's partials (one read of the
+// logits), fp32 with the two-pass kernel.
+ttt_status run_ce(ttt_ctx* c, int n, int nt, const int32_t* labels, float scale, float* loss, hipStream_t st) {
+  if (c->dt == DT::BF16)
+    TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
+          ce_fwd_bwd_lse(c->dt, c->logits, c->lse_part, n, nt, c->V, labels, scale, loss, c->dz, c->d_err, st));
+  else
+    TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
+          ce_fwd_bwd(c->dt, c->logits, n, nt, c->V, labels, scale, loss, c->dz, c->d_err, st));
   return TTT_OK;
 }
 
@@ -788,6 +808,11 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   Af(&c->h_f, (size_t)b * d);
   Af(&c->r_f, b);
   Af(&c->logits, (size_t)b * c->V);
+  if (c->dt == DT::BF16) {
+    void* p = nullptr;
+    A(&p, (size_t)b * ((c->V + 63) / 64) * sizeof(float2));
+    c->lse_part = (float2*)p;
+  }
   A(&c->dz, (size_t)b * c->V * es);
   Af(&c->gh, (size_t)b * d);
   A(&c->gh_t, (size_t)b * d * es);
@@ -960,8 +985,8 @@ ttt_status ttt_prefill(ttt_ctx* c, const int32_t* tok, int64_t T, float* loss, f
     const int nt = (int)(std::min<int64_t>(a0 + n, T - 1) - a0);
     if (nt <= 0) continue;
     const float scale = red_sum ? 1.f : 1.f / nt;
-    TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
-          ce_fwd_bwd(c->dt, c->logits, n, nt, c->V, tok + a0 + 1, scale, loss + a0, c->dz, c->d_err, st));
+    r = run_ce(c, n, nt, tok + a0 + 1, scale, loss + a0, st);
+    if (r != TTT_OK) return r;
     r = loop_backward(c, a0, n, st);
     if (r != TTT_OK) return r;
   }
@@ -1020,9 +1045,8 @@ ttt_status ttt_decode_step_update(ttt_ctx* c, const int32_t* token, float* logit
     r = loop_forward(c, c->tokhist, u, n, st);
     if (r != TTT_OK) return r;
     const float scale = c->cfg.reduction == TTT_LOSS_SUM ? 1.f : 1.f / n;
-    TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
-          ce_fwd_bwd(c->dt, c->logits, n, n, c->V, c->tokhist + u + 1, scale, loss ? loss : c->dloss, c->dz,
-                     c->d_err, st));
+    r = run_ce(c, n, n, c->tokhist + u + 1, scale, loss ? loss : c->dloss, st);
+    if (r != TTT_OK) return r;
     r = loop_backward(c, u, n, st);
     if (r != TTT_OK) return r;
     HIPCHK(c, hipEventRecord(c->ev_join, c->side));

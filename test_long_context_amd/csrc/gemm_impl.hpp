@@ -532,7 +532,7 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, floatx4 
   auto al = [](const void* p, int a) { return p == nullptr || ((uintptr_t)p & (a - 1)) == 0; };
   bool vec = (g.ldc % 4) == 0;
   if constexpr (EPI == (int)Epi::STORE_F32 || EPI == (int)Epi::PARTIAL || EPI == (int)Epi::ADD_F32 ||
-                EPI == (int)Epi::SGD)
+                EPI == (int)Epi::SGD || EPI == (int)Epi::STORE_F32_LSE)
     vec = vec && al(g.C, 16);
   else
     vec = vec && al(g.C, 8);
@@ -595,6 +595,34 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, floatx4 
       }
 #pragma unroll
       for (int k = 0; k < NCH; ++k) cur[k] = nxt[k];
+    } else if constexpr (EPI == (int)Epi::STORE_F32_LSE) {
+      // the 16 lanes that hold one row's chunks of a 64-column group (CPR is
+      // a multiple of 16) also reduce that group's (max, sum exp)
+      static_assert(CPR % 16 == 0, "64-column groups inside the wave strip");
+      const int np = (g.N + 63) / 64;
+#pragma unroll
+      for (int c = lane; c < 16 * CPR; c += 64) {
+        const int row = c / CPR, col = (c % CPR) * 4;
+        const floatx4 v = *(const floatx4*)(strip + row * SP + col);
+        const int m = mw + 16 * i + row, n = nw + col;
+        const bool in = m < g.M && n < g.N;
+        if (in) epi_chunk<(int)Epi::STORE_F32>(g, m, n, v, vec);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (in && n + e < g.N) mx = fmaxf(mx, v[e]);
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+        float sm = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (in && n + e < g.N) sm += __expf(v[e] - mx);
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 16);
+        const int ng = nw + ((c % CPR) & ~15) * 4;  // first column of the group
+        if ((lane & 15) == 0 && m < g.M && ng < g.N)
+          ((float2*)g.C2)[(long)m * np + ng / 64] = make_float2(mx, sm);
+      }
     } else {
 #pragma unroll
       for (int c = lane; c < 16 * CPR; c += 64) {

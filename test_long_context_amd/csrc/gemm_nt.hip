@@ -13,6 +13,8 @@ hipError_t gemm_nt(DT dt, Epi e, int cfg, const GemmArgs& g, hipStream_t st) {
     if (e == Epi::PARTIAL) return gemm_cfg<bf16, true, true, (int)Epi::PARTIAL, true>(c, g, st);
     return hipErrorInvalidValue;
   }
+  if (dt == DT::BF16 && e == Epi::STORE_F32_LSE)
+    return gemm_cfg<bf16, true, true, (int)Epi::STORE_F32_LSE, false>(cfg, g, st);
   if (dt == DT::BF16) return gemm_by_epi<bf16, true, true>(e, cfg, g, st);
   return gemm_by_epi<float, true, true>(e, cfg, g, st);
 }

@@ -18,7 +18,11 @@ extern "C" ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajo
                                 int32_t M, int32_t N, int32_t K, void* C, int64_t ldc, void* C2,
                                 void* C3, const void* X, float scale, int32_t kchunk, int32_t tile,
                                 void* stream) {
-  if (!dt_ok(dtype) || epi < 0 || epi > TTTK_EPI_PARTIAL || M < 0 || N < 0 || K < 0) return TTT_ERR_INVALID_ARG;
+  if (!dt_ok(dtype) || epi < 0 || (epi > TTTK_EPI_PARTIAL && epi != TTTK_EPI_STORE_F32_LSE) || M < 0 || N < 0 ||
+      K < 0)
+    return TTT_ERR_INVALID_ARG;
+  if (epi == TTTK_EPI_STORE_F32_LSE && (dtype != TTT_BF16 || !a_kmajor || !b_kmajor || !C2 || B2))
+    return TTT_ERR_INVALID_ARG;
   if (!A || !B || !C || !al16(A) || !al16(B)) return TTT_ERR_INVALID_ARG;
   if (tile < 0 || tile > 6) return TTT_ERR_INVALID_ARG;
   // contiguous dimensions: K for k-major operands, M / N otherwise
@@ -221,4 +225,15 @@ extern "C" ttt_status tttk_dw_sgd(int32_t nprob, const tttk_dw_problem* probs, i
     if (!dw_sgd_supported(u[i])) return TTT_ERR_UNSUPPORTED;
   }
   return dw_sgd(u, nprob, K, lr, grid, (hipStream_t)stream) == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+extern "C" ttt_status tttk_ce_lse(const float* logits, const void* parts, int32_t n, int32_t nt, int32_t V,
+                                  const int32_t* labels, float scale, float* loss, void* dz, int* err, void* stream) {
+  if (!logits || !parts || !labels || !loss || !dz || !err || n < 0 || nt < 0 || nt > n || V < 1)
+    return TTT_ERR_INVALID_ARG;
+  if (V % 4) return TTT_ERR_UNSUPPORTED;
+  return ce_fwd_bwd_lse(DT::BF16, logits, (const float2*)parts, n, nt, V, labels, scale, loss, dz, err,
+                        (hipStream_t)stream) == hipSuccess
+             ? TTT_OK
+             : TTT_ERR_HIP;
 }

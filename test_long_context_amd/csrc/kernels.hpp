@@ -29,6 +29,8 @@ enum class Epi : int {
                 // C3 (T, optional) = round(master - C2)
   PARTIAL,      // C (float) [split][M][ldc] = acc  (split-K)
   PARTIAL_BF16, // C (bf16) [split][M][ldc] = acc  (split-K gradient partials; bf16 NN only)
+  STORE_F32_LSE,// C (float) = acc, and per 64-column group of each row its (max, sum of
+                // exp(x - max)) into C2 (float2 [M][ceil(N / 64)]); bf16 NT only
 };
 
 struct GemmArgs {
@@ -106,6 +108,11 @@ hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, 
 // rows >= nt get dz = 0. Also flags non-finite losses in *err (bit 2).
 hipError_t ce_fwd_bwd(DT dt, const float* logits, int n, int nt, int V, const int32_t* labels,
                       float scale, float* loss, void* dz, int* err, hipStream_t st);
+// The same from the logits' per-64-column (max, sum exp) partials (float2
+// [n][ceil(V / 64)], Epi::STORE_F32_LSE): one read of the logits, one write
+// of dz. bf16 dz, V a multiple of 4.
+hipError_t ce_fwd_bwd_lse(DT dt, const float* logits, const float2* parts, int n, int nt, int V,
+                          const int32_t* labels, float scale, float* loss, void* dz, int* err, hipStream_t st);
 // D[h][t] = sum_j dO[t, h, j] O[t, h, j].
 hipError_t attn_rowdot(DT dt, const void* dO, const void* O, int n, int H, int dh, float* D,
                        hipStream_t st);

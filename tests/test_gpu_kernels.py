@@ -269,3 +269,58 @@ def test_dw_sgd_3b_block_shapes_sampled():
         Wg = p["W"]
         assert torch.equal(p["Hi"], Wg.to(bf))
         assert torch.equal(p["Lo"], (Wg - Wg.to(bf).float()).to(bf))
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6])
+def test_gemm_store_f32_lse_epilogue(tile):
+    """STORE_F32_LSE: C = A B^T in fp32 and, per row and 64-column group, the
+    group's (max, sum exp(x - max)) -- ragged last group and ragged rows."""
+    g = torch.Generator().manual_seed(31)
+    M, N, K = 264, 520, 200
+    A = rnd(g, M * K)
+    B = rnd(g, N * K)
+    acc = logical(A, M, K, True) @ logical(B, N, K, True).T
+    np_ = (N + 63) // 64
+    C = torch.full((M * N,), float("nan"), device=dev)
+    P = torch.full((M * np_ * 2,), float("nan"), device=dev)
+    tla.gemm(A.to(dev), B.to(dev), M, N, K, "store_f32_lse", C, C2=P, tile=tile)
+    assert float((C.cpu().double().view(M, N) - acc).abs().max() / acc.abs().max()) < 1e-5
+    Pg = P.cpu().double().view(M, np_, 2)
+    for gi in range(np_):
+        blk = acc[:, 64 * gi:min(N, 64 * gi + 64)]
+        mx = blk.max(dim=1).values
+        sm = torch.exp(blk - mx[:, None]).sum(dim=1)
+        assert float((Pg[:, gi, 0] - mx).abs().max()) < 1e-5 * float(acc.abs().max())
+        assert float(((Pg[:, gi, 1] - sm) / sm).abs().max()) < 1e-5
+
+
+def test_ce_from_lse_partials():
+    """Single-pass CE: loss and dz from the logits and their per-64-column
+    partials, against float64 (rows past nt get dz = 0)."""
+    g = torch.Generator().manual_seed(32)
+    n, nt, V = 37, 30, 1000
+    z = torch.randn(n, V, generator=g, dtype=torch.float64) * 3
+    lab = torch.randint(0, V, (nt,), generator=g, dtype=torch.int32)
+    np_ = (V + 63) // 64
+    parts = torch.zeros(n, np_, 2, dtype=torch.float32)
+    for gi in range(np_):
+        blk = z[:, 64 * gi:min(V, 64 * gi + 64)]
+        mx = blk.max(dim=1).values
+        parts[:, gi, 0] = mx.float()
+        parts[:, gi, 1] = torch.exp(blk - mx[:, None]).sum(dim=1).float()
+    loss = torch.empty(nt, device=dev)
+    dz = torch.empty(n, V, dtype=bf, device=dev)
+    err = torch.zeros(4, dtype=torch.int32, device=dev)
+    scale = 1.0 / nt
+    tla.ce_lse(z.float().to(dev), parts.to(dev), n, nt, V, lab.to(dev), scale, loss, dz, err)
+    torch.cuda.synchronize()
+    lse = torch.logsumexp(z[:nt], dim=1)
+    want_loss = lse - z[torch.arange(nt), lab.long()]
+    assert float(((loss.cpu().double() - want_loss) / want_loss).abs().max()) < 1e-5
+    p = torch.softmax(z[:nt], dim=1)
+    p[torch.arange(nt), lab.long()] -= 1.0
+    want_dz = p * scale
+    got = dz.cpu().double()
+    assert float((got[:nt] - want_dz).abs().max()) <= 2 ** -8 * float(want_dz.abs().max())
+    assert float(got[nt:].abs().max()) == 0.0
+    assert int(err.cpu()[0]) == 0
