@@ -511,6 +511,44 @@ def decode_update_bench(args, c, w, tok, tla, torch):
     print(json.dumps(out), flush=True)
 
 
+def kb_sweep(args, tla, torch, synth):
+    """Throughput of the 3B-shape prefill over the window k and the
+    mini-batch b ([P2] 学会如何"持续学习": the ablation over k, b and the number
+    of updated blocks): a 32768-token stream (the 128K stream's first 32K)
+    for each (k, b) pair, one warm-up and two timed passes each."""
+    T = args.seq or 32768
+    rows = []
+    for k in (4096, 8192, 16384):
+        for b in (512, 1024, 2048):
+            c = synth.config(args.workload, window=k, minibatch=b)
+            w = synth.gen_weights(c, device="cuda")
+            tok = synth.gen_tokens(c, n=T, device="cuda")
+            m = tla.TTT(c, w, max_seq=T + 1024)
+            loss = torch.empty(T - 1, dtype=torch.float32, device="cuda")
+            m.reset()
+            m.prefill(tok, loss)
+            m.sync()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(2):
+                m.reset()
+                m.prefill(tok, loss)
+            e1.record()
+            torch.cuda.synchronize()
+            m.sync()
+            ms = e0.elapsed_time(e1) / 2
+            fl = algorithmic_flops(c, T)
+            rows.append(dict(window=k, minibatch=b, ms=round(ms, 1), tokens_per_s=round(T / ms * 1e3, 1),
+                             mfma_peak_frac=round(fl / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+                             algorithmic_tflop=round(fl / 1e12, 1), mean_loss=round(float(loss.mean()), 4)))
+            print(f"# k={k} b={b}: {ms:.1f} ms  {T / ms * 1e3:.0f} tok/s", file=sys.stderr, flush=True)
+            m.close()
+            del w, m
+            torch.cuda.empty_cache()
+    print(json.dumps(dict(metric="TTT prefill tokens/s over window k and mini-batch b, 3B shape, 1 MI355X",
+                          config=dict(workload=f"{args.workload}-shape prefill, T={T}"), rows=rows)), flush=True)
+
+
 def pmc_busy(c, T, d):
     """MFMA busy of the attention-forward launches of one step, from a rocprofv3
     --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_INSTS_MFMA
@@ -555,6 +593,7 @@ def main():
     ap.add_argument("--pmc-update-summary", nargs=4, metavar="DIR",
                     help="bytes per update launch from counter runs of --update-replay and --copy-probe")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--sweep-kb", action="store_true", help="prefill throughput over window k and mini-batch b")
     ap.add_argument("--decode-updates", action="store_true",
                     help="measure decode with test-time updates every mini-batch instead")
     ap.add_argument("--e2", action="store_true", help="measure the E2-TTT chunk-end kernel instead")
@@ -577,6 +616,9 @@ def main():
 
     if args.e2:
         e2_bench(args, tla, torch, synth)
+        return
+    if args.sweep_kb:
+        kb_sweep(args, tla, torch, synth)
         return
     c = synth.config(args.workload)
     T = args.seq or c["seq"]
