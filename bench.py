@@ -549,6 +549,47 @@ def kb_sweep(args, tla, torch, synth):
                           config=dict(workload=f"{args.workload}-shape prefill, T={T}"), rows=rows)), flush=True)
 
 
+def multi_seq(args, tla, torch, synth):
+    """Throughput of the 3B-shape prefill with B independent sequences side
+    by side (n_seq = B: the loop's products with frozen weights on B b rows,
+    the fast-weight products batched): B streams of 32768 tokens each, one
+    warm-up and two timed passes per B."""
+    T = args.seq or 32768
+    rows = []
+    for B in (1, 2, 4, 8):
+        c = synth.config(args.workload, n_seq=B)
+        w = synth.gen_weights(c, device="cuda")
+        tok = torch.stack([synth.gen_tokens(c, n=T, device="cuda", seed=c["seed"] + 100 * j) for j in range(B)])
+        m = tla.TTT(c, w, max_seq=T + 1024)
+        loss = torch.empty(B, T - 1, dtype=torch.float32, device="cuda")
+        m.timing_enable((1 << 9) - 1)
+        m.prefill(tok if B > 1 else tok[0], loss if B > 1 else loss[0])
+        m.sync()
+        classes = {x["kind"]: round(x["ms"], 1) for x in (m.timing_read(k) for k in range(9))}
+        m.timing_enable(0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(2):
+            m.reset()
+            m.prefill(tok if B > 1 else tok[0], loss if B > 1 else loss[0])
+        e1.record()
+        torch.cuda.synchronize()
+        m.sync()
+        ms = e0.elapsed_time(e1) / 2
+        fl = algorithmic_flops(c, T) * B
+        rows.append(dict(n_seq=B, ms=round(ms, 1), tokens_per_s=round(B * T / ms * 1e3, 1),
+                         mfma_peak_frac=round(fl / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+                         algorithmic_tflop=round(fl / 1e12, 1), mean_loss=round(float(loss.mean()), 4),
+                         warmup_class_ms=classes))
+        print(f"# B={B}: {ms:.1f} ms  {B * T / ms * 1e3:.0f} tok/s", file=sys.stderr, flush=True)
+        m.close()
+        del w, m, tok, loss
+        torch.cuda.empty_cache()
+    print(json.dumps(dict(metric="TTT prefill tokens/s with B sequences side by side, 3B shape, 1 MI355X",
+                          config=dict(workload=f"{args.workload}-shape prefill, T={T} per sequence, b=1024, "
+                                               f"k=8192"), rows=rows)), flush=True)
+
+
 def pmc_busy(c, T, d):
     """MFMA busy of the attention-forward launches of one step, from a rocprofv3
     --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_INSTS_MFMA
@@ -594,6 +635,8 @@ def main():
                     help="bytes per update launch from counter runs of --update-replay and --copy-probe")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--sweep-kb", action="store_true", help="prefill throughput over window k and mini-batch b")
+    ap.add_argument("--multi-seq", action="store_true",
+                    help="prefill throughput with 1, 2, 4 and 8 sequences side by side")
     ap.add_argument("--decode-updates", action="store_true",
                     help="measure decode with test-time updates every mini-batch instead")
     ap.add_argument("--e2", action="store_true", help="measure the E2-TTT chunk-end kernel instead")
@@ -619,6 +662,9 @@ def main():
         return
     if args.sweep_kb:
         kb_sweep(args, tla, torch, synth)
+        return
+    if args.multi_seq:
+        multi_seq(args, tla, torch, synth)
         return
     c = synth.config(args.workload)
     T = args.seq or c["seq"]

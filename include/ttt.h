@@ -98,6 +98,12 @@ typedef struct {
                            * not depend on it. Negative => TTT_ERR_INVALID_ARG;
                            * a ring slice of one key head of 2^31 bytes or more
                            * => TTT_ERR_UNSUPPORTED. */
+  int32_t n_seq;          /* B: independent sequences processed side by side by
+                           * ttt_prefill, each with its own fast weights, window
+                           * and losses (the same T for all); 0 => 1, at most 64.
+                           * Rings, residual stream and fast weights are held
+                           * per sequence; the loop's products with frozen
+                           * weights run on B b rows. Decode needs n_seq 1. */
 } ttt_config;
 
 /* Weights (device pointers, storage dtype). Per-layer fields are host arrays
@@ -140,7 +146,11 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
  * a mini-batch with no target is forward only. loss (device float [T-1])
  * receives the prequential per-token losses. last_logits (device float [V]
  * or NULL) receives the logits at position T-1. Leaves the context at
- * position T with the adapted fast weights. */
+ * position T with the adapted fast weights.
+ * With n_seq = B > 1, tokens holds B rows of T ids ([B][T], row-major) and
+ * each row is its own sequence: loss is [B][T-1] and last_logits [B][V];
+ * sequence j's results equal those of a single-sequence context fed row j
+ * (up to the order of floating-point sums, which the row count can change). */
 ttt_status ttt_prefill(ttt_ctx* ctx, const int32_t* tokens, int64_t T, float* loss,
                        float* last_logits, void* stream);
 
@@ -150,7 +160,8 @@ ttt_status ttt_prefill(ttt_ctx* ctx, const int32_t* tokens, int64_t T, float* lo
  * update. Requires 1 <= p < max_seq (after a prefill). The token is read
  * from device memory so that the per-token launch sequence can be captured
  * once as a HIP graph and replayed. Cost independent of the context length
- * ([P1] 实验结果 -> 推理延迟: latency flat in the context). */
+ * ([P1] 实验结果 -> 推理延迟: latency flat in the context). A context with
+ * n_seq > 1 returns TTT_ERR_UNSUPPORTED. */
 ttt_status ttt_decode_step(ttt_ctx* ctx, const int32_t* token, float* logits, void* stream);
 
 /* Decode with test-time training continuing into generation ([P2]
@@ -173,9 +184,15 @@ ttt_status ttt_decode_step_update(ttt_ctx* ctx, const int32_t* token, float* log
 
 /* Copies dynamic block dyn_idx's current fast weights (fp32 master) into
  * device float buffers w1 [Fd, d], w2 [Fd, d], w3 [d, Fd]: the compressed
- * context W_T ([P1] 持续学习框架: the sequence is learned into the weights). */
+ * context W_T ([P1] 持续学习框架: the sequence is learned into the weights).
+ * With n_seq > 1 these are sequence 0's. */
 ttt_status ttt_get_fast_weights(ttt_ctx* ctx, int32_t dyn_idx, float* w1, float* w2, float* w3,
                                 void* stream);
+
+/* The same for sequence seq of a multi-sequence context (0 <= seq < n_seq,
+ * else TTT_ERR_INVALID_ARG). */
+ttt_status ttt_get_fast_weights_seq(ttt_ctx* ctx, int32_t seq, int32_t dyn_idx, float* w1, float* w2,
+                                    float* w3, void* stream);
 
 /* Restores W0 and position 0 (the rings are overwritten before being read):
  * the per-sequence restart of the inner loop ([P1] 完整PyTorch实现: the

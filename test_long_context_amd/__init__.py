@@ -35,7 +35,8 @@ class Config(ctypes.Structure):
                 ("n_dynamic", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("reduction", ctypes.c_int32), ("prefix_slab", ctypes.c_int32)]
+                ("reduction", ctypes.c_int32), ("prefix_slab", ctypes.c_int32),
+                ("n_seq", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.ttt_decode_step.argtypes = [vp, vp, vp, vp]
         L.ttt_decode_step_update.argtypes = [vp, vp, vp, vp, ctypes.POINTER(i32), vp]
         L.ttt_get_fast_weights.argtypes = [vp, i32, vp, vp, vp, vp]
+        L.ttt_get_fast_weights_seq.argtypes = [vp, i32, i32, vp, vp, vp, vp]
         L.ttt_reset.argtypes = [vp, vp]
         L.ttt_sync.argtypes = [vp, vp]
         L.ttt_position.argtypes = [vp]
@@ -106,6 +108,7 @@ def lib() -> ctypes.CDLL:
         L.tttk_ce_lse.argtypes = [vp, vp, i32, i32, i32, vp, f32, vp, vp, vp, vp]
         L.tttk_dw_sgd.argtypes = [i32, ctypes.POINTER(DwProblem), i32, f32, i32, vp]
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_decode_step_update", "ttt_get_fast_weights",
+                  "ttt_get_fast_weights_seq",
                   "ttt_reset", "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan", "e2ttt_mixer_forward",
                   "ttt_timing_enable", "ttt_timing_read", "tttk_gemm", "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce", "tttk_ce_lse",
                   "tttk_dw_sgd"):
@@ -132,7 +135,7 @@ def make_config(c: dict, max_seq: Optional[int] = None) -> Config:
                   alpha=float(c["alpha"]), rms_eps=float(c["rms_eps"]),
                   rope_theta=float(c["rope_theta"]), dtype=0 if c["dtype"] == "f32" else 1,
                   reduction=0 if c.get("reduction", "mean") == "mean" else 1,
-                  prefix_slab=int(c.get("prefix_slab", 0)))
+                  prefix_slab=int(c.get("prefix_slab", 0)), n_seq=int(c.get("n_seq", 0)))
 
 
 def _ptr(t) -> int:
@@ -175,11 +178,22 @@ class TTT:
         if st != TTT_OK:
             raise TTTError(st, f"{what}: {lib().ttt_last_error(self.h).decode()}")
 
+    @property
+    def n_seq(self) -> int:
+        return max(1, int(self.cfg.get("n_seq", 0)))
+
     def prefill(self, tokens, loss=None, last_logits=None, stream=None):
+        """tokens: [T] (one sequence) or [n_seq, T]; returns the losses,
+        [T - 1] or [n_seq, T - 1]."""
         import torch
-        T = tokens.numel()
+        B = self.n_seq
+        T = tokens.shape[-1]
+        if tokens.numel() != B * T or (B > 1 and tokens.dim() != 2):
+            raise ValueError(f"tokens must hold {B} row(s) of T ids, got shape {tuple(tokens.shape)}")
         if loss is None:
-            loss = torch.empty(T - 1, dtype=torch.float32, device=tokens.device)
+            loss = torch.empty(*((B,) if B > 1 else ()), T - 1, dtype=torch.float32, device=tokens.device)
+        if loss.numel() != B * (T - 1) or (last_logits is not None and last_logits.numel() != B * self.cfg["vocab"]):
+            raise ValueError("loss must hold n_seq (T - 1) values and last_logits n_seq vocab")
         self._chk(lib().ttt_prefill(self.h, _ptr(tokens), T, _ptr(loss), _ptr(last_logits),
                                     _stream(stream)), "ttt_prefill")
         return loss
@@ -206,15 +220,15 @@ class TTT:
                                                _stream(stream)), "ttt_decode_step_update")
         return logits, (loss if upd.value else None)
 
-    def fast_weights(self, i: int, stream=None):
+    def fast_weights(self, i: int, stream=None, seq: int = 0):
         import torch
         d, Fd = self.cfg["d_model"], self.cfg["dyn_ffn_hidden"]
         dev = torch.device("cuda")
         w1 = torch.empty(Fd, d, dtype=torch.float32, device=dev)
         w2 = torch.empty(Fd, d, dtype=torch.float32, device=dev)
         w3 = torch.empty(d, Fd, dtype=torch.float32, device=dev)
-        self._chk(lib().ttt_get_fast_weights(self.h, i, _ptr(w1), _ptr(w2), _ptr(w3), _stream(stream)),
-                  "ttt_get_fast_weights")
+        self._chk(lib().ttt_get_fast_weights_seq(self.h, seq, i, _ptr(w1), _ptr(w2), _ptr(w3), _stream(stream)),
+                  "ttt_get_fast_weights_seq")
         return w1, w2, w3
 
     def reset(self, stream=None):

@@ -13,6 +13,14 @@
 //              dynamic MLP weights, whose dW products apply the fp32 SGD update
 //              W -= alpha dW in their epilogue (bf16 working copy re-rounded
 //              from the fp32 master).
+//
+// Several sequences (n_seq = B > 1) run side by side, each with its own key/
+// value rings, residual stream and fast weights: the loop's activations hold
+// the B mini-batches one after another (rows j n .. j n + n - 1 belong to
+// sequence j), so the products with frozen weights see M = B n rows, the
+// products with fast weights run as one batched launch of B products, and
+// the position-dependent kernels (RoPE, attention, cross-entropy) run once
+// per sequence on its slice.
 #include <math.h>
 #include <string.h>
 
@@ -49,6 +57,8 @@ struct ttt_ctx {
   int L = 0, d = 0, H = 0, Hk = 0, dh = 0, F = 0, Fd = 0, V = 0, k = 0, b = 0, nd = 0, s = 0;
   int64_t max_seq = 0, cap = 0, slab = 0;
   int QKV = 0;  // (H + 2 Hk) dh
+  int B = 1;            // sequences side by side
+  size_t ring_seq = 0;  // elements of one sequence's slice of a layer's ring (Hk cap dh)
   int64_t pos = 0;
   std::string err;
   std::vector<void*> allocs;
@@ -59,16 +69,16 @@ struct ttt_ctx {
   float* final_norm = nullptr;
   std::vector<float*> attn_norm, mlp_norm, dyn_norm;
   std::vector<void*> wqkv, wo, w12, w3;       // static, storage dtype
-  std::vector<float*> m12, m3;               // dynamic fp32 masters (interleaved W1|W2)
+  std::vector<float*> m12, m3;               // dynamic fp32 masters (interleaved W1|W2), [B] each
   std::vector<void*> dw12, dw3;              // dynamic working copies (== master for f32)
   std::vector<void*> dw12_lo, dw3_lo;        // bf16: low terms, master ~= working + low
   std::vector<void*> w0_12, w0_3;            // W0 snapshot (storage dtype, interleaved)
-  std::vector<void*> kring, vring;           // per layer [Hk][cap][dh]
-  std::vector<void*> vtring;                 // per layer [Hk][dh][cap] (values transposed)
+  std::vector<void*> kring, vring;           // per layer [B][Hk][cap][dh]
+  std::vector<void*> vtring;                 // per layer [B][Hk][dh][cap] (values transposed)
   float2* rope = nullptr;                    // [max_seq][dh/2] (cos, sin)
 
   // prefix / shared activations
-  float* hres = nullptr;   // [max_seq, d] residual stream (input of block s's dynamic MLP)
+  float* hres = nullptr;   // [B][max_seq, d] residual stream (input of block s's dynamic MLP)
   float* rbuf = nullptr;   // [slab]
   void* xn = nullptr;      // [slab, d]
   void* qkv = nullptr;     // [slab, QKV]
@@ -76,7 +86,7 @@ struct ttt_ctx {
   void* ob = nullptr;      // [slab, H dh]
   void* hmid = nullptr;    // [slab, max(F, Fd)]
 
-  // loop (per dynamic block i = l - s)
+  // loop (per dynamic block i = l - s; every [b, ...] buffer holds B b rows)
   std::vector<float*> h_att, h_mlp, h_dyn, r_att, r_mlp, r_dyn, lse;
   std::vector<void*> q_l, o_l, h12_s, xn_d, h12_d, hm_d;
   float* h_f = nullptr;
@@ -103,7 +113,7 @@ struct ttt_ctx {
   float* dec = nullptr;                      // decode scratch
   int dec_split = 1;
   int32_t* d_tok = nullptr;                  // decode input token
-  int32_t* tokhist = nullptr;                // [max_seq] every token consumed (prefill and decode)
+  int32_t* tokhist = nullptr;                // [B][max_seq] every token consumed (prefill and decode)
   float* dloss = nullptr;                    // [b] losses of a decode-time update (when the caller passes none)
   int64_t trained = 0;                       // positions below it were used, with their targets, by an update
   // fast-weight updates run on side streams, overlapping the rest of the
@@ -241,7 +251,8 @@ ttt_status validate(const ttt_config* cfg) {
   if (c.reduction != TTT_LOSS_MEAN && c.reduction != TTT_LOSS_SUM) return TTT_ERR_INVALID_ARG;
   if (c.n_layers < 1 || c.d_model < 1 || c.n_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 ||
       c.ffn_hidden < 1 || c.dyn_ffn_hidden < 1 || c.vocab < 2 || c.minibatch < 1 ||
-      c.max_seq < 2 || c.n_dynamic < 0 || c.n_dynamic > c.n_layers || c.prefix_slab < 0)
+      c.max_seq < 2 || c.n_dynamic < 0 || c.n_dynamic > c.n_layers || c.prefix_slab < 0 || c.n_seq < 0 ||
+      c.n_seq > 64)
     return TTT_ERR_INVALID_ARG;
   if (c.window < c.minibatch) return TTT_ERR_INVALID_ARG;  // k >= b
   if (!(c.alpha >= 0.f) || !isfinite(c.alpha) || !(c.rms_eps > 0.f) || !(c.rope_theta > 1.f))
@@ -312,19 +323,38 @@ GemmArgs ga(const void* A, long lda, const void* B, long ldb, int M, int N, int 
   return g;
 }
 
+// One product per sequence with the sequence's own fast weights, in one
+// launch: product j reads A + j sA, B (and its low term) + j sB and writes
+// C + j sC, C2 (and C3) + j sC2, with X + j sX (elements).
+struct Bat {
+  int n = 1;
+  long sA = 0, sB = 0, sC = 0, sC2 = 0, sX = 0;
+};
+void set_batch(GemmArgs& g, const Bat& b) {
+  if (b.n <= 1) return;
+  g.batch = b.n;
+  g.sA = b.sA;
+  g.sB = b.sB;
+  g.sC = b.sC;
+  g.sC2 = b.sC2;
+  g.sX = b.sX;
+}
+
 // C (float partials) = A [M, K] (k-major) * B (k-row-major [K, N]), split-K;
-// *nsplit receives the number of partial slices written.
+// *nsplit receives the number of partial slices written. Batched (bt.n > 1):
+// product j's rows follow product j - 1's inside each slice, so the slices
+// hold bt.n M rows, as for one product of that many rows.
 ttt_status gemm_nn_split(ttt_ctx* c, int kind, const void* A, long lda, const void* B, long ldb, int M,
-                         int N, int K, float* part, int* nsplit, hipStream_t st) {
+                         int N, int K, float* part, int* nsplit, hipStream_t st, const Bat& bt = Bat{}) {
   // bf16: 256 x 256 tiles, K split so that the grid is about one workgroup
   // per CU (measured at the 3B dX shapes: better than more, smaller tiles)
   const int gran = gemm_k_granule(c->dt);
   int s;
   if (c->dt == DT::BF16) {
-    const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    const int tiles = ((M + 255) / 256) * ((N + 255) / 256) * bt.n;
     s = std::max(1, std::min(256 / tiles, K / 512));
   } else {
-    s = choose_split(((M + 127) / 128) * ((N + 127) / 128), K);
+    s = choose_split(((M + 127) / 128) * ((N + 127) / 128) * bt.n, K);
   }
   s = std::min(s, c->max_split);
   int chunk = (K + s - 1) / s;
@@ -332,12 +362,18 @@ ttt_status gemm_nn_split(ttt_ctx* c, int kind, const void* A, long lda, const vo
   s = (K + chunk - 1) / chunk;
   GemmArgs g = ga(A, lda, B, ldb, M, N, K, part, N);
   g.kchunk = chunk;
+  if (bt.n > 1) {
+    Bat b2 = bt;
+    b2.sC = (long)M * N;
+    set_batch(g, b2);
+    g.split_ld = (long)bt.n * M * N;
+  }
   if (c->dt == DT::BF16) g.tile = 5;
   *nsplit = s;
   // bf16: the gradient partials are stored in bf16 (half the traffic of
   // writing them here and reading them back in the RMSNorm backward)
   const Epi e = c->dt == DT::BF16 ? Epi::PARTIAL_BF16 : Epi::PARTIAL;
-  TCALL(kind, gfl(M, N, K), 0, gemm(c->dt, true, false, e, g, st));
+  TCALL(kind, gfl(M, N, K) * bt.n, 0, gemm(c->dt, true, false, e, g, st));
   return TTT_OK;
 }
 
@@ -351,12 +387,18 @@ hipError_t attn_fwd_any(DT dt, const AttnArgs& a, hipStream_t st) {
   return attn_fwd2_supported(dt, a) ? attn_fwd2(dt, a, st) : attn_fwd(dt, a, st);
 }
 
-AttnArgs attn_args(ttt_ctx* c, int l, const void* q, void* o, float* lse, int n, int64_t p0) {
+// Sequence j's slice of a per-sequence buffer of `per` elements of es bytes.
+inline void* sq(void* p, int j, size_t per, size_t es) {
+  return p ? (void*)((char*)p + (size_t)j * per * es) : nullptr;
+}
+inline float* sqf(float* p, int j, size_t per) { return p ? p + (size_t)j * per : nullptr; }
+
+AttnArgs attn_args(ttt_ctx* c, int l, int j, const void* q, void* o, float* lse, int n, int64_t p0) {
   AttnArgs a{};
   a.q = q;
-  a.k = c->kring[l];
-  a.v = c->vring[l];
-  a.vt = c->vtring[l];
+  a.k = sq(c->kring[l], j, c->ring_seq, c->es);
+  a.v = sq(c->vring[l], j, c->ring_seq, c->es);
+  a.vt = sq(c->vtring[l], j, c->ring_seq, c->es);
   a.o = o;
   a.lse = lse;
   a.n = n;
@@ -371,21 +413,22 @@ AttnArgs attn_args(ttt_ctx* c, int l, const void* q, void* o, float* lse, int n,
 }
 
 // ------------------------------------------------------------ prefix phase
-// Positions [pb, pe) (tok: the token of position 0 onwards).
-ttt_status run_prefix(ttt_ctx* c, const int32_t* tok, int64_t pb, int64_t pe, hipStream_t st) {
+// Positions [pb, pe) of sequence j (tok: its token of position 0 onwards).
+ttt_status run_prefix(ttt_ctx* c, int j, const int32_t* tok, int64_t pb, int64_t pe, hipStream_t st) {
   const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, F = c->F;
   const float eps = c->cfg.rms_eps;
+  const size_t rs = c->ring_seq, es = c->es;
   for (int64_t p0 = pb; p0 < pe; p0 += c->slab) {
     const int n = (int)std::min<int64_t>(c->slab, pe - p0);
-    float* h = c->hres + p0 * d;
+    float* h = c->hres + ((size_t)j * c->max_seq + p0) * d;
     TCALL(KC_OT, 0, 0, embed_gather(c->dt, tok + p0, n, c->embed, d, h, c->V, c->d_err, st));
     for (int l = 0; l <= c->s; ++l) {
       TCALL(KC_OT, 0, 0, rmsnorm_fwd(c->dt, h, c->attn_norm[l], n, d, eps, c->xn, c->rbuf, st));
       TCALL(KC_GP, gfl(n, QKV, d), 0,
             gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
-      TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, p0, c->rope, c->qb, c->kring[l],
-                                      c->vring[l], c->vtring[l], (int)c->cap, 0, st));
-      AttnArgs a = attn_args(c, l, c->qb, c->ob, nullptr, n, p0);
+      TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, p0, c->rope, c->qb, sq(c->kring[l], j, rs, es),
+                                      sq(c->vring[l], j, rs, es), sq(c->vtring[l], j, rs, es), (int)c->cap, 0, st));
+      AttnArgs a = attn_args(c, l, j, c->qb, c->ob, nullptr, n, p0);
       TCALL(KC_AP, 4.0 * H * dh * window_pairs(p0, n, c->k), 0, attn_fwd_any(c->dt, a, st));
       TCALL(KC_GP, gfl(n, d, H * dh), 0,
             gemm(c->dt, true, true, Epi::ADD_F32, ga(c->ob, (long)H * dh, c->wo[l], (long)H * dh, n, d, H * dh, h, d), st));
@@ -404,13 +447,14 @@ ttt_status run_prefix(ttt_ctx* c, const int32_t* tok, int64_t pb, int64_t pe, hi
 // Residual-stream product C[M, N] += A B^T at a mini-batch's row count: too
 // few output tiles to fill the CUs, so K is split and the partial sums are
 // left in c->part for the next fused RMSNorm to add (returns their count).
+// Batched (bt.n > 1, M rows per product): each slice holds bt.n M rows.
 ttt_status gemm_resid(ttt_ctx* c, int kind, const void* A, long lda, const void* B, long ldb, const void* B2, int M,
-                      int N, int K, int* np, hipStream_t st) {
+                      int N, int K, int* np, hipStream_t st, const Bat& bt = Bat{}) {
   const int gran = gemm_k_granule(c->dt);
   int s = 1;
   if (c->dt == DT::BF16) {
     const int bm = 256, bn = B2 ? 128 : 256;
-    const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * bt.n;
     s = std::max(1, std::min(256 / tiles, K / 512));
   }
   s = std::min(s, c->max_split);
@@ -420,106 +464,144 @@ ttt_status gemm_resid(ttt_ctx* c, int kind, const void* A, long lda, const void*
   GemmArgs g = ga(A, lda, B, ldb, M, N, K, c->part, N);
   g.B2 = B2;
   g.kchunk = chunk;
+  if (bt.n > 1) {
+    Bat b2 = bt;
+    b2.sC = (long)M * N;
+    set_batch(g, b2);
+    g.split_ld = (long)bt.n * M * N;
+  }
   if (c->dt == DT::BF16) g.tile = 5;
   *np = s;
-  TCALL(kind, gfl(M, N, K) * (B2 ? 2.0 : 1.0), 0, gemm(c->dt, true, true, Epi::PARTIAL, g, st));
+  TCALL(kind, gfl(M, N, K) * (B2 ? 2.0 : 1.0) * bt.n, 0, gemm(c->dt, true, true, Epi::PARTIAL, g, st));
   return TTT_OK;
 }
 
-ttt_status loop_forward(ttt_ctx* c, const int32_t* tok, int64_t a0, int n, hipStream_t st) {
+// Forward of the mini-batch [a0, a0 + n) of every sequence.
+ttt_status loop_forward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
   const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s, F = c->F, Fd = c->Fd;
+  const int B = c->B, nb = B * n;
+  const size_t es = c->es, rs = c->ring_seq;
   const float eps = c->cfg.rms_eps;
   // the residual stream lives in the buffers saved for the backward: xr is
   // the latest one, and each fused RMSNorm adds the pending partial sums to
   // it and saves the result as the next
-  const float* xr = c->hres + a0 * d;
+  const float* xr = nullptr;
   int np = 0;  // split-K partial sums of the last residual product, pending in c->part
   for (int l = s; l < c->L; ++l) {
     const int i = l - s;
     if (l > s) {
       // attention sublayer (adds the pending dynamic-MLP output of block l-1)
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_att[i], c->attn_norm[l], n, d, eps,
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_att[i], c->attn_norm[l], nb, d, eps,
                                             c->xn, c->r_att[i], st));
       xr = c->h_att[i];
-      TCALL(KC_GL, gfl(n, QKV, d), 0,
-            gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, n, QKV, d, c->qkv, QKV), st));
-      TCALL(KC_OT, 0, 0, rope_scatter(c->dt, c->qkv, n, H, Hk, dh, a0, c->rope, c->q_l[i], c->kring[l],
-                                      c->vring[l], c->vtring[l], (int)c->cap, 0, st));
-      AttnArgs a = attn_args(c, l, c->q_l[i], c->o_l[i], c->lse[i], n, a0);
-      if (attn_fwd2_supported(c->dt, a)) {
-        a.ksplit = std::min(4, attn_fwd2_splits(a));
-        a.opart = c->apart;
-        a.mlpart = c->aml;
+      TCALL(KC_GL, gfl(nb, QKV, d), 0,
+            gemm(c->dt, true, true, Epi::STORE, ga(c->xn, d, c->wqkv[l], d, nb, QKV, d, c->qkv, QKV), st));
+      for (int j = 0; j < B; ++j) {
+        void* q = sq(c->q_l[i], j, (size_t)n * H * dh, es);
+        TCALL(KC_OT, 0, 0, rope_scatter(c->dt, sq(c->qkv, j, (size_t)n * QKV, es), n, H, Hk, dh, a0, c->rope, q,
+                                        sq(c->kring[l], j, rs, es), sq(c->vring[l], j, rs, es),
+                                        sq(c->vtring[l], j, rs, es), (int)c->cap, 0, st));
+        AttnArgs a = attn_args(c, l, j, q, sq(c->o_l[i], j, (size_t)n * H * dh, es),
+                               sqf(c->lse[i], j, (size_t)H * n), n, a0);
+        if (attn_fwd2_supported(c->dt, a)) {
+          a.ksplit = std::min(4, attn_fwd2_splits(a));
+          a.opart = sqf(c->apart, j, (size_t)4 * c->b * H * dh);
+          a.mlpart = sqf(c->aml, j, (size_t)4 * 2 * H * c->b);
+        }
+        TCALL(KC_AL, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_fwd_any(c->dt, a, st));
+        TCALL(KC_OT, 0, 0, attn_fwd2_combine(a, st));
       }
-      TCALL(KC_AL, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_fwd_any(c->dt, a, st));
-      TCALL(KC_OT, 0, 0, attn_fwd2_combine(a, st));
-      RUN(gemm_resid(c, KC_GL, c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, nullptr, n, d, H * dh, &np, st));
+      RUN(gemm_resid(c, KC_GL, c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, nullptr, nb, d, H * dh, &np, st));
       // static MLP sublayer
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_mlp[i], c->mlp_norm[l], n, d, eps,
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_mlp[i], c->mlp_norm[l], nb, d, eps,
                                             c->xn, c->r_mlp[i], st));
       xr = c->h_mlp[i];
-      GemmArgs g = ga(c->xn, d, c->w12[l], d, n, 2 * F, d, c->h12_s[i], 2 * F);
+      GemmArgs g = ga(c->xn, d, c->w12[l], d, nb, 2 * F, d, c->h12_s[i], 2 * F);
       g.C2 = c->hmid;
-      TCALL(KC_GL, gfl(n, 2 * F, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
-      RUN(gemm_resid(c, KC_GL, c->hmid, F, c->w3[l], F, nullptr, n, d, F, &np, st));
+      TCALL(KC_GL, gfl(nb, 2 * F, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
+      RUN(gemm_resid(c, KC_GL, c->hmid, F, c->w3[l], F, nullptr, nb, d, F, &np, st));
       // the previous mini-batch's update of this block (side stream) reads
       // xn_d and the saved activations written from here on
       HIPCHK(c, hipStreamWaitEvent(st, c->ev_upd[i], 0));
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_dyn[i], c->dyn_norm[i], n, d, eps,
+      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_dyn[i], c->dyn_norm[i], nb, d, eps,
                                             c->xn_d[i], c->r_dyn[i], st));
       xr = c->h_dyn[i];
     } else {
       // block s: the residual stream comes from the hoisted prefix
       HIPCHK(c, hipStreamWaitEvent(st, c->ev_upd[i], 0));
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, nullptr, 0, nullptr, c->h_dyn[i], c->dyn_norm[i], n,
-                                            d, eps, c->xn_d[i], c->r_dyn[i], st));
+      for (int j = 0; j < B; ++j)
+        TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, c->hres + ((size_t)j * c->max_seq + a0) * d, nullptr, 0, nullptr,
+                                              sqf(c->h_dyn[i], j, (size_t)n * d), c->dyn_norm[i], n, d, eps,
+                                              sq(c->xn_d[i], j, (size_t)n * d, es), sqf(c->r_dyn[i], j, n), st));
       xr = c->h_dyn[i];
     }
-    // dynamic MLP sublayer under the current fast weights
+    // dynamic MLP sublayer under each sequence's current fast weights
     // (bf16: the fp32 master enters as two bf16 terms, working + low: one
     // step moves W by less than half a bf16 ulp, so RNE(master) alone would
     // round most updates back to the old weights, coherently)
     GemmArgs g = ga(c->xn_d[i], d, c->dw12[i], d, n, 2 * Fd, d, c->h12_d[i], 2 * Fd);
     g.C2 = c->hm_d[i];
     g.B2 = c->dw12_lo[i];
-    TCALL(KC_GL, gfl(n, 2 * Fd, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
-    RUN(gemm_resid(c, KC_GL, c->hm_d[i], Fd, c->dw3[i], Fd, c->dw3_lo[i], n, d, Fd, &np, st));
+    Bat b12;
+    b12.n = B;
+    b12.sA = (long)n * d;
+    b12.sB = 2L * Fd * d;
+    b12.sC = (long)n * 2 * Fd;
+    b12.sC2 = (long)n * Fd;
+    set_batch(g, b12);
+    TCALL(KC_GL, gfl(nb, 2 * Fd, d), 0, gemm(c->dt, true, true, Epi::SWIGLU, g, st));
+    Bat b3;
+    b3.n = B;
+    b3.sA = (long)n * Fd;
+    b3.sB = (long)d * Fd;
+    RUN(gemm_resid(c, KC_GL, c->hm_d[i], Fd, c->dw3[i], Fd, c->dw3_lo[i], n, d, Fd, &np, st, b3));
   }
-  TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_f, c->final_norm, n, d, eps, c->xn,
+  TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_f, c->final_norm, nb, d, eps, c->xn,
                                         c->r_f, st));
   {
     // bf16: the epilogue also leaves each row's per-64-column (max, sum exp)
     // for the single-pass cross-entropy
-    GemmArgs g = ga(c->xn, d, c->lm_head, d, n, c->V, d, c->logits, c->V);
+    GemmArgs g = ga(c->xn, d, c->lm_head, d, nb, c->V, d, c->logits, c->V);
     g.C2 = c->lse_part;
-    TCALL(KC_LM, gfl(n, c->V, d), 0,
+    TCALL(KC_LM, gfl(nb, c->V, d), 0,
           gemm(c->dt, true, true, c->dt == DT::BF16 ? Epi::STORE_F32_LSE : Epi::STORE_F32, g, st));
   }
   return TTT_OK;
 }
 
-// Softmax CE + logit gradient of a mini-batch's n rows (the first nt have
-// labels): bf16 from the lm_head epilogue's partials (one read of the
-// logits), fp32 with the two-pass kernel.
-ttt_status run_ce(ttt_ctx* c, int n, int nt, const int32_t* labels, float scale, float* loss, hipStream_t st) {
-  if (c->dt == DT::BF16)
-    TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
-          ce_fwd_bwd_lse(c->dt, c->logits, c->lse_part, n, nt, c->V, labels, scale, loss, c->dz, c->d_err, st));
-  else
-    TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
-          ce_fwd_bwd(c->dt, c->logits, n, nt, c->V, labels, scale, loss, c->dz, c->d_err, st));
+// Softmax CE + logit gradient of each sequence's mini-batch [a0, a0 + n)
+// (the first nt rows have labels, read from the token history): bf16 from
+// the lm_head epilogue's partials (one read of the logits), fp32 with the
+// two-pass kernel. Sequence j's losses go to loss0 + j ldl.
+ttt_status run_ce(ttt_ctx* c, int64_t a0, int n, int nt, float scale, float* loss0, int64_t ldl, hipStream_t st) {
+  const size_t ng = (c->V + 63) / 64;
+  for (int j = 0; j < c->B; ++j) {
+    const int32_t* labels = c->tokhist + (size_t)j * c->max_seq + a0 + 1;
+    float* logits = c->logits + (size_t)j * n * c->V;
+    float* loss = loss0 + (size_t)j * ldl;
+    void* dz = sq(c->dz, j, (size_t)n * c->V, c->es);
+    if (c->dt == DT::BF16)
+      TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
+            ce_fwd_bwd_lse(c->dt, logits, c->lse_part + (size_t)j * n * ng, n, nt, c->V, labels, scale, loss, dz,
+                           c->d_err, st));
+    else
+      TCALL(KC_CE, 0, (double)n * c->V * (4.0 + c->es),
+            ce_fwd_bwd(c->dt, logits, n, nt, c->V, labels, scale, loss, dz, c->d_err, st));
+  }
   return TTT_OK;
 }
 
 ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
   const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s, F = c->F, Fd = c->Fd;
+  const int B = c->B, nb = B * n;
+  const size_t es = c->es;
   const float lr = c->cfg.alpha;
   const double upd_bytes = 8.0 + (c->dt == DT::F32 ? 0.0 : (double)c->es);  // master r/w + working copy
   int ns = 1;
   const int nd = c->nd;
   // lm_head^T and the final norm
-  RUN(gemm_nn_split(c, KC_LM, c->dz, c->V, c->lm_head, d, n, d, c->V, c->part, &ns, st));
-  TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_f, c->final_norm, c->r_f, n, d, c->gh, c->ghd_t[nd - 1], 0, st));
+  RUN(gemm_nn_split(c, KC_LM, c->dz, c->V, c->lm_head, d, nb, d, c->V, c->part, &ns, st));
+  TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_f, c->final_norm, c->r_f, nb, d, c->gh, c->ghd_t[nd - 1], 0, st));
   for (int l = c->L - 1; l >= s; --l) {
     const int i = l - s;
     void* gt = c->ghd_t[i];
@@ -527,16 +609,30 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     {
       GemmArgs g = ga(gt, d, c->dw3[i], Fd, n, Fd, d, c->dh12d[i], 2 * Fd);
       g.X = c->h12_d[i];
-      TCALL(KC_GL, gfl(n, Fd, d), 0, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
+      Bat bt;
+      bt.n = B;
+      bt.sA = (long)n * d;
+      bt.sB = (long)d * Fd;
+      bt.sC = (long)n * 2 * Fd;
+      bt.sX = (long)n * 2 * Fd;
+      set_batch(g, bt);
+      TCALL(KC_GL, gfl(nb, Fd, d), 0, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
     }
-    if (l > s) RUN(gemm_nn_split(c, KC_GL, c->dh12d[i], 2 * Fd, c->dw12[i], d, n, d, 2 * Fd, c->part, &ns, st));
+    if (l > s) {
+      Bat bt;
+      bt.n = B;
+      bt.sA = (long)n * 2 * Fd;
+      bt.sB = 2L * Fd * d;
+      RUN(gemm_nn_split(c, KC_GL, c->dh12d[i], 2 * Fd, c->dw12[i], d, n, d, 2 * Fd, c->part, &ns, st, bt));
+    }
     // dW3 = dY^T Hmid and dW12 = dH12^T U, with W -= alpha dW in the epilogue,
     // on the side stream once this block's products with the old W are queued
     hipStream_t us1 = c->upd_main ? st : c->side, us2 = c->upd_main ? st : c->side2;
     HIPCHK(c, hipEventRecord(c->ev_dyn[i], st));
     HIPCHK(c, hipStreamWaitEvent(us1, c->ev_dyn[i], 0));
     if (c->dt == DT::BF16 && c->fused_update) {
-      // both products in one persistent launch (shapes checked at init)
+      // both products in one persistent launch (shapes checked at init;
+      // single-sequence contexts only)
       hipStream_t st = us1;
       const DwUpdate u[2] = {
           DwUpdate{c->dh12d[i], 2L * Fd, c->xn_d[i], d, c->m12[i], c->dw12[i], c->dw12_lo[i], d, 2 * Fd, d},
@@ -552,7 +648,14 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         g.C2 = c->dw3[i];
         g.C3 = c->dw3_lo[i];
         g.scale = lr;
-        TCALL(KC_SGD, gfl(d, Fd, n), (double)d * Fd * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g, st));
+        Bat bt;
+        bt.n = B;
+        bt.sA = (long)n * d;
+        bt.sB = (long)n * Fd;
+        bt.sC = bt.sC2 = (long)d * Fd;
+        set_batch(g, bt);
+        TCALL(KC_SGD, gfl(d, Fd, n) * B, (double)d * Fd * upd_bytes * B,
+              gemm(c->dt, false, false, Epi::SGD, g, st));
         HIPCHK(c, hipEventRecord(c->ev_w3, st));
       }
       {
@@ -561,46 +664,60 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         g2.C2 = c->dw12[i];
         g2.C3 = c->dw12_lo[i];
         g2.scale = lr;
-        TCALL(KC_SGD, gfl(2 * Fd, d, n), 2.0 * Fd * d * upd_bytes, gemm(c->dt, false, false, Epi::SGD, g2, st));
+        Bat bt;
+        bt.n = B;
+        bt.sA = (long)n * 2 * Fd;
+        bt.sB = (long)n * d;
+        bt.sC = bt.sC2 = 2L * Fd * d;
+        set_batch(g2, bt);
+        TCALL(KC_SGD, gfl(2 * Fd, d, n) * B, 2.0 * Fd * d * upd_bytes * B,
+              gemm(c->dt, false, false, Epi::SGD, g2, st));
         // the block's update is done once both products are
         HIPCHK(c, hipStreamWaitEvent(st, c->ev_w3, 0));
         HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
       }
     }
     if (l == s) break;
-    TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], n, d, c->gh, c->gh_t, 1, st));
+    TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], nb, d, c->gh, c->gh_t, 1, st));
     // static MLP
     {
-      GemmArgs g = ga(c->gh_t, d, c->w3[l], F, n, F, d, c->dh12, 2 * F);
+      GemmArgs g = ga(c->gh_t, d, c->w3[l], F, nb, F, d, c->dh12, 2 * F);
       g.X = c->h12_s[i];
-      TCALL(KC_GL, gfl(n, F, d), 0, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
-      RUN(gemm_nn_split(c, KC_GL, c->dh12, 2 * F, c->w12[l], d, n, d, 2 * F, c->part, &ns, st));
-      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_mlp[i], c->mlp_norm[l], c->r_mlp[i], n, d, c->gh, c->gh_t, 1, st));
+      TCALL(KC_GL, gfl(nb, F, d), 0, gemm(c->dt, true, false, Epi::SWIGLU_BWD, g, st));
+      RUN(gemm_nn_split(c, KC_GL, c->dh12, 2 * F, c->w12[l], d, nb, d, 2 * F, c->part, &ns, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_mlp[i], c->mlp_norm[l], c->r_mlp[i], nb, d, c->gh, c->gh_t, 1, st));
     }
     // attention
     {
-      TCALL(KC_GL, gfl(n, H * dh, d), 0,
-            gemm(c->dt, true, false, Epi::STORE, ga(c->gh_t, d, c->wo[l], (long)H * dh, n, H * dh, d, c->dO, (long)H * dh), st));
-      TCALL(KC_OT, 0, 0, attn_rowdot(c->dt, c->dO, c->o_l[i], n, H, dh, c->Dbuf, st));
-      AttnArgs a = attn_args(c, l, c->q_l[i], c->o_l[i], c->lse[i], n, a0);
-      a.dO = c->dO;
-      a.D = c->Dbuf;
-      a.dq = c->dq;
-      a.dk = c->dk;
-      a.dv = c->dv;
-      int qp = 1, kp = 1;
-      if (attn_bwd2_supported(c->dt, a)) {
-        qp = attn_bwd2_dq_parts(a);
-        kp = attn_bwd2_kv_parts(a);
-        TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq2(c->dt, a, st));
-        TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv2(c->dt, a, st));
-      } else {
-        TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq(c->dt, a, st));
-        TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv(c->dt, a, st));
+      TCALL(KC_GL, gfl(nb, H * dh, d), 0,
+            gemm(c->dt, true, false, Epi::STORE, ga(c->gh_t, d, c->wo[l], (long)H * dh, nb, H * dh, d, c->dO, (long)H * dh), st));
+      for (int j = 0; j < B; ++j) {
+        const size_t qe = (size_t)n * H * dh;
+        void* dO = sq(c->dO, j, qe, es);
+        void* o = sq(c->o_l[i], j, qe, es);
+        float* D = sqf(c->Dbuf, j, (size_t)H * n);
+        TCALL(KC_OT, 0, 0, attn_rowdot(c->dt, dO, o, n, H, dh, D, st));
+        AttnArgs a = attn_args(c, l, j, sq(c->q_l[i], j, qe, es), o, sqf(c->lse[i], j, (size_t)H * n), n, a0);
+        a.dO = dO;
+        a.D = D;
+        a.dq = sqf(c->dq, j, (size_t)ATTN_BWD2_MAX_DQ_PARTS * c->b * H * dh);
+        a.dk = sqf(c->dk, j, (size_t)H * c->b * dh);
+        a.dv = sqf(c->dv, j, (size_t)H * c->b * dh);
+        int qp = 1, kp = 1;
+        if (attn_bwd2_supported(c->dt, a)) {
+          qp = attn_bwd2_dq_parts(a);
+          kp = attn_bwd2_kv_parts(a);
+          TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq2(c->dt, a, st));
+          TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv2(c->dt, a, st));
+        } else {
+          TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq(c->dt, a, st));
+          TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv(c->dt, a, st));
+        }
+        TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, a.dq, qp, a.dk, a.dv, kp, n, H, Hk, dh, a0, c->rope,
+                                         sq(c->dqkv, j, (size_t)n * QKV, es), st));
       }
-      TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, c->dq, qp, c->dk, c->dv, kp, n, H, Hk, dh, a0, c->rope, c->dqkv, st));
-      RUN(gemm_nn_split(c, KC_GL, c->dqkv, QKV, c->wqkv[l], d, n, d, QKV, c->part, &ns, st));
-      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], n, d, c->gh, c->ghd_t[i - 1], 1, st));
+      RUN(gemm_nn_split(c, KC_GL, c->dqkv, QKV, c->wqkv[l], d, nb, d, QKV, c->part, &ns, st));
+      TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], nb, d, c->gh, c->ghd_t[i - 1], 1, st));
     }
   }
   // the next mini-batch's forward waits for each block's update just before
@@ -707,8 +824,10 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   c->QKV = (c->H + 2 * c->Hk) * c->dh;
   ring_shape(*cfg, &c->slab, &c->cap);
   c->max_split = 16;
+  c->B = cfg->n_seq > 0 ? cfg->n_seq : 1;
+  c->ring_seq = (size_t)c->Hk * c->cap * c->dh;
   const size_t es = c->es;
-  const int d = c->d, L = c->L, nd = c->nd, b = c->b;
+  const int d = c->d, L = c->L, nd = c->nd, B = c->B, b = c->b * c->B;  // b: loop rows (B mini-batches)
   const int64_t S = c->slab;
   const int Fm = std::max(c->F, c->Fd);
 
@@ -736,9 +855,9 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     A(&c->wo[l], (size_t)d * c->H * c->dh * es);
     A(&c->w12[l], (size_t)2 * c->F * d * es);
     A(&c->w3[l], (size_t)d * c->F * es);
-    A(&c->kring[l], (size_t)c->Hk * c->cap * c->dh * es);
-    A(&c->vring[l], (size_t)c->Hk * c->cap * c->dh * es);
-    if (c->dt == DT::BF16) A(&c->vtring[l], (size_t)c->Hk * c->cap * c->dh * es);
+    A(&c->kring[l], B * c->ring_seq * es);
+    A(&c->vring[l], B * c->ring_seq * es);
+    if (c->dt == DT::BF16) A(&c->vtring[l], B * c->ring_seq * es);
   }
   c->dyn_norm.resize(nd);
   c->m12.resize(nd);
@@ -751,16 +870,16 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   c->w0_3.resize(nd);
   for (int i = 0; i < nd && ok; ++i) {
     Af(&c->dyn_norm[i], d);
-    Af(&c->m12[i], (size_t)2 * c->Fd * d);
-    Af(&c->m3[i], (size_t)d * c->Fd);
+    Af(&c->m12[i], (size_t)B * 2 * c->Fd * d);
+    Af(&c->m3[i], (size_t)B * d * c->Fd);
     if (c->dt == DT::F32) {
       c->dw12[i] = c->m12[i];
       c->dw3[i] = c->m3[i];
     } else {
-      A(&c->dw12[i], (size_t)2 * c->Fd * d * es);
-      A(&c->dw3[i], (size_t)d * c->Fd * es);
-      A(&c->dw12_lo[i], (size_t)2 * c->Fd * d * es);
-      A(&c->dw3_lo[i], (size_t)d * c->Fd * es);
+      A(&c->dw12[i], (size_t)B * 2 * c->Fd * d * es);
+      A(&c->dw3[i], (size_t)B * d * c->Fd * es);
+      A(&c->dw12_lo[i], (size_t)B * 2 * c->Fd * d * es);
+      A(&c->dw3_lo[i], (size_t)B * d * c->Fd * es);
     }
     A(&c->w0_12[i], (size_t)2 * c->Fd * d * es);
     A(&c->w0_3[i], (size_t)d * c->Fd * es);
@@ -770,7 +889,7 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     A(&p, (size_t)c->max_seq * (c->dh / 2) * sizeof(float2));
     c->rope = (float2*)p;
   }
-  Af(&c->hres, (size_t)c->max_seq * d);
+  Af(&c->hres, (size_t)B * c->max_seq * d);
   Af(&c->rbuf, (size_t)S);
   A(&c->xn, (size_t)S * d * es);
   A(&c->qkv, (size_t)S * c->QKV * es);
@@ -853,10 +972,10 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     c->d_pos = (int64_t*)p;
     A(&p, 64);
     c->d_tok = (int32_t*)p;
-    A(&p, (size_t)c->max_seq * sizeof(int32_t));
+    A(&p, (size_t)B * c->max_seq * sizeof(int32_t));
     c->tokhist = (int32_t*)p;
   }
-  Af(&c->dloss, (size_t)b);
+  Af(&c->dloss, (size_t)c->b);
   c->dec_split = decode_attn_splits(c->dt, c->H, c->Hk, c->dh, c->k, c->dt == DT::BF16);
   // bf16 update products: two GEMM launches with the SGD epilogue on two
   // side streams (default), or, with TTT_UPDATE_KERNEL=fused, both in one
@@ -866,7 +985,7 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   // waves, one per SIMD, wait for every K step's operand loads.
   {
     const char* uk = getenv("TTT_UPDATE_KERNEL");
-    c->fused_update = c->dt == DT::BF16 && uk && strcmp(uk, "fused") == 0;
+    c->fused_update = c->dt == DT::BF16 && B == 1 && uk && strcmp(uk, "fused") == 0;
     const char* us = getenv("TTT_UPDATE_STREAM");
     c->upd_main = us && strcmp(us, "main") == 0;
     const char* ug = getenv("TTT_UPDATE_GRID");
@@ -910,9 +1029,9 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     UP(interleave(c->w12[l], w->w1[l], c->F, d, es, 0, st));
     UP(interleave(c->w12[l], w->w2[l], c->F, d, es, 1, st));
     UP(hipMemcpyAsync(c->w3[l], w->w3[l], (size_t)d * c->F * es, D2D, st));
-    UP(fill_zero_bytes(c->kring[l], (size_t)c->Hk * c->cap * c->dh * es, st));
-    UP(fill_zero_bytes(c->vring[l], (size_t)c->Hk * c->cap * c->dh * es, st));
-    if (c->vtring[l]) UP(fill_zero_bytes(c->vtring[l], (size_t)c->Hk * c->cap * c->dh * es, st));
+    UP(fill_zero_bytes(c->kring[l], B * c->ring_seq * es, st));
+    UP(fill_zero_bytes(c->vring[l], B * c->ring_seq * es, st));
+    if (c->vtring[l]) UP(fill_zero_bytes(c->vtring[l], B * c->ring_seq * es, st));
   }
   for (int i = 0; i < nd; ++i) {
     UP(cast_from(c->dt, w->dyn_norm[i], c->dyn_norm[i], d, st));
@@ -949,15 +1068,17 @@ ttt_status ttt_reset(ttt_ctx* c, void* stream) {
   const size_t es = c->es;
   for (int i = 0; i < c->nd; ++i) {
     const size_t n12 = (size_t)2 * c->Fd * c->d, n3 = (size_t)c->d * c->Fd;
-    HIPCHK(c, cast_from(c->dt, c->w0_12[i], c->m12[i], n12, st));
-    HIPCHK(c, cast_from(c->dt, c->w0_3[i], c->m3[i], n3, st));
-    if (c->dt != DT::F32) {
-      // W0 is exact in the storage dtype: working copy = W0, low term = 0
-      HIPCHK(c, hipMemcpyAsync(c->dw12[i], c->w0_12[i], n12 * es, hipMemcpyDeviceToDevice, st));
-      HIPCHK(c, hipMemcpyAsync(c->dw3[i], c->w0_3[i], n3 * es, hipMemcpyDeviceToDevice, st));
-      if (c->dw12_lo[i]) HIPCHK(c, fill_zero_bytes(c->dw12_lo[i], n12 * es, st));
-      if (c->dw3_lo[i]) HIPCHK(c, fill_zero_bytes(c->dw3_lo[i], n3 * es, st));
+    for (int j = 0; j < c->B; ++j) {
+      HIPCHK(c, cast_from(c->dt, c->w0_12[i], c->m12[i] + j * n12, n12, st));
+      HIPCHK(c, cast_from(c->dt, c->w0_3[i], c->m3[i] + j * n3, n3, st));
+      if (c->dt != DT::F32) {
+        // W0 is exact in the storage dtype: working copy = W0, low term = 0
+        HIPCHK(c, hipMemcpyAsync(sq(c->dw12[i], j, n12, es), c->w0_12[i], n12 * es, hipMemcpyDeviceToDevice, st));
+        HIPCHK(c, hipMemcpyAsync(sq(c->dw3[i], j, n3, es), c->w0_3[i], n3 * es, hipMemcpyDeviceToDevice, st));
+      }
     }
+    if (c->dw12_lo[i]) HIPCHK(c, fill_zero_bytes(c->dw12_lo[i], c->B * n12 * es, st));
+    if (c->dw3_lo[i]) HIPCHK(c, fill_zero_bytes(c->dw3_lo[i], c->B * n3 * es, st));
   }
   c->pos = 0;
   c->trained = 0;
@@ -971,21 +1092,27 @@ ttt_status ttt_prefill(ttt_ctx* c, const int32_t* tok, int64_t T, float* loss, f
   if (T < 2 || T > c->max_seq) return fail(c, TTT_ERR_INVALID_ARG, "T outside [2, max_seq]");
   if (c->pos != 0) return fail(c, TTT_ERR_STATE, "prefill needs position 0 (call ttt_reset)");
   hipStream_t st = (hipStream_t)stream;
-  HIPCHK(c, hipMemcpyAsync(c->tokhist, tok, (size_t)T * sizeof(int32_t), hipMemcpyDeviceToDevice, st));
-  ttt_status r = run_prefix(c, tok, 0, T, st);
-  if (r != TTT_OK) return r;
+  // sequence j's tokens go to row j of the token history; every later step
+  // reads them from there
+  HIPCHK(c, hipMemcpy2DAsync(c->tokhist, (size_t)c->max_seq * sizeof(int32_t), tok, (size_t)T * sizeof(int32_t),
+                             (size_t)T * sizeof(int32_t), c->B, hipMemcpyDeviceToDevice, st));
+  ttt_status r = TTT_OK;
+  for (int j = 0; j < c->B; ++j) {
+    r = run_prefix(c, j, c->tokhist + (size_t)j * c->max_seq, 0, T, st);
+    if (r != TTT_OK) return r;
+  }
   const float red_sum = c->cfg.reduction == TTT_LOSS_SUM;
   for (int64_t a0 = 0; a0 < T; a0 += c->b) {
     const int n = (int)std::min<int64_t>(c->b, T - a0);
-    r = loop_forward(c, tok, a0, n, st);
+    r = loop_forward(c, a0, n, st);
     if (r != TTT_OK) return r;
     if (a0 + n == T && last_logits)
-      HIPCHK(c, hipMemcpyAsync(last_logits, c->logits + (size_t)(n - 1) * c->V, (size_t)c->V * 4,
-                               hipMemcpyDeviceToDevice, st));
+      HIPCHK(c, hipMemcpy2DAsync(last_logits, (size_t)c->V * 4, c->logits + (size_t)(n - 1) * c->V,
+                                 (size_t)n * c->V * 4, (size_t)c->V * 4, c->B, hipMemcpyDeviceToDevice, st));
     const int nt = (int)(std::min<int64_t>(a0 + n, T - 1) - a0);
     if (nt <= 0) continue;
     const float scale = red_sum ? 1.f : 1.f / nt;
-    r = run_ce(c, n, nt, tok + a0 + 1, scale, loss + a0, st);
+    r = run_ce(c, a0, n, nt, scale, loss + a0, T - 1, st);
     if (r != TTT_OK) return r;
     r = loop_backward(c, a0, n, st);
     if (r != TTT_OK) return r;
@@ -1002,6 +1129,7 @@ ttt_status ttt_prefill(ttt_ctx* c, const int32_t* tok, int64_t T, float* loss, f
 ttt_status ttt_decode_step(ttt_ctx* c, const int32_t* token, float* logits, void* stream) {
   if (!c) return TTT_ERR_INVALID_ARG;
   if (!token || !logits) return fail(c, TTT_ERR_INVALID_ARG, "null token or logits");
+  if (c->B > 1) return fail(c, TTT_ERR_UNSUPPORTED, "decode runs on single-sequence contexts (n_seq 1)");
   if (c->pos < 1 || c->pos >= c->max_seq)
     return fail(c, TTT_ERR_STATE, "decode needs a prefilled context with position < max_seq");
   hipStream_t st = (hipStream_t)stream;
@@ -1030,6 +1158,7 @@ ttt_status ttt_decode_step_update(ttt_ctx* c, const int32_t* token, float* logit
   if (!c) return TTT_ERR_INVALID_ARG;
   if (updated) *updated = 0;
   if (!token || !logits) return fail(c, TTT_ERR_INVALID_ARG, "null token or logits");
+  if (c->B > 1) return fail(c, TTT_ERR_UNSUPPORTED, "decode runs on single-sequence contexts (n_seq 1)");
   if (c->pos < 1 || c->pos >= c->max_seq)
     return fail(c, TTT_ERR_STATE, "decode needs a prefilled context with position < max_seq");
   hipStream_t st = (hipStream_t)stream;
@@ -1040,12 +1169,12 @@ ttt_status ttt_decode_step_update(ttt_ctx* c, const int32_t* token, float* logit
     // mini-batch would run it
     const int n = c->b;
     HIPCHK(c, hipMemcpyAsync(c->tokhist + p, token, sizeof(int32_t), hipMemcpyDeviceToDevice, st));
-    ttt_status r = run_prefix(c, c->tokhist, u, u + n, st);
+    ttt_status r = run_prefix(c, 0, c->tokhist, u, u + n, st);
     if (r != TTT_OK) return r;
-    r = loop_forward(c, c->tokhist, u, n, st);
+    r = loop_forward(c, u, n, st);
     if (r != TTT_OK) return r;
     const float scale = c->cfg.reduction == TTT_LOSS_SUM ? 1.f : 1.f / n;
-    r = run_ce(c, n, n, c->tokhist + u + 1, scale, loss ? loss : c->dloss, st);
+    r = run_ce(c, u, n, n, scale, loss ? loss : c->dloss, 0, st);
     if (r != TTT_OK) return r;
     r = loop_backward(c, u, n, st);
     if (r != TTT_OK) return r;
@@ -1057,14 +1186,21 @@ ttt_status ttt_decode_step_update(ttt_ctx* c, const int32_t* token, float* logit
   return ttt_decode_step(c, token, logits, stream);
 }
 
-ttt_status ttt_get_fast_weights(ttt_ctx* c, int32_t i, float* w1, float* w2, float* w3, void* stream) {
+ttt_status ttt_get_fast_weights_seq(ttt_ctx* c, int32_t seq, int32_t i, float* w1, float* w2, float* w3,
+                                    void* stream) {
   if (!c) return TTT_ERR_INVALID_ARG;
   if (i < 0 || i >= c->nd || !w1 || !w2 || !w3) return fail(c, TTT_ERR_INVALID_ARG, "bad dyn index or null");
+  if (seq < 0 || seq >= c->B) return fail(c, TTT_ERR_INVALID_ARG, "sequence index outside [0, n_seq)");
   hipStream_t st = (hipStream_t)stream;
-  HIPCHK(c, deinterleave(w1, c->m12[i], c->Fd, c->d, 4, 0, st));
-  HIPCHK(c, deinterleave(w2, c->m12[i], c->Fd, c->d, 4, 1, st));
-  HIPCHK(c, hipMemcpyAsync(w3, c->m3[i], (size_t)c->d * c->Fd * 4, hipMemcpyDeviceToDevice, st));
+  const size_t n12 = (size_t)2 * c->Fd * c->d, n3 = (size_t)c->d * c->Fd;
+  HIPCHK(c, deinterleave(w1, c->m12[i] + seq * n12, c->Fd, c->d, 4, 0, st));
+  HIPCHK(c, deinterleave(w2, c->m12[i] + seq * n12, c->Fd, c->d, 4, 1, st));
+  HIPCHK(c, hipMemcpyAsync(w3, c->m3[i] + seq * n3, n3 * 4, hipMemcpyDeviceToDevice, st));
   return TTT_OK;
+}
+
+ttt_status ttt_get_fast_weights(ttt_ctx* c, int32_t i, float* w1, float* w2, float* w3, void* stream) {
+  return ttt_get_fast_weights_seq(c, 0, i, w1, w2, w3, stream);
 }
 
 ttt_status ttt_sync(ttt_ctx* c, void* stream) {

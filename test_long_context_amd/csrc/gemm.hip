@@ -12,7 +12,8 @@ int gemm_k_granule(DT) { return 64; }
 int gemm_pick_cfg(DT dt, bool ak, bool bk, const GemmArgs& g) {
   if (dt != DT::BF16) return 0;
   const long splits = g.kchunk > 0 ? (g.K + g.kchunk - 1) / g.kchunk : 1;
-  auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * (long)((g.N + bn - 1) / bn) * splits; };
+  const long nb = g.batch > 1 ? g.batch : 1;
+  auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * (long)((g.N + bn - 1) / bn) * splits * nb; };
   if (ak && bk) return tiles(256, 256) >= 256 ? 5 : 1;
   if (ak) return tiles(256, 256) >= 192 ? 5 : 1;
   return 1;

@@ -41,6 +41,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 }
 static constexpr uint32_t OOB = 0xFFFFFFF0u;
 
+// Batched launches (grid.y = batch): the view of product blockIdx.y, each
+// operand pointer advanced by its stride times the element size it has
+// under this epilogue (A, B, B2, C3 and X are T; C and C2 per epilogue).
+template <typename T, int EPI>
+__device__ __forceinline__ GemmArgs batch_view(const GemmArgs& g0) {
+  constexpr long TS = sizeof(T);
+  constexpr long CS = (EPI == (int)Epi::STORE || EPI == (int)Epi::SWIGLU || EPI == (int)Epi::SWIGLU_BWD) ? TS
+                      : EPI == (int)Epi::PARTIAL_BF16                                                 ? 2
+                                                                                                      : 4;
+  constexpr long C2S = EPI == (int)Epi::STORE_F32_LSE ? 8 : TS;
+  GemmArgs g = g0;
+  if (g0.batch > 1) {
+    const long j = blockIdx.y;
+    auto off = [j](const void* p, long s, long es) -> void* {
+      return p ? (void*)((const char*)p + j * s * es) : nullptr;
+    };
+    g.A = off(g0.A, g0.sA, TS);
+    g.B = off(g0.B, g0.sB, TS);
+    g.B2 = off(g0.B2, g0.sB, TS);
+    g.C = off(g0.C, g0.sC, CS);
+    g.C2 = off(g0.C2, g0.sC2, C2S);
+    g.C3 = off(g0.C3, g0.sC2, TS);
+    g.X = off(g0.X, g0.sX, TS);
+  }
+  return g;
+}
+
+// Elements between the split-K slices of a PARTIAL epilogue's output.
+__device__ __forceinline__ long split_offset(const GemmArgs& g) {
+  return (long)blockIdx.z * (g.split_ld > 0 ? g.split_ld : (long)g.M * g.ldc);
+}
+
 template <typename T>
 __device__ __forceinline__ void bld8(Frag8<T>& f, __amdgpu_buffer_rsrc_t r, uint32_t off);
 template <>
@@ -162,9 +194,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, floatx4 (&acc)[
           } else if constexpr (EPI == (int)Epi::ADD_F32) {
             ((float*)g.C)[idx] += a;
           } else if constexpr (EPI == (int)Epi::PARTIAL) {
-            ((float*)g.C)[(long)blockIdx.z * g.M * g.ldc + idx] = a;
+            ((float*)g.C)[split_offset(g) + idx] = a;
           } else if constexpr (EPI == (int)Epi::PARTIAL_BF16) {
-            ((bf16*)g.C)[(long)blockIdx.z * g.M * g.ldc + idx] = (bf16)a;
+            ((bf16*)g.C)[split_offset(g) + idx] = (bf16)a;
           } else if constexpr (EPI == (int)Epi::SGD) {
             float* W = (float*)g.C;
             const float w = W[idx] - g.scale * a;
@@ -192,7 +224,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, floatx4 (&acc)[
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM, int EPI, bool SPLITB>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-gemm_kernel(GemmArgs g) {
+gemm_kernel(GemmArgs g0) {
+  const GemmArgs g = batch_view<T, EPI>(g0);
   constexpr int NWN = BN / WN;
   constexpr int NT = (BM / WM) * NWN * 64;
   constexpr int LDS = BK + 8;
@@ -427,11 +460,11 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& g, int m, int n, float
     if (vec) *(bf16x4*)C = cvt4(w);
     else for (int e = 0; e < ne; ++e) C[e] = (bf16)w[e];
   } else if constexpr (EPI == (int)Epi::STORE_F32 || EPI == (int)Epi::PARTIAL) {
-    float* C = (float*)g.C + idx + (EPI == (int)Epi::PARTIAL ? (long)blockIdx.z * g.M * g.ldc : 0);
+    float* C = (float*)g.C + idx + (EPI == (int)Epi::PARTIAL ? split_offset(g) : 0);
     if (vec) *(floatx4*)C = v;
     else for (int e = 0; e < ne; ++e) C[e] = v[e];
   } else if constexpr (EPI == (int)Epi::PARTIAL_BF16) {
-    bf16* C = (bf16*)g.C + idx + (long)blockIdx.z * g.M * g.ldc;
+    bf16* C = (bf16*)g.C + idx + split_offset(g);
     if (vec) *(bf16x4*)C = cvt4(v);
     else for (int e = 0; e < ne; ++e) C[e] = (bf16)v[e];
   } else if constexpr (EPI == (int)Epi::ADD_F32) {
@@ -640,7 +673,8 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, floatx4 
 
 template <int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, bool SPLITB>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-gemm_bf16_kernel(GemmArgs g) {
+gemm_bf16_kernel(GemmArgs g0) {
+  const GemmArgs g = batch_view<bf16, EPI>(g0);
   constexpr int NWN = BN / WN;
   constexpr int NW = (BM / WM) * NWN;
   constexpr int NT = NW * 64;
@@ -754,7 +788,7 @@ static hipError_t gemm_launch(const GemmArgs& g, hipStream_t st) {
   const int tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
   int splits = 1;
   if (g.kchunk > 0) splits = (g.K + g.kchunk - 1) / g.kchunk;
-  dim3 grid(tm * tn, 1, splits);
+  dim3 grid(tm * tn, g.batch > 1 ? g.batch : 1, splits);
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, AK, BKM, EPI, SPLITB>), grid, dim3(NT), 0, st, g);
   return hipGetLastError();
@@ -765,7 +799,7 @@ static hipError_t gemm_bf16_launch(const GemmArgs& g, hipStream_t st) {
   const int tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
   int splits = 1;
   if (g.kchunk > 0) splits = (g.K + g.kchunk - 1) / g.kchunk;
-  dim3 grid(tm * tn, 1, splits);
+  dim3 grid(tm * tn, g.batch > 1 ? g.batch : 1, splits);
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, AK, BKM, EPI, SPLITB>), grid, dim3(NT), 0, st, g);
   return hipGetLastError();

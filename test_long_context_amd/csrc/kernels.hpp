@@ -47,6 +47,12 @@ struct GemmArgs {
   float scale;
   int kchunk;  // split-K chunk (multiple of gemm_k_granule); <= 0 means no split
   int tile;    // tile configuration (0 = chosen from the shape)
+  // Batched products (batch > 1: grid.y = batch): product j reads and writes
+  // A + j sA, B and B2 + j sB, C + j sC, C2 and C3 + j sC2, X + j sX
+  // (strides in elements of each operand's type)
+  int batch;
+  long sA, sB, sC, sC2, sX;
+  long split_ld;  // PARTIAL epilogues: elements between split-K slices (0: M ldc)
 };
 
 hipError_t gemm(DT dt, bool a_kmajor, bool b_kmajor, Epi epi, const GemmArgs& g, hipStream_t st);

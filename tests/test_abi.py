@@ -50,6 +50,9 @@ def _init(cfg_overrides, ptr=1, max_seq=256):
     (dict(vocab=250), -2),                       # not a multiple of 8
     (dict(d_model=8208), -2),                    # residual row wider than one workgroup keeps
     (dict(prefix_slab=-1), -1),                  # negative prefix slab
+    (dict(n_seq=-1), -1),                        # negative sequence count
+    (dict(n_seq=65), -1),                        # more sequences than a context takes
+    (dict(n_seq=64), None),                      # 64 sequences side by side
     (dict(window=1 << 30), None),                # window clamped to max_seq: a 512-slot ring
     (dict(prefix_slab=64), None),                # small slab: 128-slot ring
     (dict(dtype="bf16", head_dim=128, n_heads=1, n_kv_heads=1, d_model=128), None),

@@ -74,7 +74,7 @@ def test_generator_cpu_gpu_identical():
     assert torch.equal(ta, tb)
 
 
-def check_fast_weights(m, g, nd, w):
+def check_fast_weights(m, g, nd, w, seq=0):
     """Fast weights after the last update against the stored oracle record:
     4096 sampled coordinates per matrix and, where stored, the maximum of
     |W_T - W0| over every row and every column (a wrong row or column moves
@@ -83,7 +83,7 @@ def check_fast_weights(m, g, nd, w):
     extrema errors never exceed the full-matrix error."""
     errs, ext = [], []
     for i in range(nd):
-        ws = m.fast_weights(i)
+        ws = m.fast_weights(i, seq=seq)
         for k, W in zip(("w1", "w2", "w3"), ws):
             den = float(g[f"d{i}_{k}_den"])
             idx = torch.from_numpy(g[f"d{i}_{k}_idx"]).cuda()
