@@ -71,6 +71,9 @@ E2_CONFIG = dict(heads=16, seq=32768, dim=128, chunk=2048, seed=5)
 # strongly correlated, so the per-chunk gradients add up coherently).
 E2_MIXER_CONFIG = dict(heads=16, seq=32768, dim=128, d_model=2048, chunk=512, eta_base=1e-4, alpha_base=0.5,
                        tau=4.0, seed=6)
+# the same mixer with a SwiGLU fast-weight net of `hidden` units per head
+E2_MLP_CONFIG = dict(heads=16, seq=32768, dim=128, hidden=256, d_model=2048, chunk=512, eta_base=3e-4,
+                     alpha_base=0.5, tau=4.0, seed=7)
 
 
 def config(name: str, **overrides) -> dict:
@@ -245,3 +248,15 @@ def gen_e2_mixer(heads: int, seq: int, dim: int, d_model: int, seed: int, device
     W = (normal(seed, 3, H * D * D, device) * 0.02).to(torch.float32).view(H, D, D)
     M = torch.zeros(H, D, D, dtype=torch.float32, device=device)
     return dict(x=x, wqkv=wqkv, bias=bias, W=W, M=M)
+
+
+def gen_e2_mlp_state(heads: int, dim: int, hidden: int, seed: int, device="cpu") -> dict:
+    """Initial SwiGLU fast-weight state per head: w1, w2 ~ N(0, 1) [H, hidden,
+    dim] (unit-norm keys give pre-activations of about unit size), w3 ~ N(0,
+    1/hidden) [H, dim, hidden], float32; momenta m1, m2, m3 = 0."""
+    H, D, Dh = heads, dim, hidden
+    w1 = normal(seed, 11, H * Dh * D, device).to(torch.float32).view(H, Dh, D)
+    w2 = normal(seed, 12, H * Dh * D, device).to(torch.float32).view(H, Dh, D)
+    w3 = (normal(seed, 13, H * D * Dh, device) / math.sqrt(Dh)).to(torch.float32).view(H, D, Dh)
+    z = lambda t: torch.zeros_like(t)
+    return dict(w1=w1, w2=w2, w3=w3, m1=z(w1), m2=z(w2), m3=z(w3))
