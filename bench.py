@@ -329,6 +329,37 @@ def e2_bench(args, tla, torch, synth):
                         config=f"E2-TTT token mixer, TTT path: T={mc['seq']}, d_model={mc['d_model']}, "
                                f"H={mc['heads']} x {mc['dim']}, C={mc['chunk']}",
                         projection_gflop=round(proj_flops / 1e9, 1))
+    # the same mixer with the SwiGLU fast-weight net
+    sc = synth.E2_MLP_CONFIG
+    sx = synth.gen_e2_mixer(sc["heads"], sc["seq"], sc["dim"], sc["d_model"], sc["seed"], device="cuda")
+    s0 = synth.gen_e2_mlp_state(sc["heads"], sc["dim"], sc["hidden"], sc["seed"], device="cuda")
+    sst = {k_: v_.clone() for k_, v_ in s0.items()}
+    so = torch.empty(sc["seq"], sc["heads"] * sc["dim"], device="cuda")
+    sts = []
+    for i in range(max(1, args.warmup) + args.steps):
+        for k_ in sst:
+            sst[k_].copy_(s0[k_])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tla.e2ttt_mixer_swiglu_forward(sx["x"], sx["wqkv"], sx["bias"], sc["eta_base"], sc["alpha_base"], sc["tau"],
+                                       sst, sc["heads"], sc["chunk"], out=so)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= max(1, args.warmup):
+            sts.append(a.elapsed_time(b))
+    sms = sorted(sts)[len(sts) // 2]
+    # matrix-product FLOPs per token and head: forward of key and query
+    # (2 x (2 Dh D + Dh D) x 2), backward through W3 twice (2 x Dh D x 2) and
+    # four aggregations (2 x (Dh D + 2 Dh D) x 2)
+    Dh_, D_ = sc["hidden"], sc["dim"]
+    fw_flops = sc["seq"] * sc["heads"] * (12 * Dh_ * D_ + 4 * Dh_ * D_ + 12 * Dh_ * D_)
+    out["swiglu_mixer"] = dict(ms_per_step=round(sms, 4), value=round(sc["seq"] / (sms * 1e-3), 1),
+                               unit="tokens/s",
+                               config=f"E2-TTT token mixer, SwiGLU fast-weight net: T={sc['seq']}, "
+                                      f"d_model={sc['d_model']}, H={sc['heads']} x {D_}, hidden {Dh_}, "
+                                      f"C={sc['chunk']}",
+                               fast_weight_gflop=round(fw_flops / 1e9, 1),
+                               fast_weight_tflops=round(fw_flops / (sms * 1e-3) / 1e12, 1))
     out["lact_baseline"] = dict(ms_per_step=round(lms, 4), value=round(H * T / (lms * 1e-3), 1),
                                 unit="token-heads/s", e2_cost_vs_lact=round(ms / lms - 1.0, 4),
                                 kernel="lact_chunk_scan (chunk-mean momentum, one aggregation per chunk)")

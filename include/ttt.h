@@ -301,12 +301,29 @@ ttt_status lact_chunk_scan(const void* k, const void* v, const float* eta, const
  * steps. out: device float [T, H D], o_t = W q_t with W the state at the
  * start of t's chunk; W, M: device float [H, D, D], updated in place. D 128
  * or 64, C a multiple of 64 up to 2048, dm a multiple of 8, pointers 16-byte
- * aligned. Not built: the SwiGLU fast-weight net and the gate that mixes
- * this path with sliding-window attention. Uses (and grows) the same cached
- * work buffer as e2ttt_chunk_scan, so the two must not run concurrently. */
+ * aligned. Uses (and grows) the same cached work buffer as
+ * e2ttt_chunk_scan, so the two must not run concurrently. */
 ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
                                float alpha_base, float tau, float* W, float* M, float* out, int32_t H,
                                int64_t T, int32_t D, int32_t dm, int32_t C, void* stream);
+
+/* The same token mixer with the SwiGLU fast-weight net ([P3] 方法细节,
+ * 快速权重网络实例化): per head f_W(x) = x + LN(W3 (SiLU(W1 x) * (W2 x)))
+ * with LN a layer normalisation over the D features without affine
+ * parameters (eps 1e-5); the per-token loss 1/2 ||f_W0(k_t) - v_t||^2 at
+ * the chunk-start W0 (Algorithm 1: its gradient g_t feeds both
+ * aggregations), and Proposition 3.1 applied to each of W1, W2, W3 with its
+ * own momentum and the shared eta_t, beta_t, gamma_t (descent). Outputs o_t =
+ * f_W(q_t) under the chunk-start state. Products run on bf16 MFMA with
+ * fp32 accumulation (weights rounded to bf16 for each chunk's products, the
+ * state kept in fp32). W1, W2, M1, M2: device float [H, Dh, D]; W3, M3:
+ * device float [H, D, Dh]; all updated in place. Other arguments as for
+ * e2ttt_mixer_forward; Dh a multiple of 32 up to 4096 (else
+ * TTT_ERR_UNSUPPORTED). Shares the same cached work buffer. */
+ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
+                                      float alpha_base, float tau, float* W1, float* W2, float* W3, float* M1,
+                                      float* M2, float* M3, float* out, int32_t H, int64_t T, int32_t D,
+                                      int32_t Dh, int32_t dm, int32_t C, void* stream);
 
 #ifdef __cplusplus
 }

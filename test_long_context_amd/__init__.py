@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.lact_chunk_scan.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
         L.e2ttt_mixer_forward.argtypes = [vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, vp, vp,
                                           i32, i64, i32, i32, i32, vp]
+        L.e2ttt_mixer_swiglu_forward.argtypes = [vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                                 vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp]
         L.e2ttt_chunk_scan_noalloc_max_bytes.argtypes = []
         L.e2ttt_chunk_scan_noalloc_max_bytes.restype = i64
         L.ttt_timing_enable.argtypes = [vp, ctypes.c_uint32]
@@ -110,6 +112,7 @@ def lib() -> ctypes.CDLL:
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_decode_step_update", "ttt_get_fast_weights",
                   "ttt_get_fast_weights_seq",
                   "ttt_reset", "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan", "e2ttt_mixer_forward",
+                  "e2ttt_mixer_swiglu_forward",
                   "ttt_timing_enable", "ttt_timing_read", "tttk_gemm", "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce", "tttk_ce_lse",
                   "tttk_dw_sgd"):
             getattr(L, f).restype = st
@@ -300,6 +303,25 @@ def e2ttt_mixer_forward(x, wqkv, bias, eta_base, alpha_base, tau, W, M, heads: i
                                    _ptr(W), _ptr(M), _ptr(out), H, T, D, dm, chunk, _stream(stream))
     if st != TTT_OK:
         raise TTTError(st, "e2ttt_mixer_forward")
+    return out
+
+
+def e2ttt_mixer_swiglu_forward(x, wqkv, bias, eta_base, alpha_base, tau, state: dict, heads: int, chunk: int,
+                               out=None, stream=None):
+    """E2-TTT token mixer, TTT path with the SwiGLU fast-weight net (see
+    include/ttt.h); state: w1, w2 [H, Dh, D], w3 [H, D, Dh] and momenta m1,
+    m2, m3 (float), updated in place. Returns out [T, H D]."""
+    import torch
+    T, dm = x.shape
+    H, Dh, D = state["w1"].shape
+    assert H == heads
+    if out is None:
+        out = torch.empty(T, H * D, dtype=torch.float32, device=x.device)
+    st = lib().e2ttt_mixer_swiglu_forward(_ptr(x), _ptr(wqkv), _ptr(bias), float(eta_base), float(alpha_base),
+                                          float(tau), *(_ptr(state[n]) for n in ("w1", "w2", "w3", "m1", "m2", "m3")),
+                                          _ptr(out), H, T, D, Dh, dm, chunk, _stream(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "e2ttt_mixer_swiglu_forward")
     return out
 
 

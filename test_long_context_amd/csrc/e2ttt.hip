@@ -788,3 +788,318 @@ extern "C" ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const
   }
   return TTT_OK;
 }
+
+// ============================================ SwiGLU fast-weight token mixer
+// [P3] 方法细节, 快速权重网络实例化: per head the fast weight is the net
+//   f_W(x) = x + LN(W3 (silu(W1 x) * (W2 x)))   (LN without affine, eps 1e-5)
+// with the per-token loss 1/2 ||f_W0(k_t) - v_t||^2 at the chunk-start W0 and
+// Proposition 3.1 applied to each of W1, W2, W3 (own momentum, shared
+// scalars). Per chunk, every step runs for all heads in one launch (grid.y =
+// head):
+//   A12 = K W12^T (SwiGLU epilogue: pre-activations A12 and H = silu * up),
+//   Y = H W3^T (fp32), the same two products for the queries;
+//   rows: LN(Y), g = k + LN(Y_k) - v, dY = LN^T g, scaled by K^W_t and K^M_t
+//         (bf16), outputs o_t = q_t + LN(Y_q);
+//   dA12 = (K dY) W3 with the SwiGLU backward in the epilogue (twice);
+//   aggregations (tokens contracted): K dY^T H -> [D, Dh], dA12^T K -> [2 Dh, D]
+//   (twice), then W = c0 W + c1 M + aggW, M = c2 M + aggM element-wise,
+//   with the bf16 copy of W for the next chunk's products.
+// W1 | W2 live 16-row interleaved (gate rows 32 j + w, up rows 32 j + 16 + w)
+// in one [2 Dh, D] matrix per head, the layout of the SwiGLU epilogues.
+namespace {
+using ttt::bf16;
+using ttt::bf16x4;
+using ttt::floatx4;
+constexpr float E2MLP_EPS = 1e-5f;
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// One wave per (token, head); blockIdx.z = 0: keys (dY), 1: queries (outputs).
+template <int D>
+__global__ void __launch_bounds__(256) e2mlp_rows_kernel(const float* __restrict__ Yk, const float* __restrict__ Yq,
+                                                         const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                         const bf16* __restrict__ v, const float* __restrict__ KW,
+                                                         const float* __restrict__ KM, int64_t T, int64_t a, int n,
+                                                         int Cmax, int H, bf16* __restrict__ dYw,
+                                                         bf16* __restrict__ dYm, float* __restrict__ out) {
+  constexpr int E = D / 64;
+  const int h = blockIdx.y;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  const bool keys = blockIdx.z == 0;
+  const int64_t row = ((int64_t)h * Cmax + i) * D + lane * E;
+  const float* y = (keys ? Yk : Yq) + row;
+  float yv[E], z[E];
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    yv[e] = y[e];
+    s += yv[e];
+  }
+  const float mu = wave_sum(s) * (1.f / D);
+  float s2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) s2 += (yv[e] - mu) * (yv[e] - mu);
+  const float r = rsqrtf(wave_sum(s2) * (1.f / D) + E2MLP_EPS);
+#pragma unroll
+  for (int e = 0; e < E; ++e) z[e] = (yv[e] - mu) * r;
+  const int64_t t = a + i;
+  const int64_t src = ((int64_t)h * T + t) * D + lane * E;
+  if (keys) {
+    float g[E];
+    float sg = 0.f, sgz = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      g[e] = (float)k[src + e] + z[e] - (float)v[src + e];
+      sg += g[e];
+      sgz += g[e] * z[e];
+    }
+    const float mg = wave_sum(sg) * (1.f / D), mgz = wave_sum(sgz) * (1.f / D);
+    const float kw = KW[(int64_t)h * T + t], km = KM[(int64_t)h * T + t];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float dy = r * (g[e] - mg - z[e] * mgz);
+      dYw[row + e] = (bf16)(kw * dy);
+      dYm[row + e] = (bf16)(km * dy);
+    }
+  } else {
+    float* o = out + (t * H + h) * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = (float)q[src + e] + z[e];
+  }
+}
+
+// W = c0 W + c1 M + aw, M = c2 M + am, Wb = bf16(W) over H heads of `per`
+// elements (a multiple of 4); c = coef[(h nch + r) * 4 + 0..2].
+__global__ void __launch_bounds__(256) e2mlp_state_kernel(float* __restrict__ W, float* __restrict__ M,
+                                                          const float* __restrict__ aw, const float* __restrict__ am,
+                                                          bf16* __restrict__ Wb, const float* __restrict__ coef,
+                                                          int64_t per, int H, int64_t nch, int64_t r) {
+  const int64_t n4 = (int64_t)H * per / 4;
+  for (int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; j < n4; j += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = 4 * j;
+    const int h = (int)(i / per);
+    const float* c = coef + ((int64_t)h * nch + r) * 4;
+    const float c0 = c[0], c1 = c[1], c2 = c[2];
+    const floatx4 w = *(const floatx4*)(W + i), m = *(const floatx4*)(M + i);
+    const floatx4 x = *(const floatx4*)(aw + i), y = *(const floatx4*)(am + i);
+    const floatx4 wn = c0 * w + c1 * m + x;
+    *(floatx4*)(W + i) = wn;
+    *(floatx4*)(M + i) = c2 * m + y;
+    bf16x4 b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = (bf16)wn[e];
+    *(bf16x4*)(Wb + i) = b;
+  }
+}
+
+__global__ void __launch_bounds__(256) e2mlp_cast_kernel(const float* __restrict__ src, bf16* __restrict__ dst,
+                                                         int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = (bf16)src[i];
+}
+
+// rows of [R, cols] fp32 <-> the 16-row interleaved pair layout ([2 R, cols])
+hipError_t il_rows(float* dst, const float* src, int64_t R, int cols, int which, bool to_pair, hipStream_t st) {
+  const size_t blk = (size_t)16 * cols * 4;
+  if (to_pair)
+    return hipMemcpy2DAsync((char*)dst + which * blk, 2 * blk, src, blk, blk, R / 16, hipMemcpyDeviceToDevice, st);
+  return hipMemcpy2DAsync(dst, blk, (const char*)src + which * blk, 2 * blk, blk, R / 16, hipMemcpyDeviceToDevice,
+                          st);
+}
+
+size_t mlp_mixer_work_bytes(int32_t H, int64_t T, int32_t D, int32_t Dh, int32_t C) {
+  const size_t al = 256, h = H, c = C, d = D, f = Dh;
+  return mixer_work_bytes(H, T, D, C) + 2 * (h * 2 * f * d * 4 + al) + h * 2 * f * d * 2 + al +
+         h * d * f * 2 + al + 2 * (h * c * 2 * f * 2 + al) + 2 * (h * c * f * 2 + al) + 2 * (h * c * d * 4 + al) +
+         2 * (h * c * d * 2 + al) + 2 * (h * c * 2 * f * 2 + al) + 2 * (h * 2 * f * d * 4 + al) +
+         2 * (h * d * f * 4 + al) + 256;
+}
+
+// batched (over heads) bf16 product for the SwiGLU mixer
+ttt::GemmArgs hg(const void* A, long lda, long sA, const void* B, long ldb, long sB, int M, int N, int K, void* C,
+                 long ldc, long sC, int H) {
+  ttt::GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.C = C;
+  g.ldc = ldc;
+  g.scale = 1.f;
+  g.batch = H;
+  g.sA = sA;
+  g.sB = sB;
+  g.sC = sC;
+  return g;
+}
+}  // namespace
+
+extern "C" ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
+                                                 float alpha_base, float tau, float* W1, float* W2, float* W3,
+                                                 float* M1, float* M2, float* M3, float* out, int32_t H, int64_t T,
+                                                 int32_t D, int32_t Dh, int32_t dm, int32_t C, void* stream) {
+  using namespace ttt;
+  if (!x || !wqkv || !bias || !W1 || !W2 || !W3 || !M1 || !M2 || !M3 || !out) return TTT_ERR_INVALID_ARG;
+  if (H < 1 || T < 1 || C < 1 || dm < 1 || Dh < 1 || !(tau > 0.f) || !(eta_base >= 0.f) || !(alpha_base >= 0.f))
+    return TTT_ERR_INVALID_ARG;
+  if (D != 128 && D != 64) return TTT_ERR_UNSUPPORTED;
+  if (C % 64 || C > 2048 || dm % 8 || Dh % 32 || Dh > 4096) return TTT_ERR_UNSUPPORTED;
+  for (const void* p : {x, wqkv, (const void*)W1, (const void*)W2, (const void*)W3, (const void*)M1,
+                        (const void*)M2, (const void*)M3, (const void*)out})
+    if ((uintptr_t)p & 15) return TTT_ERR_INVALID_ARG;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return TTT_ERR_NO_DEVICE;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t N = 3LL * H * D + 3LL * H, nch = (T + C - 1) / C;
+  const size_t need = mlp_mixer_work_bytes(H, T, D, Dh, C);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_e2_mu);
+  if (g_e2.bytes < need || g_e2.dev != dev) {
+    if (g_e2.p) {
+      (void)hipStreamSynchronize(st);
+      (void)hipFree(g_e2.p);
+    }
+    g_e2.p = nullptr;
+    g_e2.bytes = 0;
+    if (hipMalloc(&g_e2.p, need) != hipSuccess) {
+      (void)hipGetLastError();
+      return TTT_ERR_OOM;
+    }
+    g_e2.bytes = need;
+    g_e2.dev = dev;
+  }
+  const size_t h = H, c = C, d = D, f = Dh;
+  Carve cv{((uintptr_t)g_e2.p + 255) & ~(uintptr_t)255};
+  float* P = cv.take<float>((size_t)T * N * 4);
+  bf16* q = cv.take<bf16>(h * T * d * 2);
+  bf16* k = cv.take<bf16>(h * T * d * 2);
+  bf16* v = cv.take<bf16>(h * T * d * 2);
+  float* eta = cv.take<float>(h * T * 4);
+  float* beta = cv.take<float>(h * T * 4);
+  float* gamma = cv.take<float>(h * T * 4);
+  float* KW = cv.take<float>(h * T * 4);
+  float* KM = cv.take<float>(h * T * 4);
+  float* coef = cv.take<float>(h * nch * 16);
+  (void)cv.take<float>(h * d * d * 4);  // (the linear mixer's second state buffer; unused here)
+  float* W12 = cv.take<float>(h * 2 * f * d * 4);
+  float* M12 = cv.take<float>(h * 2 * f * d * 4);
+  bf16* W12b = cv.take<bf16>(h * 2 * f * d * 2);
+  bf16* W3b = cv.take<bf16>(h * d * f * 2);
+  bf16* A12k = cv.take<bf16>(h * c * 2 * f * 2);
+  bf16* A12q = cv.take<bf16>(h * c * 2 * f * 2);
+  bf16* Hk = cv.take<bf16>(h * c * f * 2);
+  bf16* Hq = cv.take<bf16>(h * c * f * 2);
+  float* Yk = cv.take<float>(h * c * d * 4);
+  float* Yq = cv.take<float>(h * c * d * 4);
+  bf16* dYw = cv.take<bf16>(h * c * d * 2);
+  bf16* dYm = cv.take<bf16>(h * c * d * 2);
+  bf16* dAw = cv.take<bf16>(h * c * 2 * f * 2);
+  bf16* dAm = cv.take<bf16>(h * c * 2 * f * 2);
+  float* a12w = cv.take<float>(h * 2 * f * d * 4);
+  float* a12m = cv.take<float>(h * 2 * f * d * 4);
+  float* a3w = cv.take<float>(h * d * f * 4);
+  float* a3m = cv.take<float>(h * d * f * 4);
+  (void)A12q;
+#define E2CHK(call)                          \
+  do {                                       \
+    if ((call) != hipSuccess) {              \
+      (void)hipGetLastError();               \
+      return TTT_ERR_HIP;                    \
+    }                                        \
+  } while (0)
+  // inputs: projections, then q, k, v and the scalars (as the linear mixer)
+  {
+    GemmArgs g{};
+    g.A = x;
+    g.B = wqkv;
+    g.M = (int)T;
+    g.N = (int)N;
+    g.K = dm;
+    g.lda = dm;
+    g.ldb = dm;
+    g.C = P;
+    g.ldc = N;
+    g.scale = 1.f;
+    E2CHK(gemm(DT::BF16, true, true, Epi::STORE_F32, g, st));
+  }
+  if (D == 128)
+    hipLaunchKernelGGL(mixer_prologue_kernel<128>, dim3((unsigned)T), dim3(256), 0, st, P, bias, H, T, eta_base,
+                       alpha_base, 1.f / tau, q, k, v, eta, beta, gamma);
+  else
+    hipLaunchKernelGGL(mixer_prologue_kernel<64>, dim3((unsigned)T), dim3(256), 0, st, P, bias, H, T, eta_base,
+                       alpha_base, 1.f / tau, q, k, v, eta, beta, gamma);
+  E2CHK(hipGetLastError());
+  E2CHK(e2_scalars(eta, beta, gamma, H, T, C, KW, KM, coef, st));
+  // state: W1 | W2 and their momenta into the interleaved pair layout
+  const int64_t R = (int64_t)H * Dh;
+  E2CHK(il_rows(W12, W1, R, D, 0, true, st));
+  E2CHK(il_rows(W12, W2, R, D, 1, true, st));
+  E2CHK(il_rows(M12, M1, R, D, 0, true, st));
+  E2CHK(il_rows(M12, M2, R, D, 1, true, st));
+  hipLaunchKernelGGL(e2mlp_cast_kernel, dim3(1024), dim3(256), 0, st, W12, W12b, (int64_t)(h * 2 * f * d));
+  hipLaunchKernelGGL(e2mlp_cast_kernel, dim3(1024), dim3(256), 0, st, W3, W3b, (int64_t)(h * d * f));
+  E2CHK(hipGetLastError());
+  const long sT = (long)T * D, s12 = 2L * Dh * D, s3 = (long)D * Dh;
+  for (int64_t r = 0; r < nch; ++r) {
+    const int n = (int)std::min<int64_t>(C, T - r * C);
+    const size_t off = (size_t)r * C * D;
+    // forward of keys and queries under the chunk-start weights
+    for (int which = 0; which < 2; ++which) {
+      const bf16* in = (which == 0 ? k : q) + off;
+      bf16* Hx = which == 0 ? Hk : Hq;
+      GemmArgs g = hg(in, D, sT, W12b, D, s12, n, 2 * Dh, D, which == 0 ? (void*)A12k : nullptr, 2 * Dh,
+                      (long)C * 2 * Dh, H);
+      g.C2 = Hx;
+      g.sC2 = (long)C * Dh;
+      E2CHK(gemm(DT::BF16, true, true, Epi::SWIGLU, g, st));
+      GemmArgs g2 = hg(Hx, Dh, (long)C * Dh, W3b, Dh, s3, n, D, Dh, which == 0 ? Yk : Yq, D, (long)C * D, H);
+      E2CHK(gemm(DT::BF16, true, true, Epi::STORE_F32, g2, st));
+    }
+    const dim3 rg((unsigned)((n + 3) / 4), (unsigned)H, 2);
+    if (D == 128)
+      hipLaunchKernelGGL(e2mlp_rows_kernel<128>, rg, dim3(256), 0, st, Yk, Yq, q, k, v, KW, KM, T, r * C, n, C, H,
+                         dYw, dYm, out);
+    else
+      hipLaunchKernelGGL(e2mlp_rows_kernel<64>, rg, dim3(256), 0, st, Yk, Yq, q, k, v, KW, KM, T, r * C, n, C, H,
+                         dYw, dYm, out);
+    E2CHK(hipGetLastError());
+    // backward through the net, once per scalar kernel, and the aggregations
+    for (int which = 0; which < 2; ++which) {
+      const bf16* dY = which == 0 ? dYw : dYm;
+      bf16* dA = which == 0 ? dAw : dAm;
+      GemmArgs gb = hg(dY, D, (long)C * D, W3b, Dh, s3, n, Dh, D, dA, 2 * Dh, (long)C * 2 * Dh, H);
+      gb.X = A12k;
+      gb.sX = (long)C * 2 * Dh;
+      E2CHK(gemm(DT::BF16, true, false, Epi::SWIGLU_BWD, gb, st));
+      GemmArgs g3 = hg(dY, D, (long)C * D, Hk, Dh, (long)C * Dh, D, Dh, n, which == 0 ? a3w : a3m, Dh, s3, H);
+      E2CHK(gemm(DT::BF16, false, false, Epi::STORE_F32, g3, st));
+      GemmArgs g12 = hg(dA, 2 * Dh, (long)C * 2 * Dh, k + off, D, sT, 2 * Dh, D, n, which == 0 ? a12w : a12m, D,
+                        s12, H);
+      E2CHK(gemm(DT::BF16, false, false, Epi::STORE_F32, g12, st));
+    }
+    hipLaunchKernelGGL(e2mlp_state_kernel, dim3(1024), dim3(256), 0, st, W12, M12, a12w, a12m, W12b, coef, s12, H,
+                       nch, r);
+    hipLaunchKernelGGL(e2mlp_state_kernel, dim3(1024), dim3(256), 0, st, W3, M3, a3w, a3m, W3b, coef, s3, H, nch,
+                       r);
+    E2CHK(hipGetLastError());
+  }
+  E2CHK(il_rows(W1, W12, R, D, 0, false, st));
+  E2CHK(il_rows(W2, W12, R, D, 1, false, st));
+  E2CHK(il_rows(M1, M12, R, D, 0, false, st));
+  E2CHK(il_rows(M2, M12, R, D, 1, false, st));
+#undef E2CHK
+  return TTT_OK;
+}

@@ -94,3 +94,13 @@ def test_ring_slice_of_2_gib_is_unsupported():
     2^30 needs 2^31 slots of 16 fp32 values."""
     st, _ = _init(dict(window=1 << 30, prefix_slab=1 << 20), max_seq=1 << 30)
     assert st == -2
+
+
+def test_e2_swiglu_mixer_argument_checks():
+    f = tla.lib().e2ttt_mixer_swiglu_forward
+    a = [16] * 10  # placeholder, 16-byte aligned pointers: rejected before any device work
+    assert f(None, *a[:2], 1e-3, 0.5, 4.0, *a[:7], 2, 64, 128, 64, 64, 64, None) == -1  # null input
+    assert f(*a[:3], 1e-3, 0.5, 4.0, *a[:7], 2, 64, 128, 48, 64, 64, None) == -2       # hidden not a multiple of 32
+    assert f(*a[:3], 1e-3, 0.5, 4.0, *a[:7], 2, 64, 96, 64, 64, 64, None) == -2       # head size 96
+    assert f(*a[:3], 1e-3, 0.5, 4.0, *a[:7], 2, 64, 128, 64, 64, 60, None) == -2      # chunk not a multiple of 64
+    assert f(*a[:3], 1e-3, 0.5, 0.0, *a[:7], 2, 64, 128, 64, 64, 64, None) == -1      # tau 0
