@@ -74,6 +74,8 @@ E2_MIXER_CONFIG = dict(heads=16, seq=32768, dim=128, d_model=2048, chunk=512, et
 # the same mixer with a SwiGLU fast-weight net of `hidden` units per head
 E2_MLP_CONFIG = dict(heads=16, seq=32768, dim=128, hidden=256, d_model=2048, chunk=512, eta_base=3e-4,
                      alpha_base=0.5, tau=4.0, seed=7)
+# the hybrid block (SWA beside the SwiGLU TTT path, gated)
+E2_HYBRID_CONFIG = dict(E2_MLP_CONFIG, window=1024, rope_theta=10000.0, seed=8)
 
 
 def config(name: str, **overrides) -> dict:
@@ -260,3 +262,11 @@ def gen_e2_mlp_state(heads: int, dim: int, hidden: int, seed: int, device="cpu")
     w3 = (normal(seed, 13, H * D * Dh, device) / math.sqrt(Dh)).to(torch.float32).view(H, D, Dh)
     z = lambda t: torch.zeros_like(t)
     return dict(w1=w1, w2=w2, w3=w3, m1=z(w1), m2=z(w2), m3=z(w3))
+
+
+def gen_gate(heads: int, dim: int, d_model: int, seed: int, device="cpu") -> dict:
+    """Gate projection of the hybrid block: wgate ~ N(0, 1/d_model) [H dim,
+    d_model] rounded to bf16, bgate = 0 float [H dim]."""
+    n = heads * dim
+    wg = (normal(seed, 21, n * d_model, device).view(n, d_model) / math.sqrt(d_model)).to(torch.bfloat16)
+    return dict(wgate=wg, bgate=torch.zeros(n, dtype=torch.float32, device=device))

@@ -701,28 +701,12 @@ size_t mixer_work_bytes(int32_t H, int64_t T, int32_t D, int32_t C) {
 }
 }  // namespace
 
-extern "C" ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
-                                          float alpha_base, float tau, float* W, float* M, float* out, int32_t H,
-                                          int64_t T, int32_t D, int32_t dm, int32_t C, void* stream) {
-  using namespace ttt;
-  if (!x || !wqkv || !bias || !W || !M || !out) return TTT_ERR_INVALID_ARG;
-  if (H < 1 || T < 1 || C < 1 || dm < 1 || !(tau > 0.f) || !(eta_base >= 0.f) || !(alpha_base >= 0.f))
-    return TTT_ERR_INVALID_ARG;
-  if (D != 128 && D != 64) return TTT_ERR_UNSUPPORTED;
-  if (C % 64 || C > 2048 || dm % 8) return TTT_ERR_UNSUPPORTED;
-  if (((uintptr_t)x & 15) || ((uintptr_t)wqkv & 15) || ((uintptr_t)W & 15) || ((uintptr_t)M & 15))
-    return TTT_ERR_INVALID_ARG;
-  int ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
-    (void)hipGetLastError();
-    return TTT_ERR_NO_DEVICE;
-  }
-  hipStream_t st = (hipStream_t)stream;
-  const int64_t N = 3LL * H * D + 3LL * H, nch = (T + C - 1) / C;
-  const size_t need = mixer_work_bytes(H, T, D, C);
+namespace {
+// Grows the process-wide work buffer to at least `need` bytes on the
+// current device (g_e2_mu held; growing waits for the stream first).
+ttt_status e2_grow(size_t need, hipStream_t st) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_e2_mu);
   if (g_e2.bytes < need || g_e2.dev != dev) {
     if (g_e2.p) {
       (void)hipStreamSynchronize(st);
@@ -737,7 +721,37 @@ extern "C" ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const
     g_e2.bytes = need;
     g_e2.dev = dev;
   }
-  Carve cv{((uintptr_t)g_e2.p + 255) & ~(uintptr_t)255};
+  return TTT_OK;
+}
+
+ttt_status device_present() {
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return TTT_ERR_NO_DEVICE;
+  }
+  return TTT_OK;
+}
+
+ttt_status mixer_check(const void* x, const void* wqkv, const float* bias, float eta_base, float alpha_base,
+                       float tau, const float* out, int32_t H, int64_t T, int32_t D, int32_t dm, int32_t C) {
+  if (!x || !wqkv || !bias || !out) return TTT_ERR_INVALID_ARG;
+  if (H < 1 || T < 1 || C < 1 || dm < 1 || !(tau > 0.f) || !(eta_base >= 0.f) || !(alpha_base >= 0.f))
+    return TTT_ERR_INVALID_ARG;
+  if (D != 128 && D != 64) return TTT_ERR_UNSUPPORTED;
+  if (C % 64 || C > 2048 || dm % 8) return TTT_ERR_UNSUPPORTED;
+  if (((uintptr_t)x & 15) || ((uintptr_t)wqkv & 15) || ((uintptr_t)out & 15)) return TTT_ERR_INVALID_ARG;
+  return TTT_OK;
+}
+
+// The linear-fast-weight mixer on a work buffer of mixer_work_bytes().
+ttt_status mixer_linear_run(const void* x, const void* wqkv, const float* bias, float eta_base, float alpha_base,
+                            float tau, float* W, float* M, float* out, int32_t H, int64_t T, int32_t D, int32_t dm,
+                            int32_t C, void* work, void* stream) {
+  using namespace ttt;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t N = 3LL * H * D + 3LL * H, nch = (T + C - 1) / C;
+  Carve cv{((uintptr_t)work + 255) & ~(uintptr_t)255};
   float* P = cv.take<float>((size_t)T * N * 4);
   bf16* q = cv.take<bf16>((size_t)H * T * D * 2);
   bf16* k = cv.take<bf16>((size_t)H * T * D * 2);
@@ -787,6 +801,19 @@ extern "C" ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const
     if (hipMemcpyAsync(W, W2, (size_t)H * D * D * 4, hipMemcpyDeviceToDevice, st) != hipSuccess) return TTT_ERR_HIP;
   }
   return TTT_OK;
+}
+}  // namespace
+
+extern "C" ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
+                                          float alpha_base, float tau, float* W, float* M, float* out, int32_t H,
+                                          int64_t T, int32_t D, int32_t dm, int32_t C, void* stream) {
+  ttt_status r = mixer_check(x, wqkv, bias, eta_base, alpha_base, tau, out, H, T, D, dm, C);
+  if (r != TTT_OK) return r;
+  if (!W || !M || ((uintptr_t)W & 15) || ((uintptr_t)M & 15)) return TTT_ERR_INVALID_ARG;
+  if ((r = device_present()) != TTT_OK) return r;
+  std::lock_guard<std::mutex> lock(g_e2_mu);
+  if ((r = e2_grow(mixer_work_bytes(H, T, D, C), (hipStream_t)stream)) != TTT_OK) return r;
+  return mixer_linear_run(x, wqkv, bias, eta_base, alpha_base, tau, W, M, out, H, T, D, dm, C, g_e2.p, stream);
 }
 
 // ============================================ SwiGLU fast-weight token mixer
@@ -943,46 +970,27 @@ ttt::GemmArgs hg(const void* A, long lda, long sA, const void* B, long ldb, long
 }
 }  // namespace
 
-extern "C" ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
-                                                 float alpha_base, float tau, float* W1, float* W2, float* W3,
-                                                 float* M1, float* M2, float* M3, float* out, int32_t H, int64_t T,
-                                                 int32_t D, int32_t Dh, int32_t dm, int32_t C, void* stream) {
-  using namespace ttt;
-  if (!x || !wqkv || !bias || !W1 || !W2 || !W3 || !M1 || !M2 || !M3 || !out) return TTT_ERR_INVALID_ARG;
-  if (H < 1 || T < 1 || C < 1 || dm < 1 || Dh < 1 || !(tau > 0.f) || !(eta_base >= 0.f) || !(alpha_base >= 0.f))
-    return TTT_ERR_INVALID_ARG;
-  if (D != 128 && D != 64) return TTT_ERR_UNSUPPORTED;
-  if (C % 64 || C > 2048 || dm % 8 || Dh % 32 || Dh > 4096) return TTT_ERR_UNSUPPORTED;
-  for (const void* p : {x, wqkv, (const void*)W1, (const void*)W2, (const void*)W3, (const void*)M1,
-                        (const void*)M2, (const void*)M3, (const void*)out})
+namespace {
+ttt_status swiglu_check(const float* W1, const float* W2, const float* W3, const float* M1, const float* M2,
+                        const float* M3, int32_t Dh) {
+  if (!W1 || !W2 || !W3 || !M1 || !M2 || !M3 || Dh < 1) return TTT_ERR_INVALID_ARG;
+  if (Dh % 32 || Dh > 4096) return TTT_ERR_UNSUPPORTED;
+  for (const void* p : {(const void*)W1, (const void*)W2, (const void*)W3, (const void*)M1, (const void*)M2,
+                        (const void*)M3})
     if ((uintptr_t)p & 15) return TTT_ERR_INVALID_ARG;
-  int ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
-    (void)hipGetLastError();
-    return TTT_ERR_NO_DEVICE;
-  }
+  return TTT_OK;
+}
+
+// The SwiGLU-fast-weight mixer on a work buffer of mlp_mixer_work_bytes().
+ttt_status mixer_swiglu_run(const void* x, const void* wqkv, const float* bias, float eta_base, float alpha_base,
+                            float tau, float* W1, float* W2, float* W3, float* M1, float* M2, float* M3, float* out,
+                            int32_t H, int64_t T, int32_t D, int32_t Dh, int32_t dm, int32_t C, void* work,
+                            void* stream) {
+  using namespace ttt;
   hipStream_t st = (hipStream_t)stream;
   const int64_t N = 3LL * H * D + 3LL * H, nch = (T + C - 1) / C;
-  const size_t need = mlp_mixer_work_bytes(H, T, D, Dh, C);
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_e2_mu);
-  if (g_e2.bytes < need || g_e2.dev != dev) {
-    if (g_e2.p) {
-      (void)hipStreamSynchronize(st);
-      (void)hipFree(g_e2.p);
-    }
-    g_e2.p = nullptr;
-    g_e2.bytes = 0;
-    if (hipMalloc(&g_e2.p, need) != hipSuccess) {
-      (void)hipGetLastError();
-      return TTT_ERR_OOM;
-    }
-    g_e2.bytes = need;
-    g_e2.dev = dev;
-  }
   const size_t h = H, c = C, d = D, f = Dh;
-  Carve cv{((uintptr_t)g_e2.p + 255) & ~(uintptr_t)255};
+  Carve cv{((uintptr_t)work + 255) & ~(uintptr_t)255};
   float* P = cv.take<float>((size_t)T * N * 4);
   bf16* q = cv.take<bf16>(h * T * d * 2);
   bf16* k = cv.take<bf16>(h * T * d * 2);
@@ -1102,4 +1110,19 @@ extern "C" ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv
   E2CHK(il_rows(M2, M12, R, D, 1, false, st));
 #undef E2CHK
   return TTT_OK;
+}
+}  // namespace
+
+extern "C" ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
+                                                 float alpha_base, float tau, float* W1, float* W2, float* W3,
+                                                 float* M1, float* M2, float* M3, float* out, int32_t H, int64_t T,
+                                                 int32_t D, int32_t Dh, int32_t dm, int32_t C, void* stream) {
+  ttt_status r = mixer_check(x, wqkv, bias, eta_base, alpha_base, tau, out, H, T, D, dm, C);
+  if (r != TTT_OK) return r;
+  if ((r = swiglu_check(W1, W2, W3, M1, M2, M3, Dh)) != TTT_OK) return r;
+  if ((r = device_present()) != TTT_OK) return r;
+  std::lock_guard<std::mutex> lock(g_e2_mu);
+  if ((r = e2_grow(mlp_mixer_work_bytes(H, T, D, Dh, C), (hipStream_t)stream)) != TTT_OK) return r;
+  return mixer_swiglu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, W3, M1, M2, M3, out, H, T, D, Dh, dm,
+                          C, g_e2.p, stream);
 }
