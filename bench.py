@@ -360,6 +360,31 @@ def e2_bench(args, tla, torch, synth):
                                       f"C={sc['chunk']}",
                                fast_weight_gflop=round(fw_flops / 1e9, 1),
                                fast_weight_tflops=round(fw_flops / (sms * 1e-3) / 1e12, 1))
+    # the hybrid block: SWA beside the SwiGLU TTT path, gated
+    hc = synth.E2_HYBRID_CONFIG
+    hx = synth.gen_e2_mixer(hc["heads"], hc["seq"], hc["dim"], hc["d_model"], hc["seed"], device="cuda")
+    hg = synth.gen_gate(hc["heads"], hc["dim"], hc["d_model"], hc["seed"], device="cuda")
+    h0 = synth.gen_e2_mlp_state(hc["heads"], hc["dim"], hc["hidden"], hc["seed"], device="cuda")
+    hst = {k_: v_.clone() for k_, v_ in h0.items()}
+    ho = torch.empty(hc["seq"], hc["heads"] * hc["dim"], device="cuda")
+    hts = []
+    for i in range(max(1, args.warmup) + args.steps):
+        for k_ in hst:
+            hst[k_].copy_(h0[k_])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tla.e2ttt_hybrid_forward(hx["x"], hx["wqkv"], hx["bias"], hg["wgate"], hg["bgate"], hc["eta_base"],
+                                 hc["alpha_base"], hc["tau"], hc["rope_theta"], hc["window"], hst, hc["heads"],
+                                 hc["chunk"], out=ho)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= max(1, args.warmup):
+            hts.append(a.elapsed_time(b))
+    hms = sorted(hts)[len(hts) // 2]
+    out["hybrid_block"] = dict(ms_per_step=round(hms, 4), value=round(hc["seq"] / (hms * 1e-3), 1), unit="tokens/s",
+                               config=f"E2-TTT hybrid block (SWA window {hc['window']} beside the SwiGLU TTT path, "
+                                      f"gated): T={hc['seq']}, d_model={hc['d_model']}, H={hc['heads']} x "
+                                      f"{hc['dim']}, hidden {hc['hidden']}, C={hc['chunk']}")
     out["lact_baseline"] = dict(ms_per_step=round(lms, 4), value=round(H * T / (lms * 1e-3), 1),
                                 unit="token-heads/s", e2_cost_vs_lact=round(ms / lms - 1.0, 4),
                                 kernel="lact_chunk_scan (chunk-mean momentum, one aggregation per chunk)")

@@ -325,6 +325,28 @@ ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv, const flo
                                       float* M2, float* M3, float* out, int32_t H, int64_t T, int32_t D,
                                       int32_t Dh, int32_t dm, int32_t C, void* stream);
 
+/* The hybrid token-mixer block ([P3] 方法细节, 混合模型架构设计 and Figure 2):
+ * sliding-window attention on the shared projections beside the TTT path,
+ * interpolated element-wise by a data-dependent gate:
+ *   out = g * o_SWA + (1 - g) * o_TTT,   g = sigmoid(x wgate^T + bgate).
+ * The TTT path is e2ttt_mixer_forward (Dh = 0: W1 = W, M1 = M [H, D, D];
+ * W2, W3, M2, M3 unused and may be NULL) or e2ttt_mixer_swiglu_forward
+ * (Dh > 0), with the same arguments and state updates. The attention uses
+ * the q, k, v columns of the same projection before the TTT path's SiLU and
+ * L2 normalisation, rounded to bf16, with RoPE (half-split rotation, base
+ * rope_theta > 1, positions 0 .. T-1) on q and k, scale 1/sqrt(D), causal
+ * window `window` >= 1 (key t visible to query i iff i - window < t <= i),
+ * one key head per query head. wgate: device bf16 [H D, dm] (16-byte
+ * aligned); bgate: device float [H D]. out: device float [T, H D] (before
+ * any output projection). Errors as for the mixer calls; a key/value store
+ * slice of one head of 2^31 bytes or more (T above 2^23 for D 128) returns
+ * TTT_ERR_UNSUPPORTED. Shares the same cached work buffer. */
+ttt_status e2ttt_hybrid_forward(const void* x, const void* wqkv, const float* bias, const void* wgate,
+                                const float* bgate, float eta_base, float alpha_base, float tau, float rope_theta,
+                                int32_t window, float* W1, float* W2, float* W3, float* M1, float* M2, float* M3,
+                                int32_t Dh, float* out, int32_t H, int64_t T, int32_t D, int32_t dm, int32_t C,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

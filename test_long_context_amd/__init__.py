@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
                                           i32, i64, i32, i32, i32, vp]
         L.e2ttt_mixer_swiglu_forward.argtypes = [vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                                  vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp]
+        L.e2ttt_hybrid_forward.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, i64, i32, i32,
+                                           i32, vp]
         L.e2ttt_chunk_scan_noalloc_max_bytes.argtypes = []
         L.e2ttt_chunk_scan_noalloc_max_bytes.restype = i64
         L.ttt_timing_enable.argtypes = [vp, ctypes.c_uint32]
@@ -112,7 +115,7 @@ def lib() -> ctypes.CDLL:
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_decode_step_update", "ttt_get_fast_weights",
                   "ttt_get_fast_weights_seq",
                   "ttt_reset", "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan", "e2ttt_mixer_forward",
-                  "e2ttt_mixer_swiglu_forward",
+                  "e2ttt_mixer_swiglu_forward", "e2ttt_hybrid_forward",
                   "ttt_timing_enable", "ttt_timing_read", "tttk_gemm", "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce", "tttk_ce_lse",
                   "tttk_dw_sgd"):
             getattr(L, f).restype = st
@@ -322,6 +325,31 @@ def e2ttt_mixer_swiglu_forward(x, wqkv, bias, eta_base, alpha_base, tau, state: 
                                           _ptr(out), H, T, D, Dh, dm, chunk, _stream(stream))
     if st != TTT_OK:
         raise TTTError(st, "e2ttt_mixer_swiglu_forward")
+    return out
+
+
+def e2ttt_hybrid_forward(x, wqkv, bias, wgate, bgate, eta_base, alpha_base, tau, rope_theta, window: int,
+                         state: dict, heads: int, chunk: int, out=None, stream=None):
+    """Hybrid token-mixer block (see include/ttt.h): state is dict(W, M)
+    (linear fast weight) or dict(w1, w2, w3, m1, m2, m3) (SwiGLU net),
+    updated in place. Returns out [T, H D]."""
+    import torch
+    T, dm = x.shape
+    if "W" in state:
+        H, D, _ = state["W"].shape
+        Dh = 0
+        ptrs = [_ptr(state["W"]), 0, 0, _ptr(state["M"]), 0, 0]
+    else:
+        H, Dh, D = state["w1"].shape
+        ptrs = [_ptr(state[n]) for n in ("w1", "w2", "w3", "m1", "m2", "m3")]
+    assert H == heads
+    if out is None:
+        out = torch.empty(T, H * D, dtype=torch.float32, device=x.device)
+    st = lib().e2ttt_hybrid_forward(_ptr(x), _ptr(wqkv), _ptr(bias), _ptr(wgate), _ptr(bgate), float(eta_base),
+                                    float(alpha_base), float(tau), float(rope_theta), int(window), *ptrs, Dh,
+                                    _ptr(out), H, T, D, dm, chunk, _stream(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "e2ttt_hybrid_forward")
     return out
 
 

@@ -1126,3 +1126,141 @@ extern "C" ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv
   return mixer_swiglu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, W3, M1, M2, M3, out, H, T, D, Dh, dm,
                           C, g_e2.p, stream);
 }
+
+// ================================================== hybrid token-mixer block
+// [P3] 方法细节, 混合模型架构设计 and Figure 2: sliding-window attention on the
+// shared projections (RoPE on q and k, before the TTT path's SiLU and L2
+// normalisation) beside the TTT path, mixed element-wise by a data-dependent
+// gate: out = g o_SWA + (1 - g) o_TTT, g = sigmoid(x Wg^T + bg). The TTT
+// path writes o_TTT into out; the attention reuses the engine's RoPE scatter
+// into key/value stores of the whole stream and its second-generation
+// window-attention kernel; one element-wise pass applies the gate.
+namespace {
+// bf16 [T, 3 H D] copy of the projections' q, k, v columns (row stride N)
+__global__ void __launch_bounds__(256) raw_qkv_kernel(const float* __restrict__ P, int64_t N, int64_t T, int W,
+                                                      bf16* __restrict__ out) {
+  const int64_t n = T * W;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / W;
+    out[i] = (bf16)P[t * N + (i - t * W)];
+  }
+}
+
+// RoPE table [T][D / 2] of (cos, sin)(p theta^(-2 j / D)), angles in float64
+__global__ void __launch_bounds__(256) rope_table_kernel(float2* __restrict__ tab, int64_t T, int half, double theta) {
+  const int64_t n = T * half;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t p = i / half;
+    const int j = (int)(i - p * half);
+    const double inv = 1.0 / pow(theta, 2.0 * j / (2.0 * half));
+    const double a = (double)p * inv;
+    tab[i] = make_float2((float)cos(a), (float)sin(a));
+  }
+}
+
+// out = s o_swa + (1 - s) out with s = sigmoid(G + bg) (G [T, HD] float)
+__global__ void __launch_bounds__(256) gate_mix_kernel(const float* __restrict__ G, const float* __restrict__ bg,
+                                                       const bf16* __restrict__ oswa, float* __restrict__ out,
+                                                       int64_t T, int HD) {
+  const int64_t n = T * HD;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(i % HD);
+    const float s = 1.f / (1.f + __expf(-(G[i] + bg[j])));
+    out[i] = s * (float)oswa[i] + (1.f - s) * out[i];
+  }
+}
+
+int64_t hybrid_cap(int64_t T) {
+  int64_t c = 64;
+  while (c < T) c <<= 1;
+  return c;
+}
+
+size_t hybrid_extra_bytes(int32_t H, int64_t T, int32_t D) {
+  const size_t al = 256, HD = (size_t)H * D, cap = (size_t)hybrid_cap(T);
+  return (size_t)T * 3 * HD * 2 + al + (size_t)T * HD * 2 + al + 3 * ((size_t)H * cap * D * 2 + al) +
+         (size_t)T * HD * 2 + al + (size_t)T * HD * 4 + al + (size_t)T * (D / 2) * 8 + al + 256;
+}
+}  // namespace
+
+extern "C" ttt_status e2ttt_hybrid_forward(const void* x, const void* wqkv, const float* bias, const void* wgate,
+                                           const float* bgate, float eta_base, float alpha_base, float tau,
+                                           float rope_theta, int32_t window, float* W1, float* W2, float* W3,
+                                           float* M1, float* M2, float* M3, int32_t Dh, float* out, int32_t H,
+                                           int64_t T, int32_t D, int32_t dm, int32_t C, void* stream) {
+  using namespace ttt;
+  ttt_status r = mixer_check(x, wqkv, bias, eta_base, alpha_base, tau, out, H, T, D, dm, C);
+  if (r != TTT_OK) return r;
+  if (!wgate || !bgate || ((uintptr_t)wgate & 15) || window < 1 || !(rope_theta > 1.f) || Dh < 0)
+    return TTT_ERR_INVALID_ARG;
+  if (Dh > 0) {
+    if ((r = swiglu_check(W1, W2, W3, M1, M2, M3, Dh)) != TTT_OK) return r;
+  } else if (!W1 || !M1 || ((uintptr_t)W1 & 15) || ((uintptr_t)M1 & 15)) {
+    return TTT_ERR_INVALID_ARG;
+  }
+  // one head's slice of a key/value store is addressed with 32-bit offsets
+  if ((int64_t)hybrid_cap(T) * D * 2 >= (int64_t(1) << 31)) return TTT_ERR_UNSUPPORTED;
+  if ((r = device_present()) != TTT_OK) return r;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t base = Dh > 0 ? mlp_mixer_work_bytes(H, T, D, Dh, C) : mixer_work_bytes(H, T, D, C);
+  std::lock_guard<std::mutex> lock(g_e2_mu);
+  if ((r = e2_grow(base + hybrid_extra_bytes(H, T, D), st)) != TTT_OK) return r;
+  // TTT path: o_TTT into out; its projections P stay at the buffer's start
+  r = Dh > 0 ? mixer_swiglu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, W3, M1, M2, M3, out, H, T, D, Dh,
+                                dm, C, g_e2.p, stream)
+             : mixer_linear_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, M1, out, H, T, D, dm, C, g_e2.p,
+                                stream);
+  if (r != TTT_OK) return r;
+  const int64_t N = 3LL * H * D + 3LL * H, HD = (int64_t)H * D, cap = hybrid_cap(T);
+  const float* P = (const float*)(((uintptr_t)g_e2.p + 255) & ~(uintptr_t)255);
+  Carve cv{(((uintptr_t)g_e2.p + base) + 255) & ~(uintptr_t)255};
+  bf16* qkv = cv.take<bf16>((size_t)T * 3 * HD * 2);
+  bf16* qr = cv.take<bf16>((size_t)T * HD * 2);
+  bf16* ks = cv.take<bf16>((size_t)H * cap * D * 2);
+  bf16* vs = cv.take<bf16>((size_t)H * cap * D * 2);
+  bf16* vts = cv.take<bf16>((size_t)H * cap * D * 2);
+  bf16* oswa = cv.take<bf16>((size_t)T * HD * 2);
+  float* G = cv.take<float>((size_t)T * HD * 4);
+  float2* tab = cv.take<float2>((size_t)T * (D / 2) * 8);
+  hipLaunchKernelGGL(raw_qkv_kernel, dim3(2048), dim3(256), 0, st, P, N, T, (int)(3 * HD), qkv);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(1024), dim3(256), 0, st, tab, T, D / 2, (double)rope_theta);
+  if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
+  // the attention reads whole key tiles, so slots the stream never writes
+  // (past T - 1, before 0) are read as masked keys: they must hold finite
+  // values (0 x NaN is NaN), so the stores start zeroed
+  for (bf16* p : {ks, vs, vts})
+    if (fill_zero_bytes(p, (size_t)H * cap * D * 2, st) != hipSuccess) return TTT_ERR_HIP;
+  if (rope_scatter(DT::BF16, qkv, (int)T, H, H, D, 0, tab, qr, ks, vs, vts, (int)cap, 0, st) != hipSuccess)
+    return TTT_ERR_HIP;
+  AttnArgs a{};
+  a.q = qr;
+  a.k = ks;
+  a.v = vs;
+  a.vt = vts;
+  a.o = oswa;
+  a.lse = nullptr;
+  a.n = (int)T;
+  a.H = H;
+  a.Hk = H;
+  a.dh = D;
+  a.cap = (int)cap;
+  a.window = (int)std::min<int64_t>(window, T);
+  a.pos0 = 0;
+  a.scale = 1.f / sqrtf((float)D);
+  if (!attn_fwd2_supported(DT::BF16, a)) return TTT_ERR_UNSUPPORTED;
+  if (attn_fwd2(DT::BF16, a, st) != hipSuccess) return TTT_ERR_HIP;
+  GemmArgs g{};
+  g.A = x;
+  g.B = wgate;
+  g.M = (int)T;
+  g.N = (int)HD;
+  g.K = dm;
+  g.lda = dm;
+  g.ldb = dm;
+  g.C = G;
+  g.ldc = HD;
+  g.scale = 1.f;
+  if (gemm(DT::BF16, true, true, Epi::STORE_F32, g, st) != hipSuccess) return TTT_ERR_HIP;
+  hipLaunchKernelGGL(gate_mix_kernel, dim3(2048), dim3(256), 0, st, G, bgate, oswa, out, T, (int)HD);
+  return hipGetLastError() == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}

@@ -104,3 +104,15 @@ def test_e2_swiglu_mixer_argument_checks():
     assert f(*a[:3], 1e-3, 0.5, 4.0, *a[:7], 2, 64, 96, 64, 64, 64, None) == -2       # head size 96
     assert f(*a[:3], 1e-3, 0.5, 4.0, *a[:7], 2, 64, 128, 64, 64, 60, None) == -2      # chunk not a multiple of 64
     assert f(*a[:3], 1e-3, 0.5, 0.0, *a[:7], 2, 64, 128, 64, 64, 64, None) == -1      # tau 0
+
+
+def test_e2_hybrid_argument_checks():
+    f = tla.lib().e2ttt_hybrid_forward
+    a = [16] * 6
+    base = (16, 16, 16, 16, 16, 1e-4, 0.5, 4.0, 10000.0)
+    dims = (2, 64, 128, 64, 64, None)
+    assert f(*base, 0, *a, 0, 16, *dims) == -1            # window 0
+    assert f(*base[:8], 1.0, 16, *a, 0, 16, *dims) == -1  # rope base 1
+    assert f(*base[:3], None, *base[4:], 16, *a, 0, 16, *dims) == -1  # no gate weights
+    assert f(*base, 16, *a, 48, 16, *dims) == -2          # SwiGLU hidden not a multiple of 32
+    assert f(*base, 16, 16, 0, 0, 0, 0, 0, -1, 16, *dims) == -1  # negative hidden

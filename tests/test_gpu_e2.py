@@ -162,3 +162,61 @@ def test_e2_swiglu_mixer_full_workload():
     eo, ew, em = run_mlp_mixer(c["heads"], c["seq"], c["dim"], c["hidden"], c["d_model"], c["chunk"], c["seed"],
                                c["eta_base"], c["alpha_base"], c["tau"])
     assert eo < 2e-2 and ew < 5e-2 and em < 5e-2
+
+
+# ------------------------------------------------- hybrid token-mixer block
+def run_hybrid(H, T, D, Dh, dm, C, window, seed, eta_base, alpha_base=0.5, tau=4.0, theta=10000.0):
+    """The hybrid block (e2ttt_hybrid_forward: SWA beside the TTT path, gated)
+    against the float64 oracle. Errors as for the mixers: outputs and momenta
+    max |x - ref| / max |ref|; weights relative to their change (SwiGLU) or
+    to max |W| (linear)."""
+    import test_long_context_amd as tla
+    from oracle import e2ttt_hybrid as Y
+    from oracle import e2ttt_mlp as X
+    say(f"case: e2 hybrid H={H} T={T} D={D} Dh={Dh} dm={dm} C={C} window={window}")
+    g = synth.gen_e2_mixer(H, T, D, dm, seed)
+    gt = synth.gen_gate(H, D, dm, seed)
+    d = {k: v.cuda() for k, v in g.items()}
+    if Dh:
+        s0 = synth.gen_e2_mlp_state(H, D, Dh, seed)
+        W = [{m: s0[w][h].double().numpy() for m, w in zip(X.MATS, ("w1", "w2", "w3"))} for h in range(H)]
+        M = [{m: s0[w][h].double().numpy() for m, w in zip(X.MATS, ("m1", "m2", "m3"))} for h in range(H)]
+    else:
+        s0 = dict(W=g["W"], M=g["M"])
+        W, M = g["W"].double().numpy(), g["M"].double().numpy()
+    st = {k: v.cuda().clone() for k, v in s0.items()}
+    out = tla.e2ttt_hybrid_forward(d["x"], d["wqkv"], d["bias"], gt["wgate"].cuda(), gt["bgate"].cuda(), eta_base,
+                                   alpha_base, tau, theta, window, st, H, C)
+    torch.cuda.synchronize()
+    Or, Wr, Mr = Y.hybrid_mixer(g["x"].double().numpy(), g["wqkv"].double().numpy(), g["bias"].numpy(),
+                                gt["wgate"].double().numpy(), gt["bgate"].double().numpy(), eta_base, alpha_base,
+                                tau, theta, window, (W, M), H, D, C)
+    eo = np.max(np.abs(out.cpu().numpy().reshape(T, H, D) - Or)) / np.max(np.abs(Or))
+    if Dh:
+        ew = em = 0.0
+        for m, wn, mn in zip(X.MATS, ("w1", "w2", "w3"), ("m1", "m2", "m3")):
+            wr = np.stack([Wr[h][m] for h in range(H)])
+            mr = np.stack([Mr[h][m] for h in range(H)])
+            ew = max(ew, np.max(np.abs(st[wn].cpu().double().numpy() - wr)) /
+                     np.max(np.abs(wr - s0[wn].double().numpy())))
+            em = max(em, np.max(np.abs(st[mn].cpu().double().numpy() - mr)) / np.max(np.abs(mr)))
+    else:
+        ew = np.max(np.abs(st["W"].cpu().numpy() - Wr)) / np.max(np.abs(Wr))
+        em = np.max(np.abs(st["M"].cpu().numpy() - Mr)) / np.max(np.abs(Mr))
+    say(f"  outputs rel err {eo:.3e}  W err {ew:.3e}  M rel err {em:.3e}")
+    return eo, ew, em
+
+
+@pytest.mark.parametrize("H,T,D,Dh,dm,C,window,eta", [(2, 300, 64, 64, 128, 64, 48, 3e-4),
+                                                      (3, 1000, 128, 0, 256, 256, 100, 1e-4),
+                                                      (1, 2048 + 77, 128, 128, 128, 2048, 1024, 3e-4)])
+def test_e2_hybrid_small_and_ragged(H, T, D, Dh, dm, C, window, eta):
+    eo, ew, em = run_hybrid(H, T, D, Dh, dm, C, window, 10, eta)
+    assert eo < 2e-2 and ew < 5e-2 and em < 5e-2
+
+
+def test_e2_hybrid_full_workload():
+    c = synth.E2_HYBRID_CONFIG
+    eo, ew, em = run_hybrid(c["heads"], c["seq"], c["dim"], c["hidden"], c["d_model"], c["chunk"], c["window"],
+                            c["seed"], c["eta_base"], c["alpha_base"], c["tau"], c["rope_theta"])
+    assert eo < 2e-2 and ew < 5e-2 and em < 5e-2
