@@ -95,8 +95,8 @@ def roof_source_hash(files=ROOF_SOURCES) -> str:
 def update_replay(c, tla, torch, blocks=2):
     """The update products of `blocks` dynamic blocks at the workload's
     shape, launched as the engine launches them (dW3 = dY^T Hmid, then dW12
-    = dH12^T U, each a GEMM with the SGD epilogue writing the fp32 master,
-    the bf16 working copy and its low term)."""
+    = dH12^T U, each a GEMM with the SGD epilogue writing the fp32 master
+    and the stochastically rounded bf16 working copy)."""
     d, Fd, b = c["d_model"], c["dyn_ffn_hidden"], c["minibatch"]
     bf = torch.bfloat16
     g = torch.Generator(device="cuda").manual_seed(0)
@@ -106,12 +106,13 @@ def update_replay(c, tla, torch, blocks=2):
     xn = (torch.randn(b, d, device="cuda", generator=g) * 0.1).to(bf)
     m3 = torch.randn(d, Fd, device="cuda", generator=g) * 0.02
     m12 = torch.randn(2 * Fd, d, device="cuda", generator=g) * 0.02
-    h3, l3 = torch.empty(d, Fd, dtype=bf, device="cuda"), torch.empty(d, Fd, dtype=bf, device="cuda")
-    h12, l12 = torch.empty(2 * Fd, d, dtype=bf, device="cuda"), torch.empty(2 * Fd, d, dtype=bf, device="cuda")
-    for _ in range(blocks):
-        tla.gemm(gt, hm, d, Fd, b, "sgd", m3, a_kmajor=False, b_kmajor=False, C2=h3, C3=l3, scale=c["alpha"])
-        tla.gemm(dh12, xn, 2 * Fd, d, b, "sgd", m12, a_kmajor=False, b_kmajor=False, C2=h12, C3=l12,
-                 scale=c["alpha"])
+    h3 = torch.empty(d, Fd, dtype=bf, device="cuda")
+    h12 = torch.empty(2 * Fd, d, dtype=bf, device="cuda")
+    for i in range(blocks):
+        tla.gemm(gt, hm, d, Fd, b, "sgd", m3, a_kmajor=False, b_kmajor=False, C2=h3, scale=c["alpha"],
+                 seed=2 * i + 1)
+        tla.gemm(dh12, xn, 2 * Fd, d, b, "sgd", m12, a_kmajor=False, b_kmajor=False, C2=h12, scale=c["alpha"],
+                 seed=2 * i + 2)
     torch.cuda.synchronize()
     print(json.dumps(dict(launches=2 * blocks)), flush=True)
 

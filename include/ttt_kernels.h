@@ -44,11 +44,15 @@ typedef enum {
  * 64x64): 0 = chosen from the shape, 1 = 128x128 (4 waves of 64x64),
  * 2 = 256x128 (4 of 128x64), 3 = 256x128 (8 of 64x64), 4 = 256x256 (4 of
  * 128x128), 5 = 256x256 (8 of 128x64), 6 = 128x256 (4 of 64x128); K steps
- * of 64. */
+ * of 64. seed (TTTK_EPI_SGD, bf16, C2 a separate working copy, C3 NULL;
+ * else 0): nonzero rounds C2 from the master stochastically -- up with
+ * probability equal to the fraction of a bf16 ulp that rounding drops,
+ * from 16 random bits hashed from (seed, element index) -- instead of to
+ * nearest. */
 ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajor, int32_t epi, const void* A,
                      int64_t lda, const void* B, int64_t ldb, const void* B2, int32_t M, int32_t N,
                      int32_t K, void* C, int64_t ldc, void* C2, void* C3, const void* X, float scale,
-                     int32_t kchunk, int32_t tile, void* stream);
+                     int32_t kchunk, int32_t tile, uint32_t seed, void* stream);
 
 /* Sliding-window attention forward for n queries at positions pos0 .. pos0+n-1
  * (q: [n, H, dh]) over a key/value store k, v: [Hk][cap][dh] indexed by

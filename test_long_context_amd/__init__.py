@@ -100,7 +100,7 @@ def lib() -> ctypes.CDLL:
         L.ttt_timing_read.argtypes = [vp, i32, dp, lp, dp, dp]
         f32 = ctypes.c_float
         L.tttk_gemm.argtypes = [i32, i32, i32, i32, vp, i64, vp, i64, vp, i32, i32, i32, vp, i64, vp, vp,
-                                vp, f32, i32, i32, vp]
+                                vp, f32, i32, i32, ctypes.c_uint32, vp]
         L.tttk_attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, vp,
                                     vp]
         L.tttk_attn_fwd_workspace.argtypes = [i32, i32, i32, i32, i32]
@@ -383,14 +383,14 @@ def _check(st, what):
 
 
 def gemm(A, B, M, N, K, epi, C, *, a_kmajor=True, b_kmajor=True, lda=None, ldb=None, ldc=None,
-         B2=None, C2=None, C3=None, X=None, scale=1.0, kchunk=0, tile=0, stream=None):
+         B2=None, C2=None, C3=None, X=None, scale=1.0, kchunk=0, tile=0, seed=0, stream=None):
     """One GEMM-family launch (include/ttt_kernels.h, tttk_gemm)."""
     lda = lda if lda is not None else (K if a_kmajor else M)
     ldb = ldb if ldb is not None else (K if b_kmajor else N)
     ldc = ldc if ldc is not None else N
     _check(lib().tttk_gemm(_dt(A), int(a_kmajor), int(b_kmajor), EPI[epi], _ptr(A), lda, _ptr(B), ldb,
                            _ptr(B2), M, N, K, _ptr(C), ldc, _ptr(C2), _ptr(C3), _ptr(X), float(scale),
-                           int(kchunk), int(tile), _stream(stream)), "tttk_gemm")
+                           int(kchunk), int(tile), int(seed), _stream(stream)), "tttk_gemm")
 
 
 def attn_fwd_workspace(n, H, dh, window, ksplit=0):

@@ -131,6 +131,7 @@ struct ttt_ctx {
   std::vector<void*> dh12d;                  // [b, 2 Fd] SwiGLU pre-activation gradients per dynamic block
   bool fused_update = false;                 // bf16: both update products in one dw_sgd launch
   bool upd_main = false;                     // update products on the caller's stream instead of side streams
+  bool sr_round = false;                     // bf16: one stochastically rounded working copy, no low term
   int upd_grid = 0;                          // its workgroups (0: two per CU)
   hipStream_t dstream = nullptr;             // decode graph capture stream
   hipGraphExec_t dgraph = nullptr;           // captured decode blocks
@@ -541,7 +542,7 @@ ttt_status loop_forward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     // round most updates back to the old weights, coherently)
     GemmArgs g = ga(c->xn_d[i], d, c->dw12[i], d, n, 2 * Fd, d, c->h12_d[i], 2 * Fd);
     g.C2 = c->hm_d[i];
-    g.B2 = c->dw12_lo[i];
+    g.B2 = c->sr_round ? nullptr : c->dw12_lo[i];
     Bat b12;
     b12.n = B;
     b12.sA = (long)n * d;
@@ -554,7 +555,8 @@ ttt_status loop_forward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     b3.n = B;
     b3.sA = (long)n * Fd;
     b3.sB = (long)d * Fd;
-    RUN(gemm_resid(c, KC_GL, c->hm_d[i], Fd, c->dw3[i], Fd, c->dw3_lo[i], n, d, Fd, &np, st, b3));
+    RUN(gemm_resid(c, KC_GL, c->hm_d[i], Fd, c->dw3[i], Fd, c->sr_round ? nullptr : c->dw3_lo[i], n, d, Fd, &np, st,
+                   b3));
   }
   TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_f, c->final_norm, nb, d, eps, c->xn,
                                         c->r_f, st));
@@ -589,6 +591,12 @@ ttt_status run_ce(ttt_ctx* c, int64_t a0, int n, int nt, float scale, float* los
             ce_fwd_bwd(c->dt, logits, n, nt, c->V, labels, scale, loss, dz, c->d_err, st));
   }
   return TTT_OK;
+}
+
+// Seed of one update product's stochastic rounding (never 0): distinct for
+// every mini-batch, dynamic block and product.
+uint32_t sr_seed(int64_t step, int block, int which) {
+  return (uint32_t)((((uint64_t)step * 64 + (uint64_t)block) * 2 + (uint64_t)which) * 0x9E3779B1ull) | 1u;
 }
 
 ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
@@ -646,7 +654,8 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         hipStream_t st = us2;
         GemmArgs g = ga(gt, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
         g.C2 = c->dw3[i];
-        g.C3 = c->dw3_lo[i];
+        g.C3 = c->sr_round ? nullptr : c->dw3_lo[i];
+        g.seed = c->sr_round ? sr_seed(a0 / c->b, i, 0) : 0u;
         g.scale = lr;
         Bat bt;
         bt.n = B;
@@ -662,7 +671,8 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         hipStream_t st = us1;
         GemmArgs g2 = ga(c->dh12d[i], 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
         g2.C2 = c->dw12[i];
-        g2.C3 = c->dw12_lo[i];
+        g2.C3 = c->sr_round ? nullptr : c->dw12_lo[i];
+        g2.seed = c->sr_round ? sr_seed(a0 / c->b, i, 1) : 0u;
         g2.scale = lr;
         Bat bt;
         bt.n = B;
@@ -826,6 +836,13 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   c->max_split = 16;
   c->B = cfg->n_seq > 0 ? cfg->n_seq : 1;
   c->ring_seq = (size_t)c->Hk * c->cap * c->dh;
+  // bf16 working copy of the fast weights: one copy rounded stochastically
+  // from the fp32 master (default), or, with TTT_WEIGHT_ROUNDING=nearest, the
+  // master rounded to nearest plus a low term (two bf16 terms in the forward)
+  {
+    const char* wr = getenv("TTT_WEIGHT_ROUNDING");
+    c->sr_round = c->dt == DT::BF16 && !(wr && strcmp(wr, "nearest") == 0);
+  }
   const size_t es = c->es;
   const int d = c->d, L = c->L, nd = c->nd, B = c->B, b = c->b * c->B;  // b: loop rows (B mini-batches)
   const int64_t S = c->slab;
@@ -878,8 +895,10 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     } else {
       A(&c->dw12[i], (size_t)B * 2 * c->Fd * d * es);
       A(&c->dw3[i], (size_t)B * d * c->Fd * es);
-      A(&c->dw12_lo[i], (size_t)B * 2 * c->Fd * d * es);
-      A(&c->dw3_lo[i], (size_t)B * d * c->Fd * es);
+      if (!c->sr_round) {
+        A(&c->dw12_lo[i], (size_t)B * 2 * c->Fd * d * es);
+        A(&c->dw3_lo[i], (size_t)B * d * c->Fd * es);
+      }
     }
     A(&c->w0_12[i], (size_t)2 * c->Fd * d * es);
     A(&c->w0_3[i], (size_t)d * c->Fd * es);
@@ -985,7 +1004,7 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   // waves, one per SIMD, wait for every K step's operand loads.
   {
     const char* uk = getenv("TTT_UPDATE_KERNEL");
-    c->fused_update = c->dt == DT::BF16 && B == 1 && uk && strcmp(uk, "fused") == 0;
+    c->fused_update = c->dt == DT::BF16 && B == 1 && !c->sr_round && uk && strcmp(uk, "fused") == 0;
     const char* us = getenv("TTT_UPDATE_STREAM");
     c->upd_main = us && strcmp(us, "main") == 0;
     const char* ug = getenv("TTT_UPDATE_GRID");

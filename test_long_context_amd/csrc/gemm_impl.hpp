@@ -446,6 +446,25 @@ __device__ __forceinline__ floatx4 upc4(bf16x4 v) {
   return r;
 }
 
+// Stochastic rounding of the bf16 working copy: a 32-bit integer mixing
+// function of (seed, element index) -- the xor-shift-multiply "lowbias32"
+// hash -- supplies 16 random bits that are added to the bits bf16 drops,
+// then the value is truncated: it rounds up with probability equal to the
+// dropped fraction, so E[bf16(w)] = w and no update is lost coherently.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+__device__ __forceinline__ bf16 sr_bf16(float w, uint32_t seed, long idx) {
+  const uint32_t r = mix32((uint32_t)idx * 0x9E3779B1u + mix32(seed ^ (uint32_t)(idx >> 32)));
+  const uint32_t u = __builtin_bit_cast(uint32_t, w) + (r & 0xFFFFu);
+  return __builtin_bit_cast(bf16, (uint16_t)(u >> 16));
+}
+
 // pre: for ADD_F32 / SGD, the chunk's fp32 C values loaded ahead (used
 // when the chunk is a whole vector)
 template <int EPI>
@@ -476,22 +495,36 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& g, int m, int n, float
     const bool two = g.C2 != g.C;
     bf16* H = (bf16*)g.C2 + idx;
     bf16* L = g.C3 ? (bf16*)g.C3 + idx : nullptr;
+    // (the same bits for every product of a batch: a sequence's rounding
+    // does not depend on its place in the batch)
+    const uint32_t sd = g.seed;
     if (vec) {
       const floatx4 w = pre - g.scale * v;
       *(floatx4*)W = w;
       if (two) {
-        const bf16x4 hi = cvt4(w);
-        *(bf16x4*)H = hi;
-        if (L) *(bf16x4*)L = cvt4(w - upc4(hi));
+        if (g.seed) {
+          bf16x4 hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hi[e] = sr_bf16(w[e], sd, idx + e);
+          *(bf16x4*)H = hi;
+        } else {
+          const bf16x4 hi = cvt4(w);
+          *(bf16x4*)H = hi;
+          if (L) *(bf16x4*)L = cvt4(w - upc4(hi));
+        }
       }
     } else {
       for (int e = 0; e < ne; ++e) {
         const float w = W[e] - g.scale * v[e];
         W[e] = w;
         if (two) {
-          const bf16 hi = (bf16)w;
-          H[e] = hi;
-          if (L) L[e] = (bf16)(w - (float)hi);
+          if (g.seed) {
+            H[e] = sr_bf16(w, sd, idx + e);
+          } else {
+            const bf16 hi = (bf16)w;
+            H[e] = hi;
+            if (L) L[e] = (bf16)(w - (float)hi);
+          }
         }
       }
     }

@@ -17,7 +17,7 @@ extern "C" ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajo
                                 const void* A, int64_t lda, const void* B, int64_t ldb, const void* B2,
                                 int32_t M, int32_t N, int32_t K, void* C, int64_t ldc, void* C2,
                                 void* C3, const void* X, float scale, int32_t kchunk, int32_t tile,
-                                void* stream) {
+                                uint32_t seed, void* stream) {
   if (!dt_ok(dtype) || epi < 0 || (epi > TTTK_EPI_PARTIAL && epi != TTTK_EPI_STORE_F32_LSE) || M < 0 || N < 0 ||
       K < 0)
     return TTT_ERR_INVALID_ARG;
@@ -32,6 +32,7 @@ extern "C" ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajo
   if (epi == TTTK_EPI_SWIGLU && (N % 32 || !C2)) return TTT_ERR_INVALID_ARG;
   if (epi == TTTK_EPI_SWIGLU_BWD && (N % 16 || !X || ldc < 2 * N)) return TTT_ERR_INVALID_ARG;
   if (epi == TTTK_EPI_SGD && !C2) return TTT_ERR_INVALID_ARG;
+  if (seed && (epi != TTTK_EPI_SGD || dtype != TTT_BF16 || C3 || C2 == C)) return TTT_ERR_INVALID_ARG;
   if (epi == TTTK_EPI_PARTIAL && kchunk > 0 && kchunk % gemm_k_granule(to_dt(dtype))) return TTT_ERR_INVALID_ARG;
   if (B2 && (dtype != TTT_BF16 || !a_kmajor || !b_kmajor ||
              (epi != TTTK_EPI_SWIGLU && epi != TTTK_EPI_ADD_F32 && epi != TTTK_EPI_PARTIAL) || !al16(B2)))
@@ -53,6 +54,7 @@ extern "C" ttt_status tttk_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajo
   g.scale = scale;
   g.kchunk = epi == TTTK_EPI_PARTIAL ? kchunk : 0;
   g.tile = tile;
+  g.seed = seed;
   if (gemm(to_dt(dtype), a_kmajor != 0, b_kmajor != 0, (Epi)epi, g, (hipStream_t)stream) != hipSuccess)
     return TTT_ERR_HIP;
   return TTT_OK;

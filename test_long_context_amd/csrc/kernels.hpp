@@ -26,7 +26,8 @@ enum class Epi : int {
   SWIGLU_BWD,   // acc = dHmid[m, j]; X = pre-activations (ld = 2N):
                 // C (T) [m, gate/up col] = (dA, dC)
   SGD,          // C (float master) -= scale * acc; C2 (T) = round(master),
-                // C3 (T, optional) = round(master - C2)
+                // C3 (T, optional) = round(master - C2); or, with seed != 0,
+                // C2 = stochastic rounding of the master (no C3)
   PARTIAL,      // C (float) [split][M][ldc] = acc  (split-K)
   PARTIAL_BF16, // C (bf16) [split][M][ldc] = acc  (split-K gradient partials; bf16 NN only)
   STORE_F32_LSE,// C (float) = acc, and per 64-column group of each row its (max, sum of
@@ -53,6 +54,10 @@ struct GemmArgs {
   int batch;
   long sA, sB, sC, sC2, sX;
   long split_ld;  // PARTIAL epilogues: elements between split-K slices (0: M ldc)
+  // SGD with a bf16 working copy: 0 = C2 is the master rounded to nearest;
+  // otherwise C2 is rounded stochastically (unbiased) with random bits from
+  // this seed and the element's index, and C3 is not written
+  uint32_t seed;
 };
 
 hipError_t gemm(DT dt, bool a_kmajor, bool b_kmajor, Epi epi, const GemmArgs& g, hipStream_t st);

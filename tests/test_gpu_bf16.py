@@ -249,7 +249,28 @@ def test_bf16_fused_update_kernel_option():
                      ffn_hidden=1024, dyn_ffn_hidden=1024, vocab=4096, window=1024, minibatch=1024,
                      n_dynamic=2, alpha=0.01)
     os.environ["TTT_UPDATE_KERNEL"] = "fused"
+    os.environ["TTT_WEIGHT_ROUNDING"] = "nearest"  # the fused kernel writes the two-term copy
     try:
         check(c, T=2600)
     finally:
         del os.environ["TTT_UPDATE_KERNEL"]
+        del os.environ["TTT_WEIGHT_ROUNDING"]
+
+
+@pytest.mark.parametrize("workload", ["small", "1b"])
+def test_bf16_two_term_working_copy_option(workload):
+    """TTT_WEIGHT_ROUNDING=nearest: the working copy rounded to nearest plus a
+    low term, both in the forward products (instead of one stochastically
+    rounded copy)."""
+    if workload == "small":
+        c = synth.config("125m", n_layers=4, d_model=256, n_heads=4, n_kv_heads=2, head_dim=128,
+                         ffn_hidden=512, dyn_ffn_hidden=512, vocab=4096, window=256, minibatch=128,
+                         n_dynamic=2, alpha=0.01)
+        T = 700
+    else:
+        c, T = synth.config("1b"), 2 * 1024 + 1
+    os.environ["TTT_WEIGHT_ROUNDING"] = "nearest"
+    try:
+        check(c, T=T)
+    finally:
+        del os.environ["TTT_WEIGHT_ROUNDING"]

@@ -124,6 +124,42 @@ def test_gemm_sgd_epilogue(lay):
     assert torch.equal(lo.cpu().view(M, N), (Wf - Wf.to(bf).float()).to(bf))
 
 
+def test_gemm_sgd_stochastic_rounding():
+    """seed != 0: the master update is unchanged and the bf16 working copy is
+    one of the master's two bf16 neighbours, rounded up with probability
+    equal to the dropped fraction of an ulp -- unbiased where rounding to
+    nearest is not. The product is zero (A = 0) so the master keeps values
+    placed at known fractions 0.1, 0.3, 0.5 and 0.8 of an ulp above a bf16
+    value; 32768 entries per fraction."""
+    M, N, K = 256, 512, 64
+    g = torch.Generator().manual_seed(17)
+    base = (torch.randn(M * N, generator=g) * 0.02).to(bf).float()
+    ulp = ((base.view(torch.int32) + (1 << 16)).view(torch.float32) - base).abs()
+    fr = torch.tensor([0.1, 0.3, 0.5, 0.8]).repeat_interleave(M * N // 4)
+    W0 = base + torch.sign(base) * fr * ulp
+    W = W0.to(dev)
+    A = torch.zeros(M * K, dtype=bf, device=dev)
+    B = torch.zeros(N * K, dtype=bf, device=dev)
+    hi = torch.empty(M * N, dtype=bf, device=dev)
+    tla.gemm(A, B, M, N, K, "sgd", W, a_kmajor=False, b_kmajor=False, C2=hi, scale=1e-3, seed=12345)
+    assert torch.equal(W.cpu(), W0)
+    h = hi.cpu().float()
+    up = (h - base).abs() > 0
+    assert torch.all((h == base) | ((h - base).abs() - ulp).abs().le(0))
+    for q, f in enumerate((0.1, 0.3, 0.5, 0.8)):
+        sl = slice(q * M * N // 4, (q + 1) * M * N // 4)
+        rate = float(up[sl].float().mean())
+        n = M * N // 4
+        say(f"  fraction {f}: rounded up {rate:.4f} of {n}")
+        assert abs(rate - f) < 6 * (f * (1 - f) / n) ** 0.5
+    # the same seed gives the same bits; another seed other bits
+    hi2 = torch.empty_like(hi)
+    tla.gemm(A, B, M, N, K, "sgd", W, a_kmajor=False, b_kmajor=False, C2=hi2, scale=1e-3, seed=12345)
+    assert torch.equal(hi, hi2)
+    tla.gemm(A, B, M, N, K, "sgd", W, a_kmajor=False, b_kmajor=False, C2=hi2, scale=1e-3, seed=777)
+    assert not torch.equal(hi, hi2)
+
+
 # The inner loop's products at the 3B shape (d 3072, F 8192, V 128256,
 # mini-batch 1024), in the launch configuration the engine picks (tile 0),
 # checked on sampled output entries.
