@@ -114,8 +114,8 @@ __device__ __forceinline__ void rms_add_parts(float4 (&a)[NVT], const PT* src, l
 // One workgroup per row; thread t holds float4 chunks t, t + RB, ... (NVT of
 // them, d <= 4 RB NVT) in registers between the reduction and the output
 // pass; the gain is requested with the row.
-template <typename T, int NVT>
-__global__ void __launch_bounds__(RB) rms_fwd_kernel(const float* x_in, const float* parts, int nsplit, long pstride,
+template <typename T, int NVT, typename PT>
+__global__ void __launch_bounds__(RB) rms_fwd_kernel(const float* x_in, const PT* parts, int nsplit, long pstride,
                                                      float* x_out, float* save, const float* g, int d, float eps,
                                                      T* y, float* r) {
   __shared__ float sh[RB / 64];
@@ -153,15 +153,15 @@ __global__ void __launch_bounds__(RB) rms_fwd_kernel(const float* x_in, const fl
   if (threadIdx.x == 0) r[t] = rr;
 }
 
-template <typename T, int NVT>
-static void rms_fwd_launch(const float* x_in, const float* parts, int nsplit, long ps, float* x_out, float* save,
+template <typename T, int NVT, typename PT>
+static void rms_fwd_launch(const float* x_in, const PT* parts, int nsplit, long ps, float* x_out, float* save,
                            const float* g, int n, int d, float eps, T* y, float* r, hipStream_t st) {
-  hipLaunchKernelGGL((rms_fwd_kernel<T, NVT>), dim3(n), dim3(RB), 0, st, x_in, parts, nsplit, ps, x_out, save, g, d,
-                     eps, y, r);
+  hipLaunchKernelGGL((rms_fwd_kernel<T, NVT, PT>), dim3(n), dim3(RB), 0, st, x_in, parts, nsplit, ps, x_out, save, g,
+                     d, eps, y, r);
 }
 
-template <typename T>
-static hipError_t rms_fwd_t(const float* x_in, const float* parts, int nsplit, long ps, float* x_out, float* save,
+template <typename T, typename PT>
+static hipError_t rms_fwd_t(const float* x_in, const PT* parts, int nsplit, long ps, float* x_out, float* save,
                             const float* g, int n, int d, float eps, T* y, float* r, hipStream_t st) {
   const int nvt = (d / 4 + RB - 1) / RB;
   switch (nvt) {
@@ -187,9 +187,18 @@ hipError_t rmsnorm_fwd_fused(DT dt, const float* x_in, const float* parts, int n
   return rms_fwd_t<float>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, (float*)y, r, st);
 }
 
+hipError_t rmsnorm_fwd_fused(DT dt, const float* x_in, const __bf16* parts, int nsplit, float* x_out, float* save,
+                             const float* g, int n, int d, float eps, void* y, float* r, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (d % 4 || d > 4 * RB * RMS_MAXV) return hipErrorInvalidValue;
+  const long ps = (long)n * d;
+  if (dt == DT::BF16) return rms_fwd_t<bf16>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, (bf16*)y, r, st);
+  return rms_fwd_t<float>(x_in, parts, nsplit, ps, x_out, save, g, n, d, eps, (float*)y, r, st);
+}
+
 hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, float eps, void* y,
                        float* r, hipStream_t st) {
-  return rmsnorm_fwd_fused(dt, x, nullptr, 0, nullptr, nullptr, g, n, d, eps, y, r, st);
+  return rmsnorm_fwd_fused(dt, x, (const float*)nullptr, 0, nullptr, nullptr, g, n, d, eps, y, r, st);
 }
 
 // dx = r (g dy) - x r^3 mean((g dy) x); dh (+)= dx; dh_t = T(dh); dy is the

@@ -132,6 +132,7 @@ struct ttt_ctx {
   bool fused_update = false;                 // bf16: both update products in one dw_sgd launch
   bool upd_main = false;                     // update products on the caller's stream instead of side streams
   bool sr_round = false;                     // bf16: one stochastically rounded working copy, no low term
+  bool fwd_parts_bf16 = false;               // bf16: the forward's split-K partial sums stored in bf16
   int upd_grid = 0;                          // its workgroups (0: two per CU)
   hipStream_t dstream = nullptr;             // decode graph capture stream
   hipGraphExec_t dgraph = nullptr;           // captured decode blocks
@@ -473,8 +474,18 @@ ttt_status gemm_resid(ttt_ctx* c, int kind, const void* A, long lda, const void*
   }
   if (c->dt == DT::BF16) g.tile = 5;
   *np = s;
-  TCALL(kind, gfl(M, N, K) * (B2 ? 2.0 : 1.0) * bt.n, 0, gemm(c->dt, true, true, Epi::PARTIAL, g, st));
+  TCALL(kind, gfl(M, N, K) * (B2 ? 2.0 : 1.0) * bt.n, 0,
+        gemm(c->dt, true, true, c->fwd_parts_bf16 ? Epi::PARTIAL_BF16 : Epi::PARTIAL, g, st));
   return TTT_OK;
+}
+
+// Fused RMSNorm of the residual stream xr plus the np pending split-K
+// partial sums in c->part (bf16 or fp32, as gemm_resid stored them).
+hipError_t rms_fwd_parts(ttt_ctx* c, const float* xr, int np, float* save, const float* gain, int n, int d, float eps,
+                         void* y, float* r, hipStream_t st) {
+  if (c->fwd_parts_bf16)
+    return rmsnorm_fwd_fused(c->dt, xr, (const __bf16*)c->part, np, nullptr, save, gain, n, d, eps, y, r, st);
+  return rmsnorm_fwd_fused(c->dt, xr, (const float*)c->part, np, nullptr, save, gain, n, d, eps, y, r, st);
 }
 
 // Forward of the mini-batch [a0, a0 + n) of every sequence.
@@ -492,7 +503,7 @@ ttt_status loop_forward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     const int i = l - s;
     if (l > s) {
       // attention sublayer (adds the pending dynamic-MLP output of block l-1)
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_att[i], c->attn_norm[l], nb, d, eps,
+      TCALL(KC_OT, 0, 0, rms_fwd_parts(c, xr, np, c->h_att[i], c->attn_norm[l], nb, d, eps,
                                             c->xn, c->r_att[i], st));
       xr = c->h_att[i];
       TCALL(KC_GL, gfl(nb, QKV, d), 0,
@@ -514,7 +525,7 @@ ttt_status loop_forward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       }
       RUN(gemm_resid(c, KC_GL, c->o_l[i], (long)H * dh, c->wo[l], (long)H * dh, nullptr, nb, d, H * dh, &np, st));
       // static MLP sublayer
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_mlp[i], c->mlp_norm[l], nb, d, eps,
+      TCALL(KC_OT, 0, 0, rms_fwd_parts(c, xr, np, c->h_mlp[i], c->mlp_norm[l], nb, d, eps,
                                             c->xn, c->r_mlp[i], st));
       xr = c->h_mlp[i];
       GemmArgs g = ga(c->xn, d, c->w12[l], d, nb, 2 * F, d, c->h12_s[i], 2 * F);
@@ -524,14 +535,14 @@ ttt_status loop_forward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       // the previous mini-batch's update of this block (side stream) reads
       // xn_d and the saved activations written from here on
       HIPCHK(c, hipStreamWaitEvent(st, c->ev_upd[i], 0));
-      TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_dyn[i], c->dyn_norm[i], nb, d, eps,
+      TCALL(KC_OT, 0, 0, rms_fwd_parts(c, xr, np, c->h_dyn[i], c->dyn_norm[i], nb, d, eps,
                                             c->xn_d[i], c->r_dyn[i], st));
       xr = c->h_dyn[i];
     } else {
       // block s: the residual stream comes from the hoisted prefix
       HIPCHK(c, hipStreamWaitEvent(st, c->ev_upd[i], 0));
       for (int j = 0; j < B; ++j)
-        TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, c->hres + ((size_t)j * c->max_seq + a0) * d, nullptr, 0, nullptr,
+        TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, c->hres + ((size_t)j * c->max_seq + a0) * d, (const float*)nullptr, 0, nullptr,
                                               sqf(c->h_dyn[i], j, (size_t)n * d), c->dyn_norm[i], n, d, eps,
                                               sq(c->xn_d[i], j, (size_t)n * d, es), sqf(c->r_dyn[i], j, n), st));
       xr = c->h_dyn[i];
@@ -558,7 +569,7 @@ ttt_status loop_forward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     RUN(gemm_resid(c, KC_GL, c->hm_d[i], Fd, c->dw3[i], Fd, c->sr_round ? nullptr : c->dw3_lo[i], n, d, Fd, &np, st,
                    b3));
   }
-  TCALL(KC_OT, 0, 0, rmsnorm_fwd_fused(c->dt, xr, c->part, np, nullptr, c->h_f, c->final_norm, nb, d, eps, c->xn,
+  TCALL(KC_OT, 0, 0, rms_fwd_parts(c, xr, np, c->h_f, c->final_norm, nb, d, eps, c->xn,
                                         c->r_f, st));
   {
     // bf16: the epilogue also leaves each row's per-64-column (max, sum exp)
@@ -842,6 +853,11 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   {
     const char* wr = getenv("TTT_WEIGHT_ROUNDING");
     c->sr_round = c->dt == DT::BF16 && !(wr && strcmp(wr, "nearest") == 0);
+    // the forward's residual products leave their split-K partial sums in
+    // bf16 (as the backward's data gradients do), fp32 with
+    // TTT_FWD_PARTIALS=f32
+    const char* fp = getenv("TTT_FWD_PARTIALS");
+    c->fwd_parts_bf16 = c->dt == DT::BF16 && !(fp && strcmp(fp, "f32") == 0);
   }
   const size_t es = c->es;
   const int d = c->d, L = c->L, nd = c->nd, B = c->B, b = c->b * c->B;  // b: loop rows (B mini-batches)

@@ -94,6 +94,9 @@ hipError_t embed_gather(DT dt, const int32_t* tok, int n, const void* embed, int
 // (either may be null) receive x; y = RMSNorm(x) * g, r = 1 / rms.
 hipError_t rmsnorm_fwd_fused(DT dt, const float* x_in, const float* parts, int nsplit, float* x_out, float* save,
                              const float* g, int n, int d, float eps, void* y, float* r, hipStream_t st);
+// ... with the partial sums stored in bf16
+hipError_t rmsnorm_fwd_fused(DT dt, const float* x_in, const __bf16* parts, int nsplit, float* x_out, float* save,
+                             const float* g, int n, int d, float eps, void* y, float* r, hipStream_t st);
 hipError_t rmsnorm_fwd(DT dt, const float* x, const float* g, int n, int d, float eps, void* y,
                        float* r, hipStream_t st);
 // dh[t] += rmsnorm_bwd(dy[t]) where dy = sum over nsplit partials of
