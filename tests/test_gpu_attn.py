@@ -107,3 +107,45 @@ def test_attention_fwd_bwd(case):
         for name, got, want in (("dq", dq, dq_ref), ("dk", dk, dk_ref), ("dv", dv, dv_ref)):
             e = rel(got.cpu(), want)
             assert e < 2e-2, (variant, name, e)
+
+
+@pytest.mark.parametrize("pos0", [0, 16384])
+def test_attention_fwd_long_stream_sampled_rows(pos0):
+    """16384 queries of 24 heads (8 key heads, dh 128) over a window of 8192
+    in a 32768-slot store, the prefill's slab shape, from position 0 (the
+    window ramps up) and from 16384 (full windows): sampled query rows of
+    every forward variant against float64 attention over each row's own
+    visible keys."""
+    n, H, Hk, dh, cap, window = 16384, 24, 8, 128, 32768, 8192
+    g = torch.Generator().manual_seed(23)
+    q = torch.randn(n, H, dh, generator=g).to(bf)
+    Kr = (torch.randn(Hk, cap, dh, generator=g) * 0.5).to(bf)
+    Vr = torch.randn(Hk, cap, dh, generator=g).to(bf)
+    sl = torch.arange(cap)
+    perm = (sl & ~15) | (sl & 3) | ((sl & 4) << 1) | ((sl & 8) >> 1)
+    VT = torch.empty(Hk, dh, cap, dtype=bf)
+    VT[:, :, perm] = Vr.transpose(1, 2)
+    rows = torch.tensor([0, 1, 31, 32, 63, 64, 127, 255, 256, 1000, 4095, 8190, 8191, 8192, 8200, 12345, 16320,
+                         16383])
+    grp = H // Hk
+    ref = torch.empty(len(rows), H, dh, dtype=torch.float64)
+    for r_i, r in enumerate(rows.tolist()):
+        p = pos0 + r
+        kp = torch.arange(max(0, p - window + 1), p + 1)
+        kk = Kr[:, kp % cap].double().repeat_interleave(grp, 0)     # [H, P, dh]
+        vv = Vr[:, kp % cap].double().repeat_interleave(grp, 0)
+        s = torch.einsum("hd,hpd->hp", q[r].double(), kk) / math.sqrt(dh)
+        ref[r_i] = torch.einsum("hp,hpd->hd", torch.softmax(s, -1), vv)
+    qd, Kd, Vd, VTd = q.to(dev), Kr.to(dev), Vr.to(dev), VT.contiguous().to(dev)
+    for variant, ksplit in ((1, 1), (2, 1), (3, 1), (4, 1), (2, 4)):
+        o = torch.full((n, H, dh), float("nan"), dtype=bf, device=dev)
+        lse = torch.empty(H, n, device=dev)
+        ws = tla.attn_fwd_workspace(n, H, dh, window, ksplit)
+        work = torch.empty(max(ws // 4, 1), device=dev)
+        tla.attn_fwd(qd, Kd, Vd, o, lse, n, H, Hk, dh, cap, window, pos0, vt=VTd, variant=variant, ksplit=ksplit,
+                     work=work)
+        got = o[rows.to(dev)].cpu()
+        e = rel(got, ref)
+        say(f"  long stream pos0={pos0} variant {variant} ksplit {ksplit}: sampled rows rel err {e:.3e}")
+        assert torch.isfinite(o).all()
+        assert e < 1e-2, (variant, ksplit, e)
