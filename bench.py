@@ -469,14 +469,14 @@ def pmc_summary(c, T, dirs, workload):
 
 def decode_bytes(c: dict, p: int) -> float:
     """HBM bytes one decode step must read at position p: every weight once
-    (static bf16, dynamic fp32 masters, lm_head) and the window's keys and
-    values in every block."""
+    (static weights and the dynamic MLPs' working copy in the storage dtype,
+    lm_head) and the window's keys and values in every block."""
     L, d, H, Hk, dh = c["n_layers"], c["d_model"], c["n_heads"], c["n_kv_heads"], c["head_dim"]
     F, Fd, V, k = c["ffn_hidden"], c["dyn_ffn_hidden"], c["vocab"], c["window"]
     Ld = c["n_dynamic"] or L - (3 * L) // 4
     es = 2 if c["dtype"] == "bf16" else 4
     static = L * ((H + 2 * Hk) * dh * d + d * H * dh + 3 * F * d) * es + V * d * es
-    dyn = Ld * 3 * Fd * d * 4
+    dyn = Ld * 3 * Fd * d * es
     kv = L * min(p + 1, k) * Hk * dh * 2 * es
     return float(static + dyn + kv)
 

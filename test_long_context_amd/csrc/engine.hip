@@ -768,10 +768,16 @@ ttt_status decode_blocks(ttt_ctx* c, hipStream_t st) {
     HIPCHK(c, gemv(c->dt, c->w12[l], h, c->mlp_norm[l], eps, 2 * c->F, d, GvEpi::SWIGLU, hm, st));
     HIPCHK(c, gemv(c->dt, c->w3[l], hm, nullptr, 0.f, d, c->F, GvEpi::ADD_F32, h, st));
     if (l >= c->s) {
-      // the dynamic MLP under the current fast weights (fp32 masters)
+      // the dynamic MLP under the current fast weights: the stochastically
+      // rounded bf16 working copy the prefill's forward uses (half the bytes
+      // of the masters), or the fp32 masters when the working copy is the
+      // two-term form (its high term alone would round updates away)
       const int i = l - c->s;
-      HIPCHK(c, gemv(DT::F32, c->m12[i], h, c->dyn_norm[i], eps, 2 * c->Fd, d, GvEpi::SWIGLU, hm, st));
-      HIPCHK(c, gemv(DT::F32, c->m3[i], hm, nullptr, 0.f, d, c->Fd, GvEpi::ADD_F32, h, st));
+      const bool wc = c->sr_round;
+      HIPCHK(c, gemv(wc ? DT::BF16 : DT::F32, wc ? c->dw12[i] : c->m12[i], h, c->dyn_norm[i], eps, 2 * c->Fd, d,
+                     GvEpi::SWIGLU, hm, st));
+      HIPCHK(c, gemv(wc ? DT::BF16 : DT::F32, wc ? c->dw3[i] : c->m3[i], hm, nullptr, 0.f, d, c->Fd,
+                     GvEpi::ADD_F32, h, st));
     }
   }
   return TTT_OK;
