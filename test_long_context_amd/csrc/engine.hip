@@ -131,6 +131,7 @@ struct ttt_ctx {
   std::vector<void*> dh12d;                  // [b, 2 Fd] SwiGLU pre-activation gradients per dynamic block
   bool fused_update = false;                 // bf16: both update products in one dw_sgd launch
   bool upd_main = false;                     // update products on the caller's stream instead of side streams
+  bool upd_at_attn = false;                  // launch a block's update when its attention backward starts
   bool sr_round = false;                     // bf16: one stochastically rounded working copy, no low term
   bool fwd_parts_bf16 = false;               // bf16: the forward's split-K partial sums stored in bf16
   int upd_grid = 0;                          // its workgroups (0: two per CU)
@@ -610,6 +611,71 @@ uint32_t sr_seed(int64_t step, int block, int which) {
   return (uint32_t)((((uint64_t)step * 64 + (uint64_t)block) * 2 + (uint64_t)which) * 0x9E3779B1ull) | 1u;
 }
 
+// The update products of dynamic block i (dW3 = dY^T Hmid and dW12 = dH12^T U,
+// with W -= alpha dW in the epilogue) on the side streams, once the main
+// stream has queued everything that reads the block's old weights.
+ttt_status launch_update(ttt_ctx* c, int i, int64_t a0, int n, hipStream_t st) {
+  const int d = c->d, Fd = c->Fd, B = c->B;
+  const float lr = c->cfg.alpha;
+  const double upd_bytes = 8.0 + (c->dt == DT::F32 ? 0.0 : (double)c->es);  // master r/w + working copy
+  void* gt = c->ghd_t[i];
+  // dW3 = dY^T Hmid and dW12 = dH12^T U, with W -= alpha dW in the epilogue,
+  // on the side stream once this block's products with the old W are queued
+  hipStream_t us1 = c->upd_main ? st : c->side, us2 = c->upd_main ? st : c->side2;
+  HIPCHK(c, hipEventRecord(c->ev_dyn[i], st));
+  HIPCHK(c, hipStreamWaitEvent(us1, c->ev_dyn[i], 0));
+  if (c->dt == DT::BF16 && c->fused_update) {
+    // both products in one persistent launch (shapes checked at init;
+    // single-sequence contexts only)
+    hipStream_t st = us1;
+    const DwUpdate u[2] = {
+        DwUpdate{c->dh12d[i], 2L * Fd, c->xn_d[i], d, c->m12[i], c->dw12[i], c->dw12_lo[i], d, 2 * Fd, d},
+        DwUpdate{gt, d, c->hm_d[i], Fd, c->m3[i], c->dw3[i], c->dw3_lo[i], Fd, d, Fd}};
+    TCALL(KC_SGD, gfl(2 * Fd, d, n) + gfl(d, Fd, n), 3.0 * Fd * d * upd_bytes,
+          dw_sgd(u, 2, n, lr, c->upd_grid, st));
+    HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
+  } else {
+    HIPCHK(c, hipStreamWaitEvent(us2, c->ev_dyn[i], 0));
+    {
+      hipStream_t st = us2;
+      GemmArgs g = ga(gt, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
+      g.C2 = c->dw3[i];
+      g.C3 = c->sr_round ? nullptr : c->dw3_lo[i];
+      g.seed = c->sr_round ? sr_seed(a0 / c->b, i, 0) : 0u;
+      g.scale = lr;
+      Bat bt;
+      bt.n = B;
+      bt.sA = (long)n * d;
+      bt.sB = (long)n * Fd;
+      bt.sC = bt.sC2 = (long)d * Fd;
+      set_batch(g, bt);
+      TCALL(KC_SGD, gfl(d, Fd, n) * B, (double)d * Fd * upd_bytes * B,
+            gemm(c->dt, false, false, Epi::SGD, g, st));
+      HIPCHK(c, hipEventRecord(c->ev_w3, st));
+    }
+    {
+      hipStream_t st = us1;
+      GemmArgs g2 = ga(c->dh12d[i], 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
+      g2.C2 = c->dw12[i];
+      g2.C3 = c->sr_round ? nullptr : c->dw12_lo[i];
+      g2.seed = c->sr_round ? sr_seed(a0 / c->b, i, 1) : 0u;
+      g2.scale = lr;
+      Bat bt;
+      bt.n = B;
+      bt.sA = (long)n * 2 * Fd;
+      bt.sB = (long)n * d;
+      bt.sC = bt.sC2 = 2L * Fd * d;
+      set_batch(g2, bt);
+      TCALL(KC_SGD, gfl(2 * Fd, d, n) * B, 2.0 * Fd * d * upd_bytes * B,
+            gemm(c->dt, false, false, Epi::SGD, g2, st));
+      // the block's update is done once both products are
+      HIPCHK(c, hipStreamWaitEvent(st, c->ev_w3, 0));
+      HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
+    }
+  }
+  return TTT_OK;
+}
+
 ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
   const int d = c->d, H = c->H, Hk = c->Hk, dh = c->dh, QKV = c->QKV, s = c->s, F = c->F, Fd = c->Fd;
   const int B = c->B, nb = B * n;
@@ -644,60 +710,11 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       bt.sB = 2L * Fd * d;
       RUN(gemm_nn_split(c, KC_GL, c->dh12d[i], 2 * Fd, c->dw12[i], d, n, d, 2 * Fd, c->part, &ns, st, bt));
     }
-    // dW3 = dY^T Hmid and dW12 = dH12^T U, with W -= alpha dW in the epilogue,
-    // on the side stream once this block's products with the old W are queued
-    hipStream_t us1 = c->upd_main ? st : c->side, us2 = c->upd_main ? st : c->side2;
-    HIPCHK(c, hipEventRecord(c->ev_dyn[i], st));
-    HIPCHK(c, hipStreamWaitEvent(us1, c->ev_dyn[i], 0));
-    if (c->dt == DT::BF16 && c->fused_update) {
-      // both products in one persistent launch (shapes checked at init;
-      // single-sequence contexts only)
-      hipStream_t st = us1;
-      const DwUpdate u[2] = {
-          DwUpdate{c->dh12d[i], 2L * Fd, c->xn_d[i], d, c->m12[i], c->dw12[i], c->dw12_lo[i], d, 2 * Fd, d},
-          DwUpdate{gt, d, c->hm_d[i], Fd, c->m3[i], c->dw3[i], c->dw3_lo[i], Fd, d, Fd}};
-      TCALL(KC_SGD, gfl(2 * Fd, d, n) + gfl(d, Fd, n), 3.0 * Fd * d * upd_bytes,
-            dw_sgd(u, 2, n, lr, c->upd_grid, st));
-      HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
-    } else {
-      HIPCHK(c, hipStreamWaitEvent(us2, c->ev_dyn[i], 0));
-      {
-        hipStream_t st = us2;
-        GemmArgs g = ga(gt, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
-        g.C2 = c->dw3[i];
-        g.C3 = c->sr_round ? nullptr : c->dw3_lo[i];
-        g.seed = c->sr_round ? sr_seed(a0 / c->b, i, 0) : 0u;
-        g.scale = lr;
-        Bat bt;
-        bt.n = B;
-        bt.sA = (long)n * d;
-        bt.sB = (long)n * Fd;
-        bt.sC = bt.sC2 = (long)d * Fd;
-        set_batch(g, bt);
-        TCALL(KC_SGD, gfl(d, Fd, n) * B, (double)d * Fd * upd_bytes * B,
-              gemm(c->dt, false, false, Epi::SGD, g, st));
-        HIPCHK(c, hipEventRecord(c->ev_w3, st));
-      }
-      {
-        hipStream_t st = us1;
-        GemmArgs g2 = ga(c->dh12d[i], 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
-        g2.C2 = c->dw12[i];
-        g2.C3 = c->sr_round ? nullptr : c->dw12_lo[i];
-        g2.seed = c->sr_round ? sr_seed(a0 / c->b, i, 1) : 0u;
-        g2.scale = lr;
-        Bat bt;
-        bt.n = B;
-        bt.sA = (long)n * 2 * Fd;
-        bt.sB = (long)n * d;
-        bt.sC = bt.sC2 = 2L * Fd * d;
-        set_batch(g2, bt);
-        TCALL(KC_SGD, gfl(2 * Fd, d, n) * B, 2.0 * Fd * d * upd_bytes * B,
-              gemm(c->dt, false, false, Epi::SGD, g2, st));
-        // the block's update is done once both products are
-        HIPCHK(c, hipStreamWaitEvent(st, c->ev_w3, 0));
-        HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
-      }
-    }
+    // the update of this block once its attention backward starts, so that
+    // it runs beside those kernels rather than the data-gradient products
+    // (2339-2343 against 2355-2357 ms per 3B step on one box; block s has no
+    // attention backward in the loop; TTT_UPDATE_AT=now launches here)
+    if (!c->upd_at_attn || l == s) RUN(launch_update(c, i, a0, n, st));
     if (l == s) break;
     TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], nb, d, c->gh, c->gh_t, 1, st));
     // static MLP
@@ -712,6 +729,7 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     {
       TCALL(KC_GL, gfl(nb, H * dh, d), 0,
             gemm(c->dt, true, false, Epi::STORE, ga(c->gh_t, d, c->wo[l], (long)H * dh, nb, H * dh, d, c->dO, (long)H * dh), st));
+      if (c->upd_at_attn) RUN(launch_update(c, i, a0, n, st));
       for (int j = 0; j < B; ++j) {
         const size_t qe = (size_t)n * H * dh;
         void* dO = sq(c->dO, j, qe, es);
@@ -1027,6 +1045,8 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   {
     const char* uk = getenv("TTT_UPDATE_KERNEL");
     c->fused_update = c->dt == DT::BF16 && B == 1 && !c->sr_round && uk && strcmp(uk, "fused") == 0;
+    const char* ua = getenv("TTT_UPDATE_AT");
+    c->upd_at_attn = !(ua && strcmp(ua, "now") == 0);
     const char* us = getenv("TTT_UPDATE_STREAM");
     c->upd_main = us && strcmp(us, "main") == 0;
     const char* ug = getenv("TTT_UPDATE_GRID");
