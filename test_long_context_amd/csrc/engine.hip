@@ -132,6 +132,8 @@ struct ttt_ctx {
   bool fused_update = false;                 // bf16: both update products in one dw_sgd launch
   bool upd_main = false;                     // update products on the caller's stream instead of side streams
   bool upd_at_attn = false;                  // launch a block's update when its attention backward starts
+  bool upd_split = false;                    // ... its dW3 product at once and only dW12 then
+  bool upd_after_dq = false;                 // ... after the query-side attention backward instead
   bool sr_round = false;                     // bf16: one stochastically rounded working copy, no low term
   bool fwd_parts_bf16 = false;               // bf16: the forward's split-K partial sums stored in bf16
   int upd_grid = 0;                          // its workgroups (0: two per CU)
@@ -614,7 +616,9 @@ uint32_t sr_seed(int64_t step, int block, int which) {
 // The update products of dynamic block i (dW3 = dY^T Hmid and dW12 = dH12^T U,
 // with W -= alpha dW in the epilogue) on the side streams, once the main
 // stream has queued everything that reads the block's old weights.
-ttt_status launch_update(ttt_ctx* c, int i, int64_t a0, int n, hipStream_t st) {
+// part: 3 = both products, 1 = dW3 only, 2 = dW12 only (dW12 completes the
+// block's update event, so it must come last).
+ttt_status launch_update(ttt_ctx* c, int i, int64_t a0, int n, hipStream_t st, int part = 3) {
   const int d = c->d, Fd = c->Fd, B = c->B;
   const float lr = c->cfg.alpha;
   const double upd_bytes = 8.0 + (c->dt == DT::F32 ? 0.0 : (double)c->es);  // master r/w + working copy
@@ -625,6 +629,7 @@ ttt_status launch_update(ttt_ctx* c, int i, int64_t a0, int n, hipStream_t st) {
   HIPCHK(c, hipEventRecord(c->ev_dyn[i], st));
   HIPCHK(c, hipStreamWaitEvent(us1, c->ev_dyn[i], 0));
   if (c->dt == DT::BF16 && c->fused_update) {
+    if (!(part & 2)) return TTT_OK;
     // both products in one persistent launch (shapes checked at init;
     // single-sequence contexts only)
     hipStream_t st = us1;
@@ -636,7 +641,7 @@ ttt_status launch_update(ttt_ctx* c, int i, int64_t a0, int n, hipStream_t st) {
     HIPCHK(c, hipEventRecord(c->ev_upd[i], st));
   } else {
     HIPCHK(c, hipStreamWaitEvent(us2, c->ev_dyn[i], 0));
-    {
+    if (part & 1) {
       hipStream_t st = us2;
       GemmArgs g = ga(gt, d, c->hm_d[i], Fd, d, Fd, n, c->m3[i], Fd);
       g.C2 = c->dw3[i];
@@ -653,7 +658,7 @@ ttt_status launch_update(ttt_ctx* c, int i, int64_t a0, int n, hipStream_t st) {
             gemm(c->dt, false, false, Epi::SGD, g, st));
       HIPCHK(c, hipEventRecord(c->ev_w3, st));
     }
-    {
+    if (part & 2) {
       hipStream_t st = us1;
       GemmArgs g2 = ga(c->dh12d[i], 2 * Fd, c->xn_d[i], d, 2 * Fd, d, n, c->m12[i], d);
       g2.C2 = c->dw12[i];
@@ -715,6 +720,7 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     // (2339-2343 against 2355-2357 ms per 3B step on one box; block s has no
     // attention backward in the loop; TTT_UPDATE_AT=now launches here)
     if (!c->upd_at_attn || l == s) RUN(launch_update(c, i, a0, n, st));
+    else if (c->upd_split) RUN(launch_update(c, i, a0, n, st, 1));
     if (l == s) break;
     TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_dyn[i], c->dyn_norm[i], c->r_dyn[i], nb, d, c->gh, c->gh_t, 1, st));
     // static MLP
@@ -729,7 +735,11 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
     {
       TCALL(KC_GL, gfl(nb, H * dh, d), 0,
             gemm(c->dt, true, false, Epi::STORE, ga(c->gh_t, d, c->wo[l], (long)H * dh, nb, H * dh, d, c->dO, (long)H * dh), st));
-      if (c->upd_at_attn) RUN(launch_update(c, i, a0, n, st));
+      bool upd_done = false;
+      if (c->upd_at_attn && !c->upd_after_dq) {
+        RUN(launch_update(c, i, a0, n, st, c->upd_split ? 2 : 3));
+        upd_done = true;
+      }
       for (int j = 0; j < B; ++j) {
         const size_t qe = (size_t)n * H * dh;
         void* dO = sq(c->dO, j, qe, es);
@@ -747,6 +757,10 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
           qp = attn_bwd2_dq_parts(a);
           kp = attn_bwd2_kv_parts(a);
           TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq2(c->dt, a, st));
+        if (c->upd_at_attn && !upd_done && j == B - 1) {
+          RUN(launch_update(c, i, a0, n, st, c->upd_split ? 2 : 3));
+          upd_done = true;
+        }
           TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv2(c->dt, a, st));
         } else {
           TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq(c->dt, a, st));
@@ -755,6 +769,7 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, a.dq, qp, a.dk, a.dv, kp, n, H, Hk, dh, a0, c->rope,
                                          sq(c->dqkv, j, (size_t)n * QKV, es), st));
       }
+      if (c->upd_at_attn && !upd_done) RUN(launch_update(c, i, a0, n, st, c->upd_split ? 2 : 3));
       RUN(gemm_nn_split(c, KC_GL, c->dqkv, QKV, c->wqkv[l], d, nb, d, QKV, c->part, &ns, st));
       TCALL(KC_OT, 0, 0, rmsnorm_bwd(c->dt, c->part, c->dt == DT::BF16, ns, c->h_att[i], c->attn_norm[l], c->r_att[i], nb, d, c->gh, c->ghd_t[i - 1], 1, st));
     }
@@ -1047,6 +1062,8 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     c->fused_update = c->dt == DT::BF16 && B == 1 && !c->sr_round && uk && strcmp(uk, "fused") == 0;
     const char* ua = getenv("TTT_UPDATE_AT");
     c->upd_at_attn = !(ua && strcmp(ua, "now") == 0);
+    c->upd_split = ua && strcmp(ua, "split") == 0;
+    c->upd_after_dq = ua && strcmp(ua, "dq") == 0;
     const char* us = getenv("TTT_UPDATE_STREAM");
     c->upd_main = us && strcmp(us, "main") == 0;
     const char* ug = getenv("TTT_UPDATE_GRID");
