@@ -55,7 +55,7 @@ TIMED_CLASSES = (ROOF_CLASS, "ce") + ATTN_CLASSES
 ROOF_SOURCES = ("test_long_context_amd/csrc/attn2.hip", "test_long_context_amd/csrc/common.hpp")
 UPD_SOURCES = ("test_long_context_amd/csrc/gemm_impl.hpp", "test_long_context_amd/csrc/gemm_tn.hip",
                "test_long_context_amd/csrc/gemm.hip", "test_long_context_amd/csrc/common.hpp",
-               "test_long_context_amd/csrc/kernels.hpp")
+               "test_long_context_amd/csrc/gemm_args.hpp")
 
 # HBM traffic of the update products (the roofline kernel) from rocprofv3
 # --pmc FETCH_SIZE / WRITE_SIZE of --update-replay, scaled by the
