@@ -262,6 +262,34 @@ __global__ void __launch_bounds__(256) mixer_prologue_kernel(const float* __rest
 // element by element by one workgroup and stays in place.
 typedef short e2_shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) e2_shortx4* e2_lds_s4_t;
+typedef __bf16 e2_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float e2_floatx2 __attribute__((ext_vector_type(2)));
+
+// raw buffer resource over nbytes from p (loads beyond it return 0); p and
+// nbytes are the same in every lane and are moved to scalar registers here
+// (a descriptor the compiler takes for divergent costs a loop per load)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t e2_rsrc(const void* p, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* q = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)__builtin_amdgcn_readfirstlane(nbytes), 0x00020000);
+}
+
+// x = hi + lo in bf16, both rounded to nearest even, two values per
+// conversion: hi = RNE(x), lo = RNE(x - hi)
+__device__ __forceinline__ void e2_split(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const e2_bf16x2 h = __builtin_convertvector((e2_floatx2){x[2 * p], x[2 * p + 1]}, e2_bf16x2);
+    const uint32_t hu = __builtin_bit_cast(uint32_t, h);
+    const float h0 = __builtin_bit_cast(float, hu << 16), h1 = __builtin_bit_cast(float, hu & 0xffff0000u);
+    const e2_bf16x2 l = __builtin_convertvector((e2_floatx2){x[2 * p] - h0, x[2 * p + 1] - h1}, e2_bf16x2);
+    hi[2 * p] = h[0];
+    hi[2 * p + 1] = h[1];
+    lo[2 * p] = l[0];
+    lo[2 * p + 1] = l[1];
+  }
+}
 
 constexpr int E2_NW = 8;  // waves per chunk workgroup
 
@@ -305,27 +333,29 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   }
   const int ib = bid >> 1, jh = bid & 1;
   const int i0 = ib * 16, j0 = jh * JH;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const bf16* Kh = K + ((int64_t)h * T + a0) * D;
   const bf16* Vh = Vv + ((int64_t)h * T + a0) * D;
   const float* KWh = KW + (int64_t)h * T + a0;
   const float* KMh = KM + (int64_t)h * T + a0;
   const float* W0 = Win + (int64_t)h * D * D;
+  // lane parts of the byte offsets within a block: a K block is BT whole
+  // rows, so vector q of lane l is bytes 16 (l + 64 q) of it; v, K^W and
+  // K^M of token 4 g of the block (column i0 + c of v)
+  const uint32_t ko = lane * 16, vo = (4 * g * D + i0 + c) * 2, so = 4 * g * 4;
 
-  Frag8<bf16> wh[KS], wl[KS];
+  // W0 rows i0 + c (this lane's B operand of e_t), requested first; the
+  // first block's operands and the state elements of the final update are
+  // requested before the W0 terms are formed, so the latencies overlap
+  floatx4 w4[KS][2];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const floatx4* src = (const floatx4*)(W0 + (i0 + c) * D + 32 * s + 8 * g);
-    const floatx4 w4[2] = {src[0], src[1]};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float w = w4[e >> 2][e & 3];
-      const bf16 hi = (bf16)w;
-      wh[s].v[e] = hi;
-      wl[s].v[e] = (bf16)(w - (float)hi);
-    }
+    w4[s][0] = src[0];
+    w4[s][1] = src[1];
   }
+  Frag8<bf16> wh[KS], wl[KS];  // formed below, once the other loads are out
   floatx4 dw[JT], dm[JT];
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) dw[jt] = dm[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -340,24 +370,33 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   // hence their share of the products (the clamped rows are finite).
   struct Blk {
     bf16x8 k[NV];
-    bf16 v[2][4];
+    unsigned short v[2][4];
     float kw[2][4], km[2][4];
   };
+  // Each block is read through buffer resources that start at the block
+  // and cover only its tokens inside the chunk (none for blocks past it), so
+  // tokens past the chunk -- only the sequence's last chunk has them, and
+  // they lie past T -- read as k = v = 0 and K^W = K^M = 0 without touching
+  // memory: their x is exactly 0 and they add nothing to the products. The
+  // loads are therefore unconditional (a skipped prefetch would make the
+  // wait for the current block's operands cover the next block's loads).
   auto load = [&](Blk& o, int blk) {
+    const int nt = max(0, min(BT, n - blk * BT));
+    const int64_t t0 = (int64_t)blk * BT;
+    const __amdgpu_buffer_rsrc_t rk = e2_rsrc(Kh + t0 * D, (uint32_t)nt * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = e2_rsrc(Vh + t0 * D, (uint32_t)nt * D * 2);
+    const __amdgpu_buffer_rsrc_t rkw = e2_rsrc(KWh + t0, (uint32_t)nt * 4);
+    const __amdgpu_buffer_rsrc_t rkm = e2_rsrc(KMh + t0, (uint32_t)nt * 4);
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const int vi = lane + 64 * q, row = vi / (D / 8), col = (vi % (D / 8)) * 8;
-      const int t = min(blk * BT + row, n - 1);
-      o.k[q] = *(const bf16x8*)(Kh + (int64_t)t * D + col);
-    }
+    for (int q = 0; q < NV; ++q)
+      o.k[q] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 1024 * q, 0, 0));
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = min(blk * BT + 16 * tile + 4 * g + e, n - 1);
-        o.v[tile][e] = Vh[(int64_t)t * D + i0 + c];
-        o.kw[tile][e] = LACT ? 0.f : KWh[t];
-        o.km[tile][e] = KMh[t];
+        o.v[tile][e] = __builtin_amdgcn_raw_buffer_load_b16(rv, vo + (16 * tile + e) * D * 2, 0, 0);
+        o.kw[tile][e] = LACT ? 0.f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkw, so + 4 * (16 * tile + e), 0, 0));
+        o.km[tile][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkm, so + 4 * (16 * tile + e), 0, 0));
       }
   };
   // operands run one block ahead of the products (two waves per SIMD hide
@@ -370,7 +409,7 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
       const int vi = lane + 64 * q, row = vi / (D / 8), col = (vi % (D / 8)) * 8;
       *(bf16x8*)(Ks + row * KP + col) = cur.k[q];
     }
-    if (blk + NW < nb) load(nxt, blk + NW);
+    load(nxt, blk + NW);
 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -405,20 +444,18 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
         if (tok < n) out[(a0 + tok) * HD + (int64_t)h * D + i0 + c] = ot[e];
       }
     }
-    Frag8<bf16> xwh, xwl, xmh, xml;
+    float xw[8], xm[8];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bool ok = blk * BT + 16 * tile + 4 * g + e < n;
-        const float ee = et[tile][e] - (float)cur.v[tile][e];
-        const float xw = ok ? cur.kw[tile][e] * ee : 0.f, xm = ok ? cur.km[tile][e] * ee : 0.f;
-        const bf16 hw = (bf16)xw, hm = (bf16)xm;
-        xwh.v[4 * tile + e] = hw;
-        xwl.v[4 * tile + e] = (bf16)(xw - (float)hw);
-        xmh.v[4 * tile + e] = hm;
-        xml.v[4 * tile + e] = (bf16)(xm - (float)hm);
+        const float ee = et[tile][e] - __builtin_bit_cast(float, (uint32_t)cur.v[tile][e] << 16);
+        xw[4 * tile + e] = cur.kw[tile][e] * ee;
+        xm[4 * tile + e] = cur.km[tile][e] * ee;
       }
+    Frag8<bf16> xwh, xwl, xmh, xml;
+    e2_split(xw, xwh.v, xwl.v);
+    e2_split(xm, xmh.v, xml.v);
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) {
       const bf16* p = Ks + (4 * g + (c >> 2)) * KP + j0 + 16 * jt + 4 * (c & 3);
@@ -436,7 +473,29 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
     }
   };
   Blk b0, b1;
-  if (wid < nb) load(b0, wid);
+  load(b0, wid);
+  // the state elements this thread updates at the end: (i, j) = (e / JH, e % JH)
+  constexpr int EPT = 16 * JH / (NW * 64);
+  static_assert(EPT * NW * 64 == 16 * JH, "the final update gives each thread the same number of elements");
+  float* Wo = Wout + (int64_t)h * D * D;
+  float* Mh = M + (int64_t)h * D * D;
+  float w0e[EPT], m0e[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = threadIdx.x + k * NW * 64;
+    const int64_t idx = (int64_t)(i0 + e / JH) * D + j0 + e % JH;
+    w0e[k] = W0[idx];
+    m0e[k] = Mh[idx];
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float w = w4[s][e >> 2][e & 3];
+      const bf16 hi = (bf16)w;
+      wh[s].v[e] = hi;
+      wl[s].v[e] = (bf16)(w - (float)hi);
+    }
   for (int blk = wid; blk < nb; blk += 2 * NW) {
     step(b0, b1, blk);
     if (blk + NW < nb) step(b1, b0, blk + NW);
@@ -455,9 +514,9 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   __syncthreads();
   const float* cf = coef + ((int64_t)h * nch + r) * 4;
   const float c0 = cf[0], c1 = cf[1], c2 = cf[2];
-  float* Wo = Wout + (int64_t)h * D * D;
-  float* Mh = M + (int64_t)h * D * D;
-  for (int e = threadIdx.x; e < 16 * JH; e += NW * 64) {
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = threadIdx.x + k * NW * 64;
     const int i = e / JH, j = e % JH;
     float sw = 0.f, sm = 0.f;
 #pragma unroll
@@ -466,9 +525,8 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
       sm += red[((w * 2 + 1) * 16 + i) * JH + j];
     }
     const int64_t idx = (int64_t)(i0 + i) * D + j0 + j;
-    const float w0 = W0[idx], m0 = Mh[idx];
-    Wo[idx] = c0 * w0 + c1 * m0 + sw;
-    Mh[idx] = c2 * m0 + sm;
+    Wo[idx] = c0 * w0e[k] + c1 * m0e[k] + sw;
+    Mh[idx] = c2 * m0e[k] + sm;
   }
 }
 
