@@ -680,12 +680,24 @@ __global__ void __launch_bounds__(256) decode_attn_mfma_kernel(const float* q, c
   const int64_t lo = p - window + 1 > 0 ? p - window + 1 : 0;
   const int64_t b0 = lo >> 5, b1 = p >> 5;
 
+  // query rows as 16-byte loads from a valid row (lanes past the group read
+  // its last row and zero it), all issued before any is used: a load under
+  // the lane condition becomes a branch with its own wait per element
   Frag8<bf16> qf[KS];
+  {
+    const floatx4* qr = (const floatx4*)(q + (long)(kh * G + min(c, G - 1)) * DH + 8 * g);
+    floatx4 qv[KS][2];
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+      qv[s][0] = qr[8 * s];
+      qv[s][1] = qr[8 * s + 1];
+    }
+    const float qs = c < G ? scale2 : 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      qf[s].v[e] = (bf16)(c < G ? q[(long)(kh * G + c) * DH + 32 * s + 8 * g + e] * scale2 : 0.f);
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s].v[e] = (bf16)(qv[s][e >> 2][e & 3] * qs);
+  }
   float m = -INFINITY, l = 0.f;
   floatx4 o[MT];
 #pragma unroll
@@ -814,6 +826,7 @@ hipError_t decode_attn(DT dt, const float* q, const void* kstore, const void* vs
                        hipStream_t st) {
   const int nsplit = decode_attn_splits(dt, H, Hk, dh, window, vtstore != nullptr);
   if (decode_mfma_ok(dt, H, Hk, dh, vtstore != nullptr)) {
+    if ((uintptr_t)q & 15) return hipErrorInvalidValue;  // query rows are read as 16-byte vectors
     const dim3 grid(Hk, nsplit);
     const float sc2 = 1.f / sqrtf((float)dh) * 1.4426950408889634f;
     if (dh == 128)
