@@ -72,23 +72,50 @@ __device__ __forceinline__ float4 f4add(float4 a, float4 b) { return make_float4
 // (one memory round trip per four partials, not one per load).
 // 4 consecutive partial values at vector index v (float or bf16 storage)
 __device__ __forceinline__ float4 ld_part4(const float* p, int v) { return ((const float4*)p)[v]; }
+// raw 4-element loads and their conversion, for code that loads several
+// parts before it uses any
+__device__ __forceinline__ float4 ld_raw4(const float* p, int v) { return ((const float4*)p)[v]; }
+__device__ __forceinline__ bf16x4 ld_raw4(const bf16* p, int v) { return ((const bf16x4*)p)[v]; }
+__device__ __forceinline__ float4 raw_f4(float4 h) { return h; }
+__device__ __forceinline__ float4 raw_f4(bf16x4 h) { return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]); }
 __device__ __forceinline__ float4 ld_part4(const bf16* p, int v) {
   const bf16x4 h = ((const bf16x4*)p)[v];
   return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
 }
 
+// Loads take a clamped (valid) index and are unconditional: under a lane
+// condition each becomes a branch with its own wait for memory; only the
+// arithmetic and the stores check v < nv.
 template <int NVT, typename PT = float>
 __device__ __forceinline__ void rms_add_parts(float4 (&a)[NVT], const PT* src, long stride, int np, long row,
                                               int nv) {
   int p = 0;
+  // the first group of up to four parts in straight-line code, so their
+  // loads go out together with the caller's (a loop header in between
+  // makes the caller's loads land before these are requested)
+  {
+    decltype(ld_raw4(src, 0)) t[4][NVT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < np)  // uniform
+#pragma unroll
+        for (int i = 0; i < NVT; ++i) t[u][i] = ld_raw4(src + u * stride + row, min((int)threadIdx.x + i * RB, nv - 1));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < np)
+#pragma unroll
+        for (int i = 0; i < NVT; ++i)
+          if (threadIdx.x + i * RB < nv) a[i] = f4add(a[i], raw_f4(t[u][i]));
+    p = np < 4 ? np : 4;
+  }
   for (; p + 4 <= np; p += 4) {
     float4 t[4][NVT];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int i = 0; i < NVT; ++i) {
-        const int v = threadIdx.x + i * RB;
-        if (v < nv) t[u][i] = ld_part4(src + (p + u) * stride + row, v);
+        const int v = min((int)threadIdx.x + i * RB, nv - 1);
+        t[u][i] = ld_part4(src + (p + u) * stride + row, v);
       }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -100,8 +127,8 @@ __device__ __forceinline__ void rms_add_parts(float4 (&a)[NVT], const PT* src, l
     float4 t[NVT];
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
-      const int v = threadIdx.x + i * RB;
-      if (v < nv) t[i] = ld_part4(src + p * stride + row, v);
+      const int v = min((int)threadIdx.x + i * RB, nv - 1);
+      t[i] = ld_part4(src + p * stride + row, v);
     }
 #pragma unroll
     for (int i = 0; i < NVT; ++i)
@@ -124,11 +151,9 @@ __global__ void __launch_bounds__(RB) rms_fwd_kernel(const float* x_in, const PT
   float4 xv[NVT], gv[NVT];
 #pragma unroll
   for (int i = 0; i < NVT; ++i) {
-    const int v = threadIdx.x + i * RB;
-    if (v < nv) {
-      xv[i] = ((const float4*)(x_in + t * d))[v];
-      gv[i] = ((const float4*)g)[v];
-    }
+    const int v = min((int)threadIdx.x + i * RB, nv - 1);
+    xv[i] = ((const float4*)(x_in + t * d))[v];
+    gv[i] = ((const float4*)g)[v];
   }
   rms_add_parts<NVT>(xv, parts, pstride, nsplit, t * d, nv);
   float ss = 0.f;
@@ -216,13 +241,14 @@ __global__ void __launch_bounds__(RB) rms_bwd_kernel(const PT* dy, int nsplit, l
   float4 a[NVT], gv[NVT], xv[NVT], hv[NVT];
 #pragma unroll
   for (int i = 0; i < NVT; ++i) {
-    const int v = threadIdx.x + i * RB;
-    if (v < nv) {
-      a[i] = ld_part4(dy + t * d, v);
-      gv[i] = ((const float4*)g)[v];
-      xv[i] = ((const float4*)(x + t * d))[v];
-      if (acc) hv[i] = ((const float4*)(dh + t * d))[v];
-    }
+    const int v = min((int)threadIdx.x + i * RB, nv - 1);
+    a[i] = ld_part4(dy + t * d, v);
+    gv[i] = ((const float4*)g)[v];
+    xv[i] = ((const float4*)(x + t * d))[v];
+  }
+  if (acc) {  // uniform
+#pragma unroll
+    for (int i = 0; i < NVT; ++i) hv[i] = ((const float4*)(dh + t * d))[min((int)threadIdx.x + i * RB, nv - 1)];
   }
   rms_add_parts<NVT, PT>(a, dy + sstride, sstride, nsplit - 1, t * d, nv);
   float dot = 0.f;
@@ -365,17 +391,17 @@ __global__ void __launch_bounds__(RB) rope_scatter_kernel(const T* qkv, int n, i
   uint4 vv;
 #pragma unroll
   for (int k = 0; k < ROPE_KR; ++k) {
-    const int gi = threadIdx.x + k * RB;
-    if (gi < ng) {
-      const int hh = gi / gph, j = (gi % gph) * 4;
-      x1[k] = *(const R4*)(row + hh * dh + j);
-      x2[k] = *(const R4*)(row + hh * dh + j + half);
-      c01[k] = tb[j / 2];
-      c23[k] = tb[j / 2 + 1];
-    }
+    // unconditional loads from a clamped (valid) group: a load under the
+    // lane condition becomes a branch with its own wait for memory
+    const int gi = min((int)threadIdx.x + k * RB, ng - 1);
+    const int hh = gi / gph, j = (gi % gph) * 4;
+    x1[k] = *(const R4*)(row + hh * dh + j);
+    x2[k] = *(const R4*)(row + hh * dh + j + half);
+    c01[k] = tb[j / 2];
+    c23[k] = tb[j / 2 + 1];
   }
   const bool hv = store && (int)threadIdx.x < nvv;
-  if (hv) vv = ((const uint4*)(row + (H + Hk) * dh))[threadIdx.x];
+  vv = ((const uint4*)(row + (H + Hk) * dh))[min((int)threadIdx.x, nvv - 1)];
 #pragma unroll
   for (int k = 0; k < ROPE_KR; ++k) {
     const int gi = threadIdx.x + k * RB;
@@ -419,8 +445,10 @@ __global__ void __launch_bounds__(256) vt_scatter_kernel(const T* qkv, int n, in
   uint4 r[MAXL];
 #pragma unroll
   for (int i = 0; i < MAXL; ++i) {
-    const int e = threadIdx.x + i * 256, t = e / vpr, v = e % vpr;
-    if (t < TT && t0 + t < n) r[i] = *(const uint4*)(qkv + (long)(t0 + t) * W + (H + Hk) * dh + kh * dh + d0 + v * VE);
+    // unconditional loads from a clamped (valid) token row (a load under the
+    // lane condition becomes a branch with its own wait for memory)
+    const int e = threadIdx.x + i * 256, t = min(e / vpr, TT - 1), v = e % vpr;
+    r[i] = *(const uint4*)(qkv + (long)min(t0 + t, n - 1) * W + (H + Hk) * dh + kh * dh + d0 + v * VE);
   }
 #pragma unroll
   for (int i = 0; i < MAXL; ++i) {
