@@ -173,18 +173,25 @@ __global__ void __launch_bounds__(NWV * 64, (QB == 1 && NWV == 4) ? 2 : 1) attn_
         // the maximum is taken on raw scores and the scale folded into the
         // exponent below (exp2(s sc2 - m) as one fma), sc2 > 0
         float tmax = -INFINITY;
+        // the tile-uniform mask decision as its own branch around two
+        // versions of the loop (folded into the element test, it costs every
+        // element of every tile a save / mask / branch of the lane mask)
+        if (full) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            float v = s[kb][qb][j];
-            if (!full) {
+            for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[kb][qb][j]);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
               const int kp = kt + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
-              if (!(kp <= qp && kp > qp - a.window)) v = -INFINITY;
+              const float v = (kp <= qp && kp > qp - a.window) ? s[kb][qb][j] : -INFINITY;
+              s[kb][qb][j] = v;
+              tmax = fmaxf(tmax, v);
             }
-            s[kb][qb][j] = v;
-            tmax = fmaxf(tmax, v);
-          }
+        }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc2;
         // lazy rescale: keep the reference max unless this tile exceeds it by
         // more than RESCALE (then p <= 2^RESCALE); wave-uniform branch
