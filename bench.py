@@ -71,16 +71,16 @@ UPD_TRAFFIC = {
 # --pmc-summary), keyed by (workload, T, source hash): valid only for the
 # kernel source the counters were taken on.
 TRAFFIC = {
-    ("3b", 131072, "218a5e2b4cdd808d"): dict(fetch_bytes_per_launch=56619038, write_bytes_per_launch=60356339,
+    ("3b", 131072, "756e38bf38a6e736"): dict(fetch_bytes_per_launch=58129086, write_bytes_per_launch=60356171,
                                              fetch_scale=1.9999, write_scale=1.0,
-                                             traffic_bytes_per_launch=173590785),
+                                             traffic_bytes_per_launch=176611137),
 }
 
 
 # MFMA busy of the same kernel (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
 # SIMDs x active cycles, --pmc-busy), keyed like TRAFFIC.
 MFMA_BUSY = {
-    ("3b", 131072, "218a5e2b4cdd808d"): 0.4277,
+    ("3b", 131072, "756e38bf38a6e736"): 0.4845,
 }
 
 
