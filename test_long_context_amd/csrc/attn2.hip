@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(NWV * 64, (QB == 1 && NWV == 4) ? 2 : 1) attn_
               tmax = fmaxf(tmax, v);
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc2;
+        tmax = xor32_max(tmax) * sc2;
         // lazy rescale: keep the reference max unless this tile exceeds it by
         // more than RESCALE (then p <= 2^RESCALE); wave-uniform branch
         const bool need = tmax > m_run[qb] + RESCALE;
@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(NWV * 64, (QB == 1 && NWV == 4) ? 2 : 1) attn_
             s[kb][qb][j] = p;
             rs += p;
           }
-        rs += __shfl_xor(rs, 32, 64);
+        rs = xor32_add(rs);
         l_run[qb] += rs;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
