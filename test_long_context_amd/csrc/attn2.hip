@@ -62,6 +62,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t n
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes, 0x00020000);
 }
 
+// max / sum of a lane's value and that of lane ^ 32 without LDS: the
+// half-swap of gfx950 (v_permlane32_swap) hands every lane both values, and
+// the operation is commutative, so the result equals op(v, shfl_xor(v, 32))
+// bit for bit whichever way round the halves are swapped
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float xor32_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 template <int DH, int QB, int NWV = 4>
 __global__ void __launch_bounds__(NWV * 64, (QB == 1 && NWV == 4) ? 2 : 1) attn_fwd2_kernel(AttnArgs a) {
   constexpr int BQ = NWV * 32 * QB;

@@ -35,21 +35,6 @@ template <typename T> struct Frag8;
 template <> struct Frag8<bf16> { bf16x8 v; };
 template <> struct Frag8<float> { floatx4 lo, hi; };
 
-// max / sum of a lane's value and that of lane ^ 32 without LDS: the
-// half-swap of gfx950 (v_permlane32_swap) hands every lane both values, and
-// the operation is commutative, so the result equals op(v, shfl_xor(v, 32))
-// bit for bit whichever way round the halves are swapped
-__device__ __forceinline__ float xor32_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
-                                                  false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
-}
-__device__ __forceinline__ float xor32_add(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
-                                                  false, false);
-  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
 __device__ __forceinline__ void mma16(floatx4& acc, const Frag8<bf16>& a, const Frag8<bf16>& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
 }
