@@ -200,12 +200,14 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq2_kernel(AttnArgs a, int ks
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          float p = __builtin_amdgcn_exp2f(sv[j] * sc2 - lse2);
-          if (!full) {
-            const int kp = kt + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
-            if (!(kp <= row && kp > row - a.window)) p = 0.f;
-          }
-          sv[j] = p * (dpv[j] - Dq);
+          const int kp = kt + kb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
+          // one select per element, after an unconditional exponential, with
+          // the tile-uniform `full` ORed in without short-circuit: written as
+          // a test inside `if (!full)`, the compiler gave every element an
+          // exec-mask region, also on tiles that need no mask
+          const bool keep = full | ((kp <= row) & (kp > row - a.window));
+          const float e = __builtin_amdgcn_exp2f(sv[j] * sc2 - lse2);
+          sv[j] = (keep ? e : 0.f) * (dpv[j] - Dq);
         }
         bf16x8 dsf[2];
         pack_slots(dsf, sv);
@@ -359,11 +361,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int ql = qb * 32 + 8 * (j >> 2) + 4 * lg + (j & 3);
-          float p = __builtin_amdgcn_exp2f(s[qb][j] * sc2 - lsc[ql]);
-          if (!full) {
-            const int qi = qt + ql;
-            if (!(qi >= key && qi < key + a.window && qi < a.n && key < a.n)) p = 0.f;
-          }
+          const int qi = qt + ql;
+          // one select per element, as in the dQ kernel
+          const bool keep = full | ((qi >= key) & (qi < key + a.window) & (qi < a.n) & (key < a.n));
+          const float e = __builtin_amdgcn_exp2f(s[qb][j] * sc2 - lsc[ql]);
+          const float p = keep ? e : 0.f;
           s[qb][j] = p;
           ds[j] = p * (dp[qb][j] - Dc[ql]);
         }
