@@ -786,7 +786,10 @@ gemm_bf16_kernel(GemmArgs g0) {
     // 2. ... then the next tile's loads into the other stage (no LDS read of
     //    this iteration follows them, so nothing waits on them before the MFMAs)
     if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
-    // 3. the products
+    // 3. the products, at raised wave priority (the SIMD's other wave, in
+    //    its fragment reads, then yields issue to these; measured 0.5% on
+    //    the prefix products)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -803,6 +806,7 @@ gemm_bf16_kernel(GemmArgs g0) {
     // keep every MFMA of this tile issued before the wait for the next
     // tile's loads: left to itself the scheduler hoists the wait (and the
     // barrier) above most of them, exposing the whole load latency
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
