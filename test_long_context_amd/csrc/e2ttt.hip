@@ -480,13 +480,18 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   float* Wo = Wout + (int64_t)h * D * D;
   float* Mh = M + (int64_t)h * D * D;
   float w0e[EPT], m0e[EPT];
+  auto load_state = [&]() {
 #pragma unroll
-  for (int k = 0; k < EPT; ++k) {
-    const int e = threadIdx.x + k * NW * 64;
-    const int64_t idx = (int64_t)(i0 + e / JH) * D + j0 + e % JH;
-    w0e[k] = W0[idx];
-    m0e[k] = Mh[idx];
-  }
+    for (int k = 0; k < EPT; ++k) {
+      const int e = threadIdx.x + k * NW * 64;
+      const int64_t idx = (int64_t)(i0 + e / JH) * D + j0 + e % JH;
+      w0e[k] = W0[idx];
+      m0e[k] = Mh[idx];
+    }
+  };
+  // (the variant with outputs has no registers to hold them through the
+  // loop: it reads them at the end)
+  if constexpr (!OUT) load_state();
 #pragma unroll
   for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -514,6 +519,7 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   __syncthreads();
   const float* cf = coef + ((int64_t)h * nch + r) * 4;
   const float c0 = cf[0], c1 = cf[1], c2 = cf[2];
+  if constexpr (OUT) load_state();
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int e = threadIdx.x + k * NW * 64;
