@@ -231,7 +231,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq2_kernel(AttnArgs a, int ks
   }
 
   if (row < a.n) {
-    float* out = a.dq + (long)z * a.n * a.H * DH + ((long)row * a.H + h) * DH;
+    const long off = (long)z * a.n * a.H * DH + ((long)row * a.H + h) * DH;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -239,7 +239,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq2_kernel(AttnArgs a, int ks
         floatx4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * jg + e] * a.scale;
-        *(floatx4*)(out + db * 32 + 8 * jg + 4 * lg) = w;
+        const long o = off + db * 32 + 8 * jg + 4 * lg;
+        if (a.parts_bf16) *(bf16x4*)((bf16*)a.dq + o) = __builtin_convertvector(w, bf16x4);
+        else *(floatx4*)(a.dq + o) = w;
       }
   }
 }
@@ -407,8 +409,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
           wk[e] = accK[db][4 * jg + e] * a.scale;
           wv[e] = accV[db][4 * jg + e];
         }
-        *(floatx4*)(a.dk + base + db * 32 + 8 * jg + 4 * lg) = wk;
-        *(floatx4*)(a.dv + base + db * 32 + 8 * jg + 4 * lg) = wv;
+        const long o = base + db * 32 + 8 * jg + 4 * lg;
+        if (a.parts_bf16) {
+          *(bf16x4*)((bf16*)a.dk + o) = __builtin_convertvector(wk, bf16x4);
+          *(bf16x4*)((bf16*)a.dv + o) = __builtin_convertvector(wv, bf16x4);
+        } else {
+          *(floatx4*)(a.dk + o) = wk;
+          *(floatx4*)(a.dv + o) = wv;
+        }
       }
   }
 }

@@ -509,8 +509,8 @@ hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, in
 }
 
 // Transpose of the rotation (rotation by -angle) for dq, dk; dv copied.
-template <typename T>
-__global__ void rope_bwd_generic_kernel(const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
+template <typename T, typename PT>
+__global__ void rope_bwd_generic_kernel(const PT* dq, int dq_parts, const PT* dk, const PT* dv, int kv_parts,
                                 int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, T* out) {
   const int t = blockIdx.x;
   const int half = dh / 2;
@@ -523,20 +523,20 @@ __global__ void rope_bwd_generic_kernel(const float* dq, int dq_parts, const flo
     const int hh = i / half, j = i % half;
     const float2 cs = tb[j];
     const bool isq = hh < H;
-    const float* src = isq ? dq + ((long)t * H + hh) * dh : dk + ((long)t * Hk + (hh - H)) * dh;
+    const PT* src = isq ? dq + ((long)t * H + hh) * dh : dk + ((long)t * Hk + (hh - H)) * dh;
     const int np = isq ? dq_parts : kv_parts;
     const long ps = isq ? qstride : kstride;
     float g1 = 0.f, g2 = 0.f;
     for (int p = 0; p < np; ++p) {
-      g1 += src[p * ps + j];
-      g2 += src[p * ps + j + half];
+      g1 += to_f(src[p * ps + j]);
+      g2 += to_f(src[p * ps + j + half]);
     }
     out[(long)t * W + hh * dh + j] = from_f<T>(g1 * cs.x + g2 * cs.y);
     out[(long)t * W + hh * dh + j + half] = from_f<T>(-g1 * cs.y + g2 * cs.x);
   }
   for (int i = threadIdx.x; i < Hk * dh; i += blockDim.x) {
     float g = 0.f;
-    for (int p = 0; p < kv_parts; ++p) g += dv[p * kstride + (long)t * Hk * dh + i];
+    for (int p = 0; p < kv_parts; ++p) g += to_f(dv[p * kstride + (long)t * Hk * dh + i]);
     out[(long)t * W + (H + Hk) * dh + i] = from_f<T>(g);
   }
 }
@@ -546,8 +546,8 @@ __global__ void rope_bwd_generic_kernel(const float* dq, int dq_parts, const flo
 // value-gradient elements; the loads of every partial are issued before the
 // first store. At most ROPE_BNP partials per side (rope_bwd_pack chooses).
 constexpr int ROPE_BKR = 2, ROPE_BNP = 8;
-template <typename T>
-__global__ void __launch_bounds__(RB) rope_bwd_kernel(const float* dq, int dq_parts, const float* dk, const float* dv,
+template <typename T, typename PT>
+__global__ void __launch_bounds__(RB) rope_bwd_kernel(const PT* dq, int dq_parts, const PT* dk, const PT* dv,
                                                       int kv_parts, int n, int H, int Hk, int dh, int64_t pos0,
                                                       const float2* tab, T* out) {
   const int t = blockIdx.x;
@@ -563,14 +563,14 @@ __global__ void __launch_bounds__(RB) rope_bwd_kernel(const float* dq, int dq_pa
     if (gi < ng) {
       const int hh = gi / gph, j = (gi % gph) * 4;
       const bool isq = hh < H;
-      const float* src = isq ? dq + ((long)t * H + hh) * dh : dk + ((long)t * Hk + (hh - H)) * dh;
+      const PT* src = isq ? dq + ((long)t * H + hh) * dh : dk + ((long)t * Hk + (hh - H)) * dh;
       const int np = isq ? dq_parts : kv_parts;
       const long ps = isq ? qstride : kstride;
 #pragma unroll
       for (int p = 0; p < ROPE_BNP; ++p)
         if (p < np) {
-          g1[k][p] = *(const float4*)(src + p * ps + j);
-          g2[k][p] = *(const float4*)(src + p * ps + j + half);
+          g1[k][p] = ld_part4(src + p * ps + j, 0);
+          g2[k][p] = ld_part4(src + p * ps + j + half, 0);
         }
       c01[k] = tb[j / 2];
       c23[k] = tb[j / 2 + 1];
@@ -579,7 +579,7 @@ __global__ void __launch_bounds__(RB) rope_bwd_kernel(const float* dq, int dq_pa
   const bool hv = (int)threadIdx.x < nvg;
 #pragma unroll
   for (int p = 0; p < ROPE_BNP; ++p)
-    if (hv && p < kv_parts) gv[p] = *(const float4*)(dv + p * kstride + (long)t * Hk * dh + 4 * threadIdx.x);
+    if (hv && p < kv_parts) gv[p] = ld_part4(dv + p * kstride + (long)t * Hk * dh, threadIdx.x);
   // partial sums added in a fixed order
 #pragma unroll
   for (int k = 0; k < ROPE_BKR; ++k) {
@@ -610,7 +610,8 @@ __global__ void __launch_bounds__(RB) rope_bwd_kernel(const float* dq, int dq_pa
   }
 }
 
-hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
+template <typename PT>
+static hipError_t rope_bwd_pack_t(DT dt, const PT* dq, int dq_parts, const PT* dk, const PT* dv, int kv_parts,
                          int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
                          hipStream_t st) {
   if (n <= 0) return hipSuccess;
@@ -618,20 +619,32 @@ hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, 
                    dq_parts <= ROPE_BNP && kv_parts >= 1 && kv_parts <= ROPE_BNP;
   if (dt == DT::BF16) {
     if (vec)
-      hipLaunchKernelGGL(rope_bwd_kernel<bf16>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H, Hk,
+      hipLaunchKernelGGL((rope_bwd_kernel<bf16, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H, Hk,
                          dh, pos0, tab, (bf16*)dqkv);
     else
-      hipLaunchKernelGGL(rope_bwd_generic_kernel<bf16>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n,
+      hipLaunchKernelGGL((rope_bwd_generic_kernel<bf16, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n,
                          H, Hk, dh, pos0, tab, (bf16*)dqkv);
   } else {
     if (vec)
-      hipLaunchKernelGGL(rope_bwd_kernel<float>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H,
+      hipLaunchKernelGGL((rope_bwd_kernel<float, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H,
                          Hk, dh, pos0, tab, (float*)dqkv);
     else
-      hipLaunchKernelGGL(rope_bwd_generic_kernel<float>, dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts,
+      hipLaunchKernelGGL((rope_bwd_generic_kernel<float, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts,
                          n, H, Hk, dh, pos0, tab, (float*)dqkv);
   }
   return hipGetLastError();
+}
+
+hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
+                         int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
+                         hipStream_t st) {
+  return rope_bwd_pack_t(dt, dq, dq_parts, dk, dv, kv_parts, n, H, Hk, dh, pos0, tab, dqkv, st);
+}
+
+hipError_t rope_bwd_pack(DT dt, const bf16* dq, int dq_parts, const bf16* dk, const bf16* dv, int kv_parts,
+                         int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
+                         hipStream_t st) {
+  return rope_bwd_pack_t(dt, dq, dq_parts, dk, dv, kv_parts, n, H, Hk, dh, pos0, tab, dqkv, st);
 }
 
 __global__ void sum_parts_kernel(const float* parts, int nparts, long count, float* dst) {

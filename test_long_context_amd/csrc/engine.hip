@@ -755,7 +755,12 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         a.dk = sqf(c->dk, j, (size_t)H * c->b * dh);
         a.dv = sqf(c->dv, j, (size_t)H * c->b * dh);
         int qp = 1, kp = 1;
-        if (attn_bwd2_supported(c->dt, a)) {
+        const bool bwd2 = attn_bwd2_supported(c->dt, a);
+        // the second-generation kernels' partial sums in bf16 (like the
+        // split-K data-gradient products'): the RoPE backward that adds
+        // them reads half the bytes
+        a.parts_bf16 = bwd2;
+        if (bwd2) {
           qp = attn_bwd2_dq_parts(a);
           kp = attn_bwd2_kv_parts(a);
           TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq2(c->dt, a, st));
@@ -768,8 +773,12 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
           TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq(c->dt, a, st));
           TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv(c->dt, a, st));
         }
-        TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, a.dq, qp, a.dk, a.dv, kp, n, H, Hk, dh, a0, c->rope,
-                                         sq(c->dqkv, j, (size_t)n * QKV, es), st));
+        if (a.parts_bf16)
+          TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, (const __bf16*)a.dq, qp, (const __bf16*)a.dk, (const __bf16*)a.dv, kp, n, H,
+                                           Hk, dh, a0, c->rope, sq(c->dqkv, j, (size_t)n * QKV, es), st));
+        else
+          TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, a.dq, qp, a.dk, a.dv, kp, n, H, Hk, dh, a0, c->rope,
+                                           sq(c->dqkv, j, (size_t)n * QKV, es), st));
       }
       if (c->upd_at_attn && !upd_done) RUN(launch_update(c, i, a0, n, st, c->upd_split ? 2 : 3));
       RUN(gemm_nn_split(c, KC_GL, c->dqkv, QKV, c->wqkv[l], d, nb, d, QKV, c->part, &ns, st));

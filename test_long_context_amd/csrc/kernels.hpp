@@ -71,6 +71,10 @@ hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, in
 hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts, int n, int H,
                          int Hk, int dh, int64_t pos0, const float2* rope_tab, void* dqkv,
                          hipStream_t st);
+// The same from bf16 partial sums.
+hipError_t rope_bwd_pack(DT dt, const __bf16* dq, int dq_parts, const __bf16* dk, const __bf16* dv, int kv_parts, int n, int H,
+                         int Hk, int dh, int64_t pos0, const float2* rope_tab, void* dqkv,
+                         hipStream_t st);
 // Fused softmax cross-entropy over the vocabulary for rows with a target
 // (rows < nt): loss[t] = lse - z[t, label]; dz (T) = (softmax - onehot) * scale;
 // rows >= nt get dz = 0. Also flags non-finite losses in *err (bit 2).
@@ -116,6 +120,9 @@ struct AttnArgs {
   float* dq;          // [n, H, dh] float
   float* dk;          // [n, Hk, dh] float, keys of this call's own positions
   float* dv;
+  // second-generation backward: its per-part dq / dk / dv partial sums are
+  // stored as bf16 (at the same element offsets, in the same buffers) when set
+  bool parts_bf16;
   // forward key-range split (second-generation forward): ksplit parts, each
   // an unnormalised output [n, H, dh] in opart and (max, sum) in mlpart
   // [ksplit][2][H][n] (log2 domain), merged by a combine pass
