@@ -82,73 +82,99 @@ def _grads(W0, k, v):
     return dict(w1=(da1, k), w2=(da2, k), w3=(dy, h))
 
 
-def _copy(Ws):
-    return [{m: np.array(w[m], np.float64) for m in MATS} for w in Ws]
+class Net:
+    """A fast-weight net for the E2 machinery below: its matrix names, its
+    forward f_W(x) -> (f, cache) and its per-token gradient factors
+    grads(W0, k, v) -> {name: (left [n, rows], right [n, cols])}. The
+    functions are looked up by name in their module at call time."""
+
+    def __init__(self, module, mats):
+        self.module, self.mats = module, mats
+
+    def forward(self, W, x):
+        return self.module.fw_forward(W, x)
+
+    def grads(self, W0, k, v):
+        return self.module._grads(W0, k, v)
 
 
-def e2_mlp_sequential(k, v, eta, beta, gamma, W, M, C, sign=-1.0):
+def _copy(Ws, mats=MATS):
+    return [{m: np.array(w[m], np.float64) for m in mats} for w in Ws]
+
+
+def _net(net):
+    import sys
+    return net if net is not None else Net(sys.modules[__name__], MATS)
+
+
+def e2_mlp_sequential(k, v, eta, beta, gamma, W, M, C, sign=-1.0, net=None):
     """Per-token recursion chunk by chunk with G_t = sign grad_W L_t at the
     chunk-start W0, for every matrix. k, v [H, T, D]; eta, beta, gamma
-    [H, T]; W, M: lists (per head) of dicts of matrices. Returns (W, M)."""
+    [H, T]; W, M: lists (per head) of dicts of matrices; net: the
+    fast-weight net (default: this module's SwiGLU net). Returns (W, M)."""
+    net = _net(net)
     k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
     eta, beta, gamma = (np.asarray(x, np.float64) for x in (eta, beta, gamma))
-    W, M = _copy(W), _copy(M)
+    W, M = _copy(W, net.mats), _copy(M, net.mats)
     H, T, _ = k.shape
     for h in range(H):
         for a in range(0, T, C):
             e = min(T, a + C)
-            G = _grads(_copy([W[h]])[0], k[h, a:e], v[h, a:e])
+            G = net.grads(_copy([W[h]], net.mats)[0], k[h, a:e], v[h, a:e])
             for t in range(e - a):
-                for m in MATS:
+                for m in net.mats:
                     l, r = G[m]
                     M[h][m] = beta[h, a + t] * M[h][m] + eta[h, a + t] * sign * np.outer(l[t], r[t])
                     W[h][m] = gamma[h, a + t] * W[h][m] + M[h][m]
     return W, M
 
 
-def e2_mlp_chunk(k, v, eta, beta, gamma, W0, M0, sign=-1.0):
+def e2_mlp_chunk(k, v, eta, beta, gamma, W0, M0, sign=-1.0, net=None):
     """Proposition 3.1 for one head and one chunk, every matrix with the
     same scalars: W_C = gamma~_0 W0 + beta~_0 R_1 M0 + sum_t K^W_t G_t,
     M_C = beta~_0 M0 + sum_t K^M_t G_t."""
+    net = _net(net)
     bt, gt, R, KM, KW = chunk_scalars(eta, beta, gamma)
-    G = _grads(W0, k, v)
+    G = net.grads(W0, k, v)
     W, M = {}, {}
-    for m in MATS:
+    for m in net.mats:
         l, r = G[m]
         W[m] = gt[0] * W0[m] + bt[0] * R[1] * M0[m] + sign * (l * KW[:, None]).T @ r
         M[m] = bt[0] * M0[m] + sign * (l * KM[:, None]).T @ r
     return W, M
 
 
-def e2_mlp_closed_form(k, v, eta, beta, gamma, W, M, C, sign=-1.0):
+def e2_mlp_closed_form(k, v, eta, beta, gamma, W, M, C, sign=-1.0, net=None):
     """e2_mlp_chunk applied chunk by chunk to every head."""
+    net = _net(net)
     k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
     eta, beta, gamma = (np.asarray(x, np.float64) for x in (eta, beta, gamma))
-    W, M = _copy(W), _copy(M)
+    W, M = _copy(W, net.mats), _copy(M, net.mats)
     H, T, _ = k.shape
     for h in range(H):
         for a in range(0, T, C):
             e = min(T, a + C)
             W[h], M[h] = e2_mlp_chunk(k[h, a:e], v[h, a:e], eta[h, a:e], beta[h, a:e], gamma[h, a:e],
-                                      W[h], M[h], sign)
+                                      W[h], M[h], sign, net)
     return W, M
 
 
-def e2_mlp_mixer(x, wqkv, bias, eta_base, alpha_base, tau, W, M, H, D, C, sign=-1.0):
+def e2_mlp_mixer(x, wqkv, bias, eta_base, alpha_base, tau, W, M, H, D, C, sign=-1.0, net=None):
     """The E2-TTT token mixer's TTT path with the SwiGLU fast-weight net,
     chunk by chunk ([P3] Algorithm 1): outputs o_t = f_W0(q_t) under the
     state at the start of t's chunk, then the chunk-end state of every
     matrix by Proposition 3.1 (descent). Inputs from mixer_inputs (bf16
     q, k, v; float32 scalars). W, M: lists (per head) of dicts. Returns
     (outputs [T, H, D], W, M)."""
+    net = _net(net)
     q, k, v, eta, beta, gamma = mixer_inputs(x, wqkv, bias, eta_base, alpha_base, tau, H, D)
     T = q.shape[1]
-    W, M = _copy(W), _copy(M)
+    W, M = _copy(W, net.mats), _copy(M, net.mats)
     out = np.zeros((T, H, D))
     for a in range(0, T, C):
         e = min(T, a + C)
         for h in range(H):
-            out[a:e, h], _ = fw_forward(W[h], q[h, a:e])
+            out[a:e, h], _ = net.forward(W[h], q[h, a:e])
             W[h], M[h] = e2_mlp_chunk(k[h, a:e], v[h, a:e], eta[h, a:e], beta[h, a:e], gamma[h, a:e],
-                                      W[h], M[h], sign)
+                                      W[h], M[h], sign, net)
     return out, W, M
