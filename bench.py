@@ -361,6 +361,37 @@ def e2_bench(args, tla, torch, synth):
                                       f"C={sc['chunk']}",
                                fast_weight_gflop=round(fw_flops / 1e9, 1),
                                fast_weight_tflops=round(fw_flops / (sms * 1e-3) / 1e12, 1))
+    # the same mixer with the GELU fast-weight net
+    gc = synth.E2_GELU_CONFIG
+    gx = synth.gen_e2_mixer(gc["heads"], gc["seq"], gc["dim"], gc["d_model"], gc["seed"], device="cuda")
+    g0 = synth.gen_e2_gelu_state(gc["heads"], gc["dim"], gc["hidden"], gc["seed"], device="cuda")
+    gst = {k_: v_.clone() for k_, v_ in g0.items()}
+    go = torch.empty(gc["seq"], gc["heads"] * gc["dim"], device="cuda")
+    gts = []
+    for i in range(max(1, args.warmup) + args.steps):
+        for k_ in gst:
+            gst[k_].copy_(g0[k_])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tla.e2ttt_mixer_gelu_forward(gx["x"], gx["wqkv"], gx["bias"], gc["eta_base"], gc["alpha_base"], gc["tau"],
+                                     gst, gc["heads"], gc["chunk"], out=go)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= max(1, args.warmup):
+            gts.append(a.elapsed_time(b))
+    gms = sorted(gts)[len(gts) // 2]
+    # matrix-product FLOPs per token and head: forward of key and query
+    # (2 x (Dh D + D Dh) x 2), backward through W2 twice (2 x D Dh x 2) and
+    # four aggregations (2 x (D Dh + Dh D) x 2)
+    Dh_, D_ = gc["hidden"], gc["dim"]
+    gf_flops = gc["seq"] * gc["heads"] * (8 * Dh_ * D_ + 4 * Dh_ * D_ + 8 * Dh_ * D_)
+    out["gelu_mixer"] = dict(ms_per_step=round(gms, 4), value=round(gc["seq"] / (gms * 1e-3), 1),
+                             unit="tokens/s",
+                             config=f"E2-TTT token mixer, GELU fast-weight net: T={gc['seq']}, "
+                                    f"d_model={gc['d_model']}, H={gc['heads']} x {D_}, hidden {Dh_}, "
+                                    f"C={gc['chunk']}",
+                             fast_weight_gflop=round(gf_flops / 1e9, 1),
+                             fast_weight_tflops=round(gf_flops / (gms * 1e-3) / 1e12, 1))
     # the hybrid block: SWA beside the SwiGLU TTT path, gated
     hc = synth.E2_HYBRID_CONFIG
     hx = synth.gen_e2_mixer(hc["heads"], hc["seq"], hc["dim"], hc["d_model"], hc["seed"], device="cuda")

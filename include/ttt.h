@@ -325,6 +325,18 @@ ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv, const flo
                                       float* M2, float* M3, float* out, int32_t H, int64_t T, int32_t D,
                                       int32_t Dh, int32_t dm, int32_t C, void* stream);
 
+/* The same token mixer with the GELU fast-weight net ([P3] 方法细节,
+ * 快速权重网络实例化): per head f_W(x) = x + LN(W2 GELU(W1 x)) with the
+ * exact GELU (u Phi(u), Phi the standard normal distribution function) and
+ * LN, loss, aggregations and outputs as for e2ttt_mixer_swiglu_forward.
+ * W1, M1: device float [H, Dh, D]; W2, M2: device float [H, D, Dh]; all
+ * updated in place. Other arguments, requirements and errors as for
+ * e2ttt_mixer_swiglu_forward. Shares the same cached work buffer. */
+ttt_status e2ttt_mixer_gelu_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
+                                    float alpha_base, float tau, float* W1, float* W2, float* M1, float* M2,
+                                    float* out, int32_t H, int64_t T, int32_t D, int32_t Dh, int32_t dm, int32_t C,
+                                    void* stream);
+
 /* The hybrid token-mixer block ([P3] 方法细节, 混合模型架构设计 and Figure 2):
  * sliding-window attention on the shared projections beside the TTT path,
  * interpolated element-wise by a data-dependent gate:

@@ -74,6 +74,8 @@ E2_MIXER_CONFIG = dict(heads=16, seq=32768, dim=128, d_model=2048, chunk=512, et
 # the same mixer with a SwiGLU fast-weight net of `hidden` units per head
 E2_MLP_CONFIG = dict(heads=16, seq=32768, dim=128, hidden=256, d_model=2048, chunk=512, eta_base=3e-4,
                      alpha_base=0.5, tau=4.0, seed=7)
+# the same token mixer with the GELU fast-weight net (same shapes)
+E2_GELU_CONFIG = dict(E2_MLP_CONFIG, seed=10)
 # the hybrid block (SWA beside the SwiGLU TTT path, gated)
 E2_HYBRID_CONFIG = dict(E2_MLP_CONFIG, window=1024, rope_theta=10000.0, seed=8)
 
@@ -262,6 +264,16 @@ def gen_e2_mlp_state(heads: int, dim: int, hidden: int, seed: int, device="cpu")
     w3 = (normal(seed, 13, H * D * Dh, device) / math.sqrt(Dh)).to(torch.float32).view(H, D, Dh)
     z = lambda t: torch.zeros_like(t)
     return dict(w1=w1, w2=w2, w3=w3, m1=z(w1), m2=z(w2), m3=z(w3))
+
+
+def gen_e2_gelu_state(heads: int, dim: int, hidden: int, seed: int, device="cpu") -> dict:
+    """Initial GELU fast-weight state per head: w1 ~ N(0, 1) [H, hidden, dim],
+    w2 ~ N(0, 1/hidden) [H, dim, hidden], float32; momenta m1, m2 = 0."""
+    H, D, Dh = heads, dim, hidden
+    w1 = normal(seed, 31, H * Dh * D, device).to(torch.float32).view(H, Dh, D)
+    w2 = (normal(seed, 32, H * D * Dh, device) / math.sqrt(Dh)).to(torch.float32).view(H, D, Dh)
+    z = lambda t: torch.zeros_like(t)
+    return dict(w1=w1, w2=w2, m1=z(w1), m2=z(w2))
 
 
 def gen_gate(heads: int, dim: int, d_model: int, seed: int, device="cpu") -> dict:

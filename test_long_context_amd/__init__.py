@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
                                           i32, i64, i32, i32, i32, vp]
         L.e2ttt_mixer_swiglu_forward.argtypes = [vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                                  vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp]
+        L.e2ttt_mixer_gelu_forward.argtypes = [vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                               vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp]
         L.e2ttt_hybrid_forward.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                            ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, i64, i32, i32,
                                            i32, vp]
@@ -115,7 +117,7 @@ def lib() -> ctypes.CDLL:
         for f in ("ttt_init", "ttt_prefill", "ttt_decode_step", "ttt_decode_step_update", "ttt_get_fast_weights",
                   "ttt_get_fast_weights_seq",
                   "ttt_reset", "ttt_sync", "e2ttt_chunk_scan", "e2ttt_chunk_scan_noalloc", "lact_chunk_scan", "e2ttt_mixer_forward",
-                  "e2ttt_mixer_swiglu_forward", "e2ttt_hybrid_forward",
+                  "e2ttt_mixer_swiglu_forward", "e2ttt_mixer_gelu_forward", "e2ttt_hybrid_forward",
                   "ttt_timing_enable", "ttt_timing_read", "tttk_gemm", "tttk_attn_fwd", "tttk_attn_bwd", "tttk_ce", "tttk_ce_lse",
                   "tttk_dw_sgd"):
             getattr(L, f).restype = st
@@ -325,6 +327,25 @@ def e2ttt_mixer_swiglu_forward(x, wqkv, bias, eta_base, alpha_base, tau, state: 
                                           _ptr(out), H, T, D, Dh, dm, chunk, _stream(stream))
     if st != TTT_OK:
         raise TTTError(st, "e2ttt_mixer_swiglu_forward")
+    return out
+
+
+def e2ttt_mixer_gelu_forward(x, wqkv, bias, eta_base, alpha_base, tau, state: dict, heads: int, chunk: int,
+                             out=None, stream=None):
+    """E2-TTT token mixer, TTT path with the GELU fast-weight net (see
+    include/ttt.h); state: w1 [H, Dh, D], w2 [H, D, Dh] and momenta m1, m2
+    (float), updated in place. Returns out [T, H D]."""
+    import torch
+    T, dm = x.shape
+    H, Dh, D = state["w1"].shape
+    assert H == heads
+    if out is None:
+        out = torch.empty(T, H * D, dtype=torch.float32, device=x.device)
+    st = lib().e2ttt_mixer_gelu_forward(_ptr(x), _ptr(wqkv), _ptr(bias), float(eta_base), float(alpha_base),
+                                        float(tau), *(_ptr(state[n]) for n in ("w1", "w2", "m1", "m2")),
+                                        _ptr(out), H, T, D, Dh, dm, chunk, _stream(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "e2ttt_mixer_gelu_forward")
     return out
 
 

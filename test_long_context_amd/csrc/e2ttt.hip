@@ -1177,6 +1177,183 @@ ttt_status mixer_swiglu_run(const void* x, const void* wqkv, const float* bias, 
 }
 }  // namespace
 
+namespace {
+// ------------------------------------------------ GELU fast-weight net
+// [P3] 方法细节, 快速权重网络实例化: f_W(x) = x + LN(W2 GELU(W1 x)) with the
+// exact GELU, u Phi(u). Same per-chunk schedule as the SwiGLU net, with a
+// plain bf16 store of the pre-activations U = x W1^T and two element-wise
+// passes: A = GELU(U) before the W2 product, dU = dA GELU'(U) after the
+// backward product dA = dY W2.
+__device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * (1.f + erff(u * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_grad_f(float u) {
+  return 0.5f * (1.f + erff(u * 0.70710678118654752f)) + u * __expf(-0.5f * u * u) * 0.39894228040143268f;
+}
+
+// rows i < n of the H blocks [Cmax, Dh] (bf16): out = GELU(U), or, with dA,
+// out = dA GELU'(U); Dh a multiple of 4
+__global__ void __launch_bounds__(256) e2gelu_kernel(const bf16* __restrict__ U, const bf16* __restrict__ dA,
+                                                     bf16* __restrict__ out, int n, int Cmax, int Dh, int H) {
+  const int64_t per = (int64_t)n * Dh / 4, total = per * H;
+  for (int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; j < total; j += (int64_t)gridDim.x * blockDim.x) {
+    const int h = (int)(j / per);
+    const int64_t i = ((int64_t)h * Cmax * Dh) + 4 * (j - h * per);
+    const bf16x4 u = *(const bf16x4*)(U + i);
+    bf16x4 r;
+    if (dA) {
+      const bf16x4 g = *(const bf16x4*)(dA + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (bf16)((float)g[e] * gelu_grad_f((float)u[e]));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (bf16)gelu_f((float)u[e]);
+    }
+    *(bf16x4*)(out + i) = r;
+  }
+}
+
+size_t gelu_mixer_work_bytes(int32_t H, int64_t T, int32_t D, int32_t Dh, int32_t C) {
+  const size_t al = 256, h = H, c = C, d = D, f = Dh;
+  return mixer_work_bytes(H, T, D, C) + 2 * (h * f * d * 2 + al) + 4 * (h * c * f * 2 + al) + 2 * (h * c * d * 4 + al) +
+         2 * (h * c * d * 2 + al) + 2 * (h * c * f * 2 + al) + 4 * (h * f * d * 4 + al) + 256;
+}
+
+ttt_status gelu_check(const float* W1, const float* W2, const float* M1, const float* M2, int32_t Dh) {
+  if (!W1 || !W2 || !M1 || !M2 || Dh < 1) return TTT_ERR_INVALID_ARG;
+  if (Dh % 32 || Dh > 4096) return TTT_ERR_UNSUPPORTED;
+  for (const void* p : {(const void*)W1, (const void*)W2, (const void*)M1, (const void*)M2})
+    if ((uintptr_t)p & 15) return TTT_ERR_INVALID_ARG;
+  return TTT_OK;
+}
+
+// The GELU-fast-weight mixer on a work buffer of gelu_mixer_work_bytes().
+ttt_status mixer_gelu_run(const void* x, const void* wqkv, const float* bias, float eta_base, float alpha_base,
+                          float tau, float* W1, float* W2, float* M1, float* M2, float* out, int32_t H, int64_t T,
+                          int32_t D, int32_t Dh, int32_t dm, int32_t C, void* work, void* stream) {
+  using namespace ttt;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t N = 3LL * H * D + 3LL * H, nch = (T + C - 1) / C;
+  const size_t h = H, c = C, d = D, f = Dh;
+  Carve cv{((uintptr_t)work + 255) & ~(uintptr_t)255};
+  float* P = cv.take<float>((size_t)T * N * 4);
+  bf16* q = cv.take<bf16>(h * T * d * 2);
+  bf16* k = cv.take<bf16>(h * T * d * 2);
+  bf16* v = cv.take<bf16>(h * T * d * 2);
+  float* eta = cv.take<float>(h * T * 4);
+  float* beta = cv.take<float>(h * T * 4);
+  float* gamma = cv.take<float>(h * T * 4);
+  float* KW = cv.take<float>(h * T * 4);
+  float* KM = cv.take<float>(h * T * 4);
+  float* coef = cv.take<float>(h * nch * 16);
+  (void)cv.take<float>(h * d * d * 4);  // (the linear mixer's second state buffer; unused here)
+  bf16* W1b = cv.take<bf16>(h * f * d * 2);
+  bf16* W2b = cv.take<bf16>(h * d * f * 2);
+  bf16* Uk = cv.take<bf16>(h * c * f * 2);
+  bf16* Uq = cv.take<bf16>(h * c * f * 2);
+  bf16* Hk = cv.take<bf16>(h * c * f * 2);
+  bf16* Hq = cv.take<bf16>(h * c * f * 2);
+  float* Yk = cv.take<float>(h * c * d * 4);
+  float* Yq = cv.take<float>(h * c * d * 4);
+  bf16* dYw = cv.take<bf16>(h * c * d * 2);
+  bf16* dYm = cv.take<bf16>(h * c * d * 2);
+  bf16* dA = cv.take<bf16>(h * c * f * 2);
+  bf16* dU = cv.take<bf16>(h * c * f * 2);
+  float* a1w = cv.take<float>(h * f * d * 4);
+  float* a1m = cv.take<float>(h * f * d * 4);
+  float* a2w = cv.take<float>(h * d * f * 4);
+  float* a2m = cv.take<float>(h * d * f * 4);
+#define E2CHK(call)                          \
+  do {                                       \
+    if ((call) != hipSuccess) {              \
+      (void)hipGetLastError();               \
+      return TTT_ERR_HIP;                    \
+    }                                        \
+  } while (0)
+  // inputs: projections, then q, k, v and the scalars (as the linear mixer)
+  {
+    GemmArgs g{};
+    g.A = x;
+    g.B = wqkv;
+    g.M = (int)T;
+    g.N = (int)N;
+    g.K = dm;
+    g.lda = dm;
+    g.ldb = dm;
+    g.C = P;
+    g.ldc = N;
+    g.scale = 1.f;
+    E2CHK(gemm(DT::BF16, true, true, Epi::STORE_F32, g, st));
+  }
+  if (D == 128)
+    hipLaunchKernelGGL(mixer_prologue_kernel<128>, dim3((unsigned)T), dim3(256), 0, st, P, bias, H, T, eta_base,
+                       alpha_base, 1.f / tau, q, k, v, eta, beta, gamma);
+  else
+    hipLaunchKernelGGL(mixer_prologue_kernel<64>, dim3((unsigned)T), dim3(256), 0, st, P, bias, H, T, eta_base,
+                       alpha_base, 1.f / tau, q, k, v, eta, beta, gamma);
+  E2CHK(hipGetLastError());
+  E2CHK(e2_scalars(eta, beta, gamma, H, T, C, KW, KM, coef, st));
+  hipLaunchKernelGGL(e2mlp_cast_kernel, dim3(1024), dim3(256), 0, st, W1, W1b, (int64_t)(h * f * d));
+  hipLaunchKernelGGL(e2mlp_cast_kernel, dim3(1024), dim3(256), 0, st, W2, W2b, (int64_t)(h * d * f));
+  E2CHK(hipGetLastError());
+  const long sT = (long)T * D, s1 = (long)Dh * D, s2 = (long)D * Dh;
+  for (int64_t r = 0; r < nch; ++r) {
+    const int n = (int)std::min<int64_t>(C, T - r * C);
+    const size_t off = (size_t)r * C * D;
+    const unsigned eg = (unsigned)std::min<int64_t>(2048, ((int64_t)H * n * Dh / 4 + 255) / 256);
+    // forward of keys and queries under the chunk-start weights
+    for (int which = 0; which < 2; ++which) {
+      const bf16* in = (which == 0 ? k : q) + off;
+      bf16* Ux = which == 0 ? Uk : Uq;
+      bf16* Hx = which == 0 ? Hk : Hq;
+      GemmArgs g = hg(in, D, sT, W1b, D, s1, n, Dh, D, Ux, Dh, (long)C * Dh, H);
+      E2CHK(gemm(DT::BF16, true, true, Epi::STORE, g, st));
+      hipLaunchKernelGGL(e2gelu_kernel, dim3(eg), dim3(256), 0, st, Ux, (const bf16*)nullptr, Hx, n, C, Dh, H);
+      E2CHK(hipGetLastError());
+      GemmArgs g2 = hg(Hx, Dh, (long)C * Dh, W2b, Dh, s2, n, D, Dh, which == 0 ? Yk : Yq, D, (long)C * D, H);
+      E2CHK(gemm(DT::BF16, true, true, Epi::STORE_F32, g2, st));
+    }
+    const dim3 rg((unsigned)((n + 3) / 4), (unsigned)H, 2);
+    if (D == 128)
+      hipLaunchKernelGGL(e2mlp_rows_kernel<128>, rg, dim3(256), 0, st, Yk, Yq, q, k, v, KW, KM, T, r * C, n, C, H,
+                         dYw, dYm, out);
+    else
+      hipLaunchKernelGGL(e2mlp_rows_kernel<64>, rg, dim3(256), 0, st, Yk, Yq, q, k, v, KW, KM, T, r * C, n, C, H,
+                         dYw, dYm, out);
+    E2CHK(hipGetLastError());
+    // backward through the net, once per scalar kernel, and the aggregations
+    for (int which = 0; which < 2; ++which) {
+      const bf16* dY = which == 0 ? dYw : dYm;
+      GemmArgs gb = hg(dY, D, (long)C * D, W2b, Dh, s2, n, Dh, D, dA, Dh, (long)C * Dh, H);
+      E2CHK(gemm(DT::BF16, true, false, Epi::STORE, gb, st));
+      hipLaunchKernelGGL(e2gelu_kernel, dim3(eg), dim3(256), 0, st, (const bf16*)Uk, (const bf16*)dA, dU, n, C, Dh, H);
+      E2CHK(hipGetLastError());
+      GemmArgs g2 = hg(dY, D, (long)C * D, Hk, Dh, (long)C * Dh, D, Dh, n, which == 0 ? a2w : a2m, Dh, s2, H);
+      E2CHK(gemm(DT::BF16, false, false, Epi::STORE_F32, g2, st));
+      GemmArgs g1 = hg(dU, Dh, (long)C * Dh, k + off, D, sT, Dh, D, n, which == 0 ? a1w : a1m, D, s1, H);
+      E2CHK(gemm(DT::BF16, false, false, Epi::STORE_F32, g1, st));
+    }
+    hipLaunchKernelGGL(e2mlp_state_kernel, dim3(1024), dim3(256), 0, st, W1, M1, a1w, a1m, W1b, coef, s1, H, nch, r);
+    hipLaunchKernelGGL(e2mlp_state_kernel, dim3(1024), dim3(256), 0, st, W2, M2, a2w, a2m, W2b, coef, s2, H, nch, r);
+    E2CHK(hipGetLastError());
+  }
+#undef E2CHK
+  return TTT_OK;
+}
+}  // namespace
+
+extern "C" ttt_status e2ttt_mixer_gelu_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
+                                               float alpha_base, float tau, float* W1, float* W2, float* M1,
+                                               float* M2, float* out, int32_t H, int64_t T, int32_t D, int32_t Dh,
+                                               int32_t dm, int32_t C, void* stream) {
+  ttt_status r = mixer_check(x, wqkv, bias, eta_base, alpha_base, tau, out, H, T, D, dm, C);
+  if (r != TTT_OK) return r;
+  if ((r = gelu_check(W1, W2, M1, M2, Dh)) != TTT_OK) return r;
+  if ((r = device_present()) != TTT_OK) return r;
+  std::lock_guard<std::mutex> lock(g_e2_mu);
+  if ((r = e2_grow(gelu_mixer_work_bytes(H, T, D, Dh, C), (hipStream_t)stream)) != TTT_OK) return r;
+  return mixer_gelu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, M1, M2, out, H, T, D, Dh, dm, C, g_e2.p,
+                        stream);
+}
+
 extern "C" ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
                                                  float alpha_base, float tau, float* W1, float* W2, float* W3,
                                                  float* M1, float* M2, float* M3, float* out, int32_t H, int64_t T,

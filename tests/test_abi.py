@@ -106,6 +106,17 @@ def test_e2_swiglu_mixer_argument_checks():
     assert f(*a[:3], 1e-3, 0.5, 0.0, *a[:7], 2, 64, 128, 64, 64, 64, None) == -1      # tau 0
 
 
+def test_e2_gelu_mixer_argument_checks():
+    f = tla.lib().e2ttt_mixer_gelu_forward
+    a = [16] * 10  # placeholder, 16-byte aligned pointers: rejected before any device work
+    assert f(None, *a[:2], 1e-3, 0.5, 4.0, *a[:5], 2, 64, 128, 64, 64, 64, None) == -1  # null input
+    assert f(*a[:3], 1e-3, 0.5, 4.0, None, *a[:4], 2, 64, 128, 64, 64, 64, None) == -1  # null W1
+    assert f(*a[:3], 1e-3, 0.5, 4.0, *a[:5], 2, 64, 128, 48, 64, 64, None) == -2       # hidden not a multiple of 32
+    assert f(*a[:3], 1e-3, 0.5, 4.0, *a[:5], 2, 64, 96, 64, 64, 64, None) == -2       # head size 96
+    assert f(*a[:3], 1e-3, 0.5, 4.0, *a[:5], 2, 64, 128, 64, 64, 60, None) == -2      # chunk not a multiple of 64
+    assert f(*a[:3], 1e-3, 0.5, 4.0, 16, 16, 16, 24, 16, 2, 64, 128, 64, 64, 64, None) == -1  # misaligned M2
+
+
 def test_e2_hybrid_argument_checks():
     f = tla.lib().e2ttt_hybrid_forward
     a = [16] * 6

@@ -164,6 +164,52 @@ def test_e2_swiglu_mixer_full_workload():
     assert eo < 2e-2 and ew < 5e-2 and em < 5e-2
 
 
+# --------------------------------------------- GELU fast-weight token mixer
+def run_gelu_mixer(H, T, D, Dh, dm, C, seed, eta_base=3e-4, alpha_base=0.5, tau=4.0):
+    """The token mixer with the GELU fast-weight net
+    (e2ttt_mixer_gelu_forward) against the float64 oracle on the same
+    bf16-valued inputs; errors as for the SwiGLU net (run_mlp_mixer)."""
+    import test_long_context_amd as tla
+    from oracle import e2ttt_gelu as G
+    say(f"case: e2 gelu mixer H={H} T={T} D={D} Dh={Dh} dm={dm} C={C}")
+    g = synth.gen_e2_mixer(H, T, D, dm, seed)
+    s0 = synth.gen_e2_gelu_state(H, D, Dh, seed)
+    d = {k: v.cuda() for k, v in g.items()}
+    st = {k: v.cuda().clone() for k, v in s0.items()}
+    out = tla.e2ttt_mixer_gelu_forward(d["x"], d["wqkv"], d["bias"], eta_base, alpha_base, tau, st, H, C)
+    torch.cuda.synchronize()
+    W = [{m: s0[m][h].double().numpy() for m in G.MATS} for h in range(H)]
+    M = [{m: s0["m" + m[1]][h].double().numpy() for m in G.MATS} for h in range(H)]
+    Or, Wr, Mr = G.e2_gelu_mixer(g["x"].double().numpy(), g["wqkv"].double().numpy(), g["bias"].numpy(),
+                                 eta_base, alpha_base, tau, W, M, H, D, C)
+    eo = np.max(np.abs(out.cpu().numpy().reshape(T, H, D) - Or)) / np.max(np.abs(Or))
+    ew, em = 0.0, 0.0
+    for m in G.MATS:
+        mn = "m" + m[1]
+        wg, mg = st[m].cpu().double().numpy(), st[mn].cpu().double().numpy()
+        wr = np.stack([Wr[h][m] for h in range(H)])
+        mr = np.stack([Mr[h][m] for h in range(H)])
+        w0 = s0[m].double().numpy()
+        ew = max(ew, np.max(np.abs(wg - wr)) / np.max(np.abs(wr - w0)))
+        em = max(em, np.max(np.abs(mg - mr)) / np.max(np.abs(mr)))
+    say(f"  outputs rel err {eo:.3e}  W err (of the change) {ew:.3e}  M rel err {em:.3e}")
+    return eo, ew, em
+
+
+@pytest.mark.parametrize("H,T,D,Dh,dm,C", [(3, 1000, 128, 256, 256, 256), (2, 200, 64, 64, 128, 64),
+                                           (1, 2048 + 77, 128, 128, 128, 2048)])
+def test_e2_gelu_mixer_small_and_ragged(H, T, D, Dh, dm, C):
+    eo, ew, em = run_gelu_mixer(H, T, D, Dh, dm, C, 11)
+    assert eo < 2e-2 and ew < 5e-2 and em < 5e-2
+
+
+def test_e2_gelu_mixer_full_workload():
+    c = synth.E2_GELU_CONFIG
+    eo, ew, em = run_gelu_mixer(c["heads"], c["seq"], c["dim"], c["hidden"], c["d_model"], c["chunk"], c["seed"],
+                                c["eta_base"], c["alpha_base"], c["tau"])
+    assert eo < 2e-2 and ew < 5e-2 and em < 5e-2
+
+
 # ------------------------------------------------- hybrid token-mixer block
 def run_hybrid(H, T, D, Dh, dm, C, window, seed, eta_base, alpha_base=0.5, tau=4.0, theta=10000.0):
     """The hybrid block (e2ttt_hybrid_forward: SWA beside the TTT path, gated)
