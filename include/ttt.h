@@ -342,8 +342,10 @@ ttt_status e2ttt_mixer_gelu_forward(const void* x, const void* wqkv, const float
  * interpolated element-wise by a data-dependent gate:
  *   out = g * o_SWA + (1 - g) * o_TTT,   g = sigmoid(x wgate^T + bgate).
  * The TTT path is e2ttt_mixer_forward (Dh = 0: W1 = W, M1 = M [H, D, D];
- * W2, W3, M2, M3 unused and may be NULL) or e2ttt_mixer_swiglu_forward
- * (Dh > 0), with the same arguments and state updates. The attention uses
+ * W2, W3, M2, M3 unused and may be NULL), e2ttt_mixer_swiglu_forward
+ * (Dh > 0) or, with Dh > 0 and W3, M3 both NULL, e2ttt_mixer_gelu_forward
+ * (W1, M1 [H, Dh, D]; W2, M2 [H, D, Dh]), with the same arguments and state
+ * updates. The attention uses
  * the q, k, v columns of the same projection before the TTT path's SiLU and
  * L2 normalisation, rounded to bf16, with RoPE (half-split rotation, base
  * rope_theta > 1, positions 0 .. T-1) on q and k, scale 1/sqrt(D), causal

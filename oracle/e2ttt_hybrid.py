@@ -26,6 +26,7 @@ from __future__ import annotations
 import numpy as np
 
 from oracle.e2ttt import _bf16, e2_mixer
+from oracle.e2ttt_gelu import e2_gelu_mixer
 from oracle.e2ttt_mlp import e2_mlp_mixer
 from oracle.ttt_e2e import rope, swa_attention
 
@@ -60,10 +61,13 @@ def gate(x, wgate, bgate):
 
 def hybrid_mixer(x, wqkv, bias, wgate, bgate, eta_base, alpha_base, tau, rope_theta, window, state, H, D, C):
     """The hybrid block: TTT path (state = (W, M) arrays for the linear fast
-    weight, or (W, M) lists of per-head dicts for the SwiGLU net), SWA
-    branch, gate. Returns (out [T, H, D], W, M)."""
+    weight, or (W, M) lists of per-head dicts for the SwiGLU net, keys w1,
+    w2, w3, or the GELU net, keys w1, w2), SWA branch, gate. Returns
+    (out [T, H, D], W, M)."""
     W, M = state
-    if isinstance(W, list):
+    if isinstance(W, list) and "w3" not in W[0]:
+        o_ttt, W, M = e2_gelu_mixer(x, wqkv, bias, eta_base, alpha_base, tau, W, M, H, D, C)
+    elif isinstance(W, list):
         o_ttt, W, M = e2_mlp_mixer(x, wqkv, bias, eta_base, alpha_base, tau, W, M, H, D, C)
     else:
         o_ttt, W, M = e2_mixer(x, wqkv, bias, eta_base, alpha_base, tau, W, M, H, D, C)

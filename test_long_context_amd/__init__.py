@@ -352,14 +352,17 @@ def e2ttt_mixer_gelu_forward(x, wqkv, bias, eta_base, alpha_base, tau, state: di
 def e2ttt_hybrid_forward(x, wqkv, bias, wgate, bgate, eta_base, alpha_base, tau, rope_theta, window: int,
                          state: dict, heads: int, chunk: int, out=None, stream=None):
     """Hybrid token-mixer block (see include/ttt.h): state is dict(W, M)
-    (linear fast weight) or dict(w1, w2, w3, m1, m2, m3) (SwiGLU net),
-    updated in place. Returns out [T, H D]."""
+    (linear fast weight), dict(w1, w2, w3, m1, m2, m3) (SwiGLU net) or
+    dict(w1, w2, m1, m2) (GELU net), updated in place. Returns out [T, H D]."""
     import torch
     T, dm = x.shape
     if "W" in state:
         H, D, _ = state["W"].shape
         Dh = 0
         ptrs = [_ptr(state["W"]), 0, 0, _ptr(state["M"]), 0, 0]
+    elif "w3" not in state:
+        H, Dh, D = state["w1"].shape
+        ptrs = [_ptr(state["w1"]), _ptr(state["w2"]), 0, _ptr(state["m1"]), _ptr(state["m2"]), 0]
     else:
         H, Dh, D = state["w1"].shape
         ptrs = [_ptr(state[n]) for n in ("w1", "w2", "w3", "m1", "m2", "m3")]

@@ -1434,8 +1434,10 @@ extern "C" ttt_status e2ttt_hybrid_forward(const void* x, const void* wqkv, cons
   if (r != TTT_OK) return r;
   if (!wgate || !bgate || ((uintptr_t)wgate & 15) || window < 1 || !(rope_theta > 1.f) || Dh < 0)
     return TTT_ERR_INVALID_ARG;
+  // Dh > 0 with W3 and M3 both null: the GELU net (W1 [H, Dh, D], W2 [H, D, Dh])
+  const bool gelu = Dh > 0 && !W3 && !M3;
   if (Dh > 0) {
-    if ((r = swiglu_check(W1, W2, W3, M1, M2, M3, Dh)) != TTT_OK) return r;
+    if ((r = gelu ? gelu_check(W1, W2, M1, M2, Dh) : swiglu_check(W1, W2, W3, M1, M2, M3, Dh)) != TTT_OK) return r;
   } else if (!W1 || !M1 || ((uintptr_t)W1 & 15) || ((uintptr_t)M1 & 15)) {
     return TTT_ERR_INVALID_ARG;
   }
@@ -1443,14 +1445,19 @@ extern "C" ttt_status e2ttt_hybrid_forward(const void* x, const void* wqkv, cons
   if ((int64_t)hybrid_cap(T) * D * 2 >= (int64_t(1) << 31)) return TTT_ERR_UNSUPPORTED;
   if ((r = device_present()) != TTT_OK) return r;
   hipStream_t st = (hipStream_t)stream;
-  const size_t base = Dh > 0 ? mlp_mixer_work_bytes(H, T, D, Dh, C) : mixer_work_bytes(H, T, D, C);
+  const size_t base = Dh > 0 ? (gelu ? gelu_mixer_work_bytes(H, T, D, Dh, C) : mlp_mixer_work_bytes(H, T, D, Dh, C))
+                             : mixer_work_bytes(H, T, D, C);
   std::lock_guard<std::mutex> lock(g_e2_mu);
   if ((r = e2_grow(base + hybrid_extra_bytes(H, T, D), st)) != TTT_OK) return r;
   // TTT path: o_TTT into out; its projections P stay at the buffer's start
-  r = Dh > 0 ? mixer_swiglu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, W3, M1, M2, M3, out, H, T, D, Dh,
-                                dm, C, g_e2.p, stream)
-             : mixer_linear_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, M1, out, H, T, D, dm, C, g_e2.p,
-                                stream);
+  if (gelu)
+    r = mixer_gelu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, M1, M2, out, H, T, D, Dh, dm, C, g_e2.p,
+                       stream);
+  else if (Dh > 0)
+    r = mixer_swiglu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, W3, M1, M2, M3, out, H, T, D, Dh, dm, C,
+                         g_e2.p, stream);
+  else
+    r = mixer_linear_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, M1, out, H, T, D, dm, C, g_e2.p, stream);
   if (r != TTT_OK) return r;
   const int64_t N = 3LL * H * D + 3LL * H, HD = (int64_t)H * D, cap = hybrid_cap(T);
   const float* P = (const float*)(((uintptr_t)g_e2.p + 255) & ~(uintptr_t)255);

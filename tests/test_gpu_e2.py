@@ -211,11 +211,11 @@ def test_e2_gelu_mixer_full_workload():
 
 
 # ------------------------------------------------- hybrid token-mixer block
-def run_hybrid(H, T, D, Dh, dm, C, window, seed, eta_base, alpha_base=0.5, tau=4.0, theta=10000.0):
+def run_hybrid(H, T, D, Dh, dm, C, window, seed, eta_base, alpha_base=0.5, tau=4.0, theta=10000.0, net="swiglu"):
     """The hybrid block (e2ttt_hybrid_forward: SWA beside the TTT path, gated)
     against the float64 oracle. Errors as for the mixers: outputs and momenta
-    max |x - ref| / max |ref|; weights relative to their change (SwiGLU) or
-    to max |W| (linear)."""
+    max |x - ref| / max |ref|; weights relative to their change (SwiGLU,
+    GELU nets) or to max |W| (linear). net: the fast-weight net for Dh > 0."""
     import test_long_context_amd as tla
     from oracle import e2ttt_hybrid as Y
     from oracle import e2ttt_mlp as X
@@ -223,10 +223,11 @@ def run_hybrid(H, T, D, Dh, dm, C, window, seed, eta_base, alpha_base=0.5, tau=4
     g = synth.gen_e2_mixer(H, T, D, dm, seed)
     gt = synth.gen_gate(H, D, dm, seed)
     d = {k: v.cuda() for k, v in g.items()}
+    mats = ("w1", "w2") if net == "gelu" else X.MATS
     if Dh:
-        s0 = synth.gen_e2_mlp_state(H, D, Dh, seed)
-        W = [{m: s0[w][h].double().numpy() for m, w in zip(X.MATS, ("w1", "w2", "w3"))} for h in range(H)]
-        M = [{m: s0[w][h].double().numpy() for m, w in zip(X.MATS, ("m1", "m2", "m3"))} for h in range(H)]
+        s0 = (synth.gen_e2_gelu_state if net == "gelu" else synth.gen_e2_mlp_state)(H, D, Dh, seed)
+        W = [{m: s0[m][h].double().numpy() for m in mats} for h in range(H)]
+        M = [{m: s0["m" + m[1]][h].double().numpy() for m in mats} for h in range(H)]
     else:
         s0 = dict(W=g["W"], M=g["M"])
         W, M = g["W"].double().numpy(), g["M"].double().numpy()
@@ -240,7 +241,8 @@ def run_hybrid(H, T, D, Dh, dm, C, window, seed, eta_base, alpha_base=0.5, tau=4
     eo = np.max(np.abs(out.cpu().numpy().reshape(T, H, D) - Or)) / np.max(np.abs(Or))
     if Dh:
         ew = em = 0.0
-        for m, wn, mn in zip(X.MATS, ("w1", "w2", "w3"), ("m1", "m2", "m3")):
+        for m in mats:
+            wn, mn = m, "m" + m[1]
             wr = np.stack([Wr[h][m] for h in range(H)])
             mr = np.stack([Mr[h][m] for h in range(H)])
             ew = max(ew, np.max(np.abs(st[wn].cpu().double().numpy() - wr)) /
@@ -258,6 +260,13 @@ def run_hybrid(H, T, D, Dh, dm, C, window, seed, eta_base, alpha_base=0.5, tau=4
                                                       (1, 2048 + 77, 128, 128, 128, 2048, 1024, 3e-4)])
 def test_e2_hybrid_small_and_ragged(H, T, D, Dh, dm, C, window, eta):
     eo, ew, em = run_hybrid(H, T, D, Dh, dm, C, window, 10, eta)
+    assert eo < 2e-2 and ew < 5e-2 and em < 5e-2
+
+
+@pytest.mark.parametrize("H,T,D,Dh,dm,C,window", [(2, 300, 64, 64, 128, 64, 48),
+                                                  (1, 2048 + 77, 128, 128, 128, 2048, 1024)])
+def test_e2_hybrid_with_gelu_net(H, T, D, Dh, dm, C, window):
+    eo, ew, em = run_hybrid(H, T, D, Dh, dm, C, window, 12, 3e-4, net="gelu")
     assert eo < 2e-2 and ew < 5e-2 and em < 5e-2
 
 
