@@ -17,11 +17,14 @@
 // writing its own partial dq; the consumer adds the parts in a fixed order.
 //
 // dK, dV: a workgroup holds 128 keys of one key head (32 per wave, K and V
-// rows in registers) for one query head of the group (grid z); query tiles of
-// 64 (Q and dO rows, plus their lse and D) stream through LDS. S = Q K^T and
-// dP = dO V^T have one key per lane column; dV^T = dO^T P and dK^T = Q^T dS
-// read dO^T and Q^T through the transposing LDS read. Each query head writes
-// its own partial dk, dv.
+// rows in registers) and walks a run of that key block's (query head, query
+// tile) pairs; query tiles of 64 (Q and dO rows, plus their lse and D) stream
+// through LDS. S = Q K^T and dP = dO V^T have one key per lane column;
+// dV^T = dO^T P and dK^T = Q^T dS read dO^T and Q^T through the transposing
+// LDS read. The first key block of a call is seen by every later query, the
+// last by its own few, so each block's pairs are cut into runs of about equal
+// length (at most one run length for the whole call, chosen so that all runs
+// fit on the CUs at once); each run writes its own partial dk, dv.
 //
 // Contraction slots of the P / dS operands follow the accumulator layout:
 // slot 8 g + e of lane group g (= lane / 32) is row 16 u + 4 g + e (e < 4) or
@@ -247,8 +250,63 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq2_kernel(AttnArgs a, int ks
 }
 
 // --------------------------------------------------------------- dK, dV
+// Query tiles seen by key block kb (keys 128 kb .. 128 kb + 127): from the
+// block's first key up to the last query that sees its last key.
+__host__ __device__ inline int kv_block_tiles(int n, int window, int kb) {
+  const int k0 = kb * 128;
+  const int64_t q_end = (int64_t)k0 + 127 + window < (int64_t)n ? (int64_t)k0 + 127 + window : (int64_t)n;
+  return (int)((q_end - k0 + BT - 1) / BT);
+}
+
+namespace {
+struct KvSched {
+  int run;    // longest run of (query head, query tile) pairs per workgroup
+  int parts;  // partial sums per key
+  int jobs;   // workgroups per key head
+};
+constexpr int KV_SLOTS = 256;  // one dK/dV workgroup per CU (448 registers per lane)
+
+KvSched kv_sched(const AttnArgs& a) {
+  const int grp = a.H / a.Hk, nkb = (a.n + 127) / 128;
+  int maxt = 0;
+  for (int kb = 0; kb < nkb; ++kb) maxt = max(maxt, grp * kv_block_tiles(a.n, a.window, kb));
+  auto jobs_for = [&](int run, int* parts) {
+    int j = 0, p = 1;
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int c = (grp * kv_block_tiles(a.n, a.window, kb) + run - 1) / run;
+      j += c;
+      p = max(p, c);
+    }
+    *parts = p;
+    return j;
+  };
+  KvSched s{maxt, 1, nkb};
+  if ((long)nkb * a.Hk >= KV_SLOTS) {
+    // the key blocks alone fill the CUs: one run per query head
+    s.run = (maxt + grp - 1) / grp;
+    s.jobs = jobs_for(s.run, &s.parts);
+    return s;
+  }
+  // shortest run whose workgroups all fit at once, with at most
+  // max(H / Hk, ATTN_BWD2_MAX_KV_PARTS) runs per key block (one run per
+  // query head of the group is always among the candidates)
+  const int maxp = max(grp, ATTN_BWD2_MAX_KV_PARTS);
+  for (int run = max(1, (maxt + maxp - 1) / maxp); run <= maxt; ++run) {
+    int parts = 1;
+    const int j = jobs_for(run, &parts);
+    if ((long)j * a.Hk <= KV_SLOTS || run == maxt) {
+      s.run = run;
+      s.parts = parts;
+      s.jobs = j;
+      break;
+    }
+  }
+  return s;
+}
+}  // namespace
+
 template <int DH>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a, int run, int parts) {
   constexpr int KS = DH / 16, DB = DH / 32, KV = DH / 8;
   constexpr int NI = BT * DH * 2 / 1024;
   __shared__ __attribute__((aligned(1024))) bf16 Qs0[BT * DH];
@@ -260,21 +318,30 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
   const int grp = a.H / a.Hk;
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin; remap so
   // that each XCD takes a contiguous range of logical blocks ordered key head,
-  // query head, key block. The key blocks of a query head then read that
-  // head's query and output-gradient rows through one L2.
-  int kh, hq, kb;
+  // key block, run. The runs of a key head then read that head's query and
+  // output-gradient rows through one L2.
+  int kh, kb, ch, nch, tasks;
   {
-    const int nkb = gridDim.x;
-    const int nwg = gridDim.x * gridDim.y * gridDim.z;
-    int id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int nwg = gridDim.x;
+    int id = blockIdx.x;
     if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
-    const int per_kh = grp * nkb;
-    kh = id / per_kh;
-    const int rem = id % per_kh;
-    hq = rem / nkb;
-    kb = rem % nkb;
+    const int jobs = nwg / a.Hk;
+    kh = id / jobs;
+    int job = id % jobs;
+    const int nkb = (a.n + 127) / 128;
+    kb = 0;
+    nch = 1;
+    tasks = grp;
+    for (; kb < nkb; ++kb) {
+      tasks = grp * kv_block_tiles(a.n, a.window, kb);
+      nch = (tasks + run - 1) / run;
+      if (job < nch) break;
+      job -= nch;
+    }
+    ch = job;
   }
-  const int h = kh * grp + hq;
+  const int ntile = tasks / grp;  // query tiles per head of this key block
+  const int t_beg = (int)((long)ch * tasks / nch), t_end = (int)((long)(ch + 1) * tasks / nch);
   const int k0 = kb * 128;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
@@ -312,11 +379,13 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
 
   const __amdgpu_buffer_rsrc_t rq = rsrc_b(a.q, (uint64_t)a.n * a.H * DH * 2);
   const __amdgpu_buffer_rsrc_t ro = rsrc_b(a.dO, (uint64_t)a.n * a.H * DH * 2);
-  const int q_end = (int)min((int64_t)a.n, (int64_t)k0 + 127 + a.window);  // exclusive
   const float sc2 = a.scale * LOG2E_B;
   const int wk_lo = kw, wk_hi = min(kw + 32, a.n) - 1;
 
-  auto dma_tile = [&](int qt, bf16* qdst, bf16* odst, float* lsd, float* Dd) {
+  // pair t of the run: query head t / ntile of the group, query tile
+  // k0 + 64 (t % ntile)
+  auto dma_tile = [&](int t, bf16* qdst, bf16* odst, float* lsd, float* Dd) {
+    const int h = kh * grp + t / ntile, qt = k0 + BT * (t % ntile);
 #pragma unroll
     for (int i = 0; i < NI / 4; ++i) {
       const int jj = wid + 4 * i;
@@ -334,9 +403,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
     }
   };
 
-  auto tile = [&](int qt, const bf16* qs_, const bf16* os_, const float* lsc, const float* Dc, bf16* qn, bf16* on,
+  auto tile = [&](int t, const bf16* qs_, const bf16* os_, const float* lsc, const float* Dc, bf16* qn, bf16* on,
                   float* lsn, float* Dn) {
-    if (qt + BT < q_end) dma_tile(qt + BT, qn, on, lsn, Dn);
+    if (t + 1 < t_end) dma_tile(t + 1, qn, on, lsn, Dn);
+    const int qt = k0 + BT * (t % ntile);
     // key t sees query i iff t <= i < t + window
     const bool any = wk_lo < a.n && (qt + BT - 1 >= wk_lo) && (qt <= wk_hi + a.window - 1);
     const bool full = (qt >= wk_hi) && (qt + BT - 1 <= wk_lo + a.window - 1) && (qt + BT <= a.n);
@@ -388,17 +458,18 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
     __syncthreads();
   };
 
-  if (k0 < q_end) dma_tile(k0, Qs0, Os0, ls0, Ds0);
+  if (t_beg < t_end) dma_tile(t_beg, Qs0, Os0, ls0, Ds0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int qt = k0; qt < q_end; qt += 2 * BT) {
-    tile(qt, Qs0, Os0, ls0, Ds0, Qs1, Os1, ls1, Ds1);
-    if (qt + BT >= q_end) break;
-    tile(qt + BT, Qs1, Os1, ls1, Ds1, Qs0, Os0, ls0, Ds0);
+  for (int t = t_beg; t < t_end; t += 2) {
+    tile(t, Qs0, Os0, ls0, Ds0, Qs1, Os1, ls1, Ds1);
+    if (t + 1 >= t_end) break;
+    tile(t + 1, Qs1, Os1, ls1, Ds1, Qs0, Os0, ls0, Ds0);
   }
 
   if (key < a.n) {
-    const long base = (long)hq * a.n * a.Hk * DH + ((long)key * a.Hk + kh) * DH;
+    const long kstride = (long)a.n * a.Hk * DH;
+    const long base = (long)ch * kstride + ((long)key * a.Hk + kh) * DH;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -418,6 +489,23 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a) {
           *(floatx4*)(a.dv + o) = wv;
         }
       }
+    // the block's first run clears the parts no run of this block writes
+    if (ch == 0)
+      for (int p = nch; p < parts; ++p)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            const long o = (long)p * kstride + ((long)key * a.Hk + kh) * DH + db * 32 + 8 * jg + 4 * lg;
+            if (a.parts_bf16) {
+              const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+              *(bf16x4*)((bf16*)a.dk + o) = z;
+              *(bf16x4*)((bf16*)a.dv + o) = z;
+            } else {
+              *(floatx4*)(a.dk + o) = floatx4{0.f, 0.f, 0.f, 0.f};
+              *(floatx4*)(a.dv + o) = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
   }
 }
 
@@ -445,7 +533,7 @@ int attn_bwd2_dq_parts(const AttnArgs& a) {
   return best;
 }
 
-int attn_bwd2_kv_parts(const AttnArgs& a) { return a.H / a.Hk; }
+int attn_bwd2_kv_parts(const AttnArgs& a) { return a.n > 0 ? kv_sched(a).parts : 1; }
 
 hipError_t attn_bwd_dq2(DT dt, const AttnArgs& a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
@@ -460,9 +548,10 @@ hipError_t attn_bwd_dq2(DT dt, const AttnArgs& a, hipStream_t st) {
 hipError_t attn_bwd_dkdv2(DT dt, const AttnArgs& a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
   if (!attn_bwd2_supported(dt, a)) return hipErrorInvalidValue;
-  const dim3 grid((a.n + 127) / 128, a.Hk, a.H / a.Hk);
-  if (a.dh == 128) hipLaunchKernelGGL(attn_bwd_dkdv2_kernel<128>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(attn_bwd_dkdv2_kernel<64>, grid, dim3(256), 0, st, a);
+  const KvSched s = kv_sched(a);
+  const dim3 grid((unsigned)(s.jobs * a.Hk));
+  if (a.dh == 128) hipLaunchKernelGGL(attn_bwd_dkdv2_kernel<128>, grid, dim3(256), 0, st, a, s.run, s.parts);
+  else hipLaunchKernelGGL(attn_bwd_dkdv2_kernel<64>, grid, dim3(256), 0, st, a, s.run, s.parts);
   return hipGetLastError();
 }
 

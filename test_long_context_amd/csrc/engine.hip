@@ -397,6 +397,12 @@ inline void* sq(void* p, int j, size_t per, size_t es) {
   return p ? (void*)((char*)p + (size_t)j * per * es) : nullptr;
 }
 inline float* sqf(float* p, int j, size_t per) { return p ? p + (size_t)j * per : nullptr; }
+// floats of one sequence's dk (or dv) partial sums: up to
+// ATTN_BWD2_MAX_KV_PARTS parts of the second-generation backward, H / Hk of
+// the first
+inline size_t kv_part_elems(const ttt_ctx* c) {
+  return (size_t)std::max(c->H / c->Hk, ATTN_BWD2_MAX_KV_PARTS) * c->b * c->Hk * c->dh;
+}
 
 AttnArgs attn_args(ttt_ctx* c, int l, int j, const void* q, void* o, float* lse, int n, int64_t p0) {
   AttnArgs a{};
@@ -752,8 +758,8 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         a.dO = dO;
         a.D = D;
         a.dq = sqf(c->dq, j, (size_t)ATTN_BWD2_MAX_DQ_PARTS * c->b * H * dh);
-        a.dk = sqf(c->dk, j, (size_t)H * c->b * dh);
-        a.dv = sqf(c->dv, j, (size_t)H * c->b * dh);
+        a.dk = sqf(c->dk, j, kv_part_elems(c));
+        a.dv = sqf(c->dv, j, kv_part_elems(c));
         int qp = 1, kp = 1;
         const bool bwd2 = attn_bwd2_supported(c->dt, a);
         // the second-generation kernels' partial sums in bf16 (like the
@@ -1025,13 +1031,13 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
   A(&c->dO, (size_t)b * c->H * c->dh * es);
   Af(&c->Dbuf, (size_t)c->H * b);
   // room for the partial sums of the second-generation backward (at most
-  // ATTN_BWD2_MAX_DQ_PARTS key splits of dq; one dk / dv part per query head
-  // of a group)
+  // ATTN_BWD2_MAX_DQ_PARTS key splits of dq, ATTN_BWD2_MAX_KV_PARTS runs of
+  // dk / dv)
   Af(&c->dq, (size_t)ATTN_BWD2_MAX_DQ_PARTS * b * c->H * c->dh);
   Af(&c->apart, (size_t)4 * b * c->H * c->dh);
   Af(&c->aml, (size_t)4 * 2 * c->H * b);
-  Af(&c->dk, (size_t)(c->H / c->Hk) * b * c->Hk * c->dh);
-  Af(&c->dv, (size_t)(c->H / c->Hk) * b * c->Hk * c->dh);
+  Af(&c->dk, (size_t)c->B * kv_part_elems(c));
+  Af(&c->dv, (size_t)c->B * kv_part_elems(c));
   A(&c->dqkv, (size_t)b * c->QKV * es);
   c->ghd_t.assign(nd, nullptr);
   c->dh12d.assign(nd, nullptr);

@@ -145,13 +145,18 @@ hipError_t attn_bwd_dq(DT dt, const AttnArgs& a, hipStream_t st);
 hipError_t attn_bwd_dkdv(DT dt, const AttnArgs& a, hipStream_t st);
 // Second-generation backward (bf16, head_dim 64/128). dq receives
 // attn_bwd2_dq_parts(a) partial sums ([parts][n][H][dh]); dk and dv receive
-// attn_bwd2_kv_parts(a) = H / Hk partial sums ([parts][n][Hk][dh]), one per
-// query head of the group.
+// attn_bwd2_kv_parts(a) partial sums ([parts][n][Hk][dh]): each 128-key
+// block's (query head, query tile) pairs are cut into at most
+// max(H / Hk, ATTN_BWD2_MAX_KV_PARTS) runs of about equal length, one
+// workgroup and one part each (parts a block's runs do not reach are written
+// as zeros).
 bool attn_bwd2_supported(DT dt, const AttnArgs& a);
 int attn_bwd2_dq_parts(const AttnArgs& a);
 // Upper bound of attn_bwd2_dq_parts().
 constexpr int ATTN_BWD2_MAX_DQ_PARTS = 8;
 int attn_bwd2_kv_parts(const AttnArgs& a);
+// attn_bwd2_kv_parts() <= max(H / Hk, ATTN_BWD2_MAX_KV_PARTS).
+constexpr int ATTN_BWD2_MAX_KV_PARTS = 8;
 hipError_t attn_bwd_dq2(DT dt, const AttnArgs& a, hipStream_t st);
 hipError_t attn_bwd_dkdv2(DT dt, const AttnArgs& a, hipStream_t st);
 // dst[i] = sum_p parts[p * count + i]
