@@ -250,14 +250,6 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq2_kernel(AttnArgs a, int ks
 }
 
 // --------------------------------------------------------------- dK, dV
-// Query tiles seen by key block kb (keys 128 kb .. 128 kb + 127): from the
-// block's first key up to the last query that sees its last key.
-__host__ __device__ inline int kv_block_tiles(int n, int window, int kb) {
-  const int k0 = kb * 128;
-  const int64_t q_end = (int64_t)k0 + 127 + window < (int64_t)n ? (int64_t)k0 + 127 + window : (int64_t)n;
-  return (int)((q_end - k0 + BT - 1) / BT);
-}
-
 namespace {
 struct KvSched {
   int run;    // longest run of (query head, query tile) pairs per workgroup
@@ -269,11 +261,11 @@ constexpr int KV_SLOTS = 256;  // one dK/dV workgroup per CU (448 registers per 
 KvSched kv_sched(const AttnArgs& a) {
   const int grp = a.H / a.Hk, nkb = (a.n + 127) / 128;
   int maxt = 0;
-  for (int kb = 0; kb < nkb; ++kb) maxt = max(maxt, grp * kv_block_tiles(a.n, a.window, kb));
+  for (int kb = 0; kb < nkb; ++kb) maxt = max(maxt, grp * attn_bwd2_kv_block_tiles(a.n, a.window, kb));
   auto jobs_for = [&](int run, int* parts) {
     int j = 0, p = 1;
     for (int kb = 0; kb < nkb; ++kb) {
-      const int c = (grp * kv_block_tiles(a.n, a.window, kb) + run - 1) / run;
+      const int c = (grp * attn_bwd2_kv_block_tiles(a.n, a.window, kb) + run - 1) / run;
       j += c;
       p = max(p, c);
     }
@@ -333,7 +325,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a, int run
     nch = 1;
     tasks = grp;
     for (; kb < nkb; ++kb) {
-      tasks = grp * kv_block_tiles(a.n, a.window, kb);
+      tasks = grp * attn_bwd2_kv_block_tiles(a.n, a.window, kb);
       nch = (tasks + run - 1) / run;
       if (job < nch) break;
       job -= nch;
@@ -490,7 +482,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv2_kernel(AttnArgs a, int run
         }
       }
     // the block's first run clears the parts no run of this block writes
-    if (ch == 0)
+    // (for consumers that add all parts of every key)
+    if (a.kv_fill && ch == 0)
       for (int p = nch; p < parts; ++p)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -534,6 +527,7 @@ int attn_bwd2_dq_parts(const AttnArgs& a) {
 }
 
 int attn_bwd2_kv_parts(const AttnArgs& a) { return a.n > 0 ? kv_sched(a).parts : 1; }
+int attn_bwd2_kv_run(const AttnArgs& a) { return a.n > 0 ? kv_sched(a).run : 1; }
 
 hipError_t attn_bwd_dq2(DT dt, const AttnArgs& a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;

@@ -509,10 +509,18 @@ hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, in
 }
 
 // Transpose of the rotation (rotation by -angle) for dq, dk; dv copied.
+// Partial sums of dk, dv at position t: kv_parts, or with kv_run > 0 those
+// of t's key block in the dK / dV kernel's runs.
+__device__ __forceinline__ int rope_kv_parts(int kv_parts, int kv_run, int kv_window, int n, int H, int Hk, int t) {
+  return kv_run > 0 ? attn_bwd2_kv_block_parts(n, kv_window, H / Hk, kv_run, t >> 7) : kv_parts;
+}
+
 template <typename T, typename PT>
-__global__ void rope_bwd_generic_kernel(const PT* dq, int dq_parts, const PT* dk, const PT* dv, int kv_parts,
-                                int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, T* out) {
+__global__ void rope_bwd_generic_kernel(const PT* dq, int dq_parts, const PT* dk, const PT* dv, int kv_parts_all,
+                                        int kv_run, int kv_window, int n, int H, int Hk, int dh, int64_t pos0,
+                                        const float2* tab, T* out) {
   const int t = blockIdx.x;
+  const int kv_parts = rope_kv_parts(kv_parts_all, kv_run, kv_window, n, H, Hk, t);
   const int half = dh / 2;
   const int W = (H + 2 * Hk) * dh;
   const long qstride = (long)n * H * dh, kstride = (long)n * Hk * dh;
@@ -548,9 +556,10 @@ __global__ void rope_bwd_generic_kernel(const PT* dq, int dq_parts, const PT* dk
 constexpr int ROPE_BKR = 2, ROPE_BNP = 8;
 template <typename T, typename PT>
 __global__ void __launch_bounds__(RB) rope_bwd_kernel(const PT* dq, int dq_parts, const PT* dk, const PT* dv,
-                                                      int kv_parts, int n, int H, int Hk, int dh, int64_t pos0,
-                                                      const float2* tab, T* out) {
+                                                      int kv_parts_all, int kv_run, int kv_window, int n, int H,
+                                                      int Hk, int dh, int64_t pos0, const float2* tab, T* out) {
   const int t = blockIdx.x;
+  const int kv_parts = rope_kv_parts(kv_parts_all, kv_run, kv_window, n, H, Hk, t);
   const int half = dh / 2;
   const int W = (H + 2 * Hk) * dh;
   const long qstride = (long)n * H * dh, kstride = (long)n * Hk * dh;
@@ -612,39 +621,39 @@ __global__ void __launch_bounds__(RB) rope_bwd_kernel(const PT* dq, int dq_parts
 
 template <typename PT>
 static hipError_t rope_bwd_pack_t(DT dt, const PT* dq, int dq_parts, const PT* dk, const PT* dv, int kv_parts,
-                         int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
-                         hipStream_t st) {
+                                  int kv_run, int kv_window, int n, int H, int Hk, int dh, int64_t pos0,
+                                  const float2* tab, void* dqkv, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   const bool vec = dh % 8 == 0 && (H + Hk) * (dh / 8) <= ROPE_BKR * RB && Hk * dh / 4 <= RB && dq_parts >= 1 &&
                    dq_parts <= ROPE_BNP && kv_parts >= 1 && kv_parts <= ROPE_BNP;
   if (dt == DT::BF16) {
     if (vec)
-      hipLaunchKernelGGL((rope_bwd_kernel<bf16, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H, Hk,
-                         dh, pos0, tab, (bf16*)dqkv);
-    else
-      hipLaunchKernelGGL((rope_bwd_generic_kernel<bf16, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n,
+      hipLaunchKernelGGL((rope_bwd_kernel<bf16, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, kv_run, kv_window, n,
                          H, Hk, dh, pos0, tab, (bf16*)dqkv);
+    else
+      hipLaunchKernelGGL((rope_bwd_generic_kernel<bf16, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, kv_run,
+                         kv_window, n, H, Hk, dh, pos0, tab, (bf16*)dqkv);
   } else {
     if (vec)
-      hipLaunchKernelGGL((rope_bwd_kernel<float, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, n, H,
-                         Hk, dh, pos0, tab, (float*)dqkv);
+      hipLaunchKernelGGL((rope_bwd_kernel<float, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts, kv_run, kv_window, n,
+                         H, Hk, dh, pos0, tab, (float*)dqkv);
     else
       hipLaunchKernelGGL((rope_bwd_generic_kernel<float, PT>), dim3(n), dim3(RB), 0, st, dq, dq_parts, dk, dv, kv_parts,
-                         n, H, Hk, dh, pos0, tab, (float*)dqkv);
+                         kv_run, kv_window, n, H, Hk, dh, pos0, tab, (float*)dqkv);
   }
   return hipGetLastError();
 }
 
 hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
-                         int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
-                         hipStream_t st) {
-  return rope_bwd_pack_t(dt, dq, dq_parts, dk, dv, kv_parts, n, H, Hk, dh, pos0, tab, dqkv, st);
+                         int kv_run, int kv_window, int n, int H, int Hk, int dh, int64_t pos0, const float2* tab,
+                         void* dqkv, hipStream_t st) {
+  return rope_bwd_pack_t(dt, dq, dq_parts, dk, dv, kv_parts, kv_run, kv_window, n, H, Hk, dh, pos0, tab, dqkv, st);
 }
 
 hipError_t rope_bwd_pack(DT dt, const bf16* dq, int dq_parts, const bf16* dk, const bf16* dv, int kv_parts,
-                         int n, int H, int Hk, int dh, int64_t pos0, const float2* tab, void* dqkv,
-                         hipStream_t st) {
-  return rope_bwd_pack_t(dt, dq, dq_parts, dk, dv, kv_parts, n, H, Hk, dh, pos0, tab, dqkv, st);
+                         int kv_run, int kv_window, int n, int H, int Hk, int dh, int64_t pos0, const float2* tab,
+                         void* dqkv, hipStream_t st) {
+  return rope_bwd_pack_t(dt, dq, dq_parts, dk, dv, kv_parts, kv_run, kv_window, n, H, Hk, dh, pos0, tab, dqkv, st);
 }
 
 __global__ void sum_parts_kernel(const float* parts, int nparts, long count, float* dst) {

@@ -760,7 +760,7 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         a.dq = sqf(c->dq, j, (size_t)ATTN_BWD2_MAX_DQ_PARTS * c->b * H * dh);
         a.dk = sqf(c->dk, j, kv_part_elems(c));
         a.dv = sqf(c->dv, j, kv_part_elems(c));
-        int qp = 1, kp = 1;
+        int qp = 1, kp = 1, krun = 0;
         const bool bwd2 = attn_bwd2_supported(c->dt, a);
         // the second-generation kernels' partial sums in bf16 (like the
         // split-K data-gradient products'): the RoPE backward that adds
@@ -769,6 +769,7 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
         if (bwd2) {
           qp = attn_bwd2_dq_parts(a);
           kp = attn_bwd2_kv_parts(a);
+          krun = attn_bwd2_kv_run(a);
           TCALL(KC_AB, 4.0 * H * dh * window_pairs(a0, n, c->k), 0, attn_bwd_dq2(c->dt, a, st));
         if (c->upd_at_attn && !upd_done && j == B - 1) {
           RUN(launch_update(c, i, a0, n, st, c->upd_split ? 2 : 3));
@@ -780,10 +781,10 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
           TCALL(KC_AB, 4.0 * H * dh * 0.5 * n * (n + 1.0), 0, attn_bwd_dkdv(c->dt, a, st));
         }
         if (a.parts_bf16)
-          TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, (const __bf16*)a.dq, qp, (const __bf16*)a.dk, (const __bf16*)a.dv, kp, n, H,
+          TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, (const __bf16*)a.dq, qp, (const __bf16*)a.dk, (const __bf16*)a.dv, kp, krun, a.window, n, H,
                                            Hk, dh, a0, c->rope, sq(c->dqkv, j, (size_t)n * QKV, es), st));
         else
-          TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, a.dq, qp, a.dk, a.dv, kp, n, H, Hk, dh, a0, c->rope,
+          TCALL(KC_OT, 0, 0, rope_bwd_pack(c->dt, a.dq, qp, a.dk, a.dv, kp, krun, a.window, n, H, Hk, dh, a0, c->rope,
                                            sq(c->dqkv, j, (size_t)n * QKV, es), st));
       }
       if (c->upd_at_attn && !upd_done) RUN(launch_update(c, i, a0, n, st, c->upd_split ? 2 : 3));

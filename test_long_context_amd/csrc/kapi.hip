@@ -183,6 +183,7 @@ extern "C" ttt_status tttk_attn_bwd(int32_t dtype, const void* q, const void* k,
     if (n == 0) return TTT_OK;
     if (!work || !al16(work)) return TTT_ERR_INVALID_ARG;
     const int qp = attn_bwd2_dq_parts(a), kp = attn_bwd2_kv_parts(a);
+    a.kv_fill = true;  // the part sums below add every part of every key
     float* wq = (float*)work;
     float* wk = wq + (long)qp * n * H * dh;
     float* wv = wk + (long)kp * n * Hk * dh;

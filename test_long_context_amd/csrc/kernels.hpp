@@ -67,14 +67,16 @@ hipError_t rope_scatter(DT dt, const void* qkv, int n, int H, int Hk, int dh, in
                         const float2* rope_tab, void* q, void* kstore, void* vstore, void* vtstore,
                         int cap, int64_t min_store_pos, hipStream_t st);
 // dQKV (T) [n, (H+2Hk) dh] from dq [n, H dh] (float), dk, dv [n, Hk dh]
-// (float): inverse rotation of dq and dk.
-hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts, int n, int H,
-                         int Hk, int dh, int64_t pos0, const float2* rope_tab, void* dqkv,
-                         hipStream_t st);
+// (float): inverse rotation of dq and dk. dq_parts partial sums of dq;
+// kv_parts of dk and dv, or, with kv_run > 0, attn_bwd2_kv_block_parts(n,
+// kv_window, H / Hk, kv_run, t / 128) of those of position t.
+hipError_t rope_bwd_pack(DT dt, const float* dq, int dq_parts, const float* dk, const float* dv, int kv_parts,
+                         int kv_run, int kv_window, int n, int H, int Hk, int dh, int64_t pos0,
+                         const float2* rope_tab, void* dqkv, hipStream_t st);
 // The same from bf16 partial sums.
-hipError_t rope_bwd_pack(DT dt, const __bf16* dq, int dq_parts, const __bf16* dk, const __bf16* dv, int kv_parts, int n, int H,
-                         int Hk, int dh, int64_t pos0, const float2* rope_tab, void* dqkv,
-                         hipStream_t st);
+hipError_t rope_bwd_pack(DT dt, const __bf16* dq, int dq_parts, const __bf16* dk, const __bf16* dv, int kv_parts,
+                         int kv_run, int kv_window, int n, int H, int Hk, int dh, int64_t pos0,
+                         const float2* rope_tab, void* dqkv, hipStream_t st);
 // Fused softmax cross-entropy over the vocabulary for rows with a target
 // (rows < nt): loss[t] = lse - z[t, label]; dz (T) = (softmax - onehot) * scale;
 // rows >= nt get dz = 0. Also flags non-finite losses in *err (bit 2).
@@ -123,6 +125,11 @@ struct AttnArgs {
   // second-generation backward: its per-part dq / dk / dv partial sums are
   // stored as bf16 (at the same element offsets, in the same buffers) when set
   bool parts_bf16;
+  // second-generation dK / dV: also write zeros into the partial sums that
+  // no run of a key block reaches (for consumers that add all
+  // attn_bwd2_kv_parts() parts of every key; the RoPE backward instead adds
+  // each key block's own attn_bwd2_kv_block_parts())
+  bool kv_fill;
   // forward key-range split (second-generation forward): ksplit parts, each
   // an unnormalised output [n, H, dh] in opart and (max, sum) in mlpart
   // [ksplit][2][H][n] (log2 domain), merged by a combine pass
@@ -157,6 +164,21 @@ constexpr int ATTN_BWD2_MAX_DQ_PARTS = 8;
 int attn_bwd2_kv_parts(const AttnArgs& a);
 // attn_bwd2_kv_parts() <= max(H / Hk, ATTN_BWD2_MAX_KV_PARTS).
 constexpr int ATTN_BWD2_MAX_KV_PARTS = 8;
+// Run length (query-tile pairs per workgroup) of the dK / dV kernel for a.
+int attn_bwd2_kv_run(const AttnArgs& a);
+// Query tiles of 64 that see key block kb (keys 128 kb .. 128 kb + 127 of a
+// call of n positions): from the block's first key up to the last query that
+// sees its last key.
+__host__ __device__ inline int attn_bwd2_kv_block_tiles(int n, int window, int kb) {
+  const int64_t k0 = (int64_t)kb * 128, lim = k0 + 127 + window;
+  const int64_t q_end = lim < (int64_t)n ? lim : (int64_t)n;
+  return (int)((q_end - k0 + 63) / 64);
+}
+// Partial sums that key block kb receives from the dK / dV kernel (runs of
+// `run` pairs over its grp query heads' tiles).
+__host__ __device__ inline int attn_bwd2_kv_block_parts(int n, int window, int grp, int run, int kb) {
+  return (grp * attn_bwd2_kv_block_tiles(n, window, kb) + run - 1) / run;
+}
 hipError_t attn_bwd_dq2(DT dt, const AttnArgs& a, hipStream_t st);
 hipError_t attn_bwd_dkdv2(DT dt, const AttnArgs& a, hipStream_t st);
 // dst[i] = sum_p parts[p * count + i]
