@@ -249,11 +249,13 @@ ttt_status ttt_timing_read(ttt_ctx* ctx, int32_t kclass, double* total_ms, int64
  * W, M: device float [H, D, D], 16-byte aligned, updated in place to the
  * state after the last chunk. D must be 128 or 64; C a multiple of 64, at
  * most 2048; T >= 1. Errors: TTT_ERR_UNSUPPORTED for other D or C,
- * TTT_ERR_INVALID_ARG for null or misaligned pointers. The call keeps one
- * device work buffer per process (grown on demand; growing it waits for the
- * calling stream), so calls must not run concurrently on different streams
- * or host threads: a later call may only start once the earlier one's work
- * on its stream is ordered before it. */
+ * TTT_ERR_INVALID_ARG for null or misaligned pointers, TTT_ERR_OOM when its
+ * work buffer cannot be had. Each call takes its own device work buffer on
+ * `stream` from the device's default memory pool (stream-ordered
+ * allocation) and gives it back on the same stream after its kernels, so
+ * calls on different streams or host threads may overlap (on different
+ * W, M). The pool keeps what is given back for later calls: its release
+ * threshold is raised on the first call on a device. */
 ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float* eta, const float* beta,
                             const float* gamma, float* W, float* M, int32_t H, int64_t T,
                             int32_t D, int32_t C, void* stream);
@@ -283,8 +285,8 @@ int64_t e2ttt_chunk_scan_noalloc_max_bytes(void);
  * with W0, M0 the state at chunk start and G_t = (W0 k_t - v_t) k_t^T:
  *   M_C = mean_t(beta_t) M0 + sum_t eta_t G_t,   W_C = W0 + M_C
  * (one update direction per chunk, no decay). Arguments, layouts and errors
- * as for e2ttt_chunk_scan without gamma; it shares that call's cached work
- * buffer, so the two must not run concurrently either. */
+ * as for e2ttt_chunk_scan without gamma, with a work buffer of its own
+ * taken in the same way. */
 ttt_status lact_chunk_scan(const void* k, const void* v, const float* eta, const float* beta, float* W,
                            float* M, int32_t H, int64_t T, int32_t D, int32_t C, void* stream);
 
@@ -301,8 +303,8 @@ ttt_status lact_chunk_scan(const void* k, const void* v, const float* eta, const
  * steps. out: device float [T, H D], o_t = W q_t with W the state at the
  * start of t's chunk; W, M: device float [H, D, D], updated in place. D 128
  * or 64, C a multiple of 64 up to 2048, dm a multiple of 8, pointers 16-byte
- * aligned. Uses (and grows) the same cached work buffer as
- * e2ttt_chunk_scan, so the two must not run concurrently. */
+ * aligned. Its work buffer is taken per call on `stream` as for
+ * e2ttt_chunk_scan. */
 ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
                                float alpha_base, float tau, float* W, float* M, float* out, int32_t H,
                                int64_t T, int32_t D, int32_t dm, int32_t C, void* stream);
@@ -319,7 +321,7 @@ ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const float* bia
  * state kept in fp32). W1, W2, M1, M2: device float [H, Dh, D]; W3, M3:
  * device float [H, D, Dh]; all updated in place. Other arguments as for
  * e2ttt_mixer_forward; Dh a multiple of 32 up to 4096 (else
- * TTT_ERR_UNSUPPORTED). Shares the same cached work buffer. */
+ * TTT_ERR_UNSUPPORTED). Work buffer per call, as for e2ttt_chunk_scan. */
 ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
                                       float alpha_base, float tau, float* W1, float* W2, float* W3, float* M1,
                                       float* M2, float* M3, float* out, int32_t H, int64_t T, int32_t D,
@@ -331,7 +333,7 @@ ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv, const flo
  * LN, loss, aggregations and outputs as for e2ttt_mixer_swiglu_forward.
  * W1, M1: device float [H, Dh, D]; W2, M2: device float [H, D, Dh]; all
  * updated in place. Other arguments, requirements and errors as for
- * e2ttt_mixer_swiglu_forward. Shares the same cached work buffer. */
+ * e2ttt_mixer_swiglu_forward (work buffer per call). */
 ttt_status e2ttt_mixer_gelu_forward(const void* x, const void* wqkv, const float* bias, float eta_base,
                                     float alpha_base, float tau, float* W1, float* W2, float* M1, float* M2,
                                     float* out, int32_t H, int64_t T, int32_t D, int32_t Dh, int32_t dm, int32_t C,
@@ -354,7 +356,7 @@ ttt_status e2ttt_mixer_gelu_forward(const void* x, const void* wqkv, const float
  * aligned); bgate: device float [H D]. out: device float [T, H D] (before
  * any output projection). Errors as for the mixer calls; a key/value store
  * slice of one head of 2^31 bytes or more (T above 2^23 for D 128) returns
- * TTT_ERR_UNSUPPORTED. Shares the same cached work buffer. */
+ * TTT_ERR_UNSUPPORTED. Work buffer per call, as for e2ttt_chunk_scan. */
 ttt_status e2ttt_hybrid_forward(const void* x, const void* wqkv, const float* bias, const void* wgate,
                                 const float* bgate, float eta_base, float alpha_base, float tau, float rope_theta,
                                 int32_t window, float* W1, float* W2, float* W3, float* M1, float* M2, float* M3,

@@ -541,13 +541,51 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
 
 // ==================================================================== C ABI
 namespace {
-struct E2Scratch {
-  void* p = nullptr;
-  size_t bytes = 0;
-  int dev = -1;
+// Device work buffer of one call: taken on the call's stream from the
+// device's default memory pool and given back on the same stream after the
+// call's kernels (stream order), so calls on different streams or host
+// threads never share one. The pool keeps what is given back for later calls
+// (its release threshold is raised once per device), so repeated calls do not
+// reach the driver.
+constexpr int E2_POOL_MAX_DEV = 64;
+bool g_pool_ready[E2_POOL_MAX_DEV] = {};
+std::mutex g_pool_mu;  // guards g_pool_ready
+
+class CallWork {
+ public:
+  CallWork() = default;
+  CallWork(const CallWork&) = delete;
+  CallWork& operator=(const CallWork&) = delete;
+  ~CallWork() {
+    if (p_) (void)hipFreeAsync(p_, st_);
+  }
+  ttt_status alloc(size_t bytes, hipStream_t st) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= E2_POOL_MAX_DEV) return TTT_ERR_HIP;
+    {
+      std::lock_guard<std::mutex> lock(g_pool_mu);
+      if (!g_pool_ready[dev]) {
+        hipMemPool_t pool = nullptr;
+        if (hipDeviceGetDefaultMemPool(&pool, dev) != hipSuccess) return TTT_ERR_HIP;
+        uint64_t keep = UINT64_MAX;
+        if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) return TTT_ERR_HIP;
+        g_pool_ready[dev] = true;
+      }
+    }
+    if (hipMallocAsync(&p_, bytes, st) != hipSuccess) {
+      (void)hipGetLastError();
+      p_ = nullptr;
+      return TTT_ERR_OOM;
+    }
+    st_ = st;
+    return TTT_OK;
+  }
+  void* get() const { return p_; }
+
+ private:
+  void* p_ = nullptr;
+  hipStream_t st_ = nullptr;
 };
-E2Scratch g_e2;
-std::mutex g_e2_mu;  // guards g_e2 on the host
 
 // Work buffer of the allocation-free entry point: a fixed device array, one
 // copy per GPU, alive until the process ends. Host code never passes the
@@ -621,26 +659,10 @@ extern "C" ttt_status e2ttt_chunk_scan(const void* k, const void* v, const float
     return TTT_ERR_NO_DEVICE;
   }
   hipStream_t st = (hipStream_t)stream;
-  const size_t need = e2_work_bytes(H, T, D, C);
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
-  // Work buffer cached per process (grown on demand, reallocated on a device change).
-  std::lock_guard<std::mutex> lock(g_e2_mu);
-  if (g_e2.bytes < need || g_e2.dev != dev) {
-    if (g_e2.p) {
-      (void)hipStreamSynchronize(st);
-      (void)hipFree(g_e2.p);
-    }
-    g_e2.p = nullptr;
-    g_e2.bytes = 0;
-    if (hipMalloc(&g_e2.p, need) != hipSuccess) {
-      (void)hipGetLastError();
-      return TTT_ERR_OOM;
-    }
-    g_e2.bytes = need;
-    g_e2.dev = dev;
-  }
-  return e2_run(k, v, eta, beta, gamma, W, M, H, T, D, C, g_e2.p, st);
+  CallWork w;
+  const ttt_status ws = w.alloc(e2_work_bytes(H, T, D, C), st);
+  if (ws != TTT_OK) return ws;
+  return e2_run(k, v, eta, beta, gamma, W, M, H, T, D, C, w.get(), st);
 }
 
 extern "C" int64_t e2ttt_chunk_scan_noalloc_max_bytes(void) { return (int64_t)E2_SCRATCH_BYTES; }
@@ -723,26 +745,10 @@ extern "C" ttt_status lact_chunk_scan(const void* k, const void* v, const float*
     return TTT_ERR_NO_DEVICE;
   }
   hipStream_t st = (hipStream_t)stream;
-  const size_t need = lact_work_bytes(H, T, D, C);
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
-  // the same cached per-process work buffer as e2ttt_chunk_scan
-  std::lock_guard<std::mutex> lock(g_e2_mu);
-  if (g_e2.bytes < need || g_e2.dev != dev) {
-    if (g_e2.p) {
-      (void)hipStreamSynchronize(st);
-      (void)hipFree(g_e2.p);
-    }
-    g_e2.p = nullptr;
-    g_e2.bytes = 0;
-    if (hipMalloc(&g_e2.p, need) != hipSuccess) {
-      (void)hipGetLastError();
-      return TTT_ERR_OOM;
-    }
-    g_e2.bytes = need;
-    g_e2.dev = dev;
-  }
-  return lact_run(k, v, eta, beta, W, M, H, T, D, C, g_e2.p, st);
+  CallWork w;
+  const ttt_status ws = w.alloc(lact_work_bytes(H, T, D, C), st);
+  if (ws != TTT_OK) return ws;
+  return lact_run(k, v, eta, beta, W, M, H, T, D, C, w.get(), st);
 }
 
 namespace {
@@ -766,28 +772,6 @@ size_t mixer_work_bytes(int32_t H, int64_t T, int32_t D, int32_t C) {
 }  // namespace
 
 namespace {
-// Grows the process-wide work buffer to at least `need` bytes on the
-// current device (g_e2_mu held; growing waits for the stream first).
-ttt_status e2_grow(size_t need, hipStream_t st) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return TTT_ERR_HIP;
-  if (g_e2.bytes < need || g_e2.dev != dev) {
-    if (g_e2.p) {
-      (void)hipStreamSynchronize(st);
-      (void)hipFree(g_e2.p);
-    }
-    g_e2.p = nullptr;
-    g_e2.bytes = 0;
-    if (hipMalloc(&g_e2.p, need) != hipSuccess) {
-      (void)hipGetLastError();
-      return TTT_ERR_OOM;
-    }
-    g_e2.bytes = need;
-    g_e2.dev = dev;
-  }
-  return TTT_OK;
-}
-
 ttt_status device_present() {
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
@@ -875,9 +859,9 @@ extern "C" ttt_status e2ttt_mixer_forward(const void* x, const void* wqkv, const
   if (r != TTT_OK) return r;
   if (!W || !M || ((uintptr_t)W & 15) || ((uintptr_t)M & 15)) return TTT_ERR_INVALID_ARG;
   if ((r = device_present()) != TTT_OK) return r;
-  std::lock_guard<std::mutex> lock(g_e2_mu);
-  if ((r = e2_grow(mixer_work_bytes(H, T, D, C), (hipStream_t)stream)) != TTT_OK) return r;
-  return mixer_linear_run(x, wqkv, bias, eta_base, alpha_base, tau, W, M, out, H, T, D, dm, C, g_e2.p, stream);
+  CallWork w;
+  if ((r = w.alloc(mixer_work_bytes(H, T, D, C), (hipStream_t)stream)) != TTT_OK) return r;
+  return mixer_linear_run(x, wqkv, bias, eta_base, alpha_base, tau, W, M, out, H, T, D, dm, C, w.get(), stream);
 }
 
 // ============================================ SwiGLU fast-weight token mixer
@@ -1348,9 +1332,9 @@ extern "C" ttt_status e2ttt_mixer_gelu_forward(const void* x, const void* wqkv, 
   if (r != TTT_OK) return r;
   if ((r = gelu_check(W1, W2, M1, M2, Dh)) != TTT_OK) return r;
   if ((r = device_present()) != TTT_OK) return r;
-  std::lock_guard<std::mutex> lock(g_e2_mu);
-  if ((r = e2_grow(gelu_mixer_work_bytes(H, T, D, Dh, C), (hipStream_t)stream)) != TTT_OK) return r;
-  return mixer_gelu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, M1, M2, out, H, T, D, Dh, dm, C, g_e2.p,
+  CallWork w;
+  if ((r = w.alloc(gelu_mixer_work_bytes(H, T, D, Dh, C), (hipStream_t)stream)) != TTT_OK) return r;
+  return mixer_gelu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, M1, M2, out, H, T, D, Dh, dm, C, w.get(),
                         stream);
 }
 
@@ -1362,10 +1346,10 @@ extern "C" ttt_status e2ttt_mixer_swiglu_forward(const void* x, const void* wqkv
   if (r != TTT_OK) return r;
   if ((r = swiglu_check(W1, W2, W3, M1, M2, M3, Dh)) != TTT_OK) return r;
   if ((r = device_present()) != TTT_OK) return r;
-  std::lock_guard<std::mutex> lock(g_e2_mu);
-  if ((r = e2_grow(mlp_mixer_work_bytes(H, T, D, Dh, C), (hipStream_t)stream)) != TTT_OK) return r;
+  CallWork w;
+  if ((r = w.alloc(mlp_mixer_work_bytes(H, T, D, Dh, C), (hipStream_t)stream)) != TTT_OK) return r;
   return mixer_swiglu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, W3, M1, M2, M3, out, H, T, D, Dh, dm,
-                          C, g_e2.p, stream);
+                          C, w.get(), stream);
 }
 
 // ================================================== hybrid token-mixer block
@@ -1447,21 +1431,21 @@ extern "C" ttt_status e2ttt_hybrid_forward(const void* x, const void* wqkv, cons
   hipStream_t st = (hipStream_t)stream;
   const size_t base = Dh > 0 ? (gelu ? gelu_mixer_work_bytes(H, T, D, Dh, C) : mlp_mixer_work_bytes(H, T, D, Dh, C))
                              : mixer_work_bytes(H, T, D, C);
-  std::lock_guard<std::mutex> lock(g_e2_mu);
-  if ((r = e2_grow(base + hybrid_extra_bytes(H, T, D), st)) != TTT_OK) return r;
+  CallWork w;
+  if ((r = w.alloc(base + hybrid_extra_bytes(H, T, D), st)) != TTT_OK) return r;
   // TTT path: o_TTT into out; its projections P stay at the buffer's start
   if (gelu)
-    r = mixer_gelu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, M1, M2, out, H, T, D, Dh, dm, C, g_e2.p,
+    r = mixer_gelu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, M1, M2, out, H, T, D, Dh, dm, C, w.get(),
                        stream);
   else if (Dh > 0)
     r = mixer_swiglu_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, W2, W3, M1, M2, M3, out, H, T, D, Dh, dm, C,
-                         g_e2.p, stream);
+                         w.get(), stream);
   else
-    r = mixer_linear_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, M1, out, H, T, D, dm, C, g_e2.p, stream);
+    r = mixer_linear_run(x, wqkv, bias, eta_base, alpha_base, tau, W1, M1, out, H, T, D, dm, C, w.get(), stream);
   if (r != TTT_OK) return r;
   const int64_t N = 3LL * H * D + 3LL * H, HD = (int64_t)H * D, cap = hybrid_cap(T);
-  const float* P = (const float*)(((uintptr_t)g_e2.p + 255) & ~(uintptr_t)255);
-  Carve cv{(((uintptr_t)g_e2.p + base) + 255) & ~(uintptr_t)255};
+  const float* P = (const float*)(((uintptr_t)w.get() + 255) & ~(uintptr_t)255);
+  Carve cv{(((uintptr_t)w.get() + base) + 255) & ~(uintptr_t)255};
   bf16* qkv = cv.take<bf16>((size_t)T * 3 * HD * 2);
   bf16* qr = cv.take<bf16>((size_t)T * HD * 2);
   bf16* ks = cv.take<bf16>((size_t)H * cap * D * 2);
