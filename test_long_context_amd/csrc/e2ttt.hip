@@ -291,7 +291,9 @@ __device__ __forceinline__ void e2_split(const float (&x)[8], bf16x8& hi, bf16x8
   }
 }
 
-constexpr int E2_NW = 8;  // waves per chunk workgroup
+// waves per chunk workgroup: 12 (three per SIMD) where the registers allow
+// it (head size 128 without outputs), else 8
+__host__ __device__ constexpr int e2_waves(int D, bool OUT) { return (D == 128 && !OUT) ? 12 : 8; }
 
 // LACT: the chunk-wise baseline's single aggregation (K^W unused, dW taken
 // as dM): W_out = coef0 W0 + coef1 M0 + dM, M = coef2 M0 + dM.
@@ -299,7 +301,7 @@ constexpr int E2_NW = 8;  // waves per chunk workgroup
 // bf16, out float [T, H D]): the two workgroups of a 16-row block take one
 // 16-token tile of every 32-token block each, with the same W0 terms.
 template <int D, bool LACT = false, bool OUT = false>
-__global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Vv,
+__global__ void __launch_bounds__(e2_waves(D, OUT) * 64) e2_chunk_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Vv,
                                                        const float* __restrict__ KW, const float* __restrict__ KM,
                                                        const float* __restrict__ coef, const float* __restrict__ Win,
                                                        float* __restrict__ Wout, float* __restrict__ M, int64_t T,
@@ -311,10 +313,19 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   constexpr int KP = D + 8;    // LDS row pitch of a K block (elements)
   constexpr int BT = 32;       // tokens per block
   constexpr int NV = BT * D / 8 / 64;  // 16-byte vectors of a K block per lane
-  constexpr int NW = E2_NW;
+  constexpr int NW = e2_waves(D, OUT);
   constexpr int RED = NW * 2 * 16 * JH;  // floats of the cross-wave sums
   static_assert(RED * 4 <= NW * BT * KP * 2, "the cross-wave sums reuse the K blocks' LDS");
   __shared__ __attribute__((aligned(16))) bf16 Kb[NW][BT * KP];
+  // per wave: the block's v columns i0 .. i0 + 15 ([32 tokens][16], read
+  // back by transposing reads) and its K^W, K^M ([64]: K^W then K^M)
+  __shared__ __attribute__((aligned(16))) bf16 Vb[NW][BT * 16];
+  __shared__ __attribute__((aligned(16))) float Sb[NW][2 * BT];
+  // with three waves per SIMD the W0 terms (the E product's B operand, the
+  // same for every wave) live in LDS instead of each wave's registers
+  constexpr bool W_LDS = NW > 8;
+  constexpr int WP = D + 8;  // LDS row pitch of the W0 terms
+  __shared__ __attribute__((aligned(16))) bf16 Wt[W_LDS ? 2 * 16 * WP : 8];
   // Workgroups are dealt to the 8 XCDs round-robin (XCD = id % 8). With
   // H % 8 == 0 the index is remapped so all 2 D / 16 workgroups of a head
   // run on one XCD (heads x, x + 8, ... on XCD x): each reads the head's
@@ -341,9 +352,11 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   const float* KMh = KM + (int64_t)h * T + a0;
   const float* W0 = Win + (int64_t)h * D * D;
   // lane parts of the byte offsets within a block: a K block is BT whole
-  // rows, so vector q of lane l is bytes 16 (l + 64 q) of it; v, K^W and
-  // K^M of token 4 g of the block (column i0 + c of v)
-  const uint32_t ko = lane * 16, vo = (4 * g * D + i0 + c) * 2, so = 4 * g * 4;
+  // rows, so vector q of lane l is bytes 16 (l + 64 q) of it; lane l reads
+  // v columns i0 + 8 (l % 2) .. + 7 of token l / 2, and K^W, K^M of token
+  // l % 32 (one coalesced load each; the lanes that need them read them
+  // back from LDS)
+  const uint32_t ko = lane * 16, vo = ((lane >> 1) * D + i0 + 8 * (lane & 1)) * 2, so = (lane & 31) * 4;
 
   // W0 rows i0 + c (this lane's B operand of e_t), requested first; the
   // first block's operands and the state elements of the final update are
@@ -361,6 +374,8 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   for (int jt = 0; jt < JT; ++jt) dw[jt] = dm[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   bf16* Ks = Kb[wid];
+  bf16* Vs = Vb[wid];
+  float* Ss = Sb[wid];
   const int nb = (n + BT - 1) / BT;
   // a block's operands: its K rows (NV vectors per lane) and, for the tokens
   // of this lane's accumulator rows, v (column i0 + c), K^W and K^M
@@ -370,8 +385,8 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   // hence their share of the products (the clamped rows are finite).
   struct Blk {
     bf16x8 k[NV];
-    unsigned short v[2][4];
-    float kw[2][4], km[2][4];
+    bf16x8 v;
+    float kw, km;
   };
   // Each block is read through buffer resources that start at the block
   // and cover only its tokens inside the chunk (none for blocks past it), so
@@ -390,14 +405,9 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
 #pragma unroll
     for (int q = 0; q < NV; ++q)
       o.k[q] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 1024 * q, 0, 0));
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o.v[tile][e] = __builtin_amdgcn_raw_buffer_load_b16(rv, vo + (16 * tile + e) * D * 2, 0, 0);
-        o.kw[tile][e] = LACT ? 0.f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkw, so + 4 * (16 * tile + e), 0, 0));
-        o.km[tile][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkm, so + 4 * (16 * tile + e), 0, 0));
-      }
+    o.v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0));
+    o.kw = LACT ? 0.f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkw, so, 0, 0));
+    o.km = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkm, so, 0, 0));
   };
   // operands run one block ahead of the products (two waves per SIMD hide
   // the rest)
@@ -409,21 +419,40 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
       const int vi = lane + 64 * q, row = vi / (D / 8), col = (vi % (D / 8)) * 8;
       *(bf16x8*)(Ks + row * KP + col) = cur.k[q];
     }
+    *(bf16x8*)(Vs + (lane >> 1) * 16 + 8 * (lane & 1)) = cur.v;
+    Ss[lane] = lane < 32 ? cur.kw : cur.km;
     load(nxt, blk + NW);
 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     floatx4 et[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
+    if constexpr (W_LDS) {
+      // (per tile the same order of products as below)
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        Frag8<bf16> a;
-        ld8(a, Ks + (16 * tile + c) * KP + 32 * s + 8 * g);
-        mma16(et[tile], a, wh[s]);
-        mma16(et[tile], a, wl[s]);
+        Frag8<bf16> bh, bl;
+        ld8(bh, Wt + c * WP + 32 * s + 8 * g);
+        ld8(bl, Wt + (16 + c) * WP + 32 * s + 8 * g);
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+          Frag8<bf16> a;
+          ld8(a, Ks + (16 * tile + c) * KP + 32 * s + 8 * g);
+          mma16(et[tile], a, bh);
+          mma16(et[tile], a, bl);
+        }
       }
+    } else {
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          Frag8<bf16> a;
+          ld8(a, Ks + (16 * tile + c) * KP + 32 * s + 8 * g);
+          mma16(et[tile], a, wh[s]);
+          mma16(et[tile], a, wl[s]);
+        }
+    }
     if constexpr (OUT) {
       // this workgroup's output tile of the block: o = Q W0^T for rows i0 .. i0 + 15
       const int tile = jh;
@@ -444,15 +473,23 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
         if (tok < n) out[(a0 + tok) * HD + (int64_t)h * D + i0 + c] = ot[e];
       }
     }
+    // v of tokens 16 tile + 4 g + e, column i0 + c (transposing reads of
+    // the wave's v slice, as for the aggregations' K^T operand), and their
+    // K^W, K^M (the same four values across each 16-lane group)
     float xw[8], xm[8];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
+    for (int tile = 0; tile < 2; ++tile) {
+      const e2_shortx4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (e2_lds_s4_t)(Vs + (16 * tile + 4 * g + (c >> 2)) * 16 + 4 * (c & 3)));
+      const floatx4 kw4 = *(const floatx4*)(Ss + 16 * tile + 4 * g);
+      const floatx4 km4 = *(const floatx4*)(Ss + BT + 16 * tile + 4 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float ee = et[tile][e] - __builtin_bit_cast(float, (uint32_t)cur.v[tile][e] << 16);
-        xw[4 * tile + e] = cur.kw[tile][e] * ee;
-        xm[4 * tile + e] = cur.km[tile][e] * ee;
+        const float ee = et[tile][e] - __builtin_bit_cast(float, (uint32_t)(unsigned short)vt[e] << 16);
+        xw[4 * tile + e] = kw4[e] * ee;
+        xm[4 * tile + e] = km4[e] * ee;
       }
+    }
     Frag8<bf16> xwh, xwl, xmh, xml;
     e2_split(xw, xwh.v, xwl.v);
     e2_split(xm, xmh.v, xml.v);
@@ -475,23 +512,23 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   Blk b0, b1;
   load(b0, wid);
   // the state elements this thread updates at the end: (i, j) = (e / JH, e % JH)
-  constexpr int EPT = 16 * JH / (NW * 64);
-  static_assert(EPT * NW * 64 == 16 * JH, "the final update gives each thread the same number of elements");
+  constexpr int NEL = 16 * JH, EPT = (NEL + NW * 64 - 1) / (NW * 64);
   float* Wo = Wout + (int64_t)h * D * D;
   float* Mh = M + (int64_t)h * D * D;
   float w0e[EPT], m0e[EPT];
   auto load_state = [&]() {
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-      const int e = threadIdx.x + k * NW * 64;
+      const int e = min((int)threadIdx.x + k * NW * 64, NEL - 1);
       const int64_t idx = (int64_t)(i0 + e / JH) * D + j0 + e % JH;
       w0e[k] = W0[idx];
       m0e[k] = Mh[idx];
     }
   };
-  // (the variant with outputs has no registers to hold them through the
-  // loop: it reads them at the end)
-  if constexpr (!OUT) load_state();
+  // (with outputs or three waves per SIMD there are no registers to hold
+  // them through the loop: they are read at the end)
+  constexpr bool LATE_STATE = OUT || NW > 8;
+  if constexpr (!LATE_STATE) load_state();
 #pragma unroll
   for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -501,6 +538,17 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
       wh[s].v[e] = hi;
       wl[s].v[e] = (bf16)(w - (float)hi);
     }
+  if constexpr (W_LDS) {
+    // every wave formed the same terms: wave 0 stores them (rows c, columns
+    // 32 s + 8 g .. + 7 of each lane), then all waves read them from LDS
+    if (wid == 0)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        *(bf16x8*)(Wt + c * WP + 32 * s + 8 * g) = wh[s].v;
+        *(bf16x8*)(Wt + (16 + c) * WP + 32 * s + 8 * g) = wl[s].v;
+      }
+    __syncthreads();
+  }
   for (int blk = wid; blk < nb; blk += 2 * NW) {
     step(b0, b1, blk);
     if (blk + NW < nb) step(b1, b0, blk + NW);
@@ -519,10 +567,11 @@ __global__ void __launch_bounds__(E2_NW * 64) e2_chunk_kernel(const bf16* __rest
   __syncthreads();
   const float* cf = coef + ((int64_t)h * nch + r) * 4;
   const float c0 = cf[0], c1 = cf[1], c2 = cf[2];
-  if constexpr (OUT) load_state();
+  if constexpr (LATE_STATE) load_state();
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int e = threadIdx.x + k * NW * 64;
+    if (e >= NEL) break;
     const int i = e / JH, j = e % JH;
     float sw = 0.f, sm = 0.f;
 #pragma unroll
@@ -633,10 +682,10 @@ ttt_status e2_run(const void* k, const void* v, const float* eta, const float* b
     const float* src = (r & 1) ? W2 : W;
     float* dst = (r & 1) ? W : W2;
     if (D == 128)
-      hipLaunchKernelGGL(e2_chunk_kernel<128>, grid, dim3(E2_NW * 64), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
+      hipLaunchKernelGGL(e2_chunk_kernel<128>, grid, dim3(e2_waves(128, false) * 64), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
                          src, dst, M, T, r * C, n, nch, r);
     else
-      hipLaunchKernelGGL(e2_chunk_kernel<64>, grid, dim3(E2_NW * 64), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
+      hipLaunchKernelGGL(e2_chunk_kernel<64>, grid, dim3(e2_waves(64, false) * 64), 0, st, (const bf16*)k, (const bf16*)v, KW, KM, coef,
                          src, dst, M, T, r * C, n, nch, r);
     if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
   }
@@ -721,10 +770,10 @@ ttt_status lact_run(const void* k, const void* v, const float* eta, const float*
     float* dst = (r & 1) ? W : W2;
     // per-token weights eta_t; the K^W argument is not read by this rule
     if (D == 128)
-      hipLaunchKernelGGL((e2_chunk_kernel<128, true>), grid, dim3(E2_NW * 64), 0, st, (const bf16*)k, (const bf16*)v,
+      hipLaunchKernelGGL((e2_chunk_kernel<128, true>), grid, dim3(e2_waves(128, false) * 64), 0, st, (const bf16*)k, (const bf16*)v,
                          eta, eta, coef, src, dst, M, T, r * C, n, nch, r);
     else
-      hipLaunchKernelGGL((e2_chunk_kernel<64, true>), grid, dim3(E2_NW * 64), 0, st, (const bf16*)k, (const bf16*)v,
+      hipLaunchKernelGGL((e2_chunk_kernel<64, true>), grid, dim3(e2_waves(64, false) * 64), 0, st, (const bf16*)k, (const bf16*)v,
                          eta, eta, coef, src, dst, M, T, r * C, n, nch, r);
     if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
   }
@@ -838,10 +887,10 @@ ttt_status mixer_linear_run(const void* x, const void* wqkv, const float* bias, 
     const float* src = (r & 1) ? W2 : W;
     float* dst = (r & 1) ? W : W2;
     if (D == 128)
-      hipLaunchKernelGGL((e2_chunk_kernel<128, false, true>), grid, dim3(E2_NW * 64), 0, st, k, v, KW, KM, coef, src,
+      hipLaunchKernelGGL((e2_chunk_kernel<128, false, true>), grid, dim3(e2_waves(128, true) * 64), 0, st, k, v, KW, KM, coef, src,
                          dst, M, T, r * C, n, nch, r, q, out);
     else
-      hipLaunchKernelGGL((e2_chunk_kernel<64, false, true>), grid, dim3(E2_NW * 64), 0, st, k, v, KW, KM, coef, src,
+      hipLaunchKernelGGL((e2_chunk_kernel<64, false, true>), grid, dim3(e2_waves(64, true) * 64), 0, st, k, v, KW, KM, coef, src,
                          dst, M, T, r * C, n, nch, r, q, out);
     if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
   }
