@@ -500,13 +500,13 @@ __device__ __forceinline__ void epi_chunk(const GemmArgs& g, int m, int n, float
     const uint32_t sd = g.seed;
     if (vec) {
       const floatx4 w = pre - g.scale * v;
-      *(floatx4*)W = w;
+      __builtin_nontemporal_store(w, (floatx4*)W);
       if (two) {
         if (g.seed) {
           bf16x4 hi;
 #pragma unroll
           for (int e = 0; e < 4; ++e) hi[e] = sr_bf16(w[e], sd, idx + e);
-          *(bf16x4*)H = hi;
+          __builtin_nontemporal_store(hi, (bf16x4*)H);
         } else {
           const bf16x4 hi = cvt4(w);
           *(bf16x4*)H = hi;
@@ -619,7 +619,11 @@ __device__ __forceinline__ void gemm_epilogue_staged(const GemmArgs& g, floatx4 
       const int c = lane + 64 * k;
       const int row = c / CPR, col = (c % CPR) * 4;
       const int m = min(mw + 16 * i + row, g.M - 1), n = min(nw + col, g.N - 4);
-      dst[k] = *(const floatx4*)((const float*)g.C + (long)m * g.ldc + n);
+      const floatx4* src = (const floatx4*)((const float*)g.C + (long)m * g.ldc + n);
+      // the SGD master is read and written once per update: streamed past
+      // the caches, which then keep the other streams' operands
+      if constexpr (EPI == (int)Epi::SGD) dst[k] = __builtin_nontemporal_load(src);
+      else dst[k] = *src;
     }
   };
   if constexpr (RMW) {
