@@ -117,6 +117,39 @@ def update_replay(c, tla, torch, blocks=2):
     print(json.dumps(dict(launches=2 * blocks)), flush=True)
 
 
+def update_isolated_us(c, tla, torch, reps=5):
+    """Average duration (us) of one update launch on an otherwise idle GPU:
+    a block's dW3 and dW12 products with the SGD epilogue, as the engine
+    launches them, timed with events over `reps` pairs after one warm-up
+    pair (run after the timed region: context for the in-step figure, which
+    shares the chip with the main stream)."""
+    d, Fd, b = c["d_model"], c["dyn_ffn_hidden"], c["minibatch"]
+    bf = torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(0)
+    gt = (torch.randn(b, d, device="cuda", generator=g) * 0.1).to(bf)
+    hm = (torch.randn(b, Fd, device="cuda", generator=g) * 0.1).to(bf)
+    dh12 = (torch.randn(b, 2 * Fd, device="cuda", generator=g) * 0.1).to(bf)
+    xn = (torch.randn(b, d, device="cuda", generator=g) * 0.1).to(bf)
+    m3 = torch.randn(d, Fd, device="cuda", generator=g) * 0.02
+    m12 = torch.randn(2 * Fd, d, device="cuda", generator=g) * 0.02
+    h3 = torch.empty(d, Fd, dtype=bf, device="cuda")
+    h12 = torch.empty(2 * Fd, d, dtype=bf, device="cuda")
+
+    def pair(i):
+        tla.gemm(gt, hm, d, Fd, b, "sgd", m3, a_kmajor=False, b_kmajor=False, C2=h3, scale=c["alpha"],
+                 seed=2 * i + 1)
+        tla.gemm(dh12, xn, 2 * Fd, d, b, "sgd", m12, a_kmajor=False, b_kmajor=False, C2=h12, scale=c["alpha"],
+                 seed=2 * i + 2)
+    pair(0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        pair(i + 1)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (2 * reps)
+
+
 def pmc_update_summary(c, dirs, workload):
     """Bytes per update launch from FETCH_SIZE and WRITE_SIZE runs of
     --update-replay and of --copy-probe (each counter scaled by copy bytes /
@@ -855,6 +888,12 @@ def main():
                 traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE of --update-replay, "
                              "copy-scaled), averaged over a block's dW3 and dW12 launches",
                 note="durations measured on the update's side streams, beside the main stream's kernels")
+    if c["dtype"] == "bf16" and c["n_dynamic"] > 0:
+        iso = update_isolated_us(c, tla, torch)
+        iso_gbs = upd["bytes"] / nu / (iso * 1e-6) / 1e9
+        roof.update(isolated_avg_launch_us=round(iso, 2), isolated_gbs=round(iso_gbs, 1),
+                    isolated_frac=round(iso_gbs / PEAK_HBM_GBS, 4),
+                    isolated_note="the same launches replayed alone on the GPU after the timed region")
     ce = live["ce"]
     c_avg, c_gbs = rate(ce, "bytes")
     attn = {k: sum(live[a][k] for a in ATTN_CLASSES) for k in ("ms", "launches", "flops", "bytes")}

@@ -721,12 +721,14 @@ ttt_status loop_backward(ttt_ctx* c, int64_t a0, int n, hipStream_t st) {
       bt.sB = 2L * Fd * d;
       RUN(gemm_nn_split(c, KC_GL, c->dh12d[i], 2 * Fd, c->dw12[i], d, n, d, 2 * Fd, c->part, &ns, st, bt));
     }
-    // the update of this block once its query-side attention backward is
-    // queued, so that it runs beside the key-side attention and the next
-    // products rather than this block's data-gradient products (2348 against
-    // 2355-2357 ms per 3B step on one box; block s has no attention backward
-    // in the loop; TTT_UPDATE_AT=now launches here, =attn before the
-    // attention backward, =split dW3 here and dW12 there)
+    // the update of this block when its attention backward starts, so that
+    // it runs beside the attention backward and the next products rather
+    // than this block's data-gradient products (with the epilogue's
+    // streamed master: 2246-2249 against 2262-2264 ms per 3B step after the
+    // query-side kernel and 2269-2271 here, one box; block s has no
+    // attention backward in the loop; TTT_UPDATE_AT=now launches here, =dq
+    // after the query-side kernel, =split dW3 here and dW12 at the
+    // attention backward)
     if (!c->upd_at_attn || l == s) RUN(launch_update(c, i, a0, n, st));
     else if (c->upd_split) RUN(launch_update(c, i, a0, n, st, 1));
     if (l == s) break;
@@ -1079,10 +1081,10 @@ ttt_status ttt_init(const ttt_config* cfg, const ttt_weights* w, void* stream, t
     const char* uk = getenv("TTT_UPDATE_KERNEL");
     c->fused_update = c->dt == DT::BF16 && B == 1 && !c->sr_round && uk && strcmp(uk, "fused") == 0;
     const char* ua = getenv("TTT_UPDATE_AT");
-    // default "dq": once the block's query-side attention backward is queued
+    // default "attn": when the block's attention backward starts
     c->upd_at_attn = !(ua && strcmp(ua, "now") == 0);
     c->upd_split = ua && strcmp(ua, "split") == 0;
-    c->upd_after_dq = !(ua && (strcmp(ua, "attn") == 0 || strcmp(ua, "split") == 0 || strcmp(ua, "now") == 0));
+    c->upd_after_dq = ua && strcmp(ua, "dq") == 0;
     const char* us = getenv("TTT_UPDATE_STREAM");
     c->upd_main = us && strcmp(us, "main") == 0;
     const char* ug = getenv("TTT_UPDATE_GRID");
